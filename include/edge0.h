@@ -1,0 +1,266 @@
+/*
+ * edge0.h - C ABI of the MI355X (gfx950) streaming-MoE decode path.
+ *
+ * Sources (cited by page title and section):
+ *   [Edge0]     "The Other Half of the Memory Wall: Serving 35B MoEs from SSD
+ *               with Trained Routing Prediction" (arXiv HTML).
+ *   [Review]    "Waking the MoE on SSD: Serving a 35B MoE at 20 tok/s on a
+ *               24 GB Desktop with Edge0" (jaehun.me review of the paper).
+ *   [Cacheable] "Cacheable by Design?" (arXiv 2608.18261).
+ *
+ * One decode step of one streaming MoE layer: a per-layer prerouter head
+ * predicts the next layer's routing one token ahead ([Edge0] §3.2 "Head",
+ * "Prediction-as-routing"), a softmax-top-K commits it ([Edge0] App. A), the
+ * int4 group-quantised experts named by the routing are dequantised from a
+ * pool of slots in HBM and run as SwiGLU FFNs with an unmerged LoRA delta
+ * ([Edge0] §3.1 "Math contract", §3.3), and the outputs are combined with
+ * the routing weights.  Staging copies predicted experts into slots ahead of
+ * use ([Edge0] Figure 1, §3.1 "Executor paths").
+ *
+ * Conventions for every call
+ *   - Pointers marked "device" are device memory on the current HIP device;
+ *     "host" pointers are host memory.  The library never allocates, frees
+ *     or retains caller memory, except inside the opaque handles
+ *     (edge0_stack, edge0_stager) which own what their create call says.
+ *   - Kernels are enqueued on the given stream (NULL = the null stream); a
+ *     call returns once its work is enqueued, and outputs are valid when the
+ *     stream reaches that point.
+ *   - bf16 and fp16 are passed as their 16-bit patterns; fp32 as float.
+ *   - Return value: EDGE0_OK (0) or a negative EDGE0_E* code.  No C++
+ *     exception crosses the ABI.  Arguments are checked before anything is
+ *     enqueued; on an error return nothing was enqueued.
+ *   - Device-side checks: an expert id outside [0, E) or a slot outside
+ *     [0, n_slots) met by a kernel is not dereferenced; that expert's
+ *     contribution is skipped and EDGE0_ERANGE is recorded in the workspace
+ *     error word (edge0_workspace_error reads and clears it).
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef EDGE0_H
+#define EDGE0_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  EDGE0_OK = 0,
+  EDGE0_EINVAL = -1,   /* NULL required pointer, unsupported shape or argument */
+  EDGE0_EHIP = -2,     /* a HIP runtime or launch error */
+  EDGE0_ENOSLOT = -3,  /* every slot of the pool is pinned by pending sets */
+  EDGE0_ERANGE = -4,   /* an expert id or slot index out of range */
+  EDGE0_ENOMEM = -5    /* an allocation owned by a handle failed */
+};
+
+/* Returns a static string describing an EDGE0_* code. */
+const char* edge0_strerror(int code);
+
+/* -------------------------------------------------------------------------
+ * Model description ([Edge0] §3 "System Design": one spec per model with
+ * expert count, K, routing family, quantisation and weight layout).
+ *
+ * Supported values: d_model % 64 == 0 and d_model / 32 in {8, 16, 32} or a
+ * multiple of 64; d_inter % 64 == 0; group_size % 32 == 0 dividing both
+ * d_model and d_inter; 1 <= top_k <= min(16, n_experts); n_experts <= 1024;
+ * 0 <= lora_rank <= 64; head_hidden % 64 == 0 (or 0 when no head is used).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t d_model;      /* d: hidden size */
+  int32_t n_experts;    /* E: routed experts per layer */
+  int32_t d_inter;      /* I: expert intermediate size */
+  int32_t top_k;        /* K: experts per token */
+  int32_t group_size;   /* g: int4 quantisation group along the input axis */
+  int32_t lora_rank;    /* r: recovery-LoRA rank, 0 = no adapter */
+  float lora_alpha;     /* alpha: the delta is scaled by alpha / r */
+  int32_t head_hidden;  /* H: prerouter fc1 width */
+} edge0_moe_shape;
+
+/* -------------------------------------------------------------------------
+ * Expert bundle = the content of one slot ([Edge0] §3.1 "Executor paths":
+ * the nine arrays gate/up/down x weights/scales/biases; §3.3: the LoRA is
+ * kept as separate low-rank factors, never merged).
+ *
+ * Dequantised weight: W[o][i] = s[o][i/g] * q[o][i] + b[o][i/g], q in 0..15
+ * ([Edge0] §2 "Quantization": int4 affine, groups along the input axis).
+ *
+ * Device layout inside a bundle (every array starts on a 256-byte boundary):
+ *   gate_q, up_q : u32 [I][d/8], row-major; input i of row o is the nibble
+ *                  at bits 4*(i%8) of word o*(d/8) + i/8.
+ *   down_q       : u32 tiled [d/64][I/32][64][4]: 1 KiB tile (rb, c) holds
+ *                  rows 64*rb..64*rb+63, inputs 32*c..32*c+31; row o of the
+ *                  tile is its 16 bytes at offset 16*(o%64), nibble order as
+ *                  above within each word.
+ *   gate_s/b, up_s/b : bf16 [I][d/g] row-major.
+ *   down_s/b     : bf16 [I/g][d] (group-major: all rows of group 0 first).
+ *   LoRA (lora_rank > 0), bf16: a_gate [r][d], b_gate [I][r], a_up [r][d],
+ *                  b_up [I][r], a_down [r][I], b_down [d][r], row-major.
+ * The logical (row-major [out][in/8] words, [out][in/g] scales) form is what
+ * edge0_pack_bundle accepts.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t gate_q, gate_s, gate_b, up_q, up_s, up_b, down_q, down_s, down_b;
+  int64_t a_gate, b_gate, a_up, b_up, a_down, b_down;  /* -1 when lora_rank == 0 */
+  int64_t bytes;                                       /* total, multiple of 256 */
+} edge0_bundle_layout;
+
+/* Byte offsets of the arrays inside one bundle.  EDGE0_EINVAL for an
+ * unsupported shape. */
+int edge0_bundle_layout_of(const edge0_moe_shape* shape, edge0_bundle_layout* out);
+
+/* Logical (row-major) expert arrays, all device pointers, as produced by a
+ * checkpoint: *_q u32 [out][in/8], *_s and *_b bf16 [out][in/g]; gate and up
+ * are [I x d], down is [d x I].  LoRA pointers may be NULL iff lora_rank == 0. */
+typedef struct {
+  const void *gate_q, *gate_s, *gate_b, *up_q, *up_s, *up_b, *down_q, *down_s, *down_b;
+  const void *a_gate, *b_gate, *a_up, *b_up, *a_down, *b_down;
+} edge0_expert_arrays;
+
+/* Writes one bundle in the device layout at bundle_dst (device, layout.bytes
+ * bytes, 256-byte aligned) from the logical arrays.  Pure data movement (no
+ * rounding); sources and destination must not overlap. */
+int edge0_pack_bundle(const edge0_moe_shape* shape, const edge0_expert_arrays* src,
+                      void* bundle_dst, hipStream_t stream);
+
+/* Pool of staged slots in HBM: slot s occupies [base + s*slot_bytes,
+ * base + s*slot_bytes + layout.bytes).  slot_bytes >= layout.bytes and a
+ * multiple of 256. */
+typedef struct {
+  void* base;           /* device */
+  int64_t slot_bytes;
+  int32_t n_slots;
+} edge0_slot_pool;
+
+/* -------------------------------------------------------------------------
+ * Workspace: scratch device memory for the single-layer calls below
+ * (partial sums, LoRA factors, the SwiGLU activations, completion counters
+ * and the error word).  The caller allocates edge0_workspace_bytes(shape)
+ * bytes (256-byte aligned) and zero-fills them once before first use; the
+ * calls leave the counters zero again.  Calls that may run concurrently
+ * need distinct workspaces.
+ * ---------------------------------------------------------------------- */
+size_t edge0_workspace_bytes(const edge0_moe_shape* shape);
+
+/* Waits for `stream`, then returns the workspace error word (EDGE0_OK or
+ * EDGE0_ERANGE) and clears it. */
+int edge0_workspace_error(void* workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Plain router + softmax-top-K commit ([Edge0] §2 "MoE routing", App. A
+ * "Softmax-topk"): logits = W_r x (fp32 accumulation); ids = the K largest
+ * logits in order (value descending, lower index first on ties);
+ * w_k = exp(l_k - l_max) / sum_{j in ids} exp(l_j - l_max), which equals
+ * g[ids]/sum g[ids] for g = softmax(l).
+ *   w_router : device bf16 [E][d]
+ *   x        : device bf16 [d]
+ *   logits_out : device fp32 [E] or NULL
+ *   ids_out  : device int32 [K];  w_out : device fp32 [K]
+ * ---------------------------------------------------------------------- */
+int edge0_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
+                 float* logits_out, int32_t* ids_out, float* w_out,
+                 void* workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Prerouter head and commit ([Edge0] §3.2 "Head", "Prediction-as-routing",
+ * "Feature drift"; [Review] toy example).  The head owned by layer N runs
+ * at token t on layer N's normalised hidden state and predicts layer N+1's
+ * routing at token t+1:
+ *   f      = [x ; onehot(ids_now) ; onehot(ids_prev)]        (d + 2E)
+ *   z1     = fc1 f + b1,  a = 0.5 z1 (1 + erf(z1 / sqrt 2))   (H)
+ *   logits = w2 a + b2 + wl x                                 (E)
+ * then the same softmax-top-K as edge0_router.  The one-hot blocks hold a 1
+ * per routed expert (binary, not weighted); ids_now is the routing layer N
+ * executed at token t, ids_prev the routing it executed at token t-1 (NULL
+ * at the first decode token: that block is zero).
+ * Head weights (fp16, device): fc1 is split into its hidden-state columns
+ * w1x [H][d] and its one-hot columns stored transposed, w1oh [2E][H] (row e
+ * is the column of expert e in this token's block, row E+e in the previous
+ * token's block); b1 [H]; w2 [E][H]; b2 [E]; wl [E][d] (linear residual,
+ * no bias).  b1, b2, wl may be NULL (zero).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *w1x, *w1oh, *b1, *w2, *b2, *wl;
+} edge0_head;
+
+int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* head, const void* x,
+                    const int32_t* ids_now, const int32_t* ids_prev,
+                    float* logits_out, int32_t* ids_out, float* w_out,
+                    void* workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * One MoE layer over the committed experts ([Edge0] §3.1 "Math contract",
+ * §3.3; Figure 1 sum node):
+ *   for each k:  e = ids[k], slot = slot_table[e]
+ *     G = gate(x) + (a/r) B_gate (A_gate x),  U = up(x) + (a/r) B_up (A_up x)
+ *     h = silu(G) * U,                        silu(z) = z / (1 + e^-z)
+ *     D_k = down(h) + (a/r) B_down (A_down h)
+ *   y = bf16( sum_k w[k] D_k )   (fp32 throughout, one rounding at the end)
+ *   slot_table : device int32 [E], id -> slot ("take" through the slot
+ *                table: indices stay on the device, [Edge0] §3.1)
+ *   ids, w     : device int32 [K], fp32 [K]
+ *   x, y       : device bf16 [d]; y must not alias x
+ * ---------------------------------------------------------------------- */
+int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                    const int32_t* slot_table, const int32_t* ids, const float* w,
+                    const void* x, void* y, void* workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Decode stack: n_layers pre-norm residual MoE blocks (no attention),
+ *   x_L = bf16(RMSNorm(h_L)),  RMSNorm(h) = h / sqrt(mean(h^2) + eps)
+ *   routing_L = committed prediction (consumer layers, step > 0) or the
+ *               plain router (every other layer, and every layer at step 0)
+ *   y_L = edge0_moe_layer(x_L),  h_{L+1} = bf16(h_L + y_L)
+ *   heads of owner layers predict (L+1, step+1) from x_L, the ids layer L
+ *   executed now and at the previous step ([Edge0] §3.2 "Head",
+ *   "Motivation": double shift, one token of lead).
+ * The handle owns its routing state, per-layer buffers and workspace.
+ * Weights stay caller-owned and must outlive the handle.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_layers;
+  int32_t owner_first, owner_last;        /* heads run at layers [first, last] */
+  int32_t consumer_first, consumer_last;  /* layers routed by predictions     */
+  float rms_eps;
+} edge0_stack_spec;
+
+typedef struct edge0_stack edge0_stack;
+
+/* slot_tables : device int32 [n_layers][E]
+ * routers     : host array [n_layers] of device bf16 [E][d] (entries of
+ *               consumer layers are still used at step 0)
+ * heads       : host array [n_layers]; entries of owner layers are used
+ * Every owner L must have L+1 a consumer and vice versa. */
+int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
+                       const edge0_stack_spec* spec, const edge0_slot_pool* pool,
+                       const int32_t* slot_tables, const void* const* routers,
+                       const edge0_head* heads);
+
+/* Runs decode step `step` (0, 1, 2, ... in order) on h0 (device bf16 [d]),
+ * writing the final hidden state to h_out (device bf16 [d]).  Uses a HIP
+ * graph of the step's launches after the first call of each step parity. */
+int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, int32_t step,
+                     hipStream_t stream);
+
+/* Device pointers to the handle's per-layer results of the last step:
+ *   x : bf16 [n_layers][d]   (normalised inputs)
+ *   y : bf16 [n_layers][d]   (layer outputs)
+ *   h : bf16 [n_layers+1][d] (h[0] = h0, h[L+1] after layer L)
+ *   ids, w : int32/fp32 [n_layers][K] (routing each layer executed)
+ *   pred_ids, pred_w : int32/fp32 [n_layers][K] (row L+1: the prediction
+ *                head L made this step for the next step) */
+typedef struct {
+  const void *x, *y, *h;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* pred_ids;
+  const float* pred_w;
+} edge0_stack_buffers;
+int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffers* out);
+void edge0_stack_destroy(edge0_stack* st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EDGE0_H */

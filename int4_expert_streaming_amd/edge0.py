@@ -1,0 +1,243 @@
+"""Thin ctypes binding of libedge0.so (the C ABI declared in include/edge0.h).
+
+Argument marshalling only: torch tensors supply device pointers, the current
+torch stream supplies the HIP stream, and every computation runs in the
+library's HIP kernels.  Importing this module loads the library and fails
+loudly if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libedge0.so")
+
+EDGE0_OK, EDGE0_EINVAL, EDGE0_EHIP, EDGE0_ENOSLOT, EDGE0_ERANGE, EDGE0_ENOMEM = 0, -1, -2, -3, -4, -5
+
+
+class Edge0Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+    return C.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+
+# --------------------------------------------------------------------- structs
+class MoeShape(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_experts", C.c_int32), ("d_inter", C.c_int32),
+                ("top_k", C.c_int32), ("group_size", C.c_int32), ("lora_rank", C.c_int32),
+                ("lora_alpha", C.c_float), ("head_hidden", C.c_int32)]
+
+
+_LAYOUT_KEYS = ("gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b", "down_q", "down_s",
+                "down_b", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+
+
+class BundleLayout(C.Structure):
+    _fields_ = [(k, C.c_int64) for k in _LAYOUT_KEYS] + [("bytes", C.c_int64)]
+
+
+class ExpertArrays(C.Structure):
+    _fields_ = [(k, C.c_void_p) for k in _LAYOUT_KEYS]
+
+
+class SlotPool(C.Structure):
+    _fields_ = [("base", C.c_void_p), ("slot_bytes", C.c_int64), ("n_slots", C.c_int32)]
+
+
+_HEAD_KEYS = ("w1x", "w1oh", "b1", "w2", "b2", "wl")
+
+
+class Head(C.Structure):
+    _fields_ = [(k, C.c_void_p) for k in _HEAD_KEYS]
+
+
+class StackSpec(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("owner_first", C.c_int32), ("owner_last", C.c_int32),
+                ("consumer_first", C.c_int32), ("consumer_last", C.c_int32),
+                ("rms_eps", C.c_float)]
+
+
+class StackBuffers(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("y", C.c_void_p), ("h", C.c_void_p), ("ids", C.c_void_p),
+                ("w", C.c_void_p), ("pred_ids", C.c_void_p), ("pred_w", C.c_void_p)]
+
+
+_P = C.c_void_p
+_SIG = {
+    "edge0_strerror": (C.c_char_p, [C.c_int]),
+    "edge0_bundle_layout_of": (C.c_int, [C.POINTER(MoeShape), C.POINTER(BundleLayout)]),
+    "edge0_pack_bundle": (C.c_int, [C.POINTER(MoeShape), C.POINTER(ExpertArrays), _P, _P]),
+    "edge0_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
+    "edge0_workspace_error": (C.c_int, [_P, _P]),
+    "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P]),
+    "edge0_prerouter": (C.c_int, [C.POINTER(MoeShape), C.POINTER(Head), _P, _P, _P, _P, _P, _P,
+                                  _P, _P]),
+    "edge0_moe_layer": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P, _P, _P,
+                                  _P, _P]),
+    "edge0_stack_create": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.POINTER(StackSpec),
+                                     C.POINTER(SlotPool), _P, C.POINTER(_P), C.POINTER(Head)]),
+    "edge0_stack_step": (C.c_int, [_P, _P, _P, C.c_int32, _P]),
+    "edge0_stack_get_buffers": (C.c_int, [_P, C.POINTER(StackBuffers)]),
+    "edge0_stack_destroy": (None, [_P]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def strerror(code: int) -> str:
+    return lib.edge0_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != EDGE0_OK:
+        raise Edge0Error(code, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_shape(s) -> MoeShape:
+    """MoeShape from any object with the MoE spec fields (d_model, n_experts,
+    d_inter, top_k, group, lora_rank, lora_alpha, head_hidden)."""
+    return MoeShape(s.d_model, s.n_experts, s.d_inter, s.top_k, s.group, s.lora_rank,
+                    float(s.lora_alpha), s.head_hidden)
+
+
+# --------------------------------------------------------------------- calls
+def edge0_bundle_layout_of(shape: MoeShape) -> BundleLayout:
+    lay = BundleLayout()
+    _check(lib.edge0_bundle_layout_of(C.byref(shape), C.byref(lay)), "edge0_bundle_layout_of")
+    return lay
+
+
+def edge0_workspace_bytes(shape: MoeShape) -> int:
+    n = lib.edge0_workspace_bytes(C.byref(shape))
+    if n == 0:
+        raise Edge0Error(EDGE0_EINVAL, "edge0_workspace_bytes")
+    return int(n)
+
+
+def new_workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace of edge0_workspace_bytes(shape) bytes."""
+    return torch.zeros(edge0_workspace_bytes(shape), dtype=torch.uint8, device=device)
+
+
+def edge0_workspace_error(workspace, stream=None) -> int:
+    return lib.edge0_workspace_error(_ptr(workspace), _stream(stream))
+
+
+def edge0_pack_bundle(shape: MoeShape, arrays: dict, bundle_dst, stream=None):
+    """arrays: name -> device tensor in the logical layout (see ExpertArrays)."""
+    src = ExpertArrays(**{k: _ptr(arrays.get(k)) for k in _LAYOUT_KEYS})
+    _check(lib.edge0_pack_bundle(C.byref(shape), C.byref(src), _ptr(bundle_dst), _stream(stream)),
+           "edge0_pack_bundle")
+
+
+def edge0_router(shape: MoeShape, w_router, x, logits_out, ids_out, w_out, workspace,
+                 stream=None):
+    _check(lib.edge0_router(C.byref(shape), _ptr(w_router), _ptr(x), _ptr(logits_out),
+                            _ptr(ids_out), _ptr(w_out), _ptr(workspace), _stream(stream)),
+           "edge0_router")
+
+
+def make_head(tensors: dict) -> Head:
+    return Head(**{k: _ptr(tensors.get(k)) for k in _HEAD_KEYS})
+
+
+def edge0_prerouter(shape: MoeShape, head: Head, x, ids_now, ids_prev, logits_out, ids_out, w_out,
+                    workspace, stream=None):
+    _check(lib.edge0_prerouter(C.byref(shape), C.byref(head), _ptr(x), _ptr(ids_now),
+                               _ptr(ids_prev), _ptr(logits_out), _ptr(ids_out), _ptr(w_out),
+                               _ptr(workspace), _stream(stream)), "edge0_prerouter")
+
+
+def edge0_moe_layer(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y, workspace,
+                    stream=None):
+    _check(lib.edge0_moe_layer(C.byref(shape), C.byref(pool), _ptr(slot_table), _ptr(ids), _ptr(w),
+                               _ptr(x), _ptr(y), _ptr(workspace), _stream(stream)),
+           "edge0_moe_layer")
+
+
+class Stack:
+    """Owner of an edge0_stack handle (decode stack runtime)."""
+
+    def __init__(self, shape: MoeShape, spec: StackSpec, pool: SlotPool, slot_tables, routers,
+                 heads):
+        self.shape, self.spec = shape, spec
+        self._keep = (slot_tables, routers, heads)
+        n = spec.n_layers
+        router_ptrs = (C.c_void_p * n)(*[_ptr(r) for r in routers])
+        head_arr = (Head * n)(*[make_head(h) if h is not None else Head() for h in heads])
+        self._handle = C.c_void_p()
+        _check(lib.edge0_stack_create(C.byref(self._handle), C.byref(shape), C.byref(spec),
+                                      C.byref(pool), _ptr(slot_tables), router_ptrs, head_arr),
+               "edge0_stack_create")
+
+    def step(self, h0, h_out, step: int, stream=None):
+        _check(lib.edge0_stack_step(self._handle, _ptr(h0), _ptr(h_out), step, _stream(stream)),
+               "edge0_stack_step")
+
+    def buffers(self) -> dict:
+        """Views of the handle's per-layer device buffers from the last step."""
+        b = StackBuffers()
+        _check(lib.edge0_stack_get_buffers(self._handle, C.byref(b)), "edge0_stack_get_buffers")
+        n, d, K = self.spec.n_layers, self.shape.d_model, self.shape.top_k
+        return {
+            "x": _wrap(b.x, (n, d), torch.int16), "y": _wrap(b.y, (n, d), torch.int16),
+            "h": _wrap(b.h, (n + 1, d), torch.int16), "ids": _wrap(b.ids, (n, K), torch.int32),
+            "w": _wrap(b.w, (n, K), torch.float32),
+            "pred_ids": _wrap(b.pred_ids, (n, K), torch.int32),
+            "pred_w": _wrap(b.pred_w, (n, K), torch.float32),
+        }
+
+    def close(self):
+        if self._handle:
+            lib.edge0_stack_destroy(self._handle)
+            self._handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_hip = C.CDLL("libamdhip64.so")
+_hip.hipMemcpy.restype = C.c_int
+_hip.hipMemcpy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int]
+
+
+def _wrap(ptr: int, shape, dtype) -> torch.Tensor:
+    """Copy a device buffer owned by the library into a new torch tensor."""
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=dtype, device="cuda")
+    torch.cuda.synchronize()
+    if _hip.hipMemcpy(out.data_ptr(), ptr, n * out.element_size(), 3) != 0:  # device to device
+        raise RuntimeError("hipMemcpy failed")
+    return out.view(*shape)

@@ -1,0 +1,77 @@
+"""Shared helpers for the GPU parity tests: a seeded layer uploaded to the
+device, and the comparison rules (rel-L2 on outputs, bit-exact ids with the
+near-tie waiver, rel 1e-5 on routing weights)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+from synth import gen as G
+
+REL_L2_MAX = 2e-3      # layer outputs, bf16 I/O with fp32 accumulation
+W_REL_MAX = 1e-5       # routing weights
+TIE_GAP = 1e-4         # ids are compared bit-exactly unless a gap is below this
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+def check_routing(gpu_ids, gpu_w, logits, k):
+    """Compare a GPU top-K against the oracle's on the oracle's logits.
+    Returns "exact" or "waived" (near tie at the K-th place); raises on a
+    mismatch.  Within the set, order may differ only between logits closer
+    than TIE_GAP; weights are compared per id."""
+    gpu_ids = np.asarray(gpu_ids)
+    ids, w = O.softmax_topk(logits, k)
+    if O.topk_gap(logits, k) < TIE_GAP:
+        return "waived"
+    assert sorted(gpu_ids.tolist()) == sorted(ids.tolist()), (gpu_ids, ids)
+    for a, b in zip(gpu_ids, ids):
+        if a != b:
+            assert abs(logits[a] - logits[b]) < TIE_GAP, (gpu_ids, ids)
+    want = dict(zip(ids.tolist(), w.tolist()))
+    for e, wv in zip(gpu_ids.tolist(), np.asarray(gpu_w, dtype=np.float64).tolist()):
+        assert abs(wv - want[e]) <= W_REL_MAX * abs(want[e]), (e, wv, want[e])
+    return "exact"
+
+
+class DeviceLayer:
+    """One seeded MoE layer (all E experts in slots 0..E-1 of a pool, or
+    permuted), its router and head, on the GPU."""
+
+    def __init__(self, S, seed=0, layer=0, slot_perm=None, lora=True):
+        import torch
+        from int4_expert_streaming_amd import edge0 as E
+        from int4_expert_streaming_amd.weights import SlotPoolBuffer, to_device, head_to_device
+        self.S = S
+        self.E = E
+        self.sh = E.make_shape(S)
+        if not lora:
+            self.sh.lora_rank = 0
+        self.experts = {e: G.expert_tensors(S, seed, layer, e) for e in range(S.n_experts)}
+        self.loras = ({e: G.lora_tensors(S, seed, layer, e) for e in range(S.n_experts)}
+                      if lora else None)
+        perm = np.arange(S.n_experts) if slot_perm is None else np.asarray(slot_perm)
+        self.pool = SlotPoolBuffer(self.sh, S.n_experts)
+        for e in range(S.n_experts):
+            self.pool.load(int(perm[e]), self.experts[e], None if not lora else self.loras[e])
+        self.table = torch.tensor(perm, dtype=torch.int32, device="cuda")
+        self.wr = G.router_weight(S, seed, layer)
+        self.wr_d = to_device(self.wr)
+        self.head = G.head_tensors(S, seed, layer)
+        self.head_d = head_to_device(self.head)
+        self.ws = E.new_workspace(self.sh)
+        self.scale = S.lora_alpha / S.lora_rank if lora else 0.0
+
+    def new_routing(self):
+        import torch
+        K = self.S.top_k
+        return (torch.zeros(K, dtype=torch.int32, device="cuda"),
+                torch.zeros(K, dtype=torch.float32, device="cuda"))
+
+    def oracle_y(self, ids, w, x_bits):
+        return O.moe_layer(self.experts, np.asarray(ids), np.asarray(w, dtype=np.float64), x_bits,
+                           self.S.group, self.loras, self.scale)

@@ -1,0 +1,84 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/*.h declares, reports the documented layouts, and rejects bad
+arguments before touching the device."""
+import ctypes as C
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(edge0_\w+)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith("typedef"):
+                names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def E():
+    from int4_expert_streaming_amd import edge0
+    return edge0
+
+
+def test_exports_every_declared_symbol(E):
+    names = _declared()
+    assert len(names) >= 12, names
+    missing = [n for n in sorted(names) if not hasattr(E.lib, n)]
+    assert not missing, missing
+
+
+def test_bundle_layouts(E):
+    from synth import gen as G
+    for S, base, lora in ((G.TINY, 61_440, 18_432), (G.QWEN3_MOE, 2_654_208, 270_336)):
+        lay = E.edge0_bundle_layout_of(E.make_shape(S))
+        assert lay.bytes == base + lora
+        assert lay.a_gate == base                     # adapter follows the nine int4 arrays
+        offs = [getattr(lay, k) for k in ("gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b",
+                                           "down_q", "down_s", "down_b")]
+        assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+        no_lora = E.make_shape(S)
+        no_lora.lora_rank = 0
+        lay0 = E.edge0_bundle_layout_of(no_lora)
+        assert lay0.bytes == base and lay0.a_gate == -1
+
+
+def test_bad_shapes_rejected(E):
+    from synth import gen as G
+    bad = []
+    for field, val in (("d_model", 100), ("d_inter", 96), ("group_size", 48), ("top_k", 0),
+                       ("top_k", 17), ("n_experts", 2000), ("lora_rank", 65), ("head_hidden", 30)):
+        s = E.make_shape(G.TINY)
+        setattr(s, field, val)
+        bad.append(s)
+    for s in bad:
+        with pytest.raises(E.Edge0Error) as ei:
+            E.edge0_bundle_layout_of(s)
+        assert ei.value.code == E.EDGE0_EINVAL
+        assert E.lib.edge0_workspace_bytes(C.byref(s)) == 0
+
+
+def test_null_arguments_rejected_before_launch(E):
+    from synth import gen as G
+    s = E.make_shape(G.TINY)
+    assert E.lib.edge0_router(C.byref(s), None, None, None, None, None, None, None) == E.EDGE0_EINVAL
+    assert E.lib.edge0_moe_layer(C.byref(s), None, None, None, None, None, None, None,
+                                 None) == E.EDGE0_EINVAL
+    pool = E.SlotPool(4096, 1000, 4)     # slot_bytes smaller than a bundle
+    assert E.lib.edge0_moe_layer(C.byref(s), C.byref(pool), 1, 1, 1, 1, 2, 1,
+                                 None) == E.EDGE0_EINVAL
+    assert E.strerror(E.EDGE0_ERANGE).startswith("expert id")
+
+
+def test_workspace_sizes(E):
+    from synth import gen as G
+    for S in (G.TINY, G.QWEN3_MOE, G.QWEN3_MOE.with_k(8)):
+        n = E.edge0_workspace_bytes(E.make_shape(S))
+        assert 0 < n < 8 << 20
