@@ -1,0 +1,178 @@
+"""Decode throughput of the 40-layer streaming-MoE stack on one MI355X.
+
+One step = one decode token through 40 Qwen3-MoE-shaped layers (hidden 2048,
+128 experts, inter 768, K = 4, int4 group 64, per-expert LoRA r=16 a=32,
+prerouter heads at layers 6..37, prediction-routed layers 7..38), all expert
+bundles resident in HBM, a fresh seeded hidden state per step.  Prints one
+JSON line (see the keys below).
+
+  python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+N_LAYERS, OWNERS, CONSUMERS = 40, (6, 37), (7, 38)
+
+
+def step_bytes(S, n_routers):
+    """Algorithmic HBM bytes of one decode step (every weight byte the step
+    must read once): K bundles + adapters per layer, 32 heads (fc1 hidden
+    columns, the 2K gathered one-hot rows, fc2, residual, biases) and the
+    plain routers that run."""
+    d, E, I, K, g, r, H = (S.d_model, S.n_experts, S.d_inter, S.top_k, S.group, S.lora_rank,
+                           S.head_hidden)
+    bundle = 3 * I * d // 2 + 3 * (I * d // g) * 2 * 2
+    lora = 2 * (r * d + I * r) * 2 + (r * I + d * r) * 2
+    head = H * d * 2 + 2 * K * H * 2 + E * H * 2 + E * d * 2 + H * 2 + E * 2
+    router = E * d * 2
+    n_heads = OWNERS[1] - OWNERS[0] + 1
+    return N_LAYERS * K * (bundle + lora) + n_heads * head + n_routers * router
+
+
+def gate_up_bytes(S):
+    """Algorithmic bytes of one gate/up launch: the K experts' gate and up
+    int4 rows with scales and biases, their LoRA B factors, the LoRA-down A
+    factor it applies to h, x once, and the activations it writes."""
+    d, I, K, g, r = S.d_model, S.d_inter, S.top_k, S.group, S.lora_rank
+    w = K * 2 * (I * d // 2 + 2 * I * (d // g) * 2)
+    lora = K * (2 * I * r * 2 + r * I * 2)
+    act = d * 2 + K * I * (4 + 2 + 2) + K * (I // 16) * (1 + r) * 4
+    return w + lora + act
+
+
+def cpu_baseline(S, seed, budget_s=15.0):
+    """The oracle timed on this host on a bounded sample: for a few layers of
+    the same stack, plain router + top-K, the MoE layer over K experts and
+    the prerouter head, extrapolated to one 40-layer step (32 heads, 8
+    routers)."""
+    import oracle as O
+    from synth import gen as G
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t_moe, t_head, t_router, n = [], [], [], 0
+    t_start = time.time()
+    scale = S.lora_alpha / S.lora_rank
+    for L in range(OWNERS[0], OWNERS[1] + 1):
+        x = G.stack_hidden(S, seed, 10_000 + L)
+        wr = G.router_weight(S, seed, L)
+        head = G.head_tensors(S, seed, L)
+        t0 = time.perf_counter()
+        logits = O.router_logits(wr, x)
+        ids, w = O.softmax_topk(logits, S.top_k)
+        t_router.append(time.perf_counter() - t0)
+        ex = {int(e): G.expert_tensors(S, seed, L, int(e)) for e in ids}
+        lo = {int(e): G.lora_tensors(S, seed, L, int(e)) for e in ids}
+        t0 = time.perf_counter()
+        O.moe_layer(ex, ids, w, x, S.group, lo, scale)
+        t_moe.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        O.prerouter_commit(head, x, ids, None, S.n_experts, S.top_k)
+        t_head.append(time.perf_counter() - t0)
+        n += 1
+        if time.time() - t_start > budget_s:
+            break
+    step_s = N_LAYERS * np.mean(t_moe) + 32 * np.mean(t_head) + 8 * np.mean(t_router)
+    return {"value": round(1.0 / step_s, 4), "unit": "tok/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} stack layers (router+top-K, MoE K={S.top_k}, head) timed, "
+                      f"extrapolated to a 40-layer step; {step_s:.2f} s/step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    from int4_expert_streaming_amd.weights import to_device
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    S = G.QWEN3_MOE
+    torch.cuda.set_device(0)
+    ds = DeviceStack(S, G.StackGen(S, args.seed), N_LAYERS, OWNERS, CONSUMERS, log=log)
+    total = args.warmup + args.steps
+    h0 = to_device(np.stack([G.stack_hidden(S, args.seed, t) for t in range(total)]))
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for t in range(args.warmup):
+        ds.step(h0[t], h_out, t)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for t in range(args.warmup, total):
+        ds.step(h0[t], h_out, t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # dominant kernel: HIP event pairs around each layer's gate/up launch, on
+    # the launching stream, over further steps of the same stack
+    ds.stack.set_timing(1)
+    gate_up_ms = []
+    for t in range(total, total + 8):
+        ds.step(h0[t % total], h_out, t)
+        gate_up_ms += ds.stack.kernel_ms()
+    ds.stack.set_timing(0)
+    tok_s = 1000.0 / ms_step
+    sbytes = step_bytes(S, n_routers=8)
+    step_gbps = sbytes * tok_s / 1e9
+    gu_bytes = gate_up_bytes(S)
+    gu_ms = float(np.mean(gate_up_ms))
+    gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
+    log(f"[bench] {ms_step * 1000:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
+        f"{step_gbps:.0f} GB/s step, gate/up {gu_ms * 1000:.2f} us = {gu_gbps:.0f} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "40-layer Qwen3-MoE-shaped decode stack, all experts resident",
+                   "d_model": S.d_model, "n_experts": S.n_experts, "d_inter": S.d_inter,
+                   "top_k": S.top_k, "group": S.group, "lora_rank": S.lora_rank,
+                   "head_hidden": S.head_hidden, "layers": N_LAYERS, "heads": "6-37",
+                   "prediction_routed": "7-38", "global_batch": 1, "parallelism": "none"},
+        "step_bytes": sbytes, "step_gbps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "k_gate_up (int4 gate/up GEMV + LoRA + SwiGLU)", "bound": "hbm",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1000, 3)},
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(S, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -65,7 +65,8 @@ const char* edge0_strerror(int code);
  * Supported values: d_model % 64 == 0 and d_model / 32 in {8, 16, 32} or a
  * multiple of 64; d_inter % 64 == 0; group_size % 32 == 0 dividing both
  * d_model and d_inter; 1 <= top_k <= min(16, n_experts); n_experts <= 1024;
- * 0 <= lora_rank <= 64; head_hidden % 64 == 0 (or 0 when no head is used).
+ * lora_rank in {0, 8, 16, 32, 64}; head_hidden % 64 == 0 (or 0 when no head
+ * is used).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t d_model;      /* d: hidden size */
@@ -259,6 +260,15 @@ typedef struct {
 } edge0_stack_buffers;
 int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffers* out);
 void edge0_stack_destroy(edge0_stack* st);
+
+/* Measurement aid: while kernel != 0, edge0_stack_step enqueues the step's
+ * launches directly instead of replaying its graph, with a HIP event pair
+ * around one launch class in every layer (kernel: 1 the gate/up GEMV, 2 the
+ * down GEMV + combine, 3 the LoRA-in GEMV; 0 turns it off).  After a step,
+ * edge0_stack_kernel_ms writes that launch's duration in ms for each layer
+ * (up to cap values) and the count to *n. */
+int edge0_stack_set_timing(edge0_stack* st, int32_t kernel);
+int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n);
 
 #ifdef __cplusplus
 }

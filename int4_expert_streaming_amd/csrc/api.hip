@@ -15,7 +15,8 @@ bool shape_ok(const edge0_moe_shape* s) {
     return false;
   if (g < 32 || g % 32 != 0 || d % g != 0 || I % g != 0) return false;
   if (E < 1 || E > 1024 || K < 1 || K > 16 || K > E) return false;
-  if (s->lora_rank < 0 || s->lora_rank > 64) return false;
+  const int r = s->lora_rank;
+  if (!(r == 0 || r == 8 || r == 16 || r == 32 || r == 64)) return false;
   if (s->lora_rank > 0 && !(s->lora_alpha == s->lora_alpha)) return false;
   if (s->head_hidden < 0 || s->head_hidden % 64 != 0) return false;
   return true;
@@ -76,6 +77,9 @@ WsLayout ws_layout(const edge0_moe_shape* s) {
   L.hp_lo = take(2 * K * I);
   L.hs = take(4 * K * (I / 16));
   L.tdpart = take(4 * K * (I / 16) * r);
+  L.td = take(4 * K * r);
+  L.cnt_td = take(4 * K);
+  L.head_logits = take(4 * E);
   L.dpart = take(4 * (d / 64) * K * (I / 32) * 64);
   L.total = off;
   return L;

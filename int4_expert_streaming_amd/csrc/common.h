@@ -66,17 +66,41 @@ __device__ __forceinline__ float chunk_dot128(uint4 q, const uint32_t* xp) {
 }
 
 // -------------------------------------------------------------- reductions
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// DPP data movement within a wave (no LDS crossbar): quad permutes, row
+// mirrors and the row broadcasts of GFX9.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
+// sum over each aligned group of 16 lanes, every lane of the group gets it
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(0.f, v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(0.f, v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(0.f, v);  // row_half_mirror
+  v += dpp_f<0x140>(0.f, v);  // row_mirror
   return v;
 }
-// sums over aligned segments of `seg` lanes (power of two); every lane of a
+// full-wave sum, the same value in every lane (fixed order)
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += dpp_f<0x142, 0xa>(0.f, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xc>(0.f, v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// sums over aligned segments of SEG lanes (8, 16 or 32); every lane of a
 // segment gets the segment's sum
 template <int SEG>
 __device__ __forceinline__ float seg_sum(float v) {
-#pragma unroll
-  for (int o = SEG / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v += dpp_f<0xB1>(0.f, v);
+  v += dpp_f<0x4E>(0.f, v);
+  v += dpp_f<0x141>(0.f, v);
+  if constexpr (SEG >= 16) v += dpp_f<0x140>(0.f, v);
+  if constexpr (SEG >= 32) {
+    v += dpp_f<0x142, 0xa>(0.f, v);                    // lanes 31 and 63 hold the sums
+    v = __shfl(v, (int)(threadIdx.x & 63) | 31, kWave);
+  }
   return v;
 }
 
@@ -124,29 +148,101 @@ __device__ __forceinline__ float row_dot(const uint16_t* __restrict__ w, const v
   return wave_sum(acc);
 }
 
+// Two-phase row dot for rows of up to 64*kPrefChunks*8 elements: the row's
+// 16-byte chunks are loaded into registers first (so the loads are in flight
+// while the caller prepares the vector), then dotted with a bf16 vector.
+constexpr int kPrefChunks = 8;  // n <= 4096
+struct RowPref {
+  uint4 c[kPrefChunks];
+};
+__device__ __forceinline__ void row_prefetch(const uint16_t* __restrict__ w, int n, RowPref& p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nc = n >> 3;
+#pragma unroll
+  for (int m = 0; m < kPrefChunks; ++m) {
+    const int c = lane + kWave * m;
+    if (c < nc) p.c[m] = *reinterpret_cast<const uint4*>(w + 8 * c);
+  }
+}
+// bf16 row (prefetched) . bf16 vector v (global or LDS)
+__device__ __forceinline__ float row_dot_pref(const RowPref& p, const uint16_t* v, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nc = n >> 3;
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < kPrefChunks; ++m) {
+    const int c = lane + kWave * m;
+    if (c < nc) {
+      const uint4 xq = *reinterpret_cast<const uint4*>(v + 8 * c);
+      const uint32_t ww[4] = {p.c[m].x, p.c[m].y, p.c[m].z, p.c[m].w};
+      const uint32_t xx[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(bf_lo(ww[q]), bf_lo(xx[q]), acc);
+        acc = fmaf(bf_hi(ww[q]), bf_hi(xx[q]), acc);
+      }
+    }
+  }
+  return wave_sum(acc);
+}
+
 // Top-K of logits[0..E) by one wave, ranked by (value descending, index
 // ascending); NaN ranks as -inf.  Weights: w_k = exp(l_k - l_max) / sum over
 // the selected.  Lane 0 writes ids_out[K], w_out[K].  E <= 1024, K <= 16.
 __device__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out, float* w_out);
 
-// Completion counting across workgroups: every thread fences its global
-// stores, then one atomic per workgroup.  Returns true (in every thread) in
-// the workgroup whose arrival makes the count reach `target`; that workgroup
-// then sees all stores the others made before arriving.  The caller resets
-// the counter to zero when done.
+// Device-coherent stores and loads for data handed between workgroups of one
+// kernel: agent-scope atomic accesses are performed at the device coherence
+// point (across all XCDs), so no cache-wide write-back or invalidate is
+// needed to publish or observe them.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Completion counting across workgroups.  Data that the last workgroup will
+// read must have been written with st_dev.  Every wave waits for its stores
+// to complete, the workgroup synchronises, and one atomic per workgroup
+// counts the arrival.  Returns true (in every thread) in the workgroup whose
+// arrival makes the count reach `target`; it then reads the others' data with
+// ld_dev.  The caller resets the counter to zero when done.
 __device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t target) {
   __shared__ int s_last;
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(counter, 1u);
+    const uint32_t old =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == target - 1);
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
 }
+
+// x = bf16(h / sqrt(mean(h^2) + eps)) into LDS by one workgroup (fixed
+// summation order, so every workgroup computes the same x)
+__device__ __forceinline__ void rmsnorm_to_lds(const uint16_t* __restrict__ h, uint16_t* xs, int d,
+                                               float eps) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    const float v = bf2f(h[j]);
+    s = fmaf(v, v, s);
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float inv = 1.f / sqrtf(red[0] / (float)d + eps);
+  for (int j = threadIdx.x; j < d; j += blockDim.x) xs[j] = (uint16_t)f2bf(bf2f(h[j]) * inv);
+  __syncthreads();
+}
+
+constexpr int kMaxD = 8192;
 
 // ---------------------------------------------------------- error word
 __device__ __forceinline__ void set_error(uint32_t* err, int code) {
@@ -162,6 +258,8 @@ struct WsLayout {
   size_t hp_hi, hp_lo;                            // u16 [K][I]
   size_t hs;                                      // fp32 [K][I/16]
   size_t tdpart;                                  // fp32 [K][I/16][r]
+  size_t td, cnt_td;                              // fp32 [K][r], u32 [K]
+  size_t head_logits;                             // fp32 [E]
   size_t dpart;                                   // fp32 [d/64][K][I/32][64]
   size_t total;
 };

@@ -39,20 +39,35 @@ __device__ __forceinline__ const uint8_t* slot_of(const MoeArgs& a, int k) {
 }
 
 // -------------------------------------------------------------- k_lora_in
+// t[k][p][rr] = A_p(e_k)[rr] . x.  With h_norm set, every workgroup first
+// computes x = bf16(RMSNorm(h_norm)) into LDS and workgroup 0 stores it.
 __global__ __launch_bounds__(256) void k_lora_in(MoeArgs a) {
+  __shared__ uint16_t xs[kMaxD];
   const int wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
   const int nrows = a.K * 2 * a.r;
-  if (row >= nrows) return;
-  const int k = row / (2 * a.r);
-  const int p = (row / a.r) & 1;
-  const int rr = row % a.r;
-  const uint8_t* b = slot_of(a, k);
+  const bool active = row < nrows;
+  const int k = active ? row / (2 * a.r) : 0;
+  const int p = active ? (row / a.r) & 1 : 0;
+  const int rr = active ? row % a.r : 0;
+  const uint8_t* b = active ? slot_of(a, k) : nullptr;
+  const uint16_t* A = nullptr;
+  if (b != nullptr)
+    A = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.a_up : a.lay.a_gate)) + (size_t)rr * a.d;
+  RowPref pf;
+  const bool pref = A != nullptr && a.d <= 64 * kPrefChunks * 8;
+  if (pref) row_prefetch(A, a.d, pf);          // in flight during the norm
+  const uint16_t* x = a.x;
+  if (a.h_norm != nullptr) {
+    rmsnorm_to_lds(a.h_norm, xs, a.d, a.eps);
+    if (blockIdx.x == 0)
+      for (int j = threadIdx.x; j < a.d; j += blockDim.x) a.x_out[j] = xs[j];
+    x = xs;
+  }
+  if (!active) return;
   float t = 0.f;
-  if (b != nullptr) {
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.a_up : a.lay.a_gate)) +
-                        (size_t)rr * a.d;
-    t = row_dot<false, false>(A, a.x, a.d);
+  if (A != nullptr) {
+    t = pref ? row_dot_pref(pf, x, a.d) : row_dot<false, false>(A, x, a.d);
   } else if ((threadIdx.x & 63) == 0) {
     set_error(a.err, EDGE0_ERANGE);
   }
@@ -60,18 +75,24 @@ __global__ __launch_bounds__(256) void k_lora_in(MoeArgs a) {
 }
 
 // -------------------------------------------------------------- k_gate_up
-// Activation chunk `col` (32 bf16 of x) as the 16 pairs chunk_dot128 expects,
-// and its fp32 sum.
-__device__ __forceinline__ float load_x_pairs(const uint16_t* __restrict__ x, int col,
-                                              uint32_t xp[16]) {
+// Activation chunk `col` (32 bf16 of x): raw load, then the 16 pairs
+// chunk_dot128 expects and its fp32 sum.
+struct XRaw {
+  uint4 v[4];
+};
+__device__ __forceinline__ void load_x_raw(const uint16_t* __restrict__ x, int col, XRaw& r) {
   const uint4* src = reinterpret_cast<const uint4*>(x + 32 * col);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) r.v[m] = src[m];
+}
+__device__ __forceinline__ float x_pairs(const XRaw& r, uint32_t xp[16]) {
+  const uint4* v = r.v;
   float sum = 0.f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const uint4 v = src[m];
-    pair_perm8(v.x, v.y, v.z, v.w, xp + 4 * m);
-    sum += bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) +
-           bf_lo(v.w) + bf_hi(v.w);
+    pair_perm8(v[m].x, v[m].y, v[m].z, v[m].w, xp + 4 * m);
+    sum += bf_lo(v[m].x) + bf_hi(v[m].x) + bf_lo(v[m].y) + bf_hi(v[m].y) + bf_lo(v[m].z) +
+           bf_hi(v[m].z) + bf_lo(v[m].w) + bf_hi(v[m].w);
   }
   return sum;
 }
@@ -84,7 +105,8 @@ __device__ __forceinline__ int pair_pos(int i) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.f + expf(-z)); }
 
-// store one row of h: fp32, the bf16 hi/lo split (hi = bf16(h), lo = bf16(h - hi))
+// store one row of h: fp32, the bf16 hi/lo split (hi = bf16(h), lo = bf16(h - hi));
+// returns hi + lo, the value the down GEMV sees
 __device__ __forceinline__ float store_h(const MoeArgs& a, int k, int i, float h) {
   const uint32_t hi = f2bf(h);
   const uint32_t lo = f2bf(h - bf2f(hi));
@@ -96,28 +118,29 @@ __device__ __forceinline__ float store_h(const MoeArgs& a, int k, int i, float h
 }
 
 // Wide rows: d/32 = 64*NJ chunks per row; lane l owns chunks l + 64 j of both
-// the gate and the up row; one row pair per step, 4 steps per wave.
+// the gate and the up row; 4 row pairs per wave.  Every global load of the
+// wave (weights, scales, biases, LoRA B rows and t) is issued before any math.
 template <int NJ>
 __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b, int k, int i0,
                                              float* h_s, float* hrep_s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int d = a.d, g = a.g, ng = d / g;
-  uint32_t xp[NJ][16];
-  float X[NJ];
+  const int d = a.d, g = a.g, ng = d / g, r = a.r;
+  constexpr int R = 4;
+  const int row0 = i0 + 4 * wave;
+  XRaw xr[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) X[j] = load_x_pairs(a.x, lane + 64 * j, xp[j]);
+  for (int j = 0; j < NJ; ++j) load_x_raw(a.x, lane + 64 * j, xr[j]);
   const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q);
   const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s);
   const uint16_t* gb = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b);
   const uint16_t* us = reinterpret_cast<const uint16_t*>(b + a.lay.up_s);
   const uint16_t* ub = reinterpret_cast<const uint16_t*>(b + a.lay.up_b);
-  constexpr int R = 4;
   uint4 qg[R][NJ], qu[R][NJ];
   uint32_t sg[R][NJ], bg[R][NJ], su[R][NJ], bu[R][NJ];
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
-    const int row = i0 + 4 * wave + ii;
+    const int row = row0 + ii;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = lane + 64 * j;
@@ -130,9 +153,27 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
       bu[ii][j] = ub[row * ng + grp];
     }
   }
+  // LoRA: lane rr < r holds B[row][rr] for the 4 rows and t[rr] (r <= 64)
+  uint32_t Bg[R], Bu[R];
+  float tg = 0.f, tu = 0.f;
+  const bool has_l = r > 0 && lane < r;
+  if (has_l) {
+    const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
+    const uint16_t* Bup = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii) {
+      Bg[ii] = Bgp[(size_t)(row0 + ii) * r + lane];
+      Bu[ii] = Bup[(size_t)(row0 + ii) * r + lane];
+    }
+    tg = a.t_in[(size_t)(k * 2 + 0) * r + lane];
+    tu = a.t_in[(size_t)(k * 2 + 1) * r + lane];
+  }
+  uint32_t xp[NJ][16];
+  float X[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
-    const int row = i0 + 4 * wave + ii;
     float G = 0.f, U = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -141,25 +182,16 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
       G += s1 * chunk_dot128(qg[ii][j], xp[j]) + (b1 - 128.f * s1) * X[j];
       U += s2 * chunk_dot128(qu[ii][j], xp[j]) + (b2 - 128.f * s2) * X[j];
     }
-    if (a.r > 0) {
-      const uint16_t* Bg = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate) + (size_t)row * a.r;
-      const uint16_t* Bu = reinterpret_cast<const uint16_t*>(b + a.lay.b_up) + (size_t)row * a.r;
-      const float* tg = a.t_in + (size_t)(k * 2 + 0) * a.r;
-      const float* tu = a.t_in + (size_t)(k * 2 + 1) * a.r;
-      float dg = 0.f, du = 0.f;
-      for (int rr = lane; rr < a.r; rr += 64) {
-        dg += bf2f(Bg[rr]) * tg[rr];
-        du += bf2f(Bu[rr]) * tu[rr];
-      }
-      G += a.scale * dg;
-      U += a.scale * du;
+    if (has_l) {
+      G += a.scale * (bf2f(Bg[ii]) * tg);
+      U += a.scale * (bf2f(Bu[ii]) * tu);
     }
     G = wave_sum(G);
     U = wave_sum(U);
     const float h = silu_f(G) * U;
     if (lane == 0) {
       h_s[4 * wave + ii] = h;
-      hrep_s[4 * wave + ii] = store_h(a, k, row, h);
+      hrep_s[4 * wave + ii] = store_h(a, k, row0 + ii, h);
     }
   }
 }
@@ -171,18 +203,21 @@ __device__ __forceinline__ void gate_up_narrow(const MoeArgs& a, const uint8_t* 
                                                float* h_s, float* hrep_s) {
   constexpr int R = 32 / CPR;
   constexpr int STEPS = 4 / R;
+  constexpr int LPR = (64 + CPR - 1) / CPR;  // LoRA terms per lane, r <= 64
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rloc = lane / (2 * CPR);
   const int p = (lane / CPR) & 1;
   const int col = lane % CPR;
-  const int d = a.d, g = a.g, ng = d / g;
-  uint32_t xp[16];
-  const float X = load_x_pairs(a.x, col, xp);
+  const int d = a.d, g = a.g, ng = d / g, r = a.r;
+  XRaw xr;
+  load_x_raw(a.x, col, xr);
   const uint32_t* q = reinterpret_cast<const uint32_t*>(b + (p ? a.lay.up_q : a.lay.gate_q));
   const uint16_t* sp = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.up_s : a.lay.gate_s));
   const uint16_t* bp = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.up_b : a.lay.gate_b));
   uint4 qq[STEPS];
   uint32_t ss[STEPS], bb[STEPS];
+  uint32_t Bl[STEPS][LPR];
+  float tl[LPR];
   const int grp = (32 * col) / g;
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
@@ -191,17 +226,31 @@ __device__ __forceinline__ void gate_up_narrow(const MoeArgs& a, const uint8_t* 
     ss[st] = sp[row * ng + grp];
     bb[st] = bp[row * ng + grp];
   }
+  if (r > 0) {
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate));
+    const float* t = a.t_in + (size_t)(k * 2 + p) * r;
+#pragma unroll
+    for (int m = 0; m < LPR; ++m) {
+      const int rr = col + m * CPR;
+      tl[m] = rr < r ? t[rr] : 0.f;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        const int row = i0 + 4 * wave + st * R + rloc;
+        Bl[st][m] = rr < r ? B[(size_t)row * r + rr] : 0u;
+      }
+    }
+  }
+  uint32_t xp[16];
+  const float X = x_pairs(xr, xp);
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int row = i0 + 4 * wave + st * R + rloc;
     const float s = bf2f(ss[st]), bv = bf2f(bb[st]);
     float v = s * chunk_dot128(qq[st], xp) + (bv - 128.f * s) * X;
-    if (a.r > 0) {
-      const uint16_t* B =
-          reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate)) + (size_t)row * a.r;
-      const float* t = a.t_in + (size_t)(k * 2 + p) * a.r;
+    if (r > 0) {
       float dl = 0.f;
-      for (int rr = col; rr < a.r; rr += CPR) dl += bf2f(B[rr]) * t[rr];
+#pragma unroll
+      for (int m = 0; m < LPR; ++m) dl += bf2f(Bl[st][m]) * tl[m];
       v += a.scale * dl;
     }
     v = seg_sum<CPR>(v);                       // G (p = 0) or U (p = 1) of this row
@@ -215,6 +264,8 @@ __device__ __forceinline__ void gate_up_narrow(const MoeArgs& a, const uint8_t* 
   }
 }
 
+// One workgroup = 16 consecutive rows of one expert's gate and up.  Also
+// writes the 16-row sum of h and the 16-row partial of A_down h.
 template <int CPR>
 __global__ __launch_bounds__(256) void k_gate_up(MoeArgs a) {
   __shared__ float h_s[16];
@@ -223,18 +274,25 @@ __global__ __launch_bounds__(256) void k_gate_up(MoeArgs a) {
   const int k = blockIdx.x / nblk;
   const int blk = blockIdx.x % nblk;
   const int i0 = blk * 16;
+  const int r = a.r;
   const uint8_t* b = slot_of(a, k);
   if (b == nullptr) {
     // unresolvable expert: zero activations, flag the error
-    for (int t = threadIdx.x; t < 16; t += blockDim.x) {
-      store_h(a, k, i0 + t, 0.f);
-    }
-    if (threadIdx.x < a.r) a.tdpart[((size_t)k * nblk + blk) * a.r + threadIdx.x] = 0.f;
+    for (int t = threadIdx.x; t < 16; t += blockDim.x) store_h(a, k, i0 + t, 0.f);
+    if ((int)threadIdx.x < r) a.tdpart[((size_t)k * nblk + blk) * r + threadIdx.x] = 0.f;
     if (threadIdx.x == 0) {
       a.hs[(size_t)k * nblk + blk] = 0.f;
       set_error(a.err, EDGE0_ERANGE);
     }
     return;
+  }
+  // A_down columns of these rows, loaded early (threads rr < r), used raw later
+  uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
+  if ((int)threadIdx.x < r) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)threadIdx.x * a.I + i0);
+    ad0 = src[0];
+    ad1 = src[1];
   }
   if constexpr (CPR >= 64) {
     gate_up_wide<CPR / 64>(a, b, k, i0, h_s, hrep_s);
@@ -247,21 +305,46 @@ __global__ __launch_bounds__(256) void k_gate_up(MoeArgs a) {
     for (int t = 0; t < 16; ++t) s += hrep_s[t];
     a.hs[(size_t)k * nblk + blk] = s;
   }
-  if (threadIdx.x < a.r) {
-    const int rr = threadIdx.x;
-    const uint16_t* Ad = reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)rr * a.I + i0;
+  if ((int)threadIdx.x < r) {
+    const uint32_t w[8] = {ad0.x, ad0.y, ad0.z, ad0.w, ad1.x, ad1.y, ad1.z, ad1.w};
     float s = 0.f;
-    for (int t = 0; t < 16; ++t) s += bf2f(Ad[t]) * h_s[t];
-    a.tdpart[((size_t)k * nblk + blk) * a.r + rr] = s;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s += bf_lo(w[m]) * h_s[2 * m] + bf_hi(w[m]) * h_s[2 * m + 1];
+    a.tdpart[((size_t)k * nblk + blk) * r + threadIdx.x] = s;
   }
 }
 
 // ------------------------------------------------------------------ k_down
+// Unit (rb, k, sl): rows 64 rb .. 64 rb + 63 of expert k's down projection
+// over input chunks of slice sl, times the routing weight w_k; the sl = 0
+// unit adds the LoRA-down delta.  The last unit of a row block sums the
+// K*S partials in a fixed order, rounds to bf16 and applies the residual.
+constexpr int kDownTiles = 4;  // tiles per wave per batch of loads
+
+constexpr int kMaxSliceChunks = 64;  // chunks per slice (cps) staged in LDS
+
+__device__ __forceinline__ void down_tile_loads(const uint4* dq, const uint16_t* ds,
+                                                const uint16_t* db, int rb, int NC, int d, int g,
+                                                int o, int lane, int base, int c1, uint4* q,
+                                                uint32_t* sv, uint32_t* bv) {
+#pragma unroll
+  for (int m = 0; m < kDownTiles; ++m) {
+    const int c = base + 4 * m;
+    if (c < c1) {
+      q[m] = dq[((size_t)rb * NC + c) * 64 + lane];
+      const int grp = (32 * c) / g;
+      sv[m] = ds[(size_t)grp * d + o];
+      bv[m] = db[(size_t)grp * d + o];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   __shared__ float red[4][64];
-  __shared__ float td[16 * 64];  // K * r <= 1024
+  __shared__ uint32_t hp_s[kMaxSliceChunks][32];  // hi pairs then lo pairs of each chunk
+  __shared__ float hsum_s[kMaxSliceChunks];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K = a.K, S = a.S, I = a.I, d = a.d;
+  const int K = a.K, S = a.S, I = a.I, d = a.d, r = a.r;
   const int NC = I / 32;
   const int u = blockIdx.x;
   const int rb = u / (K * S);
@@ -270,65 +353,117 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   const int cps = (NC + S - 1) / S;
   const int c0 = sl * cps;
   const int c1 = min(NC, c0 + cps);
-  const uint8_t* b = slot_of(a, k);
-  float part = 0.f;
+  const int o = rb * 64 + lane;
+  const uint8_t* b = slot_of(a, k);  // uniform over the workgroup
+  const float wk = a.w[k];
+  const uint4* dq = nullptr;
+  const uint16_t *ds = nullptr, *db = nullptr;
+  uint4 q[kDownTiles];
+  uint32_t sv[kDownTiles], bv[kDownTiles];
+  // LoRA-down delta for these rows (slice 0 only, wave 0): t_down = sum over
+  // the 16-row partials of A_down h, where element t = blk*r + rr of the
+  // partials goes to lane t % 64 (which always holds rr = lane % r, r
+  // dividing 64), and B_down row o (r bf16).  Loaded before the tiles.
+  const bool lora_here = b != nullptr && r > 0 && sl == 0 && wave == 0;
+  const int ntd = (I / 16) * r;
+  constexpr int kTd = 16;
+  float tdr[kTd];
+  uint4 bdr[8];
   if (b != nullptr) {
-    const uint4* dq = reinterpret_cast<const uint4*>(b + a.lay.down_q);
-    const uint16_t* ds = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
-    const uint16_t* db = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
+    dq = reinterpret_cast<const uint4*>(b + a.lay.down_q);
+    ds = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
+    db = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
+    if (lora_here) {
+      const float* tp = a.tdpart + (size_t)k * ntd;
+#pragma unroll
+      for (int m = 0; m < kTd; ++m) tdr[m] = (lane + 64 * m < ntd) ? tp[lane + 64 * m] : 0.f;
+      const uint4* Bdp = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(b + a.lay.b_down) + (size_t)o * r);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        if (8 * m < r) bdr[m] = Bdp[m];
+    }
+    // first batch of this wave's tiles: in flight while the slice's
+    // activation pairs and chunk sums are staged in LDS
+    down_tile_loads(dq, ds, db, rb, NC, d, a.g, o, lane, c0 + wave, c1, q, sv, bv);
     const uint32_t* hph = reinterpret_cast<const uint32_t*>(a.hp_hi + (size_t)k * I);
     const uint32_t* hpl = reinterpret_cast<const uint32_t*>(a.hp_lo + (size_t)k * I);
     const float* hs = a.hs + (size_t)k * (I / 16);
-    const int o = rb * 64 + lane;
-    for (int c = c0 + wave; c < c1; c += 4) {
-      const uint4 q = dq[((size_t)rb * NC + c) * 64 + lane];
-      const int grp = (32 * c) / a.g;
-      const float s = bf2f(ds[(size_t)grp * d + o]);
-      const float bv = bf2f(db[(size_t)grp * d + o]);
-      const float acc = chunk_dot128(q, hph + 16 * c) + chunk_dot128(q, hpl + 16 * c);
-      const float H = hs[2 * c] + hs[2 * c + 1];
-      part += s * acc + (bv - 128.f * s) * H;
+    const int ncs = c1 - c0;
+    for (int t = threadIdx.x; t < ncs * 32; t += blockDim.x) {
+      const int cc = t >> 5, j = t & 31;
+      hp_s[cc][j] = j < 16 ? hph[16 * (c0 + cc) + j] : hpl[16 * (c0 + cc) + j - 16];
     }
+    for (int t = threadIdx.x; t < ncs; t += blockDim.x)
+      hsum_s[t] = hs[2 * (c0 + t)] + hs[2 * (c0 + t) + 1];
   } else if (threadIdx.x == 0) {
     set_error(a.err, EDGE0_ERANGE);
+  }
+  __syncthreads();  // every thread, unconditionally
+  float part = 0.f;
+  if (b != nullptr) {
+    for (int base = c0 + wave; base < c1; base += 4 * kDownTiles) {
+      if (base != c0 + wave)
+        down_tile_loads(dq, ds, db, rb, NC, d, a.g, o, lane, base, c1, q, sv, bv);
+#pragma unroll
+      for (int m = 0; m < kDownTiles; ++m) {
+        const int c = base + 4 * m;
+        if (c < c1) {
+          const float s = bf2f(sv[m]), bb = bf2f(bv[m]);
+          const uint32_t* hp = hp_s[c - c0];
+          const float acc = chunk_dot128(q[m], hp) + chunk_dot128(q[m], hp + 16);
+          part += s * acc + (bb - 128.f * s) * hsum_s[c - c0];
+        }
+      }
+    }
+    if (lora_here) {
+      float tdv = 0.f;
+#pragma unroll
+      for (int m = 0; m < kTd; ++m) tdv += tdr[m];
+      for (int t = lane + 64 * kTd; t < ntd; t += 64) tdv += a.tdpart[(size_t)k * ntd + t];
+      for (int off = r; off < 64; off <<= 1) tdv += __shfl_xor(tdv, off, kWave);
+      float dl = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (8 * m < r) {
+          const uint32_t bw[4] = {bdr[m].x, bdr[m].y, bdr[m].z, bdr[m].w};
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            dl += bf_lo(bw[q2]) * __shfl(tdv, 8 * m + 2 * q2, kWave);
+            dl += bf_hi(bw[q2]) * __shfl(tdv, 8 * m + 2 * q2 + 1, kWave);
+          }
+        }
+      }
+      part += a.scale * dl;
+    }
   }
   red[wave][lane] = part;
   __syncthreads();
   if (wave == 0) {
-    const float t = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    const float t = (red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]) * wk;
     a.dpart[(((size_t)rb * K + k) * S + sl) * 64 + lane] = t;
   }
-  if (!last_arrival(a.cnt_down + rb, (uint32_t)(K * S))) return;
-  // fixup: this workgroup finishes rows rb*64 .. rb*64+63
-  const int r = a.r;
-  const int nblk = I / 16;
-  for (int t = threadIdx.x; t < K * r; t += blockDim.x) {
-    const int kk = t / r, rr = t % r;
-    float s = 0.f;
-    for (int blk = 0; blk < nblk; ++blk) s += a.tdpart[((size_t)kk * nblk + blk) * r + rr];
-    td[t] = s;
+}
+
+// y[o] = bf16(sum over experts k and slices s of the down partials, in that
+// fixed order); optional residual h_out = bf16(h_res + y)
+__global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= a.d) return;
+  const int rb = o / 64, lane = o % 64;
+  const float* p = a.dpart + (size_t)rb * a.K * a.S * 64 + lane;
+  const int n = a.K * a.S;
+  float yv = 0.f;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = (j0 + m < n) ? p[(size_t)(j0 + m) * 64] : 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) yv += v[m];
   }
-  __syncthreads();
-  if (wave == 0) {
-    const int o = rb * 64 + lane;
-    float yv = 0.f;
-    for (int kk = 0; kk < K; ++kk) {
-      float D = 0.f;
-      for (int s2 = 0; s2 < S; ++s2) D += a.dpart[(((size_t)rb * K + kk) * S + s2) * 64 + lane];
-      const uint8_t* bk = slot_of(a, kk);
-      if (r > 0 && bk != nullptr) {
-        const uint16_t* Bd = reinterpret_cast<const uint16_t*>(bk + a.lay.b_down) + (size_t)o * r;
-        float dl = 0.f;
-        for (int rr = 0; rr < r; ++rr) dl += bf2f(Bd[rr]) * td[kk * r + rr];
-        D += a.scale * dl;
-      }
-      yv += a.w[kk] * D;
-    }
-    const uint32_t yb = f2bf(yv);
-    a.y[o] = (uint16_t)yb;
-    if (a.h_out != nullptr) a.h_out[o] = (uint16_t)f2bf(bf2f(a.h_res[o]) + bf2f(yb));
-  }
-  if (threadIdx.x == 0) atomicExch(a.cnt_down + rb, 0u);
+  const uint32_t yb = f2bf(yv);
+  a.y[o] = (uint16_t)yb;
+  if (a.h_out != nullptr) a.h_out[o] = (uint16_t)f2bf(bf2f(a.h_res[o]) + bf2f(yb));
 }
 
 // ------------------------------------------------------------ bundle pack
@@ -379,6 +514,9 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->y = static_cast<uint16_t*>(y);
   a->h_res = nullptr;
   a->h_out = nullptr;
+  a->h_norm = nullptr;
+  a->x_out = nullptr;
+  a->eps = 0.f;
   a->d = sh->d_model;
   a->E = sh->n_experts;
   a->I = sh->d_inter;
@@ -395,21 +533,32 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
   a->hs = reinterpret_cast<float*>(ws + L.hs);
   a->tdpart = reinterpret_cast<float*>(ws + L.tdpart);
+  a->td = reinterpret_cast<float*>(ws + L.td);
+  a->cnt_td = reinterpret_cast<uint32_t*>(ws + L.cnt_td);
   a->dpart = reinterpret_cast<float*>(ws + L.dpart);
   const int RB = a->d / 64, NC = a->I / 32;
   int S = (512 + RB * a->K - 1) / (RB * a->K);
-  a->S = S < 1 ? 1 : (S > NC ? NC : S);
+  S = S < 1 ? 1 : (S > NC ? NC : S);
+  const int min_s = (NC + kMaxSliceChunks - 1) / kMaxSliceChunks;  // slice fits the LDS stage
+  a->S = S < min_s ? min_s : S;
   return EDGE0_OK;
 }
 
-int launch_moe(const MoeArgs& a, hipStream_t stream) {
-  if (a.r > 0) {
+int launch_moe(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
+  auto mark = [&](int which, bool start) {
+    if (timing && timing->which == which)
+      (void)hipEventRecord(start ? timing->start : timing->stop, stream);
+  };
+  if (a.r > 0 || a.h_norm != nullptr) {
     const int rows = a.K * 2 * a.r;
-    k_lora_in<<<(rows + 3) / 4, 256, 0, stream>>>(a);
+    mark(3, true);
+    k_lora_in<<<rows > 0 ? (rows + 3) / 4 : 1, 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
+    mark(3, false);
   }
   const int cpr = a.d / 32;
   const int grid2 = a.K * (a.I / 16);
+  mark(1, true);
   switch (cpr) {
     case 8: k_gate_up<8><<<grid2, 256, 0, stream>>>(a); break;
     case 16: k_gate_up<16><<<grid2, 256, 0, stream>>>(a); break;
@@ -421,8 +570,13 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
     default: return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();
+  mark(1, false);
   const int grid3 = (a.d / 64) * a.K * a.S;
+  mark(2, true);
   k_down<<<grid3, 256, 0, stream>>>(a);
+  E0_CHECK_LAUNCH();
+  mark(2, false);
+  k_combine<<<(a.d + 255) / 256, 256, 0, stream>>>(a);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }

@@ -13,8 +13,11 @@ struct MoeArgs {
   const int32_t* table;
   const int32_t* ids;
   const float* w;
-  const uint16_t* x;
+  const uint16_t* x;        // normalised input (bf16 [d])
   uint16_t* y;
+  const uint16_t* h_norm;   // optional: the first kernel computes x = bf16(RMSNorm(h_norm))
+  uint16_t* x_out;          //   and workgroup 0 stores it here (then x == x_out)
+  float eps;
   const uint16_t* h_res;  // optional residual input: h_out = bf16(h_res + y)
   uint16_t* h_out;
   int d, E, I, K, g, r;
@@ -28,6 +31,8 @@ struct MoeArgs {
   uint16_t* hp_lo;
   float* hs;
   float* tdpart;
+  float* td;                // A_down h, [K][r]
+  uint32_t* cnt_td;         // [K]
   float* dpart;
   int S;  // down slices
 };
@@ -35,6 +40,16 @@ struct MoeArgs {
 int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const int32_t* table,
                   const int32_t* ids, const float* w, const void* x, void* y, void* workspace,
                   MoeArgs* a);
-int launch_moe(const MoeArgs& a, hipStream_t stream);
+// Optional event pair recorded around one of the launches (measurement aid):
+// which = 1 the gate/up GEMV, 2 the down GEMV + combine, 3 the LoRA-in GEMV.
+struct LaunchTiming {
+  int which;
+  hipEvent_t start, stop;
+};
+int launch_moe(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+
+int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
+                  const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
+                  int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream);
 
 }  // namespace e0

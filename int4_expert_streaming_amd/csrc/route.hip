@@ -25,7 +25,7 @@ __device__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out, f
     const int idx = lane + kWave * j;
     float x = -INFINITY;
     if (j < nper && idx < E) {
-      x = __builtin_nontemporal_load(logits + idx);
+      x = ld_dev(logits + idx);
       if (x != x) x = -INFINITY;
     }
     v[j] = x;
@@ -71,20 +71,35 @@ __device__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out, f
 }
 
 // ---------------------------------------------------------------- router
+// With h_norm set, every workgroup computes x = bf16(RMSNorm(h_norm)) into LDS
+// and workgroup 0 stores it to x_out.
 __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ wr,
-                                                const uint16_t* __restrict__ x, int d, int E,
-                                                int K, float* __restrict__ logits,
+                                                const uint16_t* __restrict__ x_in,
+                                                const uint16_t* __restrict__ h_norm,
+                                                uint16_t* __restrict__ x_out, float eps, int d,
+                                                int E, int K, float* __restrict__ logits,
                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                 uint32_t* __restrict__ counter) {
+  __shared__ uint16_t xs[kMaxD];
   const int wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
+  RowPref pf;
+  const bool pref = row < E && d <= 64 * kPrefChunks * 8;
+  if (pref) row_prefetch(wr + (size_t)row * d, d, pf);   // in flight during the norm
+  const uint16_t* x = x_in;
+  if (h_norm != nullptr) {
+    rmsnorm_to_lds(h_norm, xs, d, eps);
+    if (blockIdx.x == 0)
+      for (int j = threadIdx.x; j < d; j += blockDim.x) x_out[j] = xs[j];
+    x = xs;
+  }
   if (row < E) {
-    const float s = row_dot<false, false>(wr + (size_t)row * d, x, d);
-    if ((threadIdx.x & 63) == 0) logits[row] = s;
+    const float s = pref ? row_dot_pref(pf, x, d) : row_dot<false, false>(wr + (size_t)row * d, x, d);
+    if ((threadIdx.x & 63) == 0) st_dev(logits + row, s);
   }
   if (last_arrival(counter, gridDim.x)) {
     if (wave == 0) wave_topk(logits, E, K, ids, w);
-    if (threadIdx.x == 0) atomicExch(counter, 0u);
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -142,11 +157,11 @@ __global__ __launch_bounds__(256) void k_head_fc2(
     float s = row_dot<true, true>(w2 + (size_t)row * H, a, H);
     if (b2 != nullptr) s += h2f(b2[row]);
     if (res != nullptr) s += res[row];
-    if ((threadIdx.x & 63) == 0) logits[row] = s;
+    if ((threadIdx.x & 63) == 0) st_dev(logits + row, s);
   }
   if (last_arrival(counter, gridDim.x)) {
     if (wave == 0) wave_topk(logits, E, K, ids, w);
-    if (threadIdx.x == 0) atomicExch(counter, 0u);
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -154,20 +169,30 @@ __global__ __launch_bounds__(256) void k_head_fc2(
 
 using namespace e0;
 
-extern "C" int edge0_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
-                            float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
-                            hipStream_t stream) {
-  if (!shape || !shape_ok(shape) || !w_router || !x || !ids_out || !w_out || !workspace)
-    return EDGE0_EINVAL;
+namespace e0 {
+int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
+                  const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
+                  int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream) {
   const WsLayout L = ws_layout(shape);
   char* ws = static_cast<char*>(workspace);
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.logits);
   const int E = shape->n_experts;
   k_router<<<(E + 3) / 4, 256, 0, stream>>>(
-      static_cast<const uint16_t*>(w_router), static_cast<const uint16_t*>(x), shape->d_model, E,
-      shape->top_k, logits, ids_out, w_out, reinterpret_cast<uint32_t*>(ws + L.cnt_router));
+      static_cast<const uint16_t*>(w_router), static_cast<const uint16_t*>(x), h_norm, x_out, eps,
+      shape->d_model, E, shape->top_k, logits, ids_out, w_out,
+      reinterpret_cast<uint32_t*>(ws + L.cnt_router));
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
+}
+}  // namespace e0
+
+extern "C" int edge0_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
+                            float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
+                            hipStream_t stream) {
+  if (!shape || !shape_ok(shape) || !w_router || !x || !ids_out || !w_out || !workspace)
+    return EDGE0_EINVAL;
+  return launch_router(shape, w_router, x, nullptr, nullptr, 0.f, logits_out, ids_out, w_out,
+                       workspace, stream);
 }
 
 extern "C" int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* head,
@@ -179,7 +204,7 @@ extern "C" int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* h
     return EDGE0_EINVAL;
   const WsLayout L = ws_layout(shape);
   char* ws = static_cast<char*>(workspace);
-  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.logits);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.head_logits);
   float* a = reinterpret_cast<float*>(ws + L.head_a);
   float* res = reinterpret_cast<float*>(ws + L.head_res);
   const int d = shape->d_model, E = shape->n_experts, K = shape->top_k, H = shape->head_hidden;

@@ -22,24 +22,6 @@
 
 namespace e0 {
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ h,
-                                                 uint16_t* __restrict__ x, int d, float eps) {
-  __shared__ float red[256];
-  float s = 0.f;
-  for (int j = threadIdx.x; j < d; j += 256) {
-    const float v = bf2f(h[j]);
-    s = fmaf(v, v, s);
-  }
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  const float inv = 1.f / sqrtf(red[0] / (float)d + eps);
-  for (int j = threadIdx.x; j < d; j += 256) x[j] = (uint16_t)f2bf(bf2f(h[j]) * inv);
-}
-
 // routing each layer executed at step s, gathered into one [L][K] array
 __global__ void k_gather_routing(const int32_t* __restrict__ exec_ids,
                                  const float* __restrict__ exec_w,
@@ -78,6 +60,12 @@ struct edge0_stack {
   size_t ws_bytes;
   int32_t last_step;
   hipStream_t cap;           // capture stream
+  hipStream_t cap_side;      // capture stream of the head branch
+  hipStream_t side;          // head branch stream for direct (timed) enqueue
+  std::vector<hipEvent_t> ev_fork;  // per layer: x and routing of the layer are ready
+  hipEvent_t ev_join;
+  int timed_kernel;          // measurement aid: which launch class carries events
+  std::vector<hipEvent_t> ev_start, ev_stop;  // one pair per layer
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
 };
 
@@ -88,15 +76,15 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
   return L >= s.owner_first && L <= s.owner_last;
 }
 
-// enqueue all launches of decode step `step` (h[0] already holds h0)
-static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
+// enqueue all launches of decode step `step` (h[0] already holds h0).  The
+// heads are off the step's critical path (their predictions are used at the
+// next step), so they run on a forked branch that joins at the end.
+static int enqueue_step(edge0_stack* st, int step, hipStream_t stream, hipStream_t side) {
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers, E = sh.n_experts;
   for (int L = 0; L < Lc; ++L) {
     uint16_t* hL = st->h + (size_t)L * d;
     uint16_t* xL = st->x + (size_t)L * d;
-    k_rmsnorm<<<1, 256, 0, stream>>>(hL, xL, d, st->spec.rms_eps);
-    E0_CHECK_LAUNCH();
     const bool by_pred = is_consumer(st->spec, L) && step > 0;
     int32_t* ids;
     float* w;
@@ -106,7 +94,9 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     } else {
       ids = st->exec_ids[step & 1] + (size_t)L * K;
       w = st->exec_w[step & 1] + (size_t)L * K;
-      const int rc = edge0_router(&sh, st->routers[L], xL, nullptr, ids, w, st->ws, stream);
+      // the router launch also computes x_L = bf16(RMSNorm(h_L))
+      const int rc = launch_router(&sh, st->routers[L], nullptr, hL, xL, st->spec.rms_eps, nullptr,
+                                   ids, w, st->ws, stream);
       if (rc != EDGE0_OK) return rc;
     }
     MoeArgs a;
@@ -115,9 +105,22 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     if (rc != EDGE0_OK) return rc;
     a.h_res = hL;
     a.h_out = st->h + (size_t)(L + 1) * d;
-    rc = launch_moe(a, stream);
+    if (by_pred) {  // the first MoE launch computes x_L
+      a.h_norm = hL;
+      a.x_out = xL;
+      a.eps = st->spec.rms_eps;
+    }
+    LaunchTiming lt{st->timed_kernel, nullptr, nullptr};
+    if (st->timed_kernel > 0) {
+      lt.start = st->ev_start[L];
+      lt.stop = st->ev_stop[L];
+    }
+    rc = launch_moe(a, stream, st->timed_kernel > 0 ? &lt : nullptr);
     if (rc != EDGE0_OK) return rc;
     if (is_owner(st->spec, L)) {
+      if (hipEventRecord(st->ev_fork[L], stream) != hipSuccess ||
+          hipStreamWaitEvent(side, st->ev_fork[L], 0) != hipSuccess)
+        return EDGE0_EHIP;
       const int32_t* prev = nullptr;
       if (step > 0) {
         const bool prev_pred = is_consumer(st->spec, L) && step - 1 > 0;
@@ -126,10 +129,14 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       }
       rc = edge0_prerouter(&sh, &st->heads[L], xL, ids, prev, nullptr,
                            st->pred_ids[(step + 1) % 3] + (size_t)(L + 1) * K,
-                           st->pred_w[(step + 1) % 3] + (size_t)(L + 1) * K, st->ws, stream);
+                           st->pred_w[(step + 1) % 3] + (size_t)(L + 1) * K, st->ws, side);
       if (rc != EDGE0_OK) return rc;
     }
   }
+  if (st->spec.owner_first <= st->spec.owner_last &&
+      (hipEventRecord(st->ev_join, side) != hipSuccess ||
+       hipStreamWaitEvent(stream, st->ev_join, 0) != hipSuccess))
+    return EDGE0_EHIP;
   k_gather_routing<<<1, 256, 0, stream>>>(st->exec_ids[step & 1], st->exec_w[step & 1],
                                           st->pred_ids[step % 3], st->pred_w[step % 3], Lc, K,
                                           st->spec.consumer_first, st->spec.consumer_last, step,
@@ -188,7 +195,15 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   for (int i = 0; i < 3 && ok; ++i)
     ok = hipMemset(st->pred_ids[i], 0, Lc * K * 4) == hipSuccess &&
          hipMemset(st->pred_w[i], 0, Lc * K * 4) == hipSuccess;
-  ok = ok && hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking) == hipSuccess &&
+       hipStreamCreateWithFlags(&st->cap_side, hipStreamNonBlocking) == hipSuccess &&
+       hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking) == hipSuccess &&
+       hipEventCreateWithFlags(&st->ev_join, hipEventDisableTiming) == hipSuccess;
+  for (int L = 0; L < Lc && ok; ++L) {
+    hipEvent_t e;
+    ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    if (ok) st->ev_fork.push_back(e);
+  }
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     edge0_stack_destroy(st);
@@ -205,12 +220,23 @@ extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, in
   const size_t d = st->shape.d_model;
   if (hipMemcpyAsync(st->h, h0, d * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return EDGE0_EHIP;
+  if (st->timed_kernel > 0) {
+    // measurement mode: the same launches enqueued directly (events cannot be
+    // timed inside a graph), each layer's chosen launch bracketed by events
+    const int rc = enqueue_step(st, step, stream, st->side);
+    if (rc != EDGE0_OK) return rc;
+    if (hipMemcpyAsync(h_out, st->h + (size_t)st->spec.n_layers * d, d * 2,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return EDGE0_EHIP;
+    st->last_step = step;
+    return EDGE0_OK;
+  }
   const int gi = step <= 1 ? step : 2 + step % 6;
   if (!st->graphs[gi]) {
     hipGraph_t g = nullptr;
     if (hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal) != hipSuccess)
       return EDGE0_EHIP;
-    const int rc = enqueue_step(st, step, st->cap);
+    const int rc = enqueue_step(st, step, st->cap, st->cap_side);
     const hipError_t ec = hipStreamEndCapture(st->cap, &g);
     if (rc != EDGE0_OK) {
       if (g) (void)hipGraphDestroy(g);
@@ -248,11 +274,41 @@ extern "C" int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffer
   return EDGE0_OK;
 }
 
+extern "C" int edge0_stack_set_timing(edge0_stack* st, int32_t kernel) {
+  if (!st || kernel < 0 || kernel > 3) return EDGE0_EINVAL;
+  const int n = st->spec.n_layers;
+  while ((int)st->ev_start.size() < n) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return EDGE0_EHIP;
+    st->ev_start.push_back(a);
+    st->ev_stop.push_back(b);
+  }
+  st->timed_kernel = kernel;
+  return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n_out) {
+  if (!st || !ms_out || !n_out || st->timed_kernel <= 0 || st->last_step < 0) return EDGE0_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess) return EDGE0_EHIP;
+  const int n = st->spec.n_layers < cap ? st->spec.n_layers : cap;
+  for (int L = 0; L < n; ++L)
+    if (hipEventElapsedTime(&ms_out[L], st->ev_start[L], st->ev_stop[L]) != hipSuccess)
+      return EDGE0_EHIP;
+  *n_out = n;
+  return EDGE0_OK;
+}
+
 extern "C" void edge0_stack_destroy(edge0_stack* st) {
   if (!st) return;
+  for (auto e : st->ev_start) (void)hipEventDestroy(e);
+  for (auto e : st->ev_stop) (void)hipEventDestroy(e);
   for (auto& g : st->graphs)
     if (g) (void)hipGraphExecDestroy(g);
   if (st->cap) (void)hipStreamDestroy(st->cap);
+  if (st->cap_side) (void)hipStreamDestroy(st->cap_side);
+  if (st->side) (void)hipStreamDestroy(st->side);
+  for (auto e : st->ev_fork) (void)hipEventDestroy(e);
+  if (st->ev_join) (void)hipEventDestroy(st->ev_join);
   (void)hipFree(st->x);
   (void)hipFree(st->y);
   (void)hipFree(st->h);

@@ -92,6 +92,9 @@ _SIG = {
     "edge0_stack_step": (C.c_int, [_P, _P, _P, C.c_int32, _P]),
     "edge0_stack_get_buffers": (C.c_int, [_P, C.POINTER(StackBuffers)]),
     "edge0_stack_destroy": (None, [_P]),
+    "edge0_stack_set_timing": (C.c_int, [_P, C.c_int32]),
+    "edge0_stack_kernel_ms": (C.c_int, [_P, C.POINTER(C.c_float), C.c_int32,
+                                        C.POINTER(C.c_int32)]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -202,6 +205,17 @@ class Stack:
     def step(self, h0, h_out, step: int, stream=None):
         _check(lib.edge0_stack_step(self._handle, _ptr(h0), _ptr(h_out), step, _stream(stream)),
                "edge0_stack_step")
+
+    def set_timing(self, kernel: int):
+        """Event pair around one launch class per layer (1 gate/up, 2 down, 3 LoRA-in)."""
+        _check(lib.edge0_stack_set_timing(self._handle, kernel), "edge0_stack_set_timing")
+
+    def kernel_ms(self) -> list:
+        n = self.spec.n_layers
+        out = (C.c_float * n)()
+        cnt = C.c_int32()
+        _check(lib.edge0_stack_kernel_ms(self._handle, out, n, C.byref(cnt)), "edge0_stack_kernel_ms")
+        return list(out[:cnt.value])
 
     def buffers(self) -> dict:
         """Views of the handle's per-layer device buffers from the last step."""

@@ -34,7 +34,7 @@ __all__ = [
     "MoEShape", "TINY", "QWEN3_MOE", "rng_for", "to_bf16_bits", "to_fp16",
     "pack_int4", "expert_tensors", "lora_tensors", "head_tensors",
     "router_weight", "hidden", "stack_hidden", "zipf_probs",
-    "zipf_trace", "grouped_routing", "EXPERT_KEYS", "LORA_KEYS", "HEAD_KEYS",
+    "zipf_trace", "grouped_routing", "EXPERT_KEYS", "LORA_KEYS", "HEAD_KEYS", "StackGen",
 ]
 
 
@@ -233,3 +233,22 @@ def grouped_routing(n_experts: int, k: int, n_tokens: int, seed: int, layer: int
         u = rng.uniform(0.1, 1.0, size=k)
         w[j] = (u / u.sum()).astype(np.float32)
     return ids, w
+
+
+class StackGen:
+    """Per-layer generator callables of a seeded synthetic stack."""
+
+    def __init__(self, shape: MoEShape, seed: int = 0):
+        self.S, self.seed = shape, seed
+
+    def expert(self, L, e):
+        return expert_tensors(self.S, self.seed, L, e)
+
+    def lora(self, L, e):
+        return lora_tensors(self.S, self.seed, L, e)
+
+    def router(self, L):
+        return router_weight(self.S, self.seed, L)
+
+    def head(self, L):
+        return head_tensors(self.S, self.seed, L)
