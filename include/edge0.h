@@ -232,7 +232,10 @@ typedef struct edge0_stack edge0_stack;
  * routers     : host array [n_layers] of device bf16 [E][d] (entries of
  *               consumer layers are still used at step 0)
  * heads       : host array [n_layers]; entries of owner layers are used
- * Every owner L must have L+1 a consumer and vice versa. */
+ * Every owner L must have L+1 a consumer and vice versa; at most 48 owners,
+ * and either all owner heads have the linear residual (wl) or none.  The
+ * heads of a step run as one batch after its last layer: the predictions
+ * are consumed at the next step ("one flush per step"). */
 int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
                        const edge0_stack_spec* spec, const edge0_slot_pool* pool,
                        const int32_t* slot_tables, const void* const* routers,

@@ -77,10 +77,9 @@ WsLayout ws_layout(const edge0_moe_shape* s) {
   L.hp_lo = take(2 * K * I);
   L.hs = take(4 * K * (I / 16));
   L.tdpart = take(4 * K * (I / 16) * r);
-  L.td = take(4 * K * r);
-  L.cnt_td = take(4 * K);
+  L.slots = take(4 * K);
   L.head_logits = take(4 * E);
-  L.dpart = take(4 * (d / 64) * K * (I / 32) * 64);
+  L.acc = take(8 * 2 * d);
   L.total = off;
   return L;
 }

@@ -164,7 +164,8 @@ __device__ __forceinline__ void row_prefetch(const uint16_t* __restrict__ w, int
     if (c < nc) p.c[m] = *reinterpret_cast<const uint4*>(w + 8 * c);
   }
 }
-// bf16 row (prefetched) . bf16 vector v (global or LDS)
+// bf16 (or, with W_FP16, fp16) row (prefetched) . bf16 vector v (global or LDS)
+template <bool W_FP16 = false>
 __device__ __forceinline__ float row_dot_pref(const RowPref& p, const uint16_t* v, int n) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nc = n >> 3;
@@ -178,18 +179,15 @@ __device__ __forceinline__ float row_dot_pref(const RowPref& p, const uint16_t* 
       const uint32_t xx[4] = {xq.x, xq.y, xq.z, xq.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc = fmaf(bf_lo(ww[q]), bf_lo(xx[q]), acc);
-        acc = fmaf(bf_hi(ww[q]), bf_hi(xx[q]), acc);
+        const float w0 = W_FP16 ? h2f(ww[q] & 0xFFFFu) : bf_lo(ww[q]);
+        const float w1 = W_FP16 ? h2f(ww[q] >> 16) : bf_hi(ww[q]);
+        acc = fmaf(w0, bf_lo(xx[q]), acc);
+        acc = fmaf(w1, bf_hi(xx[q]), acc);
       }
     }
   }
   return wave_sum(acc);
 }
-
-// Top-K of logits[0..E) by one wave, ranked by (value descending, index
-// ascending); NaN ranks as -inf.  Weights: w_k = exp(l_k - l_max) / sum over
-// the selected.  Lane 0 writes ids_out[K], w_out[K].  E <= 1024, K <= 16.
-__device__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out, float* w_out);
 
 // Device-coherent stores and loads for data handed between workgroups of one
 // kernel: agent-scope atomic accesses are performed at the device coherence
@@ -200,6 +198,87 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 }
 __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ top-K
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+// (value descending, index ascending) order: is (ov, oi) before (bv, bi)?
+__device__ __forceinline__ void argmax_take(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ void argmax_dpp(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL, ROW_MASK>(bv, bv);
+  const int oi = dpp_i<CTRL, ROW_MASK>(bi, bi);
+  argmax_take(bv, bi, ov, oi);
+}
+// wave-wide first element in (value descending, index ascending) order;
+// every lane gets it
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_dpp<0xB1>(bv, bi);
+  argmax_dpp<0x4E>(bv, bi);
+  argmax_dpp<0x141>(bv, bi);
+  argmax_dpp<0x140>(bv, bi);
+  argmax_dpp<0x142, 0xa>(bv, bi);
+  argmax_dpp<0x143, 0xc>(bv, bi);
+  bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 63));
+  bi = __builtin_amdgcn_readlane(bi, 63);
+}
+
+// Top-K of logits[0..E) by one wave, ranked by (value descending, index
+// ascending); NaN ranks as -inf.  Weights: w_k = exp(l_k - l_max) / sum over
+// the selected.  Lanes < K write ids_out[lane], w_out[lane] (global or LDS).
+// E <= 1024, K <= 16.  COHERENT: logits were written by other workgroups of
+// the running kernel with st_dev, so they are read with ld_dev.
+template <bool COHERENT>
+__device__ __forceinline__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out,
+                                          float* w_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kMaxPer = 16;
+  float v[kMaxPer];
+  const int nper = (E + kWave - 1) / kWave;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int idx = lane + kWave * j;
+    float x = -INFINITY;
+    if (j < nper && idx < E) {
+      x = COHERENT ? ld_dev(logits + idx) : logits[idx];
+      if (x != x) x = -INFINITY;
+    }
+    v[j] = x;
+  }
+  uint32_t taken = 0;  // bit j: element lane + 64 j already selected
+  float my_v = -INFINITY;  // lane kk keeps the kk-th selection
+  int my_i = 0;
+  for (int kk = 0; kk < K; ++kk) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int idx = lane + kWave * j;
+      if ((j < nper) && (idx < E) && !((taken >> j) & 1u)) argmax_take(bv, bi, v[j], idx);
+    }
+    wave_argmax(bv, bi);
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (lane == kk) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  const float m = __shfl(my_v, 0, kWave);
+  const float ex = lane < K ? expf(my_v - m) : 0.f;
+  float den = 0.f;
+  for (int j = 0; j < K; ++j) den += __shfl(ex, j, kWave);  // fixed order
+  if (lane < K) {
+    ids_out[lane] = my_i;
+    w_out[lane] = ex / den;
+  }
 }
 
 // Completion counting across workgroups.  Data that the last workgroup will
@@ -219,6 +298,18 @@ __device__ __forceinline__ bool last_arrival(uint32_t* counter, uint32_t target)
   }
   __syncthreads();
   return s_last != 0;
+}
+
+// Down-projection partial sums are accumulated in 64-bit fixed point (32
+// fractional bits): integer addition is associative, so the sum is exact and
+// the same in any arrival order.
+constexpr float kFixScale = 4294967296.0f;  // 2^32
+__device__ __forceinline__ unsigned long long to_fix(float v) {
+  const float c = fminf(fmaxf(v * kFixScale, -9.2e18f), 9.2e18f);
+  return (unsigned long long)__float2ll_rn(c);
+}
+__device__ __forceinline__ float from_fix(unsigned long long v) {
+  return (float)(long long)v * (1.0f / kFixScale);
 }
 
 // x = bf16(h / sqrt(mean(h^2) + eps)) into LDS by one workgroup (fixed
@@ -258,9 +349,9 @@ struct WsLayout {
   size_t hp_hi, hp_lo;                            // u16 [K][I]
   size_t hs;                                      // fp32 [K][I/16]
   size_t tdpart;                                  // fp32 [K][I/16][r]
-  size_t td, cnt_td;                              // fp32 [K][r], u32 [K]
+  size_t slots;                                   // int32 [K]
   size_t head_logits;                             // fp32 [E]
-  size_t dpart;                                   // fp32 [d/64][K][I/32][64]
+  size_t acc;                                     // int64 [2][d] fixed-point y
   size_t total;
 };
 

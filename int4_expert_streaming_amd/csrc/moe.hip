@@ -8,70 +8,171 @@
 // 64), §3.1 "Executor paths" (nine arrays per expert, slot table), §3.3
 // (LoRA served unmerged as a parallel delta).
 //
-// Three launches per layer, all HBM-bound at batch 1:
-//   k_lora_in : t = A x for the gate and up adapters of the K experts
-//               (K*2*r bf16 rows of length d), one wave per row.
-//   k_gate_up : gate and up rows of the K experts, one wave per row pair
-//               (row-major weights; each lane owns 32-input chunks and keeps
-//               its activation chunk in registers), LoRA B t, SwiGLU.  Writes
-//               h as bf16 hi/lo pairs for the down GEMV, per-16-row sums of
-//               h, and per-16-row partials of A_down h.
-//   k_down    : tiled down weights (1 KiB tile = 64 rows x 32 inputs; lane =
-//               output row, the tile's activation chunk is wave-uniform);
-//               units split the K*I reduction into slices; the last unit of
-//               a 64-row block sums the slices in a fixed order, adds the
-//               LoRA-down term and the routing weights, and rounds to bf16.
+// A layer is a short chain of launches, each one dependent round trip to
+// memory (a kernel boundary inside a HIP graph costs less than any
+// in-kernel hand-off between workgroups on this chip):
+//   k_layer_in : the previous layer's combine and residual, RMSNorm, and
+//                then either the router rows or (routing known) the LoRA A x
+//                rows; resolves the K slots through the slot table once.
+//                Router layers run it twice (router rows; then top-K, which
+//                every workgroup computes, and the A x rows).
+//   k_gate_up  : gate and up rows of the K experts, one wave per row pair
+//                (row-major weights; each lane owns 32-input chunks and keeps
+//                its activation chunk in registers), LoRA B t, SwiGLU.  Writes
+//                h as bf16 hi/lo pairs, per-16-row sums of h, and per-16-row
+//                partials of A_down h.
+//   k_down     : tiled down weights (1 KiB tile = 64 rows x 32 inputs; lane =
+//                output row, the tile's activation chunk is wave-uniform and
+//                staged in LDS); a unit = 64 rows x one input slice over all
+//                K experts, weighted by w_k, plus (slice 0) the LoRA-down
+//                delta.  Writes S partial rows.
+//   k_combine  : y = bf16(sum of the S partials) for the single-layer call
+//                and the stack's last layer (otherwise the next layer's
+//                k_layer_in does it).
 //
 // Int4 arithmetic: each 32-input chunk accumulates sum (128 + q) x with
 // v_dot2_f32_bf16 on exact bf16 "128 + q" nibble pairs, and the group affine
 // is applied per chunk as s * acc + (b - 128 s) * sum(x), which equals
-// sum (s q + b) x.  Everything after the loads is fp32.
+// sum (s q + b) x.  Everything after the loads is fp32, rounded once to bf16.
+#include <cstdlib>
+
 #include "moe_internal.h"
 
 namespace e0 {
 
-__device__ __forceinline__ const uint8_t* slot_of(const MoeArgs& a, int k) {
-  const int e = a.ids[k];
-  if (e < 0 || e >= a.E) return nullptr;
-  const int s = a.table[e];
+// routed expert k -> its bundle, from the slots resolved by k_layer_in
+__device__ __forceinline__ const uint8_t* slot_ptr(const MoeArgs& a, int k) {
+  const int s = a.slots[k];
   if (s < 0 || s >= a.n_slots) return nullptr;
   return a.pool + (size_t)s * (size_t)a.slot_bytes;
 }
+// id -> slot through the table (-1 when the id or its slot is invalid)
+__device__ __forceinline__ int resolve_slot(const MoeArgs& a, int e) {
+  if (e < 0 || e >= a.E) return -1;
+  const int s = a.table[e];
+  return (s < 0 || s >= a.n_slots) ? -1 : s;
+}
 
-// -------------------------------------------------------------- k_lora_in
-// t[k][p][rr] = A_p(e_k)[rr] . x.  With h_norm set, every workgroup first
-// computes x = bf16(RMSNorm(h_norm)) into LDS and workgroup 0 stores it.
-__global__ __launch_bounds__(256) void k_lora_in(MoeArgs a) {
+// ------------------------------------------------------------ k_layer_in
+
+// PER = d / 256 elements of the hidden state per thread
+template <int PER>
+__global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
+  constexpr int kMaxPerThread = PER;
   __shared__ uint16_t xs[kMaxD];
-  const int wave = threadIdx.x >> 6;
+  __shared__ int32_t ids_s[16];
+  __shared__ float w_s[16];
+  __shared__ float red[256];
+  const int d = a.d, K = a.K, r = a.r, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int row = blockIdx.x * 4 + wave;
-  const int nrows = a.K * 2 * a.r;
+  const bool router = li.flags & IN_ROUTER, lora = li.flags & IN_LORA;
+  const int nrows = router ? a.E : (lora ? K * 2 * r : 0);
   const bool active = row < nrows;
-  const int k = active ? row / (2 * a.r) : 0;
-  const int p = active ? (row / a.r) & 1 : 0;
-  const int rr = active ? row % a.r : 0;
-  const uint8_t* b = active ? slot_of(a, k) : nullptr;
-  const uint16_t* A = nullptr;
-  if (b != nullptr)
-    A = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.a_up : a.lay.a_gate)) + (size_t)rr * a.d;
+  // weight row of this wave, in flight during the prologue (when its address
+  // does not depend on the top-K computed here)
   RowPref pf;
-  const bool pref = A != nullptr && a.d <= 64 * kPrefChunks * 8;
-  if (pref) row_prefetch(A, a.d, pf);          // in flight during the norm
+  const uint16_t* wrow = nullptr;
+  if (active && router) wrow = li.w_router + (size_t)row * d;
+  if (active && lora && !(li.flags & IN_TOPK)) {
+    const int s = resolve_slot(a, a.ids[row / (2 * r)]);
+    if (s >= 0)
+      wrow = reinterpret_cast<const uint16_t*>(a.pool + (size_t)s * a.slot_bytes +
+                                               (((row / r) & 1) ? a.lay.a_up : a.lay.a_gate)) +
+             (size_t)(row % r) * d;
+  }
+  const bool pref = wrow != nullptr && d <= 64 * kPrefChunks * 8;
+  if (pref) row_prefetch(wrow, d, pf);
+  // prologue: combine, residual, RMSNorm
   const uint16_t* x = a.x;
-  if (a.h_norm != nullptr) {
-    rmsnorm_to_lds(a.h_norm, xs, a.d, a.eps);
+  if (li.flags & (IN_COMBINE | IN_NORM)) {
+    // every load of the prologue is issued before any use: h_prev and the
+    // previous layer's fixed-point y for this thread's elements j = tid + 256 m
+    constexpr int per = PER;
+    const bool comb = li.flags & IN_COMBINE;
+    uint32_t hb[kMaxPerThread];
+    unsigned long long av[kMaxPerThread];
+#pragma unroll
+    for (int m = 0; m < kMaxPerThread; ++m) {
+      const int j = tid + 256 * m;
+      hb[m] = li.h_prev[j];
+      av[m] = comb ? a.acc_prev[j] : 0ull;
+    }
+    // this layer's accumulator starts from zero (its down units add into it)
     if (blockIdx.x == 0)
-      for (int j = threadIdx.x; j < a.d; j += blockDim.x) a.x_out[j] = xs[j];
+      for (int j = tid; j < d; j += 256) a.acc[j] = 0ull;
+    float hv[kMaxPerThread];
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < kMaxPerThread; ++m) {
+      const int j = tid + 256 * m;
+      hv[m] = bf2f(hb[m]);
+      if (comb) {
+        const uint32_t yb = f2bf(from_fix(av[m]));
+        hv[m] = bf2f(f2bf(hv[m] + bf2f(yb)));
+        if (blockIdx.x == 0) {
+          li.y_prev_out[j] = (uint16_t)yb;
+          li.h_out[j] = (uint16_t)f2bf(hv[m]);
+        }
+      }
+      ss = fmaf(hv[m], hv[m], ss);
+    }
+    red[tid] = ss;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    const float inv = 1.f / sqrtf(red[0] / (float)d + li.eps);
+#pragma unroll
+    for (int m = 0; m < kMaxPerThread; ++m) {
+      const int j = tid + 256 * m;
+      if (m < per) {
+        const uint16_t xb = (uint16_t)f2bf(hv[m] * inv);
+        xs[j] = xb;
+        if (blockIdx.x == 0) li.x_out[j] = xb;
+      }
+    }
+    __syncthreads();
     x = xs;
   }
+  if (!(li.flags & (IN_COMBINE | IN_NORM)) && blockIdx.x == 0 && (li.flags & IN_LORA))
+    for (int j = tid; j < d; j += 256) a.acc[j] = 0ull;
+  // routing known to this launch: given, or top-K of the router logits
+  const int32_t* ids = a.ids;
+  if (li.flags & IN_TOPK) {
+    if (wave == 0) wave_topk<false>(li.logits, a.E, K, ids_s, w_s);
+    __syncthreads();
+    if (blockIdx.x == 0 && tid < K) {
+      li.ids_out[tid] = ids_s[tid];
+      li.w_out[tid] = w_s[tid];
+    }
+    ids = ids_s;
+  }
+  if (lora && blockIdx.x == 0 && tid < K) a.slots[tid] = resolve_slot(a, ids[tid]);
+  if (!lora && !router && blockIdx.x == 0 && tid < K) a.slots[tid] = resolve_slot(a, ids[tid]);
   if (!active) return;
+  if (router) {
+    const float s = pref ? row_dot_pref(pf, x, d) : row_dot<false, false>(wrow, x, d);
+    if (lane == 0) li.logits[row] = s;
+    return;
+  }
+  // LoRA A x rows
+  const int k = row / (2 * r), p = (row / r) & 1, rr = row % r;
+  if (li.flags & IN_TOPK) {
+    const int s = resolve_slot(a, ids[k]);
+    wrow = s < 0 ? nullptr
+                 : reinterpret_cast<const uint16_t*>(a.pool + (size_t)s * a.slot_bytes +
+                                                     (p ? a.lay.a_up : a.lay.a_gate)) +
+                       (size_t)rr * d;
+  }
   float t = 0.f;
-  if (A != nullptr) {
-    t = pref ? row_dot_pref(pf, x, a.d) : row_dot<false, false>(A, x, a.d);
-  } else if ((threadIdx.x & 63) == 0) {
+  if (wrow != nullptr) {
+    t = pref ? row_dot_pref(pf, x, d) : row_dot<false, false>(wrow, x, d);
+  } else if (lane == 0) {
     set_error(a.err, EDGE0_ERANGE);
   }
-  if ((threadIdx.x & 63) == 0) a.t_in[row] = t;
+  if (lane == 0) a.t_in[row] = t;
 }
 
 // -------------------------------------------------------------- k_gate_up
@@ -275,7 +376,7 @@ __global__ __launch_bounds__(256) void k_gate_up(MoeArgs a) {
   const int blk = blockIdx.x % nblk;
   const int i0 = blk * 16;
   const int r = a.r;
-  const uint8_t* b = slot_of(a, k);
+  const uint8_t* b = slot_ptr(a, k);
   if (b == nullptr) {
     // unresolvable expert: zero activations, flag the error
     for (int t = threadIdx.x; t < 16; t += blockDim.x) store_h(a, k, i0 + t, 0.f);
@@ -315,153 +416,167 @@ __global__ __launch_bounds__(256) void k_gate_up(MoeArgs a) {
 }
 
 // ------------------------------------------------------------------ k_down
-// Unit (rb, k, sl): rows 64 rb .. 64 rb + 63 of expert k's down projection
-// over input chunks of slice sl, times the routing weight w_k; the sl = 0
-// unit adds the LoRA-down delta.  The last unit of a row block sums the
-// K*S partials in a fixed order, rounds to bf16 and applies the residual.
-constexpr int kDownTiles = 4;  // tiles per wave per batch of loads
+// Unit (rb, sl): rows 64 rb .. 64 rb + 63 over input chunks of slice sl, for
+// all K experts, each tile's contribution weighted by w_k; slice-0 units add
+// the LoRA-down deltas.  The partial row is added to the layer's fixed-point
+// accumulator (exact, order-independent).
+// The unit's nt = K * ncs tiles (expert-major) are split into contiguous runs
+// of TPW tiles per wave; every address is wave-uniform scalar arithmetic so
+// all of a wave's tile loads are in flight together.  An expert whose slot is
+// invalid reads slot 0 with weight 0 (never an out-of-range address).
+constexpr int kMaxSliceChunks = 64;  // expert-chunks per unit staged in LDS
 
-constexpr int kMaxSliceChunks = 64;  // chunks per slice (cps) staged in LDS
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ void down_tile_loads(const uint4* dq, const uint16_t* ds,
-                                                const uint16_t* db, int rb, int NC, int d, int g,
-                                                int o, int lane, int base, int c1, uint4* q,
-                                                uint32_t* sv, uint32_t* bv) {
-#pragma unroll
-  for (int m = 0; m < kDownTiles; ++m) {
-    const int c = base + 4 * m;
-    if (c < c1) {
-      q[m] = dq[((size_t)rb * NC + c) * 64 + lane];
-      const int grp = (32 * c) / g;
-      sv[m] = ds[(size_t)grp * d + o];
-      bv[m] = db[(size_t)grp * d + o];
-    }
-  }
-}
-
+template <int TPW>
 __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   __shared__ float red[4][64];
   __shared__ uint32_t hp_s[kMaxSliceChunks][32];  // hi pairs then lo pairs of each chunk
   __shared__ float hsum_s[kMaxSliceChunks];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K = a.K, S = a.S, I = a.I, d = a.d, r = a.r;
+  __shared__ float td_s[4][64];                   // t_down of the expert each wave handles
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(threadIdx.x >> 6);
+  const int K = a.K, S = a.S, I = a.I, r = a.r, d = a.d;
   const int NC = I / 32;
-  const int u = blockIdx.x;
-  const int rb = u / (K * S);
-  const int k = (u / S) % K;
-  const int sl = u % S;
+  const int rb = blockIdx.x / S;
+  const int sl = blockIdx.x % S;
   const int cps = (NC + S - 1) / S;
   const int c0 = sl * cps;
-  const int c1 = min(NC, c0 + cps);
+  const int ncs = min(NC, c0 + cps) - c0;
+  const int nt = K * ncs;
   const int o = rb * 64 + lane;
-  const uint8_t* b = slot_of(a, k);  // uniform over the workgroup
-  const float wk = a.w[k];
-  const uint4* dq = nullptr;
-  const uint16_t *ds = nullptr, *db = nullptr;
-  uint4 q[kDownTiles];
-  uint32_t sv[kDownTiles], bv[kDownTiles];
-  // LoRA-down delta for these rows (slice 0 only, wave 0): t_down = sum over
-  // the 16-row partials of A_down h, where element t = blk*r + rr of the
-  // partials goes to lane t % 64 (which always holds rr = lane % r, r
-  // dividing 64), and B_down row o (r bf16).  Loaded before the tiles.
-  const bool lora_here = b != nullptr && r > 0 && sl == 0 && wave == 0;
+  // this wave's tiles: t = wave * TPW + m
+  uint4 q[TPW];
+  uint32_t sv[TPW], bv[TPW];
+  float wt[TPW];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int t = wave * TPW + m;
+    const bool valid = t < nt;
+    const int tc = valid ? t : 0;
+    const int kk = tc / ncs, c = c0 + tc % ncs;
+    int slot = a.slots[kk];
+    const bool ok = slot >= 0 && slot < a.n_slots;
+    wt[m] = (valid && ok) ? a.w[kk] : 0.f;
+    slot = ok ? slot : 0;
+    const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+    q[m] = reinterpret_cast<const uint4*>(b + a.lay.down_q)[((size_t)rb * NC + c) * 64 + lane];
+    const int grp = (32 * c) / a.g;
+    sv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_s)[(size_t)grp * d + o];
+    bv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_b)[(size_t)grp * d + o];
+  }
+  // LoRA-down for slice-0 units: wave w handles experts w, w+4, ...; t_down
+  // of expert k = sum over the 16-row partials of A_down h, where element
+  // t = blk*r + rr goes to lane t % 64 (which always holds rr = lane % r,
+  // r dividing 64); B_down row o.  The first expert's inputs are loaded here.
+  const bool lora_unit = r > 0 && sl == 0;
   const int ntd = (I / 16) * r;
   constexpr int kTd = 16;
   float tdr[kTd];
   uint4 bdr[8];
-  if (b != nullptr) {
-    dq = reinterpret_cast<const uint4*>(b + a.lay.down_q);
-    ds = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
-    db = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
-    if (lora_here) {
-      const float* tp = a.tdpart + (size_t)k * ntd;
+  auto lora_loads = [&](int kk) {
+    int slot = a.slots[kk];
+    slot = (slot >= 0 && slot < a.n_slots) ? slot : 0;
+    const float* tp = a.tdpart + (size_t)kk * ntd;
 #pragma unroll
-      for (int m = 0; m < kTd; ++m) tdr[m] = (lane + 64 * m < ntd) ? tp[lane + 64 * m] : 0.f;
-      const uint4* Bdp = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(b + a.lay.b_down) + (size_t)o * r);
+    for (int m = 0; m < kTd; ++m) tdr[m] = (lane + 64 * m < ntd) ? tp[lane + 64 * m] : 0.f;
+    const uint4* Bdp = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(a.pool + (size_t)slot * a.slot_bytes + a.lay.b_down) +
+        (size_t)o * r);
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-        if (8 * m < r) bdr[m] = Bdp[m];
+    for (int m = 0; m < 8; ++m)
+      if (8 * m < r) bdr[m] = Bdp[m];
+  };
+  if (lora_unit && wave < K) lora_loads(wave);
+  // stage the unit's activation pairs and chunk sums (all K experts) in LDS
+  {
+    constexpr int kStage = kMaxSliceChunks * 32 / 256;  // words per thread
+    uint32_t st[kStage];
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      const int t = threadIdx.x + 256 * m;
+      if (t < nt * 32) {
+        const int tt = t >> 5, j = t & 31;
+        const int kk = tt / ncs, c = c0 + tt % ncs;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(j < 16 ? a.hp_hi : a.hp_lo) +
+                              (size_t)kk * (I / 2);
+        st[m] = src[16 * c + (j & 15)];
+      }
     }
-    // first batch of this wave's tiles: in flight while the slice's
-    // activation pairs and chunk sums are staged in LDS
-    down_tile_loads(dq, ds, db, rb, NC, d, a.g, o, lane, c0 + wave, c1, q, sv, bv);
-    const uint32_t* hph = reinterpret_cast<const uint32_t*>(a.hp_hi + (size_t)k * I);
-    const uint32_t* hpl = reinterpret_cast<const uint32_t*>(a.hp_lo + (size_t)k * I);
-    const float* hs = a.hs + (size_t)k * (I / 16);
-    const int ncs = c1 - c0;
-    for (int t = threadIdx.x; t < ncs * 32; t += blockDim.x) {
-      const int cc = t >> 5, j = t & 31;
-      hp_s[cc][j] = j < 16 ? hph[16 * (c0 + cc) + j] : hpl[16 * (c0 + cc) + j - 16];
+    float h0v = 0.f, h1v = 0.f;
+    const int tt = threadIdx.x;
+    if (tt < nt) {
+      const int kk = tt / ncs, c = c0 + tt % ncs;
+      const float* hs = a.hs + (size_t)kk * (I / 16);
+      h0v = hs[2 * c];
+      h1v = hs[2 * c + 1];
     }
-    for (int t = threadIdx.x; t < ncs; t += blockDim.x)
-      hsum_s[t] = hs[2 * (c0 + t)] + hs[2 * (c0 + t) + 1];
-  } else if (threadIdx.x == 0) {
-    set_error(a.err, EDGE0_ERANGE);
+#pragma unroll
+    for (int m = 0; m < kStage; ++m) {
+      const int t = threadIdx.x + 256 * m;
+      if (t < nt * 32) hp_s[t >> 5][t & 31] = st[m];
+    }
+    if (tt < nt) hsum_s[tt] = h0v + h1v;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (unsigned)K) {
+    const int slot = a.slots[threadIdx.x];
+    if (slot < 0 || slot >= a.n_slots) set_error(a.err, EDGE0_ERANGE);
   }
   __syncthreads();  // every thread, unconditionally
   float part = 0.f;
-  if (b != nullptr) {
-    for (int base = c0 + wave; base < c1; base += 4 * kDownTiles) {
-      if (base != c0 + wave)
-        down_tile_loads(dq, ds, db, rb, NC, d, a.g, o, lane, base, c1, q, sv, bv);
 #pragma unroll
-      for (int m = 0; m < kDownTiles; ++m) {
-        const int c = base + 4 * m;
-        if (c < c1) {
-          const float s = bf2f(sv[m]), bb = bf2f(bv[m]);
-          const uint32_t* hp = hp_s[c - c0];
-          const float acc = chunk_dot128(q[m], hp) + chunk_dot128(q[m], hp + 16);
-          part += s * acc + (bb - 128.f * s) * hsum_s[c - c0];
-        }
-      }
+  for (int m = 0; m < TPW; ++m) {
+    const int t = wave * TPW + m;
+    if (t < nt) {
+      const float s = bf2f(sv[m]), bb = bf2f(bv[m]);
+      const uint32_t* hp = hp_s[t];
+      const float acc = chunk_dot128(q[m], hp) + chunk_dot128(q[m], hp + 16);
+      part += wt[m] * (s * acc + (bb - 128.f * s) * hsum_s[t]);
     }
-    if (lora_here) {
+  }
+  if (lora_unit) {
+    for (int kk = wave; kk < K; kk += 4) {
+      const int slot = a.slots[kk];
+      if (slot < 0 || slot >= a.n_slots) continue;
+      if (kk != wave) lora_loads(kk);
       float tdv = 0.f;
 #pragma unroll
       for (int m = 0; m < kTd; ++m) tdv += tdr[m];
-      for (int t = lane + 64 * kTd; t < ntd; t += 64) tdv += a.tdpart[(size_t)k * ntd + t];
+      for (int t = lane + 64 * kTd; t < ntd; t += 64) tdv += a.tdpart[(size_t)kk * ntd + t];
       for (int off = r; off < 64; off <<= 1) tdv += __shfl_xor(tdv, off, kWave);
+      td_s[wave][lane] = tdv;  // lane rr (< r) holds t_down[rr]; read back as a broadcast
+      __builtin_amdgcn_wave_barrier();
       float dl = 0.f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (8 * m < r) {
           const uint32_t bw[4] = {bdr[m].x, bdr[m].y, bdr[m].z, bdr[m].w};
+          const float4 t0 = *reinterpret_cast<const float4*>(&td_s[wave][8 * m]);
+          const float4 t1 = *reinterpret_cast<const float4*>(&td_s[wave][8 * m + 4]);
+          const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            dl += bf_lo(bw[q2]) * __shfl(tdv, 8 * m + 2 * q2, kWave);
-            dl += bf_hi(bw[q2]) * __shfl(tdv, 8 * m + 2 * q2 + 1, kWave);
+            dl += bf_lo(bw[q2]) * tv[2 * q2];
+            dl += bf_hi(bw[q2]) * tv[2 * q2 + 1];
           }
         }
       }
-      part += a.scale * dl;
+      __builtin_amdgcn_wave_barrier();
+      part += a.w[kk] * (a.scale * dl);
     }
   }
   red[wave][lane] = part;
   __syncthreads();
-  if (wave == 0) {
-    const float t = (red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]) * wk;
-    a.dpart[(((size_t)rb * K + k) * S + sl) * 64 + lane] = t;
-  }
+  if (wave == 0)
+    atomicAdd(a.acc + o, to_fix(red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]));
 }
 
-// y[o] = bf16(sum over experts k and slices s of the down partials, in that
-// fixed order); optional residual h_out = bf16(h_res + y)
+// y = bf16 of the layer's fixed-point accumulator; optional residual
+// h_out = bf16(h_res + y).  (In the stack the next layer's k_layer_in does it.)
 __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= a.d) return;
-  const int rb = o / 64, lane = o % 64;
-  const float* p = a.dpart + (size_t)rb * a.K * a.S * 64 + lane;
-  const int n = a.K * a.S;
-  float yv = 0.f;
-  for (int j0 = 0; j0 < n; j0 += 16) {
-    float v[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) v[m] = (j0 + m < n) ? p[(size_t)(j0 + m) * 64] : 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) yv += v[m];
-  }
-  const uint32_t yb = f2bf(yv);
+  const uint32_t yb = f2bf(from_fix(a.acc[o]));
   a.y[o] = (uint16_t)yb;
   if (a.h_out != nullptr) a.h_out[o] = (uint16_t)f2bf(bf2f(a.h_res[o]) + bf2f(yb));
 }
@@ -500,7 +615,7 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   edge0_bundle_layout lay;
   if (bundle_layout(sh, &lay) != EDGE0_OK) return EDGE0_EINVAL;
   if (!pool || !pool->base || pool->n_slots <= 0 || pool->slot_bytes < lay.bytes ||
-      pool->slot_bytes % 256 != 0 || !table || !ids || !w || !x || !y || !workspace || x == y)
+      pool->slot_bytes % 256 != 0 || !table || !ids || !w || !workspace)
     return EDGE0_EINVAL;
   const WsLayout L = ws_layout(sh);
   char* ws = static_cast<char*>(workspace);
@@ -533,32 +648,50 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
   a->hs = reinterpret_cast<float*>(ws + L.hs);
   a->tdpart = reinterpret_cast<float*>(ws + L.tdpart);
-  a->td = reinterpret_cast<float*>(ws + L.td);
-  a->cnt_td = reinterpret_cast<uint32_t*>(ws + L.cnt_td);
-  a->dpart = reinterpret_cast<float*>(ws + L.dpart);
+  a->slots = reinterpret_cast<int32_t*>(ws + L.slots);
+  a->acc = reinterpret_cast<unsigned long long*>(ws + L.acc);
+  a->acc_prev = a->acc + a->d;
+  // down units: 64-row blocks x input slices, about 256 of them, and a
+  // unit's expert-chunks fit the LDS stage
   const int RB = a->d / 64, NC = a->I / 32;
-  int S = (512 + RB * a->K - 1) / (RB * a->K);
+  int S = (256 + RB - 1) / RB;
   S = S < 1 ? 1 : (S > NC ? NC : S);
-  const int min_s = (NC + kMaxSliceChunks - 1) / kMaxSliceChunks;  // slice fits the LDS stage
-  a->S = S < min_s ? min_s : S;
+  while ((a->K * ((NC + S - 1) / S)) > kMaxSliceChunks && S < NC) ++S;
+  a->S = S;
+  if ((a->K * ((NC + S - 1) / S) + 3) / 4 > 16) return EDGE0_EINVAL;
   return EDGE0_OK;
 }
 
-int launch_moe(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
-  auto mark = [&](int which, bool start) {
-    if (timing && timing->which == which)
-      (void)hipEventRecord(start ? timing->start : timing->stop, stream);
-  };
-  if (a.r > 0 || a.h_norm != nullptr) {
-    const int rows = a.K * 2 * a.r;
-    mark(3, true);
-    k_lora_in<<<rows > 0 ? (rows + 3) / 4 : 1, 256, 0, stream>>>(a);
-    E0_CHECK_LAUNCH();
-    mark(3, false);
+#define E0_MARK(kind, is_start)                                                 \
+  do {                                                                         \
+    if (timing && timing->which == (kind))                                     \
+      (void)hipEventRecord((is_start) ? timing->start : timing->stop, stream); \
+  } while (0)
+
+int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
+                    const LaunchTiming* timing) {
+  const int rows = (li.flags & IN_ROUTER) ? a.E : ((li.flags & IN_LORA) ? a.K * 2 * a.r : 0);
+  E0_MARK(3, true);
+  const int grid = rows > 0 ? (rows + 3) / 4 : 1;
+  switch (a.d / 256) {
+    case 1: k_layer_in<1><<<grid, 256, 0, stream>>>(a, li); break;
+    case 2: k_layer_in<2><<<grid, 256, 0, stream>>>(a, li); break;
+    case 4: k_layer_in<4><<<grid, 256, 0, stream>>>(a, li); break;
+    case 8: k_layer_in<8><<<grid, 256, 0, stream>>>(a, li); break;
+    case 16: k_layer_in<16><<<grid, 256, 0, stream>>>(a, li); break;
+    case 24: k_layer_in<24><<<grid, 256, 0, stream>>>(a, li); break;
+    case 32: k_layer_in<32><<<grid, 256, 0, stream>>>(a, li); break;
+    default: return EDGE0_EINVAL;
   }
+  E0_CHECK_LAUNCH();
+  E0_MARK(3, false);
+  return EDGE0_OK;
+}
+
+int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
   const int cpr = a.d / 32;
   const int grid2 = a.K * (a.I / 16);
-  mark(1, true);
+  E0_MARK(1, true);
   switch (cpr) {
     case 8: k_gate_up<8><<<grid2, 256, 0, stream>>>(a); break;
     case 16: k_gate_up<16><<<grid2, 256, 0, stream>>>(a); break;
@@ -570,12 +703,28 @@ int launch_moe(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing)
     default: return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();
-  mark(1, false);
-  const int grid3 = (a.d / 64) * a.K * a.S;
-  mark(2, true);
-  k_down<<<grid3, 256, 0, stream>>>(a);
+  E0_MARK(1, false);
+  E0_MARK(2, true);
+  {
+    const int NC = a.I / 32, cps = (NC + a.S - 1) / a.S;
+    const int tpw = (a.K * cps + 3) / 4;
+    const int grid = (a.d / 64) * a.S;
+    if (tpw <= 1) k_down<1><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 2) k_down<2><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 3) k_down<3><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 4) k_down<4><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 6) k_down<6><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 8) k_down<8><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 12) k_down<12><<<grid, 256, 0, stream>>>(a);
+    else if (tpw <= 16) k_down<16><<<grid, 256, 0, stream>>>(a);
+    else return EDGE0_EINVAL;
+  }
   E0_CHECK_LAUNCH();
-  mark(2, false);
+  E0_MARK(2, false);
+  return EDGE0_OK;
+}
+
+int launch_combine(const MoeArgs& a, hipStream_t stream) {
   k_combine<<<(a.d + 255) / 256, 256, 0, stream>>>(a);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
@@ -588,11 +737,15 @@ using namespace e0;
 extern "C" int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                                const int32_t* slot_table, const int32_t* ids, const float* w,
                                const void* x, void* y, void* workspace, hipStream_t stream) {
-  if (!shape || !shape_ok(shape)) return EDGE0_EINVAL;
+  if (!shape || !shape_ok(shape) || !x || !y || x == y) return EDGE0_EINVAL;
   MoeArgs a;
-  const int rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, workspace, &a);
+  int rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, workspace, &a);
   if (rc != EDGE0_OK) return rc;
-  return launch_moe(a, stream);
+  LayerIn li{};
+  li.flags = IN_LORA;  // with r = 0 it only resolves the slots
+  if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+  if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
+  return launch_combine(a, stream);
 }
 
 extern "C" int edge0_pack_bundle(const edge0_moe_shape* shape, const edge0_expert_arrays* src,

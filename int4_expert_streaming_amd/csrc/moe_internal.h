@@ -31,22 +31,74 @@ struct MoeArgs {
   uint16_t* hp_lo;
   float* hs;
   float* tdpart;
-  float* td;                // A_down h, [K][r]
-  uint32_t* cnt_td;         // [K]
-  float* dpart;
+  int32_t* slots;           // [K] slot of each routed expert (-1: invalid), set by k_layer_in
+  unsigned long long* acc;  // [d] this layer's y in fixed point (down units add into it)
+  const unsigned long long* acc_prev;  // [d] the previous layer's (combined by k_layer_in)
   int S;  // down slices
 };
 
 int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const int32_t* table,
                   const int32_t* ids, const float* w, const void* x, void* y, void* workspace,
                   MoeArgs* a);
+// First launch of a layer (k_layer_in), by flags:
+//   IN_COMBINE: y_prev = bf16(acc_prev), h = bf16(h_prev + y_prev)
+//   IN_NORM:    x = bf16(RMSNorm(h)) (h = h_prev without IN_COMBINE)
+//   IN_ROUTER:  router logits rows
+//   IN_TOPK:    softmax-top-K of `logits` (computed by every workgroup)
+//   IN_LORA:    t = A x rows of the K experts' gate/up adapters
+// Workgroup 0 stores h, y_prev, x, the committed ids/w and the slots.
+enum { IN_COMBINE = 1, IN_NORM = 2, IN_ROUTER = 4, IN_TOPK = 8, IN_LORA = 16 };
+struct LayerIn {
+  int flags;
+  const uint16_t* h_prev;
+  uint16_t* h_out;
+  uint16_t* y_prev_out;
+  uint16_t* x_out;
+  float eps;
+  const uint16_t* w_router;
+  float* logits;
+  int32_t* ids_out;
+  float* w_out;
+};
+
 // Optional event pair recorded around one of the launches (measurement aid):
-// which = 1 the gate/up GEMV, 2 the down GEMV + combine, 3 the LoRA-in GEMV.
+// which = 1 the gate/up GEMV, 2 the down GEMV, 3 the layer-input launch.
 struct LaunchTiming {
   int which;
   hipEvent_t start, stop;
 };
-int launch_moe(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
+                    const LaunchTiming* timing = nullptr);
+int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+int launch_combine(const MoeArgs& a, hipStream_t stream);
+
+// A batch of prerouter heads (one per owner layer): head i reads x at
+// x + i*x_stride and its routing at ids_now/ids_prev + i*ids_stride (ids_prev
+// may be NULL), and writes its committed ids/w at ids_out/w_out +
+// i*out_stride.  a, res, logits are [n][H], [n][E], [n][E]; counters [n].
+constexpr int kMaxHeads = 48;
+struct HeadBatch {
+  int n, d, E, K, H;
+  int has_res;
+  const uint16_t* w1x[kMaxHeads];
+  const uint16_t* w1oh[kMaxHeads];
+  const uint16_t* b1[kMaxHeads];
+  const uint16_t* w2[kMaxHeads];
+  const uint16_t* b2[kMaxHeads];
+  const uint16_t* wl[kMaxHeads];
+  const uint16_t* x;
+  int x_stride;
+  const int32_t* ids_now;
+  const int32_t* ids_prev;
+  int ids_stride;
+  float *a, *res, *logits;
+  uint32_t* counters;
+  int32_t* ids_out;
+  float* w_out;
+  int out_stride;
+  uint32_t* err;
+};
+int launch_heads(const HeadBatch& hb, hipStream_t stream);
 
 int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
                   const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,

@@ -10,65 +10,9 @@
 // loads per lane, fp32 accumulation, a wave butterfly for the row sum.  The
 // top-K runs in the last workgroup to finish (completion counter in the
 // workspace), so a router or head call is one or two launches.
-#include "common.h"
+#include "moe_internal.h"
 
 namespace e0 {
-
-// ------------------------------------------------------------------ top-K
-__device__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out, float* w_out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kMaxPer = 16;  // E <= 1024
-  float v[kMaxPer];
-  const int nper = (E + kWave - 1) / kWave;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    const int idx = lane + kWave * j;
-    float x = -INFINITY;
-    if (j < nper && idx < E) {
-      x = ld_dev(logits + idx);
-      if (x != x) x = -INFINITY;
-    }
-    v[j] = x;
-  }
-  uint32_t taken = 0;  // bit j: element lane + 64 j already selected
-  float my_v = -INFINITY;  // lane kk keeps the kk-th selection
-  int my_i = 0;
-  for (int kk = 0; kk < K; ++kk) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int idx = lane + kWave * j;
-      const bool ok = (j < nper) && (idx < E) && !((taken >> j) & 1u);
-      if (ok && (v[j] > bv || (v[j] == bv && idx < bi))) {
-        bv = v[j];
-        bi = idx;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    if (lane == kk) {
-      my_v = bv;
-      my_i = bi;
-    }
-  }
-  const float m = __shfl(my_v, 0, kWave);
-  const float ex = lane < K ? expf(my_v - m) : 0.f;
-  float den = 0.f;
-  for (int j = 0; j < K; ++j) den += __shfl(ex, j, kWave);  // fixed order
-  if (lane < K) {
-    ids_out[lane] = my_i;
-    w_out[lane] = ex / den;
-  }
-}
 
 // ---------------------------------------------------------------- router
 // With h_norm set, every workgroup computes x = bf16(RMSNorm(h_norm)) into LDS
@@ -98,71 +42,97 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ wr,
     if ((threadIdx.x & 63) == 0) st_dev(logits + row, s);
   }
   if (last_arrival(counter, gridDim.x)) {
-    if (wave == 0) wave_topk(logits, E, K, ids, w);
+    if (wave == 0) wave_topk<true>(logits, E, K, ids, w);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ------------------------------------------------------------ prerouter
-// fc1 rows [0, H): a[h] = gelu(w1x[h] . x + sum of the one-hot columns + b1[h]);
-// residual rows [H, H+E): res[e] = wl[e] . x
-__global__ __launch_bounds__(256) void k_head_fc1(
-    const uint16_t* __restrict__ w1x, const uint16_t* __restrict__ w1oh,
-    const uint16_t* __restrict__ b1, const uint16_t* __restrict__ wl,
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_now,
-    const int32_t* __restrict__ ids_prev, int d, int E, int K, int H, float* __restrict__ a,
-    float* __restrict__ res, uint32_t* __restrict__ err) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  if (row < H) {
-    float s = row_dot<true, false>(w1x + (size_t)row * d, x, d);
-    // gather of the one-hot columns: lane j < K this token's ids, lane
-    // K <= j < 2K the previous token's (block offset E)
+// Heads run batched: one launch covers the fc1 (and residual) rows of every
+// head of the batch, one the fc2 rows and each head's top-K (the last
+// workgroup of a head, per-head completion counter).  A batch of one is the
+// single-head call; the stack runs the heads of all owner layers of a step
+// as one batch after the step's layers ("one flush per step").
+__device__ __forceinline__ float gelu_erf_f(float z) {
+  return 0.5f * z * (1.f + erff(z * 0.70710678118654752440f));
+}
+
+// fc1 rows [0, H) of head i: a[i][h] = gelu(w1x[h] . x_i + sum of the one-hot
+// columns + b1[h]); residual rows [H, H+E): res[i][e] = wl[e] . x_i
+__global__ __launch_bounds__(256) void k_heads_fc1(HeadBatch hb) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H = hb.H, E = hb.E, K = hb.K, d = hb.d;
+  const int per = (H + (hb.has_res ? E : 0) + 3) / 4;
+  const int i = blockIdx.x / per;
+  const int row = (blockIdx.x % per) * 4 + wave;
+  const uint16_t* x = hb.x + (size_t)i * hb.x_stride;
+  const bool fc1 = row < H;
+  const bool resrow = !fc1 && hb.has_res && row < H + E;
+  if (!fc1 && !resrow) return;
+  const uint16_t* wrow = fc1 ? hb.w1x[i] + (size_t)row * d : hb.wl[i] + (size_t)(row - H) * d;
+  RowPref pf;
+  const bool pref = d <= 64 * kPrefChunks * 8;
+  if (pref) row_prefetch(wrow, d, pf);
+  if (fc1) {
+    // one-hot columns: lane j < K this token's ids, K <= j < 2K the previous
+    // token's (block offset E); loaded with the row
     float g = 0.f;
     if (lane < 2 * K) {
       const bool prev = lane >= K;
-      const int32_t* src = prev ? ids_prev : ids_now;
+      const int32_t* src = prev ? hb.ids_prev : hb.ids_now;
       if (src != nullptr) {
-        const int id = src[prev ? lane - K : lane];
+        const int id = src[(size_t)i * hb.ids_stride + (prev ? lane - K : lane)];
         if (id >= 0 && id < E) {
-          g = h2f(w1oh[(size_t)(prev ? E + id : id) * H + row]);
+          g = h2f(hb.w1oh[i][(size_t)(prev ? E + id : id) * H + row]);
         } else {
-          set_error(err, EDGE0_ERANGE);
+          set_error(hb.err, EDGE0_ERANGE);
         }
       }
     }
-    // fixed-order sum of the gathered columns (lanes 0..2K-1 in order)
+    const float b1 = hb.b1[i] != nullptr ? h2f(hb.b1[i][row]) : 0.f;
+    float s = pref ? row_dot_pref<true>(pf, x, d) : row_dot<true, false>(wrow, x, d);
     float gs = 0.f;
-    for (int j = 0; j < 2 * K; ++j) gs += __shfl(g, j, kWave);
-    s += gs;
-    if (b1 != nullptr) s += h2f(b1[row]);
-    if (lane == 0) a[row] = 0.5f * s * (1.f + erff(s * 0.70710678118654752440f));
-  } else if (wl != nullptr && row < H + E) {
-    const int e = row - H;
-    const float s = row_dot<true, false>(wl + (size_t)e * d, x, d);
-    if (lane == 0) res[e] = s;
+    for (int j = 0; j < 2 * K; ++j) gs += __shfl(g, j, kWave);  // fixed order
+    s += gs + b1;
+    if (lane == 0) hb.a[(size_t)i * H + row] = gelu_erf_f(s);
+  } else {
+    const float s = pref ? row_dot_pref<true>(pf, x, d) : row_dot<true, false>(wrow, x, d);
+    if (lane == 0) hb.res[(size_t)i * E + row - H] = s;
   }
 }
 
-// logits[e] = w2[e] . a + b2[e] + res[e]; then top-K in the last workgroup
-__global__ __launch_bounds__(256) void k_head_fc2(
-    const uint16_t* __restrict__ w2, const uint16_t* __restrict__ b2,
-    const float* __restrict__ a, const float* __restrict__ res, int E, int K, int H,
-    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
-    uint32_t* __restrict__ counter) {
+// logits[i][e] = w2[e] . a_i + b2[e] + res[i][e]; then top-K of head i in its
+// last workgroup
+__global__ __launch_bounds__(256) void k_heads_fc2(HeadBatch hb) {
   const int wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wave;
+  const int H = hb.H, E = hb.E, K = hb.K;
+  const int per = (E + 3) / 4;
+  const int i = blockIdx.x / per;
+  const int row = (blockIdx.x % per) * 4 + wave;
+  float* logits = hb.logits + (size_t)i * E;
   if (row < E) {
-    float s = row_dot<true, true>(w2 + (size_t)row * H, a, H);
-    if (b2 != nullptr) s += h2f(b2[row]);
-    if (res != nullptr) s += res[row];
+    float s = row_dot<true, true>(hb.w2[i] + (size_t)row * H, hb.a + (size_t)i * H, H);
+    if (hb.b2[i] != nullptr) s += h2f(hb.b2[i][row]);
+    if (hb.has_res) s += hb.res[(size_t)i * E + row];
     if ((threadIdx.x & 63) == 0) st_dev(logits + row, s);
   }
-  if (last_arrival(counter, gridDim.x)) {
-    if (wave == 0) wave_topk(logits, E, K, ids, w);
-    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (last_arrival(hb.counters + i, (uint32_t)per)) {
+    if (wave == 0)
+      wave_topk<true>(logits, E, K, hb.ids_out + (size_t)i * hb.out_stride,
+                      hb.w_out + (size_t)i * hb.out_stride);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(hb.counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+int launch_heads(const HeadBatch& hb, hipStream_t stream) {
+  if (hb.n < 1 || hb.n > kMaxHeads) return EDGE0_EINVAL;
+  const int per1 = (hb.H + (hb.has_res ? hb.E : 0) + 3) / 4;
+  k_heads_fc1<<<hb.n * per1, 256, 0, stream>>>(hb);
+  E0_CHECK_LAUNCH();
+  k_heads_fc2<<<hb.n * ((hb.E + 3) / 4), 256, 0, stream>>>(hb);
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
 }
 
 }  // namespace e0
@@ -204,21 +174,28 @@ extern "C" int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* h
     return EDGE0_EINVAL;
   const WsLayout L = ws_layout(shape);
   char* ws = static_cast<char*>(workspace);
-  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.head_logits);
-  float* a = reinterpret_cast<float*>(ws + L.head_a);
-  float* res = reinterpret_cast<float*>(ws + L.head_res);
-  const int d = shape->d_model, E = shape->n_experts, K = shape->top_k, H = shape->head_hidden;
-  const int rows1 = H + (head->wl ? E : 0);
-  k_head_fc1<<<(rows1 + 3) / 4, 256, 0, stream>>>(
-      static_cast<const uint16_t*>(head->w1x), static_cast<const uint16_t*>(head->w1oh),
-      static_cast<const uint16_t*>(head->b1), static_cast<const uint16_t*>(head->wl),
-      static_cast<const uint16_t*>(x), ids_now, ids_prev, d, E, K, H, a, res,
-      reinterpret_cast<uint32_t*>(ws + L.err));
-  E0_CHECK_LAUNCH();
-  k_head_fc2<<<(E + 3) / 4, 256, 0, stream>>>(
-      static_cast<const uint16_t*>(head->w2), static_cast<const uint16_t*>(head->b2), a,
-      head->wl ? res : nullptr, E, K, H, logits, ids_out, w_out,
-      reinterpret_cast<uint32_t*>(ws + L.cnt_head));
-  E0_CHECK_LAUNCH();
-  return EDGE0_OK;
+  HeadBatch hb{};
+  hb.n = 1;
+  hb.d = shape->d_model;
+  hb.E = shape->n_experts;
+  hb.K = shape->top_k;
+  hb.H = shape->head_hidden;
+  hb.has_res = head->wl != nullptr;
+  hb.w1x[0] = static_cast<const uint16_t*>(head->w1x);
+  hb.w1oh[0] = static_cast<const uint16_t*>(head->w1oh);
+  hb.b1[0] = static_cast<const uint16_t*>(head->b1);
+  hb.w2[0] = static_cast<const uint16_t*>(head->w2);
+  hb.b2[0] = static_cast<const uint16_t*>(head->b2);
+  hb.wl[0] = static_cast<const uint16_t*>(head->wl);
+  hb.x = static_cast<const uint16_t*>(x);
+  hb.ids_now = ids_now;
+  hb.ids_prev = ids_prev;
+  hb.a = reinterpret_cast<float*>(ws + L.head_a);
+  hb.res = reinterpret_cast<float*>(ws + L.head_res);
+  hb.logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.head_logits);
+  hb.counters = reinterpret_cast<uint32_t*>(ws + L.cnt_head);
+  hb.ids_out = ids_out;
+  hb.w_out = w_out;
+  hb.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  return launch_heads(hb, stream);
 }

@@ -15,6 +15,7 @@
 // s.  A consumer layer at step s>0 routes by pred[s%3][L].  Three prediction
 // buffers keep the routing of step s-1 (the heads' "previous token" input)
 // intact while step s writes the next predictions.
+#include <cstdlib>
 #include <new>
 #include <vector>
 
@@ -54,16 +55,16 @@ struct edge0_stack {
   float* exec_w[2];
   int32_t* pred_ids[3];
   float* pred_w[3];
-  int32_t* run_ids;          // [L][K] routing executed in the last step
-  float* run_w;
+  float* logits;             // [E] router logits of the current layer
+  int32_t* run_ids[2];       // [L][K] routing executed, by step parity
+  float* run_w[2];
+  float *head_a, *head_res, *head_logits;
+  uint32_t* head_cnt;
   void* ws;
   size_t ws_bytes;
   int32_t last_step;
   hipStream_t cap;           // capture stream
-  hipStream_t cap_side;      // capture stream of the head branch
-  hipStream_t side;          // head branch stream for direct (timed) enqueue
-  std::vector<hipEvent_t> ev_fork;  // per layer: x and routing of the layer are ready
-  hipEvent_t ev_join;
+  HeadBatch heads_batch;     // head weights of the owner layers and scratch
   int timed_kernel;          // measurement aid: which launch class carries events
   std::vector<hipEvent_t> ev_start, ev_stop;  // one pair per layer
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
@@ -79,69 +80,80 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
 // enqueue all launches of decode step `step` (h[0] already holds h0).  The
 // heads are off the step's critical path (their predictions are used at the
 // next step), so they run on a forked branch that joins at the end.
-static int enqueue_step(edge0_stack* st, int step, hipStream_t stream, hipStream_t side) {
+static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers, E = sh.n_experts;
+  MoeArgs a{};
   for (int L = 0; L < Lc; ++L) {
     uint16_t* hL = st->h + (size_t)L * d;
     uint16_t* xL = st->x + (size_t)L * d;
     const bool by_pred = is_consumer(st->spec, L) && step > 0;
-    int32_t* ids;
-    float* w;
-    if (by_pred) {
-      ids = st->pred_ids[step % 3] + (size_t)L * K;
-      w = st->pred_w[step % 3] + (size_t)L * K;
-    } else {
-      ids = st->exec_ids[step & 1] + (size_t)L * K;
-      w = st->exec_w[step & 1] + (size_t)L * K;
-      // the router launch also computes x_L = bf16(RMSNorm(h_L))
-      const int rc = launch_router(&sh, st->routers[L], nullptr, hL, xL, st->spec.rms_eps, nullptr,
-                                   ids, w, st->ws, stream);
-      if (rc != EDGE0_OK) return rc;
-    }
-    MoeArgs a;
+    int32_t* ids = by_pred ? st->pred_ids[step % 3] + (size_t)L * K
+                           : st->exec_ids[step & 1] + (size_t)L * K;
+    float* w = by_pred ? st->pred_w[step % 3] + (size_t)L * K : st->exec_w[step & 1] + (size_t)L * K;
     int rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
                            st->y + (size_t)L * d, st->ws, &a);
     if (rc != EDGE0_OK) return rc;
-    a.h_res = hL;
-    a.h_out = st->h + (size_t)(L + 1) * d;
-    if (by_pred) {  // the first MoE launch computes x_L
-      a.h_norm = hL;
-      a.x_out = xL;
-      a.eps = st->spec.rms_eps;
+    // fixed-point y accumulators alternate between layers
+    unsigned long long* acc0 = a.acc;
+    a.acc = acc0 + (size_t)(L & 1) * d;
+    a.acc_prev = acc0 + (size_t)((L + 1) & 1) * d;
+    // layer input: the previous layer's combine + residual (L > 0), RMSNorm,
+    // then the LoRA A x rows (routing known) or the router rows
+    LayerIn li{};
+    li.flags = IN_NORM | (L > 0 ? IN_COMBINE : 0);
+    li.h_prev = L > 0 ? st->h + (size_t)(L - 1) * d : hL;
+    li.h_out = hL;
+    li.y_prev_out = L > 0 ? st->y + (size_t)(L - 1) * d : nullptr;
+    li.x_out = xL;
+    li.eps = st->spec.rms_eps;
+    if (by_pred) {
+      li.flags |= IN_LORA;
+      if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+    } else {
+      li.flags |= IN_ROUTER;
+      li.w_router = static_cast<const uint16_t*>(st->routers[L]);
+      li.logits = st->logits;
+      if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+      LayerIn l2{};
+      l2.flags = IN_TOPK | IN_LORA;
+      l2.logits = st->logits;
+      l2.ids_out = ids;
+      l2.w_out = w;
+      if ((rc = launch_layer_in(a, l2, stream)) != EDGE0_OK) return rc;
     }
     LaunchTiming lt{st->timed_kernel, nullptr, nullptr};
     if (st->timed_kernel > 0) {
       lt.start = st->ev_start[L];
       lt.stop = st->ev_stop[L];
     }
-    rc = launch_moe(a, stream, st->timed_kernel > 0 ? &lt : nullptr);
-    if (rc != EDGE0_OK) return rc;
-    if (is_owner(st->spec, L)) {
-      if (hipEventRecord(st->ev_fork[L], stream) != hipSuccess ||
-          hipStreamWaitEvent(side, st->ev_fork[L], 0) != hipSuccess)
-        return EDGE0_EHIP;
-      const int32_t* prev = nullptr;
-      if (step > 0) {
-        const bool prev_pred = is_consumer(st->spec, L) && step - 1 > 0;
-        prev = prev_pred ? st->pred_ids[(step - 1) % 3] + (size_t)L * K
-                         : st->exec_ids[(step - 1) & 1] + (size_t)L * K;
-      }
-      rc = edge0_prerouter(&sh, &st->heads[L], xL, ids, prev, nullptr,
-                           st->pred_ids[(step + 1) % 3] + (size_t)(L + 1) * K,
-                           st->pred_w[(step + 1) % 3] + (size_t)(L + 1) * K, st->ws, side);
-      if (rc != EDGE0_OK) return rc;
-    }
+    if ((rc = launch_expert_gemvs(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+      return rc;
   }
-  if (st->spec.owner_first <= st->spec.owner_last &&
-      (hipEventRecord(st->ev_join, side) != hipSuccess ||
-       hipStreamWaitEvent(stream, st->ev_join, 0) != hipSuccess))
-    return EDGE0_EHIP;
+  // the last layer's combine and residual
+  a.h_res = st->h + (size_t)(Lc - 1) * d;
+  a.h_out = st->h + (size_t)Lc * d;
+  int rc = launch_combine(a, stream);
+  if (rc != EDGE0_OK) return rc;
   k_gather_routing<<<1, 256, 0, stream>>>(st->exec_ids[step & 1], st->exec_w[step & 1],
                                           st->pred_ids[step % 3], st->pred_w[step % 3], Lc, K,
                                           st->spec.consumer_first, st->spec.consumer_last, step,
-                                          st->run_ids, st->run_w);
+                                          st->run_ids[step & 1], st->run_w[step & 1]);
   E0_CHECK_LAUNCH();
+  // every owner layer's head, batched: layer L's head reads x_L and the
+  // routing layer L executed now and at the previous step, and commits the
+  // routing of layer L+1 for the next step
+  if (st->spec.owner_first <= st->spec.owner_last) {
+    HeadBatch hb = st->heads_batch;
+    const int L0 = st->spec.owner_first;
+    hb.x = st->x + (size_t)L0 * d;
+    hb.ids_now = st->run_ids[step & 1] + (size_t)L0 * K;
+    hb.ids_prev = step > 0 ? st->run_ids[(step - 1) & 1] + (size_t)L0 * K : nullptr;
+    hb.ids_out = st->pred_ids[(step + 1) % 3] + (size_t)(L0 + 1) * K;
+    hb.w_out = st->pred_w[(step + 1) % 3] + (size_t)(L0 + 1) * K;
+    rc = launch_heads(hb, stream);
+    if (rc != EDGE0_OK) return rc;
+  }
   return EDGE0_OK;
 }
 
@@ -154,6 +166,11 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
     return EDGE0_EINVAL;
   const int Lc = spec->n_layers;
   if (Lc < 1 || spec->rms_eps < 0.f) return EDGE0_EINVAL;
+  if (spec->owner_last - spec->owner_first + 1 > kMaxHeads) return EDGE0_EINVAL;
+  // the batched heads either all carry the linear residual or none does
+  for (int L = spec->owner_first; L <= spec->owner_last; ++L)
+    if (L >= 0 && L < Lc && (heads[L].wl == nullptr) != (heads[spec->owner_first].wl == nullptr))
+      return EDGE0_EINVAL;
   // every owner L predicts consumer L+1 and every consumer has an owner
   for (int L = 0; L < Lc; ++L) {
     if (is_owner(*spec, L) && !(L + 1 < Lc && is_consumer(*spec, L + 1))) return EDGE0_EINVAL;
@@ -178,8 +195,44 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
             hipMalloc((void**)&st->y, Lc * d * 2) == hipSuccess &&
             hipMalloc((void**)&st->h, (Lc + 1) * d * 2) == hipSuccess &&
             hipMalloc(&st->ws, st->ws_bytes) == hipSuccess &&
-            hipMalloc((void**)&st->run_ids, Lc * K * 4) == hipSuccess &&
-            hipMalloc((void**)&st->run_w, Lc * K * 4) == hipSuccess;
+            hipMalloc((void**)&st->run_ids[0], Lc * K * 4) == hipSuccess &&
+            hipMalloc((void**)&st->run_ids[1], Lc * K * 4) == hipSuccess &&
+            hipMalloc((void**)&st->run_w[0], Lc * K * 4) == hipSuccess &&
+            hipMalloc((void**)&st->run_w[1], Lc * K * 4) == hipSuccess &&
+            hipMalloc((void**)&st->logits, (size_t)shape->n_experts * 4) == hipSuccess;
+  const int n_heads = spec->owner_last >= spec->owner_first ? spec->owner_last - spec->owner_first + 1 : 0;
+  const size_t E = shape->n_experts, H = shape->head_hidden;
+  ok = ok && hipMalloc((void**)&st->head_a, (n_heads + 1) * H * 4) == hipSuccess &&
+       hipMalloc((void**)&st->head_res, (n_heads + 1) * E * 4) == hipSuccess &&
+       hipMalloc((void**)&st->head_logits, (n_heads + 1) * E * 4) == hipSuccess &&
+       hipMalloc((void**)&st->head_cnt, (n_heads + 1) * 4) == hipSuccess &&
+       hipMemset(st->head_cnt, 0, (n_heads + 1) * 4) == hipSuccess;
+  if (ok && n_heads > 0) {
+    HeadBatch& hb = st->heads_batch;
+    hb.n = n_heads;
+    hb.d = shape->d_model;
+    hb.E = shape->n_experts;
+    hb.K = shape->top_k;
+    hb.H = shape->head_hidden;
+    hb.has_res = heads[spec->owner_first].wl != nullptr;
+    for (int i = 0; i < n_heads; ++i) {
+      const edge0_head& h = heads[spec->owner_first + i];
+      hb.w1x[i] = static_cast<const uint16_t*>(h.w1x);
+      hb.w1oh[i] = static_cast<const uint16_t*>(h.w1oh);
+      hb.b1[i] = static_cast<const uint16_t*>(h.b1);
+      hb.w2[i] = static_cast<const uint16_t*>(h.w2);
+      hb.b2[i] = static_cast<const uint16_t*>(h.b2);
+      hb.wl[i] = static_cast<const uint16_t*>(h.wl);
+    }
+    hb.x_stride = shape->d_model;
+    hb.ids_stride = shape->top_k;
+    hb.out_stride = shape->top_k;
+    hb.a = st->head_a;
+    hb.res = st->head_res;
+    hb.logits = st->head_logits;
+    hb.counters = st->head_cnt;
+    hb.err = reinterpret_cast<uint32_t*>(st->ws);  // the workspace error word (offset 0)
+  }
   for (int i = 0; i < 2 && ok; ++i)
     ok = hipMalloc((void**)&st->exec_ids[i], Lc * K * 4) == hipSuccess &&
          hipMalloc((void**)&st->exec_w[i], Lc * K * 4) == hipSuccess;
@@ -195,15 +248,7 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   for (int i = 0; i < 3 && ok; ++i)
     ok = hipMemset(st->pred_ids[i], 0, Lc * K * 4) == hipSuccess &&
          hipMemset(st->pred_w[i], 0, Lc * K * 4) == hipSuccess;
-  ok = ok && hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking) == hipSuccess &&
-       hipStreamCreateWithFlags(&st->cap_side, hipStreamNonBlocking) == hipSuccess &&
-       hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking) == hipSuccess &&
-       hipEventCreateWithFlags(&st->ev_join, hipEventDisableTiming) == hipSuccess;
-  for (int L = 0; L < Lc && ok; ++L) {
-    hipEvent_t e;
-    ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
-    if (ok) st->ev_fork.push_back(e);
-  }
+  ok = ok && hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     edge0_stack_destroy(st);
@@ -223,7 +268,7 @@ extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, in
   if (st->timed_kernel > 0) {
     // measurement mode: the same launches enqueued directly (events cannot be
     // timed inside a graph), each layer's chosen launch bracketed by events
-    const int rc = enqueue_step(st, step, stream, st->side);
+    const int rc = enqueue_step(st, step, stream);
     if (rc != EDGE0_OK) return rc;
     if (hipMemcpyAsync(h_out, st->h + (size_t)st->spec.n_layers * d, d * 2,
                        hipMemcpyDeviceToDevice, stream) != hipSuccess)
@@ -236,7 +281,7 @@ extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, in
     hipGraph_t g = nullptr;
     if (hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal) != hipSuccess)
       return EDGE0_EHIP;
-    const int rc = enqueue_step(st, step, st->cap, st->cap_side);
+    const int rc = enqueue_step(st, step, st->cap);
     const hipError_t ec = hipStreamEndCapture(st->cap, &g);
     if (rc != EDGE0_OK) {
       if (g) (void)hipGraphDestroy(g);
@@ -265,8 +310,8 @@ extern "C" int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffer
   out->x = st->x;
   out->y = st->y;
   out->h = st->h;
-  out->ids = st->run_ids;
-  out->w = st->run_w;
+  out->ids = st->run_ids[s & 1];
+  out->w = st->run_w[s & 1];
   out->pred_ids = st->pred_ids[(s + 1) % 3];
   out->pred_w = st->pred_w[(s + 1) % 3];
   (void)Lc;
@@ -305,16 +350,20 @@ extern "C" void edge0_stack_destroy(edge0_stack* st) {
   for (auto& g : st->graphs)
     if (g) (void)hipGraphExecDestroy(g);
   if (st->cap) (void)hipStreamDestroy(st->cap);
-  if (st->cap_side) (void)hipStreamDestroy(st->cap_side);
-  if (st->side) (void)hipStreamDestroy(st->side);
-  for (auto e : st->ev_fork) (void)hipEventDestroy(e);
-  if (st->ev_join) (void)hipEventDestroy(st->ev_join);
+
   (void)hipFree(st->x);
   (void)hipFree(st->y);
   (void)hipFree(st->h);
   (void)hipFree(st->ws);
-  (void)hipFree(st->run_ids);
-  (void)hipFree(st->run_w);
+  for (int i = 0; i < 2; ++i) {
+    (void)hipFree(st->run_ids[i]);
+    (void)hipFree(st->run_w[i]);
+  }
+  (void)hipFree(st->logits);
+  (void)hipFree(st->head_a);
+  (void)hipFree(st->head_res);
+  (void)hipFree(st->head_logits);
+  (void)hipFree(st->head_cnt);
   for (int i = 0; i < 2; ++i) {
     (void)hipFree(st->exec_ids[i]);
     (void)hipFree(st->exec_w[i]);
