@@ -34,7 +34,8 @@
 // v_dot2_f32_bf16 on exact bf16 "128 + q" nibble pairs, and the group affine
 // is applied per chunk as s * acc + (b - 128 s) * sum(x), which equals
 // sum (s q + b) x.  Everything after the loads is fp32, rounded once to bf16.
-#include <cstdlib>
+
+#include <hip/hip_ext.h>
 
 #include "moe_internal.h"
 
@@ -691,6 +692,13 @@ int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
 int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
   const int cpr = a.d / 32;
   const int grid2 = a.K * (a.I / 16);
+  if (timing && timing->which == 1 && cpr == 64) {
+    // measured launch: the dispatch itself records the events at the
+    // kernel's start and end
+    hipExtLaunchKernelGGL(k_gate_up<64>, dim3(grid2), dim3(256), 0, stream, timing->start,
+                          timing->stop, 0, a);
+    E0_CHECK_LAUNCH();
+  } else {
   E0_MARK(1, true);
   switch (cpr) {
     case 8: k_gate_up<8><<<grid2, 256, 0, stream>>>(a); break;
@@ -704,6 +712,7 @@ int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming
   }
   E0_CHECK_LAUNCH();
   E0_MARK(1, false);
+  }
   E0_MARK(2, true);
   {
     const int NC = a.I / 32, cps = (NC + a.S - 1) / a.S;
