@@ -35,7 +35,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "f64_to_bf16_bits", "unpack_int4", "dequant", "lora_proj",
     "silu", "gelu_erf", "expert_ffn", "moe_layer", "router_logits",
-    "softmax_topk", "prerouter_feature", "prerouter_logits", "prerouter_commit",
+    "softmax_topk", "softmax_at", "prerouter_feature", "prerouter_logits", "prerouter_commit",
     "rmsnorm", "stack_layer", "stack_step", "canonical_requests", "lru_replay",
     "grouped_layer", "topk_gap", "NoSlotError",
 ]
@@ -175,6 +175,17 @@ def softmax_topk(logits, k: int):
     return ids, w
 
 
+def softmax_at(logits, ids) -> np.ndarray:
+    """Weights of a routing whose ids are given rather than chosen:
+    g = softmax(l) over all experts, w = g[ids] / sum(g[ids]) (the weight
+    line of [Edge0] App. A "Softmax-topk", applied to the given set)."""
+    l = np.asarray(logits, dtype=np.float64)
+    g = np.exp(l - l.max())
+    g = g / g.sum()
+    ids = np.asarray(ids, dtype=np.int64)
+    return g[ids] / g[ids].sum()
+
+
 def topk_gap(logits, k: int) -> float:
     """Gap between the k-th and (k+1)-th largest logit (inf when k = E)."""
     s = np.sort(np.asarray(logits, dtype=np.float64))[::-1]
@@ -300,20 +311,25 @@ class NoSlotError(RuntimeError):
 
 
 def canonical_requests(n_steps: int, n_layers: int, owners=range(6, 38),
-                       consumers=range(7, 39)):
+                       consumers=range(7, 39), heads_at_end: bool = False):
     """Request/consume events in the canonical host order, per step t and
     layer L: a layer that does not consume a prediction (or any layer at
     t = 0) requests its own set right before it computes; every layer
-    consumes its set when it computes; after an owner layer L computes, the
-    set predicted for (L+1, t+1) is requested."""
+    consumes its set when it computes; once the head of owner layer L has
+    run, the set predicted for (L+1, t+1) is requested.  A head runs right
+    after its layer, or - with ``heads_at_end``, the heads of a step flushed
+    as one batch after its last layer ([Edge0] §3.2 "Head": one flush per
+    step) - after the step's last layer, in owner order."""
     ev = []
     for t in range(n_steps):
         for L in range(n_layers):
             if not (L in consumers and t > 0):
                 ev.append(("req", L, t))
             ev.append(("use", L, t))
-            if L in owners:
+            if L in owners and not heads_at_end:
                 ev.append(("req", L + 1, t + 1))
+        if heads_at_end:
+            ev.extend(("req", L + 1, t + 1) for L in owners)
     return ev
 
 

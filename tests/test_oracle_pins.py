@@ -467,6 +467,57 @@ def test_canonical_requests_order():
     assert [e for e in ev if e[2] == 1 and e[0] == "req" and e[1] >= 2] == [("req", 2, 1), ("req", 3, 1)]
 
 
+def test_canonical_requests_heads_at_end():
+    """Batched heads: a step's predicted sets are requested after its last
+    layer, in owner order; the per-layer events are otherwise unchanged."""
+    ev = O.canonical_requests(2, 4, owners=range(1, 3), consumers=range(2, 4), heads_at_end=True)
+    assert ev[:10] == [("req", 0, 0), ("use", 0, 0), ("req", 1, 0), ("use", 1, 0),
+                       ("req", 2, 0), ("use", 2, 0), ("req", 3, 0), ("use", 3, 0),
+                       ("req", 2, 1), ("req", 3, 1)]
+    # step 1: layers 2, 3 consume the sets requested at the end of step 0
+    assert ev[10:16] == [("req", 0, 1), ("use", 0, 1), ("req", 1, 1), ("use", 1, 1),
+                         ("use", 2, 1), ("use", 3, 1)]
+    # every request is used exactly once before the end, except the last
+    # step's predictions
+    reqs = [e[1:] for e in ev if e[0] == "req"]
+    uses = [e[1:] for e in ev if e[0] == "use"]
+    assert sorted(set(reqs) - set(uses)) == [(2, 2), (3, 2)]
+    assert sorted(uses) == sorted(set(uses))
+
+
+def test_lru_on_demand_order_never_pins_two_sets():
+    """With no consumers every set is requested right before its use, so at
+    most one set is pinned: a pool of exactly K slots never runs out, and
+    with K slots every request of a new layer misses entirely."""
+    E, K, L, T = 16, 4, 5, 6
+    trace = G.zipf_trace(E, K, L, T, seed=5, keep_p=0.2)
+    ev = O.canonical_requests(T, L, owners=range(0), consumers=range(0))
+    recs, tot = O.lru_replay(ev, lambda l, t: trace[t, l], K)
+    assert len(recs) == L * T
+    for r in recs:
+        assert sorted(r["slots"]) == list(range(K))
+        if L > 1:
+            assert not any(r["hit"])
+
+
+def test_softmax_at_closed_forms():
+    """w_i / w_j = exp(l_i - l_j); sum w = 1; shift invariance; on the top-K
+    ids it reproduces the committed weights."""
+    rng = np.random.default_rng(11)
+    l = rng.normal(size=32)
+    ids = np.array([5, 17, 2, 30])
+    w = O.softmax_at(l, ids)
+    assert abs(w.sum() - 1.0) < 1e-15
+    for i in range(4):
+        for j in range(4):
+            assert abs(w[i] / w[j] - math.exp(l[ids[i]] - l[ids[j]])) < 1e-12 * max(1, w[i] / w[j])
+    assert np.allclose(O.softmax_at(l + 123.0, ids), w, rtol=1e-12, atol=0)
+    tid, tw = O.softmax_topk(l, 4)
+    assert np.allclose(O.softmax_at(l, tid), tw, rtol=1e-14, atol=0)
+    # a single id gets weight 1
+    assert O.softmax_at(l, [7])[0] == 1.0
+
+
 # ---------------------------------------------------------------- grouped
 def test_grouped_is_per_token():
     shape = G.TINY
