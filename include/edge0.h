@@ -273,6 +273,115 @@ void edge0_stack_destroy(edge0_stack* st);
 int edge0_stack_set_timing(edge0_stack* st, int32_t kernel);
 int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n);
 
+/* -------------------------------------------------------------------------
+ * Expert staging ([Edge0] Figure 1: bounded streaming pool with LRU
+ * replacement and a staged fixed-slot double buffer; §3.1 "Executor paths":
+ * experts are copied into slots and the kernels index them through the slot
+ * table; §3.2 "Motivation": the next token's sets are known one token ahead,
+ * so their reads overlap compute; Table 1 caption: one LRU of bundles shared
+ * by all layers; [Cacheable] App. E: LRU replay).
+ *
+ * One pool of n_slots slots is shared by all layers.  A request names a
+ * layer L, a step t and the set of expert ids layer L will use at step t.
+ * Its ids are pinned from the request until edge0_*_release(L, t); then,
+ * in order, a resident (L, id) is a hit, a missing one takes the lowest free
+ * slot, else evicts the unpinned slot touched longest ago.  Every touched id
+ * takes the next value of one global clock, so the choice is deterministic.
+ * At most two sets of a layer (steps t and t+1) may be pending at once.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t requests;     /* sets requested */
+  int64_t touches;      /* ids requested (hits + misses) */
+  int64_t hits, misses;
+  int64_t evictions;    /* misses that replaced a resident bundle */
+  int64_t bytes_staged; /* host-to-device bytes enqueued (stager only) */
+} edge0_stage_stats;
+
+/* Host-only replacement policy (no device work), also used by the stager. */
+typedef struct edge0_lru edge0_lru;
+int edge0_lru_create(edge0_lru** out, int32_t n_slots, int32_t n_layers, int32_t n_experts);
+/* ids: host int32 [n], distinct, each in [0, n_experts); n <= 16.
+ * slots_out (host int32 [n]) receives each id's slot; hit_out (host int32
+ * [n], may be NULL) 1 for a hit; evicted_out (host int32 [n], may be NULL)
+ * the key L'*n_experts + e' whose bundle the miss replaced, or -1.
+ * EDGE0_ENOSLOT (state unchanged) when the misses exceed the free and
+ * unpinned slots; EDGE0_EINVAL for a bad id, a duplicate, or a set of
+ * (layer, step) already pending. */
+int edge0_lru_request(edge0_lru* lru, int32_t layer, int32_t step, const int32_t* ids,
+                      int32_t n, int32_t* slots_out, int32_t* hit_out, int32_t* evicted_out);
+/* Unpins the set of (layer, step); EDGE0_EINVAL if it is not pending. */
+int edge0_lru_release(edge0_lru* lru, int32_t layer, int32_t step);
+int edge0_lru_stats(const edge0_lru* lru, edge0_stage_stats* out);
+void edge0_lru_destroy(edge0_lru* lru);
+
+/* The stager: the same policy plus the data movement.
+ *   pool         : the device slot pool (pool.slot_bytes >= the bundle
+ *                  layout's bytes)
+ *   host_bundles : host array [n_layers * n_experts]; entry L*E + e points to
+ *                  the bundle of (L, e) in the device bundle layout, in pinned
+ *                  host memory (hipHostMalloc), layout.bytes bytes.  Kept,
+ *                  not copied: it must outlive the handle.
+ *   slot_table   : device int32 [n_layers][n_experts]; the stager sets it to
+ *                  -1 at create and keeps it equal to the pool's content
+ *                  (id -> slot, -1 when not resident), written on the streams
+ *                  that stage.
+ * The handle owns its policy state and HIP events (released by destroy). */
+typedef struct edge0_stager edge0_stager;
+int edge0_stager_create(edge0_stager** out, const edge0_moe_shape* shape,
+                        const edge0_slot_pool* pool, int32_t n_layers,
+                        const void* const* host_bundles, int32_t* slot_table);
+/* Request (layer, step, ids) and enqueue on `stream` the copies of the
+ * missing bundles into their slots and the slot-table update: on a side
+ * stream this prefetches (the copies overlap whatever the compute stream
+ * runs), on the compute stream it is a blocking on-demand fill.  A copy
+ * into a slot that a layer read before first waits for that layer's
+ * release point; a hit on a slot being filled on another stream waits for
+ * that fill.  slots_out: host int32 [n] or NULL. */
+int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step, const int32_t* ids,
+                        int32_t n, int32_t* slots_out, hipStream_t stream);
+/* Makes compute_stream wait until the set of (layer, step) is in its slots
+ * (no-op when it was staged on compute_stream itself). */
+int edge0_stager_wait(edge0_stager* sg, int32_t layer, int32_t step, hipStream_t compute_stream);
+/* Marks the point on compute_stream after the last kernel reading the set
+ * of (layer, step) and unpins it: later copies into its slots wait for
+ * that point. */
+int edge0_stager_release(edge0_stager* sg, int32_t layer, int32_t step,
+                         hipStream_t compute_stream);
+int edge0_stager_stats(const edge0_stager* sg, edge0_stage_stats* out);
+void edge0_stager_destroy(edge0_stager* sg);
+
+/* One decode step of the stack over a staged pool, with the routing ids of
+ * every layer given (a routing trace): the weights are the softmax of the
+ * layer's own logits taken at the given ids, w = g[ids] / sum g[ids]
+ * ([Edge0] App. A), from the plain router of the layer or, for a
+ * prediction-routed layer, from the logits its head produced at the
+ * previous step.
+ *   ahead = 1 (prediction arm): prediction-routed layers (step > 0) use sets
+ *     staged one step ahead on copy_stream; every other layer runs its
+ *     router, then fills its own set on demand on `stream`.  After the
+ *     step's batched heads, the sets of the next step's prediction-routed
+ *     layers (next_ids_host) are requested on copy_stream, which first
+ *     waits for the heads ("one flush per step").
+ *   ahead = 0 (on-demand arm): every layer runs its router and then fills
+ *     its set on demand on `stream`; no heads run.
+ *   ids_dev  : device int32 [n_layers][K], the routing of this step
+ *   ids_host : host int32 [n_layers][K], the same ids
+ *   next_ids_host : host int32 [n_layers][K], the routing of step + 1 (ahead
+ *     = 1; NULL on the last step: nothing is prefetched)
+ * The stack must have been created on the stager's pool and slot table.
+ * Enqueued directly (not as a graph).  The requests follow the canonical
+ * order: per layer its own request (if any) before it computes and its
+ * release after; the next step's predicted sets after the last layer. */
+typedef struct {
+  const int32_t* ids_dev;
+  const int32_t* ids_host;
+  const int32_t* next_ids_host;
+  int32_t ahead;
+  hipStream_t copy_stream;
+} edge0_stage_plan;
+int edge0_stack_step_staged(edge0_stack* st, edge0_stager* sg, const edge0_stage_plan* plan,
+                            const void* h0, void* h_out, int32_t step, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

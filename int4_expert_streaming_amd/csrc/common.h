@@ -281,6 +281,29 @@ __device__ __forceinline__ void wave_topk(const float* logits, int E, int K, int
   }
 }
 
+// Weights of a routing whose ids are given: w_k = exp(l[id_k] - m) /
+// sum_j exp(l[id_j] - m), m the largest of the K logits (g[ids] / sum g[ids]
+// for g = softmax(l)).  Lanes 0..K-1 of one wave; an id outside [0, E) gets
+// weight 0 and records EDGE0_ERANGE.
+__device__ __forceinline__ void wave_softmax_at(const float* logits, const int32_t* ids, int E,
+                                                int K, float* w_out, uint32_t* err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float v = -INFINITY;
+  bool ok = true;
+  if (lane < K) {
+    const int id = ids[lane];
+    ok = id >= 0 && id < E;
+    if (ok) v = logits[id];
+  }
+  float m = -INFINITY;
+  for (int j = 0; j < K; ++j) m = fmaxf(m, __shfl(v, j, kWave));
+  const float ex = (lane < K && ok) ? expf(v - m) : 0.f;
+  float den = 0.f;
+  for (int j = 0; j < K; ++j) den += __shfl(ex, j, kWave);  // fixed order
+  if (lane < K) w_out[lane] = den > 0.f ? ex / den : 0.f;
+  if (lane < K && !ok) atomicOr(err, (uint32_t)(-EDGE0_ERANGE));
+}
+
 // Completion counting across workgroups.  Data that the last workgroup will
 // read must have been written with st_dev.  Every wave waits for its stores
 // to complete, the workgroup synchronises, and one atomic per workgroup

@@ -150,6 +150,8 @@ __global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
     }
     ids = ids_s;
   }
+  if ((li.flags & IN_GATHER) && blockIdx.x == 0 && wave == 0)
+    wave_softmax_at(li.logits, a.ids, a.E, K, li.w_out, a.err);
   if (lora && blockIdx.x == 0 && tid < K) a.slots[tid] = resolve_slot(a, ids[tid]);
   if (!lora && !router && blockIdx.x == 0 && tid < K) a.slots[tid] = resolve_slot(a, ids[tid]);
   if (!active) return;

@@ -46,8 +46,10 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
 //   IN_ROUTER:  router logits rows
 //   IN_TOPK:    softmax-top-K of `logits` (computed by every workgroup)
 //   IN_LORA:    t = A x rows of the K experts' gate/up adapters
+//   IN_GATHER:  routing ids given (a.ids); w = softmax of `logits` taken at
+//               those ids, stored to w_out
 // Workgroup 0 stores h, y_prev, x, the committed ids/w and the slots.
-enum { IN_COMBINE = 1, IN_NORM = 2, IN_ROUTER = 4, IN_TOPK = 8, IN_LORA = 16 };
+enum { IN_COMBINE = 1, IN_NORM = 2, IN_ROUTER = 4, IN_TOPK = 8, IN_LORA = 16, IN_GATHER = 32 };
 struct LayerIn {
   int flags;
   const uint16_t* h_prev;
@@ -99,6 +101,11 @@ struct HeadBatch {
   uint32_t* err;
 };
 int launch_heads(const HeadBatch& hb, hipStream_t stream);
+
+// what the stack runtime needs to know of a stager
+edge0_slot_pool stager_pool(const edge0_stager* sg);
+const int32_t* stager_table(const edge0_stager* sg);
+int stager_layers(const edge0_stager* sg);
 
 int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
                   const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,

@@ -68,6 +68,7 @@ struct edge0_stack {
   int timed_kernel;          // measurement aid: which launch class carries events
   std::vector<hipEvent_t> ev_start, ev_stop;  // one pair per layer
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
+  hipEvent_t ev_heads;       // staged steps: the heads of the step have run
 };
 
 static bool is_consumer(const edge0_stack_spec& s, int L) {
@@ -303,6 +304,132 @@ extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, in
   return EDGE0_OK;
 }
 
+// ----------------------------------------------------------- staged step
+// host ids of every layer: in range and distinct (checked before anything
+// is enqueued)
+static bool ids_ok(const int32_t* ids, int n_layers, int K, int E) {
+  for (int L = 0; L < n_layers; ++L)
+    for (int i = 0; i < K; ++i) {
+      const int32_t v = ids[L * K + i];
+      if (v < 0 || v >= E) return false;
+      for (int j = 0; j < i; ++j)
+        if (ids[L * K + j] == v) return false;
+    }
+  return true;
+}
+
+static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_stage_plan& plan,
+                               int step, hipStream_t stream) {
+  const edge0_moe_shape& sh = st->shape;
+  const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers, E = sh.n_experts;
+  const bool ahead = plan.ahead != 0;
+  float* w_exec = st->exec_w[step & 1];
+  MoeArgs a{};
+  int rc;
+  for (int L = 0; L < Lc; ++L) {
+    uint16_t* hL = st->h + (size_t)L * d;
+    uint16_t* xL = st->x + (size_t)L * d;
+    const bool by_pred = ahead && is_consumer(st->spec, L) && step > 0;
+    const int32_t* ids = plan.ids_dev + (size_t)L * K;
+    float* w = w_exec + (size_t)L * K;
+    rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
+                       st->y + (size_t)L * d, st->ws, &a);
+    if (rc != EDGE0_OK) return rc;
+    unsigned long long* acc0 = a.acc;
+    a.acc = acc0 + (size_t)(L & 1) * d;
+    a.acc_prev = acc0 + (size_t)((L + 1) & 1) * d;
+    LayerIn li{};
+    li.flags = IN_NORM | (L > 0 ? IN_COMBINE : 0);
+    li.h_prev = L > 0 ? st->h + (size_t)(L - 1) * d : hL;
+    li.h_out = hL;
+    li.y_prev_out = L > 0 ? st->y + (size_t)(L - 1) * d : nullptr;
+    li.x_out = xL;
+    li.eps = st->spec.rms_eps;
+    if (by_pred) {
+      // the set was staged one step ahead: wait for its copies, weights
+      // from the logits the owner's head produced at the previous step
+      if ((rc = edge0_stager_wait(sg, L, step, stream)) != EDGE0_OK) return rc;
+      li.flags |= IN_GATHER | IN_LORA;
+      li.logits = st->head_logits + (size_t)(L - 1 - st->spec.owner_first) * E;
+      li.w_out = w;
+      if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+    } else {
+      // router first; the set is known once it ran: fill it on demand on the
+      // compute stream, then the weights and the LoRA A x rows
+      li.flags |= IN_ROUTER;
+      li.w_router = static_cast<const uint16_t*>(st->routers[L]);
+      li.logits = st->logits;
+      if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+      if ((rc = edge0_stage_experts(sg, L, step, plan.ids_host + (size_t)L * K, K, nullptr,
+                                    stream)) != EDGE0_OK)
+        return rc;
+      LayerIn l2{};
+      l2.flags = IN_GATHER | IN_LORA;
+      l2.logits = st->logits;
+      l2.w_out = w;
+      if ((rc = launch_layer_in(a, l2, stream)) != EDGE0_OK) return rc;
+    }
+    if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
+    if ((rc = edge0_stager_release(sg, L, step, stream)) != EDGE0_OK) return rc;
+  }
+  a.h_res = st->h + (size_t)(Lc - 1) * d;
+  a.h_out = st->h + (size_t)Lc * d;
+  if ((rc = launch_combine(a, stream)) != EDGE0_OK) return rc;
+  // every layer executed the given ids
+  k_gather_routing<<<1, 256, 0, stream>>>(plan.ids_dev, w_exec, plan.ids_dev, w_exec, Lc, K, 1, 0,
+                                          step, st->run_ids[step & 1], st->run_w[step & 1]);
+  E0_CHECK_LAUNCH();
+  if (!ahead || st->spec.owner_first > st->spec.owner_last) return EDGE0_OK;
+  HeadBatch hb = st->heads_batch;
+  const int L0 = st->spec.owner_first;
+  hb.x = st->x + (size_t)L0 * d;
+  hb.ids_now = st->run_ids[step & 1] + (size_t)L0 * K;
+  hb.ids_prev = step > 0 ? st->run_ids[(step - 1) & 1] + (size_t)L0 * K : nullptr;
+  hb.ids_out = st->pred_ids[(step + 1) % 3] + (size_t)(L0 + 1) * K;
+  hb.w_out = st->pred_w[(step + 1) % 3] + (size_t)(L0 + 1) * K;
+  if ((rc = launch_heads(hb, stream)) != EDGE0_OK) return rc;
+  if (!plan.next_ids_host) return EDGE0_OK;
+  // the next step's predicted sets, known once the heads ran
+  if (!st->ev_heads &&
+      hipEventCreateWithFlags(&st->ev_heads, hipEventDisableTiming) != hipSuccess)
+    return EDGE0_EHIP;
+  if (hipEventRecord(st->ev_heads, stream) != hipSuccess ||
+      hipStreamWaitEvent(plan.copy_stream, st->ev_heads, 0) != hipSuccess)
+    return EDGE0_EHIP;
+  for (int L = st->spec.owner_first; L <= st->spec.owner_last; ++L)
+    if ((rc = edge0_stage_experts(sg, L + 1, step + 1, plan.next_ids_host + (size_t)(L + 1) * K,
+                                  K, nullptr, plan.copy_stream)) != EDGE0_OK)
+      return rc;
+  return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_step_staged(edge0_stack* st, edge0_stager* sg,
+                                       const edge0_stage_plan* plan, const void* h0, void* h_out,
+                                       int32_t step, hipStream_t stream) {
+  if (!st || !sg || !plan || !plan->ids_dev || !plan->ids_host || !h0 || !h_out || step < 0)
+    return EDGE0_EINVAL;
+  if (plan->ahead != 0 && plan->ahead != 1) return EDGE0_EINVAL;
+  if (step != 0 && step != st->last_step + 1) return EDGE0_EINVAL;
+  const edge0_slot_pool sp = stager_pool(sg);
+  const int Lc = st->spec.n_layers, K = st->shape.top_k, E = st->shape.n_experts;
+  if (sp.base != st->pool.base || sp.slot_bytes != st->pool.slot_bytes ||
+      sp.n_slots != st->pool.n_slots || stager_table(sg) != st->tables || stager_layers(sg) != Lc)
+    return EDGE0_EINVAL;
+  if (!ids_ok(plan->ids_host, Lc, K, E)) return EDGE0_EINVAL;
+  if (plan->ahead && plan->next_ids_host && !ids_ok(plan->next_ids_host, Lc, K, E))
+    return EDGE0_EINVAL;
+  const size_t d = st->shape.d_model;
+  if (hipMemcpyAsync(st->h, h0, d * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return EDGE0_EHIP;
+  const int rc = enqueue_staged_step(st, sg, *plan, step, stream);
+  if (rc != EDGE0_OK) return rc;
+  if (hipMemcpyAsync(h_out, st->h + (size_t)Lc * d, d * 2, hipMemcpyDeviceToDevice, stream) !=
+      hipSuccess)
+    return EDGE0_EHIP;
+  st->last_step = step;
+  return EDGE0_OK;
+}
+
 extern "C" int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffers* out) {
   if (!st || !out || st->last_step < 0) return EDGE0_EINVAL;
   const int s = st->last_step;
@@ -350,6 +477,7 @@ extern "C" void edge0_stack_destroy(edge0_stack* st) {
   for (auto& g : st->graphs)
     if (g) (void)hipGraphExecDestroy(g);
   if (st->cap) (void)hipStreamDestroy(st->cap);
+  if (st->ev_heads) (void)hipEventDestroy(st->ev_heads);
 
   (void)hipFree(st->x);
   (void)hipFree(st->y);

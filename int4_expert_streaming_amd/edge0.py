@@ -75,7 +75,18 @@ class StackBuffers(C.Structure):
                 ("w", C.c_void_p), ("pred_ids", C.c_void_p), ("pred_w", C.c_void_p)]
 
 
+class StageStats(C.Structure):
+    _fields_ = [("requests", C.c_int64), ("touches", C.c_int64), ("hits", C.c_int64),
+                ("misses", C.c_int64), ("evictions", C.c_int64), ("bytes_staged", C.c_int64)]
+
+
+class StagePlan(C.Structure):
+    _fields_ = [("ids_dev", C.c_void_p), ("ids_host", C.c_void_p), ("next_ids_host", C.c_void_p),
+                ("ahead", C.c_int32), ("copy_stream", C.c_void_p)]
+
+
 _P = C.c_void_p
+_I32P = C.POINTER(C.c_int32)
 _SIG = {
     "edge0_strerror": (C.c_char_p, [C.c_int]),
     "edge0_bundle_layout_of": (C.c_int, [C.POINTER(MoeShape), C.POINTER(BundleLayout)]),
@@ -95,6 +106,20 @@ _SIG = {
     "edge0_stack_set_timing": (C.c_int, [_P, C.c_int32]),
     "edge0_stack_kernel_ms": (C.c_int, [_P, C.POINTER(C.c_float), C.c_int32,
                                         C.POINTER(C.c_int32)]),
+    "edge0_stack_step_staged": (C.c_int, [_P, _P, C.POINTER(StagePlan), _P, _P, C.c_int32, _P]),
+    "edge0_lru_create": (C.c_int, [C.POINTER(_P), C.c_int32, C.c_int32, C.c_int32]),
+    "edge0_lru_request": (C.c_int, [_P, C.c_int32, C.c_int32, _I32P, C.c_int32, _I32P, _I32P,
+                                    _I32P]),
+    "edge0_lru_release": (C.c_int, [_P, C.c_int32, C.c_int32]),
+    "edge0_lru_stats": (C.c_int, [_P, C.POINTER(StageStats)]),
+    "edge0_lru_destroy": (None, [_P]),
+    "edge0_stager_create": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.POINTER(SlotPool),
+                                      C.c_int32, C.POINTER(_P), _P]),
+    "edge0_stage_experts": (C.c_int, [_P, C.c_int32, C.c_int32, _I32P, C.c_int32, _I32P, _P]),
+    "edge0_stager_wait": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
+    "edge0_stager_release": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
+    "edge0_stager_stats": (C.c_int, [_P, C.POINTER(StageStats)]),
+    "edge0_stager_destroy": (None, [_P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -240,6 +265,110 @@ class Stack:
             self.close()
         except Exception:
             pass
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+def _stats(s: StageStats) -> dict:
+    return {k: int(getattr(s, k)) for k, _ in StageStats._fields_}
+
+
+class Lru:
+    """Host-only slot replacement policy (edge0_lru_*)."""
+
+    def __init__(self, n_slots: int, n_layers: int, n_experts: int):
+        self._handle = C.c_void_p()
+        _check(lib.edge0_lru_create(C.byref(self._handle), n_slots, n_layers, n_experts),
+               "edge0_lru_create")
+
+    def request(self, layer: int, step: int, ids):
+        """-> (slots, hit flags, evicted keys), each an int32 array."""
+        ids = _i32(ids)
+        n = ids.shape[0]
+        slots, hit, ev = (np.zeros(n, np.int32) for _ in range(3))
+        _check(lib.edge0_lru_request(self._handle, layer, step, _i32p(ids), n, _i32p(slots),
+                                     _i32p(hit), _i32p(ev)), "edge0_lru_request")
+        return slots, hit, ev
+
+    def release(self, layer: int, step: int):
+        _check(lib.edge0_lru_release(self._handle, layer, step), "edge0_lru_release")
+
+    def stats(self) -> dict:
+        s = StageStats()
+        _check(lib.edge0_lru_stats(self._handle, C.byref(s)), "edge0_lru_stats")
+        return _stats(s)
+
+    def close(self):
+        if self._handle:
+            lib.edge0_lru_destroy(self._handle)
+            self._handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Stager:
+    """Owner of an edge0_stager handle: the LRU pool plus host-to-device staging."""
+
+    def __init__(self, shape: MoeShape, pool: SlotPool, n_layers: int, host_ptrs, slot_table):
+        self._keep = (host_ptrs, slot_table)
+        arr = (C.c_void_p * len(host_ptrs))(*host_ptrs)
+        self._handle = C.c_void_p()
+        _check(lib.edge0_stager_create(C.byref(self._handle), C.byref(shape), C.byref(pool),
+                                       n_layers, arr, _ptr(slot_table)), "edge0_stager_create")
+
+    def stage(self, layer: int, step: int, ids, stream=None) -> np.ndarray:
+        ids = _i32(ids)
+        slots = np.zeros(ids.shape[0], np.int32)
+        _check(lib.edge0_stage_experts(self._handle, layer, step, _i32p(ids), ids.shape[0],
+                                       _i32p(slots), _stream(stream)), "edge0_stage_experts")
+        return slots
+
+    def wait(self, layer: int, step: int, stream=None):
+        _check(lib.edge0_stager_wait(self._handle, layer, step, _stream(stream)),
+               "edge0_stager_wait")
+
+    def release(self, layer: int, step: int, stream=None):
+        _check(lib.edge0_stager_release(self._handle, layer, step, _stream(stream)),
+               "edge0_stager_release")
+
+    def stats(self) -> dict:
+        s = StageStats()
+        _check(lib.edge0_stager_stats(self._handle, C.byref(s)), "edge0_stager_stats")
+        return _stats(s)
+
+    def close(self):
+        if self._handle:
+            lib.edge0_stager_destroy(self._handle)
+            self._handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def stack_step_staged(stack: "Stack", stager: Stager, h0, h_out, step: int, ids_dev, ids_host,
+                      next_ids_host, ahead: bool, copy_stream, stream=None):
+    """One staged decode step (edge0_stack_step_staged).  ids_host and
+    next_ids_host are int32 numpy arrays [n_layers][K] (next may be None)."""
+    ids_host = _i32(ids_host)
+    nxt = None if next_ids_host is None else _i32(next_ids_host)
+    plan = StagePlan(_ptr(ids_dev), ids_host.ctypes.data, None if nxt is None else nxt.ctypes.data,
+                     1 if ahead else 0, _stream(copy_stream))
+    _check(lib.edge0_stack_step_staged(stack._handle, stager._handle, C.byref(plan), _ptr(h0),
+                                       _ptr(h_out), step, _stream(stream)),
+           "edge0_stack_step_staged")
 
 
 _hip = C.CDLL("libamdhip64.so")

@@ -51,16 +51,82 @@ class DeviceStack:
 
     def _pack_layer(self, L, parts):
         En = self.S.n_experts
-        keys = list(parts[0][0].keys()) + (list(parts[0][1].keys()) if parts[0][1] else [])
-        stacked = {}
-        for k in keys:
-            src = [p[0][k] if k in p[0] else p[1][k] for p in parts]
-            stacked[k] = to_device(np.stack(src))
-        for e in range(En):
-            E.edge0_pack_bundle(self.sh, {k: v[e] for k, v in stacked.items()},
-                                self.pool.slot_ptr(L * En + e))
-        torch.cuda.synchronize()
-        del stacked
+        pack_layer(self.sh, parts, lambda e: self.pool.slot_ptr(L * En + e))
 
     def step(self, h0, h_out, step):
         self.stack.step(h0, h_out, step)
+
+
+def pack_layer(sh, parts, dst_of):
+    """Packs one layer's experts (parts[e] = (expert arrays, lora arrays))
+    into the device bundles at dst_of(e)."""
+    keys = list(parts[0][0].keys()) + (list(parts[0][1].keys()) if parts[0][1] else [])
+    stacked = {}
+    for k in keys:
+        src = [p[0][k] if k in p[0] else p[1][k] for p in parts]
+        stacked[k] = to_device(np.stack(src))
+    for e in range(len(parts)):
+        E.edge0_pack_bundle(sh, {k: v[e] for k, v in stacked.items()}, dst_of(e))
+    torch.cuda.synchronize()
+
+
+class HostBundles:
+    """Every (layer, expert) bundle in the device bundle layout, in pinned
+    host memory (the source tier of the staged pool): packed on the device
+    one layer at a time and copied back."""
+
+    def __init__(self, shape, gen, n_layers, threads=16, log=print):
+        self.sh = E.make_shape(shape)
+        En = shape.n_experts
+        self.bundle_bytes = int(E.edge0_bundle_layout_of(self.sh).bytes)
+        bb = self.bundle_bytes
+        self.mem = torch.empty(n_layers * En * bb, dtype=torch.uint8, pin_memory=True)
+        tmp = SlotPoolBuffer(self.sh, En)
+        t0 = time.time()
+        with ThreadPoolExecutor(threads) as ex:
+            for L in range(n_layers):
+                parts = list(ex.map(lambda e: (gen.expert(L, e), gen.lora(L, e)), range(En)))
+                pack_layer(self.sh, parts, tmp.slot_ptr)
+                self.mem[L * En * bb:(L + 1) * En * bb].copy_(tmp.mem[:En * bb])
+                if log and (L % 8 == 7 or L == n_layers - 1):
+                    log(f"[host] packed layer {L + 1}/{n_layers} ({time.time() - t0:.1f}s)")
+        del tmp
+        base = self.mem.data_ptr()
+        self.ptrs = [base + k * bb for k in range(n_layers * En)]
+
+    def bundle(self, L, e, n_experts):
+        k = L * n_experts + e
+        return self.mem[k * self.bundle_bytes:(k + 1) * self.bundle_bytes]
+
+
+class StreamedStack:
+    """The decode stack over a bounded HBM pool of n_slots slots, staged from
+    pinned host bundles by the library's stager, routed by a given trace."""
+
+    def __init__(self, shape, gen, n_layers, owners, consumers, n_slots, eps=1e-6, threads=16,
+                 log=print, host=None):
+        self.S = shape
+        self.sh = E.make_shape(shape)
+        En = shape.n_experts
+        self.n_layers = n_layers
+        self.spec = E.StackSpec(n_layers, owners[0], owners[1], consumers[0], consumers[1], eps)
+        self.owners = range(owners[0], owners[1] + 1)
+        self.consumers = range(consumers[0], consumers[1] + 1)
+        self.host = host if host is not None else HostBundles(shape, gen, n_layers, threads, log)
+        self.pool = SlotPoolBuffer(self.sh, n_slots)
+        self.table = torch.full((n_layers, En), -1, dtype=torch.int32, device="cuda")
+        with ThreadPoolExecutor(threads) as ex:
+            routers = list(ex.map(gen.router, range(n_layers)))
+            heads = list(ex.map(lambda L: gen.head(L) if L in self.owners else None,
+                                range(n_layers)))
+        self.routers = [to_device(r) for r in routers]
+        self.heads = [None if h is None else head_to_device(h) for h in heads]
+        torch.cuda.synchronize()
+        self.stack = E.Stack(self.sh, self.spec, self.pool.pool, self.table, self.routers,
+                             self.heads)
+        self.stager = E.Stager(self.sh, self.pool.pool, n_layers, self.host.ptrs, self.table)
+        self.copy_stream = torch.cuda.Stream()
+
+    def step(self, h0, h_out, step, ids_dev, ids_host, next_ids_host, ahead=True):
+        E.stack_step_staged(self.stack, self.stager, h0, h_out, step, ids_dev, ids_host,
+                            next_ids_host, ahead, self.copy_stream)

@@ -82,3 +82,25 @@ def test_workspace_sizes(E):
     for S in (G.TINY, G.QWEN3_MOE, G.QWEN3_MOE.with_k(8)):
         n = E.edge0_workspace_bytes(E.make_shape(S))
         assert 0 < n < 8 << 20
+
+
+def test_staging_calls_reject_null_arguments(E):
+    """Stager and staged-step entry points check their arguments before any
+    device work (no GPU needed)."""
+    import ctypes as C
+    from synth import gen as G
+    sh = E.make_shape(G.TINY)
+    h = C.c_void_p()
+    pool = E.SlotPool(None, 1 << 20, 4)
+    assert E.lib.edge0_stager_create(C.byref(h), C.byref(sh), C.byref(pool), 2, None, None) == \
+        E.EDGE0_EINVAL
+    ids = (C.c_int32 * 4)(0, 1, 2, 3)
+    assert E.lib.edge0_stage_experts(None, 0, 0, ids, 4, None, None) == E.EDGE0_EINVAL
+    assert E.lib.edge0_stager_wait(None, 0, 0, None) == E.EDGE0_EINVAL
+    assert E.lib.edge0_stager_release(None, 0, 0, None) == E.EDGE0_EINVAL
+    plan = E.StagePlan(None, None, None, 1, None)
+    assert E.lib.edge0_stack_step_staged(None, None, C.byref(plan), None, None, 0, None) == \
+        E.EDGE0_EINVAL
+    st = E.StageStats()
+    assert E.lib.edge0_stager_stats(None, C.byref(st)) == E.EDGE0_EINVAL
+    assert E.lib.edge0_lru_create(C.byref(h), 0, 1, 8) == E.EDGE0_EINVAL

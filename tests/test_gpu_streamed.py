@@ -1,0 +1,127 @@
+"""GPU parity of the staged decode stack (edge0_stager_* and
+edge0_stack_step_staged) against the oracle.
+
+Routing comes from a seeded Zipf trace; each layer's weights are the softmax
+of its own logits taken at the trace ids (plain router, or - prediction arm,
+step > 0, prediction-routed layer - the logits its owner's head produced at
+the previous step).  After every step:
+  * the device slot table equals the oracle LRU replay's resident map for
+    the same canonical request order, bit-exact, and the stager's counters
+    equal the replay's;
+  * every resident slot holds the bytes of its host bundle;
+  * every checked layer matches the oracle teacher-forced (the GPU's hidden
+    state entering the layer): x, weights (rel 1e-5), y (rel-L2 2e-3), h."""
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import gen as G
+from tests.layer_setup import REL_L2_MAX, W_REL_MAX, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _resident(events, ids_of, n_slots, n_layers, n_experts):
+    """The oracle's id -> slot map after the events, as a [L][E] table."""
+    recs, tot = O.lru_replay(events, ids_of, n_slots)
+    owner = {}
+    for r in recs:
+        for e, s in zip(r["ids"], r["slots"]):
+            owner[s] = (r["L"], e)
+    table = np.full((n_layers, n_experts), -1, np.int32)
+    for s, (L, e) in owner.items():
+        table[L, e] = s
+    return table, tot
+
+
+def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of, keep_p=0.1):
+    import torch
+    from int4_expert_streaming_amd.stackbuild import StreamedStack
+    from int4_expert_streaming_amd.weights import to_device
+    gen = G.StackGen(S, seed)
+    En, K = S.n_experts, S.top_k
+    ss = StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
+    trace = G.zipf_trace(En, K, n_layers, steps + 1, seed + 100, keep_p=keep_p)
+    trace_dev = torch.from_numpy(trace).cuda()
+    own = range(owners[0], owners[1] + 1) if ahead else range(0)
+    con = range(consumers[0], consumers[1] + 1) if ahead else range(0)
+    ids_of = lambda L, t: trace[t, L]
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    router = {L: gen.router(L) for L in range(n_layers)}
+    head = {L: gen.head(L) for L in own}
+    prev_x = None
+    worst = 0.0
+    for t in range(steps):
+        print(f"[streamed] ahead={ahead} step {t}", flush=True)
+        h0 = G.stack_hidden(S, seed, t)
+        ss.step(to_device(h0), h_out, t, trace_dev[t], trace[t], trace[t + 1] if ahead else None,
+                ahead)
+        torch.cuda.synchronize()
+        # slot table and counters against the replay of the same requests
+        ev = O.canonical_requests(t + 1, n_layers, own, con, heads_at_end=True)
+        want, tot = _resident(ev, ids_of, n_slots, n_layers, En)
+        got = ss.table.cpu().numpy()
+        assert np.array_equal(got, want), (t, np.argwhere(got != want)[:8])
+        st = ss.stager.stats()
+        assert (st["hits"], st["misses"]) == (tot["hits"], tot["misses"]), (st, tot)
+        assert st["bytes_staged"] == st["misses"] * ss.host.bundle_bytes
+        # resident slots hold their bundles
+        pool = ss.pool.mem.view(n_slots, -1)
+        for L, e in zip(*np.nonzero(want >= 0)):
+            if (L + e + t) % 7 == 0 or S.d_model <= 256:
+                s = int(want[L, e])
+                assert torch.equal(pool[s].cpu(), ss.host.bundle(int(L), int(e), En)), (L, e, s)
+        # layers, teacher-forced
+        b = ss.stack.buffers()
+        snap = {k: v.cpu().numpy() for k, v in b.items()}
+        hh, xx, yy = (snap[k].view(np.uint16) for k in ("h", "x", "y"))
+        assert np.array_equal(hh[0], h0)
+        assert np.array_equal(snap["ids"], trace[t])
+        for L in layers_of(t):
+            x_o = O.f64_to_bf16_bits(O.rmsnorm(O.bf16_to_f64(hh[L])))
+            diff = np.abs(x_o.astype(np.int32) - xx[L].astype(np.int32))
+            assert diff.max() <= 1 and np.count_nonzero(diff) <= max(2, S.d_model // 200)
+            ids = trace[t, L]
+            if ahead and L in con and t > 0:
+                logits = O.prerouter_logits(head[L - 1], prev_x[L - 1], trace[t - 1, L - 1],
+                                            trace[t - 2, L - 1] if t >= 2 else None, En)
+            else:
+                logits = O.router_logits(router[L], xx[L])
+            w_o = O.softmax_at(logits, ids)
+            assert np.max(np.abs(snap["w"][L] - w_o) / np.abs(w_o)) <= W_REL_MAX, (L, t)
+            ex = {int(e): gen.expert(L, int(e)) for e in ids}
+            lo = {int(e): gen.lora(L, int(e)) for e in ids}
+            y_o = O.moe_layer(ex, ids, w_o, xx[L], S.group, lo, S.lora_alpha / S.lora_rank)
+            rel = rel_l2(O.bf16_to_f64(yy[L]), y_o)
+            worst = max(worst, rel)
+            assert rel <= REL_L2_MAX, (L, t, rel)
+            h_next = O.f64_to_bf16_bits(O.bf16_to_f64(hh[L]) + O.bf16_to_f64(yy[L]))
+            assert np.array_equal(h_next, hh[L + 1]), (L, t)
+        prev_x = xx.copy()
+    return ss, worst
+
+
+@pytest.mark.parametrize("ahead", [True, False])
+def test_small_streamed_stack_every_layer(torch_cuda, ahead):
+    """10 tiny layers, a 40-slot pool (160 bundles: constant eviction)."""
+    ss, worst = _run(G.TINY, 5, 10, (2, 7), (3, 8), 40, 6, ahead, lambda t: range(10))
+    print(f"[streamed] tiny ahead={ahead}: worst rel-L2 {worst:.3e}, {ss.stager.stats()}")
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_streamed_stack_sampled_layers(torch_cuda):
+    """12 Qwen3-MoE-shaped layers over a 64-slot pool (at most 36 pinned),
+    prediction arm: evictions from the second step on."""
+    sample = {0: [0, 2, 3, 11], 1: [2, 3, 4, 10], 2: [3, 6, 9, 11], 3: [1, 3, 8, 10]}
+    ss, worst = _run(G.QWEN3_MOE, 1, 12, (2, 9), (3, 10), 64, 4, True, lambda t: sample[t],
+                     keep_p=0.06)
+    assert ss.stager.stats()["evictions"] > 0
+    print(f"[streamed] qwen3moe: worst rel-L2 {worst:.3e}, {ss.stager.stats()}")
