@@ -319,29 +319,36 @@ void edge0_lru_destroy(edge0_lru* lru);
  *                  layout's bytes)
  *   host_bundles : host array [n_layers * n_experts]; entry L*E + e points to
  *                  the bundle of (L, e) in the device bundle layout, in pinned
- *                  host memory (hipHostMalloc), layout.bytes bytes.  Kept,
- *                  not copied: it must outlive the handle.
+ *                  host memory the device can read (hipHostMalloc), 16-byte
+ *                  aligned, layout.bytes bytes; EDGE0_EINVAL otherwise.  The
+ *                  memory must outlive the handle (the array is copied).
  *   slot_table   : device int32 [n_layers][n_experts]; the stager sets it to
  *                  -1 at create and keeps it equal to the pool's content
- *                  (id -> slot, -1 when not resident), written on the streams
- *                  that stage.
+ *                  (id -> slot, -1 when not resident) as of the last wait or
+ *                  flush on the compute stream.
  * The handle owns its policy state and HIP events (released by destroy). */
 typedef struct edge0_stager edge0_stager;
 int edge0_stager_create(edge0_stager** out, const edge0_moe_shape* shape,
                         const edge0_slot_pool* pool, int32_t n_layers,
                         const void* const* host_bundles, int32_t* slot_table);
-/* Request (layer, step, ids) and enqueue on `stream` the copies of the
- * missing bundles into their slots and the slot-table update: on a side
+/* Request (layer, step, ids) and enqueue on `stream` one copy kernel that
+ * reads the missing bundles from host memory into their slots: on a side
  * stream this prefetches (the copies overlap whatever the compute stream
- * runs), on the compute stream it is a blocking on-demand fill.  A copy
+ * runs), on the compute stream it is a blocking on-demand fill.  The
+ * slot-table update is queued for the compute stream (edge0_stager_wait).  A copy
  * into a slot that a layer read before first waits for that layer's
  * release point; a hit on a slot being filled on another stream waits for
  * that fill.  slots_out: host int32 [n] or NULL. */
 int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step, const int32_t* ids,
                         int32_t n, int32_t* slots_out, hipStream_t stream);
-/* Makes compute_stream wait until the set of (layer, step) is in its slots
- * (no-op when it was staged on compute_stream itself). */
+/* Before the kernels that read the set of (layer, step): applies the
+ * pending slot-table updates on compute_stream and makes it wait until the
+ * set is in its slots (no event wait when it was staged on compute_stream
+ * itself).  The slot table is written on the compute stream only. */
 int edge0_stager_wait(edge0_stager* sg, int32_t layer, int32_t step, hipStream_t compute_stream);
+/* Applies the pending slot-table updates on compute_stream (the table then
+ * maps every resident key once the stream reaches this point). */
+int edge0_stager_flush(edge0_stager* sg, hipStream_t compute_stream);
 /* Marks the point on compute_stream after the last kernel reading the set
  * of (layer, step) and unpins it: later copies into its slots wait for
  * that point. */

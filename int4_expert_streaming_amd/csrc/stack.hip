@@ -361,7 +361,8 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
       li.logits = st->logits;
       if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
       if ((rc = edge0_stage_experts(sg, L, step, plan.ids_host + (size_t)L * K, K, nullptr,
-                                    stream)) != EDGE0_OK)
+                                    stream)) != EDGE0_OK ||
+          (rc = edge0_stager_wait(sg, L, step, stream)) != EDGE0_OK)
         return rc;
       LayerIn l2{};
       l2.flags = IN_GATHER | IN_LORA;
@@ -400,7 +401,8 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
     if ((rc = edge0_stage_experts(sg, L + 1, step + 1, plan.next_ids_host + (size_t)(L + 1) * K,
                                   K, nullptr, plan.copy_stream)) != EDGE0_OK)
       return rc;
-  return EDGE0_OK;
+  // their slot-table updates, on the compute stream (ahead of their use)
+  return edge0_stager_flush(sg, stream);
 }
 
 extern "C" int edge0_stack_step_staged(edge0_stack* st, edge0_stager* sg,

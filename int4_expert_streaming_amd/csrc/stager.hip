@@ -13,18 +13,22 @@
 // its release; its ids are then taken in order - a resident key is a hit, a
 // missing key takes the lowest free slot, else the unpinned resident slot
 // with the oldest stamp; every touched key takes the next value of one
-// global clock.  The stager adds the data movement: per request, the misses'
-// bundles are copied host-to-device into their slots and the slot table is
-// patched by one small kernel on the staging stream, then a ready event is
-// recorded there.  Cross-stream hazards are ordered with events only:
+// global clock.  The stager adds the data movement: per request, one kernel
+// copies the misses' bundles from pinned host memory into their slots on the
+// staging stream, then a ready event is recorded.  Cross-stream hazards are ordered with events only:
 //   - a copy into a slot that some layer read waits for the release event
 //     recorded on the compute stream after that layer's kernels;
 //   - a hit on a slot whose fill ran on another stream waits for that fill's
 //     ready event;
 //   - the compute stream waits for a set's ready event before the layer
 //     (edge0_stager_wait).
-// Events are per (layer, step parity): at most two sets of a layer are
-// pending, and waiting on a later record of the same event only delays.
+// Each record has a serial, so a wait targets exactly the record it needs
+// and is dropped once that record has completed.  The slot table is written
+// on the compute stream only: a request's updates (its new keys, -1 for the
+// keys it evicted) are queued and applied, coalesced in request order, by
+// the next edge0_stager_wait or edge0_stager_flush.  A new key's entry may
+// land before its copy finishes; only a set holding that key reads it, and
+// such a set is ordered after the copy.
 #include <map>
 #include <new>
 #include <set>
@@ -140,17 +144,79 @@ struct Lru {
   }
 };
 
-// slot-table entries to set, passed by value (captured at launch)
-constexpr int kMaxPatch = 32;
+// Slot-table entries to set, passed by value (captured at launch); the
+// entries of one launch have distinct indices.
+constexpr int kMaxPatch = 384;
 struct TablePatch {
   int n;
   int32_t idx[kMaxPatch];
   int32_t val[kMaxPatch];
 };
 __global__ void k_patch_table(int32_t* __restrict__ table, TablePatch p) {
-  const int i = threadIdx.x;
-  if (i < p.n) table[p.idx[i]] = p.val[i];
+  for (int i = threadIdx.x; i < p.n; i += blockDim.x) table[p.idx[i]] = p.val[i];
 }
+
+// One request's fills: bundle b of the list is copied from pinned host
+// memory (read by the kernel over the host link) into its slot.  A kernel
+// rather than the DMA engine: the copy then orders with the layer kernels on
+// the compute stream without an engine switch, and 32 workgroups per bundle
+// already saturate the link.
+constexpr int kCopyWGs = 32;
+struct CopyList {
+  const uint4* src[16];
+  uint4* dst[16];
+};
+__global__ __launch_bounds__(256) void k_stage_copy(CopyList c, int64_t n16) {
+  const uint4* __restrict__ src = c.src[blockIdx.y];
+  uint4* __restrict__ dst = c.dst[blockIdx.y];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// A ring of events whose records carry serial numbers.  An entry is reused
+// only after its previous record completed (a host wait, which also bounds
+// how far the host runs ahead), so a serial that is no longer in the ring has
+// completed and needs no wait.
+struct EventRing {
+  std::vector<hipEvent_t> ev;
+  std::vector<uint64_t> serial;  // serial held by each entry, 0 = none
+  std::vector<hipStream_t> stream;
+  uint64_t last = 0;
+
+  bool init(int n) {
+    ev.assign(n, nullptr);
+    serial.assign(n, 0);
+    stream.assign(n, nullptr);
+    for (int i = 0; i < n; ++i)
+      if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) return false;
+    return true;
+  }
+  void destroy() {
+    for (auto e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  // records the next serial on s; 0 on a HIP error
+  uint64_t record(hipStream_t s) {
+    const uint64_t q = last + 1;
+    const size_t i = q % ev.size();
+    if (serial[i] != 0 && hipEventSynchronize(ev[i]) != hipSuccess) return 0;
+    if (hipEventRecord(ev[i], s) != hipSuccess) return 0;
+    last = q;
+    serial[i] = q;
+    stream[i] = s;
+    return q;
+  }
+  // the event a stream s must wait on to be ordered after record q, or
+  // nullptr when no wait is needed (none, recycled, same stream, complete)
+  hipEvent_t pending(uint64_t q, hipStream_t s) const {
+    if (q == 0) return nullptr;
+    const size_t i = q % ev.size();
+    if (serial[i] != q || stream[i] == s) return nullptr;
+    if (hipEventQuery(ev[i]) == hipSuccess) return nullptr;
+    return ev[i];
+  }
+};
+constexpr int kRing = 1024;
 
 }  // namespace e0
 
@@ -165,15 +231,40 @@ struct edge0_stager {
   edge0_moe_shape shape;
   edge0_slot_pool pool;
   int64_t bundle_bytes = 0;
-  std::vector<const void*> host;  // [L * E]
+  std::vector<const void*> host;  // [L * E] device addresses of the pinned host bundles
   int32_t* table = nullptr;
-  std::vector<hipEvent_t> ev_ready, ev_rel;  // [L][2]
-  // per slot: the event index (L*2 + parity) and stream of its last fill
-  // and of the last release of a set that read it (-1: none)
-  std::vector<int32_t> fill_ev, rel_ev;
-  std::vector<hipStream_t> fill_stream, rel_stream;
-  std::map<std::pair<int, int>, hipStream_t> staged_on;  // pending (L, t) -> stream
+  EventRing ready;  // recorded after each request's copies, on its stream
+  EventRing rel;    // recorded at each release, on the compute stream
+  // per slot: serial of the request that last filled it and of the last
+  // release of a set that read it
+  std::vector<uint64_t> fill_q, rel_q;
+  struct Staged {
+    hipStream_t stream;
+    uint64_t q;
+  };
+  std::map<std::pair<int, int>, Staged> staged;  // pending (L, t)
+  std::vector<std::pair<int32_t, int32_t>> patches;  // table updates not yet applied, in order
 };
+
+// Applies the pending slot-table updates on `stream`, in request order (a
+// later update of an entry replaces an earlier one).
+static int flush_patches(edge0_stager* sg, hipStream_t stream) {
+  if (sg->patches.empty()) return EDGE0_OK;
+  std::map<int32_t, int32_t> last;
+  for (const auto& pv : sg->patches) last[pv.first] = pv.second;
+  sg->patches.clear();
+  TablePatch p{};
+  for (auto it = last.begin(); it != last.end();) {
+    p.n = 0;
+    for (; it != last.end() && p.n < kMaxPatch; ++it) {
+      p.idx[p.n] = it->first;
+      p.val[p.n++] = it->second;
+    }
+    k_patch_table<<<1, 256, 0, stream>>>(sg->table, p);
+    E0_CHECK_LAUNCH();
+  }
+  return EDGE0_OK;
+}
 
 extern "C" int edge0_lru_create(edge0_lru** out, int32_t n_slots, int32_t n_layers,
                                 int32_t n_experts) {
@@ -215,10 +306,9 @@ extern "C" void edge0_lru_destroy(edge0_lru* h) { delete h; }
 
 extern "C" void edge0_stager_destroy(edge0_stager* sg) {
   if (!sg) return;
-  for (auto e : sg->ev_ready)
-    if (e) (void)hipEventDestroy(e);
-  for (auto e : sg->ev_rel)
-    if (e) (void)hipEventDestroy(e);
+  (void)hipDeviceSynchronize();
+  sg->ready.destroy();
+  sg->rel.destroy();
   delete sg;
 }
 
@@ -232,8 +322,20 @@ extern "C" int edge0_stager_create(edge0_stager** out, const edge0_moe_shape* sh
   if (bundle_layout(shape, &lay) != EDGE0_OK) return EDGE0_EINVAL;
   if (pool->slot_bytes < lay.bytes || pool->slot_bytes % 256 != 0) return EDGE0_EINVAL;
   const int E = shape->n_experts;
-  for (int64_t i = 0; i < (int64_t)n_layers * E; ++i)
-    if (!host_bundles[i]) return EDGE0_EINVAL;
+  // every bundle must be pinned host memory the device can read, 16-byte
+  // aligned; the kernels use its device address
+  std::vector<const void*> dev_ptrs((size_t)n_layers * E);
+  for (int64_t i = 0; i < (int64_t)n_layers * E; ++i) {
+    if (!host_bundles[i] || reinterpret_cast<uintptr_t>(host_bundles[i]) % 16 != 0)
+      return EDGE0_EINVAL;
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, host_bundles[i]) != hipSuccess) {
+      (void)hipGetLastError();  // clear the sticky error of the failed query
+      return EDGE0_EINVAL;
+    }
+    if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return EDGE0_EINVAL;
+    dev_ptrs[i] = attr.devicePointer;
+  }
   edge0_stager* sg = new (std::nothrow) edge0_stager();
   if (!sg) return EDGE0_ENOMEM;
   int rc = sg->lru.init(pool->n_slots, n_layers, E);
@@ -244,20 +346,13 @@ extern "C" int edge0_stager_create(edge0_stager** out, const edge0_moe_shape* sh
   sg->shape = *shape;
   sg->pool = *pool;
   sg->bundle_bytes = lay.bytes;
-  sg->host.assign(host_bundles, host_bundles + (size_t)n_layers * E);
+  sg->host = std::move(dev_ptrs);
   sg->table = slot_table;
-  sg->ev_ready.assign((size_t)n_layers * 2, nullptr);
-  sg->ev_rel.assign((size_t)n_layers * 2, nullptr);
-  bool ok = true;
-  for (size_t i = 0; i < sg->ev_ready.size() && ok; ++i)
-    ok = hipEventCreateWithFlags(&sg->ev_ready[i], hipEventDisableTiming) == hipSuccess &&
-         hipEventCreateWithFlags(&sg->ev_rel[i], hipEventDisableTiming) == hipSuccess;
-  sg->fill_ev.assign(pool->n_slots, -1);
-  sg->rel_ev.assign(pool->n_slots, -1);
-  sg->fill_stream.assign(pool->n_slots, nullptr);
-  sg->rel_stream.assign(pool->n_slots, nullptr);
-  ok = ok && hipMemset(slot_table, 0xFF, (size_t)n_layers * E * 4) == hipSuccess &&
-       hipDeviceSynchronize() == hipSuccess;
+  sg->fill_q.assign(pool->n_slots, 0);
+  sg->rel_q.assign(pool->n_slots, 0);
+  const bool ok = sg->ready.init(kRing) && sg->rel.init(kRing) &&
+                  hipMemset(slot_table, 0xFF, (size_t)n_layers * E * 4) == hipSuccess &&
+                  hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     edge0_stager_destroy(sg);
     return EDGE0_EHIP;
@@ -275,94 +370,84 @@ extern "C" int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step
   if (rc != EDGE0_OK) return rc;
   int32_t slots[16], hit[16], evicted[16];
   sg->lru.apply(layer, step, keys, slots, hit, evicted);
-  sg->staged_on[{layer, step}] = stream;
-  const int E = sg->shape.n_experts;
-  const int my_ev = layer * 2 + (step & 1);
-  // hazards first: every wait this request needs, each event once
-  int waits[2 * 16];
+  // hazards: a hit on a slot filled on another stream waits for that fill; a
+  // copy into a slot waits for the last release of a set that read it
+  hipEvent_t waits[32];
   int n_waits = 0;
-  auto add_wait = [&](int ev) {
+  auto add = [&](hipEvent_t e) {
+    if (!e) return;
     for (int j = 0; j < n_waits; ++j)
-      if (waits[j] == ev * 2 + 0) return;
-    waits[n_waits++] = ev * 2 + 0;
-  };
-  auto add_rel = [&](int ev) {
-    for (int j = 0; j < n_waits; ++j)
-      if (waits[j] == ev * 2 + 1) return;
-    waits[n_waits++] = ev * 2 + 1;
+      if (waits[j] == e) return;
+    waits[n_waits++] = e;
   };
   for (int i = 0; i < n; ++i) {
     const int s = slots[i];
-    if (hit[i]) {
-      if (sg->fill_ev[s] >= 0 && sg->fill_stream[s] != stream) add_wait(sg->fill_ev[s]);
-    } else {
-      if (sg->rel_ev[s] >= 0 && sg->rel_stream[s] != stream) add_rel(sg->rel_ev[s]);
-      if (sg->fill_ev[s] >= 0 && sg->fill_stream[s] != stream) add_wait(sg->fill_ev[s]);
-    }
+    add(sg->ready.pending(sg->fill_q[s], stream));
+    if (!hit[i]) add(sg->rel.pending(sg->rel_q[s], stream));
   }
-  for (int j = 0; j < n_waits; ++j) {
-    hipEvent_t e = (waits[j] & 1) ? sg->ev_rel[waits[j] >> 1] : sg->ev_ready[waits[j] >> 1];
-    if (hipStreamWaitEvent(stream, e, 0) != hipSuccess) return EDGE0_EHIP;
-  }
-  TablePatch p{};
+  for (int j = 0; j < n_waits; ++j)
+    if (hipStreamWaitEvent(stream, waits[j], 0) != hipSuccess) return EDGE0_EHIP;
   uint8_t* base = static_cast<uint8_t*>(sg->pool.base);
+  CopyList cl{};
+  int n_copy = 0;
   for (int i = 0; i < n; ++i) {
     if (hit[i]) continue;
     const int s = slots[i];
-    if (hipMemcpyAsync(base + (size_t)s * sg->pool.slot_bytes, sg->host[keys[i]],
-                       (size_t)sg->bundle_bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-      return EDGE0_EHIP;
+    cl.src[n_copy] = static_cast<const uint4*>(sg->host[keys[i]]);
+    cl.dst[n_copy++] = reinterpret_cast<uint4*>(base + (size_t)s * sg->pool.slot_bytes);
     sg->lru.stats.bytes_staged += sg->bundle_bytes;
-    if (evicted[i] >= 0) {
-      p.idx[p.n] = evicted[i];
-      p.val[p.n++] = -1;
-    }
-    p.idx[p.n] = keys[i];
-    p.val[p.n++] = s;
-    sg->fill_ev[s] = my_ev;
-    sg->fill_stream[s] = stream;
-    sg->rel_ev[s] = -1;
-    sg->rel_stream[s] = nullptr;
+    if (evicted[i] >= 0) sg->patches.emplace_back(evicted[i], -1);
+    sg->patches.emplace_back(keys[i], s);
   }
-  if (p.n > 0) {
-    k_patch_table<<<1, 64, 0, stream>>>(sg->table, p);
+  if (n_copy > 0) {
+    k_stage_copy<<<dim3(kCopyWGs, n_copy), 256, 0, stream>>>(cl, sg->bundle_bytes / 16);
     E0_CHECK_LAUNCH();
   }
-  if (hipEventRecord(sg->ev_ready[my_ev], stream) != hipSuccess) return EDGE0_EHIP;
+  const uint64_t q = sg->ready.record(stream);
+  if (q == 0) return EDGE0_EHIP;
+  for (int i = 0; i < n; ++i)
+    if (!hit[i]) {
+      sg->fill_q[slots[i]] = q;
+      sg->rel_q[slots[i]] = 0;
+    }
+  sg->staged[{layer, step}] = {stream, q};
   if (slots_out)
     for (int i = 0; i < n; ++i) slots_out[i] = slots[i];
-  (void)E;
   return EDGE0_OK;
 }
 
 extern "C" int edge0_stager_wait(edge0_stager* sg, int32_t layer, int32_t step,
                                  hipStream_t compute_stream) {
   if (!sg) return EDGE0_EINVAL;
-  auto it = sg->staged_on.find({layer, step});
-  if (it == sg->staged_on.end()) return EDGE0_EINVAL;
-  if (it->second == compute_stream) return EDGE0_OK;
-  return hipStreamWaitEvent(compute_stream, sg->ev_ready[layer * 2 + (step & 1)], 0) == hipSuccess
-             ? EDGE0_OK
-             : EDGE0_EHIP;
+  auto it = sg->staged.find({layer, step});
+  if (it == sg->staged.end()) return EDGE0_EINVAL;
+  int rc = flush_patches(sg, compute_stream);
+  if (rc != EDGE0_OK) return rc;
+  hipEvent_t e = sg->ready.pending(it->second.q, compute_stream);
+  if (e && hipStreamWaitEvent(compute_stream, e, 0) != hipSuccess) return EDGE0_EHIP;
+  return EDGE0_OK;
 }
 
 extern "C" int edge0_stager_release(edge0_stager* sg, int32_t layer, int32_t step,
                                     hipStream_t compute_stream) {
   if (!sg) return EDGE0_EINVAL;
   if (!sg->lru.pending.count({layer, step})) return EDGE0_EINVAL;
-  const int ev = layer * 2 + (step & 1);
-  if (hipEventRecord(sg->ev_rel[ev], compute_stream) != hipSuccess) return EDGE0_EHIP;
+  const uint64_t q = sg->rel.record(compute_stream);
+  if (q == 0) return EDGE0_EHIP;
   std::vector<int32_t> keys;
   const int rc = sg->lru.release(layer, step, &keys);
   if (rc != EDGE0_OK) return rc;
   for (int key : keys) {
     const int s = sg->lru.slot_of[key];
-    if (s < 0) continue;
-    sg->rel_ev[s] = ev;
-    sg->rel_stream[s] = compute_stream;
+    if (s >= 0) sg->rel_q[s] = q;
   }
-  sg->staged_on.erase({layer, step});
+  sg->staged.erase({layer, step});
   return EDGE0_OK;
+}
+
+extern "C" int edge0_stager_flush(edge0_stager* sg, hipStream_t compute_stream) {
+  if (!sg) return EDGE0_EINVAL;
+  return flush_patches(sg, compute_stream);
 }
 
 extern "C" int edge0_stager_stats(const edge0_stager* sg, edge0_stage_stats* out) {

@@ -118,6 +118,7 @@ _SIG = {
     "edge0_stage_experts": (C.c_int, [_P, C.c_int32, C.c_int32, _I32P, C.c_int32, _I32P, _P]),
     "edge0_stager_wait": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
     "edge0_stager_release": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
+    "edge0_stager_flush": (C.c_int, [_P, _P]),
     "edge0_stager_stats": (C.c_int, [_P, C.POINTER(StageStats)]),
     "edge0_stager_destroy": (None, [_P]),
 }
@@ -340,6 +341,9 @@ class Stager:
     def release(self, layer: int, step: int, stream=None):
         _check(lib.edge0_stager_release(self._handle, layer, step, _stream(stream)),
                "edge0_stager_release")
+
+    def flush(self, stream=None):
+        _check(lib.edge0_stager_flush(self._handle, _stream(stream)), "edge0_stager_flush")
 
     def stats(self) -> dict:
         s = StageStats()

@@ -125,3 +125,26 @@ def test_qwen3moe_streamed_stack_sampled_layers(torch_cuda):
                      keep_p=0.06)
     assert ss.stager.stats()["evictions"] > 0
     print(f"[streamed] qwen3moe: worst rel-L2 {worst:.3e}, {ss.stager.stats()}")
+
+
+def test_stager_rejects_pageable_host_memory(torch_cuda):
+    """Host bundles must be pinned (device-readable); pageable memory is
+    refused at create, before any copy could touch it."""
+    import numpy as np
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import SlotPoolBuffer
+    sh = E.make_shape(G.TINY)
+    bb = int(E.edge0_bundle_layout_of(sh).bytes)
+    pageable = np.zeros(2 * G.TINY.n_experts * bb, np.uint8)
+    ptrs = [pageable.ctypes.data + k * bb for k in range(2 * G.TINY.n_experts)]
+    pool = SlotPoolBuffer(sh, 4)
+    table = torch.full((2, G.TINY.n_experts), -1, dtype=torch.int32, device="cuda")
+    with pytest.raises(E.Edge0Error) as ei:
+        E.Stager(sh, pool.pool, 2, ptrs, table)
+    assert ei.value.code == E.EDGE0_EINVAL
+    # a pinned buffer is accepted
+    pinned = torch.zeros(2 * G.TINY.n_experts * bb, dtype=torch.uint8, pin_memory=True)
+    sg = E.Stager(sh, pool.pool, 2, [pinned.data_ptr() + k * bb for k in range(2 * G.TINY.n_experts)],
+                  table)
+    sg.close()
