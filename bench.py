@@ -194,11 +194,15 @@ def bench_streamed(args, log):
     log(f"[streamed] host link: DMA copies {bw_dma:.1f} GB/s, fill kernel {bw_kernel:.1f} GB/s "
         f"({bb}-byte bundles); trace overlap {overlap:.3f}")
     arms = {}
-    order = ["ahead", "demand", "resident"] if args.seed % 2 == 0 else ["demand", "ahead", "resident"]
+    order = ["ahead", "demand", "ahead_dma", "demand_dma", "resident"]
+    if args.seed % 2:
+        order = ["demand", "ahead", "demand_dma", "ahead_dma", "resident"]
     for arm in order:
         slots = N_LAYERS * S.n_experts if arm == "resident" else n_slots
         ss = StreamedStack(S, gen, N_LAYERS, OWNERS, CONSUMERS, slots, log=None, host=host)
-        ahead = arm != "demand"
+        if arm.endswith("_dma"):
+            ss.stager.set_copy_mode(1)
+        ahead = not arm.startswith("demand")
         if arm == "resident":  # every bundle staged before timing
             for L in range(N_LAYERS):
                 for e0 in range(0, S.n_experts, 16):
@@ -228,7 +232,7 @@ def bench_streamed(args, log):
         del ss
         torch.cuda.synchronize()
     t_comp = arms["resident"]["ms_per_step"]
-    for arm in ("ahead", "demand"):
+    for arm in ("ahead", "demand", "ahead_dma", "demand_dma"):
         a = arms[arm]
         copy_ms = a["h2d_bytes_per_step"] / (bw * 1e9) * 1e3
         exposed = max(0.0, a["ms_per_step"] - t_comp)

@@ -354,6 +354,13 @@ int edge0_stager_flush(edge0_stager* sg, hipStream_t compute_stream);
  * that point. */
 int edge0_stager_release(edge0_stager* sg, int32_t layer, int32_t step,
                          hipStream_t compute_stream);
+/* How fills move bytes: EDGE0_COPY_KERNEL (default) - one kernel per
+ * request reads the host bundles over the host link, so a fill on the
+ * compute stream orders with the layer kernels without switching engines;
+ * EDGE0_COPY_DMA - one hipMemcpyAsync per bundle on the DMA engines.  Same
+ * results; EDGE0_EINVAL for another value. */
+enum { EDGE0_COPY_KERNEL = 0, EDGE0_COPY_DMA = 1 };
+int edge0_stager_set_copy_mode(edge0_stager* sg, int32_t mode);
 int edge0_stager_stats(const edge0_stager* sg, edge0_stage_stats* out);
 void edge0_stager_destroy(edge0_stager* sg);
 

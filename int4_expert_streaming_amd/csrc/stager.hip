@@ -244,6 +244,7 @@ struct edge0_stager {
   };
   std::map<std::pair<int, int>, Staged> staged;  // pending (L, t)
   std::vector<std::pair<int32_t, int32_t>> patches;  // table updates not yet applied, in order
+  int copy_mode = EDGE0_COPY_KERNEL;
 };
 
 // Applies the pending slot-table updates on `stream`, in request order (a
@@ -399,10 +400,14 @@ extern "C" int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step
     if (evicted[i] >= 0) sg->patches.emplace_back(evicted[i], -1);
     sg->patches.emplace_back(keys[i], s);
   }
-  if (n_copy > 0) {
+  if (n_copy > 0 && sg->copy_mode == EDGE0_COPY_KERNEL) {
     k_stage_copy<<<dim3(kCopyWGs, n_copy), 256, 0, stream>>>(cl, sg->bundle_bytes / 16);
     E0_CHECK_LAUNCH();
   }
+  for (int i = 0; i < n_copy && sg->copy_mode == EDGE0_COPY_DMA; ++i)
+    if (hipMemcpyAsync(cl.dst[i], cl.src[i], (size_t)sg->bundle_bytes, hipMemcpyHostToDevice,
+                       stream) != hipSuccess)
+      return EDGE0_EHIP;
   const uint64_t q = sg->ready.record(stream);
   if (q == 0) return EDGE0_EHIP;
   for (int i = 0; i < n; ++i)
@@ -448,6 +453,12 @@ extern "C" int edge0_stager_release(edge0_stager* sg, int32_t layer, int32_t ste
 extern "C" int edge0_stager_flush(edge0_stager* sg, hipStream_t compute_stream) {
   if (!sg) return EDGE0_EINVAL;
   return flush_patches(sg, compute_stream);
+}
+
+extern "C" int edge0_stager_set_copy_mode(edge0_stager* sg, int32_t mode) {
+  if (!sg || (mode != EDGE0_COPY_KERNEL && mode != EDGE0_COPY_DMA)) return EDGE0_EINVAL;
+  sg->copy_mode = mode;
+  return EDGE0_OK;
 }
 
 extern "C" int edge0_stager_stats(const edge0_stager* sg, edge0_stage_stats* out) {

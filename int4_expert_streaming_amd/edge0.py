@@ -119,6 +119,7 @@ _SIG = {
     "edge0_stager_wait": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
     "edge0_stager_release": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
     "edge0_stager_flush": (C.c_int, [_P, _P]),
+    "edge0_stager_set_copy_mode": (C.c_int, [_P, C.c_int32]),
     "edge0_stager_stats": (C.c_int, [_P, C.POINTER(StageStats)]),
     "edge0_stager_destroy": (None, [_P]),
 }
@@ -341,6 +342,10 @@ class Stager:
     def release(self, layer: int, step: int, stream=None):
         _check(lib.edge0_stager_release(self._handle, layer, step, _stream(stream)),
                "edge0_stager_release")
+
+    def set_copy_mode(self, mode: int):
+        """0: fill kernel (default); 1: DMA copies (hipMemcpyAsync)."""
+        _check(lib.edge0_stager_set_copy_mode(self._handle, mode), "edge0_stager_set_copy_mode")
 
     def flush(self, stream=None):
         _check(lib.edge0_stager_flush(self._handle, _stream(stream)), "edge0_stager_flush")

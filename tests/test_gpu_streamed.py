@@ -42,13 +42,15 @@ def _resident(events, ids_of, n_slots, n_layers, n_experts):
     return table, tot
 
 
-def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of, keep_p=0.1):
+def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of, keep_p=0.1,
+         copy_mode=0):
     import torch
     from int4_expert_streaming_amd.stackbuild import StreamedStack
     from int4_expert_streaming_amd.weights import to_device
     gen = G.StackGen(S, seed)
     En, K = S.n_experts, S.top_k
     ss = StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
+    ss.stager.set_copy_mode(copy_mode)
     trace = G.zipf_trace(En, K, n_layers, steps + 1, seed + 100, keep_p=keep_p)
     trace_dev = torch.from_numpy(trace).cuda()
     own = range(owners[0], owners[1] + 1) if ahead else range(0)
@@ -109,11 +111,14 @@ def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of,
     return ss, worst
 
 
-@pytest.mark.parametrize("ahead", [True, False])
-def test_small_streamed_stack_every_layer(torch_cuda, ahead):
-    """10 tiny layers, a 40-slot pool (160 bundles: constant eviction)."""
-    ss, worst = _run(G.TINY, 5, 10, (2, 7), (3, 8), 40, 6, ahead, lambda t: range(10))
-    print(f"[streamed] tiny ahead={ahead}: worst rel-L2 {worst:.3e}, {ss.stager.stats()}")
+@pytest.mark.parametrize("ahead,copy_mode", [(True, 0), (False, 0), (True, 1), (False, 1)])
+def test_small_streamed_stack_every_layer(torch_cuda, ahead, copy_mode):
+    """10 tiny layers, a 40-slot pool (160 bundles: constant eviction); both
+    arms, fills by the copy kernel (0) or by DMA copies (1)."""
+    ss, worst = _run(G.TINY, 5, 10, (2, 7), (3, 8), 40, 6, ahead, lambda t: range(10),
+                     copy_mode=copy_mode)
+    print(f"[streamed] tiny ahead={ahead} mode={copy_mode}: worst rel-L2 {worst:.3e}, "
+          f"{ss.stager.stats()}")
 
 
 @pytest.mark.timeout(900)
