@@ -208,6 +208,34 @@ int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                     const void* x, void* y, void* workspace, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Several tokens through one MoE layer, grouped by expert.  Defined token by
+ * token exactly as edge0_moe_layer: for token j with routing ids[j][.],
+ * w[j][.],  y[j] = bf16( sum_k w[j][k] D_{ids[j][k]}(x[j]) )  ([Edge0] §3.1
+ * "Math contract", §3.3); the grouping only reorders the work.  The (token,
+ * k) pairs are bucketed by expert on the device (counting sort, stable by
+ * token), so each routed expert's weights are read once per call; experts
+ * chosen by >= 16 tokens run their products on MFMA (bf16 operands holding
+ * the exact 128 + q nibble values and the activations, fp32 accumulation,
+ * the group affine applied per group in fp32), the others as multi-token
+ * GEMVs.
+ *   n_tokens   : 0..64 (0: nothing is enqueued)
+ *   slot_table : device int32 [E], id -> slot
+ *   ids, w     : device int32 / fp32 [n_tokens][K]
+ *   x, y       : device bf16 [n_tokens][d]; y must not alias x
+ *   workspace  : edge0_grouped_workspace_bytes(shape) bytes, zero-filled once
+ *                before first use (calls leave it ready for the next call);
+ *                calls that may run concurrently need distinct workspaces
+ *   flags      : 0, or EDGE0_GROUPED_NO_MFMA to run every expert as GEMVs
+ * Supported shapes: those of edge0_moe_layer with d_inter <= 1024 and
+ * d_model <= 4096 (edge0_grouped_workspace_bytes returns 0 otherwise). */
+enum { EDGE0_GROUPED_NO_MFMA = 1 };
+size_t edge0_grouped_workspace_bytes(const edge0_moe_shape* shape);
+int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                      const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
+                      const float* w, const void* x, void* y, void* workspace, int32_t flags,
+                      hipStream_t stream);
+
+/* -------------------------------------------------------------------------
  * Decode stack: n_layers pre-norm residual MoE blocks (no attention),
  *   x_L = bf16(RMSNorm(h_L)),  RMSNorm(h) = h / sqrt(mean(h^2) + eps)
  *   routing_L = committed prediction (consumer layers, step > 0) or the

@@ -65,6 +65,28 @@ __device__ __forceinline__ float chunk_dot128(uint4 q, const uint32_t* xp) {
   return acc;
 }
 
+// Activation chunk `col` (32 bf16 of x): raw load, then the 16 pairs
+// chunk_dot128 expects and its fp32 sum.
+struct XRaw {
+  uint4 v[4];
+};
+__device__ __forceinline__ void load_x_raw(const uint16_t* __restrict__ x, int col, XRaw& r) {
+  const uint4* src = reinterpret_cast<const uint4*>(x + 32 * col);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) r.v[m] = src[m];
+}
+__device__ __forceinline__ float x_pairs(const XRaw& r, uint32_t xp[16]) {
+  const uint4* v = r.v;
+  float sum = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    pair_perm8(v[m].x, v[m].y, v[m].z, v[m].w, xp + 4 * m);
+    sum += bf_lo(v[m].x) + bf_hi(v[m].x) + bf_lo(v[m].y) + bf_hi(v[m].y) + bf_lo(v[m].z) +
+           bf_hi(v[m].z) + bf_lo(v[m].w) + bf_hi(v[m].w);
+  }
+  return sum;
+}
+
 // -------------------------------------------------------------- reductions
 // DPP data movement within a wave (no LDS crossbar): quad permutes, row
 // mirrors and the row broadcasts of GFX9.

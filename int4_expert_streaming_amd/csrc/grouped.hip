@@ -1,0 +1,569 @@
+// Several tokens through one MoE layer, grouped by expert: every routed
+// expert's weights are read once per call however many tokens chose it.
+//
+// The result is defined token by token, exactly as the single-token layer
+// ([Edge0] = "The Other Half of the Memory Wall: Serving 35B MoEs from SSD
+// with Trained Routing Prediction", §3.1 "Math contract", §3.3 unmerged
+// LoRA, Figure 1 sum node); the grouping only reorders the work.
+//
+// Launches (all on the caller's stream):
+//   k_grp_route   : one workgroup buckets the T*K (token, k) pairs by expert
+//                   (counting sort, stable in pair order, so by token), lists
+//                   the active experts with their first pair and count, and
+//                   resolves each active expert's slot once.
+//   k_grp_lora_in : t = A x for every pair's gate and up adapters.
+//   k_grp_gate_up : one workgroup = 16 rows of one active expert's gate and
+//                   up; the rows stay in registers while the expert's tokens
+//                   stream through LDS in batches; SwiGLU; h stored as bf16
+//                   hi/lo pairs, per-16-row sums, and A_down h accumulated in
+//                   fixed point per pair.
+//   k_grp_gate_up_mfma : the same for experts with >= 16 tokens, on MFMA.
+//   k_grp_down    : one workgroup = 64 output rows of one active expert; the
+//                   tiled down weights stay in registers while the tokens' h
+//                   batches stream through LDS; the LoRA-down delta; each
+//                   token's weighted row added to its fixed-point output.
+//   k_grp_down_mfma : the same for experts with >= 16 tokens, on MFMA.
+//   k_grp_out     : y = bf16 of each token's accumulator; clears the
+//                   accumulators for the next call.
+// Int4 arithmetic is the single-token path's: exact bf16 "128 + q" nibble
+// pairs against pair-permuted activations, the group affine folded per
+// 32-input chunk, fp32 everywhere, one bf16 rounding of y.
+#include "moe_internal.h"
+
+namespace e0 {
+
+constexpr int kGrpMaxTokens = 64;
+
+struct GrpArgs {
+  const uint8_t* pool;
+  int64_t slot_bytes;
+  int32_t n_slots;
+  const int32_t* table;
+  const int32_t* ids;  // [T][K]
+  const float* w;      // [T][K]
+  const uint16_t* x;   // [T][d]
+  uint16_t* y;         // [T][d]
+  int T, d, E, I, K, g, r;
+  float scale;
+  edge0_bundle_layout lay;
+  int Amax;  // grid bound on the number of active experts: min(E, T*K)
+  int P;     // T*K
+  // workspace
+  uint32_t* err;
+  int32_t* info;      // [0] active experts, [1] valid pairs, [2] experts with >= 16 tokens
+  int32_t* act_e;     // [Amax]
+  int32_t* act_off;   // [Amax] first sorted pair
+  int32_t* act_cnt;   // [Amax]
+  int32_t* act_slot;  // [Amax] slot, or -1
+  int32_t* pair_tok;  // [P] token of each sorted pair
+  int32_t* pair_act;  // [P] active expert of each sorted pair
+  float* pair_w;      // [P] routing weight of each sorted pair
+  float* t_in;        // [P][2][r]
+  uint16_t* hp_hi;    // [P][I] pair-permuted
+  uint16_t* hp_lo;
+  float* hs;                   // [P][I/16]
+  unsigned long long* tdown;   // [P][r] A_down h, fixed point
+  unsigned long long* acc;     // [T][d] y, fixed point
+};
+
+// ------------------------------------------------------------- bucketing
+__global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
+  __shared__ int cnt[1024];
+  __shared__ int first[1024];
+  __shared__ int ids_s[kGrpMaxTokens * 16];
+  const int tid = threadIdx.x;
+  const int E = a.E, P = a.P;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  for (int p = tid; p < P; p += 1024) {
+    int e = a.ids[p];
+    if (e < 0 || e >= E) {
+      set_error(a.err, EDGE0_ERANGE);
+      e = -1;
+    }
+    ids_s[p] = e;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024)
+    if (ids_s[p] >= 0) atomicAdd(&cnt[ids_s[p]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int na = 0, run = 0, big = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = cnt[e];
+      first[e] = run;
+      if (c > 0) {
+        a.act_e[na] = e;
+        a.act_off[na] = run;
+        a.act_cnt[na] = c;
+        const int s = a.table[e];
+        const bool ok = s >= 0 && s < a.n_slots;
+        a.act_slot[na] = ok ? s : -1;
+        if (!ok) set_error(a.err, EDGE0_ERANGE);
+        big += c >= 16;
+        cnt[e] = na;  // from here on: the active index of expert e
+        ++na;
+        run += c;
+      }
+    }
+    a.info[0] = na;
+    a.info[1] = run;
+    a.info[2] = big;
+  }
+  __syncthreads();
+  // stable scatter: a pair's rank among the earlier pairs of its expert
+  for (int p = tid; p < P; p += 1024) {
+    const int e = ids_s[p];
+    if (e < 0) continue;
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += ids_s[q] == e;
+    const int dst = first[e] + rank;
+    a.pair_tok[dst] = p / a.K;
+    a.pair_act[dst] = cnt[e];
+    a.pair_w[dst] = a.w[p];
+  }
+}
+
+__device__ __forceinline__ const uint8_t* grp_bundle(const GrpArgs& a, int act) {
+  const int s = a.act_slot[act];
+  return s < 0 ? nullptr : a.pool + (size_t)s * (size_t)a.slot_bytes;
+}
+
+// ------------------------------------------------------------ LoRA A x
+// one wave per row (sorted pair q, projection p, rank row rr)
+__global__ __launch_bounds__(256) void k_grp_lora_in(GrpArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = a.r;
+  const int q = row / (2 * r), p = (row / r) & 1, rr = row % r;
+  if (q >= a.info[1]) return;
+  const uint8_t* b = grp_bundle(a, a.pair_act[q]);
+  float t = 0.f;
+  if (b != nullptr) {
+    const uint16_t* wrow =
+        reinterpret_cast<const uint16_t*>(b + (p ? a.lay.a_up : a.lay.a_gate)) + (size_t)rr * a.d;
+    t = row_dot<false, false>(wrow, a.x + (size_t)a.pair_tok[q] * a.d, a.d);
+  }
+  if ((threadIdx.x & 63) == 0) a.t_in[row] = t;
+}
+
+// position of element i of h in the pair-permuted order of its 8-group
+__device__ __forceinline__ int grp_pair_pos(int i) {
+  const int s = i & 7;
+  return (i & ~7) + (s < 4 ? 2 * s : 2 * (s - 4) + 1);
+}
+__device__ __forceinline__ float grp_silu(float z) { return z / (1.f + expf(-z)); }
+
+// One token's h for one row: stored as hi/lo bf16 pairs; returns hi + lo.
+__device__ __forceinline__ float grp_store_h(const GrpArgs& a, int q, int i, float h) {
+  const uint32_t hi = f2bf(h);
+  const uint32_t lo = f2bf(h - bf2f(hi));
+  const size_t base = (size_t)q * a.I + grp_pair_pos(i);
+  a.hp_hi[base] = (uint16_t)hi;
+  a.hp_lo[base] = (uint16_t)lo;
+  return bf2f(hi) + bf2f(lo);
+}
+
+// Per-16-row epilogue of one token: the sum of h over the rows and the
+// partial A_down h (threads rr < r), added in fixed point.
+__device__ __forceinline__ void grp_rows_epilogue(const GrpArgs& a, int q, int blk, int i0,
+                                                  const float* h_s, const float* hrep_s,
+                                                  const uint4& ad0, const uint4& ad1) {
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int t = 0; t < 16; ++t) s += hrep_s[t];
+    a.hs[(size_t)q * (a.I / 16) + blk] = s;
+  }
+  if ((int)threadIdx.x < a.r) {
+    const uint32_t w[8] = {ad0.x, ad0.y, ad0.z, ad0.w, ad1.x, ad1.y, ad1.z, ad1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s += bf_lo(w[m]) * h_s[2 * m] + bf_hi(w[m]) * h_s[2 * m + 1];
+    atomicAdd(a.tdown + (size_t)q * a.r + threadIdx.x, to_fix(s));
+  }
+  (void)i0;
+}
+
+// ------------------------------------------------------- gate/up (GEMV)
+// Token batches staged in LDS: kGrpXBytes of activations per batch.
+constexpr int kGrpXBytes = 32768;
+
+// NJ = ceil(d/32 / 64) chunks per lane; lane l owns chunks l + 64 j (< d/32)
+// of 4 row pairs of its wave.
+template <int NJ>
+__global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int max_cnt) {
+  __shared__ uint16_t xs[kGrpXBytes / 2];
+  __shared__ float h_s[16];
+  __shared__ float hrep_s[16];
+  const int nblk = a.I / 16;
+  const int act = blockIdx.x / nblk;
+  const int blk = blockIdx.x % nblk;
+  if (act >= a.info[0]) return;
+  const int n = a.act_cnt[act];
+  if (n < min_cnt || n > max_cnt) return;
+  const uint8_t* b = grp_bundle(a, act);
+  if (b == nullptr) return;
+  const int q0 = a.act_off[act];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d = a.d, g = a.g, ng = d / g, r = a.r, cpr = d / 32;
+  const int i0 = blk * 16, row0 = i0 + 4 * wave;
+  // the wave's 4 gate and 4 up rows, with their scales and biases
+  const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q);
+  const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q);
+  const uint16_t* gsp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s);
+  const uint16_t* gbp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b);
+  const uint16_t* usp = reinterpret_cast<const uint16_t*>(b + a.lay.up_s);
+  const uint16_t* ubp = reinterpret_cast<const uint16_t*>(b + a.lay.up_b);
+  uint4 qg[4][NJ], qu[4][NJ];
+  float sg[4][NJ], cg[4][NJ], su[4][NJ], cu[4][NJ];  // s and (b - 128 s)
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int row = row0 + ii;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = lane + 64 * j;
+      const bool on = col < cpr;
+      const int cc = on ? col : 0;
+      qg[ii][j] = on ? reinterpret_cast<const uint4*>(gq + (size_t)row * (d / 8))[cc]
+                     : make_uint4(0, 0, 0, 0);
+      qu[ii][j] = on ? reinterpret_cast<const uint4*>(uq + (size_t)row * (d / 8))[cc]
+                     : make_uint4(0, 0, 0, 0);
+      const int grp = (32 * cc) / g;
+      const float s1 = bf2f(gsp[row * ng + grp]), b1 = bf2f(gbp[row * ng + grp]);
+      const float s2 = bf2f(usp[row * ng + grp]), b2 = bf2f(ubp[row * ng + grp]);
+      sg[ii][j] = on ? s1 : 0.f;
+      cg[ii][j] = on ? b1 - 128.f * s1 : 0.f;
+      su[ii][j] = on ? s2 : 0.f;
+      cu[ii][j] = on ? b2 - 128.f * s2 : 0.f;
+    }
+  }
+  const bool has_l = r > 0 && lane < r;
+  float Bg[4] = {0.f, 0.f, 0.f, 0.f}, Bu[4] = {0.f, 0.f, 0.f, 0.f};
+  if (has_l) {
+    const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
+    const uint16_t* Bup = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      Bg[ii] = bf2f(Bgp[(size_t)(row0 + ii) * r + lane]);
+      Bu[ii] = bf2f(Bup[(size_t)(row0 + ii) * r + lane]);
+    }
+  }
+  uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
+  if ((int)threadIdx.x < r) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)threadIdx.x * a.I + i0);
+    ad0 = src[0];
+    ad1 = src[1];
+  }
+  const int bt = kGrpXBytes / (2 * d) < 1 ? 1 : kGrpXBytes / (2 * d);  // tokens per batch
+  for (int j0 = 0; j0 < n; j0 += bt) {
+    const int nb = n - j0 < bt ? n - j0 : bt;
+    __syncthreads();  // previous batch fully consumed
+    // stage the batch's activations: 16 bytes per thread per step
+    const int n16 = nb * d / 8;
+    for (int t = threadIdx.x; t < n16; t += 256) {
+      const int jj = t / (d / 8), c8 = t % (d / 8);
+      const int tok = a.pair_tok[q0 + j0 + jj];
+      reinterpret_cast<uint4*>(xs)[t] =
+          reinterpret_cast<const uint4*>(a.x + (size_t)tok * d)[c8];
+    }
+    __syncthreads();
+    for (int jj = 0; jj < nb; ++jj) {
+      const int q = q0 + j0 + jj;
+      uint32_t xp[NJ][16];
+      float X[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = lane + 64 * j;
+        XRaw xr;
+        if (col < cpr) {
+          const uint4* src = reinterpret_cast<const uint4*>(xs + (size_t)jj * d + 32 * col);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) xr.v[m] = src[m];
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) xr.v[m] = make_uint4(0, 0, 0, 0);
+        }
+        X[j] = x_pairs(xr, xp[j]);
+      }
+      float tg = 0.f, tu = 0.f;
+      if (has_l) {
+        tg = a.t_in[((size_t)q * 2 + 0) * r + lane];
+        tu = a.t_in[((size_t)q * 2 + 1) * r + lane];
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float G = 0.f, U = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          G += sg[ii][j] * chunk_dot128(qg[ii][j], xp[j]) + cg[ii][j] * X[j];
+          U += su[ii][j] * chunk_dot128(qu[ii][j], xp[j]) + cu[ii][j] * X[j];
+        }
+        if (has_l) {
+          G += a.scale * (Bg[ii] * tg);
+          U += a.scale * (Bu[ii] * tu);
+        }
+        G = wave_sum(G);
+        U = wave_sum(U);
+        if (lane == 0) {
+          const float h = grp_silu(G) * U;
+          h_s[4 * wave + ii] = h;
+          hrep_s[4 * wave + ii] = grp_store_h(a, q, row0 + ii, h);
+        }
+      }
+      __syncthreads();
+      grp_rows_epilogue(a, q, blk, i0, h_s, hrep_s, ad0, ad1);
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------- down (GEMV)
+// CPW = 32-input chunks per wave: wave w owns chunks w, w + 4, ... of the
+// tiled down weights of 64 output rows (lane = row).  Tokens in batches of
+// kGrpBT; wave 0 adds the LoRA-down delta and scatters the weighted rows.
+constexpr int kGrpBT = 8;
+constexpr int kGrpMaxNC = 32;  // d_inter <= 1024
+
+template <int CPW>
+__global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int max_cnt) {
+  __shared__ uint32_t hp_s[kGrpBT][kGrpMaxNC][32];  // hi pairs then lo pairs of each chunk
+  __shared__ float hsum_s[kGrpBT][kGrpMaxNC];
+  __shared__ float red[4][kGrpBT][64];
+  __shared__ float td_s[kGrpBT][64];
+  const int nrb = a.d / 64;
+  const int act = blockIdx.x / nrb;
+  const int rb = blockIdx.x % nrb;
+  if (act >= a.info[0]) return;
+  const int n = a.act_cnt[act];
+  if (n < min_cnt || n > max_cnt) return;
+  const uint8_t* b = grp_bundle(a, act);
+  if (b == nullptr) return;
+  const int q0 = a.act_off[act];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d = a.d, I = a.I, r = a.r, NC = I / 32;
+  const int o = rb * 64 + lane;
+  uint4 qv[CPW];
+  float sv[CPW], cv[CPW];
+#pragma unroll
+  for (int m = 0; m < CPW; ++m) {
+    const int c = wave + 4 * m;
+    const bool on = c < NC;
+    const int cc = on ? c : 0;
+    qv[m] = reinterpret_cast<const uint4*>(b + a.lay.down_q)[((size_t)rb * NC + cc) * 64 + lane];
+    const int grp = (32 * cc) / a.g;
+    const float s = bf2f(reinterpret_cast<const uint16_t*>(b + a.lay.down_s)[(size_t)grp * d + o]);
+    const float bb = bf2f(reinterpret_cast<const uint16_t*>(b + a.lay.down_b)[(size_t)grp * d + o]);
+    sv[m] = on ? s : 0.f;
+    cv[m] = on ? bb - 128.f * s : 0.f;
+  }
+  // LoRA-down row o (wave 0): r <= 64 bf16 as packed pairs
+  uint32_t bd[32];
+  if (wave == 0) {
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(b + a.lay.b_down) + (size_t)o * (r / 2);
+#pragma unroll
+    for (int m = 0; m < 32; ++m) bd[m] = 2 * m < r ? src[m] : 0u;
+  }
+  for (int j0 = 0; j0 < n; j0 += kGrpBT) {
+    const int nb = n - j0 < kGrpBT ? n - j0 : kGrpBT;
+    __syncthreads();  // previous batch consumed
+    for (int t = threadIdx.x; t < nb * NC * 32; t += 256) {
+      const int jj = t / (NC * 32), rem = t % (NC * 32);
+      const int c = rem >> 5, wd = rem & 31;
+      const int q = q0 + j0 + jj;
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(wd < 16 ? a.hp_hi : a.hp_lo) + (size_t)q * (I / 2);
+      hp_s[jj][c][wd] = src[16 * c + (wd & 15)];
+    }
+    for (int t = threadIdx.x; t < nb * NC; t += 256) {
+      const int jj = t / NC, c = t % NC;
+      const float* hs = a.hs + (size_t)(q0 + j0 + jj) * (I / 16);
+      hsum_s[jj][c] = hs[2 * c] + hs[2 * c + 1];
+    }
+    for (int t = threadIdx.x; t < nb * r; t += 256) {
+      const int jj = t / r, rr = t % r;
+      td_s[jj][rr] = from_fix(a.tdown[(size_t)(q0 + j0 + jj) * r + rr]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < kGrpBT; ++jj) {
+      float part = 0.f;
+      if (jj < nb) {
+#pragma unroll
+        for (int m = 0; m < CPW; ++m) {
+          const int c = wave + 4 * m;
+          if (c < NC) {
+            const uint32_t* hp = hp_s[jj][c];
+            const float accv = chunk_dot128(qv[m], hp) + chunk_dot128(qv[m], hp + 16);
+            part += sv[m] * accv + cv[m] * hsum_s[jj][c];
+          }
+        }
+      }
+      red[wave][jj][lane] = part;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int jj = 0; jj < nb; ++jj) {
+        float tot = red[0][jj][lane] + red[1][jj][lane] + red[2][jj][lane] + red[3][jj][lane];
+        if (r > 0) {
+          float dl = 0.f;
+#pragma unroll
+          for (int m = 0; m < 32; ++m)
+            if (2 * m < r) dl += bf_lo(bd[m]) * td_s[jj][2 * m] + bf_hi(bd[m]) * td_s[jj][2 * m + 1];
+          tot += a.scale * dl;
+        }
+        const int q = q0 + j0 + jj;
+        atomicAdd(a.acc + (size_t)a.pair_tok[q] * d + o, to_fix(a.pair_w[q] * tot));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ output
+__global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < a.T * a.d) {
+    a.y[i] = (uint16_t)f2bf(from_fix(a.acc[i]));
+    a.acc[i] = 0ull;
+  }
+  for (int j = i; j < a.P * a.r; j += gridDim.x * 256) a.tdown[j] = 0ull;
+}
+
+// ------------------------------------------------------------- host side
+struct GrpWs {
+  size_t err, info, act_e, act_off, act_cnt, act_slot, pair_tok, pair_act, pair_w, t_in, hp_hi,
+      hp_lo, hs, tdown, acc, total;
+};
+static GrpWs grp_ws_layout(const edge0_moe_shape* s) {
+  GrpWs L{};
+  const size_t T = kGrpMaxTokens, d = s->d_model, E = s->n_experts, I = s->d_inter;
+  const size_t P = T * s->top_k, r = s->lora_rank;
+  const size_t A = E < P ? E : P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + (bytes ? bytes : 4) + 255) & ~(size_t)255;
+    return o;
+  };
+  L.err = take(4);
+  L.info = take(16);
+  L.act_e = take(4 * A);
+  L.act_off = take(4 * A);
+  L.act_cnt = take(4 * A);
+  L.act_slot = take(4 * A);
+  L.pair_tok = take(4 * P);
+  L.pair_act = take(4 * P);
+  L.pair_w = take(4 * P);
+  L.t_in = take(4 * P * 2 * r);
+  L.hp_hi = take(2 * P * I);
+  L.hp_lo = take(2 * P * I);
+  L.hs = take(4 * P * (I / 16));
+  L.tdown = take(8 * P * r);
+  L.acc = take(8 * T * d);
+  L.total = off;
+  return L;
+}
+
+static bool grouped_shape_ok(const edge0_moe_shape* s) {
+  return shape_ok(s) && s->d_inter / 32 <= kGrpMaxNC && s->d_model <= 4096;
+}
+
+static int launch_grp_gate_up(const GrpArgs& a, int lo, int hi, hipStream_t st) {
+  const int grid = a.Amax * (a.I / 16);
+  switch ((a.d / 32 + 63) / 64) {
+    case 1: k_grp_gate_up<1><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 2: k_grp_gate_up<2><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    default: return EDGE0_EINVAL;
+  }
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+
+static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
+  const int grid = a.Amax * (a.d / 64);
+  switch ((a.I / 32 + 3) / 4) {
+    case 1: k_grp_down<1><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 2: k_grp_down<2><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 3: k_grp_down<3><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 4: k_grp_down<4><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 5: k_grp_down<5><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 6: k_grp_down<6><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 7: k_grp_down<7><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 8: k_grp_down<8><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    default: return EDGE0_EINVAL;
+  }
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+
+}  // namespace e0
+
+using namespace e0;
+
+extern "C" size_t edge0_grouped_workspace_bytes(const edge0_moe_shape* shape) {
+  if (!grouped_shape_ok(shape)) return 0;
+  return grp_ws_layout(shape).total;
+}
+
+extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                 const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
+                                 const float* w, const void* x, void* y, void* workspace,
+                                 int32_t flags, hipStream_t stream) {
+  if (!shape || !grouped_shape_ok(shape) || !pool || !pool->base || !slot_table || !workspace ||
+      n_tokens < 0 || n_tokens > kGrpMaxTokens || (flags & ~EDGE0_GROUPED_NO_MFMA) != 0)
+    return EDGE0_EINVAL;
+  if (n_tokens == 0) return EDGE0_OK;
+  if (!ids || !w || !x || !y) return EDGE0_EINVAL;
+  edge0_bundle_layout lay;
+  if (bundle_layout(shape, &lay) != EDGE0_OK || pool->slot_bytes < lay.bytes) return EDGE0_EINVAL;
+  const GrpWs L = grp_ws_layout(shape);
+  char* ws = static_cast<char*>(workspace);
+  GrpArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool->base);
+  a.slot_bytes = pool->slot_bytes;
+  a.n_slots = pool->n_slots;
+  a.table = slot_table;
+  a.ids = ids;
+  a.w = w;
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.T = n_tokens;
+  a.d = shape->d_model;
+  a.E = shape->n_experts;
+  a.I = shape->d_inter;
+  a.K = shape->top_k;
+  a.g = shape->group_size;
+  a.r = shape->lora_rank;
+  a.scale = a.r > 0 ? shape->lora_alpha / (float)a.r : 0.f;
+  a.lay = lay;
+  a.P = n_tokens * a.K;
+  a.Amax = a.E < a.P ? a.E : a.P;
+  a.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  a.info = reinterpret_cast<int32_t*>(ws + L.info);
+  a.act_e = reinterpret_cast<int32_t*>(ws + L.act_e);
+  a.act_off = reinterpret_cast<int32_t*>(ws + L.act_off);
+  a.act_cnt = reinterpret_cast<int32_t*>(ws + L.act_cnt);
+  a.act_slot = reinterpret_cast<int32_t*>(ws + L.act_slot);
+  a.pair_tok = reinterpret_cast<int32_t*>(ws + L.pair_tok);
+  a.pair_act = reinterpret_cast<int32_t*>(ws + L.pair_act);
+  a.pair_w = reinterpret_cast<float*>(ws + L.pair_w);
+  a.t_in = reinterpret_cast<float*>(ws + L.t_in);
+  a.hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
+  a.hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
+  a.hs = reinterpret_cast<float*>(ws + L.hs);
+  a.tdown = reinterpret_cast<unsigned long long*>(ws + L.tdown);
+  a.acc = reinterpret_cast<unsigned long long*>(ws + L.acc);
+  k_grp_route<<<1, 1024, 0, stream>>>(a);
+  E0_CHECK_LAUNCH();
+  if (a.r > 0) {
+    k_grp_lora_in<<<(a.P * 2 * a.r + 3) / 4, 256, 0, stream>>>(a);
+    E0_CHECK_LAUNCH();
+  }
+  int rc = launch_grp_gate_up(a, 1, 1 << 30, stream);
+  if (rc != EDGE0_OK) return rc;
+  rc = launch_grp_down(a, 1, 1 << 30, stream);
+  if (rc != EDGE0_OK) return rc;
+  const int n_out = a.T * a.d;
+  k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}

@@ -107,6 +107,9 @@ _SIG = {
     "edge0_stack_kernel_ms": (C.c_int, [_P, C.POINTER(C.c_float), C.c_int32,
                                         C.POINTER(C.c_int32)]),
     "edge0_stack_step_staged": (C.c_int, [_P, _P, C.POINTER(StagePlan), _P, _P, C.c_int32, _P]),
+    "edge0_grouped_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
+    "edge0_moe_grouped": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, C.c_int32, _P,
+                                    _P, _P, _P, _P, C.c_int32, _P]),
     "edge0_lru_create": (C.c_int, [C.POINTER(_P), C.c_int32, C.c_int32, C.c_int32]),
     "edge0_lru_request": (C.c_int, [_P, C.c_int32, C.c_int32, _I32P, C.c_int32, _I32P, _I32P,
                                     _I32P]),
@@ -212,6 +215,24 @@ def edge0_moe_layer(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y, w
     _check(lib.edge0_moe_layer(C.byref(shape), C.byref(pool), _ptr(slot_table), _ptr(ids), _ptr(w),
                                _ptr(x), _ptr(y), _ptr(workspace), _stream(stream)),
            "edge0_moe_layer")
+
+
+EDGE0_GROUPED_NO_MFMA = 1
+
+
+def new_grouped_workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace for edge0_moe_grouped."""
+    n = lib.edge0_grouped_workspace_bytes(C.byref(shape))
+    if n == 0:
+        raise Edge0Error(EDGE0_EINVAL, "edge0_grouped_workspace_bytes")
+    return torch.zeros(int(n), dtype=torch.uint8, device=device)
+
+
+def edge0_moe_grouped(shape: MoeShape, pool: SlotPool, slot_table, n_tokens: int, ids, w, x, y,
+                      workspace, flags: int = 0, stream=None):
+    _check(lib.edge0_moe_grouped(C.byref(shape), C.byref(pool), _ptr(slot_table), n_tokens,
+                                 _ptr(ids), _ptr(w), _ptr(x), _ptr(y), _ptr(workspace), flags,
+                                 _stream(stream)), "edge0_moe_grouped")
 
 
 class Stack:
