@@ -418,6 +418,279 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
   }
 }
 
+// ------------------------------------------------------------ MFMA paths
+// v_mfma_f32_32x32x16_bf16 (lane l: A[l%32][8(l/32)+i], B[8(l/32)+i][l%32],
+// accumulator 4J+i = C[8J + 4(l/32) + i][l%32]).  A = activations (rows =
+// tokens of the expert, padded to 32), B = weights (columns = 32 weight
+// rows), so a lane's 16 accumulators share one weight row and one scale and
+// bias per group.  Per group the products start from zero and are folded in
+// fp32: s * acc + (b - 128 s) * (sum of the group's activations).  Within a
+// group lane half j takes SPG = g/16 consecutive packed words (8 inputs
+// each); step t of the group feeds word j*SPG + t, as exact bf16 128 + q in
+// the pair order (e0,e4,e1,e5,e2,e6,e3,e7), against activations in the same
+// order (pair_perm8, or the pair-permuted h pairs).  The 4 waves split the
+// groups; partial tiles meet in LDS.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ bf16x8_t q4_operand(uint32_t word) {
+  const uint4 v = make_uint4(q4pair(word, 0), q4pair(word, 1), q4pair(word, 2), q4pair(word, 3));
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ bf16x8_t x_operand(uint4 raw) {
+  uint32_t o[4];
+  pair_perm8(raw.x, raw.y, raw.z, raw.w, o);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+__device__ __forceinline__ float raw_sum8(uint4 v) {
+  return bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) +
+         bf_lo(v.w) + bf_hi(v.w);
+}
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// SPG consecutive packed words starting at p (4-byte aligned; 16-byte
+// aligned when SPG >= 4)
+template <int SPG>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[SPG]) {
+  if constexpr (SPG % 4 == 0) {
+#pragma unroll
+    for (int m = 0; m < SPG / 4; ++m) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[m];
+      w[4 * m] = v.x;
+      w[4 * m + 1] = v.y;
+      w[4 * m + 2] = v.z;
+      w[4 * m + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < SPG; ++m) w[m] = p[m];
+  }
+}
+
+constexpr int kMfmaMinTokens = 16;
+
+// One workgroup = 32 rows of one active expert's gate and up, all its tokens
+// in tiles of 32.
+template <int SPG>
+__global__ __launch_bounds__(256) void k_grp_gate_up_mfma(GrpArgs a, int min_cnt) {
+  __shared__ float red[4][2][32][33];  // per wave: [G or U][weight row][token]
+  __shared__ float hbuf[32][33];       // h [token][row]
+  __shared__ float hrep_s[32][33];     // the value the down product sees (hi + lo)
+  __shared__ float tl_s[32][2][64];    // LoRA t of the tile's tokens
+  __shared__ float bl_s[2][32][64];    // B_gate / B_up rows of the block
+  __shared__ float ad_s[64][32];       // A_down columns of the block
+  const int nb32 = a.I / 32;
+  const int act = blockIdx.x / nb32;
+  const int rb = blockIdx.x % nb32;
+  if (act >= a.info[0]) return;
+  const int n = a.act_cnt[act];
+  if (n < min_cnt) return;
+  const uint8_t* b = grp_bundle(a, act);
+  if (b == nullptr) return;
+  const int q0 = a.act_off[act];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nn = lane & 31, jh = lane >> 5;
+  const int d = a.d, g = a.g, ng = d / g, r = a.r, I = a.I;
+  const int row0 = rb * 32, row = row0 + nn;
+  if (r > 0) {
+    const uint16_t* Bg = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
+    const uint16_t* Bu = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
+    for (int t = tid; t < 32 * r; t += 256) {
+      const int rr = t % r, rw = t / r;
+      bl_s[0][rw][rr] = bf2f(Bg[(size_t)(row0 + rw) * r + rr]);
+      bl_s[1][rw][rr] = bf2f(Bu[(size_t)(row0 + rw) * r + rr]);
+    }
+    const uint16_t* Ad = reinterpret_cast<const uint16_t*>(b + a.lay.a_down);
+    for (int t = tid; t < 32 * r; t += 256) {
+      const int c = t % 32, rr = t / 32;
+      ad_s[rr][c] = bf2f(Ad[(size_t)rr * I + row0 + c]);
+    }
+  }
+  const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
+  const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
+  const uint16_t* gsp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s) + (size_t)row * ng;
+  const uint16_t* gbp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b) + (size_t)row * ng;
+  const uint16_t* usp = reinterpret_cast<const uint16_t*>(b + a.lay.up_s) + (size_t)row * ng;
+  const uint16_t* ubp = reinterpret_cast<const uint16_t*>(b + a.lay.up_b) + (size_t)row * ng;
+  for (int t0 = 0; t0 < n; t0 += 32) {
+    const int mt = n - t0 < 32 ? n - t0 : 32;
+    __syncthreads();  // LDS of the previous tile consumed; staging above done
+    for (int t = tid; t < mt * 2 * r; t += 256) {
+      const int m = t / (2 * r), rem = t % (2 * r);
+      tl_s[m][rem / r][rem % r] = a.t_in[(size_t)(q0 + t0 + m) * 2 * r + rem];
+    }
+    const bool tok_ok = nn < mt;
+    const uint16_t* xrow = a.x + (size_t)a.pair_tok[q0 + t0 + (tok_ok ? nn : 0)] * d;
+    f32x16_t accG, accU;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accG[v] = accU[v] = 0.f;
+    for (int G = wave; G < ng; G += 4) {
+      uint32_t wg[SPG], wu[SPG];
+      load_words<SPG>(gq + (size_t)G * (g / 8) + jh * SPG, wg);
+      load_words<SPG>(uq + (size_t)G * (g / 8) + jh * SPG, wu);
+      uint4 xr[SPG];
+#pragma unroll
+      for (int t = 0; t < SPG; ++t)
+        xr[t] = tok_ok ? reinterpret_cast<const uint4*>(xrow + G * g + jh * (g / 2))[t]
+                       : make_uint4(0, 0, 0, 0);
+      const float sg = bf2f(gsp[G]), cbg = bf2f(gbp[G]) - 128.f * sg;
+      const float su = bf2f(usp[G]), cbu = bf2f(ubp[G]) - 128.f * su;
+      float sx = 0.f;
+#pragma unroll
+      for (int t = 0; t < SPG; ++t) sx += raw_sum8(xr[t]);
+      sx += __shfl_xor(sx, 32, kWave);  // the group's sum for token nn
+      f32x16_t cg, cu;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cg[v] = cu[v] = 0.f;
+#pragma unroll
+      for (int t = 0; t < SPG; ++t) {
+        const bf16x8_t xo = x_operand(xr[t]);
+        cg = mfma32(xo, q4_operand(wg[t]), cg);
+        cu = mfma32(xo, q4_operand(wu[t]), cu);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+        const float sxm = __shfl(sx, m, kWave);
+        accG[v] += sg * cg[v] + cbg * sxm;
+        accU[v] += su * cu[v] + cbu * sxm;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+      red[wave][0][nn][m] = accG[v];
+      red[wave][1][nn][m] = accU[v];
+    }
+    __syncthreads();
+    for (int t = tid; t < mt * 32; t += 256) {
+      const int m = t / 32, rw = t % 32;
+      float Gv = red[0][0][rw][m] + red[1][0][rw][m] + red[2][0][rw][m] + red[3][0][rw][m];
+      float Uv = red[0][1][rw][m] + red[1][1][rw][m] + red[2][1][rw][m] + red[3][1][rw][m];
+      if (r > 0) {
+        float dg = 0.f, du = 0.f;
+        for (int rr = 0; rr < r; ++rr) {
+          dg += bl_s[0][rw][rr] * tl_s[m][0][rr];
+          du += bl_s[1][rw][rr] * tl_s[m][1][rr];
+        }
+        Gv += a.scale * dg;
+        Uv += a.scale * du;
+      }
+      const float h = grp_silu(Gv) * Uv;
+      hbuf[m][rw] = h;
+      hrep_s[m][rw] = grp_store_h(a, q0 + t0 + m, row0 + rw, h);
+    }
+    __syncthreads();
+    for (int t = tid; t < mt * 2; t += 256) {
+      const int m = t / 2, half = t % 2;
+      float sm = 0.f;
+      for (int k = 0; k < 16; ++k) sm += hrep_s[m][16 * half + k];
+      a.hs[(size_t)(q0 + t0 + m) * (I / 16) + rb * 2 + half] = sm;
+    }
+    for (int t = tid; t < mt * r; t += 256) {
+      const int m = t / r, rr = t % r;
+      float sm = 0.f;
+      for (int k = 0; k < 32; ++k) sm += ad_s[rr][k] * hbuf[m][k];
+      atomicAdd(a.tdown + (size_t)(q0 + t0 + m) * r + rr, to_fix(sm));
+    }
+  }
+}
+
+// One workgroup = 32 output rows of one active expert's down projection,
+// all its tokens in tiles of 32; h enters as its bf16 hi and lo parts.
+template <int SPG>
+__global__ __launch_bounds__(256) void k_grp_down_mfma(GrpArgs a, int min_cnt) {
+  __shared__ float red[4][32][33];  // per wave: [output row][token]
+  __shared__ float bd_s[32][64];    // B_down rows of the block
+  __shared__ float td_s[32][64];    // t_down of the tile's tokens
+  const int nb32 = a.d / 32;
+  const int act = blockIdx.x / nb32;
+  const int ob = blockIdx.x % nb32;
+  if (act >= a.info[0]) return;
+  const int n = a.act_cnt[act];
+  if (n < min_cnt) return;
+  const uint8_t* b = grp_bundle(a, act);
+  if (b == nullptr) return;
+  const int q0 = a.act_off[act];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nn = lane & 31, jh = lane >> 5;
+  const int d = a.d, g = a.g, I = a.I, r = a.r, NC = I / 32, ngI = I / g;
+  const int o0 = ob * 32, o = o0 + nn;
+  const int trb = o / 64, within = o % 64;
+  if (r > 0) {
+    const uint16_t* Bd = reinterpret_cast<const uint16_t*>(b + a.lay.b_down);
+    for (int t = tid; t < 32 * r; t += 256) bd_s[t / r][t % r] = bf2f(Bd[(size_t)(o0 + t / r) * r + t % r]);
+  }
+  const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q);
+  const uint16_t* dsp = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
+  const uint16_t* dbp = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
+  for (int t0 = 0; t0 < n; t0 += 32) {
+    const int mt = n - t0 < 32 ? n - t0 : 32;
+    __syncthreads();
+    for (int t = tid; t < mt * r; t += 256)
+      td_s[t / r][t % r] = from_fix(a.tdown[(size_t)(q0 + t0 + t / r) * r + t % r]);
+    const bool tok_ok = nn < mt;
+    const int q = q0 + t0 + (tok_ok ? nn : 0);
+    const uint16_t* hhi = a.hp_hi + (size_t)q * I;
+    const uint16_t* hlo = a.hp_lo + (size_t)q * I;
+    const float* hsq = a.hs + (size_t)q * (I / 16);
+    f32x16_t acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int G = wave; G < ngI; G += 4) {
+      // words j*SPG .. j*SPG+SPG-1 of the group: input i0 = G*g + j*g/2, in
+      // the tiled layout chunk i0/32, word (i0%32)/8 of row o's 16 bytes
+      const int i0 = G * g + jh * (g / 2);
+      uint32_t wd[SPG];
+#pragma unroll
+      for (int t = 0; t < SPG; ++t) {
+        const int ii = i0 + 8 * t;
+        wd[t] = dq[(((size_t)trb * NC + ii / 32) * 64 + within) * 4 + (ii % 32) / 8];
+      }
+      uint4 hh[SPG], hl[SPG];
+#pragma unroll
+      for (int t = 0; t < SPG; ++t) {
+        hh[t] = tok_ok ? reinterpret_cast<const uint4*>(hhi + i0)[t] : make_uint4(0, 0, 0, 0);
+        hl[t] = tok_ok ? reinterpret_cast<const uint4*>(hlo + i0)[t] : make_uint4(0, 0, 0, 0);
+      }
+      const float sd = bf2f(dsp[(size_t)G * d + o]);
+      const float cbd = bf2f(dbp[(size_t)G * d + o]) - 128.f * sd;
+      float sh = 0.f;
+      if (tok_ok)
+        for (int k = 0; k < g / 16; ++k) sh += hsq[G * (g / 16) + k];
+      f32x16_t c;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c[v] = 0.f;
+#pragma unroll
+      for (int t = 0; t < SPG; ++t) {
+        const bf16x8_t wo = q4_operand(wd[t]);
+        c = mfma32(__builtin_bit_cast(bf16x8_t, hh[t]), wo, c);
+        c = mfma32(__builtin_bit_cast(bf16x8_t, hl[t]), wo, c);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+        acc[v] += sd * c[v] + cbd * __shfl(sh, m, kWave);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave][nn][8 * (v >> 2) + 4 * jh + (v & 3)] = acc[v];
+    __syncthreads();
+    for (int t = tid; t < mt * 32; t += 256) {
+      const int m = t / 32, rw = t % 32;
+      float tot = red[0][rw][m] + red[1][rw][m] + red[2][rw][m] + red[3][rw][m];
+      if (r > 0) {
+        float dl = 0.f;
+        for (int rr = 0; rr < r; ++rr) dl += bd_s[rw][rr] * td_s[m][rr];
+        tot += a.scale * dl;
+      }
+      const int qq = q0 + t0 + m;
+      atomicAdd(a.acc + (size_t)a.pair_tok[qq] * d + o0 + rw, to_fix(a.pair_w[qq] * tot));
+    }
+  }
+}
+
 // ------------------------------------------------------------ output
 __global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -464,7 +737,9 @@ static GrpWs grp_ws_layout(const edge0_moe_shape* s) {
 }
 
 static bool grouped_shape_ok(const edge0_moe_shape* s) {
-  return shape_ok(s) && s->d_inter / 32 <= kGrpMaxNC && s->d_model <= 4096;
+  const int g = s->group_size;
+  return shape_ok(s) && s->d_inter / 32 <= kGrpMaxNC && s->d_model <= 4096 &&
+         (g == 32 || g == 64 || g == 128);
 }
 
 static int launch_grp_gate_up(const GrpArgs& a, int lo, int hi, hipStream_t st) {
@@ -491,6 +766,24 @@ static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
     case 8: k_grp_down<8><<<grid, 256, 0, st>>>(a, lo, hi); break;
     default: return EDGE0_EINVAL;
   }
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+
+// which = 0 gate/up, 1 down
+static int launch_grp_mfma(const GrpArgs& a, int which, hipStream_t st) {
+  const int grid = a.Amax * ((which ? a.d : a.I) / 32);
+  const int spg = a.g / 16;
+#define E0_GRP_MFMA(S)                                                   \
+  if (which) k_grp_down_mfma<S><<<grid, 256, 0, st>>>(a, kMfmaMinTokens); \
+  else k_grp_gate_up_mfma<S><<<grid, 256, 0, st>>>(a, kMfmaMinTokens)
+  switch (spg) {
+    case 2: E0_GRP_MFMA(2); break;
+    case 4: E0_GRP_MFMA(4); break;
+    case 8: E0_GRP_MFMA(8); break;
+    default: return EDGE0_EINVAL;
+  }
+#undef E0_GRP_MFMA
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
@@ -558,9 +851,13 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
     k_grp_lora_in<<<(a.P * 2 * a.r + 3) / 4, 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
   }
-  int rc = launch_grp_gate_up(a, 1, 1 << 30, stream);
-  if (rc != EDGE0_OK) return rc;
-  rc = launch_grp_down(a, 1, 1 << 30, stream);
+  // experts with >= kMfmaMinTokens tokens on MFMA, the others as GEMVs
+  const bool mfma = !(flags & EDGE0_GROUPED_NO_MFMA) && n_tokens >= kMfmaMinTokens;
+  const int gemv_max = mfma ? kMfmaMinTokens - 1 : 1 << 30;
+  int rc = launch_grp_gate_up(a, 1, gemv_max, stream);
+  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 0, stream);
+  if (rc == EDGE0_OK) rc = launch_grp_down(a, 1, gemv_max, stream);
+  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 1, stream);
   if (rc != EDGE0_OK) return rc;
   const int n_out = a.T * a.d;
   k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);

@@ -63,10 +63,13 @@ def test_grouped_tiny(torch_cuda, T):
     lay = _layer(S)
     ids, w = G.grouped_routing(S.n_experts, S.top_k, T, seed=10 + T)
     x = G.hidden(S, 20 + T, n=T)
+    ys = {}
     for flags in (0, 1):
         y, _ = _call(lay, ids, w, x, flags)
+        ys[flags] = y
         worst = _check(lay, ids, w, x, y)
         print(f"[grouped] tiny T={T} flags={flags}: worst rel-L2 {worst:.3e}")
+    _paths_ran(ys, ids, np.bincount(ids.ravel(), minlength=S.n_experts))
 
 
 @pytest.mark.parametrize("T", [1, 4, 8, 16, 32])
@@ -76,12 +79,28 @@ def test_grouped_qwen3moe_k8(torch_cuda, T):
     ids, w = G.grouped_routing(S.n_experts, 8, T, seed=T)
     x = G.hidden(S, 100 + T, n=T)
     counts = np.bincount(ids.ravel(), minlength=S.n_experts)
+    ys = {}
     for flags in (0, 1):
         y, _ = _call(lay, ids, w, x, flags)
+        ys[flags] = y
         worst = _check(lay, ids, w, x, y)
         print(f"[grouped] qwen3moe K=8 T={T} flags={flags}: {np.count_nonzero(counts)} experts, "
               f"max {counts.max()} tokens/expert, {int((counts >= 16).sum())} on MFMA; "
               f"worst rel-L2 {worst:.3e}")
+    _paths_ran(ys, ids, counts)
+
+
+def _paths_ran(ys, ids, counts):
+    """Tokens routed only to GEMV experts are bit-identical between the two
+    calls; a token that uses an MFMA expert shows the MFMA path's rounding
+    (at least one must differ when any expert has >= 16 tokens)."""
+    big = set(np.nonzero(counts >= 16)[0].tolist())
+    differs = [not np.array_equal(ys[0][j], ys[1][j]) for j in range(ids.shape[0])]
+    for j in range(ids.shape[0]):
+        if not big.intersection(ids[j].tolist()):
+            assert not differs[j], j
+    if big:
+        assert any(differs)
 
 
 def test_grouped_deterministic_and_workspace_reuse(torch_cuda):
