@@ -263,6 +263,88 @@ def bench_streamed(args, log):
     print(json.dumps(out), flush=True)
 
 
+def bench_grouped(args, log):
+    """Grouped multi-token layer (Qwen3-MoE shapes, K = 8) at 1, 4, 8, 16 and
+    32 tokens per call, Zipf(1.1) routing.  Calls rotate over 64 layer
+    instances in distinct HBM slots (8 generated layers, each placed 8 times),
+    so the 256 MB MALL holds no earlier call's experts."""
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import pack_layer
+    from int4_expert_streaming_amd.weights import SlotPoolBuffer, to_device
+    S = G.QWEN3_MOE.with_k(8)
+    sh = E.make_shape(S)
+    En, K, d, I, r = S.n_experts, S.top_k, S.d_model, S.d_inter, S.lora_rank
+    n_gen, n_inst = 8, 64
+    gen = G.StackGen(S, args.seed)
+    pool = SlotPoolBuffer(sh, n_inst * En)
+    bb = pool.slot_bytes
+    t0 = time.time()
+    for L in range(n_gen):
+        parts = [(gen.expert(L, e), gen.lora(L, e)) for e in range(En)]
+        pack_layer(sh, parts, lambda e: pool.slot_ptr(L * En + e))
+    for i in range(n_gen, n_inst):  # copies of the generated layers at new addresses
+        src = (i % n_gen) * En * bb
+        pool.mem[i * En * bb:(i + 1) * En * bb].copy_(pool.mem[src:src + En * bb])
+    torch.cuda.synchronize()
+    log(f"[grouped] {n_inst} layer instances ready ({time.time() - t0:.1f}s), "
+        f"{pool.mem.numel() / 1e9:.1f} GB")
+    tables = [torch.arange(i * En, (i + 1) * En, dtype=torch.int32, device="cuda")
+              for i in range(n_inst)]
+    ws = E.new_grouped_workspace(sh)
+    stream = torch.cuda.current_stream()
+    results = {}
+    for T in (1, 4, 8, 16, 32):
+        routes = [G.grouped_routing(En, K, T, seed=args.seed * 1000 + 17 * T + i, layer=i % n_gen)
+                  for i in range(n_inst)]
+        ids = [to_device(rt[0]) for rt in routes]
+        ws_ = [torch.from_numpy(rt[1]).cuda() for rt in routes]
+        xs = [to_device(G.hidden(S, 500 + T * 100 + i, n=T)) for i in range(n_inst)]
+        y = torch.empty((T, d), dtype=torch.int16, device="cuda")
+        counts = [np.bincount(rt[0].ravel(), minlength=En) for rt in routes]
+        union = float(np.mean([np.count_nonzero(c) for c in counts]))
+        on_mfma = float(np.mean([int((c >= 16).sum()) for c in counts])) if T >= 16 else 0.0
+
+        def call(i):
+            E.edge0_moe_grouped(sh, pool.pool, tables[i], T, ids[i], ws_[i], xs[i], y, ws)
+
+        for i in range(32):
+            call(i % n_inst)
+        torch.cuda.synchronize()
+        n_calls = 256
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for c in range(n_calls):
+            call(c % n_inst)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+        nbytes = union * bb
+        flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
+        results[T] = {"us_per_call": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
+                      "experts": round(union, 2), "experts_on_mfma": round(on_mfma, 2),
+                      "union_bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "tflops": round(flops / (us * 1e-6) / 1e12, 3)}
+        log(f"[grouped] T={T}: {results[T]}")
+    best = results[32]
+    out = {
+        "metric": "grouped MoE layer tok/s (K=8, Qwen3-MoE shapes) + union-bytes GB/s vs peak",
+        "value": best["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": 256, "warmup": 32,
+        "ms_per_step": round(best["us_per_call"] / 1000, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "one Qwen3-MoE-shaped layer, 32 tokens per call, K=8, Zipf(1.1) "
+                               "routing, 64 rotated layer instances",
+                   "d_model": d, "n_experts": En, "d_inter": I, "top_k": K, "group": S.group,
+                   "lora_rank": r, "global_batch": 32, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": best["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": best["frac_of_hbm_peak"], "traffic": None},
+        "per_tokens": {str(k): v for k, v in results.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,9 +352,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--workload", choices=["resident", "streamed"], default="resident",
+    ap.add_argument("--workload", choices=["resident", "streamed", "grouped"], default="resident",
                     help="resident: every bundle in HBM (the headline line); streamed: "
-                         "experts staged from pinned host memory into a 3 GiB pool")
+                         "experts staged from pinned host memory into a 3 GiB pool; grouped: "
+                         "the multi-token grouped layer at 1-32 tokens per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (hardware counter "
                          "calibration: known bytes moved) and exit")
@@ -297,6 +380,9 @@ def main():
 
     if args.workload == "streamed":
         bench_streamed(args, log)
+        return
+    if args.workload == "grouped":
+        bench_grouped(args, log)
         return
 
     import torch
