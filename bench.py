@@ -306,20 +306,27 @@ def bench_grouped(args, log):
         union = float(np.mean([np.count_nonzero(c) for c in counts]))
         on_mfma = float(np.mean([int((c >= 16).sum()) for c in counts])) if T >= 16 else 0.0
 
-        def call(i):
-            E.edge0_moe_grouped(sh, pool.pool, tables[i], T, ids[i], ws_[i], xs[i], y, ws)
+        def timed(flags, n_calls=256):
+            for i in range(32):
+                E.edge0_moe_grouped(sh, pool.pool, tables[i % n_inst], T, ids[i % n_inst],
+                                    ws_[i % n_inst], xs[i % n_inst], y, ws, flags)
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for c in range(n_calls):
+                i = c % n_inst
+                E.edge0_moe_grouped(sh, pool.pool, tables[i], T, ids[i], ws_[i], xs[i], y, ws,
+                                    flags)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) * 1e3 / n_calls
 
-        for i in range(32):
-            call(i % n_inst)
-        torch.cuda.synchronize()
-        n_calls = 256
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for c in range(n_calls):
-            call(c % n_inst)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+        us = timed(0)
+        if args.mfma_sweep:
+            sweep = {"gemv_only": round(timed(E.EDGE0_GROUPED_NO_MFMA), 2)}
+            for mn in (1, 2, 4, 8):
+                sweep[f"mfma_from_{mn}"] = round(timed(E.grouped_mfma_min(mn)), 2)
+            log(f"[grouped] T={T} us/call by MFMA threshold: default {us:.2f}, {sweep}")
         nbytes = union * bb
         flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
         results[T] = {"us_per_call": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
@@ -356,6 +363,8 @@ def main():
                     help="resident: every bundle in HBM (the headline line); streamed: "
                          "experts staged from pinned host memory into a 3 GiB pool; grouped: "
                          "the multi-token grouped layer at 1-32 tokens per call")
+    ap.add_argument("--mfma-sweep", action="store_true",
+                    help="grouped workload: also time other MFMA thresholds")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (hardware counter "
                          "calibration: known bytes moved) and exit")

@@ -225,10 +225,13 @@ int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
  *   workspace  : edge0_grouped_workspace_bytes(shape) bytes, zero-filled once
  *                before first use (calls leave it ready for the next call);
  *                calls that may run concurrently need distinct workspaces
- *   flags      : 0, or EDGE0_GROUPED_NO_MFMA to run every expert as GEMVs
+ *   flags      : 0, or EDGE0_GROUPED_NO_MFMA to run every expert as GEMVs;
+ *                EDGE0_GROUPED_MFMA_MIN(n) (1 <= n <= 255) moves the MFMA
+ *                threshold from 16 tokens per expert to n
  * Supported shapes: those of edge0_moe_layer with d_inter <= 1024 and
  * d_model <= 4096 (edge0_grouped_workspace_bytes returns 0 otherwise). */
 enum { EDGE0_GROUPED_NO_MFMA = 1 };
+#define EDGE0_GROUPED_MFMA_MIN(n) (((n) & 0xFF) << 8)
 size_t edge0_grouped_workspace_bytes(const edge0_moe_shape* shape);
 int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                       const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,

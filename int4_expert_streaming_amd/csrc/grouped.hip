@@ -50,7 +50,7 @@ struct GrpArgs {
   int P;     // T*K
   // workspace
   uint32_t* err;
-  int32_t* info;      // [0] active experts, [1] valid pairs, [2] experts with >= 16 tokens
+  int32_t* info;      // [0] active experts, [1] valid pairs
   int32_t* act_e;     // [Amax]
   int32_t* act_off;   // [Amax] first sorted pair
   int32_t* act_cnt;   // [Amax]
@@ -67,13 +67,30 @@ struct GrpArgs {
 };
 
 // ------------------------------------------------------------- bucketing
+// inclusive prefix sum over a wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// One workgroup of 1024 threads, one expert per thread (E <= 1024): counts
+// by LDS atomics, exclusive scans of the counts and of the "active" flags,
+// then each pair's destination = its expert's first sorted position + the
+// number of earlier pairs of the same expert (stable).
 __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
   __shared__ int cnt[1024];
   __shared__ int first[1024];
+  __shared__ int actidx[1024];
   __shared__ int ids_s[kGrpMaxTokens * 16];
-  const int tid = threadIdx.x;
+  __shared__ int wtot[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.P;
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  cnt[tid] = 0;
   for (int p = tid; p < P; p += 1024) {
     int e = a.ids[p];
     if (e < 0 || e >= E) {
@@ -86,31 +103,42 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
   for (int p = tid; p < P; p += 1024)
     if (ids_s[p] >= 0) atomicAdd(&cnt[ids_s[p]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int na = 0, run = 0, big = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt[e];
-      first[e] = run;
-      if (c > 0) {
-        a.act_e[na] = e;
-        a.act_off[na] = run;
-        a.act_cnt[na] = c;
-        const int s = a.table[e];
-        const bool ok = s >= 0 && s < a.n_slots;
-        a.act_slot[na] = ok ? s : -1;
-        if (!ok) set_error(a.err, EDGE0_ERANGE);
-        big += c >= 16;
-        cnt[e] = na;  // from here on: the active index of expert e
-        ++na;
-        run += c;
-      }
-    }
-    a.info[0] = na;
-    a.info[1] = run;
-    a.info[2] = big;
+  const int c = tid < E ? cnt[tid] : 0;
+  const int f = c > 0 ? 1 : 0;
+  const int ic = wave_incl_scan(c), iff = wave_incl_scan(f);
+  if (lane == 63) {
+    wtot[0][wave] = ic;
+    wtot[1][wave] = iff;
   }
   __syncthreads();
-  // stable scatter: a pair's rank among the earlier pairs of its expert
+  int bc = 0, bf = 0, tc = 0, tf = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) {
+      bc += wtot[0][w];
+      bf += wtot[1][w];
+    }
+    tc += wtot[0][w];
+    tf += wtot[1][w];
+  }
+  const int xc = bc + ic - c, xf = bf + iff - f;  // exclusive prefixes
+  if (tid < E) {
+    first[tid] = xc;
+    actidx[tid] = xf;
+    if (f) {
+      a.act_e[xf] = tid;
+      a.act_off[xf] = xc;
+      a.act_cnt[xf] = c;
+      const int s = a.table[tid];
+      const bool ok = s >= 0 && s < a.n_slots;
+      a.act_slot[xf] = ok ? s : -1;
+      if (!ok) set_error(a.err, EDGE0_ERANGE);
+    }
+  }
+  if (tid == 0) {
+    a.info[0] = tf;
+    a.info[1] = tc;
+  }
+  __syncthreads();
   for (int p = tid; p < P; p += 1024) {
     const int e = ids_s[p];
     if (e < 0) continue;
@@ -118,7 +146,7 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
     for (int q = 0; q < p; ++q) rank += ids_s[q] == e;
     const int dst = first[e] + rank;
     a.pair_tok[dst] = p / a.K;
-    a.pair_act[dst] = cnt[e];
+    a.pair_act[dst] = actidx[e];
     a.pair_w[dst] = a.w[p];
   }
 }
@@ -469,6 +497,7 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[SPG]
 }
 
 constexpr int kMfmaMinTokens = 16;
+constexpr int kGW = 8;  // groups per wave per pass (their weights held in registers)
 
 // One workgroup = 32 rows of one active expert's gate and up, all its tokens
 // in tiles of 32.
@@ -525,36 +554,62 @@ __global__ __launch_bounds__(256) void k_grp_gate_up_mfma(GrpArgs a, int min_cnt
     f32x16_t accG, accU;
 #pragma unroll
     for (int v = 0; v < 16; ++v) accG[v] = accU[v] = 0.f;
-    for (int G = wave; G < ng; G += 4) {
-      uint32_t wg[SPG], wu[SPG];
-      load_words<SPG>(gq + (size_t)G * (g / 8) + jh * SPG, wg);
-      load_words<SPG>(uq + (size_t)G * (g / 8) + jh * SPG, wu);
-      uint4 xr[SPG];
+    // passes of up to kGW groups per wave: every weight load of the pass is
+    // issued first, the activations of group i+1 while group i computes
+    for (int G0 = wave; G0 < ng; G0 += 4 * kGW) {
+      uint32_t wg[kGW][SPG], wu[kGW][SPG];
+      uint32_t sc[kGW][4];  // raw bf16 s, b of gate and up
 #pragma unroll
-      for (int t = 0; t < SPG; ++t)
-        xr[t] = tok_ok ? reinterpret_cast<const uint4*>(xrow + G * g + jh * (g / 2))[t]
-                       : make_uint4(0, 0, 0, 0);
-      const float sg = bf2f(gsp[G]), cbg = bf2f(gbp[G]) - 128.f * sg;
-      const float su = bf2f(usp[G]), cbu = bf2f(ubp[G]) - 128.f * su;
-      float sx = 0.f;
-#pragma unroll
-      for (int t = 0; t < SPG; ++t) sx += raw_sum8(xr[t]);
-      sx += __shfl_xor(sx, 32, kWave);  // the group's sum for token nn
-      f32x16_t cg, cu;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) cg[v] = cu[v] = 0.f;
-#pragma unroll
-      for (int t = 0; t < SPG; ++t) {
-        const bf16x8_t xo = x_operand(xr[t]);
-        cg = mfma32(xo, q4_operand(wg[t]), cg);
-        cu = mfma32(xo, q4_operand(wu[t]), cu);
+      for (int i = 0; i < kGW; ++i) {
+        const int G = G0 + 4 * i;
+        if (G < ng) {
+          load_words<SPG>(gq + (size_t)G * (g / 8) + jh * SPG, wg[i]);
+          load_words<SPG>(uq + (size_t)G * (g / 8) + jh * SPG, wu[i]);
+          sc[i][0] = gsp[G];
+          sc[i][1] = gbp[G];
+          sc[i][2] = usp[G];
+          sc[i][3] = ubp[G];
+        }
       }
+      uint4 xr[2][SPG];
+      auto load_x = [&](int i, uint4 (&dst)[SPG]) {
+        const int G = G0 + 4 * i;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-        const float sxm = __shfl(sx, m, kWave);
-        accG[v] += sg * cg[v] + cbg * sxm;
-        accU[v] += su * cu[v] + cbu * sxm;
+        for (int t = 0; t < SPG; ++t)
+          dst[t] = (tok_ok && G < ng)
+                       ? reinterpret_cast<const uint4*>(xrow + G * g + jh * (g / 2))[t]
+                       : make_uint4(0, 0, 0, 0);
+      };
+      load_x(0, xr[0]);
+#pragma unroll
+      for (int i = 0; i < kGW; ++i) {
+        const int G = G0 + 4 * i;
+        if (i + 1 < kGW) load_x(i + 1, xr[(i + 1) & 1]);
+        if (G < ng) {
+          const uint4* xv = xr[i & 1];
+          const float sg = bf2f(sc[i][0]), cbg = bf2f(sc[i][1]) - 128.f * sg;
+          const float su = bf2f(sc[i][2]), cbu = bf2f(sc[i][3]) - 128.f * su;
+          float sx = 0.f;
+#pragma unroll
+          for (int t = 0; t < SPG; ++t) sx += raw_sum8(xv[t]);
+          sx += __shfl_xor(sx, 32, kWave);  // the group's sum for token nn
+          f32x16_t cg, cu;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) cg[v] = cu[v] = 0.f;
+#pragma unroll
+          for (int t = 0; t < SPG; ++t) {
+            const bf16x8_t xo = x_operand(xv[t]);
+            cg = mfma32(xo, q4_operand(wg[i][t]), cg);
+            cu = mfma32(xo, q4_operand(wu[i][t]), cu);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+            const float sxm = __shfl(sx, m, kWave);
+            accG[v] += sg * cg[v] + cbg * sxm;
+            accU[v] += su * cu[v] + cbu * sxm;
+          }
+        }
       }
     }
 #pragma unroll
@@ -638,40 +693,63 @@ __global__ __launch_bounds__(256) void k_grp_down_mfma(GrpArgs a, int min_cnt) {
     f32x16_t acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    for (int G = wave; G < ngI; G += 4) {
-      // words j*SPG .. j*SPG+SPG-1 of the group: input i0 = G*g + j*g/2, in
-      // the tiled layout chunk i0/32, word (i0%32)/8 of row o's 16 bytes
-      const int i0 = G * g + jh * (g / 2);
-      uint32_t wd[SPG];
+    for (int G0 = wave; G0 < ngI; G0 += 4 * kGW) {
+      // the pass's weights first: words j*SPG .. of each group (input
+      // i0 = G*g + j*g/2; tiled layout: chunk i0/32, word (i0%32)/8 of row
+      // o's 16 bytes), then the h pairs of group i+1 while group i computes
+      uint32_t wd[kGW][SPG];
+      uint32_t sc[kGW][2];
 #pragma unroll
-      for (int t = 0; t < SPG; ++t) {
-        const int ii = i0 + 8 * t;
-        wd[t] = dq[(((size_t)trb * NC + ii / 32) * 64 + within) * 4 + (ii % 32) / 8];
+      for (int i = 0; i < kGW; ++i) {
+        const int G = G0 + 4 * i;
+        if (G < ngI) {
+          const int i0 = G * g + jh * (g / 2);
+#pragma unroll
+          for (int t = 0; t < SPG; ++t) {
+            const int ii = i0 + 8 * t;
+            wd[i][t] = dq[(((size_t)trb * NC + ii / 32) * 64 + within) * 4 + (ii % 32) / 8];
+          }
+          sc[i][0] = dsp[(size_t)G * d + o];
+          sc[i][1] = dbp[(size_t)G * d + o];
+        }
       }
-      uint4 hh[SPG], hl[SPG];
+      uint4 hh[2][SPG], hl[2][SPG];
+      auto load_h = [&](int i, uint4 (&dh)[SPG], uint4 (&dl)[SPG]) {
+        const int G = G0 + 4 * i;
+        const int i0 = G * g + jh * (g / 2);
+        const bool on = tok_ok && G < ngI;
 #pragma unroll
-      for (int t = 0; t < SPG; ++t) {
-        hh[t] = tok_ok ? reinterpret_cast<const uint4*>(hhi + i0)[t] : make_uint4(0, 0, 0, 0);
-        hl[t] = tok_ok ? reinterpret_cast<const uint4*>(hlo + i0)[t] : make_uint4(0, 0, 0, 0);
-      }
-      const float sd = bf2f(dsp[(size_t)G * d + o]);
-      const float cbd = bf2f(dbp[(size_t)G * d + o]) - 128.f * sd;
-      float sh = 0.f;
-      if (tok_ok)
-        for (int k = 0; k < g / 16; ++k) sh += hsq[G * (g / 16) + k];
-      f32x16_t c;
+        for (int t = 0; t < SPG; ++t) {
+          dh[t] = on ? reinterpret_cast<const uint4*>(hhi + i0)[t] : make_uint4(0, 0, 0, 0);
+          dl[t] = on ? reinterpret_cast<const uint4*>(hlo + i0)[t] : make_uint4(0, 0, 0, 0);
+        }
+      };
+      load_h(0, hh[0], hl[0]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) c[v] = 0.f;
+      for (int i = 0; i < kGW; ++i) {
+        const int G = G0 + 4 * i;
+        if (i + 1 < kGW) load_h(i + 1, hh[(i + 1) & 1], hl[(i + 1) & 1]);
+        if (G < ngI) {
+          const float sd = bf2f(sc[i][0]);
+          const float cbd = bf2f(sc[i][1]) - 128.f * sd;
+          float sh = 0.f;
+          if (tok_ok)
+            for (int k = 0; k < g / 16; ++k) sh += hsq[G * (g / 16) + k];
+          f32x16_t c;
 #pragma unroll
-      for (int t = 0; t < SPG; ++t) {
-        const bf16x8_t wo = q4_operand(wd[t]);
-        c = mfma32(__builtin_bit_cast(bf16x8_t, hh[t]), wo, c);
-        c = mfma32(__builtin_bit_cast(bf16x8_t, hl[t]), wo, c);
-      }
+          for (int v = 0; v < 16; ++v) c[v] = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-        acc[v] += sd * c[v] + cbd * __shfl(sh, m, kWave);
+          for (int t = 0; t < SPG; ++t) {
+            const bf16x8_t wo = q4_operand(wd[i][t]);
+            c = mfma32(__builtin_bit_cast(bf16x8_t, hh[i & 1][t]), wo, c);
+            c = mfma32(__builtin_bit_cast(bf16x8_t, hl[i & 1][t]), wo, c);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+            acc[v] += sd * c[v] + cbd * __shfl(sh, m, kWave);
+          }
+        }
       }
     }
 #pragma unroll
@@ -771,12 +849,12 @@ static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
 }
 
 // which = 0 gate/up, 1 down
-static int launch_grp_mfma(const GrpArgs& a, int which, hipStream_t st) {
+static int launch_grp_mfma(const GrpArgs& a, int which, int min_cnt, hipStream_t st) {
   const int grid = a.Amax * ((which ? a.d : a.I) / 32);
   const int spg = a.g / 16;
-#define E0_GRP_MFMA(S)                                                   \
-  if (which) k_grp_down_mfma<S><<<grid, 256, 0, st>>>(a, kMfmaMinTokens); \
-  else k_grp_gate_up_mfma<S><<<grid, 256, 0, st>>>(a, kMfmaMinTokens)
+#define E0_GRP_MFMA(S)                                            \
+  if (which) k_grp_down_mfma<S><<<grid, 256, 0, st>>>(a, min_cnt); \
+  else k_grp_gate_up_mfma<S><<<grid, 256, 0, st>>>(a, min_cnt)
   switch (spg) {
     case 2: E0_GRP_MFMA(2); break;
     case 4: E0_GRP_MFMA(4); break;
@@ -802,7 +880,7 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
                                  const float* w, const void* x, void* y, void* workspace,
                                  int32_t flags, hipStream_t stream) {
   if (!shape || !grouped_shape_ok(shape) || !pool || !pool->base || !slot_table || !workspace ||
-      n_tokens < 0 || n_tokens > kGrpMaxTokens || (flags & ~EDGE0_GROUPED_NO_MFMA) != 0)
+      n_tokens < 0 || n_tokens > kGrpMaxTokens || (flags & ~(EDGE0_GROUPED_NO_MFMA | 0xFF00)) != 0)
     return EDGE0_EINVAL;
   if (n_tokens == 0) return EDGE0_OK;
   if (!ids || !w || !x || !y) return EDGE0_EINVAL;
@@ -851,13 +929,15 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
     k_grp_lora_in<<<(a.P * 2 * a.r + 3) / 4, 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
   }
-  // experts with >= kMfmaMinTokens tokens on MFMA, the others as GEMVs
-  const bool mfma = !(flags & EDGE0_GROUPED_NO_MFMA) && n_tokens >= kMfmaMinTokens;
-  const int gemv_max = mfma ? kMfmaMinTokens - 1 : 1 << 30;
-  int rc = launch_grp_gate_up(a, 1, gemv_max, stream);
-  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 0, stream);
-  if (rc == EDGE0_OK) rc = launch_grp_down(a, 1, gemv_max, stream);
-  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 1, stream);
+  // experts with >= min_mfma tokens on MFMA, the others as GEMVs
+  const int fm = (flags >> 8) & 0xFF;
+  const int min_mfma = fm ? fm : kMfmaMinTokens;
+  const bool mfma = !(flags & EDGE0_GROUPED_NO_MFMA) && n_tokens >= min_mfma;
+  const int gemv_max = mfma ? min_mfma - 1 : 1 << 30;
+  int rc = gemv_max >= 1 ? launch_grp_gate_up(a, 1, gemv_max, stream) : EDGE0_OK;
+  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 0, min_mfma, stream);
+  if (rc == EDGE0_OK && gemv_max >= 1) rc = launch_grp_down(a, 1, gemv_max, stream);
+  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 1, min_mfma, stream);
   if (rc != EDGE0_OK) return rc;
   const int n_out = a.T * a.d;
   k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);

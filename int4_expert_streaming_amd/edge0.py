@@ -220,6 +220,11 @@ def edge0_moe_layer(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y, w
 EDGE0_GROUPED_NO_MFMA = 1
 
 
+def grouped_mfma_min(n: int) -> int:
+    """Flag moving the grouped layer's MFMA threshold to n tokens per expert."""
+    return (n & 0xFF) << 8
+
+
 def new_grouped_workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
     """Zero-filled workspace for edge0_moe_grouped."""
     n = lib.edge0_grouped_workspace_bytes(C.byref(shape))

@@ -25,6 +25,8 @@ def torch_cuda():
 
 
 _LAYERS = {}
+# default (MFMA at >= 16 tokens per expert), GEMV only, MFMA for every expert
+FLAG_SETS = (0, 1, 1 << 8)
 
 
 def _layer(S):
@@ -64,11 +66,11 @@ def test_grouped_tiny(torch_cuda, T):
     ids, w = G.grouped_routing(S.n_experts, S.top_k, T, seed=10 + T)
     x = G.hidden(S, 20 + T, n=T)
     ys = {}
-    for flags in (0, 1):
+    for flags in FLAG_SETS:
         y, _ = _call(lay, ids, w, x, flags)
         ys[flags] = y
         worst = _check(lay, ids, w, x, y)
-        print(f"[grouped] tiny T={T} flags={flags}: worst rel-L2 {worst:.3e}")
+        print(f"[grouped] tiny T={T} flags={flags:#x}: worst rel-L2 {worst:.3e}")
     _paths_ran(ys, ids, np.bincount(ids.ravel(), minlength=S.n_experts))
 
 
@@ -80,11 +82,11 @@ def test_grouped_qwen3moe_k8(torch_cuda, T):
     x = G.hidden(S, 100 + T, n=T)
     counts = np.bincount(ids.ravel(), minlength=S.n_experts)
     ys = {}
-    for flags in (0, 1):
+    for flags in FLAG_SETS:
         y, _ = _call(lay, ids, w, x, flags)
         ys[flags] = y
         worst = _check(lay, ids, w, x, y)
-        print(f"[grouped] qwen3moe K=8 T={T} flags={flags}: {np.count_nonzero(counts)} experts, "
+        print(f"[grouped] qwen3moe K=8 T={T} flags={flags:#x}: {np.count_nonzero(counts)} experts, "
               f"max {counts.max()} tokens/expert, {int((counts >= 16).sum())} on MFMA; "
               f"worst rel-L2 {worst:.3e}")
     _paths_ran(ys, ids, counts)
