@@ -13,6 +13,36 @@ W_REL_MAX = 1e-5       # routing weights
 TIE_GAP = 1e-4         # ids are compared bit-exactly unless a gap is below this
 
 
+def check_bf16_rounding(got_bits, exact, rel=1e-5):
+    """A bf16 vector computed in fp32 against its exact fp64 value: every
+    element is the round-to-nearest-even of the exact value, except where the
+    exact value lies within `rel` (fp32 error of the computation) of the
+    midpoint between two bf16 neighbours; there either neighbour is correct.
+    Returns the number of such near-midpoint elements that rounded the other
+    way."""
+    got_bits = np.asarray(got_bits, dtype=np.uint16)
+    exact = np.asarray(exact, dtype=np.float64)
+    want = O.f64_to_bf16_bits(exact)
+    diff = np.nonzero(got_bits != want)[0]
+    if diff.size == 0:
+        return 0
+    g = O.bf16_to_f64(got_bits[diff])
+    w = O.bf16_to_f64(want[diff])
+    e = exact[diff]
+    lo, hi = np.minimum(g, w), np.maximum(g, w)
+    # the two values must be adjacent bf16 numbers bracketing the exact value
+    step = hi - lo
+    bits_lo = O.f64_to_bf16_bits(lo).astype(np.int32)
+    bits_hi = O.f64_to_bf16_bits(hi).astype(np.int32)
+    adjacent = (np.abs(bits_hi - bits_lo) == 1) | ((lo < 0) & (hi > 0))
+    assert adjacent.all(), (diff[~adjacent], g[~adjacent], w[~adjacent])
+    assert ((e >= lo) & (e <= hi)).all(), diff
+    mid = (lo + hi) / 2
+    near = np.abs(e - mid) <= rel * np.abs(e) + 1e-300
+    assert near.all(), (diff[~near], e[~near], mid[~near], step[~near])
+    return int(diff.size)
+
+
 def rel_l2(got, want) -> float:
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)

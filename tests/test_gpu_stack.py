@@ -12,7 +12,7 @@ import pytest
 
 import oracle as O
 from synth import gen as G
-from tests.layer_setup import REL_L2_MAX, check_routing, rel_l2
+from tests.layer_setup import REL_L2_MAX, check_bf16_rounding, check_routing, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -46,11 +46,10 @@ def check_layer(S, gen, L, t, snap, prev_snap, owners, consumers, report):
     """Teacher-forced comparison of layer L at step t."""
     lay = OracleLayer(gen, L)
     h_in = snap["h"][L]
-    # normalised input: the oracle's rounding of the same h (rare 1-ulp flips)
-    x_o = O.f64_to_bf16_bits(O.rmsnorm(O.bf16_to_f64(h_in)))
+    # normalised input: the rounding of the exact RMSNorm of the same h, up to
+    # near-midpoint cases the fp32 computation may round either way
+    check_bf16_rounding(snap["x"][L], O.rmsnorm(O.bf16_to_f64(h_in)))
     x_g = snap["x"][L]
-    diff = np.abs(x_o.astype(np.int32) - x_g.astype(np.int32))
-    assert diff.max() <= 1 and np.count_nonzero(diff) <= max(2, S.d_model // 200), (L, diff.max())
     # routing
     if L in consumers and t > 0:
         assert np.array_equal(snap["ids"][L], prev_snap["pred_ids"][L])

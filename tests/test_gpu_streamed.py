@@ -16,7 +16,7 @@ import pytest
 
 import oracle as O
 from synth import gen as G
-from tests.layer_setup import REL_L2_MAX, W_REL_MAX, rel_l2
+from tests.layer_setup import REL_L2_MAX, W_REL_MAX, check_bf16_rounding, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -88,9 +88,7 @@ def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of,
         assert np.array_equal(hh[0], h0)
         assert np.array_equal(snap["ids"], trace[t])
         for L in layers_of(t):
-            x_o = O.f64_to_bf16_bits(O.rmsnorm(O.bf16_to_f64(hh[L])))
-            diff = np.abs(x_o.astype(np.int32) - xx[L].astype(np.int32))
-            assert diff.max() <= 1 and np.count_nonzero(diff) <= max(2, S.d_model // 200)
+            check_bf16_rounding(xx[L], O.rmsnorm(O.bf16_to_f64(hh[L])))
             ids = trace[t, L]
             if ahead and L in con and t > 0:
                 logits = O.prerouter_logits(head[L - 1], prev_x[L - 1], trace[t - 1, L - 1],

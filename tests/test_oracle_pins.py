@@ -527,3 +527,21 @@ def test_grouped_is_per_token():
     y = O.grouped_layer(experts, ids, w, x, shape.group, lora, 2.0)
     for j in range(3):
         assert np.array_equal(y[j], O.moe_layer(experts, ids[j], w[j], x[j], shape.group, lora, 2.0))
+
+
+def test_bf16_rounding_check_accepts_only_midpoint_flips():
+    """The GPU-vs-oracle rounding criterion: a flip is accepted only at a
+    near-midpoint exact value, between adjacent bf16 numbers."""
+    from tests.layer_setup import check_bf16_rounding
+    one = O.f64_to_bf16_bits(np.array([1.0]))[0]
+    step = 2.0 ** -7
+    # exact value just below the midpoint 1 + step/2: RNE gives 1.0; 1+step accepted
+    e = np.array([1.0 + step / 2 - 1e-9])
+    assert check_bf16_rounding(np.array([one + 1], np.uint16), e) == 1
+    # far from the midpoint: the other neighbour is rejected
+    with pytest.raises(AssertionError):
+        check_bf16_rounding(np.array([one + 1], np.uint16), np.array([1.0 + step / 8]))
+    # two steps away: rejected
+    with pytest.raises(AssertionError):
+        check_bf16_rounding(np.array([one + 2], np.uint16), e)
+    assert check_bf16_rounding(np.array([one], np.uint16), np.array([1.0])) == 0
