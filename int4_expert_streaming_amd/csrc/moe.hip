@@ -63,13 +63,29 @@ __global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
   __shared__ uint16_t xs[kMaxD];
   __shared__ int32_t ids_s[16];
   __shared__ float w_s[16];
-  __shared__ float red[256];
+  __shared__ float red[4];
   const int d = a.d, K = a.K, r = a.r, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int row = blockIdx.x * 4 + wave;
   const bool router = li.flags & IN_ROUTER, lora = li.flags & IN_LORA;
   const int nrows = router ? a.E : (lora ? K * 2 * r : 0);
   const bool active = row < nrows;
+  // Load order matters (loads complete in issue order): first the
+  // prologue's h_prev and fixed-point y, then the chain that locates this
+  // wave's weight row (ids, slot table) and the row itself, which lands
+  // while the prologue computes.
+  const bool has_pro = li.flags & (IN_COMBINE | IN_NORM);
+  const bool comb = li.flags & IN_COMBINE;
+  uint32_t hb[kMaxPerThread];
+  unsigned long long av[kMaxPerThread];
+  if (has_pro) {
+#pragma unroll
+    for (int m = 0; m < kMaxPerThread; ++m) {
+      const int j = tid + 256 * m;
+      hb[m] = li.h_prev[j];
+      av[m] = comb ? a.acc_prev[j] : 0ull;
+    }
+  }
   // weight row of this wave, in flight during the prologue (when its address
   // does not depend on the top-K computed here)
   RowPref pf;
@@ -86,19 +102,8 @@ __global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
   if (pref) row_prefetch(wrow, d, pf);
   // prologue: combine, residual, RMSNorm
   const uint16_t* x = a.x;
-  if (li.flags & (IN_COMBINE | IN_NORM)) {
-    // every load of the prologue is issued before any use: h_prev and the
-    // previous layer's fixed-point y for this thread's elements j = tid + 256 m
+  if (has_pro) {
     constexpr int per = PER;
-    const bool comb = li.flags & IN_COMBINE;
-    uint32_t hb[kMaxPerThread];
-    unsigned long long av[kMaxPerThread];
-#pragma unroll
-    for (int m = 0; m < kMaxPerThread; ++m) {
-      const int j = tid + 256 * m;
-      hb[m] = li.h_prev[j];
-      av[m] = comb ? a.acc_prev[j] : 0ull;
-    }
     // this layer's accumulator starts from zero (its down units add into it)
     if (blockIdx.x == 0)
       for (int j = tid; j < d; j += 256) a.acc[j] = 0ull;
@@ -118,13 +123,10 @@ __global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
       }
       ss = fmaf(hv[m], hv[m], ss);
     }
-    red[tid] = ss;
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) red[tid] += red[tid + o];
-      __syncthreads();
-    }
-    const float inv = 1.f / sqrtf(red[0] / (float)d + li.eps);
+    const float inv = 1.f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + li.eps);
 #pragma unroll
     for (int m = 0; m < kMaxPerThread; ++m) {
       const int j = tid + 256 * m;
@@ -255,6 +257,8 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
   float X[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
+  // per-lane partials of the 4 gate (v[0..3]) and 4 up (v[4..7]) rows
+  float v[8];
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
     float G = 0.f, U = 0.f;
@@ -269,13 +273,40 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
       G += a.scale * (bf2f(Bg[ii]) * tg);
       U += a.scale * (bf2f(Bu[ii]) * tu);
     }
-    G = wave_sum(G);
-    U = wave_sum(U);
-    const float h = silu_f(G) * U;
-    if (lane == 0) {
-      h_s[4 * wave + ii] = h;
-      hrep_s[4 * wave + ii] = store_h(a, k, row0 + ii, h);
-    }
+    v[ii] = G;
+    v[4 + ii] = U;
+  }
+  // the 8 wave sums at once: halving exchanges across lane bits 5, 4, 3 (each
+  // lane keeps half of its values and adds its partner's copy of that half),
+  // then a sum over lane bits 0-2; lane bits (5, 4, 3) then index the value
+  // (gate or up, row)
+  const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1;
+  float w4[4], w2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b5 ? v[4 + i] : v[i], send = b5 ? v[i] : v[4 + i];
+    w4[i] = keep + __shfl_xor(send, 32, kWave);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b4 ? w4[2 + i] : w4[i], send = b4 ? w4[i] : w4[2 + i];
+    w2[i] = keep + __shfl_xor(send, 16, kWave);
+  }
+  float w1;
+  {
+    const float keep = b3 ? w2[1] : w2[0], send = b3 ? w2[0] : w2[1];
+    w1 = keep + dpp_f<0x128>(0.f, send);  // row_ror:8 = lane ^ 8 within a row
+  }
+  w1 += dpp_f<0xB1>(0.f, w1);   // quad_perm [1,0,3,2]
+  w1 += dpp_f<0x4E>(0.f, w1);   // quad_perm [2,3,0,1]
+  w1 += dpp_f<0x141>(0.f, w1);  // row_half_mirror
+  // lanes 8*ii hold G of row ii, lanes 32 + 8*ii its U
+  const float Uo = __shfl_xor(w1, 32, kWave);
+  if (b5 == 0 && (lane & 7) == 0) {
+    const int ii = lane >> 3;
+    const float h = silu_f(w1) * Uo;
+    h_s[4 * wave + ii] = h;
+    hrep_s[4 * wave + ii] = store_h(a, k, row0 + ii, h);
   }
 }
 
