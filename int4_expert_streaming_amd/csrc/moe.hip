@@ -205,13 +205,18 @@ __device__ __forceinline__ float store_h(const MoeArgs& a, int k, int i, float h
 // Wide rows: d/32 = 64*NJ chunks per row; lane l owns chunks l + 64 j of both
 // the gate and the up row; 4 row pairs per wave.  Every global load of the
 // wave (weights, scales, biases, LoRA B rows and t) is issued before any math.
+// Wide rows (d >= 2048): 8 waves of 2 row pairs per 16-row workgroup (two
+// waves per SIMD hide each other's latency); narrow rows: 4 waves.
+constexpr int kWideRowsPerWave = 2;
+constexpr int gate_up_threads(int cpr) { return cpr >= 64 ? 64 * 16 / kWideRowsPerWave : 256; }
+
 template <int NJ>
 __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b, int k, int i0,
                                              float* h_s, float* hrep_s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int d = a.d, g = a.g, ng = d / g, r = a.r;
-  constexpr int R = 4;
-  const int row0 = i0 + 4 * wave;
+  constexpr int R = kWideRowsPerWave;
+  const int row0 = i0 + R * wave;
   XRaw xr[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) load_x_raw(a.x, lane + 64 * j, xr[j]);
@@ -257,8 +262,8 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
   float X[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
-  // per-lane partials of the 4 gate (v[0..3]) and 4 up (v[4..7]) rows
-  float v[8];
+  // per-lane partials of the R gate (v[0..R-1]) and R up (v[R..2R-1]) rows
+  float v[2 * R];
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
     float G = 0.f, U = 0.f;
@@ -274,39 +279,55 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
       U += a.scale * (bf2f(Bu[ii]) * tu);
     }
     v[ii] = G;
-    v[4 + ii] = U;
+    v[R + ii] = U;
   }
-  // the 8 wave sums at once: halving exchanges across lane bits 5, 4, 3 (each
-  // lane keeps half of its values and adds its partner's copy of that half),
-  // then a sum over lane bits 0-2; lane bits (5, 4, 3) then index the value
-  // (gate or up, row)
-  const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1;
-  float w4[4], w2[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float keep = b5 ? v[4 + i] : v[i], send = b5 ? v[i] : v[4 + i];
-    w4[i] = keep + __shfl_xor(send, 32, kWave);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float keep = b4 ? w4[2 + i] : w4[i], send = b4 ? w4[i] : w4[2 + i];
-    w2[i] = keep + __shfl_xor(send, 16, kWave);
-  }
+  // the 2R wave sums at once: halving exchanges across the top lane bits
+  // (each lane keeps half of its values and adds its partner's copy of that
+  // half), then a sum over the remaining low lane bits; the top bits then
+  // index the value (gate or up, row): lane 64/(2R) * ii holds G of row ii,
+  // lane 32 + 64/(2R) * ii its U
+  const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
   float w1;
-  {
+  if constexpr (R == 1) {
+    const float keep = b5 ? v[1] : v[0], send = b5 ? v[0] : v[1];
+    w1 = row16_sum(keep + __shfl_xor(send, 32, kWave));
+    w1 += __shfl_xor(w1, 16, kWave);
+  } else if constexpr (R == 2) {
+    float w2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b5 ? v[2 + i] : v[i], send = b5 ? v[i] : v[2 + i];
+      w2[i] = keep + __shfl_xor(send, 32, kWave);
+    }
+    const float keep = b4 ? w2[1] : w2[0], send = b4 ? w2[0] : w2[1];
+    w1 = row16_sum(keep + __shfl_xor(send, 16, kWave));
+  } else {
+    static_assert(R == 4, "1, 2 or 4 rows per wave");
+    const int b3 = (lane >> 3) & 1;
+    float w4[4], w2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b5 ? v[4 + i] : v[i], send = b5 ? v[i] : v[4 + i];
+      w4[i] = keep + __shfl_xor(send, 32, kWave);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b4 ? w4[2 + i] : w4[i], send = b4 ? w4[i] : w4[2 + i];
+      w2[i] = keep + __shfl_xor(send, 16, kWave);
+    }
     const float keep = b3 ? w2[1] : w2[0], send = b3 ? w2[0] : w2[1];
     w1 = keep + dpp_f<0x128>(0.f, send);  // row_ror:8 = lane ^ 8 within a row
+    w1 += dpp_f<0xB1>(0.f, w1);   // quad_perm [1,0,3,2]
+    w1 += dpp_f<0x4E>(0.f, w1);   // quad_perm [2,3,0,1]
+    w1 += dpp_f<0x141>(0.f, w1);  // row_half_mirror
   }
-  w1 += dpp_f<0xB1>(0.f, w1);   // quad_perm [1,0,3,2]
-  w1 += dpp_f<0x4E>(0.f, w1);   // quad_perm [2,3,0,1]
-  w1 += dpp_f<0x141>(0.f, w1);  // row_half_mirror
-  // lanes 8*ii hold G of row ii, lanes 32 + 8*ii its U
   const float Uo = __shfl_xor(w1, 32, kWave);
-  if (b5 == 0 && (lane & 7) == 0) {
-    const int ii = lane >> 3;
+  constexpr int kSpan = 64 / (2 * R);
+  if (b5 == 0 && (lane % kSpan) == 0) {
+    const int ii = lane / kSpan;
     const float h = silu_f(w1) * Uo;
-    h_s[4 * wave + ii] = h;
-    hrep_s[4 * wave + ii] = store_h(a, k, row0 + ii, h);
+    h_s[R * wave + ii] = h;
+    hrep_s[R * wave + ii] = store_h(a, k, row0 + ii, h);
   }
 }
 
@@ -381,7 +402,7 @@ __device__ __forceinline__ void gate_up_narrow(const MoeArgs& a, const uint8_t* 
 // One workgroup = 16 consecutive rows of one expert's gate and up.  Also
 // writes the 16-row sum of h and the 16-row partial of A_down h.
 template <int CPR>
-__global__ __launch_bounds__(256) void k_gate_up(MoeArgs a) {
+__global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
   __shared__ float h_s[16];
   __shared__ float hrep_s[16];
   const int nblk = a.I / 16;
@@ -707,19 +728,20 @@ int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming
   if (timing && timing->which == 1 && cpr == 64) {
     // measured launch: the dispatch itself records the events at the
     // kernel's start and end
-    hipExtLaunchKernelGGL(k_gate_up<64>, dim3(grid2), dim3(256), 0, stream, timing->start,
+    hipExtLaunchKernelGGL(k_gate_up<64>, dim3(grid2), dim3(gate_up_threads(64)), 0, stream,
+                          timing->start,
                           timing->stop, 0, a);
     E0_CHECK_LAUNCH();
   } else {
   E0_MARK(1, true);
   switch (cpr) {
-    case 8: k_gate_up<8><<<grid2, 256, 0, stream>>>(a); break;
-    case 16: k_gate_up<16><<<grid2, 256, 0, stream>>>(a); break;
-    case 32: k_gate_up<32><<<grid2, 256, 0, stream>>>(a); break;
-    case 64: k_gate_up<64><<<grid2, 256, 0, stream>>>(a); break;
-    case 128: k_gate_up<128><<<grid2, 256, 0, stream>>>(a); break;
-    case 192: k_gate_up<192><<<grid2, 256, 0, stream>>>(a); break;
-    case 256: k_gate_up<256><<<grid2, 256, 0, stream>>>(a); break;
+    case 8: k_gate_up<8><<<grid2, gate_up_threads(8), 0, stream>>>(a); break;
+    case 16: k_gate_up<16><<<grid2, gate_up_threads(16), 0, stream>>>(a); break;
+    case 32: k_gate_up<32><<<grid2, gate_up_threads(32), 0, stream>>>(a); break;
+    case 64: k_gate_up<64><<<grid2, gate_up_threads(64), 0, stream>>>(a); break;
+    case 128: k_gate_up<128><<<grid2, gate_up_threads(128), 0, stream>>>(a); break;
+    case 192: k_gate_up<192><<<grid2, gate_up_threads(192), 0, stream>>>(a); break;
+    case 256: k_gate_up<256><<<grid2, gate_up_threads(256), 0, stream>>>(a); break;
     default: return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();
