@@ -688,7 +688,7 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   // down units: 64-row blocks x input slices, about 256 of them, and a
   // unit's expert-chunks fit the LDS stage
   const int RB = a->d / 64, NC = a->I / 32;
-  int S = (256 + RB - 1) / RB;
+  int S = (768 + RB - 1) / RB;
   S = S < 1 ? 1 : (S > NC ? NC : S);
   while ((a->K * ((NC + S - 1) / S)) > kMaxSliceChunks && S < NC) ++S;
   a->S = S;
