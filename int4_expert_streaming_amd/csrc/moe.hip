@@ -202,90 +202,72 @@ __device__ __forceinline__ float store_h(const MoeArgs& a, int k, int i, float h
   return bf2f(hi) + bf2f(lo);
 }
 
-// Wide rows: d/32 = 64*NJ chunks per row; lane l owns chunks l + 64 j of both
-// the gate and the up row; 4 row pairs per wave.  Every global load of the
-// wave (weights, scales, biases, LoRA B rows and t) is issued before any math.
 // Wide rows (d >= 2048): 8 waves of 2 row pairs per 16-row workgroup (two
 // waves per SIMD hide each other's latency); narrow rows: 4 waves.
 constexpr int kWideRowsPerWave = 2;
 constexpr int gate_up_threads(int cpr) { return cpr >= 64 ? 64 * 16 / kWideRowsPerWave : 256; }
 
-template <int NJ>
-__device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b, int k, int i0,
-                                             float* h_s, float* hrep_s) {
+// Wide rows: d/32 = 64*NJ chunks per row; lane l owns chunks l + 64 j of both
+// the gate and the up row of the wave's R row pairs.  gu_load issues every
+// weight load of the wave (int4 words, scales, biases, LoRA B rows);
+// gu_finish takes x (global or LDS) and the lane's LoRA t, and computes.
+template <int NJ, int RR = kWideRowsPerWave>
+struct GuW {
+  static constexpr int R = RR;
+  uint4 qg[R][NJ], qu[R][NJ];
+  uint32_t sg[R][NJ], bg[R][NJ], su[R][NJ], bu[R][NJ];
+  uint32_t Bg[R], Bu[R];
+};
+
+template <int NJ, int RR = kWideRowsPerWave>
+__device__ __forceinline__ void gu_load(const MoeArgs& a, const uint8_t* b, int i0,
+                                        GuW<NJ, RR>& w) {
+  constexpr int R = RR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int d = a.d, g = a.g, ng = d / g, r = a.r;
-  constexpr int R = kWideRowsPerWave;
   const int row0 = i0 + R * wave;
-  XRaw xr[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) load_x_raw(a.x, lane + 64 * j, xr[j]);
   const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q);
   const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s);
   const uint16_t* gb = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b);
   const uint16_t* us = reinterpret_cast<const uint16_t*>(b + a.lay.up_s);
   const uint16_t* ub = reinterpret_cast<const uint16_t*>(b + a.lay.up_b);
-  uint4 qg[R][NJ], qu[R][NJ];
-  uint32_t sg[R][NJ], bg[R][NJ], su[R][NJ], bu[R][NJ];
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
     const int row = row0 + ii;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = lane + 64 * j;
-      qg[ii][j] = reinterpret_cast<const uint4*>(gq + (size_t)row * (d / 8))[col];
-      qu[ii][j] = reinterpret_cast<const uint4*>(uq + (size_t)row * (d / 8))[col];
+      w.qg[ii][j] = reinterpret_cast<const uint4*>(gq + (size_t)row * (d / 8))[col];
+      w.qu[ii][j] = reinterpret_cast<const uint4*>(uq + (size_t)row * (d / 8))[col];
       const int grp = (32 * col) / g;
-      sg[ii][j] = gs[row * ng + grp];
-      bg[ii][j] = gb[row * ng + grp];
-      su[ii][j] = us[row * ng + grp];
-      bu[ii][j] = ub[row * ng + grp];
+      w.sg[ii][j] = gs[row * ng + grp];
+      w.bg[ii][j] = gb[row * ng + grp];
+      w.su[ii][j] = us[row * ng + grp];
+      w.bu[ii][j] = ub[row * ng + grp];
     }
   }
-  // LoRA: lane rr < r holds B[row][rr] for the 4 rows and t[rr] (r <= 64)
-  uint32_t Bg[R], Bu[R];
-  float tg = 0.f, tu = 0.f;
-  const bool has_l = r > 0 && lane < r;
-  if (has_l) {
-    const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
-    const uint16_t* Bup = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
-#pragma unroll
-    for (int ii = 0; ii < R; ++ii) {
-      Bg[ii] = Bgp[(size_t)(row0 + ii) * r + lane];
-      Bu[ii] = Bup[(size_t)(row0 + ii) * r + lane];
-    }
-    tg = a.t_in[(size_t)(k * 2 + 0) * r + lane];
-    tu = a.t_in[(size_t)(k * 2 + 1) * r + lane];
-  }
-  uint32_t xp[NJ][16];
-  float X[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
-  // per-lane partials of the R gate (v[0..R-1]) and R up (v[R..2R-1]) rows
-  float v[2 * R];
+  // LoRA: lane rr < r holds B[row][rr] of the R rows (r <= 64).  Loaded
+  // without a branch (lanes >= r, or r = 0, read an in-bundle word that is
+  // never used), so no control flow separates these loads from their uses.
+  const int rc = r > 0 ? r : 1;
+  const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.b_gate : 0));
+  const uint16_t* Bup = reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.b_up : 0));
+  const int rl = lane % rc;
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
-    float G = 0.f, U = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const float s1 = bf2f(sg[ii][j]), b1 = bf2f(bg[ii][j]);
-      const float s2 = bf2f(su[ii][j]), b2 = bf2f(bu[ii][j]);
-      G += s1 * chunk_dot128(qg[ii][j], xp[j]) + (b1 - 128.f * s1) * X[j];
-      U += s2 * chunk_dot128(qu[ii][j], xp[j]) + (b2 - 128.f * s2) * X[j];
-    }
-    if (has_l) {
-      G += a.scale * (bf2f(Bg[ii]) * tg);
-      U += a.scale * (bf2f(Bu[ii]) * tu);
-    }
-    v[ii] = G;
-    v[R + ii] = U;
+    w.Bg[ii] = Bgp[(size_t)(row0 + ii) * rc + rl];
+    w.Bu[ii] = Bup[(size_t)(row0 + ii) * rc + rl];
   }
-  // the 2R wave sums at once: halving exchanges across the top lane bits
-  // (each lane keeps half of its values and adds its partner's copy of that
-  // half), then a sum over the remaining low lane bits; the top bits then
-  // index the value (gate or up, row): lane 64/(2R) * ii holds G of row ii,
-  // lane 32 + 64/(2R) * ii its U
+}
+
+// Sums of 2R per-lane values over the wave at once: halving exchanges across
+// the top lane bits (each lane keeps half of its values and adds its
+// partner's copy of that half), then a sum over the remaining low lane bits.
+// Value v is then in lane (64 / 2R) * v.
+template <int R>
+__device__ __forceinline__ float wave_sums_2r(const float (&v)[2 * R]) {
+  const int lane = threadIdx.x & 63;
   const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
   float w1;
   if constexpr (R == 1) {
@@ -302,7 +284,7 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
     const float keep = b4 ? w2[1] : w2[0], send = b4 ? w2[0] : w2[1];
     w1 = row16_sum(keep + __shfl_xor(send, 16, kWave));
   } else {
-    static_assert(R == 4, "1, 2 or 4 rows per wave");
+    static_assert(R == 4, "1, 2 or 4");
     const int b3 = (lane >> 3) & 1;
     float w4[4], w2[2];
 #pragma unroll
@@ -321,14 +303,67 @@ __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b,
     w1 += dpp_f<0x4E>(0.f, w1);   // quad_perm [2,3,0,1]
     w1 += dpp_f<0x141>(0.f, w1);  // row_half_mirror
   }
+  return w1;
+}
+
+template <int NJ, int RR = kWideRowsPerWave>
+__device__ __forceinline__ void gu_finish(const MoeArgs& a, const GuW<NJ, RR>& w, int k, int i0,
+                                          const uint16_t* xsrc, float tg, float tu, float* h_s,
+                                          float* hrep_s) {
+  constexpr int R = RR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = i0 + R * wave;
+  const bool has_l = a.r > 0 && lane < a.r;
+  XRaw xr[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) load_x_raw(xsrc, lane + 64 * j, xr[j]);
+  uint32_t xp[NJ][16];
+  float X[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
+  // per-lane partials of the R gate (v[0..R-1]) and R up (v[R..2R-1]) rows
+  float v[2 * R];
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii) {
+    float G = 0.f, U = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float s1 = bf2f(w.sg[ii][j]), b1 = bf2f(w.bg[ii][j]);
+      const float s2 = bf2f(w.su[ii][j]), b2 = bf2f(w.bu[ii][j]);
+      G += s1 * chunk_dot128(w.qg[ii][j], xp[j]) + (b1 - 128.f * s1) * X[j];
+      U += s2 * chunk_dot128(w.qu[ii][j], xp[j]) + (b2 - 128.f * s2) * X[j];
+    }
+    if (has_l) {
+      G += a.scale * (bf2f(w.Bg[ii]) * tg);
+      U += a.scale * (bf2f(w.Bu[ii]) * tu);
+    }
+    v[ii] = G;
+    v[R + ii] = U;
+  }
+  // lane (64/2R) * ii holds G of row ii, lane 32 + (64/2R) * ii its U
+  const float w1 = wave_sums_2r<R>(v);
   const float Uo = __shfl_xor(w1, 32, kWave);
   constexpr int kSpan = 64 / (2 * R);
-  if (b5 == 0 && (lane % kSpan) == 0) {
+  if (lane < 32 && (lane % kSpan) == 0) {
     const int ii = lane / kSpan;
     const float h = silu_f(w1) * Uo;
     h_s[R * wave + ii] = h;
     hrep_s[R * wave + ii] = store_h(a, k, row0 + ii, h);
   }
+}
+
+template <int NJ>
+__device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b, int k, int i0,
+                                             float* h_s, float* hrep_s) {
+  GuW<NJ> w;
+  gu_load<NJ>(a, b, i0, w);
+  const int lane = threadIdx.x & 63, r = a.r;
+  float tg = 0.f, tu = 0.f;
+  if (r > 0 && lane < r) {
+    tg = a.t_in[(size_t)(k * 2 + 0) * r + lane];
+    tu = a.t_in[(size_t)(k * 2 + 1) * r + lane];
+  }
+  gu_finish<NJ>(a, w, k, i0, a.x, tg, tu, h_s, hrep_s);
 }
 
 // Narrow rows: d/32 = CPR in {8, 16, 32} chunks per row; a step covers
@@ -446,6 +481,185 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) s += bf_lo(w[m]) * h_s[2 * m] + bf_hi(w[m]) * h_s[2 * m + 1];
     a.tdpart[((size_t)k * nblk + blk) * r + threadIdx.x] = s;
+  }
+}
+
+// ------------------------------------------------------------- k_layer_fused
+// A prediction-routed layer's input and gate/up in one launch (wide rows,
+// lora_rank <= 16): every workgroup (16 rows of one routed expert) loads its
+// int4 rows and its expert's 2r LoRA A rows first, then redundantly forms the
+// layer input from L2-resident data (previous layer's fixed-point y, h,
+// RMSNorm) into LDS, computes t = A x for its expert (rows spread over the
+// waves), and runs the gate/up rows on x and t from LDS.  Workgroup 0 stores
+// h, y_prev, x and clears this layer's accumulator; the first workgroup of
+// each expert publishes its slot for the down kernel.  Replaces k_layer_in +
+// k_gate_up (one fewer dependent launch per layer).
+constexpr int kFusedMaxRank = 16;  // 2r A rows over 8 waves: <= 4 rows per wave
+constexpr int kFusedRowsPerWave = 2;  // 8 waves: 16 rows of gate and up per workgroup
+
+template <int NJ>
+__global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
+  constexpr int PER = 4 * NJ;  // hidden elements per thread (d = 2048 NJ, 512 threads)
+  constexpr int AR = 2 * kFusedMaxRank / 8;
+  constexpr int RW = kFusedRowsPerWave, ROWS = 8 * RW;  // rows per workgroup
+  __shared__ uint16_t xs[2048 * NJ];
+  __shared__ float t_s[2][kFusedMaxRank];
+  __shared__ float red[8];
+  __shared__ float h_s[ROWS];
+  __shared__ float hrep_s[ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = a.d, r = a.r;
+  const int nwg = a.I / ROWS;
+  const int k = blockIdx.x / nwg;
+  const int i0 = (blockIdx.x % nwg) * ROWS;
+  const int nblk = a.I / 16;
+  const int blk = i0 / 16;  // first 16-row block of the workgroup
+  // 1. the prologue's loads: h_prev and the previous layer's fixed-point y,
+  // written by other workgroups (other XCDs) just before; few wide requests.
+  // Thread tid owns elements j = 4 (tid + 512 c) + e, c < NJ, e < 4.
+  uint32_t hb[PER];
+  unsigned long long av[PER];
+#pragma unroll
+  for (int c = 0; c < NJ; ++c) {
+    const int j0 = 4 * (tid + 512 * c);
+    const uint2 hq = *reinterpret_cast<const uint2*>(li.h_prev + j0);
+    const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
+    const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
+    hb[4 * c + 0] = hq.x & 0xFFFFu;
+    hb[4 * c + 1] = hq.x >> 16;
+    hb[4 * c + 2] = hq.y & 0xFFFFu;
+    hb[4 * c + 3] = hq.y >> 16;
+    av[4 * c + 0] = a0.x;
+    av[4 * c + 1] = a0.y;
+    av[4 * c + 2] = a1.x;
+    av[4 * c + 3] = a1.y;
+  }
+  // 2. this expert's bundle, then every weight load of the wave (HBM).  No
+  // branch separates these loads from the prologue's first use of hb/av, so
+  // the wait before it covers only the loads issued before them; an invalid
+  // slot reads slot 0 and its results are discarded.
+  const int slot = resolve_slot(a, a.ids[k]);
+  const bool ok = slot >= 0;
+  const uint8_t* b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
+  GuW<NJ, RW> gw;
+  gu_load<NJ, RW>(a, b, i0, gw);
+  uint4 ar[AR][4 * NJ];  // LoRA A rows (wave + 8 m, clamped): this lane's 32 NJ elements
+  const int nr2 = r > 0 ? 2 * r : 1;
+#pragma unroll
+  for (int m = 0; m < AR; ++m) {
+    const int tr = min(wave + 8 * m, nr2 - 1);
+    const int rr = r > 0 ? tr % r : 0;
+    const uint16_t* arow = reinterpret_cast<const uint16_t*>(
+                               b + ((r > 0 && tr >= r) ? a.lay.a_up : a.lay.a_gate)) +
+                           (size_t)rr * d;
+#pragma unroll
+    for (int q = 0; q < 4 * NJ; ++q)
+      ar[m][q] = reinterpret_cast<const uint4*>(arow + 32 * NJ * lane)[q];
+  }
+  // 3. combine, residual, RMSNorm -> x in LDS
+  float hv[PER];
+  float ss = 0.f;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const uint32_t yb = f2bf(from_fix(av[m]));
+    hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
+    ss = fmaf(hv[m], hv[m], ss);
+    av[m] = yb;  // keep y_prev's bits for the stores below
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
+  const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
+  uint32_t xw[2 * NJ];
+#pragma unroll
+  for (int c = 0; c < NJ; ++c) {
+    xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
+    xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
+    *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = make_uint2(xw[2 * c], xw[2 * c + 1]);
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) {
+      const int j0 = 4 * (tid + 512 * c);
+      *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
+      *reinterpret_cast<uint2*>(li.y_prev_out + j0) =
+          make_uint2((uint32_t)av[4 * c] | ((uint32_t)av[4 * c + 1] << 16),
+                     (uint32_t)av[4 * c + 2] | ((uint32_t)av[4 * c + 3] << 16));
+      *reinterpret_cast<uint2*>(li.h_out + j0) =
+          make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
+                     f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
+    }
+    for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
+  }
+  if (blk == 0 && tid == 0) {
+    a.slots[k] = ok ? slot : -1;
+    if (!ok) set_error(a.err, EDGE0_ERANGE);
+  }
+  // A_down columns of the workgroup's rows: thread (sub, rr) = 16-row block
+  // sub, rank row rr
+  constexpr int NSUB = ROWS / 16;
+  const int sub = tid / 64, rrd = tid % 64;
+  uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
+  if (sub < NSUB && rrd < r) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)rrd * a.I + i0 + 16 * sub);
+    ad0 = src[0];
+    ad1 = src[1];
+  }
+  if (!ok) {
+    for (int t = tid; t < ROWS; t += 512) store_h(a, k, i0 + t, 0.f);
+    if (sub < NSUB && rrd < r) a.tdpart[((size_t)k * nblk + blk + sub) * r + rrd] = 0.f;
+    if (tid < NSUB) a.hs[(size_t)k * nblk + blk + tid] = 0.f;
+    return;
+  }
+  // 4. t = A x: wave rows tr = wave + 8 m; lane's 32 NJ elements of x
+  if (r > 0) {
+    const uint4* xv = reinterpret_cast<const uint4*>(xs + 32 * NJ * lane);
+    float tv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4 * NJ; ++q) {
+      const uint4 xq = xv[q];
+#pragma unroll
+      for (int m = 0; m < AR; ++m) {
+        tv[m] = dot2bf(ar[m][q].x, xq.x, tv[m]);
+        tv[m] = dot2bf(ar[m][q].y, xq.y, tv[m]);
+        tv[m] = dot2bf(ar[m][q].z, xq.z, tv[m]);
+        tv[m] = dot2bf(ar[m][q].w, xq.w, tv[m]);
+      }
+    }
+    // rows m = 0..3 of the wave end up in lanes 0, 16, 32, 48
+    const float tr4 = wave_sums_2r<2>(tv);
+    if ((lane & 15) == 0) {
+      const int m = lane >> 4;
+      const int tr = wave + 8 * m;
+      if (m < AR && tr < 2 * r) t_s[tr / r][tr % r] = tr4;
+    }
+  }
+  __syncthreads();
+  float tg = 0.f, tu = 0.f;
+  if (r > 0 && lane < r) {
+    tg = t_s[0][lane];
+    tu = t_s[1][lane];
+  }
+  // 5. gate/up rows on x and t from LDS, then the 16-row epilogue
+  gu_finish<NJ, RW>(a, gw, k, i0, xs, tg, tu, h_s, hrep_s);
+  __syncthreads();
+  if (tid < NSUB) {
+    float sm = 0.f;
+    for (int t = 0; t < 16; ++t) sm += hrep_s[16 * tid + t];
+    a.hs[(size_t)k * nblk + blk + tid] = sm;
+  }
+  if (sub < NSUB && rrd < r) {
+    const uint32_t wd[8] = {ad0.x, ad0.y, ad0.z, ad0.w, ad1.x, ad1.y, ad1.z, ad1.w};
+    const float* hsb = h_s + 16 * sub;
+    float sm = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) sm += bf_lo(wd[m]) * hsb[2 * m] + bf_hi(wd[m]) * hsb[2 * m + 1];
+    a.tdpart[((size_t)k * nblk + blk + sub) * r + rrd] = sm;
   }
 }
 
@@ -747,6 +961,10 @@ int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming
   E0_CHECK_LAUNCH();
   E0_MARK(1, false);
   }
+  return launch_down(a, stream, timing);
+}
+
+int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
   E0_MARK(2, true);
   {
     const int NC = a.I / 32, cps = (NC + a.S - 1) / a.S;
@@ -764,6 +982,32 @@ int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming
   }
   E0_CHECK_LAUNCH();
   E0_MARK(2, false);
+  return EDGE0_OK;
+}
+
+bool layer_fused_ok(const MoeArgs& a) {
+  return (a.d == 2048 || a.d == 4096) && a.r <= kFusedMaxRank &&
+         a.I % (8 * kFusedRowsPerWave) == 0;
+}
+
+int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
+                       const LaunchTiming* timing) {
+  if (!layer_fused_ok(a)) return EDGE0_EINVAL;
+  const int grid = a.K * (a.I / (8 * kFusedRowsPerWave));
+  if (timing && timing->which == 1) {
+    // measured launch: events recorded by the dispatch at its start and end
+    if (a.d == 2048)
+      hipExtLaunchKernelGGL(k_layer_fused<1>, dim3(grid), dim3(512), 0, stream, timing->start,
+                            timing->stop, 0, a, li);
+    else
+      hipExtLaunchKernelGGL(k_layer_fused<2>, dim3(grid), dim3(512), 0, stream, timing->start,
+                            timing->stop, 0, a, li);
+  } else if (a.d == 2048) {
+    k_layer_fused<1><<<grid, 512, 0, stream>>>(a, li);
+  } else {
+    k_layer_fused<2><<<grid, 512, 0, stream>>>(a, li);
+  }
+  E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
 

@@ -72,6 +72,14 @@ struct LaunchTiming {
 int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
                     const LaunchTiming* timing = nullptr);
 int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+// the down GEMV alone (after k_layer_fused)
+int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+// Layer input + gate/up in one launch for a layer whose routing (a.ids) is
+// known before it starts; li carries the prologue (combine, residual, RMSNorm)
+// arguments.  Wide rows (d_model 2048 or 4096), lora_rank <= 16.
+bool layer_fused_ok(const MoeArgs& a);
+int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
+                       const LaunchTiming* timing = nullptr);
 int launch_combine(const MoeArgs& a, hipStream_t stream);
 
 // A batch of prerouter heads (one per owner layer): head i reads x at

@@ -108,6 +108,20 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     li.y_prev_out = L > 0 ? st->y + (size_t)(L - 1) * d : nullptr;
     li.x_out = xL;
     li.eps = st->spec.rms_eps;
+    LaunchTiming lt{st->timed_kernel, nullptr, nullptr};
+    if (st->timed_kernel > 0) {
+      lt.start = st->ev_start[L];
+      lt.stop = st->ev_stop[L];
+    }
+    if (by_pred && layer_fused_ok(a) && L > 0) {
+      // routing known before the layer: input and gate/up in one launch
+      li.flags |= IN_LORA;
+      if ((rc = launch_layer_fused(a, li, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
+              EDGE0_OK ||
+          (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+        return rc;
+      continue;
+    }
     if (by_pred) {
       li.flags |= IN_LORA;
       if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
@@ -122,11 +136,6 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       l2.ids_out = ids;
       l2.w_out = w;
       if ((rc = launch_layer_in(a, l2, stream)) != EDGE0_OK) return rc;
-    }
-    LaunchTiming lt{st->timed_kernel, nullptr, nullptr};
-    if (st->timed_kernel > 0) {
-      lt.start = st->ev_start[L];
-      lt.stop = st->ev_stop[L];
     }
     if ((rc = launch_expert_gemvs(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
       return rc;
