@@ -111,6 +111,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0x143, 0xc>(0.f, v);  // row_bcast:31 into rows 2 and 3
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// Eight wave sums at once: halving exchanges across lane bits 5, 4, 3 (each
+// lane keeps half of its values and adds its partner's copy of that half),
+// then a sum over lane bits 0-2.  The sum of v[m] ends up in lanes 8m..8m+7.
+__device__ __forceinline__ float wave_sums8(const float (&v)[8]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1;
+  float w4[4], w2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b5 ? v[4 + i] : v[i], send = b5 ? v[i] : v[4 + i];
+    w4[i] = keep + __shfl_xor(send, 32, kWave);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b4 ? w4[2 + i] : w4[i], send = b4 ? w4[i] : w4[2 + i];
+    w2[i] = keep + __shfl_xor(send, 16, kWave);
+  }
+  const float keep = b3 ? w2[1] : w2[0], send = b3 ? w2[0] : w2[1];
+  float w1 = keep + dpp_f<0x128>(0.f, send);  // row_ror:8 = lane ^ 8 within a row
+  w1 += dpp_f<0xB1>(0.f, w1);                 // quad_perm [1,0,3,2]
+  w1 += dpp_f<0x4E>(0.f, w1);                 // quad_perm [2,3,0,1]
+  w1 += dpp_f<0x141>(0.f, w1);                // row_half_mirror
+  return w1;
+}
+
 // sums over aligned segments of SEG lanes (8, 16 or 32); every lane of a
 // segment gets the segment's sum
 template <int SEG>

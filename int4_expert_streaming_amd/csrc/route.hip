@@ -101,28 +101,61 @@ __global__ __launch_bounds__(256) void k_heads_fc1(HeadBatch hb) {
   }
 }
 
-// logits[i][e] = w2[e] . a_i + b2[e] + res[i][e]; then top-K of head i in its
-// last workgroup
-__global__ __launch_bounds__(256) void k_heads_fc2(HeadBatch hb) {
-  const int wave = threadIdx.x >> 6;
+// logits[i][e] = w2[e] . a_i + b2[e] + res[i][e], then head i's top-K: one
+// workgroup per head (16 waves; each wave 8 rows at a time, one 16-byte
+// chunk of each fp16 row per lane, the 8 row sums reduced together); the
+// logits meet in LDS and wave 0 commits the top-K.
+__global__ __launch_bounds__(1024) void k_heads_fc2(HeadBatch hb) {
+  __shared__ float lg_s[1024];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = hb.H, E = hb.E, K = hb.K;
-  const int per = (E + 3) / 4;
-  const int i = blockIdx.x / per;
-  const int row = (blockIdx.x % per) * 4 + wave;
-  float* logits = hb.logits + (size_t)i * E;
-  if (row < E) {
-    float s = row_dot<true, true>(hb.w2[i] + (size_t)row * H, hb.a + (size_t)i * H, H);
-    if (hb.b2[i] != nullptr) s += h2f(hb.b2[i][row]);
-    if (hb.has_res) s += hb.res[(size_t)i * E + row];
-    if ((threadIdx.x & 63) == 0) st_dev(logits + row, s);
+  const float* av = hb.a + (size_t)i * H;
+  const uint16_t* w2 = hb.w2[i];
+  const int nch = H / 8;  // 16-byte chunks per row
+  for (int rb = 8 * wave; rb < E; rb += 128) {
+    float v[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+      const float4 a0 = reinterpret_cast<const float4*>(av + 8 * c)[0];
+      const float4 a1 = reinterpret_cast<const float4*>(av + 8 * c)[1];
+      uint4 q[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        q[m] = rb + m < E ? reinterpret_cast<const uint4*>(w2 + (size_t)(rb + m) * H)[c]
+                          : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        float s = v[m];
+        s = fmaf(h2f(q[m].x & 0xFFFFu), a0.x, s);
+        s = fmaf(h2f(q[m].x >> 16), a0.y, s);
+        s = fmaf(h2f(q[m].y & 0xFFFFu), a0.z, s);
+        s = fmaf(h2f(q[m].y >> 16), a0.w, s);
+        s = fmaf(h2f(q[m].z & 0xFFFFu), a1.x, s);
+        s = fmaf(h2f(q[m].z >> 16), a1.y, s);
+        s = fmaf(h2f(q[m].w & 0xFFFFu), a1.z, s);
+        s = fmaf(h2f(q[m].w >> 16), a1.w, s);
+        v[m] = s;
+      }
+    }
+    // row rb + m ends up in lane 8 m
+    const float sum = wave_sums8(v);
+    if ((lane & 7) == 0) {
+      const int e = rb + (lane >> 3);
+      if (e < E) {
+        float s = sum;
+        if (hb.b2[i] != nullptr) s += h2f(hb.b2[i][e]);
+        if (hb.has_res) s += hb.res[(size_t)i * E + e];
+        lg_s[e] = s;
+        hb.logits[(size_t)i * E + e] = s;
+      }
+    }
   }
-  if (last_arrival(hb.counters + i, (uint32_t)per)) {
-    if (wave == 0)
-      wave_topk<true>(logits, E, K, hb.ids_out + (size_t)i * hb.out_stride,
-                      hb.w_out + (size_t)i * hb.out_stride);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(hb.counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  __syncthreads();
+  if (wave == 0)
+    wave_topk<false>(lg_s, E, K, hb.ids_out + (size_t)i * hb.out_stride,
+                     hb.w_out + (size_t)i * hb.out_stride);
 }
 
 int launch_heads(const HeadBatch& hb, hipStream_t stream) {
@@ -130,7 +163,7 @@ int launch_heads(const HeadBatch& hb, hipStream_t stream) {
   const int per1 = (hb.H + (hb.has_res ? hb.E : 0) + 3) / 4;
   k_heads_fc1<<<hb.n * per1, 256, 0, stream>>>(hb);
   E0_CHECK_LAUNCH();
-  k_heads_fc2<<<hb.n * ((hb.E + 3) / 4), 256, 0, stream>>>(hb);
+  k_heads_fc2<<<hb.n, 1024, 0, stream>>>(hb);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
