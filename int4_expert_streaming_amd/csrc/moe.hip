@@ -497,7 +497,10 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 constexpr int kFusedMaxRank = 16;  // 2r A rows over 8 waves: <= 4 rows per wave
 constexpr int kFusedRowsPerWave = 2;  // 8 waves: 16 rows of gate and up per workgroup
 
-template <int NJ>
+// TOPK: a router layer after its router launch (which formed x and the
+// logits): every wave commits the top-K of li.logits itself (no hand-off),
+// workgroup 0 stores ids/w, and x is read instead of formed.
+template <int NJ, bool TOPK>
 __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   constexpr int PER = 4 * NJ;  // hidden elements per thread (d = 2048 NJ, 512 threads)
   constexpr int AR = 2 * kFusedMaxRank / 8;
@@ -507,6 +510,8 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   __shared__ float red[8];
   __shared__ float h_s[ROWS];
   __shared__ float hrep_s[ROWS];
+  __shared__ int32_t ids_w[TOPK ? 8 : 1][16];
+  __shared__ float w_w[TOPK ? 8 : 1][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = a.d, r = a.r;
   const int nwg = a.I / ROWS;
@@ -519,26 +524,40 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   // Thread tid owns elements j = 4 (tid + 512 c) + e, c < NJ, e < 4.
   uint32_t hb[PER];
   unsigned long long av[PER];
+  uint2 xq[NJ];
+  if constexpr (TOPK) {
 #pragma unroll
-  for (int c = 0; c < NJ; ++c) {
-    const int j0 = 4 * (tid + 512 * c);
-    const uint2 hq = *reinterpret_cast<const uint2*>(li.h_prev + j0);
-    const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
-    const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
-    hb[4 * c + 0] = hq.x & 0xFFFFu;
-    hb[4 * c + 1] = hq.x >> 16;
-    hb[4 * c + 2] = hq.y & 0xFFFFu;
-    hb[4 * c + 3] = hq.y >> 16;
-    av[4 * c + 0] = a0.x;
-    av[4 * c + 1] = a0.y;
-    av[4 * c + 2] = a1.x;
-    av[4 * c + 3] = a1.y;
+    for (int c = 0; c < NJ; ++c) xq[c] = *reinterpret_cast<const uint2*>(a.x + 4 * (tid + 512 * c));
+  } else {
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) {
+      const int j0 = 4 * (tid + 512 * c);
+      const uint2 hq = *reinterpret_cast<const uint2*>(li.h_prev + j0);
+      const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
+      const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
+      hb[4 * c + 0] = hq.x & 0xFFFFu;
+      hb[4 * c + 1] = hq.x >> 16;
+      hb[4 * c + 2] = hq.y & 0xFFFFu;
+      hb[4 * c + 3] = hq.y >> 16;
+      av[4 * c + 0] = a0.x;
+      av[4 * c + 1] = a0.y;
+      av[4 * c + 2] = a1.x;
+      av[4 * c + 3] = a1.y;
+    }
   }
   // 2. this expert's bundle, then every weight load of the wave (HBM).  No
   // branch separates these loads from the prologue's first use of hb/av, so
   // the wait before it covers only the loads issued before them; an invalid
   // slot reads slot 0 and its results are discarded.
-  const int slot = resolve_slot(a, a.ids[k]);
+  int expert;
+  if constexpr (TOPK) {
+    wave_topk<false>(li.logits, a.E, a.K, ids_w[wave], w_w[wave]);
+    __builtin_amdgcn_wave_barrier();  // the wave reads back what its lanes stored
+    expert = ids_w[wave][k];
+  } else {
+    expert = a.ids[k];
+  }
+  const int slot = resolve_slot(a, expert);
   const bool ok = slot >= 0;
   const uint8_t* b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
   GuW<NJ, RW> gw;
@@ -556,7 +575,16 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
     for (int q = 0; q < 4 * NJ; ++q)
       ar[m][q] = reinterpret_cast<const uint4*>(arow + 32 * NJ * lane)[q];
   }
-  // 3. combine, residual, RMSNorm -> x in LDS
+  // 3. combine, residual, RMSNorm -> x in LDS (TOPK: x as given)
+  if constexpr (TOPK) {
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = xq[c];
+    __syncthreads();
+    if (blockIdx.x == 0 && tid < a.K) {
+      li.ids_out[tid] = ids_w[0][tid];
+      li.w_out[tid] = w_w[0][tid];
+    }
+  } else {
   float hv[PER];
   float ss = 0.f;
 #pragma unroll
@@ -595,6 +623,7 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
     }
     for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
   }
+  }  // prologue
   if (blk == 0 && tid == 0) {
     a.slots[k] = ok ? slot : -1;
     if (!ok) set_error(a.err, EDGE0_ERANGE);
@@ -994,18 +1023,15 @@ int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
                        const LaunchTiming* timing) {
   if (!layer_fused_ok(a)) return EDGE0_EINVAL;
   const int grid = a.K * (a.I / (8 * kFusedRowsPerWave));
+  const bool topk = li.flags & IN_TOPK;
+  auto kern = a.d == 2048 ? (topk ? k_layer_fused<1, true> : k_layer_fused<1, false>)
+                          : (topk ? k_layer_fused<2, true> : k_layer_fused<2, false>);
   if (timing && timing->which == 1) {
     // measured launch: events recorded by the dispatch at its start and end
-    if (a.d == 2048)
-      hipExtLaunchKernelGGL(k_layer_fused<1>, dim3(grid), dim3(512), 0, stream, timing->start,
-                            timing->stop, 0, a, li);
-    else
-      hipExtLaunchKernelGGL(k_layer_fused<2>, dim3(grid), dim3(512), 0, stream, timing->start,
-                            timing->stop, 0, a, li);
-  } else if (a.d == 2048) {
-    k_layer_fused<1><<<grid, 512, 0, stream>>>(a, li);
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, stream, timing->start, timing->stop, 0,
+                          a, li);
   } else {
-    k_layer_fused<2><<<grid, 512, 0, stream>>>(a, li);
+    kern<<<grid, 512, 0, stream>>>(a, li);
   }
   E0_CHECK_LAUNCH();
   return EDGE0_OK;

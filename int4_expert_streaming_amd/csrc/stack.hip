@@ -135,6 +135,14 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       l2.logits = st->logits;
       l2.ids_out = ids;
       l2.w_out = w;
+      if (layer_fused_ok(a)) {
+        // top-K, LoRA-in and gate/up in one launch
+        if ((rc = launch_layer_fused(a, l2, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
+                EDGE0_OK ||
+            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+          return rc;
+        continue;
+      }
       if ((rc = launch_layer_in(a, l2, stream)) != EDGE0_OK) return rc;
     }
     if ((rc = launch_expert_gemvs(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
