@@ -515,8 +515,14 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = a.d, r = a.r;
   const int nwg = a.I / ROWS;
-  const int k = blockIdx.x / nwg;
-  const int i0 = (blockIdx.x % nwg) * ROWS;
+  // XCD-aware order: consecutive workgroups go to different XCDs
+  // (round-robin over 8), so logical block L = (id % 8) * (grid / 8) + id / 8
+  // gives each XCD a contiguous range of an expert's blocks and the expert's
+  // shared LoRA A rows are fetched by few XCD L2s
+  const int gsz = gridDim.x;
+  const int lb = (gsz % 8 == 0) ? (blockIdx.x % 8) * (gsz / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int k = lb / nwg;
+  const int i0 = (lb % nwg) * ROWS;
   const int nblk = a.I / 16;
   const int blk = i0 / 16;  // first 16-row block of the workgroup
   // 1. the prologue's loads: h_prev and the previous layer's fixed-point y,
@@ -580,7 +586,7 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
 #pragma unroll
     for (int c = 0; c < NJ; ++c) *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = xq[c];
     __syncthreads();
-    if (blockIdx.x == 0 && tid < a.K) {
+    if (lb == 0 && tid < a.K) {
       li.ids_out[tid] = ids_w[0][tid];
       li.w_out[tid] = w_w[0][tid];
     }
@@ -609,7 +615,7 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
     *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = make_uint2(xw[2 * c], xw[2 * c + 1]);
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (lb == 0) {
 #pragma unroll
     for (int c = 0; c < NJ; ++c) {
       const int j0 = 4 * (tid + 512 * c);
