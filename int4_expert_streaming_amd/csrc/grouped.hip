@@ -497,6 +497,7 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[SPG]
 }
 
 constexpr int kMfmaMinTokens = 16;
+constexpr int kFusedRank = 16;  // LoRA rank bound of the pipelined MFMA kernels
 constexpr int kGW = 8;  // groups per wave per pass (their weights held in registers)
 
 // One workgroup = 32 rows of one active expert's gate and up, all its tokens
@@ -769,6 +770,311 @@ __global__ __launch_bounds__(256) void k_grp_down_mfma(GrpArgs a, int min_cnt) {
   }
 }
 
+// ------------------------------------------------- MFMA, pipelined (v2)
+// GEMM-shaped variants for I % 128 == 0, d % 128 == 0 and lora_rank <= 16:
+// a workgroup covers 128 weight rows (4 waves x 32, each wave the full
+// reduction) for up to 32 tokens of one expert; the activation tile is
+// staged in LDS in chunks of kKC inputs (double-buffered, shared by the 4
+// waves, with each group's activation sum), and each wave's weight words of
+// the next chunk are in flight while the current chunk computes.  Operand
+// order and the per-group fold are those of the kernels above.
+constexpr int kKC = 128;  // inputs per staged chunk
+
+// Stage the activations of chunk c (tokens m < mt of the tile): thread t ->
+// token t / 8, 16 inputs (16 p .. 16 p + 15), p = t % 8; each group's sum
+// from the threads of its parts (neighbouring lanes of the same token).
+template <int SPG>
+__device__ __forceinline__ void grp_stage_x(const GrpArgs& a, int q0, int t0, int mt, int c,
+                                            uint16_t (*xs)[kKC], float (*gs)[8]) {
+  constexpr int G = 16 * SPG;     // group size
+  constexpr int PPG = G / 16;     // parts per group (2, 4, 8)
+  const int t = threadIdx.x, m = t >> 3, p = t & 7;
+  uint4 v[2];
+  float sum = 0.f;
+  if (m < mt) {
+    const uint16_t* src = a.x + (size_t)a.pair_tok[q0 + t0 + m] * a.d + c * kKC + 16 * p;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      v[u] = reinterpret_cast<const uint4*>(src)[u];
+      sum += raw_sum8(v[u]);
+    }
+  } else {
+    v[0] = v[1] = make_uint4(0, 0, 0, 0);
+  }
+  reinterpret_cast<uint4*>(&xs[m][16 * p])[0] = v[0];
+  reinterpret_cast<uint4*>(&xs[m][16 * p])[1] = v[1];
+  sum += __shfl_xor(sum, 1, kWave);
+  if constexpr (PPG >= 4) sum += __shfl_xor(sum, 2, kWave);
+  if constexpr (PPG >= 8) sum += __shfl_xor(sum, 4, kWave);
+  if (p % PPG == 0) gs[m][p / PPG] = sum;
+}
+
+template <int SPG>
+__global__ __launch_bounds__(256, 2) void k_grp_gate_up_mfma2(GrpArgs a, int min_cnt) {
+  constexpr int G = 16 * SPG, CG = kKC / G;  // group size, groups per chunk
+  __shared__ uint16_t xs[2][32][kKC];
+  __shared__ float gsx[2][32][8];
+  __shared__ float tl_s[32][2][kFusedRank];
+  __shared__ float bl_s[2][128][kFusedRank];
+  const int nb = a.I / 128;
+  const int act = blockIdx.x / nb;
+  const int rb = blockIdx.x % nb;
+  if (act >= a.info[0]) return;
+  const int n = a.act_cnt[act];
+  if (n < min_cnt) return;
+  const uint8_t* b = grp_bundle(a, act);
+  if (b == nullptr) return;
+  const int q0 = a.act_off[act];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nn = lane & 31, jh = lane >> 5;
+  const int d = a.d, ng = d / G, r = a.r, I = a.I;
+  const int row = rb * 128 + 32 * wave + nn;
+  const int nch = d / kKC;
+  const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
+  const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
+  const uint16_t* gsp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s) + (size_t)row * ng;
+  const uint16_t* gbp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b) + (size_t)row * ng;
+  const uint16_t* usp = reinterpret_cast<const uint16_t*>(b + a.lay.up_s) + (size_t)row * ng;
+  const uint16_t* ubp = reinterpret_cast<const uint16_t*>(b + a.lay.up_b) + (size_t)row * ng;
+  if (r > 0) {
+    const uint16_t* Bg = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
+    const uint16_t* Bu = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
+    for (int t = tid; t < 128 * r; t += 256) {
+      const int rw = t / r, rr = t % r;
+      bl_s[0][rw][rr] = bf2f(Bg[(size_t)(rb * 128 + rw) * r + rr]);
+      bl_s[1][rw][rr] = bf2f(Bu[(size_t)(rb * 128 + rw) * r + rr]);
+    }
+  }
+  uint32_t wg[2][CG][SPG], wu[2][CG][SPG], sc[2][CG][4];
+  auto load_w = [&](int c, int bi) {
+#pragma unroll
+    for (int i = 0; i < CG; ++i) {
+      const int Gi = c * CG + i;
+      load_words<SPG>(gq + (size_t)Gi * (G / 8) + jh * SPG, wg[bi][i]);
+      load_words<SPG>(uq + (size_t)Gi * (G / 8) + jh * SPG, wu[bi][i]);
+      sc[bi][i][0] = gsp[Gi];
+      sc[bi][i][1] = gbp[Gi];
+      sc[bi][i][2] = usp[Gi];
+      sc[bi][i][3] = ubp[Gi];
+    }
+  };
+  for (int t0 = 0; t0 < n; t0 += 32) {
+    const int mt = n - t0 < 32 ? n - t0 : 32;
+    __syncthreads();  // previous tile's LDS consumed
+    for (int t = tid; t < mt * 2 * r; t += 256) {
+      const int m = t / (2 * r), rem = t % (2 * r);
+      tl_s[m][rem / r][rem % r] = a.t_in[(size_t)(q0 + t0 + m) * 2 * r + rem];
+    }
+    f32x16_t accG, accU;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accG[v] = accU[v] = 0.f;
+    load_w(0, 0);
+    grp_stage_x<SPG>(a, q0, t0, mt, 0, xs[0], gsx[0]);
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      __syncthreads();  // chunk c staged; the other buffer free
+      if (c + 1 < nch) {
+        if (buf) load_w(c + 1, 0); else load_w(c + 1, 1);
+        grp_stage_x<SPG>(a, q0, t0, mt, c + 1, xs[buf ^ 1], gsx[buf ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < CG; ++i) {
+        f32x16_t cg, cu;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cg[v] = cu[v] = 0.f;
+        uint32_t w_g[SPG], w_u[SPG], s_[4];
+#pragma unroll
+        for (int st = 0; st < SPG; ++st) {
+          w_g[st] = buf ? wg[1][i][st] : wg[0][i][st];
+          w_u[st] = buf ? wu[1][i][st] : wu[0][i][st];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_[q] = buf ? sc[1][i][q] : sc[0][i][q];
+#pragma unroll
+        for (int st = 0; st < SPG; ++st) {
+          const uint4 xr = *reinterpret_cast<const uint4*>(&xs[buf][nn][i * G + jh * (G / 2) + 8 * st]);
+          const bf16x8_t xo = x_operand(xr);
+          cg = mfma32(xo, q4_operand(w_g[st]), cg);
+          cu = mfma32(xo, q4_operand(w_u[st]), cu);
+        }
+        const float sg = bf2f(s_[0]), cbg = bf2f(s_[1]) - 128.f * sg;
+        const float su = bf2f(s_[2]), cbu = bf2f(s_[3]) - 128.f * su;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+          const float sxm = gsx[buf][m][i];
+          accG[v] += sg * cg[v] + cbg * sxm;
+          accU[v] += su * cu[v] + cbu * sxm;
+        }
+      }
+    }
+    // epilogue: LoRA B t, SwiGLU, h pairs and the 16-row sums of this wave
+    const int rl = 32 * wave + nn;  // row within the workgroup
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+      float Gv = accG[v], Uv = accU[v];
+      if (r > 0) {
+        float dg = 0.f, du = 0.f;
+        for (int rr = 0; rr < r; ++rr) {
+          dg += bl_s[0][rl][rr] * tl_s[m][0][rr];
+          du += bl_s[1][rl][rr] * tl_s[m][1][rr];
+        }
+        Gv += a.scale * dg;
+        Uv += a.scale * du;
+      }
+      const float h = grp_silu(Gv) * Uv;
+      const float hr = m < mt ? grp_store_h(a, q0 + t0 + m, row, h) : 0.f;
+      const float s16 = row16_sum(hr);  // rows of the same 16-row block
+      if ((nn & 15) == 0 && m < mt) a.hs[(size_t)(q0 + t0 + m) * (I / 16) + (row >> 4)] = s16;
+    }
+  }
+}
+
+template <int SPG>
+__global__ __launch_bounds__(256, 2) void k_grp_down_mfma2(GrpArgs a, int min_cnt) {
+  constexpr int G = 16 * SPG, CG = kKC / G;
+  __shared__ uint16_t hs_hi[2][32][kKC];
+  __shared__ uint16_t hs_lo[2][32][kKC];
+  __shared__ uint16_t ad_s[2][kFusedRank][kKC];   // A_down rows of the chunk
+  __shared__ float gsh[2][32][kKC / 16];          // 16-row sums of h per chunk
+  __shared__ float td_s[32][kFusedRank + 1];      // t_down [token][rank]
+  __shared__ float bd_s[128][kFusedRank];
+  const int nb = a.d / 128;
+  const int act = blockIdx.x / nb;
+  const int ob = blockIdx.x % nb;
+  if (act >= a.info[0]) return;
+  const int n = a.act_cnt[act];
+  if (n < min_cnt) return;
+  const uint8_t* b = grp_bundle(a, act);
+  if (b == nullptr) return;
+  const int q0 = a.act_off[act];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nn = lane & 31, jh = lane >> 5;
+  const int d = a.d, I = a.I, r = a.r, NC = I / 32;
+  const int o = ob * 128 + 32 * wave + nn;
+  const int trb = o / 64, within = o % 64;
+  const int nch = I / kKC;
+  const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q);
+  const uint16_t* dsp = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
+  const uint16_t* dbp = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
+  const uint16_t* adp = reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.a_down : 0));
+  if (r > 0) {
+    const uint16_t* Bd = reinterpret_cast<const uint16_t*>(b + a.lay.b_down);
+    for (int t = tid; t < 128 * r; t += 256)
+      bd_s[t / r][t % r] = bf2f(Bd[(size_t)(ob * 128 + t / r) * r + t % r]);
+  }
+  uint32_t wd[2][CG][SPG], sc[2][CG][2];
+  auto load_w = [&](int c, int bi) {
+#pragma unroll
+    for (int i = 0; i < CG; ++i) {
+      const int Gi = c * CG + i;
+      const int i0 = Gi * G + jh * (G / 2);
+#pragma unroll
+      for (int st = 0; st < SPG; ++st) {
+        const int ii = i0 + 8 * st;
+        wd[bi][i][st] = dq[(((size_t)trb * NC + ii / 32) * 64 + within) * 4 + (ii % 32) / 8];
+      }
+      sc[bi][i][0] = dsp[(size_t)Gi * d + o];
+      sc[bi][i][1] = dbp[(size_t)Gi * d + o];
+    }
+  };
+  auto stage_h = [&](int t0, int mt, int c, int buf) {
+    // thread t -> token t / 8, 16 inputs of the chunk; h pairs as stored
+    const int t = tid, m = t >> 3, p = t & 7;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint4 hv = make_uint4(0, 0, 0, 0), lv = hv;
+      if (m < mt) {
+        const size_t off = (size_t)(q0 + t0 + m) * I + c * kKC + 16 * p + 8 * u;
+        hv = *reinterpret_cast<const uint4*>(a.hp_hi + off);
+        lv = *reinterpret_cast<const uint4*>(a.hp_lo + off);
+      }
+      reinterpret_cast<uint4*>(&hs_hi[buf][m][16 * p])[u] = hv;
+      reinterpret_cast<uint4*>(&hs_lo[buf][m][16 * p])[u] = lv;
+    }
+    gsh[buf][m][p] = m < mt ? a.hs[(size_t)(q0 + t0 + m) * (I / 16) + c * (kKC / 16) + p] : 0.f;
+    // A_down rows of the chunk (ranks >= r are zero)
+    for (int e = t; e < kFusedRank * (kKC / 8); e += 256) {
+      const int rr = e / (kKC / 8), k8 = e % (kKC / 8);
+      uint4 av = make_uint4(0, 0, 0, 0);
+      if (rr < r) av = *reinterpret_cast<const uint4*>(adp + (size_t)rr * I + c * kKC + 8 * k8);
+      reinterpret_cast<uint4*>(&ad_s[buf][rr][0])[k8] = av;
+    }
+  };
+  for (int t0 = 0; t0 < n; t0 += 32) {
+    const int mt = n - t0 < 32 ? n - t0 : 32;
+    __syncthreads();
+    f32x16_t acc, tdv;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = tdv[v] = 0.f;
+    load_w(0, 0);
+    stage_h(t0, mt, 0, 0);
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      __syncthreads();
+      if (c + 1 < nch) {
+        if (buf) load_w(c + 1, 0); else load_w(c + 1, 1);
+        stage_h(t0, mt, c + 1, buf ^ 1);
+      }
+#pragma unroll
+      for (int i = 0; i < CG; ++i) {
+        f32x16_t cc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cc[v] = 0.f;
+#pragma unroll
+        for (int st = 0; st < SPG; ++st) {
+          const int col = i * G + jh * (G / 2) + 8 * st;
+          const bf16x8_t hh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&hs_hi[buf][nn][col]));
+          const bf16x8_t hl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&hs_lo[buf][nn][col]));
+          const bf16x8_t wo = q4_operand(buf ? wd[1][i][st] : wd[0][i][st]);
+          cc = mfma32(hh, wo, cc);
+          cc = mfma32(hl, wo, cc);
+          if (wave == 0 && r > 0) {
+            // t_down += h A_down^T (lane nn = rank; A_down in the pair order of h)
+            const uint4 araw = nn < kFusedRank ? *reinterpret_cast<const uint4*>(&ad_s[buf][nn][col])
+                                               : make_uint4(0, 0, 0, 0);
+            const bf16x8_t ao = x_operand(araw);
+            tdv = mfma32(hh, ao, tdv);
+            tdv = mfma32(hl, ao, tdv);
+          }
+        }
+        const uint32_t s0 = buf ? sc[1][i][0] : sc[0][i][0];
+        const uint32_t s1 = buf ? sc[1][i][1] : sc[0][i][1];
+        const float sd = bf2f(s0), cbd = bf2f(s1) - 128.f * sd;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+          float sh = 0.f;
+#pragma unroll
+          for (int k = 0; k < G / 16; ++k) sh += gsh[buf][m][i * (G / 16) + k];
+          acc[v] += sd * cc[v] + cbd * sh;
+        }
+      }
+    }
+    if (wave == 0 && nn < kFusedRank) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) td_s[8 * (v >> 2) + 4 * jh + (v & 3)][nn] = tdv[v];
+    }
+    __syncthreads();
+    const int rl = 32 * wave + nn;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
+      if (m < mt) {
+        float tot = acc[v];
+        if (r > 0) {
+          float dl = 0.f;
+          for (int rr = 0; rr < r; ++rr) dl += bd_s[rl][rr] * td_s[m][rr];
+          tot += a.scale * dl;
+        }
+        const int qq = q0 + t0 + m;
+        atomicAdd(a.acc + (size_t)a.pair_tok[qq] * d + o, to_fix(a.pair_w[qq] * tot));
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ output
 __global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -848,10 +1154,29 @@ static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
   return EDGE0_OK;
 }
 
+static bool grp_mfma2_ok(const GrpArgs& a) {
+  return a.I % 128 == 0 && a.d % 128 == 0 && a.r <= kFusedRank && a.g <= kKC;
+}
+
 // which = 0 gate/up, 1 down
 static int launch_grp_mfma(const GrpArgs& a, int which, int min_cnt, hipStream_t st) {
-  const int grid = a.Amax * ((which ? a.d : a.I) / 32);
   const int spg = a.g / 16;
+  if (grp_mfma2_ok(a)) {
+    const int grid2 = a.Amax * ((which ? a.d : a.I) / 128);
+#define E0_GRP_MFMA2(S)                                                     \
+  if (which) k_grp_down_mfma2<S><<<grid2, 256, 0, st>>>(a, min_cnt);        \
+  else k_grp_gate_up_mfma2<S><<<grid2, 256, 0, st>>>(a, min_cnt)
+    switch (spg) {
+      case 2: E0_GRP_MFMA2(2); break;
+      case 4: E0_GRP_MFMA2(4); break;
+      case 8: E0_GRP_MFMA2(8); break;
+      default: return EDGE0_EINVAL;
+    }
+#undef E0_GRP_MFMA2
+    E0_CHECK_LAUNCH();
+    return EDGE0_OK;
+  }
+  const int grid = a.Amax * ((which ? a.d : a.I) / 32);
 #define E0_GRP_MFMA(S)                                            \
   if (which) k_grp_down_mfma<S><<<grid, 256, 0, st>>>(a, min_cnt); \
   else k_grp_gate_up_mfma<S><<<grid, 256, 0, st>>>(a, min_cnt)

@@ -496,6 +496,7 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 // k_gate_up (one fewer dependent launch per layer).
 constexpr int kFusedMaxRank = 16;  // 2r A rows over 8 waves: <= 4 rows per wave
 constexpr int kFusedRowsPerWave = 2;  // 8 waves: 16 rows of gate and up per workgroup
+constexpr int kFusedMaxExperts = 256;  // slot-table row held in 4 registers per lane
 
 // TOPK: a router layer after its router launch (which formed x and the
 // logits): every wave commits the top-K of li.logits itself (no hand-off),
@@ -525,6 +526,12 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   const int i0 = (lb % nwg) * ROWS;
   const int nblk = a.I / 16;
   const int blk = i0 / 16;  // first 16-row block of the workgroup
+  // 0. the layer's slot-table row (E <= 256), lane l holding entries
+  // l + 64 j: issued first, so resolving the routed expert's slot below is
+  // a register read rather than one more dependent memory round trip
+  int32_t tbl[kFusedMaxExperts / 64];
+#pragma unroll
+  for (int j = 0; j < kFusedMaxExperts / 64; ++j) tbl[j] = a.table[min(lane + 64 * j, a.E - 1)];
   // 1. the prologue's loads: h_prev and the previous layer's fixed-point y,
   // written by other workgroups (other XCDs) just before; few wide requests.
   // Thread tid owns elements j = 4 (tid + 512 c) + e, c < NJ, e < 4.
@@ -563,12 +570,21 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   } else {
     expert = a.ids[k];
   }
-  const int slot = resolve_slot(a, expert);
+  int slot;
+  {
+    const int ec = min(max(expert, 0), a.E - 1);  // wave-uniform
+    int v = tbl[0];
+#pragma unroll
+    for (int j = 1; j < kFusedMaxExperts / 64; ++j) v = (ec >> 6) == j ? tbl[j] : v;
+    slot = __builtin_amdgcn_readlane(v, ec & 63);
+    if (expert < 0 || expert >= a.E || slot < 0 || slot >= a.n_slots) slot = -1;
+  }
   const bool ok = slot >= 0;
   const uint8_t* b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
   GuW<NJ, RW> gw;
   gu_load<NJ, RW>(a, b, i0, gw);
-  uint4 ar[AR][4 * NJ];  // LoRA A rows (wave + 8 m, clamped): this lane's 32 NJ elements
+  uint4 ar[AR][4 * NJ];  // LoRA A rows (wave + 8 m, clamped): 16-byte pieces lane + 64 q,
+                        // so each load instruction reads 1 KiB of a row contiguously
   const int nr2 = r > 0 ? 2 * r : 1;
 #pragma unroll
   for (int m = 0; m < AR; ++m) {
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
                            (size_t)rr * d;
 #pragma unroll
     for (int q = 0; q < 4 * NJ; ++q)
-      ar[m][q] = reinterpret_cast<const uint4*>(arow + 32 * NJ * lane)[q];
+      ar[m][q] = reinterpret_cast<const uint4*>(arow)[lane + 64 * q];
   }
   // 3. combine, residual, RMSNorm -> x in LDS (TOPK: x as given)
   if constexpr (TOPK) {
@@ -651,13 +667,13 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
     if (tid < NSUB) a.hs[(size_t)k * nblk + blk + tid] = 0.f;
     return;
   }
-  // 4. t = A x: wave rows tr = wave + 8 m; lane's 32 NJ elements of x
+  // 4. t = A x: wave rows tr = wave + 8 m; x pieces in the A rows' order
   if (r > 0) {
-    const uint4* xv = reinterpret_cast<const uint4*>(xs + 32 * NJ * lane);
+    const uint4* xv = reinterpret_cast<const uint4*>(xs) + lane;
     float tv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 4 * NJ; ++q) {
-      const uint4 xq = xv[q];
+      const uint4 xq = xv[64 * q];
 #pragma unroll
       for (int m = 0; m < AR; ++m) {
         tv[m] = dot2bf(ar[m][q].x, xq.x, tv[m]);
@@ -1022,7 +1038,7 @@ int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing
 
 bool layer_fused_ok(const MoeArgs& a) {
   return (a.d == 2048 || a.d == 4096) && a.r <= kFusedMaxRank &&
-         a.I % (8 * kFusedRowsPerWave) == 0;
+         a.I % (8 * kFusedRowsPerWave) == 0 && a.E <= kFusedMaxExperts;
 }
 
 int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
