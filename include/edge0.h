@@ -295,12 +295,44 @@ typedef struct {
 int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffers* out);
 void edge0_stack_destroy(edge0_stack* st);
 
+/* How edge0_stack_step runs the layers (the results are the same, within
+ * the tolerance of fp32 summation order; heads and the gathered routing run
+ * as ordinary launches after the layers in both modes):
+ *   EDGE0_STACK_GRAPHS (default): the step's per-layer launches, replayed as
+ *     HIP graphs (two or three dependent launches per layer).
+ *   EDGE0_STACK_PERSISTENT: one cooperative launch of K * d_inter / 16
+ *     workgroups runs every layer.  The workgroups hand the layer input, h
+ *     and the fixed-point y to each other through device-coherent memory,
+ *     separated by grid-wide arrival counters, and each issues the loads of
+ *     its next phase (consumer layers' experts are known from the previous
+ *     step's predictions) before it waits ([Edge0] §3.2 "Prediction-as-
+ *     routing": the routing is committed one token ahead).  Requires
+ *     d_model 2048, n_experts <= 256, lora_rank 0, 8 or 16, top_k <= 16,
+ *     d_inter % 32 == 0, d_model/64 dividing K * d_inter / 16 (and at least
+ *     n_experts and 2 * top_k * lora_rank of them, and a multiple of 8),
+ *     n_layers <= 48, and a device that can keep that
+ *     many workgroups resident; otherwise EDGE0_EINVAL and the mode is
+ *     unchanged.  Every wait is bounded (edge0_stack_set_spin_limit): a
+ *     workgroup that waits longer records EDGE0_EHIP in the workspace error
+ *     word and the launch ends early with incomplete results; the handle
+ *     must then be destroyed.
+ * EDGE0_EINVAL for another mode value. */
+enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1 };
+int edge0_stack_set_mode(edge0_stack* st, int32_t mode);
+/* Polls per wait of the persistent mode before a workgroup gives up (0: the
+ * default, about a second).  A failure-path aid; EDGE0_EINVAL for polls < 0. */
+int edge0_stack_set_spin_limit(edge0_stack* st, int64_t polls);
+/* Workspace error word of the handle (see edge0_workspace_error): the
+ * recorded codes, cleared. */
+int edge0_stack_error(edge0_stack* st);
+
 /* Measurement aid: while kernel != 0, edge0_stack_step enqueues the step's
  * launches directly instead of replaying its graph, with a HIP event pair
  * around one launch class in every layer (kernel: 1 the gate/up GEMV, 2 the
  * down GEMV + combine, 3 the LoRA-in GEMV; 0 turns it off).  After a step,
  * edge0_stack_kernel_ms writes that launch's duration in ms for each layer
- * (up to cap values) and the count to *n. */
+ * (up to cap values) and the count to *n.  In the persistent mode the one
+ * layer launch of the step is bracketed and *n is 1. */
 int edge0_stack_set_timing(edge0_stack* st, int32_t kernel);
 int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n);
 

@@ -12,6 +12,15 @@ namespace e0 {
 
 constexpr int kWave = 64;
 
+// threadIdx.x through an empty asm: index arithmetic derived from it is
+// recomputed where it is used instead of being hoisted out of a long loop
+// and kept live (or spilled) across it
+__device__ __forceinline__ int tid_here() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ------------------------------------------------------------------ dtypes
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -115,6 +115,52 @@ edge0_slot_pool stager_pool(const edge0_stager* sg);
 const int32_t* stager_table(const edge0_stager* sg);
 int stager_layers(const edge0_stager* sg);
 
+
+// The resident decode step as one persistent cooperative launch (flow.hip):
+// G = K * d_inter / 16 workgroups stay resident for all layers and hand data
+// to each other through device-coherent memory and arrival counters.
+constexpr int kFlowMaxPhases = 192;  // up to 4 phases per layer
+constexpr int kFlowCounters = 8;     // arrival counters per phase, 256 bytes apart
+constexpr int64_t kFlowDefaultSpin = 1 << 21;  // polls per wait (about a second)
+struct FlowArgs {
+  int d, E, I, K, g, r, n_layers;
+  float scale, eps;
+  edge0_bundle_layout lay;
+  const uint8_t* pool;
+  int64_t slot_bytes;
+  int32_t n_slots;
+  const int32_t* tables;             // [L][E]
+  const uint16_t* const* routers;    // device array [L] of bf16 [E][d]
+  const int32_t* pred_ids;           // [L][K] routing of consumer layers (step > 0)
+  const float* pred_w;
+  int32_t* exec_ids;                 // [L][K] routing the router layers commit
+  float* exec_w;
+  int consumer_first, consumer_last, step;
+  uint16_t *x, *y, *h;               // [L][d], [L][d], [L+1][d]; h[0] holds h0
+  unsigned long long* acc;           // [2][d] fixed-point y
+  uint32_t* hp_hi;                   // [K][I/2] pair words of bf16(h)
+  uint32_t* hp_lo;                   // [K][I/2] pair words of bf16(h - bf16(h))
+  float* hs;                         // [K][I/16]
+  unsigned long long* tdown;         // [K][r] A_down h, fixed point
+  float* t_in;                       // [K][2r] LoRA A x of the routed experts
+  float* logits;                     // [E]
+  uint32_t* cnt;                     // [kFlowMaxPhases][8][64] arrival counters
+  uint32_t* err;
+  uint32_t* abort_word;
+  int64_t spin;
+  int S;                             // down slices: G = (d / 64) * S
+  int cps;                           // input chunks per down slice
+  uint32_t target[kFlowMaxPhases];   // counter value that completes phase p
+};
+// shapes the persistent step covers: d_model 2048, n_experts <= 256,
+// lora_rank 0, 8 or 16, top_k <= 16, d_inter % 32 == 0, G a multiple of d/64,
+// at most 16 down tiles per unit, 4 * n_layers <= kFlowMaxPhases
+bool flow_shape_ok(const edge0_moe_shape& sh, int n_layers);
+int flow_grid(const edge0_moe_shape& sh);
+// EDGE0_OK when G workgroups of the step kernel can be resident at once
+int flow_coresident(int G);
+int launch_flow_step(const FlowArgs& a, int G, hipStream_t stream);
+
 int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
                   const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
                   int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream);

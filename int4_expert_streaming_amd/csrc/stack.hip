@@ -69,6 +69,13 @@ struct edge0_stack {
   std::vector<hipEvent_t> ev_start, ev_stop;  // one pair per layer
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
   hipEvent_t ev_heads;       // staged steps: the heads of the step have run
+  // persistent mode (EDGE0_STACK_PERSISTENT)
+  int mode;
+  uint32_t* flow_cnt;                // [kFlowMaxPhases][kFlowCounters][64] arrival counters
+  uint32_t* flow_abort;              // raised by a workgroup whose wait timed out
+  const uint16_t** flow_routers;     // device copy of the router pointers
+  std::vector<uint32_t> flow_uses;   // completed uses of each counter
+  int64_t flow_spin;                 // polls per wait before giving up
 };
 
 static bool is_consumer(const edge0_stack_spec& s, int L) {
@@ -77,6 +84,8 @@ static bool is_consumer(const edge0_stack_spec& s, int L) {
 static bool is_owner(const edge0_stack_spec& s, int L) {
   return L >= s.owner_first && L <= s.owner_last;
 }
+
+static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream);
 
 // enqueue all launches of decode step `step` (h[0] already holds h0).  The
 // heads are off the step's critical path (their predictions are used at the
@@ -151,8 +160,17 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
   // the last layer's combine and residual
   a.h_res = st->h + (size_t)(Lc - 1) * d;
   a.h_out = st->h + (size_t)Lc * d;
-  int rc = launch_combine(a, stream);
+  const int rc = launch_combine(a, stream);
   if (rc != EDGE0_OK) return rc;
+  return enqueue_tail(st, step, stream);
+}
+
+// after the layers: the routing every layer executed, gathered, and every
+// owner layer's head, batched
+static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream) {
+  const edge0_moe_shape& sh = st->shape;
+  const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers;
+  int rc = EDGE0_OK;
   k_gather_routing<<<1, 256, 0, stream>>>(st->exec_ids[step & 1], st->exec_w[step & 1],
                                           st->pred_ids[step % 3], st->pred_w[step % 3], Lc, K,
                                           st->spec.consumer_first, st->spec.consumer_last, step,
@@ -173,6 +191,76 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     if (rc != EDGE0_OK) return rc;
   }
   return EDGE0_OK;
+}
+
+// Persistent mode: layers 0..n-1 as one cooperative launch, then the
+// gathered routing and the batched heads as usual.
+static int enqueue_flow_step(edge0_stack* st, int step, hipStream_t stream) {
+  const edge0_moe_shape& sh = st->shape;
+  const int Lc = st->spec.n_layers, K = sh.top_k;
+  const WsLayout wl = ws_layout(&sh);
+  char* ws = static_cast<char*>(st->ws);
+  FlowArgs a{};
+  a.d = sh.d_model;
+  a.E = sh.n_experts;
+  a.I = sh.d_inter;
+  a.K = K;
+  a.g = sh.group_size;
+  a.r = sh.lora_rank;
+  a.n_layers = Lc;
+  a.scale = sh.lora_rank > 0 ? sh.lora_alpha / (float)sh.lora_rank : 0.f;
+  a.eps = st->spec.rms_eps;
+  if (bundle_layout(&sh, &a.lay) != EDGE0_OK) return EDGE0_EINVAL;
+  a.pool = static_cast<const uint8_t*>(st->pool.base);
+  a.slot_bytes = st->pool.slot_bytes;
+  a.n_slots = st->pool.n_slots;
+  a.tables = st->tables;
+  a.routers = st->flow_routers;
+  a.pred_ids = st->pred_ids[step % 3];
+  a.pred_w = st->pred_w[step % 3];
+  a.exec_ids = st->exec_ids[step & 1];
+  a.exec_w = st->exec_w[step & 1];
+  a.consumer_first = st->spec.consumer_first;
+  a.consumer_last = st->spec.consumer_last;
+  a.step = step;
+  a.x = st->x;
+  a.y = st->y;
+  a.h = st->h;
+  a.acc = reinterpret_cast<unsigned long long*>(ws + wl.acc);
+  a.hp_hi = reinterpret_cast<uint32_t*>(ws + wl.hp_hi);
+  a.hp_lo = reinterpret_cast<uint32_t*>(ws + wl.hp_lo);
+  a.hs = reinterpret_cast<float*>(ws + wl.hs);
+  a.tdown = reinterpret_cast<unsigned long long*>(ws + wl.tdpart);  // K * r <= its size / 8
+  a.t_in = reinterpret_cast<float*>(ws + wl.t_in);
+  a.logits = st->logits;
+  a.cnt = st->flow_cnt;
+  a.err = reinterpret_cast<uint32_t*>(ws + wl.err);
+  a.abort_word = st->flow_abort;
+  a.spin = st->flow_spin;
+  const int G = flow_grid(sh);
+  const int rbs = sh.d_model / 64, NC = sh.d_inter / 32;
+  a.S = G / rbs;
+  a.cps = (NC + a.S - 1) / a.S;
+  // the phases of this step in order (R for router layers, T when there is
+  // LoRA, A, D); each of phase p's counters completes when it has received
+  // G / kFlowCounters more arrivals than at its last use
+  int p = 0;
+  for (int L = 0; L < Lc; ++L) {
+    const bool by_pred = is_consumer(st->spec, L) && step > 0;
+    const int n = (by_pred ? 2 : 3) + (sh.lora_rank > 0 ? 1 : 0);
+    for (int i = 0; i < n; ++i, ++p)
+      a.target[p] = (uint32_t)(G / kFlowCounters) * (st->flow_uses[p] + 1u);
+  }
+  LaunchTiming lt{st->timed_kernel, nullptr, nullptr};
+  if (st->timed_kernel > 0 && hipEventRecord(st->ev_start[0], stream) != hipSuccess)
+    return EDGE0_EHIP;
+  const int rc = launch_flow_step(a, G, stream);
+  if (rc != EDGE0_OK) return rc;
+  (void)lt;
+  if (st->timed_kernel > 0 && hipEventRecord(st->ev_stop[0], stream) != hipSuccess)
+    return EDGE0_EHIP;
+  for (int i = 0; i < p; ++i) ++st->flow_uses[i];
+  return enqueue_tail(st, step, stream);
 }
 
 extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
@@ -283,6 +371,15 @@ extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, in
   const size_t d = st->shape.d_model;
   if (hipMemcpyAsync(st->h, h0, d * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return EDGE0_EHIP;
+  if (st->mode == EDGE0_STACK_PERSISTENT) {
+    const int rc = enqueue_flow_step(st, step, stream);
+    if (rc != EDGE0_OK) return rc;
+    if (hipMemcpyAsync(h_out, st->h + (size_t)st->spec.n_layers * d, d * 2,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return EDGE0_EHIP;
+    st->last_step = step;
+    return EDGE0_OK;
+  }
   if (st->timed_kernel > 0) {
     // measurement mode: the same launches enqueued directly (events cannot be
     // timed inside a graph), each layer's chosen launch bracketed by events
@@ -481,11 +578,55 @@ extern "C" int edge0_stack_set_timing(edge0_stack* st, int32_t kernel) {
 extern "C" int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n_out) {
   if (!st || !ms_out || !n_out || st->timed_kernel <= 0 || st->last_step < 0) return EDGE0_EINVAL;
   if (hipDeviceSynchronize() != hipSuccess) return EDGE0_EHIP;
-  const int n = st->spec.n_layers < cap ? st->spec.n_layers : cap;
+  const int n = st->mode == EDGE0_STACK_PERSISTENT ? (cap > 0 ? 1 : 0)
+                                                   : (st->spec.n_layers < cap ? st->spec.n_layers : cap);
   for (int L = 0; L < n; ++L)
     if (hipEventElapsedTime(&ms_out[L], st->ev_start[L], st->ev_stop[L]) != hipSuccess)
       return EDGE0_EHIP;
   *n_out = n;
+  return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_set_mode(edge0_stack* st, int32_t mode) {
+  if (!st || (mode != EDGE0_STACK_GRAPHS && mode != EDGE0_STACK_PERSISTENT)) return EDGE0_EINVAL;
+  if (mode == EDGE0_STACK_PERSISTENT) {
+    const int Lc = st->spec.n_layers;
+    if (!flow_shape_ok(st->shape, Lc)) return EDGE0_EINVAL;
+    const int rc = flow_coresident(flow_grid(st->shape));
+    if (rc != EDGE0_OK) return rc;
+    if (!st->flow_cnt) {
+      const size_t cnt_bytes = (size_t)kFlowMaxPhases * kFlowCounters * 64 * 4;
+      if (hipMalloc((void**)&st->flow_cnt, cnt_bytes) != hipSuccess ||
+          hipMalloc((void**)&st->flow_abort, 4) != hipSuccess ||
+          hipMalloc((void**)&st->flow_routers, Lc * sizeof(void*)) != hipSuccess)
+        return EDGE0_ENOMEM;
+      if (hipMemset(st->flow_cnt, 0, cnt_bytes) != hipSuccess ||
+          hipMemset(st->flow_abort, 0, 4) != hipSuccess ||
+          hipMemcpy(st->flow_routers, st->routers.data(), Lc * sizeof(void*),
+                    hipMemcpyHostToDevice) != hipSuccess)
+        return EDGE0_EHIP;
+      st->flow_uses.assign(kFlowMaxPhases, 0u);
+      if (st->flow_spin <= 0) st->flow_spin = kFlowDefaultSpin;
+    }
+  }
+  st->mode = mode;
+  return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_error(edge0_stack* st) {
+  if (!st) return EDGE0_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess) return EDGE0_EHIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, st->ws, 4, hipMemcpyDeviceToHost) != hipSuccess) return EDGE0_EHIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(st->ws, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return EDGE0_EHIP;
+  if (v & (uint32_t)(-EDGE0_EHIP)) return EDGE0_EHIP;
+  return v ? EDGE0_ERANGE : EDGE0_OK;
+}
+
+extern "C" int edge0_stack_set_spin_limit(edge0_stack* st, int64_t polls) {
+  if (!st || polls < 0) return EDGE0_EINVAL;
+  st->flow_spin = polls > 0 ? polls : kFlowDefaultSpin;
   return EDGE0_OK;
 }
 
@@ -497,6 +638,9 @@ extern "C" void edge0_stack_destroy(edge0_stack* st) {
     if (g) (void)hipGraphExecDestroy(g);
   if (st->cap) (void)hipStreamDestroy(st->cap);
   if (st->ev_heads) (void)hipEventDestroy(st->ev_heads);
+  (void)hipFree(st->flow_cnt);
+  (void)hipFree(st->flow_abort);
+  (void)hipFree(const_cast<uint16_t**>(st->flow_routers));
 
   (void)hipFree(st->x);
   (void)hipFree(st->y);

@@ -104,6 +104,9 @@ _SIG = {
     "edge0_stack_get_buffers": (C.c_int, [_P, C.POINTER(StackBuffers)]),
     "edge0_stack_destroy": (None, [_P]),
     "edge0_stack_set_timing": (C.c_int, [_P, C.c_int32]),
+    "edge0_stack_set_mode": (C.c_int, [_P, C.c_int32]),
+    "edge0_stack_set_spin_limit": (C.c_int, [_P, C.c_int64]),
+    "edge0_stack_error": (C.c_int, [_P]),
     "edge0_stack_kernel_ms": (C.c_int, [_P, C.POINTER(C.c_float), C.c_int32,
                                         C.POINTER(C.c_int32)]),
     "edge0_stack_step_staged": (C.c_int, [_P, _P, C.POINTER(StagePlan), _P, _P, C.c_int32, _P]),
@@ -218,6 +221,8 @@ def edge0_moe_layer(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y, w
 
 
 EDGE0_GROUPED_NO_MFMA = 1
+EDGE0_STACK_GRAPHS = 0
+EDGE0_STACK_PERSISTENT = 1
 
 
 def grouped_mfma_min(n: int) -> int:
@@ -258,6 +263,18 @@ class Stack:
     def step(self, h0, h_out, step: int, stream=None):
         _check(lib.edge0_stack_step(self._handle, _ptr(h0), _ptr(h_out), step, _stream(stream)),
                "edge0_stack_step")
+
+    def set_mode(self, mode: int):
+        """EDGE0_STACK_GRAPHS (per-layer launches as graphs) or
+        EDGE0_STACK_PERSISTENT (one cooperative launch for the layers)."""
+        _check(lib.edge0_stack_set_mode(self._handle, mode), "edge0_stack_set_mode")
+
+    def set_spin_limit(self, polls: int):
+        _check(lib.edge0_stack_set_spin_limit(self._handle, polls), "edge0_stack_set_spin_limit")
+
+    def error(self) -> int:
+        """The handle's recorded error code (EDGE0_OK, EDGE0_ERANGE, EDGE0_EHIP), cleared."""
+        return int(lib.edge0_stack_error(self._handle))
 
     def set_timing(self, kernel: int):
         """Event pair around one launch class per layer (1 gate/up, 2 down, 3 LoRA-in)."""

@@ -150,3 +150,60 @@ def test_qwen3moe_stack_sampled_layers(torch_cuda):
     assert report.count("exact") >= 0.8 * len(report), report
     print(f"[stack] qwen3moe: worst rel-L2 {max(rels):.3e}, median {np.median(rels):.3e}, "
           f"waived {report.count('waived')}/{len(report)}")
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_stack_persistent_sampled_layers(torch_cuda):
+    """The persistent mode (one cooperative launch for the 40 layers), the
+    configuration the benchmark times: router layers at step 0 and at 0-6 and
+    39, prediction-routed layers after, teacher-forced on sampled layers."""
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    S, seed = G.QWEN3_MOE, 0
+    owners, consumers = range(6, 38), range(7, 39)
+    ds = DeviceStack(S, G.StackGen(S, seed), 40, (6, 37), (7, 38))
+    ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
+    sample = {0: [0, 1, 6, 7, 20, 39], 1: [0, 5, 6, 7, 8, 22, 37, 38, 39],
+              2: [1, 7, 19, 38, 39], 3: [6, 7, 30]}
+    report, rels = _run(ds, S, seed, 4, lambda t: sample[t], owners, consumers)
+    assert ds.stack.error() == E.EDGE0_OK
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[stack] qwen3moe persistent: worst rel-L2 {max(rels):.3e}, median "
+          f"{np.median(rels):.3e}, waived {report.count('waived')}/{len(report)}")
+
+
+def test_persistent_mode_rejects_unsupported_shape(torch_cuda):
+    """The tiny layer shape (d_model 256) is outside the persistent path:
+    EDGE0_EINVAL and the graph mode stays in force."""
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    S = G.TINY
+    ds = DeviceStack(S, G.StackGen(S, 1), 4, (1, 2), (2, 3), log=None)
+    with pytest.raises(E.Edge0Error) as ei:
+        ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
+    assert ei.value.code == E.EDGE0_EINVAL
+    with pytest.raises(E.Edge0Error):
+        ds.stack.set_mode(7)
+
+
+def test_persistent_mode_bounded_wait_reports_error(torch_cuda):
+    """A workgroup that waits past the spin limit at a grid boundary records
+    EDGE0_EHIP, raises the abort word and leaves; every other workgroup exits
+    on seeing it.  Forced from the host with a limit of one poll, on a
+    4-layer stack of Qwen3-MoE-shaped layers; the launch must end (no hang)
+    and report the error."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    from int4_expert_streaming_amd.weights import to_device
+    S = G.QWEN3_MOE
+    ds = DeviceStack(S, G.StackGen(S, 5), 4, (1, 2), (2, 3), log=None)
+    ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
+    ds.stack.set_spin_limit(1)
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    ds.step(to_device(G.stack_hidden(S, 5, 0)), h_out, 0)
+    torch.cuda.synchronize()
+    assert ds.stack.error() == E.EDGE0_EHIP
+    with pytest.raises(E.Edge0Error):
+        ds.stack.set_spin_limit(-1)
+    ds.stack.close()
