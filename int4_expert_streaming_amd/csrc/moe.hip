@@ -416,18 +416,8 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   gu_load<NJ, RW>(a, b, i0, gw);
   uint4 ar[AR][4 * NJ];  // LoRA A rows (wave + 8 m, clamped): 16-byte pieces lane + 64 q,
                         // so each load instruction reads 1 KiB of a row contiguously
-  const int nr2 = r > 0 ? 2 * r : 1;
-#pragma unroll
-  for (int m = 0; m < AR; ++m) {
-    const int tr = min(wave + 8 * m, nr2 - 1);
-    const int rr = r > 0 ? tr % r : 0;
-    const uint16_t* arow = reinterpret_cast<const uint16_t*>(
-                               b + ((r > 0 && tr >= r) ? a.lay.a_up : a.lay.a_gate)) +
-                           (size_t)rr * d;
-#pragma unroll
-    for (int q = 0; q < 4 * NJ; ++q)
-      ar[m][q] = reinterpret_cast<const uint4*>(arow)[lane + 64 * q];
-  }
+                        // (loaded after the prologue)
+
   // 3. combine, residual, RMSNorm -> x in LDS (TOPK: x as given)
   if constexpr (TOPK) {
 #pragma unroll
@@ -477,6 +467,21 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
     for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
   }
   }  // prologue
+  // LoRA A rows, issued only once x is formed: they are L2-shared by the
+  // expert's workgroups, and requested earlier they delay the prologue's
+  // reads of the previous layer's output
+  const int nr2 = r > 0 ? 2 * r : 1;
+#pragma unroll
+  for (int m = 0; m < AR; ++m) {
+    const int tr = min(wave + 8 * m, nr2 - 1);
+    const int rr = r > 0 ? tr % r : 0;
+    const uint16_t* arow = reinterpret_cast<const uint16_t*>(
+                               b + ((r > 0 && tr >= r) ? a.lay.a_up : a.lay.a_gate)) +
+                           (size_t)rr * d;
+#pragma unroll
+    for (int q = 0; q < 4 * NJ; ++q)
+      ar[m][q] = reinterpret_cast<const uint4*>(arow)[lane + 64 * q];
+  }
   if (blk == 0 && tid == 0) {
     a.slots[k] = ok ? slot : -1;
     if (!ok) set_error(a.err, EDGE0_ERANGE);
