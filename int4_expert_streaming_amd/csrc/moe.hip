@@ -552,9 +552,11 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
 
 // ------------------------------------------------------------------ k_down
 // Unit (rb, sl): rows 64 rb .. 64 rb + 63 over input chunks of slice sl, for
-// all K experts, each tile's contribution weighted by w_k; slice-0 units add
-// the LoRA-down deltas.  The partial row is added to the layer's fixed-point
-// accumulator (exact, order-independent).
+// all K experts, each tile's contribution weighted by w_k.  The LoRA-down
+// delta is linear in t_down = A_down h = sum over chunks of the chunk's part,
+// so each tile (k, c) also adds (alpha/r) w_k B_down[o] . (A_down h)_c: every
+// unit carries an equal share of it.  The partial row is added to the layer's
+// fixed-point accumulator (exact, order-independent).
 // The unit's nt = K * ncs tiles (expert-major) are split into contiguous runs
 // of TPW tiles per wave; every address is wave-uniform scalar arithmetic so
 // all of a wave's tile loads are in flight together.  An expert whose slot is
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   __shared__ float red[4][64];
   __shared__ uint32_t hp_s[kMaxSliceChunks][32];  // hi pairs then lo pairs of each chunk
   __shared__ float hsum_s[kMaxSliceChunks];
-  __shared__ float td_s[4][64];                   // t_down of the expert each wave handles
+  __shared__ float tdc_s[kMaxSliceChunks][64];    // per tile: the chunk's part of A_down h
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int K = a.K, S = a.S, I = a.I, r = a.r, d = a.d;
@@ -584,6 +586,8 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   uint4 q[TPW];
   uint32_t sv[TPW], bv[TPW];
   float wt[TPW];
+  constexpr int kBd = 2;  // B_down pieces (8 ranks each) held per tile; more are read in the loop
+  uint4 bdq[TPW][kBd];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int t = wave * TPW + m;
@@ -599,30 +603,12 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
     const int grp = (32 * c) / a.g;
     sv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_s)[(size_t)grp * d + o];
     bv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_b)[(size_t)grp * d + o];
-  }
-  // LoRA-down for slice-0 units: wave w handles experts w, w+4, ...; t_down
-  // of expert k = sum over the 16-row partials of A_down h, where element
-  // t = blk*r + rr goes to lane t % 64 (which always holds rr = lane % r,
-  // r dividing 64); B_down row o.  The first expert's inputs are loaded here.
-  const bool lora_unit = r > 0 && sl == 0;
-  const int ntd = (I / 16) * r;
-  constexpr int kTd = 16;
-  float tdr[kTd];
-  uint4 bdr[8];
-  auto lora_loads = [&](int kk) {
-    int slot = a.slots[kk];
-    slot = (slot >= 0 && slot < a.n_slots) ? slot : 0;
-    const float* tp = a.tdpart + (size_t)kk * ntd;
-#pragma unroll
-    for (int m = 0; m < kTd; ++m) tdr[m] = (lane + 64 * m < ntd) ? tp[lane + 64 * m] : 0.f;
+    // B_down row o of the tile's expert (r bf16; an in-bundle word when r = 0)
     const uint4* Bdp = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(a.pool + (size_t)slot * a.slot_bytes + a.lay.b_down) +
-        (size_t)o * r);
+        reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.b_down : 0)) + (size_t)o * r);
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      if (8 * m < r) bdr[m] = Bdp[m];
-  };
-  if (lora_unit && wave < K) lora_loads(wave);
+    for (int j = 0; j < kBd; ++j) bdq[m][j] = (8 * j < r) ? Bdp[j] : make_uint4(0, 0, 0, 0);
+  }
   // stage the unit's activation pairs and chunk sums (all K experts) in LDS
   {
     constexpr int kStage = kMaxSliceChunks * 32 / 256;  // words per thread
@@ -652,6 +638,13 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
       if (t < nt * 32) hp_s[t >> 5][t & 31] = st[m];
     }
     if (tt < nt) hsum_s[tt] = h0v + h1v;
+    // each tile's chunk part of A_down h: its two 16-row partials
+    for (int e = threadIdx.x; e < nt * r; e += 256) {
+      const int te = e / r, rr = e % r;
+      const int kk = te / ncs, c = c0 + te % ncs;
+      const float* tp = a.tdpart + ((size_t)kk * (I / 16) + 2 * c) * r;
+      tdc_s[te][rr] = tp[rr] + tp[r + rr];
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x < (unsigned)K) {
     const int slot = a.slots[threadIdx.x];
@@ -666,38 +659,31 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
       const float s = bf2f(sv[m]), bb = bf2f(bv[m]);
       const uint32_t* hp = hp_s[t];
       const float acc = chunk_dot128(q[m], hp) + chunk_dot128(q[m], hp + 16);
-      part += wt[m] * (s * acc + (bb - 128.f * s) * hsum_s[t]);
-    }
-  }
-  if (lora_unit) {
-    for (int kk = wave; kk < K; kk += 4) {
-      const int slot = a.slots[kk];
-      if (slot < 0 || slot >= a.n_slots) continue;
-      if (kk != wave) lora_loads(kk);
-      float tdv = 0.f;
+      float dl = 0.f;  // B_down[o] . (A_down h)_c
+      for (int j = 0; 8 * j < r; ++j) {
+        uint4 bw4;
+        if (j < kBd) {
+          bw4 = bdq[m][j];
+        } else {
+          const int kk = t / ncs;
+          int slot = a.slots[kk];
+          slot = (slot >= 0 && slot < a.n_slots) ? slot : 0;
+          bw4 = reinterpret_cast<const uint4*>(
+              reinterpret_cast<const uint16_t*>(a.pool + (size_t)slot * a.slot_bytes +
+                                                a.lay.b_down) +
+              (size_t)o * r)[j];
+        }
+        const uint32_t bw[4] = {bw4.x, bw4.y, bw4.z, bw4.w};
+        const float4 t0 = *reinterpret_cast<const float4*>(&tdc_s[t][8 * j]);
+        const float4 t1 = *reinterpret_cast<const float4*>(&tdc_s[t][8 * j + 4]);
+        const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
-      for (int m = 0; m < kTd; ++m) tdv += tdr[m];
-      for (int t = lane + 64 * kTd; t < ntd; t += 64) tdv += a.tdpart[(size_t)kk * ntd + t];
-      for (int off = r; off < 64; off <<= 1) tdv += __shfl_xor(tdv, off, kWave);
-      td_s[wave][lane] = tdv;  // lane rr (< r) holds t_down[rr]; read back as a broadcast
-      __builtin_amdgcn_wave_barrier();
-      float dl = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        if (8 * m < r) {
-          const uint32_t bw[4] = {bdr[m].x, bdr[m].y, bdr[m].z, bdr[m].w};
-          const float4 t0 = *reinterpret_cast<const float4*>(&td_s[wave][8 * m]);
-          const float4 t1 = *reinterpret_cast<const float4*>(&td_s[wave][8 * m + 4]);
-          const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            dl += bf_lo(bw[q2]) * tv[2 * q2];
-            dl += bf_hi(bw[q2]) * tv[2 * q2 + 1];
-          }
+        for (int q2 = 0; q2 < 4; ++q2) {
+          dl += bf_lo(bw[q2]) * tv[2 * q2];
+          dl += bf_hi(bw[q2]) * tv[2 * q2 + 1];
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      part += a.w[kk] * (a.scale * dl);
+      part += wt[m] * (s * acc + (bb - 128.f * s) * hsum_s[t] + a.scale * dl);
     }
   }
   red[wave][lane] = part;
