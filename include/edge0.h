@@ -319,8 +319,11 @@ void edge0_stack_destroy(edge0_stack* st);
  * EDGE0_EINVAL for another mode value. */
 enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1 };
 int edge0_stack_set_mode(edge0_stack* st, int32_t mode);
-/* Polls per wait of the persistent mode before a workgroup gives up (0: the
- * default, about a second).  A failure-path aid; EDGE0_EINVAL for polls < 0. */
+/* Polls per bounded wait before a workgroup gives up (0: the default, about
+ * a second): the persistent mode's phase waits, and in the graphs mode the
+ * gate/up workgroups' wait for their expert's LoRA A x, which workgroups of
+ * the same launch compute.  A timed-out wait records EDGE0_EHIP (see
+ * edge0_stack_error).  A failure-path aid; EDGE0_EINVAL for polls < 0. */
 int edge0_stack_set_spin_limit(edge0_stack* st, int64_t polls);
 /* Workspace error word of the handle (see edge0_workspace_error): the
  * recorded codes, cleared. */

@@ -424,6 +424,7 @@ struct WsLayout {
   size_t err, cnt_router, cnt_head, cnt_down;     // u32 words / counters
   size_t logits, head_a, head_res;                // fp32
   size_t t_in;                                    // fp32 [K][2][r]
+  size_t t_hand;                                  // fp32 [K][2r] LoRA A x handed between workgroups
   size_t hf;                                      // fp32 [K][I]
   size_t hp_hi, hp_lo;                            // u16 [K][I]
   size_t hs;                                      // fp32 [K][I/16]

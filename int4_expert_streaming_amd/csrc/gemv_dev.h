@@ -44,11 +44,13 @@ struct GuW {
   uint32_t Bg[R], Bu[R];
 };
 
+// `wave` selects the rows (R * wave ..): a wave that only needs the loads
+// issued in order (not their values) passes the index of another wave
 template <int NJ, int RR = kWideRowsPerWave>
 __device__ __forceinline__ void gu_load(const MoeArgs& a, const uint8_t* b, int i0,
-                                        GuW<NJ, RR>& w) {
+                                        GuW<NJ, RR>& w, int wave = tid_here() >> 6) {
   constexpr int R = RR;
-  const int lane = tid_here() & 63, wave = tid_here() >> 6;
+  const int lane = tid_here() & 63;
   const int d = a.d, g = a.g, ng = d / g, r = a.r;
   const int row0 = i0 + R * wave;
   const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q);
@@ -131,17 +133,13 @@ __device__ __forceinline__ float wave_sums_2r(const float (&v)[2 * R]) {
   return w1;
 }
 
-// STORE: rows of h go to the workspace (store_h); otherwise only h_s and
-// hrep_s (hi + lo, the value the down GEMV sees) are written and the caller
-// publishes them.
-template <int NJ, int RR = kWideRowsPerWave, bool STORE = true>
-__device__ __forceinline__ void gu_finish(const MoeArgs& a, const GuW<NJ, RR>& w, int k, int i0,
-                                          const uint16_t* xsrc, float tg, float tu, float* h_s,
-                                          float* hrep_s) {
+// Per-lane partials of the wave's R gate rows (v[0..R-1]) and R up rows
+// (v[R..2R-1]) on x (global or LDS), without the LoRA term.
+template <int NJ, int RR>
+__device__ __forceinline__ void gu_base(const GuW<NJ, RR>& w, const uint16_t* xsrc,
+                                        float (&v)[2 * RR]) {
   constexpr int R = RR;
-  const int lane = tid_here() & 63, wave = tid_here() >> 6;
-  const int row0 = i0 + R * wave;
-  const bool has_l = a.r > 0 && lane < a.r;
+  const int lane = tid_here() & 63;
   XRaw xr[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) load_x_raw(xsrc, lane + 64 * j, xr[j]);
@@ -149,8 +147,6 @@ __device__ __forceinline__ void gu_finish(const MoeArgs& a, const GuW<NJ, RR>& w
   float X[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
-  // per-lane partials of the R gate (v[0..R-1]) and R up (v[R..2R-1]) rows
-  float v[2 * R];
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
     float G = 0.f, U = 0.f;
@@ -161,12 +157,28 @@ __device__ __forceinline__ void gu_finish(const MoeArgs& a, const GuW<NJ, RR>& w
       G += s1 * chunk_dot128(w.qg[ii][j], xp[j]) + (b1 - 128.f * s1) * X[j];
       U += s2 * chunk_dot128(w.qu[ii][j], xp[j]) + (b2 - 128.f * s2) * X[j];
     }
-    if (has_l) {
-      G += a.scale * (bf2f(w.Bg[ii]) * tg);
-      U += a.scale * (bf2f(w.Bu[ii]) * tu);
-    }
     v[ii] = G;
     v[R + ii] = U;
+  }
+}
+
+// The LoRA term (lane rr < r adds scale * B[row][rr] * t[rr]), the sums over
+// the wave and the SwiGLU of the R rows.  STORE: rows of h go to the
+// workspace (store_h); otherwise only h_s and hrep_s (hi + lo, the value the
+// down GEMV sees) are written and the caller publishes them.
+template <int NJ, int RR, bool STORE>
+__device__ __forceinline__ void gu_epilogue(const MoeArgs& a, const GuW<NJ, RR>& w, int k,
+                                            int i0, float (&v)[2 * RR], float tg, float tu,
+                                            float* h_s, float* hrep_s) {
+  constexpr int R = RR;
+  const int lane = tid_here() & 63, wave = tid_here() >> 6;
+  const int row0 = i0 + R * wave;
+  if (a.r > 0 && lane < a.r) {
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii) {
+      v[ii] += a.scale * (bf2f(w.Bg[ii]) * tg);
+      v[R + ii] += a.scale * (bf2f(w.Bu[ii]) * tu);
+    }
   }
   // lane (64/2R) * ii holds G of row ii, lane 32 + (64/2R) * ii its U
   const float w1 = wave_sums_2r<R>(v);
@@ -183,6 +195,16 @@ __device__ __forceinline__ void gu_finish(const MoeArgs& a, const GuW<NJ, RR>& w
       hrep_s[R * wave + ii] = bf2f(hi) + bf2f(f2bf(h - bf2f(hi)));
     }
   }
+}
+
+// gate/up of the wave's R row pairs: gu_base then gu_epilogue
+template <int NJ, int RR = kWideRowsPerWave, bool STORE = true>
+__device__ __forceinline__ void gu_finish(const MoeArgs& a, const GuW<NJ, RR>& w, int k, int i0,
+                                          const uint16_t* xsrc, float tg, float tu, float* h_s,
+                                          float* hrep_s) {
+  float v[2 * RR];
+  gu_base<NJ, RR>(w, xsrc, v);
+  gu_epilogue<NJ, RR, STORE>(a, w, k, i0, v, tg, tu, h_s, hrep_s);
 }
 
 

@@ -316,44 +316,67 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 }
 
 // ------------------------------------------------------------- k_layer_fused
-// A prediction-routed layer's input and gate/up in one launch (wide rows,
-// lora_rank <= 16): every workgroup (16 rows of one routed expert) loads its
-// int4 rows and its expert's 2r LoRA A rows first, then redundantly forms the
-// layer input from L2-resident data (previous layer's fixed-point y, h,
-// RMSNorm) into LDS, computes t = A x for its expert (rows spread over the
-// waves), and runs the gate/up rows on x and t from LDS.  Workgroup 0 stores
-// h, y_prev, x and clears this layer's accumulator; the first workgroup of
-// each expert publishes its slot for the down kernel.  Replaces k_layer_in +
-// k_gate_up (one fewer dependent launch per layer).
-constexpr int kFusedMaxRank = 16;  // 2r A rows over 8 waves: <= 4 rows per wave
+// A layer's input and gate/up in one launch for a layer whose routing is
+// known when it starts (wide rows, lora_rank <= 16).  Two kinds of workgroup:
+//  - a.n_prod LoRA producers, the first workgroups of the grid (dispatched
+//    before any workgroup that waits for them): each loads a.prod_rows of
+//    the routed experts' LoRA A rows, forms the layer input x like every
+//    other workgroup and stores t = A x for its rows into t_hand;
+//  - K * d_inter / 16 gate/up workgroups (16 rows of one routed expert):
+//    each loads its int4 rows first, forms x redundantly from L2-resident
+//    data (previous layer's fixed-point y, h, RMSNorm) into LDS and computes
+//    the rows' dot products, while a ninth wave waits (bounded) for the
+//    expert's t in t_hand; then the LoRA term and the SwiGLU epilogue.
+// Gate/up workgroup 0 stores h, y_prev, x and clears this layer's
+// accumulator; the first workgroup of each expert publishes its slot for the
+// down kernel.  One launch replaces k_layer_in + k_gate_up, and A x is
+// computed once per expert instead of once per workgroup.
+constexpr int kFusedMaxRank = 16;
 constexpr int kFusedRowsPerWave = 2;  // 8 waves: 16 rows of gate and up per workgroup
 constexpr int kFusedMaxExperts = 256;  // slot-table row held in 4 registers per lane
+constexpr int kFusedMaxProdRows = 8;   // A rows per producer: 2, 4 or 8
 
 // TOPK: a router layer after its router launch (which formed x and the
 // logits): every wave commits the top-K of li.logits itself (no hand-off),
 // workgroup 0 stores ids/w, and x is read instead of formed.
+constexpr int kFusedThreads = 576;  // 8 compute waves + the hand-off wave
+
 template <int NJ, bool TOPK>
-__global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
+__global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerIn li) {
   constexpr int PER = 4 * NJ;  // hidden elements per thread (d = 2048 NJ, 512 threads)
-  constexpr int AR = 2 * kFusedMaxRank / 8;
   constexpr int RW = kFusedRowsPerWave, ROWS = 8 * RW;  // rows per workgroup
+  constexpr int MU = kFusedMaxProdRows * NJ / 2;        // producer: A pieces per thread (max)
   __shared__ uint16_t xs[2048 * NJ];
   __shared__ float t_s[2][kFusedMaxRank];
   __shared__ float red[8];
+  __shared__ float redp[MU][8];
   __shared__ float h_s[ROWS];
   __shared__ float hrep_s[ROWS];
-  __shared__ int32_t ids_w[TOPK ? 8 : 1][16];
-  __shared__ float w_w[TOPK ? 8 : 1][16];
+  __shared__ int32_t ids_w[TOPK ? 9 : 1][16];
+  __shared__ float w_w[TOPK ? 9 : 1][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // compute waves 0-7; wave 8 waits for the hand-off.  Wave 8 issues wave
+  // 0's loads too (tl, wl): no branch then separates any wave's loads from
+  // their first use, so each wait covers only the loads issued before them
+  const bool cw = wave < 8;
+  const int tl = cw ? tid : tid - 512, wl = cw ? wave : 0;
   const int d = a.d, r = a.r;
   const int nwg = a.I / ROWS;
-  // XCD-aware order: consecutive workgroups go to different XCDs
-  // (round-robin over 8), so logical block L = (id % 8) * (grid / 8) + id / 8
-  // gives each XCD a contiguous range of an expert's blocks and the expert's
-  // shared LoRA A rows are fetched by few XCD L2s
-  const int gsz = gridDim.x;
-  const int lb = (gsz % 8 == 0) ? (blockIdx.x % 8) * (gsz / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int k = lb / nwg;
+  const int P = a.n_prod;
+  const bool prod = (int)blockIdx.x < P;
+  // XCD-aware order of the gate/up workgroups: consecutive workgroups go to
+  // different XCDs (round-robin over 8; P is a multiple of 8), so logical
+  // block L = (id % 8) * (n / 8) + id / 8 gives each XCD a contiguous range
+  // of an expert's blocks
+  int k, lb = 0;
+  if (prod) {
+    k = (int)blockIdx.x * a.prod_rows / (2 * r);
+    if (k >= a.K) return;  // padding producer
+  } else {
+    const int id = blockIdx.x - P, gsz = gridDim.x - P;
+    lb = (gsz % 8 == 0) ? (id % 8) * (gsz / 8) + id / 8 : id;
+    k = lb / nwg;
+  }
   const int i0 = (lb % nwg) * ROWS;
   const int nblk = a.I / 16;
   const int blk = i0 / 16;  // first 16-row block of the workgroup
@@ -366,33 +389,27 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   // 1. the prologue's loads: h_prev and the previous layer's fixed-point y,
   // written by other workgroups (other XCDs) just before; few wide requests.
   // Thread tid owns elements j = 4 (tid + 512 c) + e, c < NJ, e < 4.
-  uint32_t hb[PER];
+  uint2 hq[NJ];  // h_prev words (bf16 pairs)
   unsigned long long av[PER];
   uint2 xq[NJ];
   if constexpr (TOPK) {
 #pragma unroll
-    for (int c = 0; c < NJ; ++c) xq[c] = *reinterpret_cast<const uint2*>(a.x + 4 * (tid + 512 * c));
+    for (int c = 0; c < NJ; ++c) xq[c] = *reinterpret_cast<const uint2*>(a.x + 4 * (tl + 512 * c));
   } else {
 #pragma unroll
     for (int c = 0; c < NJ; ++c) {
-      const int j0 = 4 * (tid + 512 * c);
-      const uint2 hq = *reinterpret_cast<const uint2*>(li.h_prev + j0);
+      const int j0 = 4 * (tl + 512 * c);
+      hq[c] = *reinterpret_cast<const uint2*>(li.h_prev + j0);
       const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
       const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
-      hb[4 * c + 0] = hq.x & 0xFFFFu;
-      hb[4 * c + 1] = hq.x >> 16;
-      hb[4 * c + 2] = hq.y & 0xFFFFu;
-      hb[4 * c + 3] = hq.y >> 16;
       av[4 * c + 0] = a0.x;
       av[4 * c + 1] = a0.y;
       av[4 * c + 2] = a1.x;
       av[4 * c + 3] = a1.y;
     }
   }
-  // 2. this expert's bundle, then every weight load of the wave (HBM).  No
-  // branch separates these loads from the prologue's first use of hb/av, so
-  // the wait before it covers only the loads issued before them; an invalid
-  // slot reads slot 0 and its results are discarded.
+  // 2. this expert's bundle; an invalid slot reads slot 0 and its results
+  // are discarded
   int expert;
   if constexpr (TOPK) {
     wave_topk<false>(li.logits, a.E, a.K, ids_w[wave], w_w[wave]);
@@ -412,76 +429,136 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
   }
   const bool ok = slot >= 0;
   const uint8_t* b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
-  GuW<NJ, RW> gw;
-  gu_load<NJ, RW>(a, b, i0, gw);
-  uint4 ar[AR][4 * NJ];  // LoRA A rows (wave + 8 m, clamped): 16-byte pieces lane + 64 q,
-                        // so each load instruction reads 1 KiB of a row contiguously
-                        // (loaded after the prologue)
 
-  // 3. combine, residual, RMSNorm -> x in LDS (TOPK: x as given)
-  if constexpr (TOPK) {
+  // 3. combine, residual, RMSNorm -> x in LDS (TOPK: x as given); `lead`
+  // stores h, y_prev, x (and the committed routing) and clears the
+  // accumulator
+  auto form_x = [&](bool lead) {
+    // the prologue's loaded values enter through an empty asm, so the
+    // compiler cannot hoist their first use (and its wait) above the weight
+    // loads issued in between
+    if constexpr (TOPK) {
 #pragma unroll
-    for (int c = 0; c < NJ; ++c) *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = xq[c];
+      for (int c = 0; c < NJ; ++c) asm volatile("" : "+v"(xq[c].x), "+v"(xq[c].y));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NJ; ++c) asm volatile("" : "+v"(hq[c].x), "+v"(hq[c].y));
+#pragma unroll
+      for (int m = 0; m < PER; ++m) asm volatile("" : "+v"(av[m]));
+    }
+    if constexpr (TOPK) {
+      if (cw) {
+#pragma unroll
+        for (int c = 0; c < NJ; ++c) *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = xq[c];
+      }
+      __syncthreads();
+      if (lead && tid < a.K) {
+        li.ids_out[tid] = ids_w[0][tid];
+        li.w_out[tid] = w_w[0][tid];
+      }
+    } else {
+      float hv[PER];
+      float ss = 0.f;
+      if (cw) {
+        uint32_t hb[PER];
+#pragma unroll
+        for (int c = 0; c < NJ; ++c) {
+          hb[4 * c + 0] = hq[c].x & 0xFFFFu;
+          hb[4 * c + 1] = hq[c].x >> 16;
+          hb[4 * c + 2] = hq[c].y & 0xFFFFu;
+          hb[4 * c + 3] = hq[c].y >> 16;
+        }
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          const uint32_t yb = f2bf(from_fix(av[m]));
+          hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
+          ss = fmaf(hv[m], hv[m], ss);
+          av[m] = yb;  // keep y_prev's bits for the stores below
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+      }
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
+      const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
+      uint32_t xw[2 * NJ];
+      if (cw) {
+#pragma unroll
+        for (int c = 0; c < NJ; ++c) {
+          xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
+          xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) =
+              make_uint2(xw[2 * c], xw[2 * c + 1]);
+        }
+      }
+      __syncthreads();
+      if (lead && cw) {
+#pragma unroll
+        for (int c = 0; c < NJ; ++c) {
+          const int j0 = 4 * (tid + 512 * c);
+          *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
+          *reinterpret_cast<uint2*>(li.y_prev_out + j0) =
+              make_uint2((uint32_t)av[4 * c] | ((uint32_t)av[4 * c + 1] << 16),
+                         (uint32_t)av[4 * c + 2] | ((uint32_t)av[4 * c + 3] << 16));
+          *reinterpret_cast<uint2*>(li.h_out + j0) =
+              make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
+                         f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
+        }
+        for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
+      }
+    }
+  };
+
+  if (prod) {
+    // LoRA producer: rows tr0 .. tr0 + RP - 1 of the expert's 2r A rows
+    // (gate rows, then up rows).  Piece u = tid + 512 m of the concatenated
+    // rows is 8 bf16: row u / (d / 8), position u % (d / 8); a wave's 64
+    // pieces lie in one row.
+    const int RP = a.prod_rows, nu = RP * d / 8;
+    const int tr0 = ((int)blockIdx.x * RP) % (2 * r);
+    uint4 ap[MU];
+#pragma unroll
+    for (int m = 0; m < MU; ++m) {
+      const int u = min(tl + 512 * m, nu - 1);  // past nu: repeats of the last piece
+      const int tr = tr0 + u / (d / 8);
+      const uint4* row = reinterpret_cast<const uint4*>(
+                             b + (tr < r ? a.lay.a_gate : a.lay.a_up)) +
+                         (size_t)(tr % r) * (d / 8);
+      ap[m] = row[u % (d / 8)];
+    }
+    form_x(false);
+    const uint4* xv = reinterpret_cast<const uint4*>(xs);
+#pragma unroll
+    for (int m = 0; m < MU; ++m) {
+      const int u = tid + 512 * m;
+      if (512 * m < nu && cw) {  // uniform over each wave
+        const uint4 xq4 = xv[u % (d / 8)];
+        float p = dot2bf(ap[m].x, xq4.x, 0.f);
+        p = dot2bf(ap[m].y, xq4.y, p);
+        p = dot2bf(ap[m].z, xq4.z, p);
+        p = dot2bf(ap[m].w, xq4.w, p);
+        p = wave_sum(p);
+        if (lane == 0) redp[m][wave] = p;
+      }
+    }
     __syncthreads();
-    if (lb == 0 && tid < a.K) {
-      li.ids_out[tid] = ids_w[0][tid];
-      li.w_out[tid] = w_w[0][tid];
+    if (tid < RP) {
+      float t = 0.f;
+      for (int m = 0; 512 * m < nu; ++m)
+        for (int w8 = 0; w8 < 8; ++w8)
+          if ((512 * m + 64 * w8) / (d / 8) == tid) t += redp[m][w8];
+      if (!ok || __float_as_uint(t) == kTHandEmpty) t = ok ? __uint_as_float(0x7FC00000u) : 0.f;
+      st_dev(a.t_hand + (size_t)k * 2 * r + tr0 + tid, t);
     }
-  } else {
-  float hv[PER];
-  float ss = 0.f;
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const uint32_t yb = f2bf(from_fix(av[m]));
-    hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
-    ss = fmaf(hv[m], hv[m], ss);
-    av[m] = yb;  // keep y_prev's bits for the stores below
+    return;
   }
-  ss = wave_sum(ss);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
-  const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
-  uint32_t xw[2 * NJ];
-#pragma unroll
-  for (int c = 0; c < NJ; ++c) {
-    xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
-    xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
-    *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = make_uint2(xw[2 * c], xw[2 * c + 1]);
-  }
-  __syncthreads();
-  if (lb == 0) {
-#pragma unroll
-    for (int c = 0; c < NJ; ++c) {
-      const int j0 = 4 * (tid + 512 * c);
-      *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
-      *reinterpret_cast<uint2*>(li.y_prev_out + j0) =
-          make_uint2((uint32_t)av[4 * c] | ((uint32_t)av[4 * c + 1] << 16),
-                     (uint32_t)av[4 * c + 2] | ((uint32_t)av[4 * c + 3] << 16));
-      *reinterpret_cast<uint2*>(li.h_out + j0) =
-          make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
-                     f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
-    }
-    for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
-  }
-  }  // prologue
-  // LoRA A rows, issued only once x is formed: they are L2-shared by the
-  // expert's workgroups, and requested earlier they delay the prologue's
-  // reads of the previous layer's output
-  const int nr2 = r > 0 ? 2 * r : 1;
-#pragma unroll
-  for (int m = 0; m < AR; ++m) {
-    const int tr = min(wave + 8 * m, nr2 - 1);
-    const int rr = r > 0 ? tr % r : 0;
-    const uint16_t* arow = reinterpret_cast<const uint16_t*>(
-                               b + ((r > 0 && tr >= r) ? a.lay.a_up : a.lay.a_gate)) +
-                           (size_t)rr * d;
-#pragma unroll
-    for (int q = 0; q < 4 * NJ; ++q)
-      ar[m][q] = reinterpret_cast<const uint4*>(arow)[lane + 64 * q];
-  }
+
+  // gate/up workgroup: every weight load of the compute waves (HBM), then x
+  GuW<NJ, RW> gw;
+  gu_load<NJ, RW>(a, b, i0, gw, wl);
+  form_x(lb == 0);
   if (blk == 0 && tid == 0) {
     a.slots[k] = ok ? slot : -1;
     if (!ok) set_error(a.err, EDGE0_ERANGE);
@@ -503,37 +580,40 @@ __global__ __launch_bounds__(512) void k_layer_fused(MoeArgs a, LayerIn li) {
     if (tid < NSUB) a.hs[(size_t)k * nblk + blk + tid] = 0.f;
     return;
   }
-  // 4. t = A x: wave rows tr = wave + 8 m; x pieces in the A rows' order
-  if (r > 0) {
-    const uint4* xv = reinterpret_cast<const uint4*>(xs) + lane;
-    float tv[4] = {0.f, 0.f, 0.f, 0.f};
+  // 4. gate/up rows on x from LDS (compute waves), meanwhile the expert's
+  // t = A x from its producers (hand-off wave: lane l < 2r polls entry l)
+  float v[2 * RW];
+  if (cw) {
+    gu_base<NJ, RW>(gw, xs, v);
+    // the dot products are done here, not after the barrier below
 #pragma unroll
-    for (int q = 0; q < 4 * NJ; ++q) {
-      const uint4 xq = xv[64 * q];
-#pragma unroll
-      for (int m = 0; m < AR; ++m) {
-        tv[m] = dot2bf(ar[m][q].x, xq.x, tv[m]);
-        tv[m] = dot2bf(ar[m][q].y, xq.y, tv[m]);
-        tv[m] = dot2bf(ar[m][q].z, xq.z, tv[m]);
-        tv[m] = dot2bf(ar[m][q].w, xq.w, tv[m]);
+    for (int i = 0; i < 2 * RW; ++i) asm volatile("" : "+v"(v[i]));
+  } else if (r > 0 && lane < 2 * r) {
+    const float* src = a.t_hand + (size_t)k * 2 * r + lane;
+    uint32_t bits;
+    int64_t n = 0;
+    for (;;) {
+      bits = __float_as_uint(ld_dev(src));
+      if (bits != kTHandEmpty) break;
+      if (++n >= a.spin) {
+        set_error(a.err, EDGE0_EHIP);
+        bits = 0;
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-    // rows m = 0..3 of the wave end up in lanes 0, 16, 32, 48
-    const float tr4 = wave_sums_2r<2>(tv);
-    if ((lane & 15) == 0) {
-      const int m = lane >> 4;
-      const int tr = wave + 8 * m;
-      if (m < AR && tr < 2 * r) t_s[tr / r][tr % r] = tr4;
-    }
+    t_s[lane / r][lane % r] = __uint_as_float(bits);
   }
   __syncthreads();
-  float tg = 0.f, tu = 0.f;
-  if (r > 0 && lane < r) {
-    tg = t_s[0][lane];
-    tu = t_s[1][lane];
+  // 5. the LoRA term and the 16-row epilogue
+  if (cw) {
+    float tg = 0.f, tu = 0.f;
+    if (r > 0 && lane < r) {
+      tg = t_s[0][lane];
+      tu = t_s[1][lane];
+    }
+    gu_epilogue<NJ, RW, true>(a, gw, k, i0, v, tg, tu, h_s, hrep_s);
   }
-  // 5. gate/up rows on x and t from LDS, then the 16-row epilogue
-  gu_finish<NJ, RW>(a, gw, k, i0, xs, tg, tu, h_s, hrep_s);
   __syncthreads();
   if (tid < NSUB) {
     float sm = 0.f;
@@ -646,9 +726,14 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
       tdc_s[te][rr] = tp[rr] + tp[r + rr];
     }
   }
-  if (blockIdx.x == 0 && threadIdx.x < (unsigned)K) {
-    const int slot = a.slots[threadIdx.x];
-    if (slot < 0 || slot >= a.n_slots) set_error(a.err, EDGE0_ERANGE);
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < (unsigned)K) {
+      const int slot = a.slots[threadIdx.x];
+      if (slot < 0 || slot >= a.n_slots) set_error(a.err, EDGE0_ERANGE);
+    }
+    // the layer kernel before this one has consumed the LoRA hand-off
+    // entries: empty them for the next
+    for (int i = threadIdx.x; i < K * 2 * r; i += 256) a.t_hand[i] = __uint_as_float(kTHandEmpty);
   }
   __syncthreads();  // every thread, unconditionally
   float part = 0.f;
@@ -764,6 +849,10 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->err = reinterpret_cast<uint32_t*>(ws + L.err);
   a->cnt_down = reinterpret_cast<uint32_t*>(ws + L.cnt_down);
   a->t_in = reinterpret_cast<float*>(ws + L.t_in);
+  a->t_hand = reinterpret_cast<float*>(ws + L.t_hand);
+  a->n_prod = 0;
+  a->prod_rows = 0;
+  a->spin = kFusedDefaultSpin;
   a->hf = reinterpret_cast<float*>(ws + L.hf);
   a->hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
   a->hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
@@ -859,23 +948,38 @@ int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing
 }
 
 bool layer_fused_ok(const MoeArgs& a) {
-  return (a.d == 2048 || a.d == 4096) && a.r <= kFusedMaxRank &&
+  return (a.d == 2048 || a.d == 4096) && a.r <= kFusedMaxRank && a.r % 8 == 0 &&
          a.I % (8 * kFusedRowsPerWave) == 0 && a.E <= kFusedMaxExperts;
+}
+
+// LoRA producers of the fused layer kernel: 2, 4 or 8 A rows each (a divisor
+// of 2r), at most 64 producers where possible, their count a multiple of 8
+static void fused_producers(const MoeArgs& a, int* n_prod, int* rows) {
+  *n_prod = 0;
+  *rows = 0;
+  if (a.r == 0) return;
+  const int nr = a.K * 2 * a.r;
+  int rp = 2;
+  while (nr / rp > 64 && rp < kFusedMaxProdRows) rp *= 2;
+  *rows = rp;
+  *n_prod = ((nr + rp - 1) / rp + 7) / 8 * 8;
 }
 
 int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
                        const LaunchTiming* timing) {
   if (!layer_fused_ok(a)) return EDGE0_EINVAL;
-  const int grid = a.K * (a.I / (8 * kFusedRowsPerWave));
+  MoeArgs b = a;
+  fused_producers(a, &b.n_prod, &b.prod_rows);
+  const int grid = b.n_prod + a.K * (a.I / (8 * kFusedRowsPerWave));
   const bool topk = li.flags & IN_TOPK;
   auto kern = a.d == 2048 ? (topk ? k_layer_fused<1, true> : k_layer_fused<1, false>)
                           : (topk ? k_layer_fused<2, true> : k_layer_fused<2, false>);
   if (timing && timing->which == 1) {
     // measured launch: events recorded by the dispatch at its start and end
-    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, stream, timing->start, timing->stop, 0,
-                          a, li);
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), 0, stream, timing->start,
+                          timing->stop, 0, b, li);
   } else {
-    kern<<<grid, 512, 0, stream>>>(a, li);
+    kern<<<grid, kFusedThreads, 0, stream>>>(b, li);
   }
   E0_CHECK_LAUNCH();
   return EDGE0_OK;

@@ -35,7 +35,17 @@ struct MoeArgs {
   unsigned long long* acc;  // [d] this layer's y in fixed point (down units add into it)
   const unsigned long long* acc_prev;  // [d] the previous layer's (combined by k_layer_in)
   int S;  // down slices
+  // LoRA A x of the fused layer kernel, computed once per routed expert by
+  // n_prod producer workgroups (prod_rows A rows each) and handed to the
+  // gate/up workgroups through t_hand: an entry holds kTHandEmpty until its
+  // value is stored; the down kernel empties it again.  Waits give up after
+  // `spin` polls (error EDGE0_EHIP).
+  float* t_hand;
+  int n_prod, prod_rows;
+  int64_t spin;
 };
+constexpr uint32_t kTHandEmpty = 0xFFFFFFFFu;  // a NaN no stored value takes
+constexpr int64_t kFusedDefaultSpin = 1 << 21;
 
 int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const int32_t* table,
                   const int32_t* ids, const float* w, const void* x, void* y, void* workspace,

@@ -75,7 +75,7 @@ struct edge0_stack {
   uint32_t* flow_abort;              // raised by a workgroup whose wait timed out
   const uint16_t** flow_routers;     // device copy of the router pointers
   std::vector<uint32_t> flow_uses;   // completed uses of each counter
-  int64_t flow_spin;                 // polls per wait before giving up
+  int64_t spin;                      // polls per bounded wait before giving up (both modes)
 };
 
 static bool is_consumer(const edge0_stack_spec& s, int L) {
@@ -104,6 +104,7 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     int rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
                            st->y + (size_t)L * d, st->ws, &a);
     if (rc != EDGE0_OK) return rc;
+    a.spin = st->spin;
     // fixed-point y accumulators alternate between layers
     unsigned long long* acc0 = a.acc;
     a.acc = acc0 + (size_t)(L & 1) * d;
@@ -236,7 +237,7 @@ static int enqueue_flow_step(edge0_stack* st, int step, hipStream_t stream) {
   a.cnt = st->flow_cnt;
   a.err = reinterpret_cast<uint32_t*>(ws + wl.err);
   a.abort_word = st->flow_abort;
-  a.spin = st->flow_spin;
+  a.spin = st->spin;
   const int G = flow_grid(sh);
   const int rbs = sh.d_model / 64, NC = sh.d_inter / 32;
   a.S = G / rbs;
@@ -295,6 +296,7 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   st->routers.assign(routers, routers + Lc);
   st->heads.assign(heads, heads + Lc);
   st->last_step = -1;
+  st->spin = kFlowDefaultSpin;
   const size_t d = shape->d_model, K = shape->top_k;
   st->ws_bytes = edge0_workspace_bytes(shape);
   bool ok = hipMalloc((void**)&st->x, Lc * d * 2) == hipSuccess &&
@@ -346,6 +348,8 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
     ok = hipMalloc((void**)&st->pred_ids[i], Lc * K * 4) == hipSuccess &&
          hipMalloc((void**)&st->pred_w[i], Lc * K * 4) == hipSuccess;
   ok = ok && hipMemset(st->ws, 0, st->ws_bytes) == hipSuccess &&
+       hipMemset(static_cast<uint8_t*>(st->ws) + ws_layout(shape).t_hand, 0xFF,
+                 (size_t)4 * K * 2 * shape->lora_rank) == hipSuccess &&
        hipMemset(st->x, 0, Lc * d * 2) == hipSuccess &&
        hipMemset(st->y, 0, Lc * d * 2) == hipSuccess;
   for (int i = 0; i < 2 && ok; ++i)
@@ -606,7 +610,6 @@ extern "C" int edge0_stack_set_mode(edge0_stack* st, int32_t mode) {
                     hipMemcpyHostToDevice) != hipSuccess)
         return EDGE0_EHIP;
       st->flow_uses.assign(kFlowMaxPhases, 0u);
-      if (st->flow_spin <= 0) st->flow_spin = kFlowDefaultSpin;
     }
   }
   st->mode = mode;
@@ -626,7 +629,13 @@ extern "C" int edge0_stack_error(edge0_stack* st) {
 
 extern "C" int edge0_stack_set_spin_limit(edge0_stack* st, int64_t polls) {
   if (!st || polls < 0) return EDGE0_EINVAL;
-  st->flow_spin = polls > 0 ? polls : kFlowDefaultSpin;
+  st->spin = polls > 0 ? polls : kFlowDefaultSpin;
+  // the step graphs hold the old limit in their launch arguments
+  for (auto& g : st->graphs)
+    if (g) {
+      (void)hipGraphExecDestroy(g);
+      g = nullptr;
+    }
   return EDGE0_OK;
 }
 
