@@ -152,6 +152,27 @@ def test_qwen3moe_stack_sampled_layers(torch_cuda):
           f"waived {report.count('waived')}/{len(report)}")
 
 
+# Wide layers run the fused layer kernel on every layer after step 0; its LoRA
+# producers take 2 A rows each for 8 experts at r = 8 (d_model 4096, two
+# 2048-wide halves per thread) and 4 A rows each for 8 experts at r = 16.
+WIDE_SHAPES = {
+    "d4096_k8_r8": G.MoEShape(4096, 16, 256, 8, 64, 8, 16.0, 64),
+    "d2048_k8_r16": G.MoEShape(2048, 32, 384, 8, 64, 16, 32.0, 64),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(WIDE_SHAPES))
+def test_wide_stack_every_layer(torch_cuda, name):
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    S, seed = WIDE_SHAPES[name], 11
+    owners, consumers = range(1, 5), range(2, 6)
+    ds = DeviceStack(S, G.StackGen(S, seed), 6, (1, 4), (2, 5))
+    report, rels = _run(ds, S, seed, 3, lambda t: range(6), owners, consumers)
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[stack] {name}: worst rel-L2 {max(rels):.3e}, waived {report.count('waived')}")
+
+
 @pytest.mark.timeout(900)
 def test_qwen3moe_stack_persistent_sampled_layers(torch_cuda):
     """The persistent mode (one cooperative launch for the 40 layers), the
