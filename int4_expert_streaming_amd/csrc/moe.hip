@@ -337,8 +337,9 @@ constexpr int kFusedMaxExperts = 256;  // slot-table row held in 4 registers per
 constexpr int kFusedMaxProdRows = 8;   // A rows per producer: 2, 4 or 8
 
 // TOPK: a router layer after its router launch (which formed x and the
-// logits): every wave commits the top-K of li.logits itself (no hand-off),
-// workgroup 0 stores ids/w, and x is read instead of formed.
+// logits): wave 0 of every workgroup commits the top-K of li.logits (no
+// hand-off between workgroups), workgroup 0 stores ids/w, and x is read
+// instead of formed.
 constexpr int kFusedThreads = 576;  // 8 compute waves + the hand-off wave
 
 template <int NJ, bool TOPK>
@@ -352,8 +353,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   __shared__ float redp[MU][8];
   __shared__ float h_s[ROWS];
   __shared__ float hrep_s[ROWS];
-  __shared__ int32_t ids_w[TOPK ? 9 : 1][16];
-  __shared__ float w_w[TOPK ? 9 : 1][16];
+  __shared__ int32_t ids_w[16];
+  __shared__ float w_w[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // compute waves 0-7; wave 8 waits for the hand-off.  Wave 8 issues wave
   // 0's loads too (tl, wl): no branch then separates any wave's loads from
@@ -412,9 +413,11 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   // are discarded
   int expert;
   if constexpr (TOPK) {
-    wave_topk<false>(li.logits, a.E, a.K, ids_w[wave], w_w[wave]);
-    __builtin_amdgcn_wave_barrier();  // the wave reads back what its lanes stored
-    expert = ids_w[wave][k];
+    // the routing, committed once per workgroup by wave 0 (nine waves each
+    // ranking the logits would contend for the CU's vector ALUs)
+    if (wave == 0) wave_topk<false>(li.logits, a.E, a.K, ids_w, w_w);
+    __syncthreads();
+    expert = ids_w[k];
   } else {
     expert = a.ids[k];
   }
@@ -453,8 +456,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       }
       __syncthreads();
       if (lead && tid < a.K) {
-        li.ids_out[tid] = ids_w[0][tid];
-        li.w_out[tid] = w_w[0][tid];
+        li.ids_out[tid] = ids_w[tid];
+        li.w_out[tid] = w_w[tid];
       }
     } else {
       float hv[PER];
