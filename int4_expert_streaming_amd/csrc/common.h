@@ -261,30 +261,79 @@ template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ int dpp_i(int old, int v) {
   return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
 }
-// (value descending, index ascending) order: is (ov, oi) before (bv, bi)?
-__device__ __forceinline__ void argmax_take(float& bv, int& bi, float ov, int oi) {
-  if (ov > bv || (ov == bv && oi < bi)) {
-    bv = ov;
-    bi = oi;
-  }
+// Top-K ranking key: (value descending, index ascending) as one unsigned
+// 64-bit order, larger first.  The value's bits are mapped to an order-
+// preserving unsigned word (NaN ranks as -inf, -0 as +0); the low word is
+// ~index, so of equal values the lower index ranks first.  0 is below every
+// key and marks a taken element.
+__device__ __forceinline__ unsigned long long topk_key(float x, int idx) {
+  if (x != x) x = -INFINITY;
+  if (x == 0.f) x = 0.f;
+  uint32_t u = __float_as_uint(x);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (uint32_t)~idx;
+}
+__device__ __forceinline__ float topk_value(unsigned long long key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ void argmax_dpp(float& bv, int& bi) {
-  const float ov = dpp_f<CTRL, ROW_MASK>(bv, bv);
-  const int oi = dpp_i<CTRL, ROW_MASK>(bi, bi);
-  argmax_take(bv, bi, ov, oi);
+__device__ __forceinline__ void keymax_dpp(unsigned long long& k) {
+  const int hi = (int)(k >> 32), lo = (int)(uint32_t)k;
+  const uint32_t ohi = (uint32_t)dpp_i<CTRL, ROW_MASK>(hi, hi);
+  const uint32_t olo = (uint32_t)dpp_i<CTRL, ROW_MASK>(lo, lo);
+  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+  k = o > k ? o : k;
 }
-// wave-wide first element in (value descending, index ascending) order;
-// every lane gets it
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-  argmax_dpp<0xB1>(bv, bi);
-  argmax_dpp<0x4E>(bv, bi);
-  argmax_dpp<0x141>(bv, bi);
-  argmax_dpp<0x140>(bv, bi);
-  argmax_dpp<0x142, 0xa>(bv, bi);
-  argmax_dpp<0x143, 0xc>(bv, bi);
-  bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 63));
-  bi = __builtin_amdgcn_readlane(bi, 63);
+// wave-wide largest key; every lane gets it
+__device__ __forceinline__ unsigned long long wave_keymax(unsigned long long k) {
+  keymax_dpp<0xB1>(k);        // quad_perm [1,0,3,2]
+  keymax_dpp<0x4E>(k);        // quad_perm [2,3,0,1]
+  keymax_dpp<0x141>(k);       // row_half_mirror
+  keymax_dpp<0x140>(k);       // row_mirror
+  keymax_dpp<0x142, 0xa>(k);  // row_bcast:15
+  keymax_dpp<0x143, 0xc>(k);  // row_bcast:31
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), 63);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Top-K of logits[0..E) by one wave, E <= 64 NPER: lane l ranks elements
+// l + 64 j by key; each of the K picks is the wave's largest remaining key.
+// Branch-free apart from the uniform loop over the picks.
+template <int NPER, bool COHERENT>
+__device__ __forceinline__ void wave_topk_n(const float* logits, int E, int K, int32_t* ids_out,
+                                            float* w_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  unsigned long long key[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int idx = lane + kWave * j;
+    float x = -INFINITY;
+    if (idx < E) x = COHERENT ? ld_dev(logits + idx) : logits[idx];
+    key[j] = idx < E ? topk_key(x, idx) : 0ull;  // past E: below every element
+  }
+  unsigned long long mine = 0;  // lane kk keeps the kk-th pick
+  for (int kk = 0; kk < K; ++kk) {
+    unsigned long long best = key[0];
+#pragma unroll
+    for (int j = 1; j < NPER; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_keymax(best);
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) key[j] = key[j] == best ? 0ull : key[j];
+    mine = lane == kk ? best : mine;
+  }
+  const float my_v = topk_value(mine);
+  const int my_i = (int)~(uint32_t)mine;
+  const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+  const float ex = lane < K ? expf(my_v - m) : 0.f;
+  float den = 0.f;
+  for (int j = 0; j < K; ++j)  // fixed order
+    den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+  if (lane < K) {
+    ids_out[lane] = my_i;
+    w_out[lane] = ex / den;
+  }
 }
 
 // Top-K of logits[0..E) by one wave, ranked by (value descending, index
@@ -295,45 +344,12 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
 template <bool COHERENT>
 __device__ __forceinline__ void wave_topk(const float* logits, int E, int K, int32_t* ids_out,
                                           float* w_out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kMaxPer = 16;
-  float v[kMaxPer];
-  const int nper = (E + kWave - 1) / kWave;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    const int idx = lane + kWave * j;
-    float x = -INFINITY;
-    if (j < nper && idx < E) {
-      x = COHERENT ? ld_dev(logits + idx) : logits[idx];
-      if (x != x) x = -INFINITY;
-    }
-    v[j] = x;
-  }
-  uint32_t taken = 0;  // bit j: element lane + 64 j already selected
-  float my_v = -INFINITY;  // lane kk keeps the kk-th selection
-  int my_i = 0;
-  for (int kk = 0; kk < K; ++kk) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int idx = lane + kWave * j;
-      if ((j < nper) && (idx < E) && !((taken >> j) & 1u)) argmax_take(bv, bi, v[j], idx);
-    }
-    wave_argmax(bv, bi);
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    if (lane == kk) {
-      my_v = bv;
-      my_i = bi;
-    }
-  }
-  const float m = __shfl(my_v, 0, kWave);
-  const float ex = lane < K ? expf(my_v - m) : 0.f;
-  float den = 0.f;
-  for (int j = 0; j < K; ++j) den += __shfl(ex, j, kWave);  // fixed order
-  if (lane < K) {
-    ids_out[lane] = my_i;
-    w_out[lane] = ex / den;
+  if (E <= 128) {
+    wave_topk_n<2, COHERENT>(logits, E, K, ids_out, w_out);
+  } else if (E <= 256) {
+    wave_topk_n<4, COHERENT>(logits, E, K, ids_out, w_out);
+  } else {
+    wave_topk_n<16, COHERENT>(logits, E, K, ids_out, w_out);
   }
 }
 
@@ -425,6 +441,7 @@ struct WsLayout {
   size_t logits, head_a, head_res;                // fp32
   size_t t_in;                                    // fp32 [K][2][r]
   size_t t_hand;                                  // fp32 [K][2r] LoRA A x handed between workgroups
+  size_t lg_hand;                                 // fp32 [2][E] router logits handed between workgroups
   size_t hf;                                      // fp32 [K][I]
   size_t hp_hi, hp_lo;                            // u16 [K][I]
   size_t hs;                                      // fp32 [K][I/16]

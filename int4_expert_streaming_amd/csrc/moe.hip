@@ -37,6 +37,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "gemv_dev.h"
 #include "moe_internal.h"
 
@@ -316,37 +318,54 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 }
 
 // ------------------------------------------------------------- k_layer_fused
-// A layer's input and gate/up in one launch for a layer whose routing is
-// known when it starts (wide rows, lora_rank <= 16).  Two kinds of workgroup:
-//  - a.n_prod LoRA producers, the first workgroups of the grid (dispatched
-//    before any workgroup that waits for them): each loads a.prod_rows of
-//    the routed experts' LoRA A rows, forms the layer input x like every
-//    other workgroup and stores t = A x for its rows into t_hand;
+// A layer's input and gate/up in one launch (wide rows, lora_rank <= 16).
+// Two kinds of workgroup:
+//  - a.n_prod producers, the first workgroups of the grid (dispatched before
+//    any workgroup that waits for them).  Each loads a.prod_rows of the
+//    routed experts' LoRA A rows, forms the layer input x like every other
+//    workgroup and stores t = A x for its rows into t_hand;
 //  - K * d_inter / 16 gate/up workgroups (16 rows of one routed expert):
-//    each loads its int4 rows first, forms x redundantly from L2-resident
-//    data (previous layer's fixed-point y, h, RMSNorm) into LDS and computes
-//    the rows' dot products, while a ninth wave waits (bounded) for the
+//    each loads its int4 rows, forms x redundantly from L2-resident data
+//    (previous layer's fixed-point y, h, RMSNorm) into LDS and computes the
+//    rows' dot products, while a ninth wave waits (bounded) for the
 //    expert's t in t_hand; then the LoRA term and the SwiGLU epilogue.
+// ROUTE (a router layer): the producers first compute a.route_rows router
+// logits each from x and publish them through lg_hand (parity a.par; the
+// other parity's entries are emptied); every workgroup then commits the
+// top-K of the published logits itself (wave 0, bounded wait) before it
+// loads its expert's rows, and gate/up workgroup 0 stores the committed
+// ids/w.  Otherwise the routing (a.ids, a.w) is given and the rows are
+// loaded before x is formed.
 // Gate/up workgroup 0 stores h, y_prev, x and clears this layer's
 // accumulator; the first workgroup of each expert publishes its slot for the
-// down kernel.  One launch replaces k_layer_in + k_gate_up, and A x is
-// computed once per expert instead of once per workgroup.
+// down kernel.  One launch replaces the router / layer-input launch and the
+// gate/up GEMV, and A x is computed once per expert instead of once per
+// workgroup.
 constexpr int kFusedMaxRank = 16;
 constexpr int kFusedRowsPerWave = 2;  // 8 waves: 16 rows of gate and up per workgroup
 constexpr int kFusedMaxExperts = 256;  // slot-table row held in 4 registers per lane
 constexpr int kFusedMaxProdRows = 8;   // A rows per producer: 2, 4 or 8
+constexpr int kFusedMaxRouteRows = 4;  // router rows per producer
+constexpr int kFusedThreads = 576;     // 8 compute waves + the hand-off wave
 
-// TOPK: a router layer after its router launch (which formed x and the
-// logits): wave 0 of every workgroup commits the top-K of li.logits (no
-// hand-off between workgroups), workgroup 0 stores ids/w, and x is read
-// instead of formed.
-constexpr int kFusedThreads = 576;  // 8 compute waves + the hand-off wave
+// slot of a (wave-uniform) expert id from the layer's table row held as
+// entries l + 64 j in word j of lane l; -1 when the id or the slot is out of
+// range
+__device__ __forceinline__ int table_slot(int t0, int t1, int t2, int t3, int expert, int E,
+                                          int n_slots) {
+  const int ec = min(max(expert, 0), E - 1);
+  const int hi = ec >> 6;
+  const int v = hi == 0 ? t0 : hi == 1 ? t1 : hi == 2 ? t2 : t3;
+  const int slot = __builtin_amdgcn_readlane(v, ec & 63);
+  return (expert < 0 || expert >= E || slot < 0 || slot >= n_slots) ? -1 : slot;
+}
 
-template <int NJ, bool TOPK>
+template <int NJ, bool ROUTE>
 __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerIn li) {
   constexpr int PER = 4 * NJ;  // hidden elements per thread (d = 2048 NJ, 512 threads)
   constexpr int RW = kFusedRowsPerWave, ROWS = 8 * RW;  // rows per workgroup
   constexpr int MU = kFusedMaxProdRows * NJ / 2;        // producer: A pieces per thread (max)
+  constexpr int MR = (kFusedMaxRouteRows * NJ + 1) / 2;  // producer: router pieces per thread
   __shared__ uint16_t xs[2048 * NJ];
   __shared__ float t_s[2][kFusedMaxRank];
   __shared__ float red[8];
@@ -355,6 +374,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   __shared__ float hrep_s[ROWS];
   __shared__ int32_t ids_w[16];
   __shared__ float w_w[16];
+  __shared__ float lg_s[ROUTE ? kFusedMaxExperts : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // compute waves 0-7; wave 8 waits for the hand-off.  Wave 8 issues wave
   // 0's loads too (tl, wl): no branch then separates any wave's loads from
@@ -365,14 +385,16 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   const int nwg = a.I / ROWS;
   const int P = a.n_prod;
   const bool prod = (int)blockIdx.x < P;
+  const bool comb = (li.flags & IN_COMBINE) != 0;
   // XCD-aware order of the gate/up workgroups: consecutive workgroups go to
   // different XCDs (round-robin over 8; P is a multiple of 8), so logical
   // block L = (id % 8) * (n / 8) + id / 8 gives each XCD a contiguous range
   // of an expert's blocks
   int k, lb = 0;
   if (prod) {
-    k = (int)blockIdx.x * a.prod_rows / (2 * r);
-    if (k >= a.K) return;  // padding producer
+    k = r > 0 ? (int)blockIdx.x * a.prod_rows / (2 * r) : a.K;  // K: no LoRA rows
+    const bool routes = ROUTE && (int)blockIdx.x * a.route_rows < a.E;
+    if (k >= a.K && !routes) return;  // padding producer
   } else {
     const int id = blockIdx.x - P, gsz = gridDim.x - P;
     lb = (gsz % 8 == 0) ? (id % 8) * (gsz / 8) + id / 8 : id;
@@ -392,129 +414,171 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   // Thread tid owns elements j = 4 (tid + 512 c) + e, c < NJ, e < 4.
   uint2 hq[NJ];  // h_prev words (bf16 pairs)
   unsigned long long av[PER];
-  uint2 xq[NJ];
-  if constexpr (TOPK) {
 #pragma unroll
-    for (int c = 0; c < NJ; ++c) xq[c] = *reinterpret_cast<const uint2*>(a.x + 4 * (tl + 512 * c));
-  } else {
-#pragma unroll
-    for (int c = 0; c < NJ; ++c) {
-      const int j0 = 4 * (tl + 512 * c);
-      hq[c] = *reinterpret_cast<const uint2*>(li.h_prev + j0);
-      const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
-      const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
-      av[4 * c + 0] = a0.x;
-      av[4 * c + 1] = a0.y;
-      av[4 * c + 2] = a1.x;
-      av[4 * c + 3] = a1.y;
-    }
+  for (int c = 0; c < NJ; ++c) {
+    const int j0 = 4 * (tl + 512 * c);
+    hq[c] = *reinterpret_cast<const uint2*>(li.h_prev + j0);
+    const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
+    const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
+    av[4 * c + 0] = a0.x;
+    av[4 * c + 1] = a0.y;
+    av[4 * c + 2] = a1.x;
+    av[4 * c + 3] = a1.y;
   }
-  // 2. this expert's bundle; an invalid slot reads slot 0 and its results
-  // are discarded
-  int expert;
-  if constexpr (TOPK) {
-    // the routing, committed once per workgroup by wave 0 (nine waves each
-    // ranking the logits would contend for the CU's vector ALUs)
-    if (wave == 0) wave_topk<false>(li.logits, a.E, a.K, ids_w, w_w);
-    __syncthreads();
-    expert = ids_w[k];
-  } else {
-    expert = a.ids[k];
-  }
-  int slot;
-  {
-    const int ec = min(max(expert, 0), a.E - 1);  // wave-uniform
-    int v = tbl[0];
-#pragma unroll
-    for (int j = 1; j < kFusedMaxExperts / 64; ++j) v = (ec >> 6) == j ? tbl[j] : v;
-    slot = __builtin_amdgcn_readlane(v, ec & 63);
-    if (expert < 0 || expert >= a.E || slot < 0 || slot >= a.n_slots) slot = -1;
-  }
-  const bool ok = slot >= 0;
-  const uint8_t* b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
+  // 2. the routed expert's bundle; an invalid slot reads slot 0 and its
+  // results are discarded
+  // (the table words are passed by value: an array captured by a lambda is
+  // placed in LDS by the compiler)
+  int slot = -1;
+  bool ok = false;
+  const uint8_t* b = a.pool;
+  const int t0 = tbl[0], t1 = tbl[1], t2 = tbl[2], t3 = tbl[3];
+  static_assert(kFusedMaxExperts == 256, "four table words per lane");
+  auto resolve = [&](int expert) {
+    slot = table_slot(t0, t1, t2, t3, expert, a.E, a.n_slots);
+    ok = slot >= 0;
+    b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
+  };
+  if constexpr (!ROUTE) resolve(a.ids[min(k, a.K - 1)]);
 
-  // 3. combine, residual, RMSNorm -> x in LDS (TOPK: x as given); `lead`
-  // stores h, y_prev, x (and the committed routing) and clears the
-  // accumulator
+  // 3. combine, residual, RMSNorm -> x in LDS; `lead` stores h, y_prev, x
+  // and clears the accumulator
   auto form_x = [&](bool lead) {
     // the prologue's loaded values enter through an empty asm, so the
     // compiler cannot hoist their first use (and its wait) above the weight
     // loads issued in between
-    if constexpr (TOPK) {
 #pragma unroll
-      for (int c = 0; c < NJ; ++c) asm volatile("" : "+v"(xq[c].x), "+v"(xq[c].y));
-    } else {
+    for (int c = 0; c < NJ; ++c) asm volatile("" : "+v"(hq[c].x), "+v"(hq[c].y));
 #pragma unroll
-      for (int c = 0; c < NJ; ++c) asm volatile("" : "+v"(hq[c].x), "+v"(hq[c].y));
+    for (int m = 0; m < PER; ++m) asm volatile("" : "+v"(av[m]));
+    float hv[PER];
+    float ss = 0.f;
+    if (cw) {
+      uint32_t hb[PER];
 #pragma unroll
-      for (int m = 0; m < PER; ++m) asm volatile("" : "+v"(av[m]));
+      for (int c = 0; c < NJ; ++c) {
+        hb[4 * c + 0] = hq[c].x & 0xFFFFu;
+        hb[4 * c + 1] = hq[c].x >> 16;
+        hb[4 * c + 2] = hq[c].y & 0xFFFFu;
+        hb[4 * c + 3] = hq[c].y >> 16;
+      }
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const uint32_t yb = comb ? f2bf(from_fix(av[m])) : 0u;
+        hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
+        ss = fmaf(hv[m], hv[m], ss);
+        av[m] = yb;  // keep y_prev's bits for the stores below
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wave] = ss;
     }
-    if constexpr (TOPK) {
-      if (cw) {
+    __syncthreads();
+    float tot = 0.f;
 #pragma unroll
-        for (int c = 0; c < NJ; ++c) *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = xq[c];
+    for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
+    const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
+    uint32_t xw[2 * NJ];
+    if (cw) {
+#pragma unroll
+      for (int c = 0; c < NJ; ++c) {
+        xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
+        xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = make_uint2(xw[2 * c], xw[2 * c + 1]);
       }
-      __syncthreads();
-      if (lead && tid < a.K) {
-        li.ids_out[tid] = ids_w[tid];
-        li.w_out[tid] = w_w[tid];
-      }
-    } else {
-      float hv[PER];
-      float ss = 0.f;
-      if (cw) {
-        uint32_t hb[PER];
+    }
+    __syncthreads();
+    if (lead && cw) {
 #pragma unroll
-        for (int c = 0; c < NJ; ++c) {
-          hb[4 * c + 0] = hq[c].x & 0xFFFFu;
-          hb[4 * c + 1] = hq[c].x >> 16;
-          hb[4 * c + 2] = hq[c].y & 0xFFFFu;
-          hb[4 * c + 3] = hq[c].y >> 16;
-        }
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-          const uint32_t yb = f2bf(from_fix(av[m]));
-          hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
-          ss = fmaf(hv[m], hv[m], ss);
-          av[m] = yb;  // keep y_prev's bits for the stores below
-        }
-        ss = wave_sum(ss);
-        if (lane == 0) red[wave] = ss;
-      }
-      __syncthreads();
-      float tot = 0.f;
-#pragma unroll
-      for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
-      const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
-      uint32_t xw[2 * NJ];
-      if (cw) {
-#pragma unroll
-        for (int c = 0; c < NJ; ++c) {
-          xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
-          xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
-          *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) =
-              make_uint2(xw[2 * c], xw[2 * c + 1]);
-        }
-      }
-      __syncthreads();
-      if (lead && cw) {
-#pragma unroll
-        for (int c = 0; c < NJ; ++c) {
-          const int j0 = 4 * (tid + 512 * c);
-          *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
+      for (int c = 0; c < NJ; ++c) {
+        const int j0 = 4 * (tid + 512 * c);
+        *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
+        if (comb)
           *reinterpret_cast<uint2*>(li.y_prev_out + j0) =
               make_uint2((uint32_t)av[4 * c] | ((uint32_t)av[4 * c + 1] << 16),
                          (uint32_t)av[4 * c + 2] | ((uint32_t)av[4 * c + 3] << 16));
-          *reinterpret_cast<uint2*>(li.h_out + j0) =
-              make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
-                         f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
-        }
-        for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
+        *reinterpret_cast<uint2*>(li.h_out + j0) =
+            make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
+                       f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
       }
+      for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
     }
   };
 
+  // ROUTE: the top-K of the producers' published logits (wave 0 polls them
+  // into LDS, bounded), committed by every workgroup itself
+  auto route = [&]() {
+    if (wave == 0) {
+      const float* src = a.lg_hand + (size_t)a.par * a.E;
+      constexpr int NL = kFusedMaxExperts / 64;
+      uint32_t v[NL];
+      int64_t n = 0;
+      for (;;) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          v[j] = lane + 64 * j < a.E ? __float_as_uint(ld_dev(src + lane + 64 * j)) : 0u;
+        bool miss = false;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) miss |= v[j] == kTHandEmpty;
+        if (!__any(miss)) break;
+        if (++n >= a.spin) {
+          set_error(a.err, EDGE0_EHIP);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        if (lane + 64 * j < a.E) lg_s[lane + 64 * j] = __uint_as_float(v[j]);
+      __builtin_amdgcn_wave_barrier();
+      wave_topk_n<kFusedMaxExperts / 64, false>(lg_s, a.E, a.K, ids_w, w_w);  // E <= 256
+    }
+    __syncthreads();
+  };
+
   if (prod) {
+    if constexpr (ROUTE) {
+      // router rows e0 .. e0 + RR - 1: piece u = tid + 512 m of the
+      // concatenated rows is 8 bf16 (row u / (d / 8)); a wave's 64 pieces
+      // lie in one row
+      const int RR = a.route_rows, e0 = (int)blockIdx.x * RR;
+      const int nr = max(0, min(RR, a.E - e0)), nu = nr * d / 8;
+      uint4 rp[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const int u = min(tl + 512 * m, max(nu - 1, 0));
+        rp[m] = reinterpret_cast<const uint4*>(li.w_router + (size_t)min(e0, a.E - 1) * d)[u];
+      }
+      form_x(false);
+      const uint4* xv = reinterpret_cast<const uint4*>(xs);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const int u = tid + 512 * m;
+        if (512 * m < nu && cw) {  // uniform over each wave
+          const uint4 xq4 = xv[u % (d / 8)];
+          float p = u < nu ? dot2bf(rp[m].x, xq4.x, 0.f) : 0.f;
+          if (u < nu) {
+            p = dot2bf(rp[m].y, xq4.y, p);
+            p = dot2bf(rp[m].z, xq4.z, p);
+            p = dot2bf(rp[m].w, xq4.w, p);
+          }
+          p = wave_sum(p);
+          if (lane == 0) redp[m][wave] = p;
+        }
+      }
+      __syncthreads();
+      if (tid < nr) {
+        float l = 0.f;
+        for (int m = 0; 512 * m < nu; ++m)
+          for (int w8 = 0; w8 < 8; ++w8)
+            if ((512 * m + 64 * w8) / (d / 8) == tid) l += redp[m][w8];
+        if (__float_as_uint(l) == kTHandEmpty) l = __uint_as_float(0x7FC00000u);
+        st_dev(a.lg_hand + (size_t)a.par * a.E + e0 + tid, l);
+        st_dev(a.lg_hand + (size_t)(1 - a.par) * a.E + e0 + tid, __uint_as_float(kTHandEmpty));
+      }
+      if (k >= a.K) return;  // router rows only
+      route();
+      resolve(ids_w[k]);
+    }
     // LoRA producer: rows tr0 .. tr0 + RP - 1 of the expert's 2r A rows
     // (gate rows, then up rows).  Piece u = tid + 512 m of the concatenated
     // rows is 8 bf16: row u / (d / 8), position u % (d / 8); a wave's 64
@@ -531,7 +595,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
                          (size_t)(tr % r) * (d / 8);
       ap[m] = row[u % (d / 8)];
     }
-    form_x(false);
+    if constexpr (!ROUTE) form_x(false);
     const uint4* xv = reinterpret_cast<const uint4*>(xs);
 #pragma unroll
     for (int m = 0; m < MU; ++m) {
@@ -558,10 +622,22 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
     return;
   }
 
-  // gate/up workgroup: every weight load of the compute waves (HBM), then x
+  // gate/up workgroup: every weight load of the compute waves (HBM) and x;
+  // a routed layer loads the rows once its top-K is committed
   GuW<NJ, RW> gw;
-  gu_load<NJ, RW>(a, b, i0, gw, wl);
-  form_x(lb == 0);
+  if constexpr (ROUTE) {
+    form_x(lb == 0);
+    route();
+    resolve(ids_w[k]);
+    if (lb == 0 && tid < a.K) {
+      li.ids_out[tid] = ids_w[tid];
+      li.w_out[tid] = w_w[tid];
+    }
+    gu_load<NJ, RW>(a, b, i0, gw, wl);
+  } else {
+    gu_load<NJ, RW>(a, b, i0, gw, wl);
+    form_x(lb == 0);
+  }
   if (blk == 0 && tid == 0) {
     a.slots[k] = ok ? slot : -1;
     if (!ok) set_error(a.err, EDGE0_ERANGE);
@@ -855,6 +931,9 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->t_hand = reinterpret_cast<float*>(ws + L.t_hand);
   a->n_prod = 0;
   a->prod_rows = 0;
+  a->lg_hand = reinterpret_cast<float*>(ws + L.lg_hand);
+  a->route_rows = 0;
+  a->par = 0;
   a->spin = kFusedDefaultSpin;
   a->hf = reinterpret_cast<float*>(ws + L.hf);
   a->hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
@@ -973,10 +1052,16 @@ int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
   if (!layer_fused_ok(a)) return EDGE0_EINVAL;
   MoeArgs b = a;
   fused_producers(a, &b.n_prod, &b.prod_rows);
+  const bool route = li.flags & IN_ROUTER;
+  if (route) {
+    // router rows: at most 64 producers, kFusedMaxRouteRows rows each
+    b.route_rows = (a.E + 63) / 64;
+    const int pr = ((a.E + b.route_rows - 1) / b.route_rows + 7) / 8 * 8;
+    b.n_prod = std::max(b.n_prod, pr);
+  }
   const int grid = b.n_prod + a.K * (a.I / (8 * kFusedRowsPerWave));
-  const bool topk = li.flags & IN_TOPK;
-  auto kern = a.d == 2048 ? (topk ? k_layer_fused<1, true> : k_layer_fused<1, false>)
-                          : (topk ? k_layer_fused<2, true> : k_layer_fused<2, false>);
+  auto kern = a.d == 2048 ? (route ? k_layer_fused<1, true> : k_layer_fused<1, false>)
+                          : (route ? k_layer_fused<2, true> : k_layer_fused<2, false>);
   if (timing && timing->which == 1) {
     // measured launch: events recorded by the dispatch at its start and end
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), 0, stream, timing->start,

@@ -42,6 +42,11 @@ struct MoeArgs {
   // `spin` polls (error EDGE0_EHIP).
   float* t_hand;
   int n_prod, prod_rows;
+  // a router layer's logits, computed by the producers (route_rows each)
+  // and handed to every workgroup through lg_hand [2][E]: parity `par` is
+  // written, the other parity's entries are emptied for the next router layer
+  float* lg_hand;
+  int route_rows, par;
   int64_t spin;
 };
 constexpr uint32_t kTHandEmpty = 0xFFFFFFFFu;  // a NaN no stored value takes
@@ -58,6 +63,8 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
 //   IN_LORA:    t = A x rows of the K experts' gate/up adapters
 //   IN_GATHER:  routing ids given (a.ids); w = softmax of `logits` taken at
 //               those ids, stored to w_out
+// k_layer_fused takes IN_COMBINE (else h = h_prev) and IN_ROUTER (the router
+// rows and the top-K inside the launch: w_router, ids_out, w_out).
 // Workgroup 0 stores h, y_prev, x, the committed ids/w and the slots.
 enum { IN_COMBINE = 1, IN_NORM = 2, IN_ROUTER = 4, IN_TOPK = 8, IN_LORA = 16, IN_GATHER = 32 };
 struct LayerIn {

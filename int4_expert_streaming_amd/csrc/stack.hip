@@ -139,20 +139,25 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       li.flags |= IN_ROUTER;
       li.w_router = static_cast<const uint16_t*>(st->routers[L]);
       li.logits = st->logits;
+      if (layer_fused_ok(a)) {
+        // router rows, top-K, LoRA-in and gate/up in one launch
+        LayerIn lr = li;
+        lr.flags |= IN_LORA;
+        lr.ids_out = ids;
+        lr.w_out = w;
+        a.par = L & 1;  // parity of the logits hand-off (router layers alternate)
+        if ((rc = launch_layer_fused(a, lr, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
+                EDGE0_OK ||
+            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+          return rc;
+        continue;
+      }
       if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
       LayerIn l2{};
       l2.flags = IN_TOPK | IN_LORA;
       l2.logits = st->logits;
       l2.ids_out = ids;
       l2.w_out = w;
-      if (layer_fused_ok(a)) {
-        // top-K, LoRA-in and gate/up in one launch
-        if ((rc = launch_layer_fused(a, l2, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
-                EDGE0_OK ||
-            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
-          return rc;
-        continue;
-      }
       if ((rc = launch_layer_in(a, l2, stream)) != EDGE0_OK) return rc;
     }
     if ((rc = launch_expert_gemvs(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
@@ -350,6 +355,8 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   ok = ok && hipMemset(st->ws, 0, st->ws_bytes) == hipSuccess &&
        hipMemset(static_cast<uint8_t*>(st->ws) + ws_layout(shape).t_hand, 0xFF,
                  (size_t)4 * K * 2 * shape->lora_rank) == hipSuccess &&
+       hipMemset(static_cast<uint8_t*>(st->ws) + ws_layout(shape).lg_hand, 0xFF,
+                 (size_t)4 * 2 * shape->n_experts) == hipSuccess &&
        hipMemset(st->x, 0, Lc * d * 2) == hipSuccess &&
        hipMemset(st->y, 0, Lc * d * 2) == hipSuccess;
   for (int i = 0; i < 2 && ok; ++i)
