@@ -179,3 +179,35 @@ def test_bad_ids_are_reported_not_dereferenced(torch_cuda):
     # and the next call on the same workspace is clean
     L.E.edge0_moe_layer(L.sh, L.pool.pool, L.table, ids, w, xd, y, L.ws)
     assert L.E.edge0_workspace_error(L.ws) == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3moe_k8"])
+def test_router_exact_ties_rank_by_index(torch_cuda, name):
+    """Experts whose router rows are identical get identical logits; the
+    committed top-K must rank that tie by ascending expert index, as the
+    oracle's (value descending, index ascending) order does.  Four copies of
+    the row that scores highest make the top four a pure tie."""
+    from int4_expert_streaming_amd.weights import to_device
+    L = layer(name)
+    S = L.S
+    x, xd = _x(S, 3)
+    lo = O.router_logits(L.wr, x)
+    top = int(np.argmax(lo))
+    copies = sorted({top, (top + 1) % S.n_experts, (top + 5) % S.n_experts, 3 % S.n_experts})
+    wr = L.wr.copy()
+    for e in copies:
+        wr[e] = L.wr[top]
+    wr_d = to_device(wr)
+    ids, w = L.new_routing()
+    logits = torch_cuda.zeros(S.n_experts, dtype=torch_cuda.float32, device="cuda")
+    L.E.edge0_router(L.sh, wr_d, xd, logits, ids, w, L.ws)
+    lg = logits.cpu().numpy()
+    assert len(set(lg[copies].tolist())) == 1  # the copies' logits are bit-identical
+    lo2 = O.router_logits(wr, x)
+    ids_o, _ = O.softmax_topk(lo2, S.top_k)
+    got = ids.cpu().numpy()
+    assert list(ids_o[:len(copies)]) == copies  # the oracle's order
+    assert list(got[:len(copies)]) == copies, (got, copies)
+    # the rest of the set and the weights as in the other router checks
+    check_routing(got, w.cpu().numpy(), lo2, S.top_k)
+    assert L.E.edge0_workspace_error(L.ws) == 0
