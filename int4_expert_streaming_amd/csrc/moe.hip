@@ -530,7 +530,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       for (int j = 0; j < NL; ++j)
         if (lane + 64 * j < a.E) lg_s[lane + 64 * j] = __uint_as_float(v[j]);
       __builtin_amdgcn_wave_barrier();
-      wave_topk_n<kFusedMaxExperts / 64, false>(lg_s, a.E, a.K, ids_w, w_w);  // E <= 256
+      if (a.E <= 128)
+        wave_topk_n<2, false>(lg_s, a.E, a.K, ids_w, w_w);
+      else
+        wave_topk_n<kFusedMaxExperts / 64, false>(lg_s, a.E, a.K, ids_w, w_w);  // E <= 256
     }
     __syncthreads();
   };
