@@ -391,7 +391,10 @@ __global__ __launch_bounds__(kFlowThreads) void k_flow_step(FlowArgs a) {
       }
       if (!flow_phase_end(a, s, p++, [] {})) return;
       if (!compute) {
-        wave_topk<true>(a.logits, a.E, K, s.ids_s, s.w_s);
+        if (a.E <= 128)  // E <= 256 in this mode
+          wave_topk_n<2, true>(a.logits, a.E, K, s.ids_s, s.w_s);
+        else
+          wave_topk_n<4, true>(a.logits, a.E, K, s.ids_s, s.w_s);
         if (w == 0 && lane < K) {
           a.exec_ids[(size_t)L * K + lane] = s.ids_s[lane];
           a.exec_w[(size_t)L * K + lane] = s.w_s[lane];
