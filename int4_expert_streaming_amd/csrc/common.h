@@ -74,6 +74,30 @@ __device__ __forceinline__ float chunk_dot128(uint4 q, const uint32_t* xp) {
   return acc;
 }
 
+// The nibble-pair mask and exponent word held in registers: a pair is then
+// one v_and_or_b32 (a three-operand instruction, which cannot take two
+// literal constants) instead of an AND and an OR.  Take them once per kernel
+// section and pass them to every chunk_dot128 that shares a weight word, so
+// the unpacked pairs are shared too.
+struct Q4Consts {
+  uint32_t m, c;
+};
+__device__ __forceinline__ Q4Consts q4_consts() {
+  Q4Consts k{0x000F000Fu, 0x43004300u};
+  asm volatile("" : "+v"(k.m), "+v"(k.c));
+  return k;
+}
+__device__ __forceinline__ float chunk_dot128(uint4 q, const uint32_t* xp, Q4Consts k) {
+  float acc = 0.f;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = dot2bf(((w[m] >> (4 * s)) & k.m) | k.c, xp[4 * m + s], acc);
+  }
+  return acc;
+}
+
 // Activation chunk `col` (32 bf16 of x): raw load, then the 16 pairs
 // chunk_dot128 expects and its fp32 sum.
 struct XRaw {

@@ -522,13 +522,14 @@ __global__ __launch_bounds__(kFlowThreads) void k_flow_step(FlowArgs a) {
     __syncthreads();
     if (compute) {
       float part = 0.f;
+      const Q4Consts kq = q4_consts();
 #pragma unroll
       for (int mm = 0; mm < kFlowTPW; ++mm) {
         const int t = wave * kFlowTPW + mm;
         if (t < nt) {
           const float sc = bf2f(pd.sv[mm]), bb = bf2f(pd.bv[mm]);
           const uint32_t* hp = s.hp_s[t];
-          const float acc = chunk_dot128(pd.q[mm], hp) + chunk_dot128(pd.q[mm], hp + 16);
+          const float acc = chunk_dot128(pd.q[mm], hp, kq) + chunk_dot128(pd.q[mm], hp + 16, kq);
           part += pd.wt[mm] * (sc * acc + (bb - 128.f * sc) * s.hsum_s[t]);
         }
       }

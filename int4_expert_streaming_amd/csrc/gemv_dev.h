@@ -147,6 +147,7 @@ __device__ __forceinline__ void gu_base(const GuW<NJ, RR>& w, const uint16_t* xs
   float X[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) X[j] = x_pairs(xr[j], xp[j]);
+  const Q4Consts kq = q4_consts();
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
     float G = 0.f, U = 0.f;
@@ -154,8 +155,8 @@ __device__ __forceinline__ void gu_base(const GuW<NJ, RR>& w, const uint16_t* xs
     for (int j = 0; j < NJ; ++j) {
       const float s1 = bf2f(w.sg[ii][j]), b1 = bf2f(w.bg[ii][j]);
       const float s2 = bf2f(w.su[ii][j]), b2 = bf2f(w.bu[ii][j]);
-      G += s1 * chunk_dot128(w.qg[ii][j], xp[j]) + (b1 - 128.f * s1) * X[j];
-      U += s2 * chunk_dot128(w.qu[ii][j], xp[j]) + (b2 - 128.f * s2) * X[j];
+      G += s1 * chunk_dot128(w.qg[ii][j], xp[j], kq) + (b1 - 128.f * s1) * X[j];
+      U += s2 * chunk_dot128(w.qu[ii][j], xp[j], kq) + (b2 - 128.f * s2) * X[j];
     }
     v[ii] = G;
     v[R + ii] = U;

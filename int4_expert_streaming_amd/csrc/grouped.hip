@@ -317,13 +317,14 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
         tg = a.t_in[((size_t)q * 2 + 0) * r + lane];
         tu = a.t_in[((size_t)q * 2 + 1) * r + lane];
       }
+      const Q4Consts kq = q4_consts();
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         float G = 0.f, U = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          G += sg[ii][j] * chunk_dot128(qg[ii][j], xp[j]) + cg[ii][j] * X[j];
-          U += su[ii][j] * chunk_dot128(qu[ii][j], xp[j]) + cu[ii][j] * X[j];
+          G += sg[ii][j] * chunk_dot128(qg[ii][j], xp[j], kq) + cg[ii][j] * X[j];
+          U += su[ii][j] * chunk_dot128(qu[ii][j], xp[j], kq) + cu[ii][j] * X[j];
         }
         if (has_l) {
           G += a.scale * (Bg[ii] * tg);
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
       td_s[jj][rr] = from_fix(a.tdown[(size_t)(q0 + j0 + jj) * r + rr]);
     }
     __syncthreads();
+    const Q4Consts kq = q4_consts();
 #pragma unroll
     for (int jj = 0; jj < kGrpBT; ++jj) {
       float part = 0.f;
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
           const int c = wave + 4 * m;
           if (c < NC) {
             const uint32_t* hp = hp_s[jj][c];
-            const float accv = chunk_dot128(qv[m], hp) + chunk_dot128(qv[m], hp + 16);
+            const float accv = chunk_dot128(qv[m], hp, kq) + chunk_dot128(qv[m], hp + 16, kq);
             part += sv[m] * accv + cv[m] * hsum_s[jj][c];
           }
         }

@@ -819,13 +819,14 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   }
   __syncthreads();  // every thread, unconditionally
   float part = 0.f;
+  const Q4Consts kq = q4_consts();
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int t = wave * TPW + m;
     if (t < nt) {
       const float s = bf2f(sv[m]), bb = bf2f(bv[m]);
       const uint32_t* hp = hp_s[t];
-      const float acc = chunk_dot128(q[m], hp) + chunk_dot128(q[m], hp + 16);
+      const float acc = chunk_dot128(q[m], hp, kq) + chunk_dot128(q[m], hp + 16, kq);
       float dl = 0.f;  // B_down[o] . (A_down h)_c
       for (int j = 0; 8 * j < r; ++j) {
         uint4 bw4;
