@@ -427,8 +427,12 @@ __device__ __forceinline__ unsigned long long to_fix(float v) {
   const float c = fminf(fmaxf(v * kFixScale, -9.2e18f), 9.2e18f);
   return (unsigned long long)__float2ll_rn(c);
 }
+// the value as fp32: hi * 2^32 + lo (two's complement words) is exact in fp64
+// while |v| < 2^53 (|value| < 2^21), so the result is rounded once, as a
+// direct 64-bit conversion would be; the scaling is a power of two
 __device__ __forceinline__ float from_fix(unsigned long long v) {
-  return (float)(long long)v * (1.0f / kFixScale);
+  const double dv = fma((double)(int)(uint32_t)(v >> 32), 4294967296.0, (double)(uint32_t)v);
+  return (float)(dv * (1.0 / kFixScale));
 }
 
 // x = bf16(h / sqrt(mean(h^2) + eps)) into LDS by one workgroup (fixed
