@@ -351,7 +351,7 @@ def bench_grouped(args, log):
         us = timed(0)
         if args.mfma_sweep:
             sweep = {"gemv_only": round(timed(E.EDGE0_GROUPED_NO_MFMA), 2)}
-            for mn in (1, 2, 4, 8):
+            for mn in (2, 4, 8, 24):
                 sweep[f"mfma_from_{mn}"] = round(timed(E.grouped_mfma_min(mn)), 2)
             log(f"[grouped] T={T} us/call by MFMA threshold: default {us:.2f}, {sweep}")
         nbytes = union * bb

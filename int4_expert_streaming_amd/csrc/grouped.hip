@@ -215,18 +215,28 @@ __device__ __forceinline__ void grp_rows_epilogue(const GrpArgs& a, int q, int b
 constexpr int kGrpXBytes = 32768;
 
 // NJ = ceil(d/32 / 64) chunks per lane; lane l owns chunks l + 64 j (< d/32)
-// of 4 row pairs of its wave.
+// of 4 row pairs of its wave.  Workgroup (slice, expert, 16-row block) takes
+// the expert's tokens [ts * slice, ts * slice + ts): an expert chosen by many
+// tokens is spread over several workgroups (each reads its rows again) and
+// no longer sets the time alone.
 template <int NJ>
-__global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int max_cnt) {
+__global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int max_cnt,
+                                                     int ts) {
   __shared__ uint16_t xs[kGrpXBytes / 2];
   __shared__ float h_s[16];
   __shared__ float hrep_s[16];
   const int nblk = a.I / 16;
-  const int act = blockIdx.x / nblk;
+  const int sl = blockIdx.x / (a.Amax * nblk);
+  const int act = (blockIdx.x / nblk) % a.Amax;
   const int blk = blockIdx.x % nblk;
   if (act >= a.info[0]) return;
   const int n = a.act_cnt[act];
   if (n < min_cnt || n > max_cnt) return;
+  // the last slice also takes any tokens beyond the slices (only an id that
+  // repeats within one token's routing can give an expert more than T pairs)
+  const bool last = sl == (int)gridDim.x / (a.Amax * nblk) - 1;
+  const int t_lo = sl * ts, t_hi = last ? n : min(n, t_lo + ts);
+  if (t_lo >= n) return;
   const uint8_t* b = grp_bundle(a, act);
   if (b == nullptr) return;
   const int q0 = a.act_off[act];
@@ -282,8 +292,8 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
     ad1 = src[1];
   }
   const int bt = kGrpXBytes / (2 * d) < 1 ? 1 : kGrpXBytes / (2 * d);  // tokens per batch
-  for (int j0 = 0; j0 < n; j0 += bt) {
-    const int nb = n - j0 < bt ? n - j0 : bt;
+  for (int j0 = t_lo; j0 < t_hi; j0 += bt) {
+    const int nb = t_hi - j0 < bt ? t_hi - j0 : bt;
     __syncthreads();  // previous batch fully consumed
     // stage the batch's activations: 16 bytes per thread per step
     const int n16 = nb * d / 8;
@@ -349,21 +359,27 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
 // CPW = 32-input chunks per wave: wave w owns chunks w, w + 4, ... of the
 // tiled down weights of 64 output rows (lane = row).  Tokens in batches of
 // kGrpBT; wave 0 adds the LoRA-down delta and scatters the weighted rows.
+// Workgroup (slice, expert, row block) takes the expert's tokens
+// [ts * slice, ts * slice + ts), as in k_grp_gate_up.
 constexpr int kGrpBT = 8;
 constexpr int kGrpMaxNC = 32;  // d_inter <= 1024
 
 template <int CPW>
-__global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int max_cnt) {
+__global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int max_cnt, int ts) {
   __shared__ uint32_t hp_s[kGrpBT][kGrpMaxNC][32];  // hi pairs then lo pairs of each chunk
   __shared__ float hsum_s[kGrpBT][kGrpMaxNC];
   __shared__ float red[4][kGrpBT][64];
   __shared__ float td_s[kGrpBT][64];
   const int nrb = a.d / 64;
-  const int act = blockIdx.x / nrb;
+  const int sl = blockIdx.x / (a.Amax * nrb);
+  const int act = (blockIdx.x / nrb) % a.Amax;
   const int rb = blockIdx.x % nrb;
   if (act >= a.info[0]) return;
   const int n = a.act_cnt[act];
   if (n < min_cnt || n > max_cnt) return;
+  const bool last = sl == (int)gridDim.x / (a.Amax * nrb) - 1;
+  const int t_lo = sl * ts, t_hi = last ? n : min(n, t_lo + ts);
+  if (t_lo >= n) return;
   const uint8_t* b = grp_bundle(a, act);
   if (b == nullptr) return;
   const int q0 = a.act_off[act];
@@ -392,8 +408,8 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
 #pragma unroll
     for (int m = 0; m < 32; ++m) bd[m] = 2 * m < r ? src[m] : 0u;
   }
-  for (int j0 = 0; j0 < n; j0 += kGrpBT) {
-    const int nb = n - j0 < kGrpBT ? n - j0 : kGrpBT;
+  for (int j0 = t_lo; j0 < t_hi; j0 += kGrpBT) {
+    const int nb = t_hi - j0 < kGrpBT ? t_hi - j0 : kGrpBT;
     __syncthreads();  // previous batch consumed
     for (int t = threadIdx.x; t < nb * NC * 32; t += 256) {
       const int jj = t / (NC * 32), rem = t % (NC * 32);
@@ -498,7 +514,6 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[SPG]
   }
 }
 
-constexpr int kMfmaMinTokens = 16;
 constexpr int kFusedRank = 16;  // LoRA rank bound of the pipelined MFMA kernels
 constexpr int kGW = 8;  // groups per wave per pass (their weights held in registers)
 
@@ -1128,11 +1143,17 @@ static bool grouped_shape_ok(const edge0_moe_shape* s) {
          (g == 32 || g == 64 || g == 128);
 }
 
+// tokens per GEMV workgroup; ceil(T / kGrpSliceTokens) slices per expert
+constexpr int kGrpSliceTokens = 8;
+static int grp_slices(const GrpArgs& a) {
+  return (a.T + kGrpSliceTokens - 1) / kGrpSliceTokens;
+}
+
 static int launch_grp_gate_up(const GrpArgs& a, int lo, int hi, hipStream_t st) {
-  const int grid = a.Amax * (a.I / 16);
+  const int grid = grp_slices(a) * a.Amax * (a.I / 16), ts = kGrpSliceTokens;
   switch ((a.d / 32 + 63) / 64) {
-    case 1: k_grp_gate_up<1><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 2: k_grp_gate_up<2><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 1: k_grp_gate_up<1><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 2: k_grp_gate_up<2><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
     default: return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();
@@ -1140,16 +1161,16 @@ static int launch_grp_gate_up(const GrpArgs& a, int lo, int hi, hipStream_t st) 
 }
 
 static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
-  const int grid = a.Amax * (a.d / 64);
+  const int grid = grp_slices(a) * a.Amax * (a.d / 64), ts = kGrpSliceTokens;
   switch ((a.I / 32 + 3) / 4) {
-    case 1: k_grp_down<1><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 2: k_grp_down<2><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 3: k_grp_down<3><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 4: k_grp_down<4><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 5: k_grp_down<5><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 6: k_grp_down<6><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 7: k_grp_down<7><<<grid, 256, 0, st>>>(a, lo, hi); break;
-    case 8: k_grp_down<8><<<grid, 256, 0, st>>>(a, lo, hi); break;
+    case 1: k_grp_down<1><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 2: k_grp_down<2><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 3: k_grp_down<3><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 4: k_grp_down<4><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 5: k_grp_down<5><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 6: k_grp_down<6><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 7: k_grp_down<7><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 8: k_grp_down<8><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
     default: return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();
@@ -1256,10 +1277,10 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
     k_grp_lora_in<<<(a.P * 2 * a.r + 3) / 4, 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
   }
-  // experts with >= min_mfma tokens on MFMA, the others as GEMVs
-  const int fm = (flags >> 8) & 0xFF;
-  const int min_mfma = fm ? fm : kMfmaMinTokens;
-  const bool mfma = !(flags & EDGE0_GROUPED_NO_MFMA) && n_tokens >= min_mfma;
+  // GEMVs for every expert unless the caller asks for MFMA from min_mfma
+  // tokens per expert on
+  const int min_mfma = (flags >> 8) & 0xFF;
+  const bool mfma = !(flags & EDGE0_GROUPED_NO_MFMA) && min_mfma > 0 && n_tokens >= min_mfma;
   const int gemv_max = mfma ? min_mfma - 1 : 1 << 30;
   int rc = gemv_max >= 1 ? launch_grp_gate_up(a, 1, gemv_max, stream) : EDGE0_OK;
   if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 0, min_mfma, stream);

@@ -226,7 +226,7 @@ EDGE0_STACK_PERSISTENT = 1
 
 
 def grouped_mfma_min(n: int) -> int:
-    """Flag moving the grouped layer's MFMA threshold to n tokens per expert."""
+    """Flag putting the grouped layer's experts with >= n tokens on MFMA."""
     return (n & 0xFF) << 8
 
 

@@ -3,9 +3,10 @@ the oracle, which defines it token by token: y_j = sum_k w_jk FFN_{e_jk}(x_j).
 Every token's output is compared (rel-L2 <= 2e-3), for the tiny shape
 (many tokens per expert, several token batches, a ragged last batch) and the
 Qwen3-MoE shape at K = 8 with 1, 4, 8, 16 and 32 tokens and Zipf(1.1)
-routing; both kernel paths (multi-token GEMV and MFMA for experts with >= 16
-tokens) and the GEMV-only path; determinism; reuse of the workspace by a
-smaller call; the empty call; invalid ids reported."""
+routing; the default GEMV path (tokens in slices of 8 per workgroup), the
+mixed path (MFMA for experts with >= 16 tokens) and MFMA for every expert;
+determinism; reuse of the workspace by a smaller call; the empty call;
+invalid ids reported."""
 import numpy as np
 import pytest
 
@@ -25,8 +26,9 @@ def torch_cuda():
 
 
 _LAYERS = {}
-# default (MFMA at >= 16 tokens per expert), GEMV only, MFMA for every expert
-FLAG_SETS = (0, 1, 1 << 8)
+# default (GEMV only), MFMA from 16 tokens per expert, MFMA for every expert
+MFMA16 = 16 << 8
+FLAG_SETS = (0, MFMA16, 1 << 8)
 
 
 def _layer(S):
@@ -97,7 +99,7 @@ def _paths_ran(ys, ids, counts):
     calls; a token that uses an MFMA expert shows the MFMA path's rounding
     (at least one must differ when any expert has >= 16 tokens)."""
     big = set(np.nonzero(counts >= 16)[0].tolist())
-    differs = [not np.array_equal(ys[0][j], ys[1][j]) for j in range(ids.shape[0])]
+    differs = [not np.array_equal(ys[0][j], ys[MFMA16][j]) for j in range(ids.shape[0])]
     for j in range(ids.shape[0]):
         if not big.intersection(ids[j].tolist()):
             assert not differs[j], j
@@ -147,3 +149,20 @@ def test_grouped_empty_and_bad_ids(torch_cuda):
     y_ok, ws = _call(lay, ids_ok, w_ok, x, ws=ws)
     assert E.edge0_workspace_error(ws) == E.EDGE0_OK
     assert np.array_equal(y, y_ok)
+
+
+def test_grouped_repeated_ids(torch_cuda):
+    """An id repeated within a token's routing adds that expert's output once
+    per repeat; here expert 2 gets 3 pairs from each of 9 tokens (27 pairs,
+    more than the 9 tokens that size the GEMV token slices)."""
+    S = G.TINY
+    lay = _layer(S)
+    T = 9
+    ids = np.tile(np.array([2, 5, 2, 2], np.int32)[:S.top_k], (T, 1))
+    rng = np.random.default_rng(4)
+    w = rng.uniform(0.05, 0.5, size=(T, S.top_k)).astype(np.float32)
+    x = G.hidden(S, 33, n=T)
+    for flags in FLAG_SETS:
+        y, _ = _call(lay, ids, w, x, flags)
+        worst = _check(lay, ids, w, x, y)
+        print(f"[grouped] tiny repeated ids flags={flags:#x}: worst rel-L2 {worst:.3e}")
