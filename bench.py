@@ -331,7 +331,6 @@ def bench_grouped(args, log):
         y = torch.empty((T, d), dtype=torch.int16, device="cuda")
         counts = [np.bincount(rt[0].ravel(), minlength=En) for rt in routes]
         union = float(np.mean([np.count_nonzero(c) for c in counts]))
-        on_mfma = float(np.mean([int((c >= 16).sum()) for c in counts])) if T >= 16 else 0.0
 
         def timed(flags, n_calls=256):
             for i in range(32):
@@ -357,7 +356,8 @@ def bench_grouped(args, log):
         nbytes = union * bb
         flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
         results[T] = {"us_per_call": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
-                      "experts": round(union, 2), "experts_on_mfma": round(on_mfma, 2),
+                      "experts": round(union, 2),
+                      "path": "mfma tiles" if T >= 4 else "gemv",
                       "union_bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                       "tflops": round(flops / (us * 1e-6) / 1e12, 3)}

@@ -213,12 +213,12 @@ int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
  * w[j][.],  y[j] = bf16( sum_k w[j][k] D_{ids[j][k]}(x[j]) )  ([Edge0] §3.1
  * "Math contract", §3.3); the grouping only reorders the work.  The (token,
  * k) pairs are bucketed by expert on the device (counting sort, stable by
- * token); each expert runs as multi-token GEMVs whose workgroups take a
- * block of rows and at most 8 of the expert's tokens, so an expert chosen by
- * many tokens is spread over several workgroups.  On request, experts chosen
- * by >= n tokens run their products on MFMA instead (bf16 operands holding
- * the exact 128 + q nibble values and the activations, fp32 accumulation,
- * the group affine applied per group in fp32).
+ * token; an id repeated within a token's routing is kept once with the
+ * repeats' weights added).  From 4 tokens per call on, every expert's
+ * products run on MFMA in tiles of up to 16 of its tokens (bf16 operands
+ * holding the exact 128 + q nibble values and the activations, fp32
+ * accumulation, the group affine applied per group in fp32); smaller calls
+ * run multi-token GEMVs (at most 8 of an expert's tokens per workgroup).
  *   n_tokens   : 0..64 (0: nothing is enqueued)
  *   slot_table : device int32 [E], id -> slot
  *   ids, w     : device int32 / fp32 [n_tokens][K]
@@ -226,9 +226,12 @@ int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
  *   workspace  : edge0_grouped_workspace_bytes(shape) bytes, zero-filled once
  *                before first use (calls leave it ready for the next call);
  *                calls that may run concurrently need distinct workspaces
- *   flags      : 0 (every expert as GEMVs), or EDGE0_GROUPED_MFMA_MIN(n)
- *                (1 <= n <= 255): experts chosen by >= n tokens on MFMA;
- *                EDGE0_GROUPED_NO_MFMA overrides EDGE0_GROUPED_MFMA_MIN
+ *   flags      : 0 (as above); EDGE0_GROUPED_NO_MFMA: every expert as
+ *                GEMVs; EDGE0_GROUPED_MFMA_MIN(n) (1 <= n <= 255): experts
+ *                chosen by >= n tokens on MFMA, the others as GEMVs.  Shapes
+ *                outside the MFMA tiles' (d_model <= 2048 and a multiple of
+ *                8 g, g of 32 or 64, d_inter a multiple of 128, even
+ *                lora_rank <= 16) always run as GEMVs.
  * Supported shapes: those of edge0_moe_layer with d_inter <= 1024 and
  * d_model <= 4096 (edge0_grouped_workspace_bytes returns 0 otherwise). */
 enum { EDGE0_GROUPED_NO_MFMA = 1 };

@@ -12,22 +12,24 @@
 //                   the active experts with their first pair and count, and
 //                   resolves each active expert's slot once.
 //   k_grp_lora_in : t = A x for every pair's gate and up adapters.
-//   k_grp_gate_up : one workgroup = 16 rows of one active expert's gate and
-//                   up; the rows stay in registers while the expert's tokens
-//                   stream through LDS in batches; SwiGLU; h stored as bf16
-//                   hi/lo pairs, per-16-row sums, and A_down h accumulated in
-//                   fixed point per pair.
-//   k_grp_gate_up_mfma : the same for experts with >= 16 tokens, on MFMA.
-//   k_grp_down    : one workgroup = 64 output rows of one active expert; the
-//                   tiled down weights stay in registers while the tokens' h
-//                   batches stream through LDS; the LoRA-down delta; each
-//                   token's weighted row added to its fixed-point output.
-//   k_grp_down_mfma : the same for experts with >= 16 tokens, on MFMA.
+//   k_grp_gu_tile : one workgroup = 16 rows of one active expert's gate and
+//                   up for a tile of up to 16 of its tokens, on MFMA
+//                   (16x16x32 bf16 against the exact 128 + q nibble values);
+//                   SwiGLU; h stored as bf16 hi/lo pairs, per-16-row sums,
+//                   and A_down h accumulated in fixed point per pair.
+//   k_grp_gate_up : the same as multi-token GEMVs (rows in registers, at most
+//                   8 tokens per workgroup), for calls of few tokens.
+//   k_grp_down_tile / k_grp_down : one workgroup = 64 output rows of one
+//                   active expert (tile on MFMA, or GEMV); the LoRA-down
+//                   delta; each token's weighted row added to its
+//                   fixed-point output.
 //   k_grp_out     : y = bf16 of each token's accumulator; clears the
 //                   accumulators for the next call.
 // Int4 arithmetic is the single-token path's: exact bf16 "128 + q" nibble
 // pairs against pair-permuted activations, the group affine folded per
 // 32-input chunk, fp32 everywhere, one bf16 rounding of y.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace e0 {
@@ -81,15 +83,19 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // One workgroup of 1024 threads, one expert per thread (E <= 1024): counts
 // by LDS atomics, exclusive scans of the counts and of the "active" flags,
 // then each pair's destination = its expert's first sorted position + the
-// number of earlier pairs of the same expert (stable).
+// number of earlier pairs of the same expert (stable).  An id repeated
+// within one token's routing is kept once, at its first k, with the
+// repeats' weights added to it in k order (w1 D(x) + w2 D(x) = (w1 + w2)
+// D(x)), so an expert holds at most one pair per token.
 __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
   __shared__ int cnt[1024];
   __shared__ int first[1024];
   __shared__ int actidx[1024];
   __shared__ int ids_s[kGrpMaxTokens * 16];
+  __shared__ float w_s[kGrpMaxTokens * 16];
   __shared__ int wtot[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, P = a.P;
+  const int E = a.E, P = a.P, K = a.K;
   cnt[tid] = 0;
   for (int p = tid; p < P; p += 1024) {
     int e = a.ids[p];
@@ -99,6 +105,20 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
     }
     ids_s[p] = e;
   }
+  __syncthreads();
+  bool dup = false;  // P <= 1024: one pair per thread
+  if (tid < P) {
+    const int e = ids_s[tid], k0 = tid - tid % K;
+    float w = a.w[tid];
+    if (e >= 0) {
+      for (int q = k0; q < tid; ++q) dup |= ids_s[q] == e;
+      for (int q = tid + 1; q < k0 + K; ++q)
+        if (ids_s[q] == e) w += a.w[q];
+    }
+    w_s[tid] = w;
+  }
+  __syncthreads();
+  if (dup) ids_s[tid] = -1;
   __syncthreads();
   for (int p = tid; p < P; p += 1024)
     if (ids_s[p] >= 0) atomicAdd(&cnt[ids_s[p]], 1);
@@ -147,7 +167,7 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
     const int dst = first[e] + rank;
     a.pair_tok[dst] = p / a.K;
     a.pair_act[dst] = actidx[e];
-    a.pair_w[dst] = a.w[p];
+    a.pair_w[dst] = w_s[p];
   }
 }
 
@@ -232,10 +252,7 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
   if (act >= a.info[0]) return;
   const int n = a.act_cnt[act];
   if (n < min_cnt || n > max_cnt) return;
-  // the last slice also takes any tokens beyond the slices (only an id that
-  // repeats within one token's routing can give an expert more than T pairs)
-  const bool last = sl == (int)gridDim.x / (a.Amax * nblk) - 1;
-  const int t_lo = sl * ts, t_hi = last ? n : min(n, t_lo + ts);
+  const int t_lo = sl * ts, t_hi = min(n, t_lo + ts);  // n <= T: the slices cover it
   if (t_lo >= n) return;
   const uint8_t* b = grp_bundle(a, act);
   if (b == nullptr) return;
@@ -377,8 +394,7 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
   if (act >= a.info[0]) return;
   const int n = a.act_cnt[act];
   if (n < min_cnt || n > max_cnt) return;
-  const bool last = sl == (int)gridDim.x / (a.Amax * nrb) - 1;
-  const int t_lo = sl * ts, t_hi = last ? n : min(n, t_lo + ts);
+  const int t_lo = sl * ts, t_hi = min(n, t_lo + ts);
   if (t_lo >= n) return;
   const uint8_t* b = grp_bundle(a, act);
   if (b == nullptr) return;
@@ -464,632 +480,388 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
   }
 }
 
-// ------------------------------------------------------------ MFMA paths
-// v_mfma_f32_32x32x16_bf16 (lane l: A[l%32][8(l/32)+i], B[8(l/32)+i][l%32],
-// accumulator 4J+i = C[8J + 4(l/32) + i][l%32]).  A = activations (rows =
-// tokens of the expert, padded to 32), B = weights (columns = 32 weight
-// rows), so a lane's 16 accumulators share one weight row and one scale and
-// bias per group.  Per group the products start from zero and are folded in
-// fp32: s * acc + (b - 128 s) * (sum of the group's activations).  Within a
-// group lane half j takes SPG = g/16 consecutive packed words (8 inputs
-// each); step t of the group feeds word j*SPG + t, as exact bf16 128 + q in
-// the pair order (e0,e4,e1,e5,e2,e6,e3,e7), against activations in the same
-// order (pair_perm8, or the pair-permuted h pairs).  The 4 waves split the
-// groups; partial tiles meet in LDS.
+// ------------------------------------------------ MFMA token tiles
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-
-__device__ __forceinline__ bf16x8_t q4_operand(uint32_t word) {
-  const uint4 v = make_uint4(q4pair(word, 0), q4pair(word, 1), q4pair(word, 2), q4pair(word, 3));
-  return __builtin_bit_cast(bf16x8_t, v);
-}
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+// activations as the MFMA operand: 8 consecutive bf16 in the pair order
+// (e0,e4,e1,e5,e2,e6,e3,e7) of the packed int4 words
 __device__ __forceinline__ bf16x8_t x_operand(uint4 raw) {
   uint32_t o[4];
   pair_perm8(raw.x, raw.y, raw.z, raw.w, o);
   return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
-__device__ __forceinline__ float raw_sum8(uint4 v) {
-  return bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) +
-         bf_lo(v.w) + bf_hi(v.w);
+// Every active expert on v_mfma_f32_16x16x32_bf16, whatever its token
+// count: A = up to 16 of the expert's tokens x 32 inputs, B = 32 inputs x 16
+// weight rows.  Lane l = (n = l % 16, j = l / 16) supplies token n's and
+// weight row n's inputs k0 .. k0 + 7 (the same inputs for both operands, so
+// the product does not depend on how the unit orders k inside the lanes);
+// accumulator v of lane l is C[token 4 j + v][row n].  Within a group of g
+// inputs quad j takes the g/4 inputs from j g/4 on, one packed word (8
+// inputs) per step, WPG = g/32 steps; per group the products start from
+// zero and are folded in fp32 as s * acc + (b - 128 s) * (the group's
+// activation sum).  The int4 operand is expanded once per tile of up to 16
+// tokens, so an expert's cost barely grows with its token count.  Rows
+// staged in LDS are swizzled (16-byte chunk c of token m at c ^ (m & 15)),
+// so the 16 lanes of a quad read 16 different banks.  A workgroup's first
+// loads (its expert's count, slot and first pair) go out together.
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ bf16x8_t q4_operand_k(uint32_t w, Q4Consts k) {
+  const uint4 v = make_uint4((w & k.m) | k.c, ((w >> 4) & k.m) | k.c, ((w >> 8) & k.m) | k.c,
+                             ((w >> 12) & k.m) | k.c);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
-// SPG consecutive packed words starting at p (4-byte aligned; 16-byte
-// aligned when SPG >= 4)
-template <int SPG>
-__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[SPG]) {
-  if constexpr (SPG % 4 == 0) {
+constexpr int kTileTok = 16;   // tokens per MFMA tile at most
+constexpr int kTileRank = 16;  // LoRA rank bound of the tile kernels
+constexpr int kTileMinCall = 4;  // default: tiles for calls of >= 4 tokens
+
+// N consecutive 32-bit words from p (p aligned to min(N, 4) words)
+template <int N>
+__device__ __forceinline__ void load_u32s(const uint32_t* p, uint32_t* w) {
+  if constexpr (N >= 4) {
 #pragma unroll
-    for (int m = 0; m < SPG / 4; ++m) {
-      const uint4 v = reinterpret_cast<const uint4*>(p)[m];
-      w[4 * m] = v.x;
-      w[4 * m + 1] = v.y;
-      w[4 * m + 2] = v.z;
-      w[4 * m + 3] = v.w;
+    for (int u = 0; u < N / 4; ++u) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[u];
+      w[4 * u] = v.x;
+      w[4 * u + 1] = v.y;
+      w[4 * u + 2] = v.z;
+      w[4 * u + 3] = v.w;
     }
+  } else if constexpr (N == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
   } else {
-#pragma unroll
-    for (int m = 0; m < SPG; ++m) w[m] = p[m];
+    w[0] = p[0];
   }
 }
+__device__ __forceinline__ float bf_at(const uint32_t* w, int i) {
+  return (i & 1) ? bf_hi(w[i >> 1]) : bf_lo(w[i >> 1]);
+}
+// element offset of input k of staged row m (rows of len bf16, len % 128 == 0)
+__device__ __forceinline__ int swz(int m, int len, int k) {
+  return m * len + ((((k >> 3) ^ (m & 15))) << 3) + (k & 7);
+}
 
-constexpr int kFusedRank = 16;  // LoRA rank bound of the pipelined MFMA kernels
-constexpr int kGW = 8;  // groups per wave per pass (their weights held in registers)
+// The tile's pair tokens through the scalar cache: pair_tok is not written
+// while the tile kernels run, so it may be read as constant memory, and a
+// wait for these loads does not wait for the vector loads in flight.
+__device__ __forceinline__ int tile_pair_tok(const GrpArgs& a, int q) {
+  const __attribute__((address_space(4))) int32_t* p =
+      (const __attribute__((address_space(4))) int32_t*)a.pair_tok;
+  return p[q];
+}
 
-// One workgroup = 32 rows of one active expert's gate and up, all its tokens
-// in tiles of 32.
-template <int SPG>
-__global__ __launch_bounds__(256) void k_grp_gate_up_mfma(GrpArgs a, int min_cnt) {
-  __shared__ float red[4][2][32][33];  // per wave: [G or U][weight row][token]
-  __shared__ float hbuf[32][33];       // h [token][row]
-  __shared__ float hrep_s[32][33];     // the value the down product sees (hi + lo)
-  __shared__ float tl_s[32][2][64];    // LoRA t of the tile's tokens
-  __shared__ float bl_s[2][32][64];    // B_gate / B_up rows of the block
-  __shared__ float ad_s[64][32];       // A_down columns of the block
-  const int nb32 = a.I / 32;
-  const int act = blockIdx.x / nb32;
-  const int rb = blockIdx.x % nb32;
-  if (act >= a.info[0]) return;
-  const int n = a.act_cnt[act];
-  if (n < min_cnt) return;
-  const uint8_t* b = grp_bundle(a, act);
-  if (b == nullptr) return;
-  const int q0 = a.act_off[act];
+// Gate/up: workgroup (tile, active expert, 16-row block).  The 4 waves split
+// the d inputs into quarters of GW groups (NW = GW * WPG words per lane per
+// matrix, loaded once); each lane reads its token's activations straight
+// from memory (the quarters do not overlap, so staging them would save
+// nothing), and a third MFMA per step against a ones operand gives each
+// group's activation sum for the fold.  The partial 16 x 16 gate and up
+// tiles meet in LDS; then one thread per (token, row): LoRA B t, SwiGLU, h
+// as bf16 hi/lo pairs, 16-row sums of h, and A_down h added in fixed point
+// per (pair, rank).  An expert holds at most T pairs (one per token), so
+// the grid's ceil(T / tm) tiles cover it and a workgroup has one tile:
+// straight-line code, nothing loop-carried.
+struct GuTileLds {
+  float red[4][2][kTileTok][kTileTok + 1];
+  float bl[2][kTileTok][kTileRank];
+  float tl[kTileTok][2][kTileRank];
+  float h[kTileTok][kTileTok + 1];
+};
+
+template <int GW, int WPG>
+__device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int q0, int t0, int mt,
+                                        int blk, const uint32_t (&wg)[GW * WPG],
+                                        const uint32_t (&wu)[GW * WPG], Q4Consts kq,
+                                        GuTileLds& sm) {
+  constexpr int NW = GW * WPG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nn = lane & 31, jh = lane >> 5;
+  const int n = lane & 15, j = lane >> 4;
   const int d = a.d, g = a.g, ng = d / g, r = a.r, I = a.I;
-  const int row0 = rb * 32, row = row0 + nn;
-  if (r > 0) {
-    const uint16_t* Bg = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
-    const uint16_t* Bu = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
-    for (int t = tid; t < 32 * r; t += 256) {
-      const int rr = t % r, rw = t / r;
-      bl_s[0][rw][rr] = bf2f(Bg[(size_t)(row0 + rw) * r + rr]);
-      bl_s[1][rw][rr] = bf2f(Bu[(size_t)(row0 + rw) * r + rr]);
+  const int i0 = blk * 16, row = i0 + n;
+  const bool lora = r > 0;
+  // this lane's A row: token n of the tile (rows past the tile repeat its
+  // last token; their results are dropped)
+  int tok = tile_pair_tok(a, q0 + t0);
+#pragma unroll
+  for (int i = 1; i < kTileTok; ++i) {
+    const int ti = tile_pair_tok(a, q0 + t0 + min(i, mt - 1));
+    tok = n == i ? ti : tok;
+  }
+  const uint4* xp =
+      reinterpret_cast<const uint4*>(a.x + (size_t)tok * d + wave * (d / 4) + j * (g / 4));
+  uint4 xa[NW];
+#pragma unroll
+  for (int gl = 0; gl < GW; ++gl)
+#pragma unroll
+    for (int s = 0; s < WPG; ++s) xa[gl * WPG + s] = xp[(gl * g + 8 * s) / 8];
+  // scales and biases of this lane's row and groups; A_down[rr][i0 .. i0+15]
+  // for thread (token, rr = tid % 16), rank clamped
+  uint32_t sgw[GW / 2], gbw[GW / 2], suw[GW / 2], ubw[GW / 2];
+  {
+    const size_t so = ((size_t)row * ng + wave * GW) / 2;  // in words
+    load_u32s<GW / 2>(reinterpret_cast<const uint32_t*>(b + a.lay.gate_s) + so, sgw);
+    load_u32s<GW / 2>(reinterpret_cast<const uint32_t*>(b + a.lay.gate_b) + so, gbw);
+    load_u32s<GW / 2>(reinterpret_cast<const uint32_t*>(b + a.lay.up_s) + so, suw);
+    load_u32s<GW / 2>(reinterpret_cast<const uint32_t*>(b + a.lay.up_b) + so, ubw);
+  }
+  const int rr = tid & 15;
+  const uint4* adp = reinterpret_cast<const uint4*>(
+      lora ? b + a.lay.a_down + ((size_t)min(rr, r - 1) * I + i0) * 2 : b + a.lay.gate_q);
+  const uint4 ad0 = adp[0], ad1 = adp[1];
+  if (lora) {
+    for (int t = tid; t < 2 * 16 * r; t += 256) {
+      const int p = t / (16 * r), rem = t % (16 * r);
+      const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate));
+      sm.bl[p][rem / r][rem % r] = bf2f(B[(size_t)(i0 + rem / r) * r + rem % r]);
     }
-    const uint16_t* Ad = reinterpret_cast<const uint16_t*>(b + a.lay.a_down);
-    for (int t = tid; t < 32 * r; t += 256) {
-      const int c = t % 32, rr = t / 32;
-      ad_s[rr][c] = bf2f(Ad[(size_t)rr * I + row0 + c]);
+    for (int t = tid; t < kTileTok * 2 * r; t += 256) {
+      const int m = t / (2 * r), rem = t % (2 * r);
+      sm.tl[m][rem / r][rem % r] = m < mt ? a.t_in[(size_t)(q0 + t0 + m) * 2 * r + rem] : 0.f;
     }
   }
-  const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
-  const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
-  const uint16_t* gsp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s) + (size_t)row * ng;
-  const uint16_t* gbp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b) + (size_t)row * ng;
-  const uint16_t* usp = reinterpret_cast<const uint16_t*>(b + a.lay.up_s) + (size_t)row * ng;
-  const uint16_t* ubp = reinterpret_cast<const uint16_t*>(b + a.lay.up_b) + (size_t)row * ng;
-  for (int t0 = 0; t0 < n; t0 += 32) {
-    const int mt = n - t0 < 32 ? n - t0 : 32;
-    __syncthreads();  // LDS of the previous tile consumed; staging above done
-    for (int t = tid; t < mt * 2 * r; t += 256) {
-      const int m = t / (2 * r), rem = t % (2 * r);
-      tl_s[m][rem / r][rem % r] = a.t_in[(size_t)(q0 + t0 + m) * 2 * r + rem];
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                0x3F803F80u, 0x3F803F80u));
+  f32x4_t accG = {0.f, 0.f, 0.f, 0.f}, accU = accG;
+#pragma unroll
+  for (int gl = 0; gl < GW; ++gl) {
+    f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = cg, cx = cg;
+#pragma unroll
+    for (int s = 0; s < WPG; ++s) {
+      const bf16x8_t xo = x_operand(xa[gl * WPG + s]);
+      cg = mfma16(xo, q4_operand_k(wg[gl * WPG + s], kq), cg);
+      cu = mfma16(xo, q4_operand_k(wu[gl * WPG + s], kq), cu);
+      cx = mfma16(xo, ones, cx);
     }
-    const bool tok_ok = nn < mt;
-    const uint16_t* xrow = a.x + (size_t)a.pair_tok[q0 + t0 + (tok_ok ? nn : 0)] * d;
-    f32x16_t accG, accU;
+    const float sg = bf_at(sgw, gl), cbg = bf_at(gbw, gl) - 128.f * sg;
+    const float su = bf_at(suw, gl), cbu = bf_at(ubw, gl) - 128.f * su;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) accG[v] = accU[v] = 0.f;
-    // passes of up to kGW groups per wave: every weight load of the pass is
-    // issued first, the activations of group i+1 while group i computes
-    for (int G0 = wave; G0 < ng; G0 += 4 * kGW) {
-      uint32_t wg[kGW][SPG], wu[kGW][SPG];
-      uint32_t sc[kGW][4];  // raw bf16 s, b of gate and up
+    for (int v = 0; v < 4; ++v) {
+      accG[v] += sg * cg[v] + cbg * cx[v];
+      accU[v] += su * cu[v] + cbu * cx[v];
+    }
+    // one group at a time: expanding every group's operands ahead would
+    // take more registers than the occupancy allows
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-      for (int i = 0; i < kGW; ++i) {
-        const int G = G0 + 4 * i;
-        if (G < ng) {
-          load_words<SPG>(gq + (size_t)G * (g / 8) + jh * SPG, wg[i]);
-          load_words<SPG>(uq + (size_t)G * (g / 8) + jh * SPG, wu[i]);
-          sc[i][0] = gsp[G];
-          sc[i][1] = gbp[G];
-          sc[i][2] = usp[G];
-          sc[i][3] = ubp[G];
-        }
+  for (int v = 0; v < 4; ++v) {
+    sm.red[wave][0][4 * j + v][n] = accG[v];
+    sm.red[wave][1][4 * j + v][n] = accU[v];
+  }
+  __syncthreads();
+  const int m = tid >> 4, rn = tid & 15;  // the 16 threads of token m are one DPP row
+  {
+    float Gv = sm.red[0][0][m][rn] + sm.red[1][0][m][rn] + sm.red[2][0][m][rn] + sm.red[3][0][m][rn];
+    float Uv = sm.red[0][1][m][rn] + sm.red[1][1][m][rn] + sm.red[2][1][m][rn] + sm.red[3][1][m][rn];
+    if (lora) {
+      float dg = 0.f, du = 0.f;
+      for (int k = 0; k < r; ++k) {
+        dg += sm.bl[0][rn][k] * sm.tl[m][0][k];
+        du += sm.bl[1][rn][k] * sm.tl[m][1][k];
       }
-      uint4 xr[2][SPG];
-      auto load_x = [&](int i, uint4 (&dst)[SPG]) {
-        const int G = G0 + 4 * i;
-#pragma unroll
-        for (int t = 0; t < SPG; ++t)
-          dst[t] = (tok_ok && G < ng)
-                       ? reinterpret_cast<const uint4*>(xrow + G * g + jh * (g / 2))[t]
-                       : make_uint4(0, 0, 0, 0);
-      };
-      load_x(0, xr[0]);
-#pragma unroll
-      for (int i = 0; i < kGW; ++i) {
-        const int G = G0 + 4 * i;
-        if (i + 1 < kGW) load_x(i + 1, xr[(i + 1) & 1]);
-        if (G < ng) {
-          const uint4* xv = xr[i & 1];
-          const float sg = bf2f(sc[i][0]), cbg = bf2f(sc[i][1]) - 128.f * sg;
-          const float su = bf2f(sc[i][2]), cbu = bf2f(sc[i][3]) - 128.f * su;
-          float sx = 0.f;
-#pragma unroll
-          for (int t = 0; t < SPG; ++t) sx += raw_sum8(xv[t]);
-          sx += __shfl_xor(sx, 32, kWave);  // the group's sum for token nn
-          f32x16_t cg, cu;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) cg[v] = cu[v] = 0.f;
-#pragma unroll
-          for (int t = 0; t < SPG; ++t) {
-            const bf16x8_t xo = x_operand(xv[t]);
-            cg = mfma32(xo, q4_operand(wg[i][t]), cg);
-            cu = mfma32(xo, q4_operand(wu[i][t]), cu);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-            const float sxm = __shfl(sx, m, kWave);
-            accG[v] += sg * cg[v] + cbg * sxm;
-            accU[v] += su * cu[v] + cbu * sxm;
-          }
-        }
-      }
+      Gv += a.scale * dg;
+      Uv += a.scale * du;
     }
+    const float h = grp_silu(Gv) * Uv;
+    const bool ok = m < mt;
+    float hr = 0.f;
+    if (ok) hr = grp_store_h(a, q0 + t0 + m, i0 + rn, h);
+    sm.h[m][rn] = ok ? h : 0.f;
+    const float s16 = row16_sum(hr);
+    if (rn == 0 && ok) a.hs[(size_t)(q0 + t0 + m) * (I / 16) + blk] = s16;
+  }
+  __syncthreads();  // h written
+  if (lora && m < mt && rr < r) {
+    const uint32_t w8[8] = {ad0.x, ad0.y, ad0.z, ad0.w, ad1.x, ad1.y, ad1.z, ad1.w};
+    float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-      red[wave][0][nn][m] = accG[v];
-      red[wave][1][nn][m] = accU[v];
-    }
-    __syncthreads();
-    for (int t = tid; t < mt * 32; t += 256) {
-      const int m = t / 32, rw = t % 32;
-      float Gv = red[0][0][rw][m] + red[1][0][rw][m] + red[2][0][rw][m] + red[3][0][rw][m];
-      float Uv = red[0][1][rw][m] + red[1][1][rw][m] + red[2][1][rw][m] + red[3][1][rw][m];
-      if (r > 0) {
-        float dg = 0.f, du = 0.f;
-        for (int rr = 0; rr < r; ++rr) {
-          dg += bl_s[0][rw][rr] * tl_s[m][0][rr];
-          du += bl_s[1][rw][rr] * tl_s[m][1][rr];
-        }
-        Gv += a.scale * dg;
-        Uv += a.scale * du;
-      }
-      const float h = grp_silu(Gv) * Uv;
-      hbuf[m][rw] = h;
-      hrep_s[m][rw] = grp_store_h(a, q0 + t0 + m, row0 + rw, h);
-    }
-    __syncthreads();
-    for (int t = tid; t < mt * 2; t += 256) {
-      const int m = t / 2, half = t % 2;
-      float sm = 0.f;
-      for (int k = 0; k < 16; ++k) sm += hrep_s[m][16 * half + k];
-      a.hs[(size_t)(q0 + t0 + m) * (I / 16) + rb * 2 + half] = sm;
-    }
-    for (int t = tid; t < mt * r; t += 256) {
-      const int m = t / r, rr = t % r;
-      float sm = 0.f;
-      for (int k = 0; k < 32; ++k) sm += ad_s[rr][k] * hbuf[m][k];
-      atomicAdd(a.tdown + (size_t)(q0 + t0 + m) * r + rr, to_fix(sm));
-    }
+    for (int u = 0; u < 8; ++u) s += bf_lo(w8[u]) * sm.h[m][2 * u] + bf_hi(w8[u]) * sm.h[m][2 * u + 1];
+    atomicAdd(a.tdown + (size_t)(q0 + t0 + m) * r + rr, to_fix(s));
   }
 }
 
-// One workgroup = 32 output rows of one active expert's down projection,
-// all its tokens in tiles of 32; h enters as its bf16 hi and lo parts.
-template <int SPG>
-__global__ __launch_bounds__(256) void k_grp_down_mfma(GrpArgs a, int min_cnt) {
-  __shared__ float red[4][32][33];  // per wave: [output row][token]
-  __shared__ float bd_s[32][64];    // B_down rows of the block
-  __shared__ float td_s[32][64];    // t_down of the tile's tokens
-  const int nb32 = a.d / 32;
-  const int act = blockIdx.x / nb32;
-  const int ob = blockIdx.x % nb32;
-  if (act >= a.info[0]) return;
-  const int n = a.act_cnt[act];
-  if (n < min_cnt) return;
-  const uint8_t* b = grp_bundle(a, act);
-  if (b == nullptr) return;
-  const int q0 = a.act_off[act];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nn = lane & 31, jh = lane >> 5;
-  const int d = a.d, g = a.g, I = a.I, r = a.r, NC = I / 32, ngI = I / g;
-  const int o0 = ob * 32, o = o0 + nn;
-  const int trb = o / 64, within = o % 64;
-  if (r > 0) {
-    const uint16_t* Bd = reinterpret_cast<const uint16_t*>(b + a.lay.b_down);
-    for (int t = tid; t < 32 * r; t += 256) bd_s[t / r][t % r] = bf2f(Bd[(size_t)(o0 + t / r) * r + t % r]);
-  }
-  const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q);
-  const uint16_t* dsp = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
-  const uint16_t* dbp = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
-  for (int t0 = 0; t0 < n; t0 += 32) {
-    const int mt = n - t0 < 32 ? n - t0 : 32;
-    __syncthreads();
-    for (int t = tid; t < mt * r; t += 256)
-      td_s[t / r][t % r] = from_fix(a.tdown[(size_t)(q0 + t0 + t / r) * r + t % r]);
-    const bool tok_ok = nn < mt;
-    const int q = q0 + t0 + (tok_ok ? nn : 0);
-    const uint16_t* hhi = a.hp_hi + (size_t)q * I;
-    const uint16_t* hlo = a.hp_lo + (size_t)q * I;
-    const float* hsq = a.hs + (size_t)q * (I / 16);
-    f32x16_t acc;
+template <int GW, int WPG>
+__global__ __launch_bounds__(256, 3) void k_grp_gu_tile(GrpArgs a, int tm, int min_cnt) {
+  constexpr int NW = GW * WPG;
+  __shared__ GuTileLds sm;
+  const int nblk = a.I / 16;
+  const int tt = blockIdx.x / (a.Amax * nblk);
+  const int act = (blockIdx.x / nblk) % a.Amax;
+  const int blk = blockIdx.x % nblk;
+  // everything the start depends on, in one round trip
+  const int n_act = a.info[0], cnt = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
+  asm volatile("" ::"s"(n_act), "s"(cnt), "s"(slot), "s"(q0));
+  const int t_first = tt * tm;
+  if (act >= n_act || t_first >= cnt || cnt < min_cnt || slot < 0) return;
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int d = a.d, g = a.g;
+  const int row = blk * 16 + n;
+  // this lane's weight words: groups wave * GW + gl, quad j
+  uint32_t wg[NW], wu[NW];
+  {
+    const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
+    const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    for (int G0 = wave; G0 < ngI; G0 += 4 * kGW) {
-      // the pass's weights first: words j*SPG .. of each group (input
-      // i0 = G*g + j*g/2; tiled layout: chunk i0/32, word (i0%32)/8 of row
-      // o's 16 bytes), then the h pairs of group i+1 while group i computes
-      uint32_t wd[kGW][SPG];
-      uint32_t sc[kGW][2];
-#pragma unroll
-      for (int i = 0; i < kGW; ++i) {
-        const int G = G0 + 4 * i;
-        if (G < ngI) {
-          const int i0 = G * g + jh * (g / 2);
-#pragma unroll
-          for (int t = 0; t < SPG; ++t) {
-            const int ii = i0 + 8 * t;
-            wd[i][t] = dq[(((size_t)trb * NC + ii / 32) * 64 + within) * 4 + (ii % 32) / 8];
-          }
-          sc[i][0] = dsp[(size_t)G * d + o];
-          sc[i][1] = dbp[(size_t)G * d + o];
-        }
-      }
-      uint4 hh[2][SPG], hl[2][SPG];
-      auto load_h = [&](int i, uint4 (&dh)[SPG], uint4 (&dl)[SPG]) {
-        const int G = G0 + 4 * i;
-        const int i0 = G * g + jh * (g / 2);
-        const bool on = tok_ok && G < ngI;
-#pragma unroll
-        for (int t = 0; t < SPG; ++t) {
-          dh[t] = on ? reinterpret_cast<const uint4*>(hhi + i0)[t] : make_uint4(0, 0, 0, 0);
-          dl[t] = on ? reinterpret_cast<const uint4*>(hlo + i0)[t] : make_uint4(0, 0, 0, 0);
-        }
-      };
-      load_h(0, hh[0], hl[0]);
-#pragma unroll
-      for (int i = 0; i < kGW; ++i) {
-        const int G = G0 + 4 * i;
-        if (i + 1 < kGW) load_h(i + 1, hh[(i + 1) & 1], hl[(i + 1) & 1]);
-        if (G < ngI) {
-          const float sd = bf2f(sc[i][0]);
-          const float cbd = bf2f(sc[i][1]) - 128.f * sd;
-          float sh = 0.f;
-          if (tok_ok)
-            for (int k = 0; k < g / 16; ++k) sh += hsq[G * (g / 16) + k];
-          f32x16_t c;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) c[v] = 0.f;
-#pragma unroll
-          for (int t = 0; t < SPG; ++t) {
-            const bf16x8_t wo = q4_operand(wd[i][t]);
-            c = mfma32(__builtin_bit_cast(bf16x8_t, hh[i & 1][t]), wo, c);
-            c = mfma32(__builtin_bit_cast(bf16x8_t, hl[i & 1][t]), wo, c);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-            acc[v] += sd * c[v] + cbd * __shfl(sh, m, kWave);
-          }
-        }
-      }
+    for (int gl = 0; gl < GW; ++gl) {
+      const int off = (wave * GW + gl) * (g / 8) + j * WPG;
+      load_u32s<WPG>(gq + off, wg + gl * WPG);
+      load_u32s<WPG>(uq + off, wu + gl * WPG);
     }
+  }
+  const Q4Consts kq = q4_consts();
+  gu_tile<GW, WPG>(a, b, q0, t_first, min(tm, cnt - t_first), blk, wg, wu, kq, sm);
+}
+
+// Down: workgroup (tile, active expert, 64 output rows); wave w owns rows
+// 16 w .. 16 w + 15 of the block over all I inputs (NW = I / 32 words per
+// lane, GD = NW / WPG groups, loaded once), two MFMAs per step (h as its hi
+// and lo bf16 halves, pair-permuted as stored) against rows staged in LDS
+// (all 4 waves read the same h); then the LoRA-down delta and each token's
+// weighted row added to its fixed-point output.  Dynamic LDS: hi and lo h
+// of tm pairs, rows of I bf16.  One tile per workgroup, as for gate/up.
+template <int NW, int WPG>
+__device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, int q0, int t0,
+                                          int mt, int tm, int rb, const uint32_t (&wd)[NW], Q4Consts kq, uint16_t* hsm,
+                                          float (&gsum)[kTileTok][NW / WPG],
+                                          float (&td_s)[kTileTok][kTileRank + 1]) {
+  constexpr int GD = NW / WPG;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int d = a.d, g = a.g, I = a.I, r = a.r;
+  const int o = rb * 64 + 16 * wave + n;
+  const bool lora = r > 0;
+  uint16_t* hh = hsm;
+  uint16_t* hl = hsm + (size_t)tm * I;
+  const int cpt = I / 8;  // 16-byte chunks per h row
+  // hi and lo h of the tile's pairs (contiguous rows): NW / 2 chunks per
+  // thread at tm = 16, all loads first
+  uint4 v[NW / 2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) red[wave][nn][8 * (v >> 2) + 4 * jh + (v & 3)] = acc[v];
-    __syncthreads();
-    for (int t = tid; t < mt * 32; t += 256) {
-      const int m = t / 32, rw = t % 32;
-      float tot = red[0][rw][m] + red[1][rw][m] + red[2][rw][m] + red[3][rw][m];
-      if (r > 0) {
+  for (int u = 0; u < NW / 2; ++u) {
+    const int idx = tid + 256 * u;
+    const int half = idx / (tm * cpt), rem = idx % (tm * cpt);  // half: 0 hi, 1 lo
+    const uint16_t* src = half == 1 ? a.hp_lo : a.hp_hi;
+    v[u] = reinterpret_cast<const uint4*>(
+        src + ((size_t)(q0 + t0 + min(rem / cpt, mt - 1))) * I)[rem % cpt];
+  }
+  // scales, biases, B_down row o (pair index clamped; r is even), and the
+  // lane's 4 pairs' tokens and routing weights
+  uint32_t sdr[GD], dbr[GD], bdw[kTileRank / 2];
+  {
+    const uint16_t* ds = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
+    const uint16_t* db = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
+#pragma unroll
+    for (int G = 0; G < GD; ++G) {
+      sdr[G] = ds[(size_t)G * d + o];
+      dbr[G] = db[(size_t)G * d + o];
+    }
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        lora ? b + a.lay.b_down + (size_t)o * r * 2 : b + a.lay.down_q);
+#pragma unroll
+    for (int k = 0; k < kTileRank / 2; ++k) bdw[k] = src[lora ? min(k, r / 2 - 1) : 0];
+  }
+  int ptok[4];
+  float pw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = q0 + t0 + min(4 * j + u, mt - 1);
+    ptok[u] = a.pair_tok[q];
+    pw[u] = a.pair_w[q];
+  }
+#pragma unroll
+  for (int u = 0; u < NW / 2; ++u) {
+    const int idx = tid + 256 * u;
+    const int half = idx / (tm * cpt), rem = idx % (tm * cpt);
+    if (half < 2)
+      *reinterpret_cast<uint4*>((half ? hl : hh) + swz(rem / cpt, I, 8 * (rem % cpt))) =
+          rem / cpt < mt ? v[u] : make_uint4(0, 0, 0, 0);
+  }
+  const int bpg = g / 16;  // 16-row sums per group
+  for (int t = tid; t < tm * GD; t += 256) {
+    const int m = t / GD, G = t % GD;
+    float s = 0.f;
+    if (m < mt) {
+      const float* hs = a.hs + (size_t)(q0 + t0 + m) * (I / 16) + G * bpg;
+      for (int u = 0; u < bpg; ++u) s += hs[u];
+    }
+    gsum[m][G] = s;
+  }
+  if (lora) {
+    for (int t = tid; t < tm * r; t += 256) {
+      const int m = t / r, k = t % r;
+      td_s[m][k] = m < mt ? from_fix(a.tdown[(size_t)(q0 + t0 + m) * r + k]) : 0.f;
+    }
+  }
+  __syncthreads();
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nr = min(n, tm - 1);
+#pragma unroll
+  for (int G = 0; G < GD; ++G) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < WPG; ++s) {
+      const int e = swz(nr, I, G * g + j * (g / 4) + 8 * s);
+      const bf16x8_t wo = q4_operand_k(wd[G * WPG + s], kq);
+      c = mfma16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(hh + e)), wo, c);
+      c = mfma16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(hl + e)), wo, c);
+    }
+    const float sd = bf2f(sdr[G]), cbd = bf2f(dbr[G]) - 128.f * sd;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += sd * c[u] + cbd * gsum[min(4 * j + u, tm - 1)][G];
+    __builtin_amdgcn_sched_barrier(0);  // one group's LDS reads at a time
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int m = 4 * j + u;
+    if (m < mt) {
+      float tot = acc[u];
+      if (lora) {
         float dl = 0.f;
-        for (int rr = 0; rr < r; ++rr) dl += bd_s[rw][rr] * td_s[m][rr];
+#pragma unroll
+        for (int k = 0; k < kTileRank / 2; ++k)
+          if (2 * k < r) dl += bf_lo(bdw[k]) * td_s[m][2 * k] + bf_hi(bdw[k]) * td_s[m][2 * k + 1];
         tot += a.scale * dl;
       }
-      const int qq = q0 + t0 + m;
-      atomicAdd(a.acc + (size_t)a.pair_tok[qq] * d + o0 + rw, to_fix(a.pair_w[qq] * tot));
+      atomicAdd(a.acc + (size_t)ptok[u] * d + o, to_fix(pw[u] * tot));
     }
   }
 }
 
-// ------------------------------------------------- MFMA, pipelined (v2)
-// GEMM-shaped variants for I % 128 == 0, d % 128 == 0 and lora_rank <= 16:
-// a workgroup covers 128 weight rows (4 waves x 32, each wave the full
-// reduction) for up to 32 tokens of one expert; the activation tile is
-// staged in LDS in chunks of kKC inputs (double-buffered, shared by the 4
-// waves, with each group's activation sum), and each wave's weight words of
-// the next chunk are in flight while the current chunk computes.  Operand
-// order and the per-group fold are those of the kernels above.
-constexpr int kKC = 128;  // inputs per staged chunk
-
-// Stage the activations of chunk c (tokens m < mt of the tile): thread t ->
-// token t / 8, 16 inputs (16 p .. 16 p + 15), p = t % 8; each group's sum
-// from the threads of its parts (neighbouring lanes of the same token).
-template <int SPG>
-__device__ __forceinline__ void grp_stage_x(const GrpArgs& a, int q0, int t0, int mt, int c,
-                                            uint16_t (*xs)[kKC], float (*gs)[8]) {
-  constexpr int G = 16 * SPG;     // group size
-  constexpr int PPG = G / 16;     // parts per group (2, 4, 8)
-  const int t = threadIdx.x, m = t >> 3, p = t & 7;
-  uint4 v[2];
-  float sum = 0.f;
-  if (m < mt) {
-    const uint16_t* src = a.x + (size_t)a.pair_tok[q0 + t0 + m] * a.d + c * kKC + 16 * p;
+template <int NW, int WPG>
+__global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int min_cnt) {
+  constexpr int GD = NW / WPG;
+  extern __shared__ __align__(16) uint16_t hsm[];
+  __shared__ float gsum[kTileTok][GD];
+  __shared__ float td_s[kTileTok][kTileRank + 1];
+  const int nrb = a.d / 64;
+  const int tt = blockIdx.x / (a.Amax * nrb);
+  const int act = (blockIdx.x / nrb) % a.Amax;
+  const int rb = blockIdx.x % nrb;
+  const int n_act = a.info[0], cnt = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
+  asm volatile("" ::"s"(n_act), "s"(cnt), "s"(slot), "s"(q0));
+  const int t_first = tt * tm;
+  if (act >= n_act || t_first >= cnt || cnt < min_cnt || slot < 0) return;
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int g = a.g, NC = a.I / 32;
+  uint32_t wd[NW];
+  {
+    const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      v[u] = reinterpret_cast<const uint4*>(src)[u];
-      sum += raw_sum8(v[u]);
-    }
-  } else {
-    v[0] = v[1] = make_uint4(0, 0, 0, 0);
-  }
-  reinterpret_cast<uint4*>(&xs[m][16 * p])[0] = v[0];
-  reinterpret_cast<uint4*>(&xs[m][16 * p])[1] = v[1];
-  sum += __shfl_xor(sum, 1, kWave);
-  if constexpr (PPG >= 4) sum += __shfl_xor(sum, 2, kWave);
-  if constexpr (PPG >= 8) sum += __shfl_xor(sum, 4, kWave);
-  if (p % PPG == 0) gs[m][p / PPG] = sum;
-}
-
-template <int SPG>
-__global__ __launch_bounds__(256, 2) void k_grp_gate_up_mfma2(GrpArgs a, int min_cnt) {
-  constexpr int G = 16 * SPG, CG = kKC / G;  // group size, groups per chunk
-  __shared__ uint16_t xs[2][32][kKC];
-  __shared__ float gsx[2][32][8];
-  __shared__ float tl_s[32][2][kFusedRank];
-  __shared__ float bl_s[2][128][kFusedRank];
-  const int nb = a.I / 128;
-  const int act = blockIdx.x / nb;
-  const int rb = blockIdx.x % nb;
-  if (act >= a.info[0]) return;
-  const int n = a.act_cnt[act];
-  if (n < min_cnt) return;
-  const uint8_t* b = grp_bundle(a, act);
-  if (b == nullptr) return;
-  const int q0 = a.act_off[act];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nn = lane & 31, jh = lane >> 5;
-  const int d = a.d, ng = d / G, r = a.r, I = a.I;
-  const int row = rb * 128 + 32 * wave + nn;
-  const int nch = d / kKC;
-  const uint32_t* gq = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
-  const uint32_t* uq = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
-  const uint16_t* gsp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s) + (size_t)row * ng;
-  const uint16_t* gbp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b) + (size_t)row * ng;
-  const uint16_t* usp = reinterpret_cast<const uint16_t*>(b + a.lay.up_s) + (size_t)row * ng;
-  const uint16_t* ubp = reinterpret_cast<const uint16_t*>(b + a.lay.up_b) + (size_t)row * ng;
-  if (r > 0) {
-    const uint16_t* Bg = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
-    const uint16_t* Bu = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
-    for (int t = tid; t < 128 * r; t += 256) {
-      const int rw = t / r, rr = t % r;
-      bl_s[0][rw][rr] = bf2f(Bg[(size_t)(rb * 128 + rw) * r + rr]);
-      bl_s[1][rw][rr] = bf2f(Bu[(size_t)(rb * 128 + rw) * r + rr]);
+    for (int G = 0; G < GD; ++G) {
+      const int k0 = G * g + j * (g / 4);
+      load_u32s<WPG>(dq + (((size_t)rb * NC + (k0 >> 5)) * 64 + 16 * wave + n) * 4 + ((k0 & 31) >> 3),
+                     wd + G * WPG);
     }
   }
-  uint32_t wg[2][CG][SPG], wu[2][CG][SPG], sc[2][CG][4];
-  auto load_w = [&](int c, int bi) {
-#pragma unroll
-    for (int i = 0; i < CG; ++i) {
-      const int Gi = c * CG + i;
-      load_words<SPG>(gq + (size_t)Gi * (G / 8) + jh * SPG, wg[bi][i]);
-      load_words<SPG>(uq + (size_t)Gi * (G / 8) + jh * SPG, wu[bi][i]);
-      sc[bi][i][0] = gsp[Gi];
-      sc[bi][i][1] = gbp[Gi];
-      sc[bi][i][2] = usp[Gi];
-      sc[bi][i][3] = ubp[Gi];
-    }
-  };
-  for (int t0 = 0; t0 < n; t0 += 32) {
-    const int mt = n - t0 < 32 ? n - t0 : 32;
-    __syncthreads();  // previous tile's LDS consumed
-    for (int t = tid; t < mt * 2 * r; t += 256) {
-      const int m = t / (2 * r), rem = t % (2 * r);
-      tl_s[m][rem / r][rem % r] = a.t_in[(size_t)(q0 + t0 + m) * 2 * r + rem];
-    }
-    f32x16_t accG, accU;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) accG[v] = accU[v] = 0.f;
-    load_w(0, 0);
-    grp_stage_x<SPG>(a, q0, t0, mt, 0, xs[0], gsx[0]);
-    for (int c = 0; c < nch; ++c) {
-      const int buf = c & 1;
-      __syncthreads();  // chunk c staged; the other buffer free
-      if (c + 1 < nch) {
-        if (buf) load_w(c + 1, 0); else load_w(c + 1, 1);
-        grp_stage_x<SPG>(a, q0, t0, mt, c + 1, xs[buf ^ 1], gsx[buf ^ 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < CG; ++i) {
-        f32x16_t cg, cu;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cg[v] = cu[v] = 0.f;
-        uint32_t w_g[SPG], w_u[SPG], s_[4];
-#pragma unroll
-        for (int st = 0; st < SPG; ++st) {
-          w_g[st] = buf ? wg[1][i][st] : wg[0][i][st];
-          w_u[st] = buf ? wu[1][i][st] : wu[0][i][st];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s_[q] = buf ? sc[1][i][q] : sc[0][i][q];
-#pragma unroll
-        for (int st = 0; st < SPG; ++st) {
-          const uint4 xr = *reinterpret_cast<const uint4*>(&xs[buf][nn][i * G + jh * (G / 2) + 8 * st]);
-          const bf16x8_t xo = x_operand(xr);
-          cg = mfma32(xo, q4_operand(w_g[st]), cg);
-          cu = mfma32(xo, q4_operand(w_u[st]), cu);
-        }
-        const float sg = bf2f(s_[0]), cbg = bf2f(s_[1]) - 128.f * sg;
-        const float su = bf2f(s_[2]), cbu = bf2f(s_[3]) - 128.f * su;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-          const float sxm = gsx[buf][m][i];
-          accG[v] += sg * cg[v] + cbg * sxm;
-          accU[v] += su * cu[v] + cbu * sxm;
-        }
-      }
-    }
-    // epilogue: LoRA B t, SwiGLU, h pairs and the 16-row sums of this wave
-    const int rl = 32 * wave + nn;  // row within the workgroup
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-      float Gv = accG[v], Uv = accU[v];
-      if (r > 0) {
-        float dg = 0.f, du = 0.f;
-        for (int rr = 0; rr < r; ++rr) {
-          dg += bl_s[0][rl][rr] * tl_s[m][0][rr];
-          du += bl_s[1][rl][rr] * tl_s[m][1][rr];
-        }
-        Gv += a.scale * dg;
-        Uv += a.scale * du;
-      }
-      const float h = grp_silu(Gv) * Uv;
-      const float hr = m < mt ? grp_store_h(a, q0 + t0 + m, row, h) : 0.f;
-      const float s16 = row16_sum(hr);  // rows of the same 16-row block
-      if ((nn & 15) == 0 && m < mt) a.hs[(size_t)(q0 + t0 + m) * (I / 16) + (row >> 4)] = s16;
-    }
-  }
-}
-
-template <int SPG>
-__global__ __launch_bounds__(256, 2) void k_grp_down_mfma2(GrpArgs a, int min_cnt) {
-  constexpr int G = 16 * SPG, CG = kKC / G;
-  __shared__ uint16_t hs_hi[2][32][kKC];
-  __shared__ uint16_t hs_lo[2][32][kKC];
-  __shared__ uint16_t ad_s[2][kFusedRank][kKC];   // A_down rows of the chunk
-  __shared__ float gsh[2][32][kKC / 16];          // 16-row sums of h per chunk
-  __shared__ float td_s[32][kFusedRank + 1];      // t_down [token][rank]
-  __shared__ float bd_s[128][kFusedRank];
-  const int nb = a.d / 128;
-  const int act = blockIdx.x / nb;
-  const int ob = blockIdx.x % nb;
-  if (act >= a.info[0]) return;
-  const int n = a.act_cnt[act];
-  if (n < min_cnt) return;
-  const uint8_t* b = grp_bundle(a, act);
-  if (b == nullptr) return;
-  const int q0 = a.act_off[act];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nn = lane & 31, jh = lane >> 5;
-  const int d = a.d, I = a.I, r = a.r, NC = I / 32;
-  const int o = ob * 128 + 32 * wave + nn;
-  const int trb = o / 64, within = o % 64;
-  const int nch = I / kKC;
-  const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q);
-  const uint16_t* dsp = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
-  const uint16_t* dbp = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
-  const uint16_t* adp = reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.a_down : 0));
-  if (r > 0) {
-    const uint16_t* Bd = reinterpret_cast<const uint16_t*>(b + a.lay.b_down);
-    for (int t = tid; t < 128 * r; t += 256)
-      bd_s[t / r][t % r] = bf2f(Bd[(size_t)(ob * 128 + t / r) * r + t % r]);
-  }
-  uint32_t wd[2][CG][SPG], sc[2][CG][2];
-  auto load_w = [&](int c, int bi) {
-#pragma unroll
-    for (int i = 0; i < CG; ++i) {
-      const int Gi = c * CG + i;
-      const int i0 = Gi * G + jh * (G / 2);
-#pragma unroll
-      for (int st = 0; st < SPG; ++st) {
-        const int ii = i0 + 8 * st;
-        wd[bi][i][st] = dq[(((size_t)trb * NC + ii / 32) * 64 + within) * 4 + (ii % 32) / 8];
-      }
-      sc[bi][i][0] = dsp[(size_t)Gi * d + o];
-      sc[bi][i][1] = dbp[(size_t)Gi * d + o];
-    }
-  };
-  auto stage_h = [&](int t0, int mt, int c, int buf) {
-    // thread t -> token t / 8, 16 inputs of the chunk; h pairs as stored
-    const int t = tid, m = t >> 3, p = t & 7;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      uint4 hv = make_uint4(0, 0, 0, 0), lv = hv;
-      if (m < mt) {
-        const size_t off = (size_t)(q0 + t0 + m) * I + c * kKC + 16 * p + 8 * u;
-        hv = *reinterpret_cast<const uint4*>(a.hp_hi + off);
-        lv = *reinterpret_cast<const uint4*>(a.hp_lo + off);
-      }
-      reinterpret_cast<uint4*>(&hs_hi[buf][m][16 * p])[u] = hv;
-      reinterpret_cast<uint4*>(&hs_lo[buf][m][16 * p])[u] = lv;
-    }
-    gsh[buf][m][p] = m < mt ? a.hs[(size_t)(q0 + t0 + m) * (I / 16) + c * (kKC / 16) + p] : 0.f;
-    // A_down rows of the chunk (ranks >= r are zero)
-    for (int e = t; e < kFusedRank * (kKC / 8); e += 256) {
-      const int rr = e / (kKC / 8), k8 = e % (kKC / 8);
-      uint4 av = make_uint4(0, 0, 0, 0);
-      if (rr < r) av = *reinterpret_cast<const uint4*>(adp + (size_t)rr * I + c * kKC + 8 * k8);
-      reinterpret_cast<uint4*>(&ad_s[buf][rr][0])[k8] = av;
-    }
-  };
-  for (int t0 = 0; t0 < n; t0 += 32) {
-    const int mt = n - t0 < 32 ? n - t0 : 32;
-    __syncthreads();
-    f32x16_t acc, tdv;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = tdv[v] = 0.f;
-    load_w(0, 0);
-    stage_h(t0, mt, 0, 0);
-    for (int c = 0; c < nch; ++c) {
-      const int buf = c & 1;
-      __syncthreads();
-      if (c + 1 < nch) {
-        if (buf) load_w(c + 1, 0); else load_w(c + 1, 1);
-        stage_h(t0, mt, c + 1, buf ^ 1);
-      }
-#pragma unroll
-      for (int i = 0; i < CG; ++i) {
-        f32x16_t cc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cc[v] = 0.f;
-#pragma unroll
-        for (int st = 0; st < SPG; ++st) {
-          const int col = i * G + jh * (G / 2) + 8 * st;
-          const bf16x8_t hh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&hs_hi[buf][nn][col]));
-          const bf16x8_t hl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&hs_lo[buf][nn][col]));
-          const bf16x8_t wo = q4_operand(buf ? wd[1][i][st] : wd[0][i][st]);
-          cc = mfma32(hh, wo, cc);
-          cc = mfma32(hl, wo, cc);
-          if (wave == 0 && r > 0) {
-            // t_down += h A_down^T (lane nn = rank; A_down in the pair order of h)
-            const uint4 araw = nn < kFusedRank ? *reinterpret_cast<const uint4*>(&ad_s[buf][nn][col])
-                                               : make_uint4(0, 0, 0, 0);
-            const bf16x8_t ao = x_operand(araw);
-            tdv = mfma32(hh, ao, tdv);
-            tdv = mfma32(hl, ao, tdv);
-          }
-        }
-        const uint32_t s0 = buf ? sc[1][i][0] : sc[0][i][0];
-        const uint32_t s1 = buf ? sc[1][i][1] : sc[0][i][1];
-        const float sd = bf2f(s0), cbd = bf2f(s1) - 128.f * sd;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-          float sh = 0.f;
-#pragma unroll
-          for (int k = 0; k < G / 16; ++k) sh += gsh[buf][m][i * (G / 16) + k];
-          acc[v] += sd * cc[v] + cbd * sh;
-        }
-      }
-    }
-    if (wave == 0 && nn < kFusedRank) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) td_s[8 * (v >> 2) + 4 * jh + (v & 3)][nn] = tdv[v];
-    }
-    __syncthreads();
-    const int rl = 32 * wave + nn;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 8 * (v >> 2) + 4 * jh + (v & 3);
-      if (m < mt) {
-        float tot = acc[v];
-        if (r > 0) {
-          float dl = 0.f;
-          for (int rr = 0; rr < r; ++rr) dl += bd_s[rl][rr] * td_s[m][rr];
-          tot += a.scale * dl;
-        }
-        const int qq = q0 + t0 + m;
-        atomicAdd(a.acc + (size_t)a.pair_tok[qq] * d + o, to_fix(a.pair_w[qq] * tot));
-      }
-    }
-  }
+  const Q4Consts kq = q4_consts();
+  down_tile<NW, WPG>(a, b, q0, t_first, min(tm, cnt - t_first), tm, rb, wd, kq, hsm, gsum, td_s);
 }
 
 // ------------------------------------------------------------ output
@@ -1177,39 +949,49 @@ static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
   return EDGE0_OK;
 }
 
-static bool grp_mfma2_ok(const GrpArgs& a) {
-  return a.I % 128 == 0 && a.d % 128 == 0 && a.r <= kFusedRank && a.g <= kKC;
+// shapes of the token-tile kernels: d <= 2048, each wave quarter of d an
+// even number of groups of 32 or 64, I a multiple of 128 up to 1024 (a
+// tile's h fits 64 KiB of LDS), LoRA rank even and <= 16
+static bool grp_tile_ok(const GrpArgs& a) {
+  const int gw = a.d / (4 * a.g);
+  return (a.g == 32 || a.g == 64) && a.d <= 2048 && a.d % (8 * a.g) == 0 &&
+         (gw == 2 || gw == 4 || gw == 8 || gw == 16) &&
+         a.I % 128 == 0 && a.I <= 1024 && a.r <= kTileRank && a.r % 2 == 0;
 }
 
-// which = 0 gate/up, 1 down
-static int launch_grp_mfma(const GrpArgs& a, int which, int min_cnt, hipStream_t st) {
-  const int spg = a.g / 16;
-  if (grp_mfma2_ok(a)) {
-    const int grid2 = a.Amax * ((which ? a.d : a.I) / 128);
-#define E0_GRP_MFMA2(S)                                                     \
-  if (which) k_grp_down_mfma2<S><<<grid2, 256, 0, st>>>(a, min_cnt);        \
-  else k_grp_gate_up_mfma2<S><<<grid2, 256, 0, st>>>(a, min_cnt)
-    switch (spg) {
-      case 2: E0_GRP_MFMA2(2); break;
-      case 4: E0_GRP_MFMA2(4); break;
-      case 8: E0_GRP_MFMA2(8); break;
-      default: return EDGE0_EINVAL;
-    }
-#undef E0_GRP_MFMA2
-    E0_CHECK_LAUNCH();
-    return EDGE0_OK;
-  }
-  const int grid = a.Amax * ((which ? a.d : a.I) / 32);
-#define E0_GRP_MFMA(S)                                            \
-  if (which) k_grp_down_mfma<S><<<grid, 256, 0, st>>>(a, min_cnt); \
-  else k_grp_gate_up_mfma<S><<<grid, 256, 0, st>>>(a, min_cnt)
-  switch (spg) {
-    case 2: E0_GRP_MFMA(2); break;
-    case 4: E0_GRP_MFMA(4); break;
-    case 8: E0_GRP_MFMA(8); break;
-    default: return EDGE0_EINVAL;
-  }
-#undef E0_GRP_MFMA
+// experts with >= min_cnt tokens
+static int launch_grp_tiles_gu(const GrpArgs& a, int min_cnt, hipStream_t st) {
+  const int tm = a.T < kTileTok ? a.T : kTileTok;
+  const int nt = (a.T + tm - 1) / tm;
+  const int wpg = a.g / 32, gw = a.d / (4 * a.g);
+  const int grid_gu = nt * a.Amax * (a.I / 16);
+#define E0_GU(GW, W) \
+  if (gw == GW && wpg == W) k_grp_gu_tile<GW, W><<<grid_gu, 256, 0, st>>>(a, tm, min_cnt)
+  bool ok = true;
+  E0_GU(2, 1); else E0_GU(4, 1); else E0_GU(8, 1); else E0_GU(16, 1);
+  else E0_GU(2, 2); else E0_GU(4, 2); else E0_GU(8, 2); else E0_GU(16, 2);
+  else ok = false;
+#undef E0_GU
+  if (!ok) return EDGE0_EINVAL;
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+static int launch_grp_tiles_down(const GrpArgs& a, int min_cnt, hipStream_t st) {
+  const int tm = a.T < kTileTok ? a.T : kTileTok;
+  const int nt = (a.T + tm - 1) / tm;
+  const int wpg = a.g / 32, nw = a.I / 32;
+  const size_t lds_dn = (size_t)2 * tm * a.I * 2;
+  const int grid_dn = nt * a.Amax * (a.d / 64);
+  bool ok = true;
+#define E0_DN(NW, W) \
+  if (nw == NW && wpg == W) k_grp_down_tile<NW, W><<<grid_dn, 256, lds_dn, st>>>(a, tm, min_cnt)
+  E0_DN(4, 1); else E0_DN(8, 1); else E0_DN(12, 1); else E0_DN(16, 1); else E0_DN(24, 1);
+  else E0_DN(32, 1);
+  else E0_DN(4, 2); else E0_DN(8, 2); else E0_DN(12, 2); else E0_DN(16, 2); else E0_DN(24, 2);
+  else E0_DN(32, 2);
+  else ok = false;
+#undef E0_DN
+  if (!ok) return EDGE0_EINVAL;
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
@@ -1277,15 +1059,21 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
     k_grp_lora_in<<<(a.P * 2 * a.r + 3) / 4, 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
   }
-  // GEMVs for every expert unless the caller asks for MFMA from min_mfma
-  // tokens per expert on
-  const int min_mfma = (flags >> 8) & 0xFF;
-  const bool mfma = !(flags & EDGE0_GROUPED_NO_MFMA) && min_mfma > 0 && n_tokens >= min_mfma;
-  const int gemv_max = mfma ? min_mfma - 1 : 1 << 30;
+  // experts with >= tile_min tokens on the MFMA token tiles, the others as
+  // GEMVs.  Default: every expert on the tiles from kTileMinCall tokens per
+  // call on (below that the GEMVs' shorter chains win).  An expert holds at
+  // most n_tokens pairs, so tile_min > n_tokens means no tiles.
+  int tile_min = 0;
+  if (!(flags & EDGE0_GROUPED_NO_MFMA) && grp_tile_ok(a)) {
+    const int fm = (flags >> 8) & 0xFF;
+    tile_min = fm ? fm : (n_tokens >= kTileMinCall ? 1 : 0);
+    if (tile_min > n_tokens) tile_min = 0;
+  }
+  const int gemv_max = tile_min ? tile_min - 1 : 1 << 30;
   int rc = gemv_max >= 1 ? launch_grp_gate_up(a, 1, gemv_max, stream) : EDGE0_OK;
-  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 0, min_mfma, stream);
+  if (rc == EDGE0_OK && tile_min) rc = launch_grp_tiles_gu(a, tile_min, stream);
   if (rc == EDGE0_OK && gemv_max >= 1) rc = launch_grp_down(a, 1, gemv_max, stream);
-  if (rc == EDGE0_OK && mfma) rc = launch_grp_mfma(a, 1, min_mfma, stream);
+  if (rc == EDGE0_OK && tile_min) rc = launch_grp_tiles_down(a, tile_min, stream);
   if (rc != EDGE0_OK) return rc;
   const int n_out = a.T * a.d;
   k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);

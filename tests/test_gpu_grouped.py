@@ -3,10 +3,12 @@ the oracle, which defines it token by token: y_j = sum_k w_jk FFN_{e_jk}(x_j).
 Every token's output is compared (rel-L2 <= 2e-3), for the tiny shape
 (many tokens per expert, several token batches, a ragged last batch) and the
 Qwen3-MoE shape at K = 8 with 1, 4, 8, 16 and 32 tokens and Zipf(1.1)
-routing; the default GEMV path (tokens in slices of 8 per workgroup), the
-mixed path (MFMA for experts with >= 16 tokens) and MFMA for every expert;
-determinism; reuse of the workspace by a smaller call; the empty call;
-invalid ids reported."""
+routing; the default path (MFMA tiles of up to 16 tokens for every expert
+from 4 tokens per call on, GEMVs below), the GEMV path (at most 8 of an
+expert's tokens per workgroup), the mixed path (tiles for experts with >= 16
+tokens) and the tiles for every expert; determinism; reuse of the workspace
+by a smaller call; one token alone equals its row of a grouped call; ids
+repeated within a token; the empty call; invalid ids reported."""
 import numpy as np
 import pytest
 
@@ -26,9 +28,12 @@ def torch_cuda():
 
 
 _LAYERS = {}
-# default (GEMV only), MFMA from 16 tokens per expert, MFMA for every expert
+# default, GEMV only, MFMA tiles from 16 tokens per expert, tiles for every
+# expert
+GEMV = 1
 MFMA16 = 16 << 8
-FLAG_SETS = (0, MFMA16, 1 << 8)
+TILES = 1 << 8
+FLAG_SETS = (0, GEMV, MFMA16, TILES)
 
 
 def _layer(S):
@@ -99,7 +104,7 @@ def _paths_ran(ys, ids, counts):
     calls; a token that uses an MFMA expert shows the MFMA path's rounding
     (at least one must differ when any expert has >= 16 tokens)."""
     big = set(np.nonzero(counts >= 16)[0].tolist())
-    differs = [not np.array_equal(ys[0][j], ys[MFMA16][j]) for j in range(ids.shape[0])]
+    differs = [not np.array_equal(ys[GEMV][j], ys[MFMA16][j]) for j in range(ids.shape[0])]
     for j in range(ids.shape[0]):
         if not big.intersection(ids[j].tolist()):
             assert not differs[j], j
@@ -118,11 +123,13 @@ def test_grouped_deterministic_and_workspace_reuse(torch_cuda):
     # a smaller call on the same workspace
     y3, ws = _call(lay, ids[:4], w[:4], x[:4], ws=ws)
     _check(lay, ids[:4], w[:4], x[:4], y3)
-    # on the GEMV path each token alone equals the grouped call's row for it:
-    # the per-token arithmetic is the same and the fixed-point sums are exact
-    y5, ws = _call(lay, ids, w, x, flags=1, ws=ws)
-    y4, ws = _call(lay, ids[2:3], w[2:3], x[2:3], flags=1, ws=ws)
-    assert np.array_equal(y4[0], y5[2])
+    # on the GEMV and tile paths each token alone equals the grouped call's
+    # row for it: a token's arithmetic does not depend on the other tokens of
+    # its tile or slice, and the fixed-point sums are exact
+    for flags in (TILES, GEMV):
+        y5, ws = _call(lay, ids, w, x, flags=flags, ws=ws)
+        y4, ws = _call(lay, ids[2:3], w[2:3], x[2:3], flags=flags, ws=ws)
+        assert np.array_equal(y4[0], y5[2]), flags
 
 
 def test_grouped_empty_and_bad_ids(torch_cuda):
@@ -153,8 +160,9 @@ def test_grouped_empty_and_bad_ids(torch_cuda):
 
 def test_grouped_repeated_ids(torch_cuda):
     """An id repeated within a token's routing adds that expert's output once
-    per repeat; here expert 2 gets 3 pairs from each of 9 tokens (27 pairs,
-    more than the 9 tokens that size the GEMV token slices)."""
+    per repeat (the oracle sums the K terms; the device evaluates the expert
+    once with the repeats' weights added); here expert 2 is chosen 3 times by
+    each of 9 tokens."""
     S = G.TINY
     lay = _layer(S)
     T = 9
