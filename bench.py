@@ -25,9 +25,9 @@ METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak
 # HBM traffic of one k_layer_fused launch from two rocprofv3 --pmc passes over
 # this workload (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), scaled by what
 # the same counters read for a device copy of known size (256 MiB copy:
-# FETCH_SIZE 131084.8 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only
+# FETCH_SIZE 131084.7 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only
 # for the kernel sources it was taken on (hash below); otherwise None.
-TRAFFIC_RECORD = {"src_sha": "c52b17e58a187a0b", "fetch_kib": 4053.5, "write_kib": 66.9,
+TRAFFIC_RECORD = {"src_sha": "72320c10bfbdf0a6", "fetch_kib": 4048.3, "write_kib": 66.9,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "moe.hip")
 HBM_PEAK_GBPS = 8000.0

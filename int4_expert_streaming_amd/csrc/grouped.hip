@@ -515,6 +515,7 @@ __device__ __forceinline__ bf16x8_t q4_operand_k(uint32_t w, Q4Consts k) {
 constexpr int kTileTok = 16;   // tokens per MFMA tile at most
 constexpr int kTileRank = 16;  // LoRA rank bound of the tile kernels
 constexpr int kTileMinCall = 4;  // default: tiles for calls of >= 4 tokens
+constexpr int kDownNT = 2;  // 64-row blocks per down workgroup (a 16-row n-tile each per wave)
 
 // N consecutive 32-bit words from p (p aligned to min(N, 4) words)
 template <int N>
@@ -717,23 +718,24 @@ __global__ __launch_bounds__(256, 3) void k_grp_gu_tile(GrpArgs a, int tm, int m
   gu_tile<GW, WPG>(a, b, q0, t_first, min(tm, cnt - t_first), blk, wg, wu, kq, sm);
 }
 
-// Down: workgroup (tile, active expert, 64 output rows); wave w owns rows
-// 16 w .. 16 w + 15 of the block over all I inputs (NW = I / 32 words per
-// lane, GD = NW / WPG groups, loaded once), two MFMAs per step (h as its hi
+// Down: workgroup (tile, active expert, kDownNT blocks of 64 output rows);
+// wave w owns rows 16 w .. 16 w + 15 of each block (one 16-row n-tile per
+// block) over all I inputs (NW = I / 32 words per lane and n-tile, GD =
+// NW / WPG groups, loaded once), two MFMAs per step and n-tile (h as its hi
 // and lo bf16 halves, pair-permuted as stored) against rows staged in LDS
-// (all 4 waves read the same h); then the LoRA-down delta and each token's
+// once for the workgroup; then the LoRA-down delta and each token's
 // weighted row added to its fixed-point output.  Dynamic LDS: hi and lo h
 // of tm pairs, rows of I bf16.  One tile per workgroup, as for gate/up.
 template <int NW, int WPG>
 __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, int q0, int t0,
-                                          int mt, int tm, int rb, const uint32_t (&wd)[NW], Q4Consts kq, uint16_t* hsm,
-                                          float (&gsum)[kTileTok][NW / WPG],
+                                          int mt, int tm, int rb,
+                                          const uint32_t (&wd)[kDownNT][NW], Q4Consts kq,
+                                          uint16_t* hsm, float (&gsum)[kTileTok][NW / WPG],
                                           float (&td_s)[kTileTok][kTileRank + 1]) {
-  constexpr int GD = NW / WPG;
+  constexpr int GD = NW / WPG, NT = kDownNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int d = a.d, g = a.g, I = a.I, r = a.r;
-  const int o = rb * 64 + 16 * wave + n;
   const bool lora = r > 0;
   uint16_t* hh = hsm;
   uint16_t* hl = hsm + (size_t)tm * I;
@@ -749,21 +751,25 @@ __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, in
     v[u] = reinterpret_cast<const uint4*>(
         src + ((size_t)(q0 + t0 + min(rem / cpt, mt - 1))) * I)[rem % cpt];
   }
-  // scales, biases, B_down row o (pair index clamped; r is even), and the
-  // lane's 4 pairs' tokens and routing weights
-  uint32_t sdr[GD], dbr[GD], bdw[kTileRank / 2];
+  // per output row o of each n-tile: scales, biases and B_down (pair index
+  // clamped; r is even); the lane's 4 pairs' tokens and routing weights
+  uint32_t sdr[NT][GD], dbr[NT][GD], bdw[NT][kTileRank / 2];
   {
     const uint16_t* ds = reinterpret_cast<const uint16_t*>(b + a.lay.down_s);
     const uint16_t* db = reinterpret_cast<const uint16_t*>(b + a.lay.down_b);
 #pragma unroll
-    for (int G = 0; G < GD; ++G) {
-      sdr[G] = ds[(size_t)G * d + o];
-      dbr[G] = db[(size_t)G * d + o];
-    }
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        lora ? b + a.lay.b_down + (size_t)o * r * 2 : b + a.lay.down_q);
+    for (int t = 0; t < NT; ++t) {
+      const int o = (rb * NT + t) * 64 + 16 * wave + n;
 #pragma unroll
-    for (int k = 0; k < kTileRank / 2; ++k) bdw[k] = src[lora ? min(k, r / 2 - 1) : 0];
+      for (int G = 0; G < GD; ++G) {
+        sdr[t][G] = ds[(size_t)G * d + o];
+        dbr[t][G] = db[(size_t)G * d + o];
+      }
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          lora ? b + a.lay.b_down + (size_t)o * r * 2 : b + a.lay.down_q);
+#pragma unroll
+      for (int k = 0; k < kTileRank / 2; ++k) bdw[t][k] = src[lora ? min(k, r / 2 - 1) : 0];
+    }
   }
   int ptok[4];
   float pw[4];
@@ -798,36 +804,53 @@ __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, in
     }
   }
   __syncthreads();
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nr = min(n, tm - 1);
 #pragma unroll
   for (int G = 0; G < GD; ++G) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t c[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) c[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < WPG; ++s) {
       const int e = swz(nr, I, G * g + j * (g / 4) + 8 * s);
-      const bf16x8_t wo = q4_operand_k(wd[G * WPG + s], kq);
-      c = mfma16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(hh + e)), wo, c);
-      c = mfma16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(hl + e)), wo, c);
-    }
-    const float sd = bf2f(sdr[G]), cbd = bf2f(dbr[G]) - 128.f * sd;
+      const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(hh + e));
+      const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(hl + e));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += sd * c[u] + cbd * gsum[min(4 * j + u, tm - 1)][G];
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8_t wo = q4_operand_k(wd[t][G * WPG + s], kq);
+        c[t] = mfma16(ah, wo, c[t]);
+        c[t] = mfma16(al, wo, c[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float sd = bf2f(sdr[t][G]), cbd = bf2f(dbr[t][G]) - 128.f * sd;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[t][u] += sd * c[t][u] + cbd * gsum[min(4 * j + u, tm - 1)][G];
+    }
     __builtin_amdgcn_sched_barrier(0);  // one group's LDS reads at a time
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int m = 4 * j + u;
     if (m < mt) {
-      float tot = acc[u];
-      if (lora) {
-        float dl = 0.f;
 #pragma unroll
-        for (int k = 0; k < kTileRank / 2; ++k)
-          if (2 * k < r) dl += bf_lo(bdw[k]) * td_s[m][2 * k] + bf_hi(bdw[k]) * td_s[m][2 * k + 1];
-        tot += a.scale * dl;
+      for (int t = 0; t < NT; ++t) {
+        float tot = acc[t][u];
+        if (lora) {
+          float dl = 0.f;
+#pragma unroll
+          for (int k = 0; k < kTileRank / 2; ++k)
+            if (2 * k < r)
+              dl += bf_lo(bdw[t][k]) * td_s[m][2 * k] + bf_hi(bdw[t][k]) * td_s[m][2 * k + 1];
+          tot += a.scale * dl;
+        }
+        const int o = (rb * NT + t) * 64 + 16 * wave + n;
+        atomicAdd(a.acc + (size_t)ptok[u] * d + o, to_fix(pw[u] * tot));
       }
-      atomicAdd(a.acc + (size_t)ptok[u] * d + o, to_fix(pw[u] * tot));
     }
   }
 }
@@ -838,7 +861,7 @@ __global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int
   extern __shared__ __align__(16) uint16_t hsm[];
   __shared__ float gsum[kTileTok][GD];
   __shared__ float td_s[kTileTok][kTileRank + 1];
-  const int nrb = a.d / 64;
+  const int nrb = a.d / (64 * kDownNT);
   const int tt = blockIdx.x / (a.Amax * nrb);
   const int act = (blockIdx.x / nrb) % a.Amax;
   const int rb = blockIdx.x % nrb;
@@ -850,15 +873,18 @@ __global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int g = a.g, NC = a.I / 32;
-  uint32_t wd[NW];
+  uint32_t wd[kDownNT][NW];
   {
     const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q);
 #pragma unroll
-    for (int G = 0; G < GD; ++G) {
-      const int k0 = G * g + j * (g / 4);
-      load_u32s<WPG>(dq + (((size_t)rb * NC + (k0 >> 5)) * 64 + 16 * wave + n) * 4 + ((k0 & 31) >> 3),
-                     wd + G * WPG);
-    }
+    for (int t = 0; t < kDownNT; ++t)
+#pragma unroll
+      for (int G = 0; G < GD; ++G) {
+        const int k0 = G * g + j * (g / 4);
+        load_u32s<WPG>(dq + (((size_t)(rb * kDownNT + t) * NC + (k0 >> 5)) * 64 + 16 * wave + n) * 4 +
+                           ((k0 & 31) >> 3),
+                       wd[t] + G * WPG);
+      }
   }
   const Q4Consts kq = q4_consts();
   down_tile<NW, WPG>(a, b, q0, t_first, min(tm, cnt - t_first), tm, rb, wd, kq, hsm, gsum, td_s);
@@ -981,7 +1007,7 @@ static int launch_grp_tiles_down(const GrpArgs& a, int min_cnt, hipStream_t st) 
   const int nt = (a.T + tm - 1) / tm;
   const int wpg = a.g / 32, nw = a.I / 32;
   const size_t lds_dn = (size_t)2 * tm * a.I * 2;
-  const int grid_dn = nt * a.Amax * (a.d / 64);
+  const int grid_dn = nt * a.Amax * (a.d / (64 * kDownNT));
   bool ok = true;
 #define E0_DN(NW, W) \
   if (nw == NW && wpg == W) k_grp_down_tile<NW, W><<<grid_dn, 256, lds_dn, st>>>(a, tm, min_cnt)
