@@ -87,9 +87,9 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
 
 static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream);
 
-// enqueue all launches of decode step `step` (h[0] already holds h0).  The
-// heads are off the step's critical path (their predictions are used at the
-// next step), so they run on a forked branch that joins at the end.
+// enqueue all launches of decode step `step` (h[0] already holds h0), one
+// stream: the heads come last (a forked branch for them, parallel nodes in
+// the captured graph, measured slower).
 static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers, E = sh.n_experts;
