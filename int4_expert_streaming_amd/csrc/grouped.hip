@@ -88,7 +88,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // repeats' weights added to it in k order (w1 D(x) + w2 D(x) = (w1 + w2)
 // D(x)), so an expert holds at most one pair per token.
 __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
-  __shared__ int cnt[1024];
+  __shared__ unsigned long long tok_mask[1024];  // per expert: the tokens that chose it
   __shared__ int first[1024];
   __shared__ int actidx[1024];
   __shared__ int ids_s[kGrpMaxTokens * 16];
@@ -96,34 +96,37 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
   __shared__ int wtot[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.P, K = a.K;
-  cnt[tid] = 0;
-  for (int p = tid; p < P; p += 1024) {
-    int e = a.ids[p];
+  // every global read up front: pair tid's id and weight (P <= 1024), expert
+  // tid's slot (E <= 1024)
+  int e = -1;
+  float w = 0.f;
+  if (tid < P) {
+    e = a.ids[tid];
+    w = a.w[tid];
     if (e < 0 || e >= E) {
       set_error(a.err, EDGE0_ERANGE);
       e = -1;
     }
-    ids_s[p] = e;
-  }
-  __syncthreads();
-  bool dup = false;  // P <= 1024: one pair per thread
-  if (tid < P) {
-    const int e = ids_s[tid], k0 = tid - tid % K;
-    float w = a.w[tid];
-    if (e >= 0) {
-      for (int q = k0; q < tid; ++q) dup |= ids_s[q] == e;
-      for (int q = tid + 1; q < k0 + K; ++q)
-        if (ids_s[q] == e) w += a.w[q];
-    }
+    ids_s[tid] = e;
     w_s[tid] = w;
   }
+  const int slot = tid < E ? a.table[tid] : -1;
+  tok_mask[tid] = 0ull;
   __syncthreads();
-  if (dup) ids_s[tid] = -1;
+  // repeats within a token: the first k keeps the summed weight; each kept
+  // pair marks its token in its expert's mask (at most one pair per token)
+  const int t = tid / K;
+  if (e >= 0) {
+    const int k0 = tid - tid % K;
+    bool dup = false;
+    for (int q = k0; q < tid; ++q) dup |= ids_s[q] == e;
+    for (int q = tid + 1; q < k0 + K; ++q)
+      if (ids_s[q] == e) w += w_s[q];
+    if (dup) e = -1;
+    else atomicOr(&tok_mask[e], 1ull << t);
+  }
   __syncthreads();
-  for (int p = tid; p < P; p += 1024)
-    if (ids_s[p] >= 0) atomicAdd(&cnt[ids_s[p]], 1);
-  __syncthreads();
-  const int c = tid < E ? cnt[tid] : 0;
+  const int c = tid < E ? __popcll(tok_mask[tid]) : 0;
   const int f = c > 0 ? 1 : 0;
   const int ic = wave_incl_scan(c), iff = wave_incl_scan(f);
   if (lane == 63) {
@@ -132,13 +135,13 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
   }
   __syncthreads();
   int bc = 0, bf = 0, tc = 0, tf = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) {
-      bc += wtot[0][w];
-      bf += wtot[1][w];
+  for (int v = 0; v < 16; ++v) {
+    if (v < wave) {
+      bc += wtot[0][v];
+      bf += wtot[1][v];
     }
-    tc += wtot[0][w];
-    tf += wtot[1][w];
+    tc += wtot[0][v];
+    tf += wtot[1][v];
   }
   const int xc = bc + ic - c, xf = bf + iff - f;  // exclusive prefixes
   if (tid < E) {
@@ -148,9 +151,8 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
       a.act_e[xf] = tid;
       a.act_off[xf] = xc;
       a.act_cnt[xf] = c;
-      const int s = a.table[tid];
-      const bool ok = s >= 0 && s < a.n_slots;
-      a.act_slot[xf] = ok ? s : -1;
+      const bool ok = slot >= 0 && slot < a.n_slots;
+      a.act_slot[xf] = ok ? slot : -1;
       if (!ok) set_error(a.err, EDGE0_ERANGE);
     }
   }
@@ -159,15 +161,12 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
     a.info[1] = tc;
   }
   __syncthreads();
-  for (int p = tid; p < P; p += 1024) {
-    const int e = ids_s[p];
-    if (e < 0) continue;
-    int rank = 0;
-    for (int q = 0; q < p; ++q) rank += ids_s[q] == e;
-    const int dst = first[e] + rank;
-    a.pair_tok[dst] = p / a.K;
+  if (e >= 0) {
+    // rank among the expert's pairs = its earlier tokens (pairs are in token order)
+    const int dst = first[e] + __popcll(tok_mask[e] & ((1ull << t) - 1ull));
+    a.pair_tok[dst] = t;
     a.pair_act[dst] = actidx[e];
-    a.pair_w[dst] = w_s[p];
+    a.pair_w[dst] = w;
   }
 }
 

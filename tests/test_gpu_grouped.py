@@ -2,7 +2,7 @@
 the oracle, which defines it token by token: y_j = sum_k w_jk FFN_{e_jk}(x_j).
 Every token's output is compared (rel-L2 <= 2e-3), for the tiny shape
 (many tokens per expert, several token batches, a ragged last batch) and the
-Qwen3-MoE shape at K = 8 with 1, 4, 8, 16 and 32 tokens and Zipf(1.1)
+Qwen3-MoE shape at K = 8 with 1, 4, 8, 16, 32 and 64 tokens and Zipf(1.1)
 routing; the default path (MFMA tiles of up to 16 tokens for every expert
 from 4 tokens per call on, GEMVs below), the GEMV path (at most 8 of an
 expert's tokens per workgroup), the mixed path (tiles for experts with >= 16
@@ -81,7 +81,7 @@ def test_grouped_tiny(torch_cuda, T):
     _paths_ran(ys, ids, np.bincount(ids.ravel(), minlength=S.n_experts))
 
 
-@pytest.mark.parametrize("T", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("T", [1, 4, 8, 16, 32, 64])
 def test_grouped_qwen3moe_k8(torch_cuda, T):
     S = G.QWEN3_MOE.with_k(8)
     lay = _layer(S)
