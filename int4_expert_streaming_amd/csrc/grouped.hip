@@ -7,11 +7,12 @@
 // LoRA, Figure 1 sum node); the grouping only reorders the work.
 //
 // Launches (all on the caller's stream):
-//   k_grp_route   : one workgroup buckets the T*K (token, k) pairs by expert
-//                   (counting sort, stable in pair order, so by token), lists
-//                   the active experts with their first pair and count, and
-//                   resolves each active expert's slot once.
-//   k_grp_lora_in : t = A x for every pair's gate and up adapters.
+//   k_grp_route_lora : workgroup 0 buckets the T*K (token, k) pairs by
+//                   expert (counting sort, stable in pair order, so by
+//                   token), lists the active experts with their first pair
+//                   and count, and resolves each active expert's slot once;
+//                   the other workgroups compute t = A x for every pair's
+//                   gate and up adapters.
 //   k_grp_gu_tile : one workgroup = 16 rows of one active expert's gate and
 //                   up for a tile of up to 16 of its tokens, on MFMA
 //                   (16x16x32 bf16 against the exact 128 + q nibble values);
@@ -58,9 +59,9 @@ struct GrpArgs {
   int32_t* act_cnt;   // [Amax]
   int32_t* act_slot;  // [Amax] slot, or -1
   int32_t* pair_tok;  // [P] token of each sorted pair
-  int32_t* pair_act;  // [P] active expert of each sorted pair
+  int32_t* pair_src;  // [P] each sorted pair's unsorted index (token * K + k)
   float* pair_w;      // [P] routing weight of each sorted pair
-  float* t_in;        // [P][2][r]
+  float* t_in;        // [P][2][r] by unsorted pair
   uint16_t* hp_hi;    // [P][I] pair-permuted
   uint16_t* hp_lo;
   float* hs;                   // [P][I/16]
@@ -87,10 +88,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // within one token's routing is kept once, at its first k, with the
 // repeats' weights added to it in k order (w1 D(x) + w2 D(x) = (w1 + w2)
 // D(x)), so an expert holds at most one pair per token.
-__global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
+__device__ __forceinline__ void grp_route(const GrpArgs& a) {
   __shared__ unsigned long long tok_mask[1024];  // per expert: the tokens that chose it
   __shared__ int first[1024];
-  __shared__ int actidx[1024];
   __shared__ int ids_s[kGrpMaxTokens * 16];
   __shared__ float w_s[kGrpMaxTokens * 16];
   __shared__ int wtot[2][16];
@@ -146,7 +146,6 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
   const int xc = bc + ic - c, xf = bf + iff - f;  // exclusive prefixes
   if (tid < E) {
     first[tid] = xc;
-    actidx[tid] = xf;
     if (f) {
       a.act_e[xf] = tid;
       a.act_off[xf] = xc;
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(1024) void k_grp_route(GrpArgs a) {
     // rank among the expert's pairs = its earlier tokens (pairs are in token order)
     const int dst = first[e] + __popcll(tok_mask[e] & ((1ull << t) - 1ull));
     a.pair_tok[dst] = t;
-    a.pair_act[dst] = actidx[e];
+    a.pair_src[dst] = tid;
     a.pair_w[dst] = w;
   }
 }
@@ -176,20 +175,30 @@ __device__ __forceinline__ const uint8_t* grp_bundle(const GrpArgs& a, int act) 
 }
 
 // ------------------------------------------------------------ LoRA A x
-// one wave per row (sorted pair q, projection p, rank row rr)
-__global__ __launch_bounds__(256) void k_grp_lora_in(GrpArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+// t = A x for every (token, k) pair in the callers' order, which needs only
+// the ids and the slot table: these workgroups run beside the bucketing in
+// the same launch.  One wave per row (pair p, projection j, rank row rr).
+__device__ __forceinline__ void grp_lora_in(const GrpArgs& a, int wg) {
   const int r = a.r;
-  const int q = row / (2 * r), p = (row / r) & 1, rr = row % r;
-  if (q >= a.info[1]) return;
-  const uint8_t* b = grp_bundle(a, a.pair_act[q]);
+  const int row = wg * 16 + (threadIdx.x >> 6);
+  const int p = row / (2 * r), j = (row / r) & 1, rr = row % r;
+  if (p >= a.P) return;
+  const int e = a.ids[p];
+  const int s = (e >= 0 && e < a.E) ? a.table[e] : -1;
   float t = 0.f;
-  if (b != nullptr) {
+  if (s >= 0 && s < a.n_slots) {  // otherwise the bucketing reports the pair
+    const uint8_t* b = a.pool + (size_t)s * (size_t)a.slot_bytes;
     const uint16_t* wrow =
-        reinterpret_cast<const uint16_t*>(b + (p ? a.lay.a_up : a.lay.a_gate)) + (size_t)rr * a.d;
-    t = row_dot<false, false>(wrow, a.x + (size_t)a.pair_tok[q] * a.d, a.d);
+        reinterpret_cast<const uint16_t*>(b + (j ? a.lay.a_up : a.lay.a_gate)) + (size_t)rr * a.d;
+    t = row_dot<false, false>(wrow, a.x + (size_t)(p / a.K) * a.d, a.d);
   }
   if ((threadIdx.x & 63) == 0) a.t_in[row] = t;
+}
+
+// workgroup 0: the bucketing; workgroups 1.. (16 waves each): LoRA A x
+__global__ __launch_bounds__(1024) void k_grp_route_lora(GrpArgs a) {
+  if (blockIdx.x == 0) grp_route(a);
+  else if (a.r > 0) grp_lora_in(a, blockIdx.x - 1);
 }
 
 // position of element i of h in the pair-permuted order of its 8-group
@@ -340,8 +349,9 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
       }
       float tg = 0.f, tu = 0.f;
       if (has_l) {
-        tg = a.t_in[((size_t)q * 2 + 0) * r + lane];
-        tu = a.t_in[((size_t)q * 2 + 1) * r + lane];
+        const int src = a.pair_src[q];
+        tg = a.t_in[((size_t)src * 2 + 0) * r + lane];
+        tu = a.t_in[((size_t)src * 2 + 1) * r + lane];
       }
       const Q4Consts kq = q4_consts();
 #pragma unroll
@@ -552,6 +562,11 @@ __device__ __forceinline__ int tile_pair_tok(const GrpArgs& a, int q) {
       (const __attribute__((address_space(4))) int32_t*)a.pair_tok;
   return p[q];
 }
+__device__ __forceinline__ int tile_pair_src(const GrpArgs& a, int q) {
+  const __attribute__((address_space(4))) int32_t* p =
+      (const __attribute__((address_space(4))) int32_t*)a.pair_src;
+  return p[q];
+}
 
 // Gate/up: workgroup (tile, active expert, 16-row block).  The 4 waves split
 // the d inputs into quarters of GW groups (NW = GW * WPG words per lane per
@@ -619,7 +634,8 @@ __device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int 
     }
     for (int t = tid; t < kTileTok * 2 * r; t += 256) {
       const int m = t / (2 * r), rem = t % (2 * r);
-      sm.tl[m][rem / r][rem % r] = m < mt ? a.t_in[(size_t)(q0 + t0 + m) * 2 * r + rem] : 0.f;
+      const int src = tile_pair_src(a, q0 + t0 + min(m, mt - 1));
+      sm.tl[m][rem / r][rem % r] = m < mt ? a.t_in[(size_t)src * 2 * r + rem] : 0.f;
     }
   }
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
@@ -901,7 +917,7 @@ __global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
 
 // ------------------------------------------------------------- host side
 struct GrpWs {
-  size_t err, info, act_e, act_off, act_cnt, act_slot, pair_tok, pair_act, pair_w, t_in, hp_hi,
+  size_t err, info, act_e, act_off, act_cnt, act_slot, pair_tok, pair_src, pair_w, t_in, hp_hi,
       hp_lo, hs, tdown, acc, total;
 };
 static GrpWs grp_ws_layout(const edge0_moe_shape* s) {
@@ -922,7 +938,7 @@ static GrpWs grp_ws_layout(const edge0_moe_shape* s) {
   L.act_cnt = take(4 * A);
   L.act_slot = take(4 * A);
   L.pair_tok = take(4 * P);
-  L.pair_act = take(4 * P);
+  L.pair_src = take(4 * P);
   L.pair_w = take(4 * P);
   L.t_in = take(4 * P * 2 * r);
   L.hp_hi = take(2 * P * I);
@@ -1070,7 +1086,7 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
   a.act_cnt = reinterpret_cast<int32_t*>(ws + L.act_cnt);
   a.act_slot = reinterpret_cast<int32_t*>(ws + L.act_slot);
   a.pair_tok = reinterpret_cast<int32_t*>(ws + L.pair_tok);
-  a.pair_act = reinterpret_cast<int32_t*>(ws + L.pair_act);
+  a.pair_src = reinterpret_cast<int32_t*>(ws + L.pair_src);
   a.pair_w = reinterpret_cast<float*>(ws + L.pair_w);
   a.t_in = reinterpret_cast<float*>(ws + L.t_in);
   a.hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
@@ -1078,12 +1094,8 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
   a.hs = reinterpret_cast<float*>(ws + L.hs);
   a.tdown = reinterpret_cast<unsigned long long*>(ws + L.tdown);
   a.acc = reinterpret_cast<unsigned long long*>(ws + L.acc);
-  k_grp_route<<<1, 1024, 0, stream>>>(a);
+  k_grp_route_lora<<<1 + (a.r > 0 ? (a.P * 2 * a.r + 15) / 16 : 0), 1024, 0, stream>>>(a);
   E0_CHECK_LAUNCH();
-  if (a.r > 0) {
-    k_grp_lora_in<<<(a.P * 2 * a.r + 3) / 4, 256, 0, stream>>>(a);
-    E0_CHECK_LAUNCH();
-  }
   // experts with >= tile_min tokens on the MFMA token tiles, the others as
   // GEMVs.  Default: every expert on the tiles from kTileMinCall tokens per
   // call on (below that the GEMVs' shorter chains win).  An expert holds at
