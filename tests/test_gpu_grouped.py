@@ -174,3 +174,16 @@ def test_grouped_repeated_ids(torch_cuda):
         y, _ = _call(lay, ids, w, x, flags)
         worst = _check(lay, ids, w, x, y)
         print(f"[grouped] tiny repeated ids flags={flags:#x}: worst rel-L2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 17), ("qwen3moe_k8", 8)])
+def test_grouped_without_lora(torch_cuda, name, T):
+    """lora_rank 0: no adapter terms on any path (tiles and GEMV)."""
+    S = G.TINY if name == "tiny" else G.QWEN3_MOE.with_k(8)
+    lay = DeviceLayer(S, seed=6, layer=1, lora=False)
+    ids, w = G.grouped_routing(S.n_experts, S.top_k, T, seed=40 + T)
+    x = G.hidden(S, 60 + T, n=T)
+    for flags in FLAG_SETS:
+        y, _ = _call(lay, ids, w, x, flags)
+        worst = _check(lay, ids, w, x, y)
+        print(f"[grouped] {name} no LoRA T={T} flags={flags:#x}: worst rel-L2 {worst:.3e}")
