@@ -580,7 +580,7 @@ __device__ __forceinline__ int tile_pair_src(const GrpArgs& a, int q) {
 // the grid's ceil(T / tm) tiles cover it and a workgroup has one tile:
 // straight-line code, nothing loop-carried.
 struct GuTileLds {
-  float red[4][2][kTileTok][kTileTok + 1];
+  float4 red[kTileTok][kTileTok][2];  // [token][row]: gate then up partials of the 4 waves
   float bl[2][kTileTok][kTileRank];
   float tl[kTileTok][2][kTileRank];
   float h[kTileTok][kTileTok + 1];
@@ -627,15 +627,17 @@ __device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int 
       lora ? b + a.lay.a_down + ((size_t)min(rr, r - 1) * I + i0) * 2 : b + a.lay.gate_q);
   const uint4 ad0 = adp[0], ad1 = adp[1];
   if (lora) {
-    for (int t = tid; t < 2 * 16 * r; t += 256) {
-      const int p = t / (16 * r), rem = t % (16 * r);
+    // rank entries past r are zero, so the epilogue's dot runs over
+    // kTileRank entries with every read issued at once
+    for (int t = tid; t < 2 * 16 * kTileRank; t += 256) {
+      const int p = t / (16 * kTileRank), rw = (t / kTileRank) % 16, k = t % kTileRank;
       const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate));
-      sm.bl[p][rem / r][rem % r] = bf2f(B[(size_t)(i0 + rem / r) * r + rem % r]);
+      sm.bl[p][rw][k] = k < r ? bf2f(B[(size_t)(i0 + rw) * r + k]) : 0.f;
     }
-    for (int t = tid; t < kTileTok * 2 * r; t += 256) {
-      const int m = t / (2 * r), rem = t % (2 * r);
+    for (int t = tid; t < kTileTok * 2 * kTileRank; t += 256) {
+      const int m = t / (2 * kTileRank), p = (t / kTileRank) & 1, k = t % kTileRank;
       const int src = tile_pair_src(a, q0 + t0 + min(m, mt - 1));
-      sm.tl[m][rem / r][rem % r] = m < mt ? a.t_in[(size_t)src * 2 * r + rem] : 0.f;
+      sm.tl[m][p][k] = m < mt && k < r ? a.t_in[((size_t)src * 2 + p) * r + k] : 0.f;
     }
   }
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
@@ -664,17 +666,19 @@ __device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int 
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    sm.red[wave][0][4 * j + v][n] = accG[v];
-    sm.red[wave][1][4 * j + v][n] = accU[v];
+    reinterpret_cast<float*>(&sm.red[4 * j + v][n][0])[wave] = accG[v];
+    reinterpret_cast<float*>(&sm.red[4 * j + v][n][1])[wave] = accU[v];
   }
   __syncthreads();
   const int m = tid >> 4, rn = tid & 15;  // the 16 threads of token m are one DPP row
   {
-    float Gv = sm.red[0][0][m][rn] + sm.red[1][0][m][rn] + sm.red[2][0][m][rn] + sm.red[3][0][m][rn];
-    float Uv = sm.red[0][1][m][rn] + sm.red[1][1][m][rn] + sm.red[2][1][m][rn] + sm.red[3][1][m][rn];
+    const float4 pg = sm.red[m][rn][0], pu = sm.red[m][rn][1];
+    float Gv = pg.x + pg.y + pg.z + pg.w;
+    float Uv = pu.x + pu.y + pu.z + pu.w;
     if (lora) {
       float dg = 0.f, du = 0.f;
-      for (int k = 0; k < r; ++k) {
+#pragma unroll
+      for (int k = 0; k < kTileRank; ++k) {
         dg += sm.bl[0][rn][k] * sm.tl[m][0][k];
         du += sm.bl[1][rn][k] * sm.tl[m][1][k];
       }
@@ -746,7 +750,7 @@ __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, in
                                           int mt, int tm, int rb,
                                           const uint32_t (&wd)[kDownNT][NW], Q4Consts kq,
                                           uint16_t* hsm, float (&gsum)[kTileTok][NW / WPG],
-                                          float (&td_s)[kTileTok][kTileRank + 1]) {
+                                          float (&td_s)[kTileTok][kTileRank]) {
   constexpr int GD = NW / WPG, NT = kDownNT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
@@ -813,9 +817,9 @@ __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, in
     gsum[m][G] = s;
   }
   if (lora) {
-    for (int t = tid; t < tm * r; t += 256) {
-      const int m = t / r, k = t % r;
-      td_s[m][k] = m < mt ? from_fix(a.tdown[(size_t)(q0 + t0 + m) * r + k]) : 0.f;
+    for (int t = tid; t < tm * kTileRank; t += 256) {
+      const int m = t / kTileRank, k = t % kTileRank;
+      td_s[m][k] = m < mt && k < r ? from_fix(a.tdown[(size_t)(q0 + t0 + m) * r + k]) : 0.f;
     }
   }
   __syncthreads();
@@ -859,8 +863,7 @@ __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, in
           float dl = 0.f;
 #pragma unroll
           for (int k = 0; k < kTileRank / 2; ++k)
-            if (2 * k < r)
-              dl += bf_lo(bdw[t][k]) * td_s[m][2 * k] + bf_hi(bdw[t][k]) * td_s[m][2 * k + 1];
+            dl += bf_lo(bdw[t][k]) * td_s[m][2 * k] + bf_hi(bdw[t][k]) * td_s[m][2 * k + 1];
           tot += a.scale * dl;
         }
         const int o = (rb * NT + t) * 64 + 16 * wave + n;
@@ -875,7 +878,7 @@ __global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int
   constexpr int GD = NW / WPG;
   extern __shared__ __align__(16) uint16_t hsm[];
   __shared__ float gsum[kTileTok][GD];
-  __shared__ float td_s[kTileTok][kTileRank + 1];
+  __shared__ float td_s[kTileTok][kTileRank];  // zero past the rank
   const int nrb = a.d / (64 * kDownNT);
   const int tt = blockIdx.x / (a.Amax * nrb);
   const int act = (blockIdx.x / nrb) % a.Amax;
