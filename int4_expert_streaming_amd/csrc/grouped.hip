@@ -583,7 +583,7 @@ struct GuTileLds {
   float4 red[kTileTok][kTileTok][2];  // [token][row]: gate then up partials of the 4 waves
   float bl[2][kTileTok][kTileRank];
   float tl[kTileTok][2][kTileRank];
-  float h[kTileTok][kTileTok + 1];
+  float h[kTileTok][kTileTok];  // read back as whole rows (float4)
 };
 
 template <int GW, int WPG>
