@@ -247,7 +247,9 @@ constexpr int kGrpXBytes = 32768;
 // the expert's tokens [ts * slice, ts * slice + ts): an expert chosen by many
 // tokens is spread over several workgroups (each reads its rows again) and
 // no longer sets the time alone.
-template <int NJ>
+// FULL: d = 2048 NJ, every lane's chunks exist (no per-lane guard on the
+// loads, which the compiler would turn into branches that wait for them).
+template <int NJ, bool FULL>
 __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int max_cnt,
                                                      int ts) {
   __shared__ uint16_t xs[kGrpXBytes / 2];
@@ -257,14 +259,12 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
   const int sl = blockIdx.x / (a.Amax * nblk);
   const int act = (blockIdx.x / nblk) % a.Amax;
   const int blk = blockIdx.x % nblk;
-  if (act >= a.info[0]) return;
-  const int n = a.act_cnt[act];
-  if (n < min_cnt || n > max_cnt) return;
+  // everything the start depends on, in one round trip
+  const int n_act = a.info[0], n = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
+  asm volatile("" ::"s"(n_act), "s"(n), "s"(slot), "s"(q0));
   const int t_lo = sl * ts, t_hi = min(n, t_lo + ts);  // n <= T: the slices cover it
-  if (t_lo >= n) return;
-  const uint8_t* b = grp_bundle(a, act);
-  if (b == nullptr) return;
-  const int q0 = a.act_off[act];
+  if (act >= n_act || n < min_cnt || n > max_cnt || t_lo >= n || slot < 0) return;
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int d = a.d, g = a.g, ng = d / g, r = a.r, cpr = d / 32;
   const int i0 = blk * 16, row0 = i0 + 4 * wave;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = lane + 64 * j;
-      const bool on = col < cpr;
+      const bool on = FULL || col < cpr;
       const int cc = on ? col : 0;
       qg[ii][j] = on ? reinterpret_cast<const uint4*>(gq + (size_t)row * (d / 8))[cc]
                      : make_uint4(0, 0, 0, 0);
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
       for (int j = 0; j < NJ; ++j) {
         const int col = lane + 64 * j;
         XRaw xr;
-        if (col < cpr) {
+        if (FULL || col < cpr) {
           const uint4* src = reinterpret_cast<const uint4*>(xs + (size_t)jj * d + 32 * col);
 #pragma unroll
           for (int m = 0; m < 4; ++m) xr.v[m] = src[m];
@@ -968,8 +968,14 @@ static int grp_slices(const GrpArgs& a) {
 static int launch_grp_gate_up(const GrpArgs& a, int lo, int hi, hipStream_t st) {
   const int grid = grp_slices(a) * a.Amax * (a.I / 16), ts = kGrpSliceTokens;
   switch ((a.d / 32 + 63) / 64) {
-    case 1: k_grp_gate_up<1><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
-    case 2: k_grp_gate_up<2><<<grid, 256, 0, st>>>(a, lo, hi, ts); break;
+    case 1:
+      if (a.d == 2048) k_grp_gate_up<1, true><<<grid, 256, 0, st>>>(a, lo, hi, ts);
+      else k_grp_gate_up<1, false><<<grid, 256, 0, st>>>(a, lo, hi, ts);
+      break;
+    case 2:
+      if (a.d == 4096) k_grp_gate_up<2, true><<<grid, 256, 0, st>>>(a, lo, hi, ts);
+      else k_grp_gate_up<2, false><<<grid, 256, 0, st>>>(a, lo, hi, ts);
+      break;
     default: return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();
