@@ -169,11 +169,6 @@ __device__ __forceinline__ void grp_route(const GrpArgs& a) {
   }
 }
 
-__device__ __forceinline__ const uint8_t* grp_bundle(const GrpArgs& a, int act) {
-  const int s = a.act_slot[act];
-  return s < 0 ? nullptr : a.pool + (size_t)s * (size_t)a.slot_bytes;
-}
-
 // ------------------------------------------------------------ LoRA A x
 // t = A x for every (token, k) pair in the callers' order, which needs only
 // the ids and the slot table: these workgroups run beside the bucketing in
@@ -400,14 +395,12 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
   const int sl = blockIdx.x / (a.Amax * nrb);
   const int act = (blockIdx.x / nrb) % a.Amax;
   const int rb = blockIdx.x % nrb;
-  if (act >= a.info[0]) return;
-  const int n = a.act_cnt[act];
-  if (n < min_cnt || n > max_cnt) return;
+  // everything the start depends on, in one round trip
+  const int n_act = a.info[0], n = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
+  asm volatile("" ::"s"(n_act), "s"(n), "s"(slot), "s"(q0));
   const int t_lo = sl * ts, t_hi = min(n, t_lo + ts);
-  if (t_lo >= n) return;
-  const uint8_t* b = grp_bundle(a, act);
-  if (b == nullptr) return;
-  const int q0 = a.act_off[act];
+  if (act >= n_act || n < min_cnt || n > max_cnt || t_lo >= n || slot < 0) return;
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int d = a.d, I = a.I, r = a.r, NC = I / 32;
   const int o = rb * 64 + lane;
