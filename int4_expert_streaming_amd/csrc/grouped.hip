@@ -20,15 +20,17 @@
 //                   and A_down h accumulated in fixed point per pair.
 //   k_grp_gate_up : the same as multi-token GEMVs (rows in registers, at most
 //                   8 tokens per workgroup), for calls of few tokens.
-//   k_grp_down_tile / k_grp_down : one workgroup = 64 output rows of one
-//                   active expert (tile on MFMA, or GEMV); the LoRA-down
-//                   delta; each token's weighted row added to its
-//                   fixed-point output.
+//   k_grp_down_tile / k_grp_down : one workgroup = 128 output rows of one
+//                   active expert for a tile of its tokens on MFMA, or 64
+//                   rows for at most 8 tokens as GEMVs; the LoRA-down delta;
+//                   each token's weighted row added to its fixed-point
+//                   output.
 //   k_grp_out     : y = bf16 of each token's accumulator; clears the
 //                   accumulators for the next call.
 // Int4 arithmetic is the single-token path's: exact bf16 "128 + q" nibble
 // pairs against pair-permuted activations, the group affine folded per
-// 32-input chunk, fp32 everywhere, one bf16 rounding of y.
+// 32-input chunk (per group on MFMA), fp32 accumulation, one bf16 rounding
+// of y.
 #include <algorithm>
 
 #include "moe_internal.h"
