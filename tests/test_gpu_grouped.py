@@ -187,3 +187,19 @@ def test_grouped_without_lora(torch_cuda, name, T):
         y, _ = _call(lay, ids, w, x, flags)
         worst = _check(lay, ids, w, x, y)
         print(f"[grouped] {name} no LoRA T={T} flags={flags:#x}: worst rel-L2 {worst:.3e}")
+
+
+def test_grouped_most_pairs(torch_cuda):
+    """64 tokens with K = E = 16 on the tiny shape: 1024 pairs (the most a
+    call holds), every expert chosen by every token, so each expert spans
+    four 16-token tiles."""
+    S = G.TINY.with_k(16)
+    lay = DeviceLayer(S, seed=8, layer=2)
+    T = 64
+    ids, w = G.grouped_routing(S.n_experts, 16, T, seed=77)
+    assert all(len(set(row.tolist())) == 16 for row in ids)
+    x = G.hidden(S, 90, n=T)
+    for flags in FLAG_SETS:
+        y, _ = _call(lay, ids, w, x, flags)
+        worst = _check(lay, ids, w, x, y)
+        print(f"[grouped] tiny K=16 T=64 flags={flags:#x}: worst rel-L2 {worst:.3e}")
