@@ -357,7 +357,7 @@ def bench_grouped(args, log):
         flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
         results[T] = {"us_per_call": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
                       "experts": round(union, 2),
-                      "path": "mfma tiles" if T >= 4 else "gemv",
+                      "path": "mfma tiles" if T >= 3 else "gemv",
                       "union_bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                       "tflops": round(flops / (us * 1e-6) / 1e12, 3)}

@@ -214,7 +214,7 @@ int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
  * "Math contract", §3.3); the grouping only reorders the work.  The (token,
  * k) pairs are bucketed by expert on the device (counting sort, stable by
  * token; an id repeated within a token's routing is kept once with the
- * repeats' weights added).  From 4 tokens per call on, every expert's
+ * repeats' weights added).  From 3 tokens per call on, every expert's
  * products run on MFMA in tiles of up to 16 of its tokens (bf16 operands
  * holding the exact 128 + q nibble values and the activations, fp32
  * accumulation, the group affine applied per group in fp32); smaller calls

@@ -518,7 +518,7 @@ __device__ __forceinline__ bf16x8_t q4_operand_k(uint32_t w, Q4Consts k) {
 }
 constexpr int kTileTok = 16;   // tokens per MFMA tile at most
 constexpr int kTileRank = 16;  // LoRA rank bound of the tile kernels
-constexpr int kTileMinCall = 4;  // default: tiles for calls of >= 4 tokens
+constexpr int kTileMinCall = 3;  // default: tiles for calls of >= 3 tokens (measured crossover)
 constexpr int kDownNT = 2;  // 64-row blocks per down workgroup (a 16-row n-tile each per wave)
 
 // N consecutive 32-bit words from p (p aligned to min(N, 4) words)

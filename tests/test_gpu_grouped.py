@@ -4,7 +4,7 @@ Every token's output is compared (rel-L2 <= 2e-3), for the tiny shape
 (many tokens per expert, several token batches, a ragged last batch) and the
 Qwen3-MoE shape at K = 8 with 1, 4, 8, 16, 32 and 64 tokens and Zipf(1.1)
 routing; the default path (MFMA tiles of up to 16 tokens for every expert
-from 4 tokens per call on, GEMVs below), the GEMV path (at most 8 of an
+from 3 tokens per call on, GEMVs below), the GEMV path (at most 8 of an
 expert's tokens per workgroup), the mixed path (tiles for experts with >= 16
 tokens) and the tiles for every expert; determinism; reuse of the workspace
 by a smaller call; one token alone equals its row of a grouped call; ids
