@@ -431,13 +431,30 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
   for (int j0 = t_lo; j0 < t_hi; j0 += kGrpBT) {
     const int nb = t_hi - j0 < kGrpBT ? t_hi - j0 : kGrpBT;
     __syncthreads();  // previous batch consumed
-    for (int t = threadIdx.x; t < nb * NC * 32; t += 256) {
-      const int jj = t / (NC * 32), rem = t % (NC * 32);
-      const int c = rem >> 5, wd = rem & 31;
-      const int q = q0 + j0 + jj;
-      const uint32_t* src =
-          reinterpret_cast<const uint32_t*>(wd < 16 ? a.hp_hi : a.hp_lo) + (size_t)q * (I / 2);
-      hp_s[jj][c][wd] = src[16 * c + (wd & 15)];
+    {
+      // the batch's h pairs, 16 bytes per thread and step: every load (at a
+      // clamped, in-range index) before any store
+      constexpr int kPer = kGrpBT * kGrpMaxNC * 32 / 4 / 256;
+      const int n4 = nb * NC * 8;  // 16-byte pieces
+      uint4 hv[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int t = min((int)threadIdx.x + 256 * u, n4 - 1);
+        const int jj = t / (NC * 8), rem = t % (NC * 8);
+        const int c = rem >> 3, w4 = rem & 7;  // pieces 0-3 hi pairs, 4-7 lo pairs
+        const uint4* src = reinterpret_cast<const uint4*>(
+            reinterpret_cast<const uint32_t*>(w4 < 4 ? a.hp_hi : a.hp_lo) +
+            (size_t)(q0 + j0 + jj) * (I / 2) + 16 * c);
+        hv[u] = src[w4 & 3];
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int t = threadIdx.x + 256 * u;
+        if (t < n4) {
+          const int jj = t / (NC * 8), rem = t % (NC * 8);
+          reinterpret_cast<uint4*>(hp_s[jj][rem >> 3])[rem & 7] = hv[u];
+        }
+      }
     }
     for (int t = threadIdx.x; t < nb * NC; t += 256) {
       const int jj = t / NC, c = t % NC;
