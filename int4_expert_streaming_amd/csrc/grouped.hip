@@ -1012,13 +1012,17 @@ static int launch_grp_down(const GrpArgs& a, int lo, int hi, hipStream_t st) {
 }
 
 // shapes of the token-tile kernels: d <= 2048, each wave quarter of d an
-// even number of groups of 32 or 64, I a multiple of 128 up to 1024 (a
-// tile's h fits 64 KiB of LDS), LoRA rank even and <= 16
+// even number of groups of 32 or 64, I / 32 one of the down-tile instances
+// (4, 8, 12, 16, 24, 32: I up to 1024, so a tile's h fits 64 KiB of LDS),
+// LoRA rank even and <= 16.  Every shape accepted here has an instance of
+// both tile kernels, so a call never fails after its first launch; other
+// shapes run as GEMVs.
 static bool grp_tile_ok(const GrpArgs& a) {
-  const int gw = a.d / (4 * a.g);
+  const int gw = a.d / (4 * a.g), nw = a.I / 32;
   return (a.g == 32 || a.g == 64) && a.d <= 2048 && a.d % (8 * a.g) == 0 &&
-         (gw == 2 || gw == 4 || gw == 8 || gw == 16) &&
-         a.I % 128 == 0 && a.I <= 1024 && a.r <= kTileRank && a.r % 2 == 0;
+         (gw == 2 || gw == 4 || gw == 8 || gw == 16) && a.I % 32 == 0 &&
+         (nw == 4 || nw == 8 || nw == 12 || nw == 16 || nw == 24 || nw == 32) &&
+         a.r <= kTileRank && a.r % 2 == 0;
 }
 
 // experts with >= min_cnt tokens

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 //    expert's t in t_hand; then the LoRA term and the SwiGLU epilogue.
 // ROUTE (a router layer): the producers first compute a.route_rows router
 // logits each from x and publish them through lg_hand (parity a.par; the
-// other parity's entries are emptied); every workgroup then commits the
+// down kernel that follows empties them again); every workgroup then commits the
 // top-K of the published logits itself (wave 0, bounded wait) before it
 // loads its expert's rows, and gate/up workgroup 0 stores the committed
 // ids/w.  Otherwise the routing (a.ids, a.w) is given and the rows are
@@ -816,6 +816,9 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
     // the layer kernel before this one has consumed the LoRA hand-off
     // entries: empty them for the next
     for (int i = threadIdx.x; i < K * 2 * r; i += 256) a.t_hand[i] = __uint_as_float(kTHandEmpty);
+    // and the router logits it read, if it was a router layer
+    if (a.lg_consumed != nullptr)
+      for (int i = threadIdx.x; i < a.E; i += 256) a.lg_consumed[i] = __uint_as_float(kTHandEmpty);
   }
   __syncthreads();  // every thread, unconditionally
   float part = 0.f;
@@ -938,6 +941,7 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->lg_hand = reinterpret_cast<float*>(ws + L.lg_hand);
   a->route_rows = 0;
   a->par = 0;
+  a->lg_consumed = nullptr;
   a->spin = kFusedDefaultSpin;
   a->hf = reinterpret_cast<float*>(ws + L.hf);
   a->hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);

@@ -47,6 +47,11 @@ struct MoeArgs {
   // written, the other parity's entries are emptied for the next router layer
   float* lg_hand;
   int route_rows, par;
+  // the E entries of lg_hand the launch before this layer's down kernel
+  // read (a router layer's logits), or NULL: the down kernel empties them,
+  // so every router layer finds both parities empty whatever the parities
+  // of the router layers before it
+  float* lg_consumed;
   int64_t spin;
 };
 constexpr uint32_t kTHandEmpty = 0xFFFFFFFFu;  // a NaN no stored value takes

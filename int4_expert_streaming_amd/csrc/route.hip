@@ -75,13 +75,24 @@ __global__ __launch_bounds__(256) void k_heads_fc1(HeadBatch hb) {
   if (pref) row_prefetch(wrow, d, pf);
   if (fc1) {
     // one-hot columns: lane j < K this token's ids, K <= j < 2K the previous
-    // token's (block offset E); loaded with the row
-    float g = 0.f;
+    // token's (block offset E); loaded with the row.  The blocks are binary
+    // multi-hots, so an id listed twice in one block sets its entry once:
+    // only its first listing in that block adds the column.
+    const bool prev = lane >= K;
+    int id = -1;
     if (lane < 2 * K) {
-      const bool prev = lane >= K;
+      const int32_t* src = prev ? hb.ids_prev : hb.ids_now;
+      if (src != nullptr) id = src[(size_t)i * hb.ids_stride + (prev ? lane - K : lane)];
+    }
+    bool first = true;
+    for (int j = 0; j < 2 * K; ++j) {
+      const int other = __shfl(id, j, kWave);
+      if (j < lane && (j >= K) == prev && other == id) first = false;
+    }
+    float g = 0.f;
+    if (lane < 2 * K && first) {
       const int32_t* src = prev ? hb.ids_prev : hb.ids_now;
       if (src != nullptr) {
-        const int id = src[(size_t)i * hb.ids_stride + (prev ? lane - K : lane)];
         if (id >= 0 && id < E) {
           g = h2f(hb.w1oh[i][(size_t)(prev ? E + id : id) * H + row]);
         } else {

@@ -145,7 +145,8 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
         lr.flags |= IN_LORA;
         lr.ids_out = ids;
         lr.w_out = w;
-        a.par = L & 1;  // parity of the logits hand-off (router layers alternate)
+        a.par = L & 1;  // parity of the logits hand-off
+        a.lg_consumed = a.lg_hand + (size_t)a.par * E;  // emptied again by the down kernel
         if ((rc = launch_layer_fused(a, lr, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
                 EDGE0_OK ||
             (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
@@ -648,6 +649,10 @@ extern "C" int edge0_stack_set_spin_limit(edge0_stack* st, int64_t polls) {
 
 extern "C" void edge0_stack_destroy(edge0_stack* st) {
   if (!st) return;
+  // the handle's launches (graphs, the persistent step, the capture stream)
+  // may still be running on the device: let them finish before their
+  // events, graphs, stream and buffers go
+  (void)hipDeviceSynchronize();
   for (auto e : st->ev_start) (void)hipEventDestroy(e);
   for (auto e : st->ev_stop) (void)hipEventDestroy(e);
   for (auto& g : st->graphs)

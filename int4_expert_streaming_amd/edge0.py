@@ -7,8 +7,10 @@ loudly if it has not been built.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
+import weakref
 
 import numpy as np
 import torch
@@ -32,6 +34,42 @@ def _load():
 
 
 lib = _load()
+
+# Handles still open at interpreter exit are closed by an exit hook that runs
+# before torch's own (hooks run last-registered first, and this module is
+# imported after torch): each destroy call synchronises the device first,
+# so no launch of a handle outlives its events, graphs or buffers, and no
+# destroy runs from a finaliser after the HIP runtime has shut down.
+_live = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live_handles():
+    for h in sorted(list(_live), key=lambda h: 0 if isinstance(h, Stager) else 1):
+        try:
+            h.close()
+        except Exception:
+            pass
+
+
+class _Handle:
+    """Context-manager and exit-hook behaviour of the opaque handles."""
+
+    def _register(self):
+        _live.add(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # --------------------------------------------------------------------- structs
@@ -245,7 +283,7 @@ def edge0_moe_grouped(shape: MoeShape, pool: SlotPool, slot_table, n_tokens: int
                                  _stream(stream)), "edge0_moe_grouped")
 
 
-class Stack:
+class Stack(_Handle):
     """Owner of an edge0_stack handle (decode stack runtime)."""
 
     def __init__(self, shape: MoeShape, spec: StackSpec, pool: SlotPool, slot_tables, routers,
@@ -259,6 +297,7 @@ class Stack:
         _check(lib.edge0_stack_create(C.byref(self._handle), C.byref(shape), C.byref(spec),
                                       C.byref(pool), _ptr(slot_tables), router_ptrs, head_arr),
                "edge0_stack_create")
+        self._register()
 
     def step(self, h0, h_out, step: int, stream=None):
         _check(lib.edge0_stack_step(self._handle, _ptr(h0), _ptr(h_out), step, _stream(stream)),
@@ -305,11 +344,6 @@ class Stack:
             lib.edge0_stack_destroy(self._handle)
             self._handle = C.c_void_p()
 
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
 
 
 def _i32(a) -> np.ndarray:
@@ -324,13 +358,14 @@ def _stats(s: StageStats) -> dict:
     return {k: int(getattr(s, k)) for k, _ in StageStats._fields_}
 
 
-class Lru:
+class Lru(_Handle):
     """Host-only slot replacement policy (edge0_lru_*)."""
 
     def __init__(self, n_slots: int, n_layers: int, n_experts: int):
         self._handle = C.c_void_p()
         _check(lib.edge0_lru_create(C.byref(self._handle), n_slots, n_layers, n_experts),
                "edge0_lru_create")
+        self._register()
 
     def request(self, layer: int, step: int, ids):
         """-> (slots, hit flags, evicted keys), each an int32 array."""
@@ -354,14 +389,9 @@ class Lru:
             lib.edge0_lru_destroy(self._handle)
             self._handle = C.c_void_p()
 
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
 
 
-class Stager:
+class Stager(_Handle):
     """Owner of an edge0_stager handle: the LRU pool plus host-to-device staging."""
 
     def __init__(self, shape: MoeShape, pool: SlotPool, n_layers: int, host_ptrs, slot_table):
@@ -370,6 +400,7 @@ class Stager:
         self._handle = C.c_void_p()
         _check(lib.edge0_stager_create(C.byref(self._handle), C.byref(shape), C.byref(pool),
                                        n_layers, arr, _ptr(slot_table)), "edge0_stager_create")
+        self._register()
 
     def stage(self, layer: int, step: int, ids, stream=None) -> np.ndarray:
         ids = _i32(ids)
@@ -403,11 +434,6 @@ class Stager:
             lib.edge0_stager_destroy(self._handle)
             self._handle = C.c_void_p()
 
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
 
 
 def stack_step_staged(stack: "Stack", stager: Stager, h0, h_out, step: int, ids_dev, ids_host,

@@ -21,9 +21,10 @@ Decisions taken on floating point: routing ranks experts on the logits
 rounded to fp32 (the precision the GPU ranks in), ties to the lower index.
 
 Readings of points the pages leave open are stated where they are used and
-listed with the design notes.  Parity unpinned: none of the functions here
-(each is pinned by the CPU tests); prediction quality of the heads is not a
-property of this code (heads are random).
+listed with the design notes.  Every function here is pinned by CPU tests
+(tests/test_oracle_pins.py; topk_gap, which decides the near-tie waivers, in
+tests/test_tolerances.py).  Not a property of this code, and so not pinned:
+the prediction quality of the heads (their weights are random).
 """
 from __future__ import annotations
 

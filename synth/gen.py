@@ -10,7 +10,10 @@ Distributions (the pages give the shapes, the configs give the ranges):
   * int4 codes q ~ U{0..15}; a uniformly random u32 word is eight independent
     uniform nibbles, so packed weights are drawn as random words directly.
   * group scale s ~ U[0.005, 0.02] (bf16); group bias b = -8*s (exact in bf16),
-    so dequantised weights s*q+b are centred on zero.
+    so dequantised weights s*q+b are centred on zero.  Opt-in variants for
+    the tests: a bias drawn independently of the scale, b ~ U[-0.16, 0.04]
+    (bf16), so a path that ignored b or derived it from s would show; and
+    another scale range (e.g. much smaller scales).
   * LoRA A ~ N(0, 0.02^2), B ~ N(0, 0.01^2) (bf16).
   * router W_r ~ N(0, 1/d) (bf16) so that a unit-RMS hidden state gives
     logits of roughly unit variance.
@@ -35,6 +38,7 @@ __all__ = [
     "pack_int4", "expert_tensors", "lora_tensors", "head_tensors",
     "router_weight", "hidden", "stack_hidden", "zipf_probs",
     "zipf_trace", "grouped_routing", "EXPERT_KEYS", "LORA_KEYS", "HEAD_KEYS", "StackGen",
+    "DEFAULT_SCALES", "FREE_BIAS_RANGE", "scale_pow2",
 ]
 
 
@@ -97,24 +101,34 @@ def pack_int4(q: np.ndarray) -> np.ndarray:
     return np.bitwise_or.reduce(q << shifts, axis=-1).astype(np.uint32)
 
 
-def _scales_biases(rng, rows, groups):
-    s = to_bf16_bits(rng.uniform(0.005, 0.02, size=(rows, groups)).astype(np.float32))
+DEFAULT_SCALES = (0.005, 0.02)
+FREE_BIAS_RANGE = (-0.16, 0.04)
+
+
+def _scales_biases(rng, rows, groups, scales=DEFAULT_SCALES, bias_rng=None):
+    s = to_bf16_bits(rng.uniform(scales[0], scales[1], size=(rows, groups)).astype(np.float32))
+    if bias_rng is not None:              # independent of s
+        b = to_bf16_bits(bias_rng.uniform(*FREE_BIAS_RANGE, size=(rows, groups)).astype(np.float32))
+        return s, b
     s_f = (s.astype(np.uint32) << 16).view(np.float32)
     b = to_bf16_bits(-8.0 * s_f)            # exact: a power-of-two multiple of a bf16 value
     return s, b
 
 
-def expert_tensors(shape: MoEShape, seed: int, layer: int, expert: int) -> dict:
+def expert_tensors(shape: MoEShape, seed: int, layer: int, expert: int, *,
+                   free_bias: bool = False, scales=DEFAULT_SCALES) -> dict:
     """The nine arrays of one expert bundle (gate, up, down x (q, s, b)).
 
     q: u32 [out][in/8]; s, b: bf16 bits [out][in/g].  gate/up are [I x d],
-    down is [d x I]."""
+    down is [d x I].  free_bias: b drawn from its own stream, independent of
+    s; scales: the range of s."""
     d, I, g = shape.d_model, shape.d_inter, shape.group
     out = {}
     for t, (name, rows, cols) in enumerate((("gate", I, d), ("up", I, d), ("down", d, I))):
         rng = rng_for(seed, _K_EXPERT, layer, expert, t)
+        brng = rng_for(seed, _K_EXPERT, layer, expert, t, 1) if free_bias else None
         out[name + "_q"] = rng.integers(0, 2**32, size=(rows, cols // 8), dtype=np.uint32)
-        out[name + "_s"], out[name + "_b"] = _scales_biases(rng, rows, cols // g)
+        out[name + "_s"], out[name + "_b"] = _scales_biases(rng, rows, cols // g, scales, brng)
     return out
 
 
@@ -163,6 +177,13 @@ def hidden(shape: MoEShape, seed: int, index: int = 0, n: int | None = None) -> 
     rng = rng_for(seed, _K_HIDDEN, index)
     size = (shape.d_model,) if n is None else (n, shape.d_model)
     return to_bf16_bits(rng.normal(0.0, 1.0, size=size).astype(np.float32))
+
+
+def scale_pow2(bits, k: int) -> np.ndarray:
+    """bf16 bit patterns times 2^k (exact for results inside the normal
+    range: only the exponent changes)."""
+    f = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return to_bf16_bits(np.ldexp(f, k).astype(np.float32))
 
 
 def stack_hidden(shape: MoEShape, seed: int, step: int) -> np.ndarray:
@@ -238,11 +259,11 @@ def grouped_routing(n_experts: int, k: int, n_tokens: int, seed: int, layer: int
 class StackGen:
     """Per-layer generator callables of a seeded synthetic stack."""
 
-    def __init__(self, shape: MoEShape, seed: int = 0):
-        self.S, self.seed = shape, seed
+    def __init__(self, shape: MoEShape, seed: int = 0, free_bias: bool = False):
+        self.S, self.seed, self.free_bias = shape, seed, free_bias
 
     def expert(self, L, e):
-        return expert_tensors(self.S, self.seed, L, e)
+        return expert_tensors(self.S, self.seed, L, e, free_bias=self.free_bias)
 
     def lora(self, L, e):
         return lora_tensors(self.S, self.seed, L, e)

@@ -5,8 +5,9 @@ state entering the layer and, on prediction-routed layers, the GPU's
 committed routing, so a near tie waived at one layer cannot cascade.  The
 small stack (tiny layer shape, 10 layers) is checked at every layer and also
 run free against the oracle; the 40-layer Qwen3-MoE-shaped stack - the one
-the benchmark times, in the same launch configuration - is checked on a
-sample of layers."""
+the benchmark times, in the same launch configuration - is checked at every
+layer of several steps, in both execution modes, at K = 4 and K = 8, and with
+group biases independent of the scales."""
 import numpy as np
 import pytest
 
@@ -76,10 +77,10 @@ def check_layer(S, gen, L, t, snap, prev_snap, owners, consumers, report):
     return rel
 
 
-def _run(ds, S, seed, steps, layers_of, owners, consumers):
+def _run(ds, S, seed, steps, layers_of, owners, consumers, free_bias=False):
     import torch
     from int4_expert_streaming_amd.weights import to_device
-    gen = G.StackGen(S, seed)
+    gen = G.StackGen(S, seed, free_bias=free_bias)
     h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
     prev, report, rels = None, [], []
     for t in range(steps):
@@ -139,17 +140,79 @@ def test_small_stack_free_running(torch_cuda):
     assert agree >= 0.9 * total
 
 
-@pytest.mark.timeout(900)
-def test_qwen3moe_stack_sampled_layers(torch_cuda):
+def _qwen3_stack(S, seed, free_bias=False):
     from int4_expert_streaming_amd.stackbuild import DeviceStack
+    return DeviceStack(S, G.StackGen(S, seed, free_bias=free_bias), 40, (6, 37), (7, 38))
+
+
+QWEN_OWNERS, QWEN_CONSUMERS = range(6, 38), range(7, 39)
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_stack_every_layer(torch_cuda):
+    """The 40-layer Qwen3-MoE-shaped stack in the configuration the benchmark
+    times (graph replay, K = 4), every layer of 3 steps teacher-forced."""
     S, seed = G.QWEN3_MOE, 0
-    owners, consumers = range(6, 38), range(7, 39)
-    ds = DeviceStack(S, G.StackGen(S, seed), 40, (6, 37), (7, 38))
-    sample = {0: [0, 5, 6, 7, 39], 1: [5, 6, 7, 8, 22, 37, 38, 39], 2: [7, 19, 38]}
-    report, rels = _run(ds, S, seed, 3, lambda t: sample[t], owners, consumers)
+    ds = _qwen3_stack(S, seed)
+    report, rels = _run(ds, S, seed, 3, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
+    assert ds.stack.error() == 0
     assert report.count("exact") >= 0.8 * len(report), report
-    print(f"[stack] qwen3moe: worst rel-L2 {max(rels):.3e}, median {np.median(rels):.3e}, "
+    print(f"[stack] qwen3moe graphs: worst rel-L2 {max(rels):.3e}, median {np.median(rels):.3e}, "
           f"waived {report.count('waived')}/{len(report)}")
+    ds.stack.close()
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_stack_free_bias_both_modes(torch_cuda):
+    """The same stack with group biases drawn independently of the scales
+    (b ~ U[-0.16, 0.04]), so a kernel that ignored b or derived it from s
+    fails: every layer of 3 steps in the graph mode, then every layer of 3
+    steps in the persistent mode (one cooperative launch per step)."""
+    from int4_expert_streaming_amd import edge0 as E
+    S, seed = G.QWEN3_MOE, 7
+    ds = _qwen3_stack(S, seed, free_bias=True)
+    for mode in (E.EDGE0_STACK_GRAPHS, E.EDGE0_STACK_PERSISTENT):
+        ds.stack.set_mode(mode)
+        report, rels = _run(ds, S, seed, 3, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS,
+                            free_bias=True)
+        assert ds.stack.error() == E.EDGE0_OK
+        assert report.count("exact") >= 0.8 * len(report), report
+        print(f"[stack] qwen3moe free bias mode {mode}: worst rel-L2 {max(rels):.3e}, "
+              f"median {np.median(rels):.3e}, waived {report.count('waived')}/{len(report)}")
+    ds.stack.close()
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_stack_k8_every_layer(torch_cuda):
+    """The 40-layer Qwen3-MoE-shaped stack at K = 8: every layer of 2 steps
+    in the graph mode, then 2 steps in the persistent mode."""
+    from int4_expert_streaming_amd import edge0 as E
+    S, seed = G.QWEN3_MOE.with_k(8), 2
+    ds = _qwen3_stack(S, seed)
+    for mode in (E.EDGE0_STACK_GRAPHS, E.EDGE0_STACK_PERSISTENT):
+        ds.stack.set_mode(mode)
+        report, rels = _run(ds, S, seed, 2, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
+        assert ds.stack.error() == E.EDGE0_OK
+        assert report.count("exact") >= 0.8 * len(report), report
+        print(f"[stack] qwen3moe K=8 mode {mode}: worst rel-L2 {max(rels):.3e}, "
+              f"waived {report.count('waived')}/{len(report)}")
+    ds.stack.close()
+
+
+# Router layers hand their logits between the workgroups of one launch; two
+# router-layer launches in a row with the same layer-index parity (1 then 5;
+# 6 then the next step's 0) must not see each other's logits.
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n_layers", [6, 7])
+def test_router_layers_same_parity_in_a_row(torch_cuda, n_layers):
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    S, seed = G.MoEShape(2048, 32, 384, 4, 64, 16, 32.0, 64), 13
+    owners, consumers = range(1, 4), range(2, 5)
+    ds = DeviceStack(S, G.StackGen(S, seed), n_layers, (1, 3), (2, 4), log=None)
+    report, rels = _run(ds, S, seed, 3, lambda t: range(n_layers), owners, consumers)
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[stack] router parity n_layers={n_layers}: worst rel-L2 {max(rels):.3e}")
+    ds.stack.close()
 
 
 # Wide layers run the fused layer kernel on every layer after step 0; its LoRA
@@ -174,23 +237,20 @@ def test_wide_stack_every_layer(torch_cuda, name):
 
 
 @pytest.mark.timeout(900)
-def test_qwen3moe_stack_persistent_sampled_layers(torch_cuda):
-    """The persistent mode (one cooperative launch for the 40 layers), the
-    configuration the benchmark times: router layers at step 0 and at 0-6 and
-    39, prediction-routed layers after, teacher-forced on sampled layers."""
+def test_qwen3moe_stack_persistent_every_layer(torch_cuda):
+    """The persistent mode (one cooperative launch for the 40 layers): router
+    layers at step 0 and at 0-6 and 39, prediction-routed layers after,
+    every layer of 4 steps teacher-forced."""
     from int4_expert_streaming_amd import edge0 as E
-    from int4_expert_streaming_amd.stackbuild import DeviceStack
     S, seed = G.QWEN3_MOE, 0
-    owners, consumers = range(6, 38), range(7, 39)
-    ds = DeviceStack(S, G.StackGen(S, seed), 40, (6, 37), (7, 38))
+    ds = _qwen3_stack(S, seed)
     ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
-    sample = {0: [0, 1, 6, 7, 20, 39], 1: [0, 5, 6, 7, 8, 22, 37, 38, 39],
-              2: [1, 7, 19, 38, 39], 3: [6, 7, 30]}
-    report, rels = _run(ds, S, seed, 4, lambda t: sample[t], owners, consumers)
+    report, rels = _run(ds, S, seed, 4, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
     assert ds.stack.error() == E.EDGE0_OK
     assert report.count("exact") >= 0.8 * len(report), report
     print(f"[stack] qwen3moe persistent: worst rel-L2 {max(rels):.3e}, median "
           f"{np.median(rels):.3e}, waived {report.count('waived')}/{len(report)}")
+    ds.stack.close()
 
 
 def test_persistent_mode_rejects_unsupported_shape(torch_cuda):

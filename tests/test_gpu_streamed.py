@@ -43,11 +43,11 @@ def _resident(events, ids_of, n_slots, n_layers, n_experts):
 
 
 def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of, keep_p=0.1,
-         copy_mode=0):
+         copy_mode=0, free_bias=False):
     import torch
     from int4_expert_streaming_amd.stackbuild import StreamedStack
     from int4_expert_streaming_amd.weights import to_device
-    gen = G.StackGen(S, seed)
+    gen = G.StackGen(S, seed, free_bias=free_bias)
     En, K = S.n_experts, S.top_k
     ss = StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
     ss.stager.set_copy_mode(copy_mode)
@@ -120,14 +120,22 @@ def test_small_streamed_stack_every_layer(torch_cuda, ahead, copy_mode):
 
 
 @pytest.mark.timeout(900)
-def test_qwen3moe_streamed_stack_sampled_layers(torch_cuda):
+def test_qwen3moe_streamed_stack_every_layer(torch_cuda):
     """12 Qwen3-MoE-shaped layers over a 64-slot pool (at most 36 pinned),
-    prediction arm: evictions from the second step on."""
-    sample = {0: [0, 2, 3, 11], 1: [2, 3, 4, 10], 2: [3, 6, 9, 11], 3: [1, 3, 8, 10]}
-    ss, worst = _run(G.QWEN3_MOE, 1, 12, (2, 9), (3, 10), 64, 4, True, lambda t: sample[t],
-                     keep_p=0.06)
+    prediction arm: evictions from the second step on; every layer of 4
+    steps, with group biases drawn independently of the scales."""
+    ss, worst = _run(G.QWEN3_MOE, 1, 12, (2, 9), (3, 10), 64, 4, True, lambda t: range(12),
+                     keep_p=0.06, free_bias=True)
     assert ss.stager.stats()["evictions"] > 0
     print(f"[streamed] qwen3moe: worst rel-L2 {worst:.3e}, {ss.stager.stats()}")
+
+
+@pytest.mark.parametrize("ahead", [True, False])
+def test_small_streamed_stack_free_bias(torch_cuda, ahead):
+    """The tiny staged stack with group biases independent of the scales."""
+    ss, worst = _run(G.TINY, 6, 10, (2, 7), (3, 8), 40, 4, ahead, lambda t: range(10),
+                     free_bias=True)
+    print(f"[streamed] tiny free bias ahead={ahead}: worst rel-L2 {worst:.3e}")
 
 
 def test_stager_rejects_pageable_host_memory(torch_cuda):
