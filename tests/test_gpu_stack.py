@@ -184,14 +184,18 @@ def test_qwen3moe_stack_free_bias_both_modes(torch_cuda):
 
 @pytest.mark.timeout(900)
 def test_qwen3moe_stack_k8_every_layer(torch_cuda):
-    """The 40-layer Qwen3-MoE-shaped stack at K = 8: every layer of 2 steps
-    in the graph mode, then 2 steps in the persistent mode."""
+    """The 40-layer Qwen3-MoE-shaped stack at K = 8: every layer of 3 steps
+    in the graph mode.  (The persistent mode refuses this shape: its 384
+    workgroups of 576 threads do not fit its co-residency rule.)"""
     from int4_expert_streaming_amd import edge0 as E
     S, seed = G.QWEN3_MOE.with_k(8), 2
     ds = _qwen3_stack(S, seed)
-    for mode in (E.EDGE0_STACK_GRAPHS, E.EDGE0_STACK_PERSISTENT):
+    with pytest.raises(E.Edge0Error) as ei:
+        ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
+    assert ei.value.code == E.EDGE0_EINVAL
+    for mode in (E.EDGE0_STACK_GRAPHS,):
         ds.stack.set_mode(mode)
-        report, rels = _run(ds, S, seed, 2, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
+        report, rels = _run(ds, S, seed, 3, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
         assert ds.stack.error() == E.EDGE0_OK
         assert report.count("exact") >= 0.8 * len(report), report
         print(f"[stack] qwen3moe K=8 mode {mode}: worst rel-L2 {max(rels):.3e}, "
