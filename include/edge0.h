@@ -52,7 +52,8 @@ enum {
   EDGE0_EHIP = -2,     /* a HIP runtime or launch error */
   EDGE0_ENOSLOT = -3,  /* every slot of the pool is pinned by pending sets */
   EDGE0_ERANGE = -4,   /* an expert id or slot index out of range */
-  EDGE0_ENOMEM = -5    /* an allocation owned by a handle failed */
+  EDGE0_ENOMEM = -5,   /* an allocation owned by a handle failed */
+  EDGE0_ESCRATCH = -6  /* the shape needs more scratch than the static workspace holds */
 };
 
 /* Returns a static string describing an EDGE0_* code. */
@@ -206,6 +207,31 @@ int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* head, const 
 int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                     const int32_t* slot_table, const int32_t* ids, const float* w,
                     const void* x, void* y, void* workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * edge0_moe_layer without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results as
+ * edge0_moe_layer, but the scratch (partial sums, LoRA factors, SwiGLU
+ * activations, the fixed-point accumulator, the error word) is a static
+ * device array of the library, EDGE0_STATIC_WORKSPACE_BYTES (1 MiB) per
+ * GPU, which each GPU the library runs on holds until the process ends.
+ * The call allocates and frees nothing.  Its first call on a device looks
+ * up that device's copy of the array and zero-fills it with a kernel on
+ * `stream`; calls leave it ready for the next.
+ *   error_out : device int32 (may be NULL): receives EDGE0_OK, or
+ *               EDGE0_ERANGE when an id or slot was out of range (that
+ *               expert's contribution was skipped), once the stream
+ *               reaches the end of the call.
+ * Returns EDGE0_ESCRATCH (nothing enqueued) when the shape's workspace
+ * (edge0_workspace_bytes) exceeds the static array.  Every call on one GPU
+ * shares its array: calls that may overlap on one GPU (several streams or
+ * threads) race and must be serialised by the caller.
+ * ---------------------------------------------------------------------- */
+#define EDGE0_STATIC_WORKSPACE_BYTES ((size_t)1 << 20)
+int edge0_moe_layer_noalloc(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                            const int32_t* slot_table, const int32_t* ids, const float* w,
+                            const void* x, void* y, int32_t* error_out, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
  * Several tokens through one MoE layer, grouped by expert.  Defined token by

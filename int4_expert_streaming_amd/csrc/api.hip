@@ -100,6 +100,7 @@ extern "C" const char* edge0_strerror(int code) {
     case EDGE0_ENOSLOT: return "every slot of the pool is pinned";
     case EDGE0_ERANGE: return "expert id or slot index out of range";
     case EDGE0_ENOMEM: return "out of memory";
+    case EDGE0_ESCRATCH: return "shape needs more scratch than the static workspace holds";
     default: return "unknown error";
   }
 }

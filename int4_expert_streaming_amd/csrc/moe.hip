@@ -38,6 +38,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gemv_dev.h"
 #include "moe_internal.h"
@@ -867,6 +868,11 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
 // h_out = bf16(h_res + y).  (In the stack the next layer's k_layer_in does it.)
 __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
   const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o == 0 && a.err_out != nullptr) {
+    // every kernel that may record an error ran before this one
+    *a.err_out = *a.err != 0u ? EDGE0_ERANGE : EDGE0_OK;
+    *a.err = 0u;
+  }
   if (o >= a.d) return;
   const uint32_t yb = f2bf(from_fix(a.acc[o]));
   a.y[o] = (uint16_t)yb;
@@ -942,6 +948,7 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->route_rows = 0;
   a->par = 0;
   a->lg_consumed = nullptr;
+  a->err_out = nullptr;
   a->spin = kFusedDefaultSpin;
   a->hf = reinterpret_cast<float*>(ws + L.hf);
   a->hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
@@ -1100,6 +1107,73 @@ extern "C" int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_po
   if (rc != EDGE0_OK) return rc;
   LayerIn li{};
   li.flags = IN_LORA;  // with r = 0 it only resolves the slots
+  if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+  if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
+  return launch_combine(a, stream);
+}
+
+// ------------------------------------------------- no-allocation variant
+// The single-layer call on a workspace the library holds itself: a file-scope
+// device array (one copy per GPU, alive until the process ends), for callers
+// that cannot allocate (code under graph capture, tight serving loops).  Its
+// device address is looked up once per device, with that device current,
+// and only that address is handed to kernels.
+namespace e0 {
+constexpr size_t kStaticScratchBytes = EDGE0_STATIC_WORKSPACE_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace e0
+
+static __device__ __align__(256) uint8_t scratch[e0::kStaticScratchBytes];
+
+namespace e0 {
+__global__ void k_zero_words(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+static bool g_scratch_zeroed[kMaxDevices];
+
+// the calling thread's current device's copy of `scratch`, zero-filled by a
+// kernel on `stream` the first time (the calls leave it ready for the next)
+static int static_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EDGE0_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return EDGE0_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    k_zero_words<<<64, 256, 0, stream>>>(static_cast<uint32_t*>(g_scratch_ptr[dev]),
+                                         kStaticScratchBytes / 4);
+    E0_CHECK_LAUNCH();
+    g_scratch_zeroed[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return EDGE0_OK;
+}
+}  // namespace e0
+
+extern "C" int edge0_moe_layer_noalloc(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                       const int32_t* slot_table, const int32_t* ids,
+                                       const float* w, const void* x, void* y,
+                                       int32_t* error_out, hipStream_t stream) {
+  if (!shape || !shape_ok(shape) || !x || !y || x == y || !pool || !slot_table || !ids || !w)
+    return EDGE0_EINVAL;
+  if (ws_layout(shape).total > kStaticScratchBytes) return EDGE0_ESCRATCH;
+  void* ws = nullptr;
+  int rc = static_scratch(&ws, stream);
+  if (rc != EDGE0_OK) return rc;
+  MoeArgs a;
+  if ((rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, ws, &a)) != EDGE0_OK) return rc;
+  a.err_out = error_out;
+  LayerIn li{};
+  li.flags = IN_LORA;
   if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
   if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
   return launch_combine(a, stream);

@@ -52,6 +52,9 @@ struct MoeArgs {
   // so every router layer finds both parities empty whatever the parities
   // of the router layers before it
   float* lg_consumed;
+  // optional (single-layer calls on the static scratch): the combine kernel
+  // moves the error word here (EDGE0_OK or EDGE0_ERANGE) and clears it
+  int32_t* err_out;
   int64_t spin;
 };
 constexpr uint32_t kTHandEmpty = 0xFFFFFFFFu;  // a NaN no stored value takes

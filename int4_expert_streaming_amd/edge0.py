@@ -19,6 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libedge0.so")
 
 EDGE0_OK, EDGE0_EINVAL, EDGE0_EHIP, EDGE0_ENOSLOT, EDGE0_ERANGE, EDGE0_ENOMEM = 0, -1, -2, -3, -4, -5
+EDGE0_ESCRATCH = -6
+EDGE0_STATIC_WORKSPACE_BYTES = 1 << 20
 
 
 class Edge0Error(RuntimeError):
@@ -134,6 +136,8 @@ _SIG = {
     "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P]),
     "edge0_prerouter": (C.c_int, [C.POINTER(MoeShape), C.POINTER(Head), _P, _P, _P, _P, _P, _P,
                                   _P, _P]),
+    "edge0_moe_layer_noalloc": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P,
+                                          _P, _P, _P, _P]),
     "edge0_moe_layer": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P, _P, _P,
                                   _P, _P]),
     "edge0_stack_create": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.POINTER(StackSpec),
@@ -256,6 +260,14 @@ def edge0_moe_layer(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y, w
     _check(lib.edge0_moe_layer(C.byref(shape), C.byref(pool), _ptr(slot_table), _ptr(ids), _ptr(w),
                                _ptr(x), _ptr(y), _ptr(workspace), _stream(stream)),
            "edge0_moe_layer")
+
+
+def edge0_moe_layer_noalloc(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y,
+                            error_out=None, stream=None):
+    """edge0_moe_layer on the library's static per-GPU workspace."""
+    _check(lib.edge0_moe_layer_noalloc(C.byref(shape), C.byref(pool), _ptr(slot_table), _ptr(ids),
+                                       _ptr(w), _ptr(x), _ptr(y), _ptr(error_out), _stream(stream)),
+           "edge0_moe_layer_noalloc")
 
 
 EDGE0_GROUPED_NO_MFMA = 1
