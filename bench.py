@@ -390,7 +390,7 @@ def main():
                     help="resident: every bundle in HBM (the headline line); streamed: "
                          "experts staged from pinned host memory into a 3 GiB pool; grouped: "
                          "the multi-token grouped layer at 1-32 tokens per call")
-    ap.add_argument("--stack-mode", choices=["graphs", "persistent"], default="graphs",
+    ap.add_argument("--stack-mode", choices=["graphs", "persistent", "xcd"], default="graphs",
                     help="resident workload: per-layer launches replayed as HIP graphs (the "
                          "default, the faster of the two here) or the layers as one persistent "
                          "cooperative launch per step")
@@ -434,13 +434,15 @@ def main():
     torch.cuda.set_device(0)
     ds = DeviceStack(S, G.StackGen(S, args.seed), N_LAYERS, OWNERS, CONSUMERS, log=log)
     from int4_expert_streaming_amd import edge0 as E
-    persistent = args.stack_mode == "persistent"
-    if persistent:
+    mode_name = args.stack_mode
+    if mode_name != "graphs":
         try:
-            ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
+            ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT if mode_name == "persistent"
+                              else E.EDGE0_STACK_XCD)
         except E.Edge0Error as e:
-            log(f"[bench] persistent mode unavailable ({e}); using per-layer graphs")
-            persistent = False
+            log(f"[bench] {mode_name} mode unavailable ({e}); using per-layer graphs")
+            mode_name = "graphs"
+    persistent = mode_name != "graphs"
     total = args.warmup + args.steps
     h0 = to_device(np.stack([G.stack_hidden(S, args.seed, t) for t in range(total)]))
     h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
@@ -470,7 +472,8 @@ def main():
         for t in range(total, total + 8):
             ds.step(h0[t % total], h_out, t)
             k_ms += ds.stack.kernel_ms()
-        k_name = "k_flow_step (all 40 layers: routing, int4 gate/up + LoRA + SwiGLU, down, combine)"
+        k_name = ("k_xstep" if mode_name == "xcd" else "k_flow_step") + \
+            " (all 40 layers: routing, int4 gate/up + LoRA + SwiGLU, down, combine)"
         k_bytes = flow_bytes(S, n_routers=8)
         k_traffic = None
     else:
@@ -498,7 +501,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "40-layer Qwen3-MoE-shaped decode stack, all experts resident",
-                   "stack_mode": "persistent" if persistent else "graphs",
+                   "stack_mode": mode_name,
                    "d_model": S.d_model, "n_experts": S.n_experts, "d_inter": S.d_inter,
                    "top_k": S.top_k, "group": S.group, "lora_rank": S.lora_rank,
                    "head_hidden": S.head_hidden, "layers": N_LAYERS, "heads": "6-37",

@@ -347,7 +347,25 @@ void edge0_stack_destroy(edge0_stack* st);
  *     word and the launch ends early with incomplete results; the handle
  *     must then be destroyed.
  * EDGE0_EINVAL for another mode value. */
-enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1 };
+/*   EDGE0_STACK_XCD: one cooperative launch of 256 workgroups (32 per XCD)
+ *     runs every layer with one grid-wide and one XCD-local hand-off per
+ *     layer.  With K routed experts each XCD works on one expert of the
+ *     routing (8/K XCDs share an expert, each a slice of its d_inter rows):
+ *     its workgroups compute the gate/up rows of the slice (each with the
+ *     expert's whole LoRA A x, from A rows held in registers), exchange the
+ *     slice's SwiGLU activations within the XCD, and add the slice's down
+ *     contribution (and its share of the LoRA-down delta) for 64 output rows
+ *     each into the layer's fixed-point y.  Each register set of weights is
+ *     reloaded for the next layer right after use: prediction-routed layers'
+ *     experts are known when the step starts ([Edge0] §3.2
+ *     "Prediction-as-routing").  Router layers share their logits within
+ *     each XCD and load their experts after the top-K.  Requires d_model
+ *     2048, top_k in {1, 2, 4, 8} with d_inter * top_k / 8 equal to 384 or
+ *     768, n_experts <= 256, lora_rank 0, 8 or 16, n_layers <= 64 and a
+ *     device that can keep 256 workgroups of 512 threads resident;
+ *     otherwise EDGE0_EINVAL.  Waits are bounded as in the persistent mode.
+ */
+enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1, EDGE0_STACK_XCD = 2 };
 int edge0_stack_set_mode(edge0_stack* st, int32_t mode);
 /* Polls per bounded wait before a workgroup gives up (0: the default, about
  * a second): the persistent mode's phase waits, and in the graphs mode the
@@ -367,6 +385,13 @@ int edge0_stack_error(edge0_stack* st);
  * (up to cap values) and the count to *n.  In the persistent mode the one
  * layer launch of the step is bracketed and *n is 1. */
 int edge0_stack_set_timing(edge0_stack* st, int32_t kernel);
+/* Measurement aid of the EDGE0_STACK_XCD mode: while trace != NULL (device
+ * uint64 [256][16]), every step's launch stores, per workgroup w, the
+ * device's 100 MHz real-time clock at up to 16 points of layer `layer` to
+ * trace[16 w + p] (0 layer start, 1 y loaded, 2 x formed, 3 LoRA A x done,
+ * 4 gate/up done, 5 h stored, 6 XCD hand-off passed, 7 h slice loaded,
+ * 8 down done, 9 y added, 10 grid hand-off passed).  NULL turns it off. */
+int edge0_stack_set_trace(edge0_stack* st, int32_t layer, uint64_t* trace);
 int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n);
 
 /* -------------------------------------------------------------------------

@@ -186,6 +186,48 @@ int flow_grid(const edge0_moe_shape& sh);
 int flow_coresident(int G);
 int launch_flow_step(const FlowArgs& a, int G, hipStream_t stream);
 
+// The resident decode step as one persistent launch with the work split by
+// XCD (xstep.hip): 256 workgroups, one grid-wide and one XCD-local hand-off
+// per layer, weights loaded one layer ahead.
+constexpr int kXMaxLayers = 64;
+struct XArgs {
+  int d, E, I, K, g, r, n_layers;
+  int P, Ix, RW;                     // XCDs per expert, slice rows, rows per workgroup
+  float scale, eps;
+  // byte offsets of the bundle arrays (32-bit: a bundle is far below 4 GiB)
+  struct {
+    uint32_t gate_q, gate_s, gate_b, up_q, up_s, up_b, down_q, down_s, down_b;
+    uint32_t a_gate, b_gate, a_up, b_up, a_down, b_down;
+  } lay;
+  const uint8_t* pool;
+  int64_t slot_bytes;
+  int32_t n_slots;
+  const int32_t* tables;             // [L][E]
+  const uint16_t* const* routers;    // device array [L] of bf16 [E][d]
+  const int32_t* pred_ids;           // [L][K] routing of prediction-routed layers
+  const float* pred_w;
+  int32_t* exec_ids;                 // [L][K] routing the router layers commit
+  float* exec_w;
+  int consumer_first, consumer_last, step;
+  uint16_t *x, *y, *h;               // [L][d], [L][d], [L+1][d]; h[0] holds h0
+  // hand-off words (tag << 32 | payload), the tag = a.tag0 + layer
+  unsigned long long* yp;            // [2][8][d] fp32 partials of y per XCD (layer parity)
+  unsigned long long* yb;            // [8][d/2] bf16 pairs of y, one copy per XCD
+  unsigned long long* xh;            // [8][768] h words of each XCD slice
+  unsigned long long* xlog;          // [8][256] router logits of each XCD
+  uint32_t tag0;                     // tag of layer 0 of this launch (never 0)
+  uint32_t* err;
+  uint32_t* abort_word;
+  int64_t spin;
+  // measurement aid: when set, workgroup w stores the 100 MHz real-time
+  // clock at 16 points of layer trace_layer to trace[16 w ..]
+  unsigned long long* trace;
+  int trace_layer;
+};
+bool xstep_shape_ok(const edge0_moe_shape& sh, int n_layers);
+int xstep_coresident();
+int launch_xstep(const XArgs& a, hipStream_t stream);
+
 int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
                   const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
                   int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream);

@@ -76,6 +76,12 @@ struct edge0_stack {
   const uint16_t** flow_routers;     // device copy of the router pointers
   std::vector<uint32_t> flow_uses;   // completed uses of each counter
   int64_t spin;                      // polls per bounded wait before giving up (both modes)
+  // XCD-split persistent mode (EDGE0_STACK_XCD)
+  unsigned long long* x_words;       // hand-off words: y partials, y copies, h slices, logits
+  uint32_t* x_abort;
+  uint32_t x_layers;                 // layers run so far (the next launch's first tag - 1)
+  unsigned long long* x_trace;       // measurement aid (edge0_stack_set_trace), or NULL
+  int x_trace_layer;
 };
 
 static bool is_consumer(const edge0_stack_spec& s, int L) {
@@ -270,6 +276,79 @@ static int enqueue_flow_step(edge0_stack* st, int step, hipStream_t stream) {
   return enqueue_tail(st, step, stream);
 }
 
+// The XCD-split persistent mode: the step's layers in one cooperative
+// launch (xstep.hip), then the gathered routing and the batched heads.
+static int enqueue_xstep_step(edge0_stack* st, int step, hipStream_t stream) {
+  const edge0_moe_shape& sh = st->shape;
+  const int Lc = st->spec.n_layers, K = sh.top_k;
+  const WsLayout wl = ws_layout(&sh);
+  char* ws = static_cast<char*>(st->ws);
+  XArgs a{};
+  a.d = sh.d_model;
+  a.E = sh.n_experts;
+  a.I = sh.d_inter;
+  a.K = K;
+  a.g = sh.group_size;
+  a.r = sh.lora_rank;
+  a.n_layers = Lc;
+  a.P = 8 / K;
+  a.Ix = sh.d_inter / a.P;
+  a.RW = a.Ix / 32;
+  a.scale = sh.lora_rank > 0 ? sh.lora_alpha / (float)sh.lora_rank : 0.f;
+  a.eps = st->spec.rms_eps;
+  edge0_bundle_layout lay;
+  if (bundle_layout(&sh, &lay) != EDGE0_OK) return EDGE0_EINVAL;
+  auto off32 = [](int64_t v) { return v < 0 ? 0u : (uint32_t)v; };  // -1: no LoRA array
+  a.lay.gate_q = off32(lay.gate_q);
+  a.lay.gate_s = off32(lay.gate_s);
+  a.lay.gate_b = off32(lay.gate_b);
+  a.lay.up_q = off32(lay.up_q);
+  a.lay.up_s = off32(lay.up_s);
+  a.lay.up_b = off32(lay.up_b);
+  a.lay.down_q = off32(lay.down_q);
+  a.lay.down_s = off32(lay.down_s);
+  a.lay.down_b = off32(lay.down_b);
+  a.lay.a_gate = off32(lay.a_gate);
+  a.lay.b_gate = off32(lay.b_gate);
+  a.lay.a_up = off32(lay.a_up);
+  a.lay.b_up = off32(lay.b_up);
+  a.lay.a_down = off32(lay.a_down);
+  a.lay.b_down = off32(lay.b_down);
+  a.pool = static_cast<const uint8_t*>(st->pool.base);
+  a.slot_bytes = st->pool.slot_bytes;
+  a.n_slots = st->pool.n_slots;
+  a.tables = st->tables;
+  a.routers = st->flow_routers;
+  a.pred_ids = st->pred_ids[step % 3];
+  a.pred_w = st->pred_w[step % 3];
+  a.exec_ids = st->exec_ids[step & 1];
+  a.exec_w = st->exec_w[step & 1];
+  a.consumer_first = st->spec.consumer_first;
+  a.consumer_last = st->spec.consumer_last;
+  a.step = step;
+  a.x = st->x;
+  a.y = st->y;
+  a.h = st->h;
+  a.yp = st->x_words;
+  a.yb = a.yp + 2 * 8 * 2048;
+  a.xh = a.yb + 8 * 1024;
+  a.xlog = a.xh + 8 * 768;
+  a.tag0 = st->x_layers + 1u;
+  a.err = reinterpret_cast<uint32_t*>(ws + wl.err);
+  a.abort_word = st->x_abort;
+  a.spin = st->spin;
+  a.trace = st->x_trace;
+  a.trace_layer = st->x_trace_layer;
+  if (st->timed_kernel > 0 && hipEventRecord(st->ev_start[0], stream) != hipSuccess)
+    return EDGE0_EHIP;
+  const int rc = launch_xstep(a, stream);
+  if (rc != EDGE0_OK) return rc;
+  if (st->timed_kernel > 0 && hipEventRecord(st->ev_stop[0], stream) != hipSuccess)
+    return EDGE0_EHIP;
+  st->x_layers += (uint32_t)Lc;  // the tags the launch used
+  return enqueue_tail(st, step, stream);
+}
+
 extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
                                   const edge0_stack_spec* spec, const edge0_slot_pool* pool,
                                   const int32_t* slot_tables, const void* const* routers,
@@ -383,8 +462,9 @@ extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, in
   const size_t d = st->shape.d_model;
   if (hipMemcpyAsync(st->h, h0, d * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return EDGE0_EHIP;
-  if (st->mode == EDGE0_STACK_PERSISTENT) {
-    const int rc = enqueue_flow_step(st, step, stream);
+  if (st->mode == EDGE0_STACK_PERSISTENT || st->mode == EDGE0_STACK_XCD) {
+    const int rc = st->mode == EDGE0_STACK_XCD ? enqueue_xstep_step(st, step, stream)
+                                               : enqueue_flow_step(st, step, stream);
     if (rc != EDGE0_OK) return rc;
     if (hipMemcpyAsync(h_out, st->h + (size_t)st->spec.n_layers * d, d * 2,
                        hipMemcpyDeviceToDevice, stream) != hipSuccess)
@@ -590,7 +670,7 @@ extern "C" int edge0_stack_set_timing(edge0_stack* st, int32_t kernel) {
 extern "C" int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n_out) {
   if (!st || !ms_out || !n_out || st->timed_kernel <= 0 || st->last_step < 0) return EDGE0_EINVAL;
   if (hipDeviceSynchronize() != hipSuccess) return EDGE0_EHIP;
-  const int n = st->mode == EDGE0_STACK_PERSISTENT ? (cap > 0 ? 1 : 0)
+  const int n = st->mode != EDGE0_STACK_GRAPHS ? (cap > 0 ? 1 : 0)
                                                    : (st->spec.n_layers < cap ? st->spec.n_layers : cap);
   for (int L = 0; L < n; ++L)
     if (hipEventElapsedTime(&ms_out[L], st->ev_start[L], st->ev_stop[L]) != hipSuccess)
@@ -599,28 +679,66 @@ extern "C" int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap
   return EDGE0_OK;
 }
 
+// device copy of the router pointers (persistent modes)
+static int ensure_routers(edge0_stack* st) {
+  if (st->flow_routers) return EDGE0_OK;
+  const int Lc = st->spec.n_layers;
+  if (hipMalloc((void**)&st->flow_routers, Lc * sizeof(void*)) != hipSuccess) return EDGE0_ENOMEM;
+  if (hipMemcpy(st->flow_routers, st->routers.data(), Lc * sizeof(void*), hipMemcpyHostToDevice) !=
+      hipSuccess)
+    return EDGE0_EHIP;
+  return EDGE0_OK;
+}
+
 extern "C" int edge0_stack_set_mode(edge0_stack* st, int32_t mode) {
-  if (!st || (mode != EDGE0_STACK_GRAPHS && mode != EDGE0_STACK_PERSISTENT)) return EDGE0_EINVAL;
+  if (!st || (mode != EDGE0_STACK_GRAPHS && mode != EDGE0_STACK_PERSISTENT &&
+              mode != EDGE0_STACK_XCD))
+    return EDGE0_EINVAL;
+  if (mode == EDGE0_STACK_XCD) {
+    if (!xstep_shape_ok(st->shape, st->spec.n_layers)) return EDGE0_EINVAL;
+    int rc = xstep_coresident();
+    if (rc != EDGE0_OK) return rc;
+    if ((rc = ensure_routers(st)) != EDGE0_OK) return rc;
+    if (!st->x_words) {
+      // y partials [2][8][2048], y copies [8][1024], h slices [8][768],
+      // logits [8][256]; tag 0 is never used, so zeroed words are stale
+      const size_t words = 2 * 8 * 2048 + 8 * 1024 + 8 * 768 + 8 * 256;
+      if (hipMalloc((void**)&st->x_words, words * 8) != hipSuccess ||
+          hipMalloc((void**)&st->x_abort, 4) != hipSuccess)
+        return EDGE0_ENOMEM;
+      if (hipMemset(st->x_words, 0, words * 8) != hipSuccess ||
+          hipMemset(st->x_abort, 0, 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return EDGE0_EHIP;
+      st->x_layers = 0;
+    }
+    st->mode = mode;
+    return EDGE0_OK;
+  }
   if (mode == EDGE0_STACK_PERSISTENT) {
     const int Lc = st->spec.n_layers;
     if (!flow_shape_ok(st->shape, Lc)) return EDGE0_EINVAL;
-    const int rc = flow_coresident(flow_grid(st->shape));
+    int rc = flow_coresident(flow_grid(st->shape));
     if (rc != EDGE0_OK) return rc;
+    if ((rc = ensure_routers(st)) != EDGE0_OK) return rc;
     if (!st->flow_cnt) {
       const size_t cnt_bytes = (size_t)kFlowMaxPhases * kFlowCounters * 64 * 4;
       if (hipMalloc((void**)&st->flow_cnt, cnt_bytes) != hipSuccess ||
-          hipMalloc((void**)&st->flow_abort, 4) != hipSuccess ||
-          hipMalloc((void**)&st->flow_routers, Lc * sizeof(void*)) != hipSuccess)
+          hipMalloc((void**)&st->flow_abort, 4) != hipSuccess)
         return EDGE0_ENOMEM;
       if (hipMemset(st->flow_cnt, 0, cnt_bytes) != hipSuccess ||
-          hipMemset(st->flow_abort, 0, 4) != hipSuccess ||
-          hipMemcpy(st->flow_routers, st->routers.data(), Lc * sizeof(void*),
-                    hipMemcpyHostToDevice) != hipSuccess)
+          hipMemset(st->flow_abort, 0, 4) != hipSuccess)
         return EDGE0_EHIP;
       st->flow_uses.assign(kFlowMaxPhases, 0u);
     }
   }
   st->mode = mode;
+  return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_set_trace(edge0_stack* st, int32_t layer, uint64_t* trace) {
+  if (!st || (trace && (layer < 0 || layer >= st->spec.n_layers))) return EDGE0_EINVAL;
+  st->x_trace = reinterpret_cast<unsigned long long*>(trace);
+  st->x_trace_layer = layer;
   return EDGE0_OK;
 }
 
@@ -659,6 +777,8 @@ extern "C" void edge0_stack_destroy(edge0_stack* st) {
     if (g) (void)hipGraphExecDestroy(g);
   if (st->cap) (void)hipStreamDestroy(st->cap);
   if (st->ev_heads) (void)hipEventDestroy(st->ev_heads);
+  (void)hipFree(st->x_words);
+  (void)hipFree(st->x_abort);
   (void)hipFree(st->flow_cnt);
   (void)hipFree(st->flow_abort);
   (void)hipFree(const_cast<uint16_t**>(st->flow_routers));

@@ -136,6 +136,7 @@ _SIG = {
     "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P]),
     "edge0_prerouter": (C.c_int, [C.POINTER(MoeShape), C.POINTER(Head), _P, _P, _P, _P, _P, _P,
                                   _P, _P]),
+    "edge0_stack_set_trace": (C.c_int, [_P, C.c_int32, _P]),
     "edge0_moe_layer_noalloc": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P,
                                           _P, _P, _P, _P]),
     "edge0_moe_layer": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P, _P, _P,
@@ -273,6 +274,7 @@ def edge0_moe_layer_noalloc(shape: MoeShape, pool: SlotPool, slot_table, ids, w,
 EDGE0_GROUPED_NO_MFMA = 1
 EDGE0_STACK_GRAPHS = 0
 EDGE0_STACK_PERSISTENT = 1
+EDGE0_STACK_XCD = 2
 
 
 def grouped_mfma_min(n: int) -> int:
@@ -330,6 +332,10 @@ class Stack(_Handle):
     def set_timing(self, kernel: int):
         """Event pair around one launch class per layer (1 gate/up, 2 down, 3 LoRA-in)."""
         _check(lib.edge0_stack_set_timing(self._handle, kernel), "edge0_stack_set_timing")
+
+    def set_trace(self, layer: int, buf=None):
+        """XCD mode: per-workgroup clock stamps of one layer into buf (int64 [256][16])."""
+        _check(lib.edge0_stack_set_trace(self._handle, layer, _ptr(buf)), "edge0_stack_set_trace")
 
     def kernel_ms(self) -> list:
         n = self.spec.n_layers
