@@ -87,6 +87,18 @@ def flow_bytes(S, n_routers):
     return N_LAYERS * (K * (bundle + lora) + act) + n_routers * E * d * 2
 
 
+def xlayer_bytes(S):
+    """Algorithmic bytes of one k_xlayer launch of a prediction-routed layer:
+    the K routed experts' bundles (gate, up, down int4 with scales and
+    biases) and adapters, read once; the previous layer's h and fixed-point
+    y read; x, y, h and the fixed-point y written (the layer's own output)."""
+    d, I, K, g, r = S.d_model, S.d_inter, S.top_k, S.group, S.lora_rank
+    bundle = 3 * I * d // 2 + 3 * (I * d // g) * 2 * 2
+    lora = 2 * (r * d + I * r) * 2 + (r * I + d * r) * 2
+    act = d * 2 + d * 8 + 3 * d * 2 + d * 8
+    return K * (bundle + lora) + act
+
+
 def gate_up_traffic():
     """Counter-derived HBM bytes per k_layer_fused launch, or None if the
     kernel sources changed since the counters were taken."""
@@ -390,7 +402,8 @@ def main():
                     help="resident: every bundle in HBM (the headline line); streamed: "
                          "experts staged from pinned host memory into a 3 GiB pool; grouped: "
                          "the multi-token grouped layer at 1-32 tokens per call")
-    ap.add_argument("--stack-mode", choices=["graphs", "persistent", "xcd"], default="graphs",
+    ap.add_argument("--stack-mode", choices=["graphs", "persistent", "xcd", "xlayer"],
+                    default="graphs",
                     help="resident workload: per-layer launches replayed as HIP graphs (the "
                          "default, the faster of the two here) or the layers as one persistent "
                          "cooperative launch per step")
@@ -437,12 +450,12 @@ def main():
     mode_name = args.stack_mode
     if mode_name != "graphs":
         try:
-            ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT if mode_name == "persistent"
-                              else E.EDGE0_STACK_XCD)
+            ds.stack.set_mode({"persistent": E.EDGE0_STACK_PERSISTENT, "xcd": E.EDGE0_STACK_XCD,
+                               "xlayer": E.EDGE0_STACK_XLAYER}[mode_name])
         except E.Edge0Error as e:
             log(f"[bench] {mode_name} mode unavailable ({e}); using per-layer graphs")
             mode_name = "graphs"
-    persistent = mode_name != "graphs"
+    persistent = mode_name in ("persistent", "xcd")
     total = args.warmup + args.steps
     h0 = to_device(np.stack([G.stack_hidden(S, args.seed, t) for t in range(total)]))
     h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
@@ -486,9 +499,15 @@ def main():
             ds.step(h0[t % total], h_out, t)
             per_layer = ds.stack.kernel_ms()
             k_ms += [per_layer[L] for L in range(CONSUMERS[0], CONSUMERS[1] + 1)]
-        k_name = "k_layer_fused (layer input + int4 gate/up GEMV + LoRA + SwiGLU)"
-        k_bytes = fused_bytes(S)
-        k_traffic = gate_up_traffic()
+        if mode_name == "xlayer":
+            k_name = ("k_xlayer (one whole layer: input, int4 gate/up + LoRA + SwiGLU, XCD-local "
+                      "hand-off of h, int4 down + LoRA, combine)")
+            k_bytes = xlayer_bytes(S)
+            k_traffic = None
+        else:
+            k_name = "k_layer_fused (layer input + int4 gate/up GEMV + LoRA + SwiGLU)"
+            k_bytes = fused_bytes(S)
+            k_traffic = gate_up_traffic()
     ds.stack.set_timing(0)
     k_mean = float(np.mean(k_ms))
     k_gbps = k_bytes / (k_mean * 1e-3) / 1e9

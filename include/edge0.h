@@ -365,7 +365,16 @@ void edge0_stack_destroy(edge0_stack* st);
  *     device that can keep 256 workgroups of 512 threads resident;
  *     otherwise EDGE0_EINVAL.  Waits are bounded as in the persistent mode.
  */
-enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1, EDGE0_STACK_XCD = 2 };
+/*   EDGE0_STACK_XLAYER: the XCD split of EDGE0_STACK_XCD, one launch per
+ *     layer, replayed as HIP graphs.  The kernel boundary hands y to the next
+ *     layer (fixed-point atomics, exact and order-free); inside a launch the
+ *     only hand-off is h within each XCD (and a router layer's logits).  A
+ *     layer's experts are loaded as its launch starts: the slots of the
+ *     predicted routing are resolved by a small kernel after the heads.  Same
+ *     shape requirements as EDGE0_STACK_XCD; waits are bounded likewise.
+ */
+enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1, EDGE0_STACK_XCD = 2,
+       EDGE0_STACK_XLAYER = 3 };
 int edge0_stack_set_mode(edge0_stack* st, int32_t mode);
 /* Polls per bounded wait before a workgroup gives up (0: the default, about
  * a second): the persistent mode's phase waits, and in the graphs mode the
@@ -386,11 +395,13 @@ int edge0_stack_error(edge0_stack* st);
  * layer launch of the step is bracketed and *n is 1. */
 int edge0_stack_set_timing(edge0_stack* st, int32_t kernel);
 /* Measurement aid of the EDGE0_STACK_XCD mode: while trace != NULL (device
- * uint64 [256][16]), every step's launch stores, per workgroup w, the
- * device's 100 MHz real-time clock at up to 16 points of layer `layer` to
- * trace[16 w + p] (0 layer start, 1 y loaded, 2 x formed, 3 LoRA A x done,
- * 4 gate/up done, 5 h stored, 6 XCD hand-off passed, 7 h slice loaded,
- * 8 down done, 9 y added, 10 grid hand-off passed).  NULL turns it off. */
+ * uint64 [256][32]), every step's launch stores, per workgroup w, the
+ * device's 100 MHz real-time clock at up to 32 points of layer `layer` to
+ * trace[32 w + p] (0 layer start, 2 staged rows landed, 3 LoRA A x done,
+ * 4 gate/up done, 5 h stored, 7 the XCD's h collected, 8 down done, 9 y
+ * partial stored, 10 y rows stored, 11 y collected; 16-24 finer points of
+ * the compute waves; 12 and 13 the shader clock counter at 0 and 11).
+ * NULL turns it off. */
 int edge0_stack_set_trace(edge0_stack* st, int32_t layer, uint64_t* trace);
 int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n);
 

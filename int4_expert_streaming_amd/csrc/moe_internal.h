@@ -228,6 +228,34 @@ bool xstep_shape_ok(const edge0_moe_shape& sh, int n_layers);
 int xstep_coresident();
 int launch_xstep(const XArgs& a, hipStream_t stream);
 
+// One layer of the same XCD split per launch (xlayer mode, graph-replayed):
+// the kernel boundary hands y to the next layer (fixed-point atomics here,
+// plain loads there), and h is handed within each XCD inside the launch.
+struct XLArgs {
+  XArgs base;                        // shape, layout, pool, error/abort, spin
+  int layer;
+  bool router;                       // routed by the plain router (else by pred_slot)
+  const uint16_t* w_router;          // router layers: bf16 [E][d]
+  const int32_t* table_row;          // router layers: [E] id -> slot
+  const int32_t* pred_slot;          // prediction-routed layers: [K] slots of the routing
+  const float* pred_w;               // ... and their weights
+  int32_t* exec_ids;                 // router layers: [K] the committed routing
+  float* exec_w;
+  const uint16_t* h_prev;            // bf16 [d]: h_{L-1} (h0 at layer 0)
+  const unsigned long long* acc_in;  // [d] fixed-point y_{L-1}, NULL at layer 0
+  unsigned long long* acc_out;       // [d] this layer's y (zero on entry)
+  unsigned long long* acc_zero;      // [d] cleared here for the layer after next
+  uint16_t *x_out, *y_prev_out, *h_out;  // records: x_L, y_{L-1}, h_L (workgroup 0)
+  unsigned long long* hx;            // [8][768] this layer's h words (tag 1 = written)
+  unsigned long long* hx_clear;      // the other parity's, cleared here
+  unsigned long long* lx;            // [8][256] router logits words
+  unsigned long long* lx_clear;
+};
+int launch_xlayer(const XLArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+// slot of every prediction-routed layer's routing: slot[L][k] = table[L][ids[L][k]]
+int launch_pred_slots(const int32_t* tables, const int32_t* ids, int32_t* slots, int n_layers,
+                      int E, int K, int n_slots, uint32_t* err, hipStream_t stream);
+
 int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
                   const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
                   int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream);

@@ -82,6 +82,10 @@ struct edge0_stack {
   uint32_t x_layers;                 // layers run so far (the next launch's first tag - 1)
   unsigned long long* x_trace;       // measurement aid (edge0_stack_set_trace), or NULL
   int x_trace_layer;
+  // XCD-split layers mode (EDGE0_STACK_XLAYER): one launch per layer, graphs
+  unsigned long long* xl_acc;        // [3][d] fixed-point y, by running layer number mod 3
+  unsigned long long* xl_words;      // [2][8][768] h words, then [2][8][256] logits words
+  int32_t* xl_slots;                 // [2][L][K] slots of the predicted routing, by step parity
 };
 
 static bool is_consumer(const edge0_stack_spec& s, int L) {
@@ -93,10 +97,123 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
 
 static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream);
 
+// The XCD-split layers mode: per layer one launch of k_xlayer (the layer's
+// input, routing, gate/up, SwiGLU, down and combine), then the last layer's
+// combine, the gathered routing, the batched heads and the slots of the
+// routing they predicted.  y buffer of layer L of step s: acc[(n_layers s +
+// L) % 3]; hand-off words by layer parity.  Step 0 starts from cleared
+// buffers (also when a handle restarts at step 0).
+__global__ void k_xl_clear(unsigned long long* a, size_t na, unsigned long long* b, size_t nb) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < na + nb;
+       i += (size_t)gridDim.x * blockDim.x) {
+    if (i < na) a[i] = 0ull;
+    else b[i - na] = 0ull;
+  }
+}
+
+static int enqueue_xlayer_step(edge0_stack* st, int step, hipStream_t stream) {
+  const edge0_moe_shape& sh = st->shape;
+  const int Lc = st->spec.n_layers, K = sh.top_k, E = sh.n_experts;
+  const size_t d = sh.d_model;
+  const WsLayout wl = ws_layout(&sh);
+  char* ws = static_cast<char*>(st->ws);
+  const size_t n_hx = 8 * 768, n_lx = 8 * 256;
+  if (step == 0) {
+    k_xl_clear<<<64, 256, 0, stream>>>(st->xl_acc, 3 * d, st->xl_words, 2 * n_hx + 2 * n_lx);
+    E0_CHECK_LAUNCH();
+  }
+  XLArgs la{};
+  XArgs& a = la.base;
+  a.d = sh.d_model;
+  a.E = E;
+  a.I = sh.d_inter;
+  a.K = K;
+  a.g = sh.group_size;
+  a.r = sh.lora_rank;
+  a.n_layers = Lc;
+  a.P = 8 / K;
+  a.Ix = sh.d_inter / a.P;
+  a.RW = a.Ix / 32;
+  a.scale = sh.lora_rank > 0 ? sh.lora_alpha / (float)sh.lora_rank : 0.f;
+  a.eps = st->spec.rms_eps;
+  edge0_bundle_layout lay;
+  if (bundle_layout(&sh, &lay) != EDGE0_OK) return EDGE0_EINVAL;
+  auto off32 = [](int64_t v) { return v < 0 ? 0u : (uint32_t)v; };
+  a.lay.gate_q = off32(lay.gate_q);
+  a.lay.gate_s = off32(lay.gate_s);
+  a.lay.gate_b = off32(lay.gate_b);
+  a.lay.up_q = off32(lay.up_q);
+  a.lay.up_s = off32(lay.up_s);
+  a.lay.up_b = off32(lay.up_b);
+  a.lay.down_q = off32(lay.down_q);
+  a.lay.down_s = off32(lay.down_s);
+  a.lay.down_b = off32(lay.down_b);
+  a.lay.a_gate = off32(lay.a_gate);
+  a.lay.b_gate = off32(lay.b_gate);
+  a.lay.a_up = off32(lay.a_up);
+  a.lay.b_up = off32(lay.b_up);
+  a.lay.a_down = off32(lay.a_down);
+  a.lay.b_down = off32(lay.b_down);
+  a.pool = static_cast<const uint8_t*>(st->pool.base);
+  a.slot_bytes = st->pool.slot_bytes;
+  a.n_slots = st->pool.n_slots;
+  a.err = reinterpret_cast<uint32_t*>(ws + wl.err);
+  a.abort_word = st->x_abort;
+  a.spin = st->spin;
+  a.trace = st->x_trace;
+  a.trace_layer = st->x_trace_layer;
+  const unsigned base = (unsigned)Lc * (unsigned)step;  // running layer number of layer 0
+  for (int L = 0; L < Lc; ++L) {
+    const unsigned ell = base + (unsigned)L;
+    la.layer = L;
+    la.router = !(is_consumer(st->spec, L) && step > 0);
+    la.w_router = static_cast<const uint16_t*>(st->routers[L]);
+    la.table_row = st->tables + (size_t)L * E;
+    la.pred_slot = st->xl_slots + ((size_t)(step & 1) * Lc + L) * K;
+    la.pred_w = st->pred_w[step % 3] + (size_t)L * K;
+    la.exec_ids = st->exec_ids[step & 1] + (size_t)L * K;
+    la.exec_w = st->exec_w[step & 1] + (size_t)L * K;
+    la.h_prev = st->h + (size_t)(L > 0 ? L - 1 : 0) * d;
+    la.acc_in = L > 0 ? st->xl_acc + (size_t)((ell + 2) % 3) * d : nullptr;
+    la.acc_out = st->xl_acc + (size_t)(ell % 3) * d;
+    la.acc_zero = st->xl_acc + (size_t)((ell + 1) % 3) * d;
+    la.x_out = st->x + (size_t)L * d;
+    la.y_prev_out = L > 0 ? st->y + (size_t)(L - 1) * d : nullptr;
+    la.h_out = st->h + (size_t)L * d;
+    la.hx = st->xl_words + (size_t)(L & 1) * n_hx;
+    la.hx_clear = st->xl_words + (size_t)((L + 1) & 1) * n_hx;
+    la.lx = st->xl_words + 2 * n_hx + (size_t)(L & 1) * n_lx;
+    la.lx_clear = st->xl_words + 2 * n_hx + (size_t)((L + 1) & 1) * n_lx;
+    LaunchTiming lt{st->timed_kernel, nullptr, nullptr};
+    if (st->timed_kernel > 0) {
+      lt.start = st->ev_start[L];
+      lt.stop = st->ev_stop[L];
+    }
+    const int rc = launch_xlayer(la, stream, st->timed_kernel > 0 ? &lt : nullptr);
+    if (rc != EDGE0_OK) return rc;
+  }
+  // the last layer's combine and residual: y = bf16(acc), h_out = bf16(h + y)
+  MoeArgs c{};
+  c.d = sh.d_model;
+  c.acc = st->xl_acc + (size_t)((base + (unsigned)Lc - 1) % 3) * d;
+  c.y = st->y + (size_t)(Lc - 1) * d;
+  c.h_res = st->h + (size_t)(Lc - 1) * d;
+  c.h_out = st->h + (size_t)Lc * d;
+  c.err_out = nullptr;
+  int rc = launch_combine(c, stream);
+  if (rc != EDGE0_OK) return rc;
+  if ((rc = enqueue_tail(st, step, stream)) != EDGE0_OK) return rc;
+  // slots of the routing the heads predicted for the next step
+  return launch_pred_slots(st->tables, st->pred_ids[(step + 1) % 3],
+                           st->xl_slots + (size_t)((step + 1) & 1) * Lc * K, Lc, E, K,
+                           st->pool.n_slots, a.err, stream);
+}
+
 // enqueue all launches of decode step `step` (h[0] already holds h0), one
 // stream: the heads come last (a forked branch for them, parallel nodes in
 // the captured graph, measured slower).
 static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
+  if (st->mode == EDGE0_STACK_XLAYER) return enqueue_xlayer_step(st, step, stream);
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers, E = sh.n_experts;
   MoeArgs a{};
@@ -670,7 +787,8 @@ extern "C" int edge0_stack_set_timing(edge0_stack* st, int32_t kernel) {
 extern "C" int edge0_stack_kernel_ms(edge0_stack* st, float* ms_out, int32_t cap, int32_t* n_out) {
   if (!st || !ms_out || !n_out || st->timed_kernel <= 0 || st->last_step < 0) return EDGE0_EINVAL;
   if (hipDeviceSynchronize() != hipSuccess) return EDGE0_EHIP;
-  const int n = st->mode != EDGE0_STACK_GRAPHS ? (cap > 0 ? 1 : 0)
+  const int n = (st->mode == EDGE0_STACK_PERSISTENT || st->mode == EDGE0_STACK_XCD)
+                    ? (cap > 0 ? 1 : 0)
                                                    : (st->spec.n_layers < cap ? st->spec.n_layers : cap);
   for (int L = 0; L < n; ++L)
     if (hipEventElapsedTime(&ms_out[L], st->ev_start[L], st->ev_stop[L]) != hipSuccess)
@@ -692,8 +810,33 @@ static int ensure_routers(edge0_stack* st) {
 
 extern "C" int edge0_stack_set_mode(edge0_stack* st, int32_t mode) {
   if (!st || (mode != EDGE0_STACK_GRAPHS && mode != EDGE0_STACK_PERSISTENT &&
-              mode != EDGE0_STACK_XCD))
+              mode != EDGE0_STACK_XCD && mode != EDGE0_STACK_XLAYER))
     return EDGE0_EINVAL;
+  if (mode == EDGE0_STACK_XLAYER) {
+    if (!xstep_shape_ok(st->shape, st->spec.n_layers)) return EDGE0_EINVAL;
+    if (!st->xl_acc) {
+      const size_t d = st->shape.d_model;
+      const size_t nw = 2 * 8 * 768 + 2 * 8 * 256;
+      const size_t ns = 2 * (size_t)st->spec.n_layers * st->shape.top_k;
+      if (hipMalloc((void**)&st->xl_acc, 3 * d * 8) != hipSuccess ||
+          hipMalloc((void**)&st->xl_words, nw * 8) != hipSuccess ||
+          hipMalloc((void**)&st->xl_slots, ns * 4) != hipSuccess ||
+          (!st->x_abort && hipMalloc((void**)&st->x_abort, 4) != hipSuccess))
+        return EDGE0_ENOMEM;
+      if (hipMemset(st->xl_acc, 0, 3 * d * 8) != hipSuccess ||
+          hipMemset(st->xl_words, 0, nw * 8) != hipSuccess ||
+          hipMemset(st->xl_slots, 0xFF, ns * 4) != hipSuccess ||
+          hipMemset(st->x_abort, 0, 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return EDGE0_EHIP;
+    }
+  }
+  // graphs captured in another mode hold other launches
+  if (mode != st->mode)
+    for (auto& g : st->graphs)
+      if (g) {
+        (void)hipGraphExecDestroy(g);
+        g = nullptr;
+      }
   if (mode == EDGE0_STACK_XCD) {
     if (!xstep_shape_ok(st->shape, st->spec.n_layers)) return EDGE0_EINVAL;
     int rc = xstep_coresident();
@@ -739,6 +882,12 @@ extern "C" int edge0_stack_set_trace(edge0_stack* st, int32_t layer, uint64_t* t
   if (!st || (trace && (layer < 0 || layer >= st->spec.n_layers))) return EDGE0_EINVAL;
   st->x_trace = reinterpret_cast<unsigned long long*>(trace);
   st->x_trace_layer = layer;
+  // the per-layer mode's step graphs hold the trace pointer in their arguments
+  for (auto& g : st->graphs)
+    if (g) {
+      (void)hipGraphExecDestroy(g);
+      g = nullptr;
+    }
   return EDGE0_OK;
 }
 
@@ -779,6 +928,9 @@ extern "C" void edge0_stack_destroy(edge0_stack* st) {
   if (st->ev_heads) (void)hipEventDestroy(st->ev_heads);
   (void)hipFree(st->x_words);
   (void)hipFree(st->x_abort);
+  (void)hipFree(st->xl_acc);
+  (void)hipFree(st->xl_words);
+  (void)hipFree(st->xl_slots);
   (void)hipFree(st->flow_cnt);
   (void)hipFree(st->flow_abort);
   (void)hipFree(const_cast<uint16_t**>(st->flow_routers));

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
     const bool next_pred = L + 1 < a.n_layers && x_is_pred(a, L + 1);
     const uint32_t tag = a.tag0 + (uint32_t)L;  // this layer's hand-offs
     unsigned long long* tr =
-        (a.trace != nullptr && L == a.trace_layer) ? a.trace + 16 * (size_t)w : nullptr;
+        (a.trace != nullptr && L == a.trace_layer) ? a.trace + 32 * (size_t)w : nullptr;
     if (wave == 0) X_MARK(0);
     if (wave == 0 && tr && lane == 0) tr[12] = __builtin_amdgcn_s_memtime();
 
@@ -407,7 +407,9 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
       load_x_raw(s.xs, lane, xr);
 #pragma unroll
       for (int m = 0; m < 4; ++m) xv[m] = reinterpret_cast<const uint4*>(s.xs)[lane + 64 * m];
+      if (wave == 0) X_MARK(16);
       x_wait_vm();  // this wave's staged rows have landed in LDS
+      if (wave == 0) X_MARK(17);
     }
     __syncthreads();  // ... and every wave's
     if (wave == 0) X_MARK(2);
@@ -468,6 +470,7 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
         const float p = wave_sum(x_row_dot(s, ar, xv));
         if (lane == 0) s.t_s[ar] = p;
       }
+      if (wave == 0) X_MARK(18);
     }
     __syncthreads();
     if (wave == 0) X_MARK(3);
@@ -493,6 +496,7 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
         v[m] = G;
         v[R + m] = U;
       }
+      if (wave == 0) X_MARK(24);
       const float w1 = wave_sums_2r<R>(v);
       const float Uo = __shfl_xor(w1, 32, kWave);
       constexpr int kSpan = 64 / (2 * R);
@@ -540,6 +544,7 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
         pair_perm8(lo[0], lo[1], lo[2], lo[3], &s.hp[c][16 + 4 * m]);
         s.hsp[c][m] = sm;
       }
+      if (wave == 0) X_MARK(19);
       if (r > 0) {
         const int col0 = lane * 2 * CPL;
         float p[kXTdRows];
@@ -560,8 +565,10 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
           if (lane == 0 && rr < r) s.td_s[rr] = sm;
         }
       }
+      if (wave == 0) X_MARK(20);
     }
     __syncthreads();
+    if (wave == 0) X_MARK(21);
 
     // ---- down tiles of the slice for output rows 64 j .. 64 j + 63
     if (!ctl) {
@@ -578,8 +585,10 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
         }
       }
       s.red[wave][lane] = part_sum;
+      if (wave == 0) X_MARK(22);
     }
     __syncthreads();
+    if (wave == 0) X_MARK(23);
     if (wave == 0) {
       float D = 0.f;
 #pragma unroll
@@ -686,6 +695,342 @@ __global__ __launch_bounds__(kXThreads) void k_xstep(XArgs a) {
           make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
     }
   }
+}
+
+// ------------------------------------------------------------ one layer
+// The same work split for one layer per launch.  y reaches the next layer
+// across the kernel boundary (fixed-point atomics into acc_out here, plain
+// loads of it there), so the only hand-off inside a launch is h within each
+// XCD (and, on a router layer, the logits within each XCD).  A hand-off word
+// holds tag 1 once written; each launch clears the other layer parity's
+// words for the layer after it, and the y buffer of the layer after next.
+__global__ void k_pred_slots(const int32_t* __restrict__ tables, const int32_t* __restrict__ ids,
+                             int32_t* __restrict__ slots, int n, int E, int K, int n_slots,
+                             uint32_t* err) {
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n * K; t += gridDim.x * blockDim.x) {
+    const int L = t / K, id = ids[t];
+    int slot = (id >= 0 && id < E) ? tables[(size_t)L * E + id] : -1;
+    if (slot < 0 || slot >= n_slots) slot = -1;
+    slots[t] = slot;
+  }
+  (void)err;
+}
+
+template <int RW>
+__global__ __launch_bounds__(kXThreads) void k_xlayer(XLArgs la) {
+  constexpr int NPW = (RW + kXWaves - 1) / kXWaves;
+  constexpr int CPL = RW / 4;
+  const XArgs& a = la.base;
+  __shared__ XLds s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool ctl = wave == kXWaves;
+  const int w = blockIdx.x, X = w % 8, j = w / 8;
+  const int K = a.K, r = a.r, E = a.E;
+  const int k = X / a.P, part = X % a.P;
+  const int i0 = part * a.Ix + j * RW;
+  const int c0 = part * a.Ix / 32;
+  const bool lead = w == 0;
+  constexpr uint32_t tag = 1u;
+  unsigned long long* xh = la.hx + (size_t)X * kXMaxIx;
+  unsigned long long* xlog = la.lx + (size_t)X * kXMaxE;
+  XGu<NPW> gu;
+  XDn<NPW, CPL> dn;
+  int slot = -1;
+  float wk = 0.f;
+  unsigned long long* tr =
+      (a.trace != nullptr && la.layer == a.trace_layer) ? a.trace + 32 * (size_t)w : nullptr;
+  if (wave == 0) X_MARK(0);
+
+  // ---- loads first: a prediction-routed layer's expert (slot known), or a
+  // router layer's router rows and slot-table row
+  if (!la.router) {
+    slot = la.pred_slot[k];
+    wk = la.pred_w[k];
+    if (!ctl) {
+      const uint8_t* b = x_bundle(a, slot);
+      x_stage_a(a, b, s);
+      x_load_gu<RW, NPW>(a, b, i0, gu);
+      x_load_dn<RW, NPW, CPL>(a, b, j, c0, dn);
+    }
+  } else {
+    if (!ctl) {
+      const int nrw = (E + kXPerXcd - 1) / kXPerXcd;
+      for (int n = wave; n < 4 * nrw; n += kXWaves)
+        x_stage_piece(s, la.w_router + (size_t)min(j + kXPerXcd * (n >> 2), E - 1) * kXD, n);
+    } else {
+      for (int e = lane; e < E; e += 64) s.tbl[e] = la.table_row[e];
+    }
+  }
+  // the previous layer's output (written before this launch), the residual
+  float hreg[4];
+  uint2 yrec = make_uint2(0, 0);
+  {
+    const uint2 hv = reinterpret_cast<const uint2*>(la.h_prev)[tid];
+    hreg[0] = bf_lo(hv.x);
+    hreg[1] = bf_hi(hv.x);
+    hreg[2] = bf_lo(hv.y);
+    hreg[3] = bf_hi(hv.y);
+    if (la.acc_in != nullptr) {
+      const ulonglong2 a0 = reinterpret_cast<const ulonglong2*>(la.acc_in)[2 * tid];
+      const ulonglong2 a1 = reinterpret_cast<const ulonglong2*>(la.acc_in)[2 * tid + 1];
+      const uint32_t y0 = f2bf(from_fix(a0.x)), y1 = f2bf(from_fix(a0.y));
+      const uint32_t y2 = f2bf(from_fix(a1.x)), y3 = f2bf(from_fix(a1.y));
+      yrec = make_uint2(y0 | (y1 << 16), y2 | (y3 << 16));
+      hreg[0] = bf2f(f2bf(hreg[0] + bf2f(y0)));
+      hreg[1] = bf2f(f2bf(hreg[1] + bf2f(y1)));
+      hreg[2] = bf2f(f2bf(hreg[2] + bf2f(y2)));
+      hreg[3] = bf2f(f2bf(hreg[3] + bf2f(y3)));
+    }
+  }
+  // clear what the next launches start from (control wave, plain stores:
+  // they are read after this launch ends)
+  if (ctl) {
+    if (lane < kXD / kXG) la.acc_zero[(kXD / kXG) * w + lane] = 0ull;
+    for (int i = lane; i < 8 * kXMaxIx / kXG; i += 64) la.hx_clear[(8 * kXMaxIx / kXG) * w + i] = 0ull;
+    if (lane < 8 * kXMaxE / kXG) la.lx_clear[(8 * kXMaxE / kXG) * w + lane] = 0ull;
+  }
+  // ---- x = bf16(RMSNorm(h)) (all 8 waves)
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(hreg[e], hreg[e], ss);
+    ss = wave_sum(ss);
+    if (lane == 0) s.ss[wave] = ss;
+  }
+  __syncthreads();
+  uint2 xrec;
+  {
+    float tot = 0.f;
+#pragma unroll
+    for (int v = 0; v <= kXWaves; ++v) tot += s.ss[v];
+    const float inv = 1.f / sqrtf(tot / (float)kXD + a.eps);
+    xrec = make_uint2(f2bf(hreg[0] * inv) | (f2bf(hreg[1] * inv) << 16),
+                      f2bf(hreg[2] * inv) | (f2bf(hreg[3] * inv) << 16));
+    reinterpret_cast<uint2*>(s.xs)[tid] = xrec;
+  }
+  __syncthreads();
+  XRaw xr;
+  uint4 xv[4];
+  if (!ctl) {
+    load_x_raw(s.xs, lane, xr);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xv[m] = reinterpret_cast<const uint4*>(s.xs)[lane + 64 * m];
+    if (wave == 0) X_MARK(1);
+    x_wait_vm();  // this wave's staged rows (and register weights) have landed
+    if (wave == 0) X_MARK(2);
+  }
+  __syncthreads();
+
+  // ---- router layer: logits, hand-off of the logits within the XCD, top-K,
+  // then this layer's expert
+  if (la.router) {
+    const int nrw = (E + kXPerXcd - 1) / kXPerXcd;
+    if (!ctl) {
+      for (int m = wave; m < nrw; m += kXWaves) {
+        const float p = wave_sum(x_row_dot(s, m, xv));
+        if (lane == 0) s.lgp[m] = p;
+      }
+    }
+    __syncthreads();
+    if (ctl) {
+      if (lane < nrw && j + kXPerXcd * lane < E)
+        x_st64(xlog + j + kXPerXcd * lane, x_word(tag, __float_as_uint(s.lgp[lane])));
+      const bool ok = x_collect<kXMaxE / 64>(a, xlog, E, tag, min(E, 32), 1,
+                                             reinterpret_cast<uint32_t*>(s.lg));
+      if (lane == 0) s.go = ok ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s.go) return;
+    if (wave == 0) wave_topk_n<kXMaxE / 64, false>(s.lg, E, K, s.ids, s.wts);
+    __syncthreads();
+    {
+      const int id = s.ids[k];
+      slot = (id >= 0 && id < E) ? s.tbl[id] : -1;
+      if (slot < 0 || slot >= a.n_slots) slot = -1;
+      wk = s.wts[k];
+    }
+    if (lead && tid < K) {
+      la.exec_ids[tid] = s.ids[tid];
+      la.exec_w[tid] = s.wts[tid];
+    }
+    __syncthreads();  // every wave has read the router rows from LDS
+    if (!ctl) {
+      const uint8_t* b = x_bundle(a, slot);
+      x_stage_a(a, b, s);
+      x_load_gu<RW, NPW>(a, b, i0, gu);
+      x_load_dn<RW, NPW, CPL>(a, b, j, c0, dn);
+      x_wait_vm();
+    }
+    __syncthreads();
+  }
+  if (tid == 0 && slot < 0) set_error(a.err, EDGE0_ERANGE);
+
+  // ---- LoRA A x (A rows in LDS)
+  if (!ctl && r > 0) {
+    for (int ar = wave; ar < 2 * r; ar += kXWaves) {
+      const float p = wave_sum(x_row_dot(s, ar, xv));
+      if (lane == 0) s.t_s[ar] = p;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) X_MARK(3);
+
+  // ---- gate/up rows, LoRA B t, SwiGLU -> this workgroup's h words
+  if (!ctl) {
+    uint32_t xp[16];
+    const float Xs = x_pairs(xr, xp);
+    const Q4Consts kq = q4_consts();
+    constexpr int R = NPW <= 2 ? 2 : 4;
+    float v[2 * R];
+#pragma unroll
+    for (int i = 0; i < 2 * R; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NPW; ++m) {
+      const float s1 = bf2f(gu.sg[m]), b1 = bf2f(gu.bg[m]);
+      const float s2 = bf2f(gu.su[m]), b2 = bf2f(gu.bu[m]);
+      float G = s1 * chunk_dot128(gu.qg[m], xp, kq) + (b1 - 128.f * s1) * Xs;
+      float U = s2 * chunk_dot128(gu.qu[m], xp, kq) + (b2 - 128.f * s2) * Xs;
+      if (r > 0 && lane < r) {
+        G += a.scale * (bf2f(gu.Bg[m]) * s.t_s[lane]);
+        U += a.scale * (bf2f(gu.Bu[m]) * s.t_s[r + lane]);
+      }
+      v[m] = G;
+      v[R + m] = U;
+    }
+    const float w1 = wave_sums_2r<R>(v);
+    const float Uo = __shfl_xor(w1, 32, kWave);
+    constexpr int kSpan = 64 / (2 * R);
+    if (lane < 32 && (lane % kSpan) == 0) {
+      const int m = lane / kSpan;
+      const int q = wave + kXWaves * m;
+      if (m < NPW && q < RW) {
+        const float hv = silu_f(w1) * Uo;
+        const uint32_t hi = f2bf(hv);
+        const uint32_t lo = f2bf(hv - bf2f(hi));
+        s.hrow[q] = hi | (lo << 16);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- hand-off of h within the XCD (control wave)
+  if (ctl) {
+    if (lane < RW) x_st64(xh + j * RW + lane, x_word(tag, s.hrow[lane]));
+    X_MARK(4);
+    const bool ok = x_collect<RW / 2>(a, xh, a.Ix, tag, kXPerXcd, RW, s.hw);
+    if (lane == 0) s.go = ok ? 1 : 0;
+    X_MARK(5);
+  }
+  __syncthreads();
+  if (!s.go) return;
+
+  // ---- activation pairs and chunk sums of the slice; A_down h
+  if (!ctl) {
+    if (tid < 4 * RW) {
+      const int c = tid >> 2, m = tid & 3;
+      const uint32_t* src = s.hw + 32 * c + 8 * m;
+      uint32_t hi[4], lo[4];
+      float sm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w0 = src[2 * e], w1 = src[2 * e + 1];
+        hi[e] = (w0 & 0xFFFFu) | (w1 << 16);
+        lo[e] = (w0 >> 16) | (w1 & 0xFFFF0000u);
+        sm += (bf_lo(w0) + bf_hi(w0)) + (bf_lo(w1) + bf_hi(w1));
+      }
+      pair_perm8(hi[0], hi[1], hi[2], hi[3], &s.hp[c][4 * m]);
+      pair_perm8(lo[0], lo[1], lo[2], lo[3], &s.hp[c][16 + 4 * m]);
+      s.hsp[c][m] = sm;
+    }
+    if (r > 0) {
+      const int col0 = lane * 2 * CPL;
+      float p[kXTdRows];
+#pragma unroll
+      for (int t = 0; t < kXTdRows; ++t) {
+        p[t] = 0.f;
+#pragma unroll
+        for (int m = 0; m < CPL; ++m) {
+          const uint32_t h0 = s.hw[col0 + 2 * m], h1 = s.hw[col0 + 2 * m + 1];
+          p[t] = fmaf(bf_lo(dn.ad[t][m]), bf_lo(h0) + bf_hi(h0), p[t]);
+          p[t] = fmaf(bf_hi(dn.ad[t][m]), bf_lo(h1) + bf_hi(h1), p[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kXTdRows; ++t) {
+        const float sm = wave_sum(p[t]);
+        const int rr = wave + kXWaves * t;
+        if (lane == 0 && rr < r) s.td_s[rr] = sm;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- down tiles, weighted, into the layer's fixed-point y
+  if (wave == 0) X_MARK(6);
+  if (!ctl) {
+    const Q4Consts kq = q4_consts();
+    float part_sum = 0.f;
+#pragma unroll
+    for (int m = 0; m < NPW; ++m) {
+      const int cc = wave + kXWaves * m;
+      if (cc < RW) {
+        const float sv = bf2f(dn.sv[m]), bv = bf2f(dn.bv[m]);
+        const uint32_t* hp = s.hp[cc];
+        const float acc = chunk_dot128(dn.q[m], hp, kq) + chunk_dot128(dn.q[m], hp + 16, kq);
+        const float hs = (s.hsp[cc][0] + s.hsp[cc][1]) + (s.hsp[cc][2] + s.hsp[cc][3]);
+        part_sum += sv * acc + (bv - 128.f * sv) * hs;
+      }
+    }
+    s.red[wave][lane] = part_sum;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float D = 0.f;
+#pragma unroll
+    for (int v = 0; v < kXWaves; ++v) D += s.red[v][lane];
+    if (r > 0) {
+      const uint32_t bw[8] = {dn.bd[0].x, dn.bd[0].y, dn.bd[0].z, dn.bd[0].w,
+                              dn.bd[1].x, dn.bd[1].y, dn.bd[1].z, dn.bd[1].w};
+      float dl = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (2 * q < r) {
+          dl += bf_lo(bw[q]) * s.td_s[2 * q];
+          dl += bf_hi(bw[q]) * s.td_s[2 * q + 1];
+        }
+      }
+      D += a.scale * dl;
+    }
+    X_MARK(7);
+    atomicAdd(la.acc_out + 64 * j + lane, to_fix((slot >= 0 ? wk : 0.f) * D));
+  }
+  // records (workgroup 0): x_L, y_{L-1}, h_L
+  if (lead) {
+    reinterpret_cast<uint2*>(la.x_out)[tid] = xrec;
+    if (la.acc_in != nullptr) reinterpret_cast<uint2*>(la.y_prev_out)[tid] = yrec;
+    reinterpret_cast<uint2*>(la.h_out)[tid] =
+        make_uint2(f2bf(hreg[0]) | (f2bf(hreg[1]) << 16), f2bf(hreg[2]) | (f2bf(hreg[3]) << 16));
+  }
+}
+
+int launch_pred_slots(const int32_t* tables, const int32_t* ids, int32_t* slots, int n_layers,
+                      int E, int K, int n_slots, uint32_t* err, hipStream_t stream) {
+  k_pred_slots<<<1, 256, 0, stream>>>(tables, ids, slots, n_layers, E, K, n_slots, err);
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+
+int launch_xlayer(const XLArgs& la, hipStream_t stream, const LaunchTiming* timing) {
+  auto kern = la.base.RW == 12 ? k_xlayer<12> : la.base.RW == 24 ? k_xlayer<24> : nullptr;
+  if (kern == nullptr) return EDGE0_EINVAL;
+  if (timing && timing->which == 1) {
+    hipExtLaunchKernelGGL(kern, dim3(kXG), dim3(kXThreads), 0, stream, timing->start, timing->stop,
+                          0, la);
+  } else {
+    kern<<<kXG, kXThreads, 0, stream>>>(la);
+  }
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
 }
 
 bool xstep_shape_ok(const edge0_moe_shape& sh, int n_layers) {

@@ -275,6 +275,7 @@ EDGE0_GROUPED_NO_MFMA = 1
 EDGE0_STACK_GRAPHS = 0
 EDGE0_STACK_PERSISTENT = 1
 EDGE0_STACK_XCD = 2
+EDGE0_STACK_XLAYER = 3
 
 
 def grouped_mfma_min(n: int) -> int:

@@ -1,9 +1,11 @@
-"""GPU parity of the XCD-split persistent step (EDGE0_STACK_XCD) against the
-oracle, teacher-forced at every layer as in tests/test_gpu_stack.py: the
-40-layer Qwen3-MoE-shaped stack at K = 4 (the benchmark's configuration)
-and K = 8, with group biases independent of the scales, a 6-layer stack of
-wide layers, switching modes on one handle, the refused shapes, and a
-bounded wait forced to time out from the host."""
+"""GPU parity of the XCD-split modes against the oracle, teacher-forced at
+every layer as in tests/test_gpu_stack.py: the persistent step
+(EDGE0_STACK_XCD) and the per-layer launches replayed as graphs
+(EDGE0_STACK_XLAYER), on the 40-layer Qwen3-MoE-shaped stack at K = 4 (the
+benchmark's configuration) and K = 8, with group biases independent of the
+scales, a 6-layer stack of wide layers, switching modes and restarting at
+step 0 on one handle, the refused shapes, and a bounded wait forced to time
+out from the host."""
 import numpy as np
 import pytest
 
@@ -108,6 +110,87 @@ def test_xcd_mode_bounded_wait_reports_error(torch_cuda):
     S = G.QWEN3_MOE
     ds = DeviceStack(S, G.StackGen(S, 5), 4, (1, 2), (2, 3), log=None)
     E = _xcd(ds)
+    ds.stack.set_spin_limit(1)
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    ds.step(to_device(G.stack_hidden(S, 5, 0)), h_out, 0)
+    torch.cuda.synchronize()
+    assert ds.stack.error() == E.EDGE0_EHIP
+    ds.stack.close()
+
+
+# ---------------------------------------------------------------- XLAYER
+def _xlayer(ds):
+    from int4_expert_streaming_amd import edge0 as E
+    ds.stack.set_mode(E.EDGE0_STACK_XLAYER)
+    return E
+
+
+@pytest.mark.timeout(900)
+def test_xlayer_stack_qwen3moe_k4_every_layer(torch_cuda):
+    S, seed = G.QWEN3_MOE, 0
+    ds = _qwen3_stack(S, seed)
+    E = _xlayer(ds)
+    report, rels = _run(ds, S, seed, 4, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
+    assert ds.stack.error() == E.EDGE0_OK
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[xlayer] qwen3moe K=4: worst rel-L2 {max(rels):.3e}, median {np.median(rels):.3e}, "
+          f"waived {report.count('waived')}/{len(report)}")
+    # the graph mode on the same handle, then this mode again from step 0
+    ds.stack.set_mode(E.EDGE0_STACK_GRAPHS)
+    _run(ds, S, seed, 2, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
+    ds.stack.set_mode(E.EDGE0_STACK_XLAYER)
+    report, rels = _run(ds, S, seed, 8, lambda t: range(40) if t in (0, 1, 6, 7) else [7, 20],
+                        QWEN_OWNERS, QWEN_CONSUMERS)
+    assert ds.stack.error() == E.EDGE0_OK
+    ds.stack.close()
+
+
+@pytest.mark.timeout(900)
+def test_xlayer_stack_qwen3moe_free_bias(torch_cuda):
+    S, seed = G.QWEN3_MOE, 7
+    ds = _qwen3_stack(S, seed, free_bias=True)
+    E = _xlayer(ds)
+    report, rels = _run(ds, S, seed, 3, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS,
+                        free_bias=True)
+    assert ds.stack.error() == E.EDGE0_OK
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[xlayer] qwen3moe free bias: worst rel-L2 {max(rels):.3e}")
+    ds.stack.close()
+
+
+@pytest.mark.timeout(900)
+def test_xlayer_stack_qwen3moe_k8_every_layer(torch_cuda):
+    S, seed = G.QWEN3_MOE.with_k(8), 2
+    ds = _qwen3_stack(S, seed)
+    E = _xlayer(ds)
+    report, rels = _run(ds, S, seed, 3, lambda t: range(40), QWEN_OWNERS, QWEN_CONSUMERS)
+    assert ds.stack.error() == E.EDGE0_OK
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[xlayer] qwen3moe K=8: worst rel-L2 {max(rels):.3e}")
+    ds.stack.close()
+
+
+@pytest.mark.timeout(600)
+def test_xlayer_stack_wide_k8(torch_cuda):
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    S, seed = G.MoEShape(2048, 32, 384, 8, 64, 16, 32.0, 64), 11
+    owners, consumers = range(1, 5), range(2, 6)
+    ds = DeviceStack(S, G.StackGen(S, seed), 6, (1, 4), (2, 5), log=None)
+    E = _xlayer(ds)
+    report, rels = _run(ds, S, seed, 4, lambda t: range(6), owners, consumers)
+    assert ds.stack.error() == E.EDGE0_OK
+    assert report.count("exact") >= 0.8 * len(report), report
+    print(f"[xlayer] wide K=8: worst rel-L2 {max(rels):.3e}")
+    ds.stack.close()
+
+
+def test_xlayer_mode_bounded_wait_reports_error(torch_cuda):
+    import torch
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    from int4_expert_streaming_amd.weights import to_device
+    S = G.QWEN3_MOE
+    ds = DeviceStack(S, G.StackGen(S, 5), 4, (1, 2), (2, 3), log=None)
+    E = _xlayer(ds)
     ds.stack.set_spin_limit(1)
     h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
     ds.step(to_device(G.stack_hidden(S, 5, 0)), h_out, 0)
