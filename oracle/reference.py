@@ -17,8 +17,10 @@ library matrix-vector products as the only non-elementwise primitive.  Layer
 outputs are returned unrounded; the stack rounds to bf16 exactly where the
 method hands bf16 from one layer to the next.
 
-Decisions taken on floating point: routing ranks experts on the logits
-rounded to fp32 (the precision the GPU ranks in), ties to the lower index.
+Decisions taken on floating point: softmax-top-K ranks experts on the
+logits rounded to fp32 (the precision the GPU ranks in), ties to the lower
+index; sigmoid-group ranks groups and experts on fp32 scores built from the
+sigmoid rounded once to fp32 (see sigmoid_group_topk).
 
 Readings of points the pages leave open are stated where they are used and
 listed with the design notes.  Every function here is pinned by CPU tests
@@ -38,7 +40,7 @@ __all__ = [
     "silu", "gelu_erf", "expert_ffn", "moe_layer", "router_logits",
     "softmax_topk", "softmax_at", "prerouter_feature", "prerouter_logits", "prerouter_commit",
     "rmsnorm", "stack_layer", "stack_step", "canonical_requests", "lru_replay",
-    "grouped_layer", "topk_gap", "NoSlotError",
+    "grouped_layer", "topk_gap", "sigmoid_group_topk", "sigmoid_group_gaps", "NoSlotError",
 ]
 
 
@@ -191,6 +193,82 @@ def topk_gap(logits, k: int) -> float:
     """Gap between the k-th and (k+1)-th largest logit (inf when k = E)."""
     s = np.sort(np.asarray(logits, dtype=np.float64))[::-1]
     return float("inf") if k >= s.shape[0] else float(s[k - 1] - s[k])
+
+
+def _sigmoid64(l: np.ndarray) -> np.ndarray:
+    """sigmoid(l) = 1 / (1 + e^-l) in fp64 (e^-l overflowing gives 0)."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-l))
+
+
+def _sigmoid_group_scores(logits, n_groups: int, bias):
+    """fp32 selection scores c = fp32(fp32(sigmoid(l)) + bias) and the fp32
+    group scores (sum of each group's two largest c, largest first)."""
+    l = np.asarray(logits, dtype=np.float64)
+    E = l.shape[0]
+    b = np.zeros(E, np.float32) if bias is None else np.asarray(bias, dtype=np.float32)
+    c = (_sigmoid64(l).astype(np.float32) + b).astype(np.float32)
+    gs = E // n_groups
+    gscore = np.empty(n_groups, np.float32)
+    for i in range(n_groups):
+        top = sorted((float(c[e]) for e in range(i * gs, (i + 1) * gs)), reverse=True)
+        gscore[i] = np.float32(np.float32(top[0]) + np.float32(top[1]))
+    return c, gscore
+
+
+def sigmoid_group_topk(logits, k: int, n_groups: int, top_groups: int, scale: float,
+                       bias=None):
+    """Sigmoid-group routing, [Edge0] App. A "Sigmoid-group (K, G of n
+    groups, scale s)" and §2 "MoE routing" (the DeepSeek-V3 family):
+
+      sigma = sigmoid(l)
+      c     = sigma + bias          (selection score; bias = 0 when absent)
+      group i = experts [i E/n, (i+1) E/n); its score = the sum of its two
+              largest c; the top_groups groups by score survive, the others
+              are masked out
+      ids   = the k largest c among the surviving experts
+      w     = scale * sigma[ids] / (sum sigma[ids] + 1e-20)
+
+    Readings: the appendix says selection uses a biased score without
+    printing the bias, so the bias is a per-expert vector added to sigma
+    for the group scores and the top-k only, while the weights use the raw
+    sigma; groups are contiguous runs of E/n experts.  Decisions are taken
+    in fp32 (the precision the GPU decides in): sigma rounded once to fp32,
+    c and the group sums fp32 additions; groups and experts rank by (score
+    descending, index ascending).  ids are listed in that rank order.
+    Weights are fp64 on the fp64 sigma."""
+    l = np.asarray(logits, dtype=np.float64)
+    E = l.shape[0]
+    if n_groups < 1 or E % n_groups or E // n_groups < 2 or not 1 <= top_groups <= n_groups:
+        raise ValueError("sigmoid-group routing needs E % n == 0, E / n >= 2, 1 <= G <= n")
+    gs = E // n_groups
+    if not 1 <= k <= top_groups * gs:
+        raise ValueError("k must not exceed the experts of the surviving groups")
+    c, gscore = _sigmoid_group_scores(l, n_groups, bias)
+    keep = sorted(range(n_groups), key=lambda i: (-float(gscore[i]), i))[:top_groups]
+    alive = [e for i in keep for e in range(i * gs, (i + 1) * gs)]
+    ids = np.array(sorted(alive, key=lambda e: (-float(c[e]), e))[:k], dtype=np.int32)
+    sig = _sigmoid64(l)
+    w = scale * sig[ids] / (sig[ids].sum() + 1e-20)
+    return ids, w
+
+
+def sigmoid_group_gaps(logits, k: int, n_groups: int, top_groups: int, bias=None):
+    """The two margins a sigmoid-group decision rests on: between the
+    top_groups-th and next group score (inf when every group survives), and
+    between the k-th and (k+1)-th selection score among the surviving
+    experts (inf when all of them are taken).  A difference of a few fp32
+    ulps in sigma can flip a decision whose margin is that small."""
+    l = np.asarray(logits, dtype=np.float64)
+    E = l.shape[0]
+    gs = E // n_groups
+    c, gscore = _sigmoid_group_scores(l, n_groups, bias)
+    gsorted = sorted((float(v) for v in gscore), reverse=True)
+    ggap = float("inf") if top_groups >= n_groups else gsorted[top_groups - 1] - gsorted[top_groups]
+    keep = sorted(range(n_groups), key=lambda i: (-float(gscore[i]), i))[:top_groups]
+    alive = sorted((float(c[e]) for i in keep for e in range(i * gs, (i + 1) * gs)), reverse=True)
+    egap = float("inf") if k >= len(alive) else alive[k - 1] - alive[k]
+    return ggap, egap
 
 
 # --------------------------------------------------------------------------
