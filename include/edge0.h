@@ -78,7 +78,19 @@ typedef struct {
   int32_t lora_rank;    /* r: recovery-LoRA rank, 0 = no adapter */
   float lora_alpha;     /* alpha: the delta is scaled by alpha / r */
   int32_t head_hidden;  /* H: prerouter fc1 width */
+  int32_t routing;      /* routing family of the commit: EDGE0_ROUTE_* */
+  int32_t n_groups;     /* sigmoid-group: n groups of E / n contiguous experts */
+  int32_t top_groups;   /* sigmoid-group: G groups survive */
+  float route_scale;    /* sigmoid-group: s, the K weights sum to s */
 } edge0_moe_shape;
+
+/* Routing families ([Edge0] §2 "MoE routing", App. A).  A zero-filled shape
+ * is softmax-top-K; the sigmoid-group fields are read only for family 1,
+ * which needs E % n == 0, E / n >= 2, n <= 64, 1 <= G <= n,
+ * K <= G * E / n and a finite s.  The decode stack (edge0_stack_create)
+ * takes softmax-top-K only. */
+#define EDGE0_ROUTE_SOFTMAX_TOPK 0
+#define EDGE0_ROUTE_SIGMOID_GROUP 1
 
 /* -------------------------------------------------------------------------
  * Expert bundle = the content of one slot ([Edge0] §3.1 "Executor paths":
@@ -150,18 +162,36 @@ size_t edge0_workspace_bytes(const edge0_moe_shape* shape);
 int edge0_workspace_error(void* workspace, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
- * Plain router + softmax-top-K commit ([Edge0] §2 "MoE routing", App. A
- * "Softmax-topk"): logits = W_r x (fp32 accumulation); ids = the K largest
- * logits in order (value descending, lower index first on ties);
- * w_k = exp(l_k - l_max) / sum_{j in ids} exp(l_j - l_max), which equals
- * g[ids]/sum g[ids] for g = softmax(l).
+ * The commit of a routing from logits l [E] ([Edge0] §2 "MoE routing",
+ * App. A), by shape->routing:
+ *  softmax-top-K ("Softmax-topk"): ids = the K largest logits in order
+ *    (value descending, lower index first on ties); w_k = exp(l_k - l_max) /
+ *    sum_{j in ids} exp(l_j - l_max), which equals g[ids]/sum g[ids] for
+ *    g = softmax(l).
+ *  sigmoid-group ("Sigmoid-group"): sigma = sigmoid(l); selection score
+ *    c = sigma + route_bias (the bias is 0 when route_bias is NULL);
+ *    group i = experts [i E/n, (i+1) E/n), scored by the sum of its two
+ *    largest c; the G best groups survive (lower group first on ties);
+ *    ids = the K largest c among their experts, in rank order (lower index
+ *    first on ties); w_k = s * sigma[ids_k] / (sum_j sigma[ids_j] + 1e-20).
+ *    The bias steers the choice only; the weights use the raw sigmoid.
+ * Decisions are taken on fp32 scores; NaN ranks lowest.
+ *   route_bias : device fp32 [E] or NULL (read by sigmoid-group only)
+ *   ids_out    : device int32 [K];  w_out : device fp32 [K]
+ * ---------------------------------------------------------------------- */
+
+/* The commit alone, from device fp32 logits [E] (one wave; no workspace). */
+int edge0_route_commit(const edge0_moe_shape* shape, const float* logits,
+                       const float* route_bias, int32_t* ids_out, float* w_out,
+                       hipStream_t stream);
+
+/* Plain router: logits = W_r x (fp32 accumulation), then the commit above.
  *   w_router : device bf16 [E][d]
  *   x        : device bf16 [d]
  *   logits_out : device fp32 [E] or NULL
- *   ids_out  : device int32 [K];  w_out : device fp32 [K]
  * ---------------------------------------------------------------------- */
-int edge0_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
-                 float* logits_out, int32_t* ids_out, float* w_out,
+int edge0_router(const edge0_moe_shape* shape, const void* w_router, const float* route_bias,
+                 const void* x, float* logits_out, int32_t* ids_out, float* w_out,
                  void* workspace, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
@@ -172,7 +202,10 @@ int edge0_router(const edge0_moe_shape* shape, const void* w_router, const void*
  *   f      = [x ; onehot(ids_now) ; onehot(ids_prev)]        (d + 2E)
  *   z1     = fc1 f + b1,  a = 0.5 z1 (1 + erf(z1 / sqrt 2))   (H)
  *   logits = w2 a + b2 + wl x                                 (E)
- * then the same softmax-top-K as edge0_router.  The one-hot blocks hold a 1
+ * then the same commit as edge0_router (shape->routing; route_bias is the
+ * predicted layer's selection bias for sigmoid-group, or NULL: the
+ * prediction is routed through the same math, [Edge0] §2 "MoE routing",
+ * §3.2 "Prediction-as-routing").  The one-hot blocks hold a 1
  * per routed expert (binary, not weighted); ids_now is the routing layer N
  * executed at token t, ids_prev the routing it executed at token t-1 (NULL
  * at the first decode token: that block is zero).
@@ -186,7 +219,8 @@ typedef struct {
   const void *w1x, *w1oh, *b1, *w2, *b2, *wl;
 } edge0_head;
 
-int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* head, const void* x,
+int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* head,
+                    const float* route_bias, const void* x,
                     const int32_t* ids_now, const int32_t* ids_prev,
                     float* logits_out, int32_t* ids_out, float* w_out,
                     void* workspace, hipStream_t stream);

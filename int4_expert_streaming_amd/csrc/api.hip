@@ -19,6 +19,16 @@ bool shape_ok(const edge0_moe_shape* s) {
   if (!(r == 0 || r == 8 || r == 16 || r == 32 || r == 64)) return false;
   if (s->lora_rank > 0 && !(s->lora_alpha == s->lora_alpha)) return false;
   if (s->head_hidden < 0 || s->head_hidden % 64 != 0) return false;
+  if (s->routing == EDGE0_ROUTE_SIGMOID_GROUP) {
+    const int n = s->n_groups, G = s->top_groups;
+    if (n < 1 || n > 64 || E % n != 0 || E / n < 2 || G < 1 || G > n || K > G * (E / n))
+      return false;
+    if (!(s->route_scale == s->route_scale) || s->route_scale == INFINITY ||
+        s->route_scale == -INFINITY)
+      return false;
+  } else if (s->routing != EDGE0_ROUTE_SOFTMAX_TOPK) {
+    return false;
+  }
   return true;
 }
 

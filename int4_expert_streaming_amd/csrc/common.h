@@ -377,6 +377,101 @@ __device__ __forceinline__ void wave_topk(const float* logits, int E, int K, int
   }
 }
 
+// Routing rule of a commit ([Edge0] App. A): kind 0 = softmax-top-K,
+// kind 1 = sigmoid-group with n_groups contiguous groups of E / n_groups
+// experts, top_groups of them surviving, weights scaled by `scale`, and an
+// optional per-expert selection bias (fp32 [E], NULL = 0).
+struct RouteRule {
+  int kind;
+  int n_groups, top_groups;
+  float scale;
+  const float* bias;
+};
+
+__device__ __forceinline__ float sigmoid_f(float l) { return 1.f / (1.f + expf(-l)); }
+
+// Sigmoid-group commit by one wave ([Edge0] App. A "Sigmoid-group"; §2 "MoE
+// routing"): sigma = sigmoid(l); selection score c = sigma + bias; a group's
+// score is the sum of its two largest c; the top_groups groups survive
+// (score descending, lower group first on ties); ids = the K largest c of
+// the survivors (lower index first on ties), listed in rank order;
+// w = scale * sigma[ids] / (sum of those sigma + 1e-20).  Decisions in fp32;
+// NaN scores rank lowest.  E = NPER * 64 at most, n_groups <= 64, K <= 16,
+// K <= top_groups * E / n_groups (checked by the caller).
+template <int NPER, bool COHERENT>
+__device__ __forceinline__ void wave_sigmoid_group_n(const float* logits, int E, int K,
+                                                     const RouteRule& rr, int32_t* ids_out,
+                                                     float* w_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = rr.n_groups, gs = E / n;
+  auto score = [&](int e) {
+    const float l = COHERENT ? ld_dev(logits + e) : logits[e];
+    return sigmoid_f(l) + (rr.bias != nullptr ? rr.bias[e] : 0.f);
+  };
+  // group scores: lane i scans group i
+  unsigned long long gkey = 0ull;
+  if (lane < n) {
+    float t1 = -INFINITY, t2 = -INFINITY;
+    for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+      const float c = score(e);
+      if (c > t1) {
+        t2 = t1;
+        t1 = c;
+      } else if (c > t2) {
+        t2 = c;
+      }
+    }
+    gkey = topk_key(t1 + t2, lane);
+  }
+  unsigned long long alive = 0ull;  // bit i: group i survives
+  for (int gg = 0; gg < rr.top_groups; ++gg) {
+    const unsigned long long best = wave_keymax(gkey);
+    alive |= 1ull << (int)~(uint32_t)best;
+    gkey = gkey == best ? 0ull : gkey;
+  }
+  unsigned long long key[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int idx = lane + kWave * j;
+    key[j] = (idx < E && ((alive >> (idx / gs)) & 1ull)) ? topk_key(score(idx), idx) : 0ull;
+  }
+  unsigned long long mine = 0;  // lane kk keeps the kk-th pick
+  for (int kk = 0; kk < K; ++kk) {
+    unsigned long long best = key[0];
+#pragma unroll
+    for (int j = 1; j < NPER; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_keymax(best);
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) key[j] = key[j] == best ? 0ull : key[j];
+    mine = lane == kk ? best : mine;
+  }
+  const int my_i = (int)~(uint32_t)mine;
+  float sg = 0.f;
+  if (lane < K) sg = sigmoid_f(COHERENT ? ld_dev(logits + my_i) : logits[my_i]);
+  float den = 0.f;
+  for (int j = 0; j < K; ++j)  // fixed order
+    den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sg), j));
+  if (lane < K) {
+    ids_out[lane] = my_i;
+    w_out[lane] = rr.scale * sg / (den + 1e-20f);
+  }
+}
+
+// The commit a rule names, by one wave (E <= 1024, K <= 16).
+template <bool COHERENT>
+__device__ __forceinline__ void wave_commit(const float* logits, int E, int K, const RouteRule& rr,
+                                            int32_t* ids_out, float* w_out) {
+  if (rr.kind == 0) {
+    wave_topk<COHERENT>(logits, E, K, ids_out, w_out);
+  } else if (E <= 128) {
+    wave_sigmoid_group_n<2, COHERENT>(logits, E, K, rr, ids_out, w_out);
+  } else if (E <= 256) {
+    wave_sigmoid_group_n<4, COHERENT>(logits, E, K, rr, ids_out, w_out);
+  } else {
+    wave_sigmoid_group_n<16, COHERENT>(logits, E, K, rr, ids_out, w_out);
+  }
+}
+
 // Weights of a routing whose ids are given: w_k = exp(l[id_k] - m) /
 // sum_j exp(l[id_j] - m), m the largest of the K logits (g[ids] / sum g[ids]
 // for g = softmax(l)).  Lanes 0..K-1 of one wave; an id outside [0, E) gets

@@ -132,6 +132,7 @@ struct HeadBatch {
   float* w_out;
   int out_stride;
   uint32_t* err;
+  RouteRule rule;                    // the commit (kind 0 in the stack)
 };
 int launch_heads(const HeadBatch& hb, hipStream_t stream);
 
@@ -256,8 +257,10 @@ int launch_xlayer(const XLArgs& a, hipStream_t stream, const LaunchTiming* timin
 int launch_pred_slots(const int32_t* tables, const int32_t* ids, int32_t* slots, int n_layers,
                       int E, int K, int n_slots, uint32_t* err, hipStream_t stream);
 
-int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
-                  const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
-                  int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream);
+RouteRule route_rule(const edge0_moe_shape* shape, const float* bias);
+int launch_router(const edge0_moe_shape* shape, const void* w_router, const float* route_bias,
+                  const void* x, const uint16_t* h_norm, uint16_t* x_out, float eps,
+                  float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
+                  hipStream_t stream);
 
 }  // namespace e0

@@ -1,9 +1,10 @@
-// Routing kernels: the plain router GEMV, the prerouter head and the
-// softmax-top-K commit.
+// Routing kernels: the plain router GEMV, the prerouter head and the commit
+// (softmax-top-K or sigmoid-group).
 //
 // [Edge0] = "The Other Half of the Memory Wall: Serving 35B MoEs from SSD
 // with Trained Routing Prediction".  Routing math: §2 "MoE routing" and
-// App. A "Softmax-topk"; head: §3.2 "Head", "Prediction-as-routing".
+// App. A "Softmax-topk", "Sigmoid-group"; head: §3.2 "Head",
+// "Prediction-as-routing".
 //
 // The GEMVs here are small (router E x d bf16; head fc1 H x d fp16 plus the
 // residual E x d, fc2 E x H) and HBM-bound: one wave per output row, 16-byte
@@ -21,7 +22,8 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ wr,
                                                 const uint16_t* __restrict__ x_in,
                                                 const uint16_t* __restrict__ h_norm,
                                                 uint16_t* __restrict__ x_out, float eps, int d,
-                                                int E, int K, float* __restrict__ logits,
+                                                int E, int K, RouteRule rr,
+                                                float* __restrict__ logits,
                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                 uint32_t* __restrict__ counter) {
   __shared__ uint16_t xs[kMaxD];
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ wr,
     if ((threadIdx.x & 63) == 0) st_dev(logits + row, s);
   }
   if (last_arrival(counter, gridDim.x)) {
-    if (wave == 0) wave_topk<true>(logits, E, K, ids, w);
+    if (wave == 0) wave_commit<true>(logits, E, K, rr, ids, w);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -165,8 +167,8 @@ __global__ __launch_bounds__(1024) void k_heads_fc2(HeadBatch hb) {
   }
   __syncthreads();
   if (wave == 0)
-    wave_topk<false>(lg_s, E, K, hb.ids_out + (size_t)i * hb.out_stride,
-                     hb.w_out + (size_t)i * hb.out_stride);
+    wave_commit<false>(lg_s, E, K, hb.rule, hb.ids_out + (size_t)i * hb.out_stride,
+                       hb.w_out + (size_t)i * hb.out_stride);
 }
 
 int launch_heads(const HeadBatch& hb, hipStream_t stream) {
@@ -184,35 +186,46 @@ int launch_heads(const HeadBatch& hb, hipStream_t stream) {
 using namespace e0;
 
 namespace e0 {
-int launch_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
-                  const uint16_t* h_norm, uint16_t* x_out, float eps, float* logits_out,
-                  int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream) {
+RouteRule route_rule(const edge0_moe_shape* shape, const float* bias) {
+  RouteRule rr{};
+  rr.kind = shape->routing;
+  rr.n_groups = shape->n_groups;
+  rr.top_groups = shape->top_groups;
+  rr.scale = shape->route_scale;
+  rr.bias = bias;
+  return rr;
+}
+
+int launch_router(const edge0_moe_shape* shape, const void* w_router, const float* route_bias,
+                  const void* x, const uint16_t* h_norm, uint16_t* x_out, float eps,
+                  float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
+                  hipStream_t stream) {
   const WsLayout L = ws_layout(shape);
   char* ws = static_cast<char*>(workspace);
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + L.logits);
   const int E = shape->n_experts;
   k_router<<<(E + 3) / 4, 256, 0, stream>>>(
       static_cast<const uint16_t*>(w_router), static_cast<const uint16_t*>(x), h_norm, x_out, eps,
-      shape->d_model, E, shape->top_k, logits, ids_out, w_out,
+      shape->d_model, E, shape->top_k, route_rule(shape, route_bias), logits, ids_out, w_out,
       reinterpret_cast<uint32_t*>(ws + L.cnt_router));
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
 }  // namespace e0
 
-extern "C" int edge0_router(const edge0_moe_shape* shape, const void* w_router, const void* x,
-                            float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
-                            hipStream_t stream) {
+extern "C" int edge0_router(const edge0_moe_shape* shape, const void* w_router,
+                            const float* route_bias, const void* x, float* logits_out,
+                            int32_t* ids_out, float* w_out, void* workspace, hipStream_t stream) {
   if (!shape || !shape_ok(shape) || !w_router || !x || !ids_out || !w_out || !workspace)
     return EDGE0_EINVAL;
-  return launch_router(shape, w_router, x, nullptr, nullptr, 0.f, logits_out, ids_out, w_out,
-                       workspace, stream);
+  return launch_router(shape, w_router, route_bias, x, nullptr, nullptr, 0.f, logits_out, ids_out,
+                       w_out, workspace, stream);
 }
 
 extern "C" int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* head,
-                               const void* x, const int32_t* ids_now, const int32_t* ids_prev,
-                               float* logits_out, int32_t* ids_out, float* w_out,
-                               void* workspace, hipStream_t stream) {
+                               const float* route_bias, const void* x, const int32_t* ids_now,
+                               const int32_t* ids_prev, float* logits_out, int32_t* ids_out,
+                               float* w_out, void* workspace, hipStream_t stream) {
   if (!shape || !shape_ok(shape) || !head || !head->w1x || !head->w1oh || !head->w2 || !x ||
       !ids_now || !ids_out || !w_out || !workspace || shape->head_hidden <= 0)
     return EDGE0_EINVAL;
@@ -241,5 +254,24 @@ extern "C" int edge0_prerouter(const edge0_moe_shape* shape, const edge0_head* h
   hb.ids_out = ids_out;
   hb.w_out = w_out;
   hb.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  hb.rule = route_rule(shape, route_bias);
   return launch_heads(hb, stream);
+}
+
+namespace e0 {
+__global__ __launch_bounds__(64) void k_commit(const float* __restrict__ logits, int E, int K,
+                                               RouteRule rr, int32_t* __restrict__ ids,
+                                               float* __restrict__ w) {
+  wave_commit<false>(logits, E, K, rr, ids, w);
+}
+}  // namespace e0
+
+extern "C" int edge0_route_commit(const edge0_moe_shape* shape, const float* logits,
+                                  const float* route_bias, int32_t* ids_out, float* w_out,
+                                  hipStream_t stream) {
+  if (!shape || !shape_ok(shape) || !logits || !ids_out || !w_out) return EDGE0_EINVAL;
+  k_commit<<<1, 64, 0, stream>>>(logits, shape->n_experts, shape->top_k,
+                                 route_rule(shape, route_bias), ids_out, w_out);
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
 }

@@ -473,6 +473,8 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   if (!out || !shape || !shape_ok(shape) || !spec || !pool || !pool->base || !slot_tables ||
       !routers || !heads)
     return EDGE0_EINVAL;
+  // the step's fused routing (router layers and heads) is softmax-top-K
+  if (shape->routing != EDGE0_ROUTE_SOFTMAX_TOPK) return EDGE0_EINVAL;
   const int Lc = spec->n_layers;
   if (Lc < 1 || spec->rms_eps < 0.f) return EDGE0_EINVAL;
   if (spec->owner_last - spec->owner_first + 1 > kMaxHeads) return EDGE0_EINVAL;

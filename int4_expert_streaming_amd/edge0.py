@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libedge0.so")
 
 EDGE0_OK, EDGE0_EINVAL, EDGE0_EHIP, EDGE0_ENOSLOT, EDGE0_ERANGE, EDGE0_ENOMEM = 0, -1, -2, -3, -4, -5
 EDGE0_ESCRATCH = -6
+EDGE0_ROUTE_SOFTMAX_TOPK = 0
+EDGE0_ROUTE_SIGMOID_GROUP = 1
 EDGE0_STATIC_WORKSPACE_BYTES = 1 << 20
 
 
@@ -78,7 +80,8 @@ class _Handle:
 class MoeShape(C.Structure):
     _fields_ = [("d_model", C.c_int32), ("n_experts", C.c_int32), ("d_inter", C.c_int32),
                 ("top_k", C.c_int32), ("group_size", C.c_int32), ("lora_rank", C.c_int32),
-                ("lora_alpha", C.c_float), ("head_hidden", C.c_int32)]
+                ("lora_alpha", C.c_float), ("head_hidden", C.c_int32), ("routing", C.c_int32),
+                ("n_groups", C.c_int32), ("top_groups", C.c_int32), ("route_scale", C.c_float)]
 
 
 _LAYOUT_KEYS = ("gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b", "down_q", "down_s",
@@ -133,9 +136,10 @@ _SIG = {
     "edge0_pack_bundle": (C.c_int, [C.POINTER(MoeShape), C.POINTER(ExpertArrays), _P, _P]),
     "edge0_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
     "edge0_workspace_error": (C.c_int, [_P, _P]),
-    "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P]),
+    "edge0_route_commit": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P]),
+    "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P]),
     "edge0_prerouter": (C.c_int, [C.POINTER(MoeShape), C.POINTER(Head), _P, _P, _P, _P, _P, _P,
-                                  _P, _P]),
+                                  _P, _P, _P]),
     "edge0_stack_set_trace": (C.c_int, [_P, C.c_int32, _P]),
     "edge0_moe_layer_noalloc": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P,
                                           _P, _P, _P, _P]),
@@ -201,11 +205,14 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def make_shape(s) -> MoeShape:
+def make_shape(s, routing: int = 0, n_groups: int = 0, top_groups: int = 0,
+               route_scale: float = 0.0) -> MoeShape:
     """MoeShape from any object with the MoE spec fields (d_model, n_experts,
-    d_inter, top_k, group, lora_rank, lora_alpha, head_hidden)."""
+    d_inter, top_k, group, lora_rank, lora_alpha, head_hidden), plus the
+    routing family (EDGE0_ROUTE_*) and its sigmoid-group parameters."""
     return MoeShape(s.d_model, s.n_experts, s.d_inter, s.top_k, s.group, s.lora_rank,
-                    float(s.lora_alpha), s.head_hidden)
+                    float(s.lora_alpha), s.head_hidden, routing, n_groups, top_groups,
+                    float(route_scale))
 
 
 # --------------------------------------------------------------------- calls
@@ -238,11 +245,16 @@ def edge0_pack_bundle(shape: MoeShape, arrays: dict, bundle_dst, stream=None):
            "edge0_pack_bundle")
 
 
+def edge0_route_commit(shape: MoeShape, logits, ids_out, w_out, route_bias=None, stream=None):
+    _check(lib.edge0_route_commit(C.byref(shape), _ptr(logits), _ptr(route_bias), _ptr(ids_out),
+                                  _ptr(w_out), _stream(stream)), "edge0_route_commit")
+
+
 def edge0_router(shape: MoeShape, w_router, x, logits_out, ids_out, w_out, workspace,
-                 stream=None):
-    _check(lib.edge0_router(C.byref(shape), _ptr(w_router), _ptr(x), _ptr(logits_out),
-                            _ptr(ids_out), _ptr(w_out), _ptr(workspace), _stream(stream)),
-           "edge0_router")
+                 stream=None, route_bias=None):
+    _check(lib.edge0_router(C.byref(shape), _ptr(w_router), _ptr(route_bias), _ptr(x),
+                            _ptr(logits_out), _ptr(ids_out), _ptr(w_out), _ptr(workspace),
+                            _stream(stream)), "edge0_router")
 
 
 def make_head(tensors: dict) -> Head:
@@ -250,8 +262,9 @@ def make_head(tensors: dict) -> Head:
 
 
 def edge0_prerouter(shape: MoeShape, head: Head, x, ids_now, ids_prev, logits_out, ids_out, w_out,
-                    workspace, stream=None):
-    _check(lib.edge0_prerouter(C.byref(shape), C.byref(head), _ptr(x), _ptr(ids_now),
+                    workspace, stream=None, route_bias=None):
+    _check(lib.edge0_prerouter(C.byref(shape), C.byref(head), _ptr(route_bias), _ptr(x),
+                               _ptr(ids_now),
                                _ptr(ids_prev), _ptr(logits_out), _ptr(ids_out), _ptr(w_out),
                                _ptr(workspace), _stream(stream)), "edge0_prerouter")
 

@@ -68,7 +68,9 @@ def test_bad_shapes_rejected(E):
 def test_null_arguments_rejected_before_launch(E):
     from synth import gen as G
     s = E.make_shape(G.TINY)
-    assert E.lib.edge0_router(C.byref(s), None, None, None, None, None, None, None) == E.EDGE0_EINVAL
+    assert E.lib.edge0_router(C.byref(s), None, None, None, None, None, None, None,
+                              None) == E.EDGE0_EINVAL
+    assert E.lib.edge0_route_commit(C.byref(s), None, None, None, None, None) == E.EDGE0_EINVAL
     assert E.lib.edge0_moe_layer(C.byref(s), None, None, None, None, None, None, None,
                                  None) == E.EDGE0_EINVAL
     pool = E.SlotPool(4096, 1000, 4)     # slot_bytes smaller than a bundle
@@ -104,3 +106,38 @@ def test_staging_calls_reject_null_arguments(E):
     st = E.StageStats()
     assert E.lib.edge0_stager_stats(None, C.byref(st)) == E.EDGE0_EINVAL
     assert E.lib.edge0_lru_create(C.byref(h), 0, 1, 8) == E.EDGE0_EINVAL
+
+
+def test_routing_fields_validated(E):
+    """Sigmoid-group needs E % n == 0, E / n >= 2, n <= 64, 1 <= G <= n,
+    K <= G E / n and a finite scale; an unknown family is rejected."""
+    from synth import gen as G
+    S = G.QWEN3_MOE.with_k(8)  # E = 128
+    SG = E.EDGE0_ROUTE_SIGMOID_GROUP
+    good = [E.make_shape(S), E.make_shape(S, SG, 8, 4, 2.5), E.make_shape(S, SG, 64, 4, 1.0),
+            E.make_shape(S, SG, 1, 1, 1.0), E.make_shape(S, SG, 8, 8, -3.0)]
+    for s in good:
+        assert E.lib.edge0_workspace_bytes(C.byref(s)) > 0
+    bad = [E.make_shape(S, 2), E.make_shape(S, -1), E.make_shape(S, SG, 0, 1, 1.0),
+           E.make_shape(S, SG, 3, 1, 1.0), E.make_shape(S, SG, 128, 4, 1.0),
+           E.make_shape(S, SG, 8, 0, 1.0), E.make_shape(S, SG, 8, 9, 1.0),
+           E.make_shape(S, SG, 32, 1, 1.0),  # K = 8 > 1 group of 4
+           E.make_shape(S, SG, 8, 4, float("nan")), E.make_shape(S, SG, 8, 4, float("inf"))]
+    for s in bad:
+        assert E.lib.edge0_workspace_bytes(C.byref(s)) == 0
+
+
+def test_stack_refuses_sigmoid_group(E):
+    # the decode stack's fused routing is softmax-top-K: another family is
+    # refused before anything is allocated or launched (placeholder pointers)
+    from synth import gen as G
+    s = E.make_shape(G.QWEN3_MOE, E.EDGE0_ROUTE_SIGMOID_GROUP, 8, 4, 2.5)
+    spec = E.StackSpec()
+    spec.n_layers = 4
+    pool = E.SlotPool(0x1000, 1 << 24, 4)
+    handle = C.c_void_p()
+    routers = (C.c_void_p * 4)(0x1000, 0x1000, 0x1000, 0x1000)
+    heads = (E.Head * 4)()
+    assert E.lib.edge0_stack_create(C.byref(handle), C.byref(s), C.byref(spec), C.byref(pool),
+                                    0x1000, routers, heads) == E.EDGE0_EINVAL
+    assert not handle.value
