@@ -530,8 +530,8 @@ int edge0_stager_set_copy_mode(edge0_stager* sg, int32_t mode);
 int edge0_stager_stats(const edge0_stager* sg, edge0_stage_stats* out);
 void edge0_stager_destroy(edge0_stager* sg);
 
-/* One decode step of the stack over a staged pool, with the routing ids of
- * every layer given (a routing trace): the weights are the softmax of the
+/* One decode step of the stack over a staged pool.  With ahead = 0 or 1 the
+ * routing ids of every layer are given (a routing trace): the weights are the softmax of the
  * layer's own logits taken at the given ids, w = g[ids] / sum g[ids]
  * ([Edge0] App. A), from the plain router of the layer or, for a
  * prediction-routed layer, from the logits its head produced at the
@@ -548,15 +548,27 @@ void edge0_stager_destroy(edge0_stager* sg);
  *   ids_host : host int32 [n_layers][K], the same ids
  *   next_ids_host : host int32 [n_layers][K], the routing of step + 1 (ahead
  *     = 1; NULL on the last step: nothing is prefetched)
+ *   ahead = EDGE0_STAGE_LOOP (2, the closed loop of [Edge0] §3.2
+ *     "Motivation" and "Prediction-as-routing"): no routing is given (ids_*
+ *     may be NULL).  A router layer commits the softmax-top-K of its own
+ *     router on the device; the host reads those K ids back (a wait on
+ *     `stream`) and fills the set on demand.  A prediction-routed layer
+ *     (step > 0) executes the routing its owner's head committed at the
+ *     previous step, staged one step ahead.  After the batched heads the
+ *     host reads every prediction back once (one wait on `stream`) and
+ *     requests the next step's predicted sets on copy_stream: the staged
+ *     set is the routed set.  The executed routing is in the buffers'
+ *     ids/w, the predictions in pred_ids/pred_w (edge0_stack_get_buffers).
  * The stack must have been created on the stager's pool and slot table.
  * Enqueued directly (not as a graph).  The requests follow the canonical
  * order: per layer its own request (if any) before it computes and its
  * release after; the next step's predicted sets after the last layer. */
+#define EDGE0_STAGE_LOOP 2
 typedef struct {
   const int32_t* ids_dev;
   const int32_t* ids_host;
   const int32_t* next_ids_host;
-  int32_t ahead;
+  int32_t ahead;              /* 0 on demand, 1 prediction arm, EDGE0_STAGE_LOOP */
   hipStream_t copy_stream;
 } edge0_stage_plan;
 int edge0_stack_step_staged(edge0_stack* st, edge0_stager* sg, const edge0_stage_plan* plan,

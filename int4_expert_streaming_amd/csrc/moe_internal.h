@@ -258,6 +258,9 @@ int launch_pred_slots(const int32_t* tables, const int32_t* ids, int32_t* slots,
                       int E, int K, int n_slots, uint32_t* err, hipStream_t stream);
 
 RouteRule route_rule(const edge0_moe_shape* shape, const float* bias);
+// the commit alone (one wave): ids/w of the K chosen experts from logits [E]
+int launch_commit(const float* logits, int E, int K, const RouteRule& rr, int32_t* ids, float* w,
+                  hipStream_t stream);
 int launch_router(const edge0_moe_shape* shape, const void* w_router, const float* route_bias,
                   const void* x, const uint16_t* h_norm, uint16_t* x_out, float eps,
                   float* logits_out, int32_t* ids_out, float* w_out, void* workspace,

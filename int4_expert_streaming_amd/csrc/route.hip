@@ -266,6 +266,15 @@ __global__ __launch_bounds__(64) void k_commit(const float* __restrict__ logits,
 }
 }  // namespace e0
 
+namespace e0 {
+int launch_commit(const float* logits, int E, int K, const RouteRule& rr, int32_t* ids, float* w,
+                  hipStream_t stream) {
+  k_commit<<<1, 64, 0, stream>>>(logits, E, K, rr, ids, w);
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+}  // namespace e0
+
 extern "C" int edge0_route_commit(const edge0_moe_shape* shape, const float* logits,
                                   const float* route_bias, int32_t* ids_out, float* w_out,
                                   hipStream_t stream) {

@@ -69,6 +69,7 @@ struct edge0_stack {
   std::vector<hipEvent_t> ev_start, ev_stop;  // one pair per layer
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
   hipEvent_t ev_heads;       // staged steps: the heads of the step have run
+  int32_t* loop_host;        // staged closed loop: pinned [2][L][K] ids read back
   // persistent mode (EDGE0_STACK_PERSISTENT)
   int mode;
   uint32_t* flow_cnt;                // [kFlowMaxPhases][kFlowCounters][64] arrival counters
@@ -648,6 +649,7 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers, E = sh.n_experts;
   const bool ahead = plan.ahead != 0;
+  const bool loop = plan.ahead == EDGE0_STAGE_LOOP;
   float* w_exec = st->exec_w[step & 1];
   MoeArgs a{};
   int rc;
@@ -655,7 +657,11 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
     uint16_t* hL = st->h + (size_t)L * d;
     uint16_t* xL = st->x + (size_t)L * d;
     const bool by_pred = ahead && is_consumer(st->spec, L) && step > 0;
-    const int32_t* ids = plan.ids_dev + (size_t)L * K;
+    // closed loop: a prediction-routed layer executes its head's committed
+    // routing, a router layer the top-K of its own router
+    const int32_t* ids =
+        loop ? (by_pred ? st->pred_ids[step % 3] : st->exec_ids[step & 1]) + (size_t)L * K
+             : plan.ids_dev + (size_t)L * K;
     float* w = w_exec + (size_t)L * K;
     rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
                        st->y + (size_t)L * d, st->ws, &a);
@@ -685,8 +691,20 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
       li.w_router = static_cast<const uint16_t*>(st->routers[L]);
       li.logits = st->logits;
       if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
-      if ((rc = edge0_stage_experts(sg, L, step, plan.ids_host + (size_t)L * K, K, nullptr,
-                                    stream)) != EDGE0_OK ||
+      const int32_t* want = loop ? nullptr : plan.ids_host + (size_t)L * K;
+      if (loop) {
+        // commit on the device; the host learns the set by reading it back
+        int32_t* exec = st->exec_ids[step & 1] + (size_t)L * K;
+        RouteRule rr{};
+        if ((rc = launch_commit(st->logits, E, K, rr, exec, w, stream)) != EDGE0_OK) return rc;
+        if (hipMemcpyAsync(st->loop_host + (size_t)L * K, exec, (size_t)K * 4,
+                           hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+          return EDGE0_EHIP;
+        want = st->loop_host + (size_t)L * K;
+        if (!ids_ok(want, 1, K, E)) return EDGE0_ERANGE;
+      }
+      if ((rc = edge0_stage_experts(sg, L, step, want, K, nullptr, stream)) != EDGE0_OK ||
           (rc = edge0_stager_wait(sg, L, step, stream)) != EDGE0_OK)
         return rc;
       LayerIn l2{};
@@ -701,9 +719,18 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
   a.h_res = st->h + (size_t)(Lc - 1) * d;
   a.h_out = st->h + (size_t)Lc * d;
   if ((rc = launch_combine(a, stream)) != EDGE0_OK) return rc;
-  // every layer executed the given ids
-  k_gather_routing<<<1, 256, 0, stream>>>(plan.ids_dev, w_exec, plan.ids_dev, w_exec, Lc, K, 1, 0,
-                                          step, st->run_ids[step & 1], st->run_w[step & 1]);
+  if (loop) {
+    // prediction-routed layers executed the heads' routing, the others their
+    // router's
+    k_gather_routing<<<1, 256, 0, stream>>>(st->exec_ids[step & 1], w_exec, st->pred_ids[step % 3],
+                                            w_exec, Lc, K, st->spec.consumer_first,
+                                            st->spec.consumer_last, step, st->run_ids[step & 1],
+                                            st->run_w[step & 1]);
+  } else {
+    // every layer executed the given ids
+    k_gather_routing<<<1, 256, 0, stream>>>(plan.ids_dev, w_exec, plan.ids_dev, w_exec, Lc, K, 1,
+                                            0, step, st->run_ids[step & 1], st->run_w[step & 1]);
+  }
   E0_CHECK_LAUNCH();
   if (!ahead || st->spec.owner_first > st->spec.owner_last) return EDGE0_OK;
   HeadBatch hb = st->heads_batch;
@@ -714,6 +741,23 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
   hb.ids_out = st->pred_ids[(step + 1) % 3] + (size_t)(L0 + 1) * K;
   hb.w_out = st->pred_w[(step + 1) % 3] + (size_t)(L0 + 1) * K;
   if ((rc = launch_heads(hb, stream)) != EDGE0_OK) return rc;
+  if (loop) {
+    // one read-back per step: every prediction the heads committed, staged
+    // for the next step on the copy stream (the host has waited for the
+    // heads, so the copies may start at once)
+    int32_t* pred = st->loop_host + (size_t)Lc * K;
+    if (hipMemcpyAsync(pred, st->pred_ids[(step + 1) % 3], (size_t)Lc * K * 4,
+                       hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return EDGE0_EHIP;
+    for (int L = st->spec.owner_first; L <= st->spec.owner_last; ++L) {
+      if (!ids_ok(pred + (size_t)(L + 1) * K, 1, K, E)) return EDGE0_ERANGE;
+      if ((rc = edge0_stage_experts(sg, L + 1, step + 1, pred + (size_t)(L + 1) * K, K, nullptr,
+                                    plan.copy_stream)) != EDGE0_OK)
+        return rc;
+    }
+    return edge0_stager_flush(sg, stream);
+  }
   if (!plan.next_ids_host) return EDGE0_OK;
   // the next step's predicted sets, known once the heads ran
   if (!st->ev_heads &&
@@ -733,18 +777,23 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
 extern "C" int edge0_stack_step_staged(edge0_stack* st, edge0_stager* sg,
                                        const edge0_stage_plan* plan, const void* h0, void* h_out,
                                        int32_t step, hipStream_t stream) {
-  if (!st || !sg || !plan || !plan->ids_dev || !plan->ids_host || !h0 || !h_out || step < 0)
-    return EDGE0_EINVAL;
-  if (plan->ahead != 0 && plan->ahead != 1) return EDGE0_EINVAL;
+  if (!st || !sg || !plan || !h0 || !h_out || step < 0) return EDGE0_EINVAL;
+  if (plan->ahead != 0 && plan->ahead != 1 && plan->ahead != EDGE0_STAGE_LOOP) return EDGE0_EINVAL;
+  const bool loop = plan->ahead == EDGE0_STAGE_LOOP;
+  if (!loop && (!plan->ids_dev || !plan->ids_host)) return EDGE0_EINVAL;
   if (step != 0 && step != st->last_step + 1) return EDGE0_EINVAL;
   const edge0_slot_pool sp = stager_pool(sg);
   const int Lc = st->spec.n_layers, K = st->shape.top_k, E = st->shape.n_experts;
   if (sp.base != st->pool.base || sp.slot_bytes != st->pool.slot_bytes ||
       sp.n_slots != st->pool.n_slots || stager_table(sg) != st->tables || stager_layers(sg) != Lc)
     return EDGE0_EINVAL;
-  if (!ids_ok(plan->ids_host, Lc, K, E)) return EDGE0_EINVAL;
-  if (plan->ahead && plan->next_ids_host && !ids_ok(plan->next_ids_host, Lc, K, E))
+  if (!loop && !ids_ok(plan->ids_host, Lc, K, E)) return EDGE0_EINVAL;
+  if (plan->ahead == 1 && plan->next_ids_host && !ids_ok(plan->next_ids_host, Lc, K, E))
     return EDGE0_EINVAL;
+  if (loop && !st->loop_host &&
+      hipHostMalloc((void**)&st->loop_host, 2 * (size_t)Lc * K * 4, hipHostMallocDefault) !=
+          hipSuccess)
+    return EDGE0_ENOMEM;
   const size_t d = st->shape.d_model;
   if (hipMemcpyAsync(st->h, h0, d * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return EDGE0_EHIP;
@@ -930,6 +979,7 @@ extern "C" void edge0_stack_destroy(edge0_stack* st) {
   if (st->ev_heads) (void)hipEventDestroy(st->ev_heads);
   (void)hipFree(st->x_words);
   (void)hipFree(st->x_abort);
+  if (st->loop_host) (void)hipHostFree(st->loop_host);
   (void)hipFree(st->xl_acc);
   (void)hipFree(st->xl_words);
   (void)hipFree(st->xl_slots);

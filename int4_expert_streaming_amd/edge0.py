@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libedge0.so")
 EDGE0_OK, EDGE0_EINVAL, EDGE0_EHIP, EDGE0_ENOSLOT, EDGE0_ERANGE, EDGE0_ENOMEM = 0, -1, -2, -3, -4, -5
 EDGE0_ESCRATCH = -6
 EDGE0_ROUTE_SOFTMAX_TOPK = 0
+EDGE0_STAGE_LOOP = 2
 EDGE0_ROUTE_SIGMOID_GROUP = 1
 EDGE0_STATIC_WORKSPACE_BYTES = 1 << 20
 
@@ -469,13 +470,16 @@ class Stager(_Handle):
 
 
 def stack_step_staged(stack: "Stack", stager: Stager, h0, h_out, step: int, ids_dev, ids_host,
-                      next_ids_host, ahead: bool, copy_stream, stream=None):
+                      next_ids_host, ahead, copy_stream, stream=None):
     """One staged decode step (edge0_stack_step_staged).  ids_host and
-    next_ids_host are int32 numpy arrays [n_layers][K] (next may be None)."""
-    ids_host = _i32(ids_host)
+    next_ids_host are int32 numpy arrays [n_layers][K] (next may be None);
+    ahead is False/True (on demand / prediction arm over the given routing)
+    or EDGE0_STAGE_LOOP (routing from the device, ids_* None)."""
+    mode = EDGE0_STAGE_LOOP if ahead == EDGE0_STAGE_LOOP else (1 if ahead else 0)
+    ids_host = None if ids_host is None else _i32(ids_host)
     nxt = None if next_ids_host is None else _i32(next_ids_host)
-    plan = StagePlan(_ptr(ids_dev), ids_host.ctypes.data, None if nxt is None else nxt.ctypes.data,
-                     1 if ahead else 0, _stream(copy_stream))
+    plan = StagePlan(_ptr(ids_dev), None if ids_host is None else ids_host.ctypes.data,
+                     None if nxt is None else nxt.ctypes.data, mode, _stream(copy_stream))
     _check(lib.edge0_stack_step_staged(stack._handle, stager._handle, C.byref(plan), _ptr(h0),
                                        _ptr(h_out), step, _stream(stream)),
            "edge0_stack_step_staged")

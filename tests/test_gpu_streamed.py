@@ -159,3 +159,92 @@ def test_stager_rejects_pageable_host_memory(torch_cuda):
     sg = E.Stager(sh, pool.pool, 2, [pinned.data_ptr() + k * bb for k in range(2 * G.TINY.n_experts)],
                   table)
     sg.close()
+
+
+def _run_loop(S, seed, n_layers, owners, consumers, n_slots, steps):
+    """The closed loop (EDGE0_STAGE_LOOP): no trace; router layers commit
+    their own top-K, prediction-routed layers execute what their owner's
+    head committed one step earlier, and those predictions are what the
+    host staged.  Checked after every step: the executed routing of a
+    prediction-routed layer is the previous step's prediction; each
+    commit against the oracle's on the oracle's logits (near-tie waivers);
+    the slot table and counters against the LRU replay of the executed and
+    predicted sets; every layer teacher-forced."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import StreamedStack
+    from int4_expert_streaming_amd.weights import to_device
+    from tests.layer_setup import check_routing
+    gen = G.StackGen(S, seed)
+    En, K = S.n_experts, S.top_k
+    ss = StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
+    own = range(owners[0], owners[1] + 1)
+    con = range(consumers[0], consumers[1] + 1)
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    router = {L: gen.router(L) for L in range(n_layers)}
+    head = {L: gen.head(L) for L in own}
+    executed, predicted = {}, {}   # step -> [L][K]
+    prev_x = None
+    stats = []
+    for t in range(steps):
+        print(f"[streamed] loop step {t}", flush=True)
+        h0 = G.stack_hidden(S, seed, t)
+        E.stack_step_staged(ss.stack, ss.stager, to_device(h0), h_out, t, None, None, None,
+                            E.EDGE0_STAGE_LOOP, ss.copy_stream)
+        torch.cuda.synchronize()
+        b = ss.stack.buffers()
+        snap = {k: v.cpu().numpy() for k, v in b.items()}
+        executed[t], predicted[t] = snap["ids"].copy(), snap["pred_ids"].copy()
+        hh, xx, yy = (snap[k].view(np.uint16) for k in ("h", "x", "y"))
+        assert np.array_equal(hh[0], h0)
+        for L in range(n_layers):
+            ids = executed[t][L]
+            assert len(set(ids.tolist())) == K and ids.min() >= 0 and ids.max() < En
+            if L in con and t > 0:
+                # prediction-as-routing: the staged (predicted) set is the routed set
+                assert np.array_equal(ids, predicted[t - 1][L]), (L, t)
+                logits = O.prerouter_logits(head[L - 1], prev_x[L - 1], executed[t - 1][L - 1],
+                                            executed[t - 2][L - 1] if t >= 2 else None, En)
+            else:
+                logits = O.router_logits(router[L], xx[L])
+            stats.append(check_routing(ids, snap["w"][L], logits, K))
+            check_bf16_rounding(xx[L], O.rmsnorm(O.bf16_to_f64(hh[L])))
+            w_o = O.softmax_at(logits, ids)
+            assert np.max(np.abs(snap["w"][L] - w_o) / np.abs(w_o)) <= W_REL_MAX, (L, t)
+            ex = {int(e): gen.expert(L, int(e)) for e in ids}
+            lo = {int(e): gen.lora(L, int(e)) for e in ids}
+            y_o = O.moe_layer(ex, ids, w_o, xx[L], S.group, lo, S.lora_alpha / S.lora_rank)
+            assert rel_l2(O.bf16_to_f64(yy[L]), y_o) <= REL_L2_MAX, (L, t)
+            h_next = O.f64_to_bf16_bits(O.bf16_to_f64(hh[L]) + O.bf16_to_f64(yy[L]))
+            assert np.array_equal(h_next, hh[L + 1]), (L, t)
+        # the predictions of this step, against the oracle's commit
+        for L in own:
+            lo_ = O.prerouter_logits(head[L], xx[L], executed[t][L],
+                                     executed[t - 1][L] if t >= 1 else None, En)
+            stats.append(check_routing(predicted[t][L + 1], snap["pred_w"][L + 1], lo_, K))
+        # slot table and counters: the replay of the executed sets and, after
+        # the step, the predicted sets of the next one
+        ids_of = lambda L, s: executed[s][L] if s in executed else predicted[s - 1][L]
+        ev = O.canonical_requests(t + 1, n_layers, own, con, heads_at_end=True)
+        want, tot = _resident(ev, ids_of, n_slots, n_layers, En)
+        got = ss.table.cpu().numpy()
+        assert np.array_equal(got, want), (t, np.argwhere(got != want)[:8])
+        st = ss.stager.stats()
+        assert (st["hits"], st["misses"]) == (tot["hits"], tot["misses"]), (st, tot)
+        prev_x = xx.copy()
+    assert stats.count("exact") >= 0.9 * len(stats), stats.count("waived")
+    return ss
+
+
+def test_small_streamed_stack_closed_loop(torch_cuda):
+    """10 tiny layers over a 40-slot pool, 6 steps, routing from the device."""
+    ss = _run_loop(G.TINY, 7, 10, (2, 7), (3, 8), 40, 6)
+    print(f"[streamed] tiny loop: {ss.stager.stats()}")
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_streamed_stack_closed_loop(torch_cuda):
+    """12 Qwen3-MoE-shaped layers over a 64-slot pool, 4 steps, routing
+    from the device (router layers' own top-K, the heads' predictions)."""
+    ss = _run_loop(G.QWEN3_MOE, 2, 12, (2, 9), (3, 10), 64, 4)
+    print(f"[streamed] qwen3moe loop: {ss.stager.stats()}")
