@@ -1,12 +1,30 @@
-"""Decode throughput of the 40-layer streaming-MoE stack on one MI355X.
+"""Throughput of the streaming-MoE decode hot path on one MI355X.
 
-One step = one decode token through 40 Qwen3-MoE-shaped layers (hidden 2048,
-128 experts, inter 768, K = 4, int4 group 64, per-expert LoRA r=16 a=32,
-prerouter heads at layers 6..37, prediction-routed layers 7..38), all expert
-bundles resident in HBM, a fresh seeded hidden state per step.  Prints one
-JSON line (see the keys below).
+The headline (D2): one step = one decode token through 40 Qwen3-MoE-shaped
+layers (hidden 2048, 128 experts, inter 768, K = 4, int4 group 64, per-expert
+LoRA r=16 a=32, prerouter heads at layers 6..37, prediction-routed layers
+7..38), all expert bundles resident in HBM, a fresh seeded hidden state per
+step.  The same JSON line carries the other measurement rows under "rows":
 
-  python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--no-cpu]
+  d0     the tiny layer (hidden 256, 16 experts): one layer call = router +
+         MoE layer + prerouter head, 10^4 back-to-back calls, us per call
+  d1_k4, d1_k8
+         one Qwen3-MoE-shaped layer at K = 4 and 8: the MoE layer call and
+         the head call, over 64 layer instances (128 heads) in distinct HBM
+         addresses, rotated so the 256 MB memory-side cache holds no earlier
+         call's weights; replayed as HIP graphs; median of 5 runs x 1024 calls
+  d3     the stack over a 3 GiB slot pool staged from pinned host memory:
+         prediction arm, on-demand arm (fill kernel and DMA copies), the
+         closed loop (routing from the device) and all-resident, 5 rounds in
+         rotated order, medians
+  d4     the grouped multi-token layer (K = 8) at 1, 4, 8, 16, 32 tokens per
+         call on the rotated instances
+
+Every row has a roofline object and the oracle timed on this host's cores
+(1 thread and all threads) on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--no-cpu] [--rows all|none]
+  python bench.py --workload streamed|grouped|layer|tiny   (one row alone)
 """
 from __future__ import annotations
 
@@ -27,37 +45,45 @@ METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak
 # the same counters read for a device copy of known size (256 MiB copy:
 # FETCH_SIZE 131084.7 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only
 # for the kernel sources it was taken on (hash below); otherwise None.
-TRAFFIC_RECORD = {"src_sha": "72320c10bfbdf0a6", "fetch_kib": 4048.3, "write_kib": 66.9,
+TRAFFIC_RECORD = {"src_sha": "e051c80a550a4218", "fetch_kib": 4046.3, "write_kib": 66.9,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "moe.hip")
 HBM_PEAK_GBPS = 8000.0
 N_LAYERS, OWNERS, CONSUMERS = 40, (6, 37), (7, 38)
 
 
+# ------------------------------------------------------------------ bytes
+def bundle_alg_bytes(S):
+    """One expert's int4 gate/up/down rows with their bf16 scales and biases."""
+    d, I, g = S.d_model, S.d_inter, S.group
+    return 3 * I * d // 2 + 3 * (I * d // g) * 2 * 2
+
+
+def lora_alg_bytes(S):
+    """One expert's six bf16 LoRA factors."""
+    d, I, r = S.d_model, S.d_inter, S.lora_rank
+    return 2 * (r * d + I * r) * 2 + (r * I + d * r) * 2
+
+
+def head_alg_bytes(S):
+    """One head call: fc1 hidden-state columns, the 2K gathered one-hot rows,
+    fc2, the linear residual and the biases (fp16)."""
+    d, E, K, H = S.d_model, S.n_experts, S.top_k, S.head_hidden
+    return H * d * 2 + 2 * K * H * 2 + E * H * 2 + E * d * 2 + H * 2 + E * 2
+
+
+def moe_alg_bytes(S):
+    """One MoE layer call: the K routed experts' bundles and adapters."""
+    return S.top_k * (bundle_alg_bytes(S) + lora_alg_bytes(S))
+
+
 def step_bytes(S, n_routers):
     """Algorithmic HBM bytes of one decode step (every weight byte the step
-    must read once): K bundles + adapters per layer, 32 heads (fc1 hidden
-    columns, the 2K gathered one-hot rows, fc2, residual, biases) and the
-    plain routers that run."""
-    d, E, I, K, g, r, H = (S.d_model, S.n_experts, S.d_inter, S.top_k, S.group, S.lora_rank,
-                           S.head_hidden)
-    bundle = 3 * I * d // 2 + 3 * (I * d // g) * 2 * 2
-    lora = 2 * (r * d + I * r) * 2 + (r * I + d * r) * 2
-    head = H * d * 2 + 2 * K * H * 2 + E * H * 2 + E * d * 2 + H * 2 + E * 2
-    router = E * d * 2
+    must read once): K bundles + adapters per layer, 32 heads and the plain
+    routers that run."""
     n_heads = OWNERS[1] - OWNERS[0] + 1
-    return N_LAYERS * K * (bundle + lora) + n_heads * head + n_routers * router
-
-
-def gate_up_bytes(S):
-    """Algorithmic bytes of one gate/up launch: the K experts' gate and up
-    int4 rows with scales and biases, their LoRA B factors, the LoRA-down A
-    factor it applies to h, x once, and the activations it writes."""
-    d, I, K, g, r = S.d_model, S.d_inter, S.top_k, S.group, S.lora_rank
-    w = K * 2 * (I * d // 2 + 2 * I * (d // g) * 2)
-    lora = K * (2 * I * r * 2 + r * I * 2)
-    act = d * 2 + K * I * (4 + 2 + 2) + K * (I // 16) * (1 + r) * 4
-    return w + lora + act
+    return N_LAYERS * moe_alg_bytes(S) + n_heads * head_alg_bytes(S) + \
+        n_routers * S.n_experts * S.d_model * 2
 
 
 def fused_bytes(S):
@@ -80,23 +106,17 @@ def flow_bytes(S, n_routers):
     layer's K bundles and adapters, the plain routers that run, and each
     layer's input/output activations: x, y, h written, the fixed-point y
     read and cleared); the heads run after it as their own launches."""
-    d, E, I, K, g, r = S.d_model, S.n_experts, S.d_inter, S.top_k, S.group, S.lora_rank
-    bundle = 3 * I * d // 2 + 3 * (I * d // g) * 2 * 2
-    lora = 2 * (r * d + I * r) * 2 + (r * I + d * r) * 2
+    d = S.d_model
     act = 3 * d * 2 + 2 * d * 8
-    return N_LAYERS * (K * (bundle + lora) + act) + n_routers * E * d * 2
+    return N_LAYERS * (moe_alg_bytes(S) + act) + n_routers * S.n_experts * d * 2
 
 
 def xlayer_bytes(S):
     """Algorithmic bytes of one k_xlayer launch of a prediction-routed layer:
-    the K routed experts' bundles (gate, up, down int4 with scales and
-    biases) and adapters, read once; the previous layer's h and fixed-point
-    y read; x, y, h and the fixed-point y written (the layer's own output)."""
-    d, I, K, g, r = S.d_model, S.d_inter, S.top_k, S.group, S.lora_rank
-    bundle = 3 * I * d // 2 + 3 * (I * d // g) * 2 * 2
-    lora = 2 * (r * d + I * r) * 2 + (r * I + d * r) * 2
-    act = d * 2 + d * 8 + 3 * d * 2 + d * 8
-    return K * (bundle + lora) + act
+    the K routed experts' bundles and adapters, read once; the previous
+    layer's h and fixed-point y read; x, y, h and the fixed-point y written."""
+    d = S.d_model
+    return moe_alg_bytes(S) + d * 2 + d * 8 + 3 * d * 2 + d * 8
 
 
 def gate_up_traffic():
@@ -113,47 +133,425 @@ def gate_up_traffic():
     return int((r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"]) * 1024)
 
 
-def cpu_baseline(S, seed, budget_s=15.0):
-    """The oracle timed on this host on a bounded sample: for a few layers of
-    the same stack, plain router + top-K, the MoE layer over K experts and
-    the prerouter head, extrapolated to one 40-layer step (32 heads, 8
-    routers)."""
+def roofline(kernel, nbytes, us):
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "bytes_per_launch": int(nbytes), "avg_launch_us": round(us, 3)}
+
+
+# ----------------------------------------------------------- CPU baseline
+def host_info():
+    """The host the oracle is timed on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"os_cpu_count": os.cpu_count(), "nproc": nproc, "model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _pool_threads():
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+
+def oracle_timed(unit, budget_s):
+    """unit() runs one unit of oracle work and returns the seconds its timed
+    part took.  Repeated within budget_s, once with the BLAS pool limited to
+    one thread and once at its own size; returns (s per unit at 1 thread,
+    s per unit at all threads, threads, units per pass)."""
+    from threadpoolctl import threadpool_limits
+    out = []
+    for limit in (1, None):
+        with threadpool_limits(limits=limit):
+            ts, t0 = [], time.time()
+            while not ts or (time.time() - t0 < budget_s and len(ts) < 64):
+                ts.append(unit())
+        out.append((float(np.mean(ts)), len(ts)))
+    return out[0][0], out[1][0], _pool_threads(), min(out[0][1], out[1][1])
+
+
+def cpu_record(value_1, value_n, unit, threads, sample):
+    return {"value": round(value_n, 6), "unit": unit, "cores": int(threads), "kind": "oracle",
+            "single_thread_value": round(value_1, 6), "host": host_info(), "sample": sample}
+
+
+def cpu_baseline_stack(S, seed, budget_s=8.0):
+    """D2: the oracle's plain router + top-K, MoE layer over K experts and
+    prerouter head on layers of the same stack, extrapolated to one 40-layer
+    step (32 heads, 8 routers)."""
     import oracle as O
     from synth import gen as G
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    t_moe, t_head, t_router, n = [], [], [], 0
-    t_start = time.time()
     scale = S.lora_alpha / S.lora_rank
-    for L in range(OWNERS[0], OWNERS[1] + 1):
+    layers = list(range(OWNERS[0], OWNERS[1] + 1))
+    state = {"i": 0}
+
+    def unit():
+        L = layers[state["i"] % len(layers)]
+        state["i"] += 1
         x = G.stack_hidden(S, seed, 10_000 + L)
-        wr = G.router_weight(S, seed, L)
-        head = G.head_tensors(S, seed, L)
+        wr, head = G.router_weight(S, seed, L), G.head_tensors(S, seed, L)
         t0 = time.perf_counter()
-        logits = O.router_logits(wr, x)
-        ids, w = O.softmax_topk(logits, S.top_k)
-        t_router.append(time.perf_counter() - t0)
+        ids, w = O.softmax_topk(O.router_logits(wr, x), S.top_k)
+        t_r = time.perf_counter() - t0
         ex = {int(e): G.expert_tensors(S, seed, L, int(e)) for e in ids}
         lo = {int(e): G.lora_tensors(S, seed, L, int(e)) for e in ids}
         t0 = time.perf_counter()
         O.moe_layer(ex, ids, w, x, S.group, lo, scale)
-        t_moe.append(time.perf_counter() - t0)
+        t_m = time.perf_counter() - t0
         t0 = time.perf_counter()
         O.prerouter_commit(head, x, ids, None, S.n_experts, S.top_k)
-        t_head.append(time.perf_counter() - t0)
-        n += 1
-        if time.time() - t_start > budget_s:
-            break
-    step_s = N_LAYERS * np.mean(t_moe) + 32 * np.mean(t_head) + 8 * np.mean(t_router)
-    return {"value": round(1.0 / step_s, 4), "unit": "tok/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} stack layers (router+top-K, MoE K={S.top_k}, head) timed, "
-                      f"extrapolated to a 40-layer step; {step_s:.2f} s/step"}
+        t_h = time.perf_counter() - t0
+        return N_LAYERS * t_m + 32 * t_h + 8 * t_r
+    s1, sn, thr, n = oracle_timed(unit, budget_s)
+    return cpu_record(1.0 / s1, 1.0 / sn, "tok/s", thr,
+                      f"{n} stack layers per thread setting (router + top-K, MoE K={S.top_k}, "
+                      f"head) timed, each extrapolated to a 40-layer step; "
+                      f"{sn:.2f} s/step at all threads, {s1:.2f} s/step at 1")
 
 
+# ------------------------------------------------------------- D0: tiny
+def row_tiny(args, log):
+    """The tiny layer: router + MoE layer + head per call, 10^4 calls."""
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import SlotPoolBuffer, head_to_device, to_device
+    S = G.TINY
+    sh = E.make_shape(S)
+    En, K = S.n_experts, S.top_k
+    pool = SlotPoolBuffer(sh, En)
+    for e in range(En):
+        pool.load(e, G.expert_tensors(S, args.seed, 0, e), G.lora_tensors(S, args.seed, 0, e))
+    table = torch.arange(En, dtype=torch.int32, device="cuda")
+    wr = to_device(G.router_weight(S, args.seed, 0))
+    head_d = head_to_device(G.head_tensors(S, args.seed, 0))  # kept alive: the head points at it
+    head = E.make_head(head_d)
+    ws = E.new_workspace(sh)
+    x = to_device(G.hidden(S, args.seed, 0))
+    y = torch.empty_like(x)
+    ids = torch.zeros(K, dtype=torch.int32, device="cuda")
+    w = torch.zeros(K, dtype=torch.float32, device="cuda")
+    pids = [torch.arange(K, dtype=torch.int32, device="cuda") for _ in range(2)]
+    pw = torch.zeros(K, dtype=torch.float32, device="cuda")
+
+    def call(i):
+        E.edge0_router(sh, wr, x, None, ids, w, ws)
+        E.edge0_moe_layer(sh, pool.pool, table, ids, w, x, y, ws)
+        E.edge0_prerouter(sh, head, x, ids, pids[(i + 1) & 1], None, pids[i & 1], pw, ws)
+
+    for i in range(200):
+        call(i)
+    torch.cuda.synchronize()
+    # issued call by call from the host (the binding's overhead included)
+    n = 10_000
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(n):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    host_us = (time.perf_counter() - h0) * 1e6 / n
+    issued_us = ev0.elapsed_time(ev1) * 1e3 / n
+    # the device's own latency: 1000 calls captured as one graph, 10 replays
+    y_ref = y.clone()
+    us, runs = _graph_time(torch, call, 1000, runs=10)
+    assert torch.equal(y, y_ref), "graph replay differs from the host-issued calls"
+    assert E.edge0_workspace_error(ws) == 0
+    nbytes = moe_alg_bytes(S) + head_alg_bytes(S) + En * S.d_model * 2
+    log(f"[d0] tiny layer call {us:.2f} us in a graph; issued from the host {issued_us:.2f} us "
+        f"(host {host_us:.2f} us)")
+    out = {"metric": "tiny layer call latency (router + MoE + head)", "value": round(us, 3),
+           "unit": "us/call", "higher_is_better": False,
+           "config": {"workload": "tiny MoE layer: hidden 256, 16 experts, inter 128, K=4, "
+                                  "group 32, LoRA r=8, head 288->64->16 + residual",
+                      "timing": "HIP graph of 1000 back-to-back calls, median of 10 replays; "
+                                f"also {n} calls issued one by one from the host"},
+           "graph_runs_us": runs, "host_issued_us_per_call": round(issued_us, 3),
+           "host_issue_us_per_call": round(host_us, 3),
+           "roofline": roofline("router + MoE layer + head (one call)", nbytes, us)}
+    out["roofline"]["note"] = "latency-bound by design (0.37 MB per call)"
+    if not args.no_cpu:
+        import oracle as O
+        wr_h, head_h = G.router_weight(S, args.seed, 0), G.head_tensors(S, args.seed, 0)
+        ex = {e: G.expert_tensors(S, args.seed, 0, e) for e in range(En)}
+        lo = {e: G.lora_tensors(S, args.seed, 0, e) for e in range(En)}
+        xh = G.hidden(S, args.seed, 0)
+
+        def unit():
+            t0 = time.perf_counter()
+            i_, w_ = O.softmax_topk(O.router_logits(wr_h, xh), K)
+            O.moe_layer(ex, i_, w_, xh, S.group, lo, S.lora_alpha / S.lora_rank)
+            O.prerouter_commit(head_h, xh, i_, None, En, K)
+            return time.perf_counter() - t0
+        s1, sn, thr, reps = oracle_timed(unit, 2.0)
+        out["cpu_baseline"] = cpu_record(s1 * 1e6, sn * 1e6, "us/call", thr,
+                                         f"{reps} single calls per thread setting")
+    return out
+
+
+# -------------------------------------------- rotated Qwen3-MoE instances
+class Instances:
+    """n_inst copies of n_gen generated Qwen3-MoE-shaped layers (all E
+    experts each) at distinct HBM addresses, plus n_heads head copies, so
+    that rotating over them defeats the 256 MB memory-side cache."""
+
+    def __init__(self, S, seed, log, n_gen=8, n_inst=64, n_heads=128):
+        import torch
+        from synth import gen as G
+        from int4_expert_streaming_amd import edge0 as E
+        from int4_expert_streaming_amd.stackbuild import pack_layer
+        from int4_expert_streaming_amd.weights import SlotPoolBuffer, head_to_device, to_device
+        self.S, self.n_gen, self.n_inst = S, n_gen, n_inst
+        En = S.n_experts
+        sh = E.make_shape(S)
+        gen = G.StackGen(S, seed)
+        self.pool = SlotPoolBuffer(sh, n_inst * En)
+        bb = self.pool.slot_bytes
+        t0 = time.time()
+        for L in range(n_gen):
+            parts = [(gen.expert(L, e), gen.lora(L, e)) for e in range(En)]
+            pack_layer(sh, parts, lambda e: self.pool.slot_ptr(L * En + e))
+        for i in range(n_gen, n_inst):
+            src = (i % n_gen) * En * bb
+            self.pool.mem[i * En * bb:(i + 1) * En * bb].copy_(self.pool.mem[src:src + En * bb])
+        self.tables = [torch.arange(i * En, (i + 1) * En, dtype=torch.int32, device="cuda")
+                       for i in range(n_inst)]
+        self.routers = [to_device(gen.router(L)) for L in range(n_gen)]
+        base = [head_to_device(gen.head(L)) for L in range(n_gen)]
+        self.heads_d = [{k: (None if v is None else v.clone()) for k, v in base[i % n_gen].items()}
+                        for i in range(n_heads)]
+        self.heads = [E.make_head(h) for h in self.heads_d]
+        torch.cuda.synchronize()
+        log(f"[instances] {n_inst} layers x {En} experts + {n_heads} heads "
+            f"({self.pool.mem.numel() / 1e9:.1f} GB) in {time.time() - t0:.1f}s")
+
+
+def _graph_time(torch, body, n_calls, runs=5, check=None):
+    """Median us per call of `body(c)` for c in 0..n_calls-1, captured as one
+    HIP graph and replayed `runs` times (after one untimed replay)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(8):
+            body(c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in range(n_calls):
+            body(c)
+    g.replay()
+    torch.cuda.synchronize()
+    if check is not None:
+        check()
+    times = []
+    for _ in range(runs):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) * 1e3 / n_calls)
+    if check is not None:
+        check()
+    return float(np.median(times)), [round(t, 3) for t in times]
+
+
+def row_layer(args, log, inst, K):
+    """D1: one Qwen3-MoE-shaped layer at K: the MoE layer call, the head call
+    and the two together, rotated over the instances."""
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    S = inst.S.with_k(K)
+    sh = E.make_shape(S)
+    En, d, n_inst = S.n_experts, S.d_model, inst.n_inst
+    n_heads = len(inst.heads)
+    ws = E.new_workspace(sh)
+    xs = [to_device(G.hidden(S, 700 + i)) for i in range(n_heads)]
+    ids, ws_w = [], []
+    for i in range(n_inst):  # routing of each instance: its router's top-K
+        a = torch.zeros(K, dtype=torch.int32, device="cuda")
+        b = torch.zeros(K, dtype=torch.float32, device="cuda")
+        E.edge0_router(sh, inst.routers[i % inst.n_gen], xs[i], None, a, b, ws)
+        ids.append(a)
+        ws_w.append(b)
+    rng = np.random.default_rng(args.seed + K)
+    prev = [torch.from_numpy(rng.choice(En, K, replace=False).astype(np.int32)).cuda()
+            for _ in range(n_heads)]
+    ys = [torch.empty(d, dtype=torch.int16, device="cuda") for _ in range(n_inst)]
+    pid = torch.zeros(K, dtype=torch.int32, device="cuda")
+    pw = torch.zeros(K, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def moe(c):
+        i = c % n_inst
+        E.edge0_moe_layer(sh, inst.pool.pool, inst.tables[i], ids[i], ws_w[i], xs[i], ys[i], ws)
+
+    def head(c):
+        i = c % n_heads
+        E.edge0_prerouter(sh, inst.heads[i], xs[i], ids[i % n_inst], prev[i], None, pid, pw, ws)
+
+    def both(c):
+        head(c)
+        moe(c)
+
+    # graph replays against an eager call of the same instance: bit-identical y
+    ref = torch.empty(d, dtype=torch.int16, device="cuda")
+    E.edge0_moe_layer(sh, inst.pool.pool, inst.tables[5], ids[5], ws_w[5], xs[5], ref, ws)
+    torch.cuda.synchronize()
+
+    def check():
+        assert torch.equal(ys[5], ref), "graph replay differs from the eager call"
+
+    n_calls = 1024
+    us_moe, runs_moe = _graph_time(torch, moe, n_calls, check=check)
+    us_head, runs_head = _graph_time(torch, head, n_calls)
+    us_both, _ = _graph_time(torch, both, n_calls)
+    assert E.edge0_workspace_error(ws) == 0
+    b_moe, b_head = moe_alg_bytes(S), head_alg_bytes(S)
+    log(f"[d1] K={K}: MoE {us_moe:.2f} us ({b_moe / us_moe / 1e3:.0f} GB/s), head {us_head:.2f} us "
+        f"({b_head / us_head / 1e3:.0f} GB/s), both {us_both:.2f} us")
+    out = {"metric": f"one Qwen3-MoE-shaped layer, K={K}: MoE layer call GB/s vs peak",
+           "value": round(b_moe / (us_moe * 1e-6) / 1e9, 1), "unit": "GB/s",
+           "higher_is_better": True,
+           "config": {"workload": f"one Qwen3-MoE-shaped layer, 1 token, K={K}, "
+                                  f"{n_inst} rotated layer instances, {n_heads} heads",
+                      "d_model": d, "n_experts": En, "d_inter": S.d_inter, "top_k": K,
+                      "group": S.group, "lora_rank": S.lora_rank, "head_hidden": S.head_hidden,
+                      "timing": f"HIP graph of {n_calls} calls, median of 5 replays"},
+           "moe_us_per_call": round(us_moe, 3), "moe_runs_us": runs_moe,
+           "head_us_per_call": round(us_head, 3), "head_runs_us": runs_head,
+           "head_plus_moe_us_per_call": round(us_both, 3),
+           "moe_bytes": b_moe, "head_bytes": b_head,
+           "head_gbps": round(b_head / (us_head * 1e-6) / 1e9, 1),
+           "head_plus_moe_gbps": round((b_moe + b_head) / (us_both * 1e-6) / 1e9, 1),
+           "roofline": roofline("edge0_moe_layer (slot/LoRA-in, int4 gate/up, int4 down, combine launches)",
+                                b_moe, us_moe)}
+    if not args.no_cpu:
+        import oracle as O
+        gen = G.StackGen(S, args.seed)
+        x = G.hidden(S, 700)
+        idh = ids[0].cpu().numpy()
+        wh = ws_w[0].cpu().numpy().astype(np.float64)
+        ex = {int(e): gen.expert(0, int(e)) for e in idh}
+        lo = {int(e): gen.lora(0, int(e)) for e in idh}
+        hd = gen.head(0)
+
+        def unit():
+            t0 = time.perf_counter()
+            O.moe_layer(ex, idh, wh, x, S.group, lo, S.lora_alpha / S.lora_rank)
+            O.prerouter_commit(hd, x, idh, None, En, K)
+            return time.perf_counter() - t0
+        s1, sn, thr, reps = oracle_timed(unit, 3.0)
+        out["cpu_baseline"] = cpu_record(
+            (b_moe + b_head) / s1 / 1e9, (b_moe + b_head) / sn / 1e9, "GB/s", thr,
+            f"{reps} single layer calls (MoE K={K} + head) per thread setting: "
+            f"{sn * 1e3:.1f} ms at all threads, {s1 * 1e3:.1f} ms at 1")
+    return out
+
+
+# ----------------------------------------------------------- D4: grouped
+def row_grouped(args, log, inst):
+    """Grouped multi-token layer (K = 8) at 1, 4, 8, 16 and 32 tokens per
+    call, Zipf(1.1) routing, rotated over the instances."""
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    S = inst.S.with_k(8)
+    sh = E.make_shape(S)
+    En, K, d, I, r = S.n_experts, S.top_k, S.d_model, S.d_inter, S.lora_rank
+    n_inst = inst.n_inst
+    bb = bundle_alg_bytes(S) + lora_alg_bytes(S)
+    gws = E.new_grouped_workspace(sh)
+    stream = torch.cuda.current_stream()
+    results = {}
+    for T in (1, 4, 8, 16, 32):
+        routes = [G.grouped_routing(En, K, T, seed=args.seed * 1000 + 17 * T + i,
+                                    layer=i % inst.n_gen) for i in range(n_inst)]
+        ids = [to_device(rt[0]) for rt in routes]
+        wts = [torch.from_numpy(rt[1]).cuda() for rt in routes]
+        xs = [to_device(G.hidden(S, 500 + T * 100 + i, n=T)) for i in range(n_inst)]
+        y = torch.empty((T, d), dtype=torch.int16, device="cuda")
+        union = float(np.mean([np.count_nonzero(np.bincount(rt[0].ravel(), minlength=En))
+                               for rt in routes]))
+
+        def timed(flags, n_calls=256):
+            for i in range(32):
+                E.edge0_moe_grouped(sh, inst.pool.pool, inst.tables[i % n_inst], T,
+                                    ids[i % n_inst], wts[i % n_inst], xs[i % n_inst], y, gws, flags)
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for c in range(n_calls):
+                i = c % n_inst
+                E.edge0_moe_grouped(sh, inst.pool.pool, inst.tables[i], T, ids[i], wts[i], xs[i],
+                                    y, gws, flags)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) * 1e3 / n_calls
+
+        us = float(np.median([timed(0) for _ in range(5)]))
+        if args.mfma_sweep:
+            sweep = {"gemv_only": round(timed(E.EDGE0_GROUPED_NO_MFMA), 2)}
+            for mn in (2, 4, 8, 24):
+                sweep[f"mfma_from_{mn}"] = round(timed(E.grouped_mfma_min(mn)), 2)
+            log(f"[d4] T={T} us/call by MFMA threshold: default {us:.2f}, {sweep}")
+        nbytes = union * bb
+        flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
+        results[T] = {"us_per_call": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
+                      "experts": round(union, 2),
+                      "path": "mfma tiles" if T >= 3 else "gemv",
+                      "union_bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "tflops": round(flops / (us * 1e-6) / 1e12, 3)}
+        log(f"[d4] T={T}: {results[T]}")
+    best = results[32]
+    out = {"metric": "grouped MoE layer tok/s (K=8, Qwen3-MoE shapes) + union-bytes GB/s vs peak",
+           "value": best["tok_s"], "unit": "tok/s", "higher_is_better": True,
+           "config": {"workload": "one Qwen3-MoE-shaped layer, 1-32 tokens per call, K=8, "
+                                  f"Zipf(1.1) routing, {n_inst} rotated layer instances",
+                      "timing": "median of 5 runs of 256 calls"},
+           "roofline": roofline("edge0_moe_grouped at T=32 (bucketing + int4 MFMA tiles)",
+                                best["union_bytes"], best["us_per_call"]),
+           "per_tokens": {str(k): v for k, v in results.items()}}
+    if not args.no_cpu:
+        import oracle as O
+        gen = G.StackGen(S, args.seed)
+        T = 4
+        idg, wg = G.grouped_routing(En, K, T, seed=args.seed * 1000 + 17 * T, layer=0)
+        xg = G.hidden(S, 500 + T * 100, n=T)
+        ex = {int(e): gen.expert(0, int(e)) for e in np.unique(idg)}
+        lo = {int(e): gen.lora(0, int(e)) for e in np.unique(idg)}
+
+        def unit():
+            t0 = time.perf_counter()
+            O.grouped_layer(ex, idg, wg.astype(np.float64), xg, S.group, lo,
+                            S.lora_alpha / S.lora_rank)
+            return time.perf_counter() - t0
+        s1, sn, thr, reps = oracle_timed(unit, 3.0)
+        out["cpu_baseline"] = cpu_record(T / s1, T / sn, "tok/s", thr,
+                                         f"{reps} grouped calls of {T} tokens (K=8) per thread "
+                                         "setting, per token as the oracle defines it")
+    return out
+
+
+# ------------------------------------------------------------ D3: staged
 def h2d_bandwidth(host_mem, nbytes, n=128):
     """Pinned host -> device copy rate (GB/s) for n copies of nbytes each on
     one stream: the host-link roofline of the staged arms."""
@@ -202,25 +600,36 @@ def stage_kernel_bandwidth(S, host, n_layers, n_sets=24):
     return nbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
 
 
-def bench_streamed(args, log):
-    """Staged decode: the 40-layer stack over a 3 GiB HBM slot pool filled
-    from pinned host bundles, routed by a Zipf(1.1) trace with ~25 % adjacent-
-    token overlap.  Arms, run in rotated order on the same host tier: the
-    prediction arm (next step's predicted sets prefetched on a side stream),
-    the on-demand arm (each set filled right after its router), and an
-    all-resident reference (every bundle in HBM, the same launches) giving
-    the compute-only step time."""
+STAGED_ARMS = ("ahead", "demand", "ahead_dma", "demand_dma", "loop", "resident")
+
+
+def row_staged(args, log, rounds=5, warmup=16, steps=64):
+    """The 40-layer stack over a 3 GiB HBM slot pool filled from pinned host
+    bundles.  Arms (each a fresh pool: cold start), in rotated order over
+    `rounds` rounds on the same host tier:
+      ahead / ahead_dma   prediction arm over a Zipf(1.1) trace (~25 %
+                          adjacent-token overlap): the next step's predicted
+                          sets staged on a side stream (fill kernel / DMA)
+      demand / demand_dma each set filled right after its router
+      loop                the closed loop: routing from the device (router
+                          top-K, the heads' predictions read back once per
+                          step and staged); random heads, so its routing
+                          statistics are the heads' own
+      resident            every bundle in HBM, the same launches: the
+                          compute-only step time"""
     import torch
     from synth import gen as G
-    from int4_expert_streaming_amd.stackbuild import HostBundles, StreamedStack
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import (HostBundles, StreamedStack,
+                                                       device_routers_heads)
     from int4_expert_streaming_amd.weights import to_device
     S = G.QWEN3_MOE
-    torch.cuda.set_device(0)
     gen = G.StackGen(S, args.seed)
     host = HostBundles(S, gen, N_LAYERS, log=log)
+    routers, heads = device_routers_heads(gen, N_LAYERS, range(OWNERS[0], OWNERS[1] + 1))
     bb = host.bundle_bytes
     n_slots = (3 << 30) // bb
-    total = args.warmup + args.steps
+    total = warmup + steps
     trace = G.zipf_trace(S.n_experts, S.top_k, N_LAYERS, total + 1, args.seed, keep_p=0.06)
     overlap = float(np.mean([len(set(trace[t, L]) & set(trace[t - 1, L])) / S.top_k
                              for t in range(1, total) for L in range(N_LAYERS)]))
@@ -230,223 +639,118 @@ def bench_streamed(args, log):
     bw_dma = h2d_bandwidth(host.mem, bb)
     bw_kernel = stage_kernel_bandwidth(S, host, N_LAYERS)
     bw = max(bw_dma, bw_kernel)
-    log(f"[streamed] host link: DMA copies {bw_dma:.1f} GB/s, fill kernel {bw_kernel:.1f} GB/s "
+    log(f"[d3] host link: DMA copies {bw_dma:.1f} GB/s, fill kernel {bw_kernel:.1f} GB/s "
         f"({bb}-byte bundles); trace overlap {overlap:.3f}")
-    arms = {}
-    order = ["ahead", "demand", "ahead_dma", "demand_dma", "resident"]
-    if args.seed % 2:
-        order = ["demand", "ahead", "demand_dma", "ahead_dma", "resident"]
-    for arm in order:
-        slots = N_LAYERS * S.n_experts if arm == "resident" else n_slots
-        ss = StreamedStack(S, gen, N_LAYERS, OWNERS, CONSUMERS, slots, log=None, host=host)
-        if arm.endswith("_dma"):
-            ss.stager.set_copy_mode(1)
-        ahead = not arm.startswith("demand")
-        if arm == "resident":  # every bundle staged before timing
-            for L in range(N_LAYERS):
-                for e0 in range(0, S.n_experts, 16):
-                    ss.stager.stage(L, 1 << 20, list(range(e0, e0 + 16)))
-                    ss.stager.release(L, 1 << 20)
-            ss.stager.flush()
+    per_arm = {a: [] for a in STAGED_ARMS}
+    for rnd in range(rounds):
+        k = rnd % len(STAGED_ARMS)
+        order = STAGED_ARMS[k:] + STAGED_ARMS[:k]
+        for arm in order:
+            slots = N_LAYERS * S.n_experts if arm == "resident" else n_slots
+            ss = StreamedStack(S, gen, N_LAYERS, OWNERS, CONSUMERS, slots, log=None, host=host,
+                               routers=routers, heads=heads)
+            if arm.endswith("_dma"):
+                ss.stager.set_copy_mode(1)
+            if arm == "resident":  # every bundle staged before timing
+                for L in range(N_LAYERS):
+                    for e0 in range(0, S.n_experts, 16):
+                        ss.stager.stage(L, 1 << 20, list(range(e0, e0 + 16)))
+                        ss.stager.release(L, 1 << 20)
+                ss.stager.flush()
+                torch.cuda.synchronize()
+            mode = {"loop": E.EDGE0_STAGE_LOOP}.get(arm, not arm.startswith("demand"))
+
+            def step(t):
+                if arm == "loop":
+                    E.stack_step_staged(ss.stack, ss.stager, h0[t], h_out, t, None, None, None,
+                                        mode, ss.copy_stream)
+                else:
+                    ss.step(h0[t], h_out, t, trace_dev[t], trace[t], trace[t + 1], mode)
+            stream = torch.cuda.current_stream()
+            for t in range(warmup):
+                step(t)
             torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        for t in range(args.warmup):
-            ss.step(h0[t], h_out, t, trace_dev[t], trace[t], trace[t + 1], ahead)
-        torch.cuda.synchronize()
-        st0 = ss.stager.stats()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for t in range(args.warmup, total):
-            ss.step(h0[t], h_out, t, trace_dev[t], trace[t], trace[t + 1], ahead)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        st1 = ss.stager.stats()
-        ms = ev0.elapsed_time(ev1) / args.steps
-        d = {k: st1[k] - st0[k] for k in st1}
-        arms[arm] = {"ms_per_step": round(ms, 4), "tok_s": round(1000.0 / ms, 2),
-                     "hit_rate": round(d["hits"] / max(1, d["touches"]), 4),
-                     "misses_per_step": round(d["misses"] / args.steps, 2),
-                     "h2d_bytes_per_step": int(d["bytes_staged"] / args.steps)}
-        log(f"[streamed] {arm}: {arms[arm]}")
-        del ss
-        torch.cuda.synchronize()
-    t_comp = arms["resident"]["ms_per_step"]
-    for arm in ("ahead", "demand", "ahead_dma", "demand_dma"):
-        a = arms[arm]
-        copy_ms = a["h2d_bytes_per_step"] / (bw * 1e9) * 1e3
-        exposed = max(0.0, a["ms_per_step"] - t_comp)
-        a["copy_ms_per_step"] = round(copy_ms, 4)
-        a["exposed_wait_ms_per_step"] = round(exposed, 4)
-        a["overlap"] = round(1.0 - exposed / copy_ms, 4) if copy_ms > 0 else None
-        a["host_link_ceiling_tok_s"] = round(1000.0 / copy_ms, 2) if copy_ms > 0 else None
-    tok_s = arms["ahead"]["tok_s"]
-    out = {
-        "metric": "staged decode tok/s (batch 1, 40-layer MoE stack, 3 GiB HBM pool)",
-        "value": tok_s, "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": arms["ahead"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "40-layer Qwen3-MoE-shaped decode stack, experts staged from "
-                               "pinned host memory into a 3 GiB HBM pool (LRU)",
-                   "n_slots": n_slots, "bundle_bytes": bb, "top_k": S.top_k,
-                   "trace": "Zipf(1.1), per-layer permutation, keep_p 0.06",
-                   "trace_overlap": round(overlap, 4), "global_batch": 1, "parallelism": "none"},
-        "h2d_gbps": {"dma_copy": round(bw_dma, 2), "fill_kernel": round(bw_kernel, 2)},
-        "roofline": {"bound": "host-link", "achieved": round(
-            arms["ahead"]["h2d_bytes_per_step"] / (arms["ahead"]["ms_per_step"] * 1e-3) / 1e9, 2),
-            "peak": round(bw, 2), "unit": "GB/s",
-            "frac": round(arms["ahead"]["h2d_bytes_per_step"] /
-                          (arms["ahead"]["ms_per_step"] * 1e-3) / 1e9 / bw, 4),
-            "traffic": None},
-        "arms": arms,
-    }
-    print(json.dumps(out), flush=True)
-
-
-def bench_grouped(args, log):
-    """Grouped multi-token layer (Qwen3-MoE shapes, K = 8) at 1, 4, 8, 16 and
-    32 tokens per call, Zipf(1.1) routing.  Calls rotate over 64 layer
-    instances in distinct HBM slots (8 generated layers, each placed 8 times),
-    so the 256 MB MALL holds no earlier call's experts."""
-    import torch
-    from synth import gen as G
-    from int4_expert_streaming_amd import edge0 as E
-    from int4_expert_streaming_amd.stackbuild import pack_layer
-    from int4_expert_streaming_amd.weights import SlotPoolBuffer, to_device
-    S = G.QWEN3_MOE.with_k(8)
-    sh = E.make_shape(S)
-    En, K, d, I, r = S.n_experts, S.top_k, S.d_model, S.d_inter, S.lora_rank
-    n_gen, n_inst = 8, 64
-    gen = G.StackGen(S, args.seed)
-    pool = SlotPoolBuffer(sh, n_inst * En)
-    bb = pool.slot_bytes
-    t0 = time.time()
-    for L in range(n_gen):
-        parts = [(gen.expert(L, e), gen.lora(L, e)) for e in range(En)]
-        pack_layer(sh, parts, lambda e: pool.slot_ptr(L * En + e))
-    for i in range(n_gen, n_inst):  # copies of the generated layers at new addresses
-        src = (i % n_gen) * En * bb
-        pool.mem[i * En * bb:(i + 1) * En * bb].copy_(pool.mem[src:src + En * bb])
-    torch.cuda.synchronize()
-    log(f"[grouped] {n_inst} layer instances ready ({time.time() - t0:.1f}s), "
-        f"{pool.mem.numel() / 1e9:.1f} GB")
-    tables = [torch.arange(i * En, (i + 1) * En, dtype=torch.int32, device="cuda")
-              for i in range(n_inst)]
-    ws = E.new_grouped_workspace(sh)
-    stream = torch.cuda.current_stream()
-    results = {}
-    for T in (1, 4, 8, 16, 32):
-        routes = [G.grouped_routing(En, K, T, seed=args.seed * 1000 + 17 * T + i, layer=i % n_gen)
-                  for i in range(n_inst)]
-        ids = [to_device(rt[0]) for rt in routes]
-        ws_ = [torch.from_numpy(rt[1]).cuda() for rt in routes]
-        xs = [to_device(G.hidden(S, 500 + T * 100 + i, n=T)) for i in range(n_inst)]
-        y = torch.empty((T, d), dtype=torch.int16, device="cuda")
-        counts = [np.bincount(rt[0].ravel(), minlength=En) for rt in routes]
-        union = float(np.mean([np.count_nonzero(c) for c in counts]))
-
-        def timed(flags, n_calls=256):
-            for i in range(32):
-                E.edge0_moe_grouped(sh, pool.pool, tables[i % n_inst], T, ids[i % n_inst],
-                                    ws_[i % n_inst], xs[i % n_inst], y, ws, flags)
-            torch.cuda.synchronize()
+            st0 = ss.stager.stats()
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record(stream)
-            for c in range(n_calls):
-                i = c % n_inst
-                E.edge0_moe_grouped(sh, pool.pool, tables[i], T, ids[i], ws_[i], xs[i], y, ws,
-                                    flags)
+            for t in range(warmup, total):
+                step(t)
             ev1.record(stream)
             torch.cuda.synchronize()
-            return ev0.elapsed_time(ev1) * 1e3 / n_calls
+            st1 = ss.stager.stats()
+            ms = ev0.elapsed_time(ev1) / steps
+            dd = {k_: st1[k_] - st0[k_] for k_ in st1}
+            rec = {"ms_per_step": ms, "hit_rate": dd["hits"] / max(1, dd["touches"]),
+                   "misses_per_step": dd["misses"] / steps,
+                   "h2d_bytes_per_step": dd["bytes_staged"] / steps}
+            if arm == "loop":
+                ids = ss.stack.buffers()["ids"].cpu().numpy()
+                rec["distinct_experts_last_step"] = int(len(np.unique(ids)))
+            per_arm[arm].append(rec)
+            del ss
+            torch.cuda.synchronize()
+        log(f"[d3] round {rnd}: " + ", ".join(f"{a} {per_arm[a][-1]['ms_per_step']:.3f} ms"
+                                              for a in STAGED_ARMS))
+    arms = {}
+    for a, recs in per_arm.items():
+        med = {k_: float(np.median([r[k_] for r in recs])) for k_ in recs[0]}
+        arms[a] = {"ms_per_step": round(med["ms_per_step"], 4),
+                   "tok_s": round(1000.0 / med["ms_per_step"], 2),
+                   "rounds_ms": [round(r["ms_per_step"], 4) for r in recs],
+                   "hit_rate": round(med["hit_rate"], 4),
+                   "misses_per_step": round(med["misses_per_step"], 2),
+                   "h2d_bytes_per_step": int(med["h2d_bytes_per_step"])}
+        if "distinct_experts_last_step" in med:
+            arms[a]["distinct_experts_last_step"] = int(med["distinct_experts_last_step"])
+    t_comp = arms["resident"]["ms_per_step"]
+    for a in STAGED_ARMS[:-1]:
+        r = arms[a]
+        copy_ms = r["h2d_bytes_per_step"] / (bw * 1e9) * 1e3
+        exposed = max(0.0, r["ms_per_step"] - t_comp)
+        r["copy_ms_per_step"] = round(copy_ms, 4)
+        r["exposed_wait_ms_per_step"] = round(exposed, 4)
+        r["overlap"] = round(1.0 - exposed / copy_ms, 4) if copy_ms > 0 else None
+        r["host_link_ceiling_tok_s"] = round(1000.0 / copy_ms, 2) if copy_ms > 0 else None
+    a = arms["ahead"]
+    achieved = a["h2d_bytes_per_step"] / (a["ms_per_step"] * 1e-3) / 1e9
+    out = {"metric": "staged decode tok/s (batch 1, 40-layer MoE stack, 3 GiB HBM pool)",
+           "value": a["tok_s"], "unit": "tok/s", "higher_is_better": True,
+           "config": {"workload": "40-layer Qwen3-MoE-shaped decode stack, experts staged from "
+                                  "pinned host memory into a 3 GiB HBM pool (LRU)",
+                      "n_slots": n_slots, "bundle_bytes": bb, "top_k": S.top_k,
+                      "trace": "Zipf(1.1), per-layer permutation, keep_p 0.06",
+                      "trace_overlap": round(overlap, 4),
+                      "timing": f"{rounds} rounds, arm order rotated, {warmup} warmup + "
+                                f"{steps} timed steps per arm and round, medians"},
+           "h2d_gbps": {"dma_copy": round(bw_dma, 2), "fill_kernel": round(bw_kernel, 2)},
+           "roofline": {"kernel": "host link (prediction arm's H2D bytes per step)",
+                        "bound": "host-link", "achieved": round(achieved, 2),
+                        "peak": round(bw, 2), "unit": "GB/s", "frac": round(achieved / bw, 4),
+                        "traffic": None},
+           "arms": arms}
+    if not args.no_cpu:
+        import oracle as O
+        own, con = range(OWNERS[0], OWNERS[1] + 1), range(CONSUMERS[0], CONSUMERS[1] + 1)
+        ev = O.canonical_requests(total, N_LAYERS, own, con, heads_at_end=True)
+        t0 = time.perf_counter()
+        O.lru_replay(ev, lambda L, t: trace[t, L], n_slots)
+        s = (time.perf_counter() - t0) / total
+        out["cpu_baseline"] = cpu_record(1e3 * s, 1e3 * s, "ms/step (LRU replay)", 1,
+                                         f"the oracle LRU replay of {total} steps of the trace "
+                                         "(single-threaded Python)")
+    del host
+    return out
 
-        us = timed(0)
-        if args.mfma_sweep:
-            sweep = {"gemv_only": round(timed(E.EDGE0_GROUPED_NO_MFMA), 2)}
-            for mn in (2, 4, 8, 24):
-                sweep[f"mfma_from_{mn}"] = round(timed(E.grouped_mfma_min(mn)), 2)
-            log(f"[grouped] T={T} us/call by MFMA threshold: default {us:.2f}, {sweep}")
-        nbytes = union * bb
-        flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
-        results[T] = {"us_per_call": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
-                      "experts": round(union, 2),
-                      "path": "mfma tiles" if T >= 3 else "gemv",
-                      "union_bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
-                      "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "tflops": round(flops / (us * 1e-6) / 1e12, 3)}
-        log(f"[grouped] T={T}: {results[T]}")
-    best = results[32]
-    out = {
-        "metric": "grouped MoE layer tok/s (K=8, Qwen3-MoE shapes) + union-bytes GB/s vs peak",
-        "value": best["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": 256, "warmup": 32,
-        "ms_per_step": round(best["us_per_call"] / 1000, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "one Qwen3-MoE-shaped layer, 32 tokens per call, K=8, Zipf(1.1) "
-                               "routing, 64 rotated layer instances",
-                   "d_model": d, "n_experts": En, "d_inter": I, "top_k": K, "group": S.group,
-                   "lora_rank": r, "global_batch": 32, "parallelism": "none"},
-        "roofline": {"bound": "hbm", "achieved": best["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": best["frac_of_hbm_peak"], "traffic": None},
-        "per_tokens": {str(k): v for k, v in results.items()},
-    }
-    print(json.dumps(out), flush=True)
 
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--workload", choices=["resident", "streamed", "grouped"], default="resident",
-                    help="resident: every bundle in HBM (the headline line); streamed: "
-                         "experts staged from pinned host memory into a 3 GiB pool; grouped: "
-                         "the multi-token grouped layer at 1-32 tokens per call")
-    ap.add_argument("--stack-mode", choices=["graphs", "persistent", "xcd", "xlayer"],
-                    default="graphs",
-                    help="resident workload: per-layer launches replayed as HIP graphs (the "
-                         "default, the faster of the two here) or the layers as one persistent "
-                         "cooperative launch per step")
-    ap.add_argument("--mfma-sweep", action="store_true",
-                    help="grouped workload: also time other MFMA thresholds")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a device-to-device copy of MIB MiB (hardware counter "
-                         "calibration: known bytes moved) and exit")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 4}))
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
-    def log(msg):
-        print(msg, file=sys.stderr, flush=True)
-
-    if args.workload == "streamed":
-        bench_streamed(args, log)
-        return
-    if args.workload == "grouped":
-        bench_grouped(args, log)
-        return
-
+# ------------------------------------------------------------ D2: stack
+def row_stack(args, log):
     import torch
     from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
     from int4_expert_streaming_amd.stackbuild import DeviceStack
     from int4_expert_streaming_amd.weights import to_device
-
     S = G.QWEN3_MOE
-    torch.cuda.set_device(0)
     ds = DeviceStack(S, G.StackGen(S, args.seed), N_LAYERS, OWNERS, CONSUMERS, log=log)
-    from int4_expert_streaming_amd import edge0 as E
     mode_name = args.stack_mode
     if mode_name != "graphs":
         try:
@@ -478,9 +782,8 @@ def main():
     step_gbps = sbytes * tok_s / 1e9
     ds.stack.set_timing(1)
     if persistent:
-        # dominant kernel: k_flow_step, the one launch that runs all 40
-        # layers, bracketed by events on the launching stream over further
-        # steps of the same stack
+        # dominant kernel: the one launch that runs all 40 layers, bracketed
+        # by events on the launching stream over further steps
         k_ms = []
         for t in range(total, total + 8):
             ds.step(h0[t % total], h_out, t)
@@ -490,10 +793,9 @@ def main():
         k_bytes = flow_bytes(S, n_routers=8)
         k_traffic = None
     else:
-        # dominant kernel: the prediction-routed layers' k_layer_fused (input +
-        # gate/up, 32 launches per step), timed by events the dispatch records
-        # at its start and end, on the launching stream, over further steps of
-        # the same stack (launch class 1 = each layer's gate/up launch)
+        # dominant kernel: the prediction-routed layers' first launch (32 per
+        # step), timed by events the dispatch records at its start and end on
+        # the launching stream, over further steps of the same stack
         k_ms = []
         for t in range(total, total + 8):
             ds.step(h0[t % total], h_out, t)
@@ -513,7 +815,8 @@ def main():
     k_gbps = k_bytes / (k_mean * 1e-3) / 1e9
     log(f"[bench] {ms_step * 1000:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
         f"{step_gbps:.0f} GB/s step, {k_name.split()[0]} {k_mean * 1000:.2f} us = {k_gbps:.0f} GB/s")
-
+    rl = roofline(k_name, k_bytes, k_mean * 1000)
+    rl["traffic"] = k_traffic
     out = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -527,15 +830,104 @@ def main():
                    "prediction_routed": "7-38", "global_batch": 1, "parallelism": "none"},
         "step_bytes": sbytes, "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": k_name,
-                     "bound": "hbm", "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(k_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": k_traffic, "bytes_per_launch": k_bytes,
-                     "avg_launch_us": round(k_mean * 1000, 3)},
+        "roofline": rl,
     }
+    del ds
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def single_row_line(row, args):
+    """A row run alone: its own JSON line in the contract's keys."""
+    out = {"metric": row["metric"], "value": row["value"], "unit": row["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
+           "higher_is_better": row.get("higher_is_better", True), "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    out.update({k: v for k, v in row.items() if k not in out})
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
+    ap.add_argument("--rows", choices=["all", "none"], default="all",
+                    help="all: the headline line also carries rows d0, d1_k4, d1_k8, d3, d4")
+    ap.add_argument("--workload", choices=["resident", "streamed", "grouped", "layer", "tiny"],
+                    default="resident",
+                    help="resident: the headline (40-layer stack, every bundle in HBM); the "
+                         "others run one row alone: streamed (d3), grouped (d4), layer (d1), "
+                         "tiny (d0)")
+    ap.add_argument("--stack-mode", choices=["graphs", "persistent", "xcd", "xlayer"],
+                    default="graphs",
+                    help="resident workload: per-layer launches replayed as HIP graphs (the "
+                         "default, the fastest here), the layers as one persistent launch per "
+                         "step, the XCD-split persistent launch, or one XCD-split launch per "
+                         "layer")
+    ap.add_argument("--mfma-sweep", action="store_true",
+                    help="grouped row: also time other MFMA thresholds")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (hardware counter "
+                         "calibration: known bytes moved) and exit")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 4}))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    import torch
+    torch.cuda.set_device(0)
+    from synth import gen as G
+    if args.workload == "streamed":
+        print(json.dumps(single_row_line(row_staged(args, log), args)), flush=True)
+        return
+    if args.workload in ("grouped", "layer"):
+        inst = Instances(G.QWEN3_MOE, args.seed, log)
+        if args.workload == "grouped":
+            row = row_grouped(args, log, inst)
+            print(json.dumps(single_row_line(row, args)), flush=True)
+        else:
+            for K in (4, 8):
+                print(json.dumps(single_row_line(row_layer(args, log, inst, K), args)), flush=True)
+        return
+    if args.workload == "tiny":
+        print(json.dumps(single_row_line(row_tiny(args, log), args)), flush=True)
+        return
+
+    out = row_stack(args, log)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(S, args.seed)
+        out["cpu_baseline"] = cpu_baseline_stack(G.QWEN3_MOE, args.seed)
+    if args.rows == "all":
+        t0 = time.time()
+        rows = {"d0": row_tiny(args, log)}
+        inst = Instances(G.QWEN3_MOE, args.seed, log)
+        rows["d1_k4"] = row_layer(args, log, inst, 4)
+        rows["d1_k8"] = row_layer(args, log, inst, 8)
+        rows["d4"] = row_grouped(args, log, inst)
+        del inst
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rows["d3"] = row_staged(args, log)
+        out["rows"] = rows
+        log(f"[bench] rows measured in {time.time() - t0:.0f}s")
     print(json.dumps(out), flush=True)
 
 

@@ -99,12 +99,22 @@ class HostBundles:
         return self.mem[k * self.bundle_bytes:(k + 1) * self.bundle_bytes]
 
 
+def device_routers_heads(gen, n_layers, owners, threads=16):
+    """Device copies of every layer's router and of the owner layers' heads
+    (None elsewhere)."""
+    with ThreadPoolExecutor(threads) as ex:
+        routers = list(ex.map(gen.router, range(n_layers)))
+        heads = list(ex.map(lambda L: gen.head(L) if L in owners else None, range(n_layers)))
+    return ([to_device(r) for r in routers],
+            [None if h is None else head_to_device(h) for h in heads])
+
+
 class StreamedStack:
     """The decode stack over a bounded HBM pool of n_slots slots, staged from
     pinned host bundles by the library's stager, routed by a given trace."""
 
     def __init__(self, shape, gen, n_layers, owners, consumers, n_slots, eps=1e-6, threads=16,
-                 log=print, host=None):
+                 log=print, host=None, routers=None, heads=None):
         self.S = shape
         self.sh = E.make_shape(shape)
         En = shape.n_experts
@@ -115,12 +125,9 @@ class StreamedStack:
         self.host = host if host is not None else HostBundles(shape, gen, n_layers, threads, log)
         self.pool = SlotPoolBuffer(self.sh, n_slots)
         self.table = torch.full((n_layers, En), -1, dtype=torch.int32, device="cuda")
-        with ThreadPoolExecutor(threads) as ex:
-            routers = list(ex.map(gen.router, range(n_layers)))
-            heads = list(ex.map(lambda L: gen.head(L) if L in self.owners else None,
-                                range(n_layers)))
-        self.routers = [to_device(r) for r in routers]
-        self.heads = [None if h is None else head_to_device(h) for h in heads]
+        if routers is None or heads is None:  # device copies, or built here
+            routers, heads = device_routers_heads(gen, n_layers, self.owners, threads)
+        self.routers, self.heads = routers, heads
         torch.cuda.synchronize()
         self.stack = E.Stack(self.sh, self.spec, self.pool.pool, self.table, self.routers,
                              self.heads)
