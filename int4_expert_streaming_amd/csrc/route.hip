@@ -114,19 +114,23 @@ __global__ __launch_bounds__(256) void k_heads_fc1(HeadBatch hb) {
   }
 }
 
-// logits[i][e] = w2[e] . a_i + b2[e] + res[i][e], then head i's top-K: one
-// workgroup per head (16 waves; each wave 8 rows at a time, one 16-byte
-// chunk of each fp16 row per lane, the 8 row sums reduced together); the
-// logits meet in LDS and wave 0 commits the top-K.
-__global__ __launch_bounds__(1024) void k_heads_fc2(HeadBatch hb) {
-  __shared__ float lg_s[1024];
-  const int i = blockIdx.x;
+// logits[i][e] = w2[e] . a_i + b2[e] + res[i][e], then head i's commit.
+// A workgroup covers 8 * kFc2Waves rows of one head (each wave 8 rows at a
+// time, one 16-byte chunk of each fp16 row per lane, the 8 row sums reduced
+// together), so a head spreads over E / 16 compute units; the logits go to
+// memory and the head's last workgroup to finish (completion counter, reset
+// by it) commits the top-K.
+constexpr int kFc2Waves = 2;
+__global__ __launch_bounds__(64 * kFc2Waves) void k_heads_fc2(HeadBatch hb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = hb.H, E = hb.E, K = hb.K;
+  const int parts = (E + 8 * kFc2Waves - 1) / (8 * kFc2Waves);
+  const int i = blockIdx.x / parts;
+  const int rb = (blockIdx.x % parts) * 8 * kFc2Waves + 8 * wave;
   const float* av = hb.a + (size_t)i * H;
   const uint16_t* w2 = hb.w2[i];
   const int nch = H / 8;  // 16-byte chunks per row
-  for (int rb = 8 * wave; rb < E; rb += 128) {
+  if (rb < E) {
     float v[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) v[m] = 0.f;
@@ -160,15 +164,16 @@ __global__ __launch_bounds__(1024) void k_heads_fc2(HeadBatch hb) {
         float s = sum;
         if (hb.b2[i] != nullptr) s += h2f(hb.b2[i][e]);
         if (hb.has_res) s += hb.res[(size_t)i * E + e];
-        lg_s[e] = s;
-        hb.logits[(size_t)i * E + e] = s;
+        st_dev(hb.logits + (size_t)i * E + e, s);
       }
     }
   }
-  __syncthreads();
-  if (wave == 0)
-    wave_commit<false>(lg_s, E, K, hb.rule, hb.ids_out + (size_t)i * hb.out_stride,
-                       hb.w_out + (size_t)i * hb.out_stride);
+  if (last_arrival(hb.counters + i, parts)) {
+    if (wave == 0)
+      wave_commit<true>(hb.logits + (size_t)i * E, E, K, hb.rule,
+                        hb.ids_out + (size_t)i * hb.out_stride, hb.w_out + (size_t)i * hb.out_stride);
+    if (tid == 0) __hip_atomic_store(hb.counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 int launch_heads(const HeadBatch& hb, hipStream_t stream) {
@@ -176,7 +181,8 @@ int launch_heads(const HeadBatch& hb, hipStream_t stream) {
   const int per1 = (hb.H + (hb.has_res ? hb.E : 0) + 3) / 4;
   k_heads_fc1<<<hb.n * per1, 256, 0, stream>>>(hb);
   E0_CHECK_LAUNCH();
-  k_heads_fc2<<<hb.n, 1024, 0, stream>>>(hb);
+  k_heads_fc2<<<hb.n * ((hb.E + 8 * kFc2Waves - 1) / (8 * kFc2Waves)), 64 * kFc2Waves, 0,
+                stream>>>(hb);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
