@@ -303,6 +303,33 @@ int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                       hipStream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Whole-layer prefill ([Edge0] §3.1 "Executor paths", whole-layer; §3.2
+ * "Two consumption profiles": prefill takes every expert of a layer, and
+ * there is nothing to predict).  The result is edge0_moe_grouped's, token by
+ * token (an id repeated within a token's routing is kept once, its weights
+ * summed in k order), for up to 4096 tokens per call: the (token, k) pairs
+ * are bucketed by expert over many workgroups, each expert's tokens run in
+ * tiles of up to 16 on bf16 MFMA (int4 weights as exact 128 + q), each
+ * tile's LoRA A x on MFMA too, and every token's weighted rows are added in
+ * fixed point (calls are bit-reproducible).
+ *   slot_table, ids, w, x, y : as edge0_moe_grouped ([n_tokens][K] routing,
+ *                [n_tokens][d] bf16 in and out; y must not alias x)
+ *   max_tokens : the token bound the workspace was sized for
+ *                (1 <= max_tokens <= 4096, n_tokens <= max_tokens)
+ *   workspace  : edge0_prefill_workspace_bytes(shape, max_tokens) bytes,
+ *                zero-filled once before first use (calls leave it ready)
+ * Shapes: those of the grouped call's MFMA tiles (d_model <= 2048 and a
+ * multiple of 8 g, g of 32 or 64, d_inter / 32 in {4, 8, 12, 16, 24, 32},
+ * even lora_rank <= 16); EDGE0_EINVAL otherwise.  An id or slot out of range
+ * is recorded in the workspace error word (edge0_workspace_error) and its
+ * pair contributes nothing. */
+size_t edge0_prefill_workspace_bytes(const edge0_moe_shape* shape, int32_t max_tokens);
+int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                      const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
+                      const float* w, const void* x, void* y, void* workspace,
+                      int32_t max_tokens, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
  * Decode stack: n_layers pre-norm residual MoE blocks (no attention),
  *   x_L = bf16(RMSNorm(h_L)),  RMSNorm(h) = h / sqrt(mean(h^2) + eps)
  *   routing_L = committed prediction (consumer layers, step > 0) or the

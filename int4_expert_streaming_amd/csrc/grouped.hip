@@ -69,6 +69,9 @@ struct GrpArgs {
   float* hs;                   // [P][I/16]
   unsigned long long* tdown;   // [P][r] A_down h, fixed point
   unsigned long long* acc;     // [T][d] y, fixed point
+  // prefill: the tile list (active expert, tile within it), info[2] entries;
+  // NULL in the grouped call, whose grid enumerates every (tile, expert)
+  const int2* tiles;
 };
 
 // ------------------------------------------------------------- bucketing
@@ -720,9 +723,18 @@ __global__ __launch_bounds__(256, 3) void k_grp_gu_tile(GrpArgs a, int tm, int m
   constexpr int NW = GW * WPG;
   __shared__ GuTileLds sm;
   const int nblk = a.I / 16;
-  const int tt = blockIdx.x / (a.Amax * nblk);
-  const int act = (blockIdx.x / nblk) % a.Amax;
   const int blk = blockIdx.x % nblk;
+  int tt, act;
+  if (a.tiles != nullptr) {  // prefill: entry blockIdx / nblk of the tile list
+    const int li = blockIdx.x / nblk;
+    if (li >= a.info[2]) return;
+    const int2 te = a.tiles[li];
+    act = te.x;
+    tt = te.y;
+  } else {
+    tt = blockIdx.x / (a.Amax * nblk);
+    act = (blockIdx.x / nblk) % a.Amax;
+  }
   // everything the start depends on, in one round trip
   const int n_act = a.info[0], cnt = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
   asm volatile("" ::"s"(n_act), "s"(cnt), "s"(slot), "s"(q0));
@@ -892,9 +904,18 @@ __global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int
   __shared__ float gsum[kTileTok][GD];
   __shared__ float td_s[kTileTok][kTileRank];  // zero past the rank
   const int nrb = a.d / (64 * kDownNT);
-  const int tt = blockIdx.x / (a.Amax * nrb);
-  const int act = (blockIdx.x / nrb) % a.Amax;
   const int rb = blockIdx.x % nrb;
+  int tt, act;
+  if (a.tiles != nullptr) {  // prefill: entry blockIdx / nrb of the tile list
+    const int li = blockIdx.x / nrb;
+    if (li >= a.info[2]) return;
+    const int2 te = a.tiles[li];
+    act = te.x;
+    tt = te.y;
+  } else {
+    tt = blockIdx.x / (a.Amax * nrb);
+    act = (blockIdx.x / nrb) % a.Amax;
+  }
   const int n_act = a.info[0], cnt = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
   asm volatile("" ::"s"(n_act), "s"(cnt), "s"(slot), "s"(q0));
   const int t_first = tt * tm;
@@ -928,6 +949,161 @@ __global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
     a.acc[i] = 0ull;
   }
   for (int j = i; j < a.P * a.r; j += gridDim.x * 256) a.tdown[j] = 0ull;
+}
+
+// ------------------------------------------------------------ prefill
+// The whole-layer path for a prompt chunk ([Edge0] §3.1 "Executor paths",
+// whole-layer; §3.2 "Two consumption profiles": prefill hits every expert of
+// a layer).  Token by token the same result as the grouped call, for up to
+// kPfMaxTokens tokens: the bucketing runs over many workgroups and lists
+// the (expert, 16-token tile) units that exist, so the tile kernels' grids
+// cover those units rather than every (tile, expert) combination, and each
+// tile's LoRA A x runs on MFMA.  Pairs are placed in an expert's run in
+// arrival order; a pair's results do not depend on its place (every MFMA
+// output element is its own row's dot product, and the outputs are added in
+// fixed point), so calls are bit-reproducible.
+constexpr int kPfMaxTokens = 4096;
+
+// pass 1: per pair, an id repeated within its token is dropped (its first
+// listing keeps the weights summed in k order); kept pairs counted per expert
+__global__ __launch_bounds__(256) void k_pf_count(GrpArgs a, int32_t* cnt, int32_t* keep,
+                                                  float* keep_w) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= a.P) return;
+  const int K = a.K, k0 = p - p % K;
+  int e = a.ids[p];
+  float w = a.w[p];
+  if (e < 0 || e >= a.E) {
+    set_error(a.err, EDGE0_ERANGE);
+    e = -1;
+  } else {
+    bool dup = false;
+    for (int q = k0; q < p; ++q) dup |= a.ids[q] == e;
+    for (int q = p + 1; q < k0 + K; ++q)
+      if (a.ids[q] == e) w += a.w[q];
+    if (dup) e = -1;
+  }
+  keep[p] = e;
+  keep_w[p] = w;
+  if (e >= 0) atomicAdd(cnt + e, 1);
+}
+
+// pass 2 (one workgroup, one expert per thread): exclusive scans of the
+// counts, the active flags and the tiles per expert; the active list, each
+// expert's first free position, the tile list; the counts cleared
+__global__ __launch_bounds__(1024) void k_pf_scan(GrpArgs a, int32_t* cnt, int32_t* fill,
+                                                  int2* tiles) {
+  __shared__ int wtot[3][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E;
+  const int c = tid < E ? cnt[tid] : 0;
+  const int f = c > 0 ? 1 : 0;
+  const int nt = (c + kTileTok - 1) / kTileTok;
+  const int ic = wave_incl_scan(c), iff = wave_incl_scan(f), it = wave_incl_scan(nt);
+  if (lane == 63) {
+    wtot[0][wave] = ic;
+    wtot[1][wave] = iff;
+    wtot[2][wave] = it;
+  }
+  __syncthreads();
+  int bc = 0, bf = 0, bt = 0, tc = 0, tf = 0, tt = 0;
+  for (int v = 0; v < 16; ++v) {
+    if (v < wave) {
+      bc += wtot[0][v];
+      bf += wtot[1][v];
+      bt += wtot[2][v];
+    }
+    tc += wtot[0][v];
+    tf += wtot[1][v];
+    tt += wtot[2][v];
+  }
+  const int xc = bc + ic - c, xf = bf + iff - f, xt = bt + it - nt;
+  if (tid < E) {
+    fill[tid] = xc;
+    cnt[tid] = 0;
+    if (f) {
+      const int slot = a.table[tid];
+      const bool ok = slot >= 0 && slot < a.n_slots;
+      a.act_e[xf] = tid;
+      a.act_off[xf] = xc;
+      a.act_cnt[xf] = c;
+      a.act_slot[xf] = ok ? slot : -1;
+      if (!ok) set_error(a.err, EDGE0_ERANGE);
+      for (int i = 0; i < nt; ++i) tiles[xt + i] = make_int2(xf, i);
+    }
+  }
+  if (tid == 0) {
+    a.info[0] = tf;
+    a.info[1] = tc;
+    a.info[2] = tt;
+  }
+}
+
+// pass 3: each kept pair to the next free position of its expert's run
+__global__ __launch_bounds__(256) void k_pf_scatter(GrpArgs a, const int32_t* keep,
+                                                    const float* keep_w, int32_t* fill) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= a.P) return;
+  const int e = keep[p];
+  if (e < 0) return;
+  const int dst = atomicAdd(fill + e, 1);
+  a.pair_tok[dst] = p / a.K;
+  a.pair_src[dst] = p;
+  a.pair_w[dst] = keep_w[p];
+}
+
+// LoRA A x of a tile's pairs, one workgroup per tile-list entry: the tile's
+// tokens (A operand, rows = tokens) against the expert's 2r LoRA A rows (B
+// operand; row q < r is A_gate's row q, then A_up's), bf16 MFMA 16x16x32
+// in one or two 16-row n-tiles; the 4 waves take quarters of d and their
+// partials are summed in LDS in wave order.  Both operands carry the same
+// 8 inputs per lane, in their natural order.
+__global__ __launch_bounds__(256) void k_pf_lora_in(GrpArgs a) {
+  __shared__ float part[4][kTileTok][2 * kTileRank];
+  const int li = blockIdx.x;
+  if (li >= a.info[2]) return;
+  const int2 te = a.tiles[li];
+  const int cnt = a.act_cnt[te.x], slot = a.act_slot[te.x], q0 = a.act_off[te.x];
+  if (slot < 0) return;  // reported by the scan; the tile kernels skip it too
+  const int t0 = te.y * kTileTok, mt = min(kTileTok, cnt - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int r = a.r, d = a.d;
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+  const int tok = a.pair_tok[q0 + t0 + min(n, mt - 1)];  // past the tile: its last token again
+  const uint16_t* xr = a.x + (size_t)tok * d;
+  const int q1 = n, q2 = 16 + n;  // this lane's B rows in the two n-tiles
+  const uint16_t* w1 = reinterpret_cast<const uint16_t*>(b + (q1 < r ? a.lay.a_gate : a.lay.a_up)) +
+                       (size_t)(q1 % r) * d;
+  const uint16_t* w2 = reinterpret_cast<const uint16_t*>(
+                           b + (q2 < 2 * r ? (q2 < r ? a.lay.a_gate : a.lay.a_up) : a.lay.a_gate)) +
+                       (size_t)(q2 < 2 * r ? q2 % r : 0) * d;
+  const bool two = 2 * r > 16;
+  f32x4_t c1 = {0.f, 0.f, 0.f, 0.f}, c2 = c1;
+  const int kq = d / 4;
+  for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 32) {
+    const bf16x8_t xo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + k0 + 8 * j));
+    const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w1 + k0 + 8 * j));
+    c1 = mfma16(xo, b1, c1);
+    if (two) {
+      const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w2 + k0 + 8 * j));
+      c2 = mfma16(xo, b2, c2);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    part[wave][4 * j + v][q1] = c1[v];
+    part[wave][4 * j + v][q2] = two ? c2[v] : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < kTileTok * 2 * r; e += 256) {
+    const int m = e / (2 * r), q = e % (2 * r);
+    if (m < mt) {
+      const float t = part[0][m][q] + part[1][m][q] + part[2][m][q] + part[3][m][q];
+      const int src = a.pair_src[q0 + t0 + m];
+      a.t_in[((size_t)src * 2 + q / r) * r + q % r] = t;
+    }
+  }
 }
 
 // ------------------------------------------------------------- host side
@@ -1026,11 +1202,11 @@ static bool grp_tile_ok(const GrpArgs& a) {
 }
 
 // experts with >= min_cnt tokens
-static int launch_grp_tiles_gu(const GrpArgs& a, int min_cnt, hipStream_t st) {
-  const int tm = a.T < kTileTok ? a.T : kTileTok;
-  const int nt = (a.T + tm - 1) / tm;
+// units = (tile, expert) units of the grid: ceil(T / tm) * Amax for the
+// grouped call, the tile list's bound for prefill
+static int launch_grp_tiles_gu(const GrpArgs& a, int min_cnt, int tm, int units, hipStream_t st) {
   const int wpg = a.g / 32, gw = a.d / (4 * a.g);
-  const int grid_gu = nt * a.Amax * (a.I / 16);
+  const int grid_gu = units * (a.I / 16);
 #define E0_GU(GW, W) \
   if (gw == GW && wpg == W) k_grp_gu_tile<GW, W><<<grid_gu, 256, 0, st>>>(a, tm, min_cnt)
   bool ok = true;
@@ -1042,12 +1218,10 @@ static int launch_grp_tiles_gu(const GrpArgs& a, int min_cnt, hipStream_t st) {
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
-static int launch_grp_tiles_down(const GrpArgs& a, int min_cnt, hipStream_t st) {
-  const int tm = a.T < kTileTok ? a.T : kTileTok;
-  const int nt = (a.T + tm - 1) / tm;
+static int launch_grp_tiles_down(const GrpArgs& a, int min_cnt, int tm, int units, hipStream_t st) {
   const int wpg = a.g / 32, nw = a.I / 32;
   const size_t lds_dn = (size_t)2 * tm * a.I * 2;
-  const int grid_dn = nt * a.Amax * (a.d / (64 * kDownNT));
+  const int grid_dn = units * (a.d / (64 * kDownNT));
   bool ok = true;
 #define E0_DN(NW, W) \
   if (nw == NW && wpg == W) k_grp_down_tile<NW, W><<<grid_dn, 256, lds_dn, st>>>(a, tm, min_cnt)
@@ -1132,10 +1306,145 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
     if (tile_min > n_tokens) tile_min = 0;
   }
   const int gemv_max = tile_min ? tile_min - 1 : 1 << 30;
+  const int tm = a.T < kTileTok ? a.T : kTileTok;
+  const int units = (a.T + tm - 1) / tm * a.Amax;
   int rc = gemv_max >= 1 ? launch_grp_gate_up(a, 1, gemv_max, stream) : EDGE0_OK;
-  if (rc == EDGE0_OK && tile_min) rc = launch_grp_tiles_gu(a, tile_min, stream);
+  if (rc == EDGE0_OK && tile_min) rc = launch_grp_tiles_gu(a, tile_min, tm, units, stream);
   if (rc == EDGE0_OK && gemv_max >= 1) rc = launch_grp_down(a, 1, gemv_max, stream);
-  if (rc == EDGE0_OK && tile_min) rc = launch_grp_tiles_down(a, tile_min, stream);
+  if (rc == EDGE0_OK && tile_min) rc = launch_grp_tiles_down(a, tile_min, tm, units, stream);
+  if (rc != EDGE0_OK) return rc;
+  const int n_out = a.T * a.d;
+  k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);
+  E0_CHECK_LAUNCH();
+  return EDGE0_OK;
+}
+
+// ------------------------------------------------------------ prefill host
+namespace e0 {
+struct PfWs {
+  size_t err, info, cnt, fill, keep, keep_w, tiles, act_e, act_off, act_cnt, act_slot, pair_tok,
+      pair_src, pair_w, t_in, hp_hi, hp_lo, hs, tdown, acc, total;
+};
+// an upper bound of the tile list: sum over experts of ceil(count / 16)
+static int pf_tiles_max(int P, int E) { return (P + kTileTok - 1) / kTileTok + (E < P ? E : P); }
+static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
+  PfWs L{};
+  const size_t T = max_tokens, d = s->d_model, E = s->n_experts, I = s->d_inter;
+  const size_t P = T * s->top_k, r = s->lora_rank;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + (bytes ? bytes : 4) + 255) & ~(size_t)255;
+    return o;
+  };
+  L.err = take(4);
+  L.info = take(16);
+  L.cnt = take(4 * E);
+  L.fill = take(4 * E);
+  L.keep = take(4 * P);
+  L.keep_w = take(4 * P);
+  L.tiles = take(8 * (size_t)pf_tiles_max((int)P, (int)E));
+  L.act_e = take(4 * E);
+  L.act_off = take(4 * E);
+  L.act_cnt = take(4 * E);
+  L.act_slot = take(4 * E);
+  L.pair_tok = take(4 * P);
+  L.pair_src = take(4 * P);
+  L.pair_w = take(4 * P);
+  L.t_in = take(4 * P * 2 * r);
+  L.hp_hi = take(2 * P * I);
+  L.hp_lo = take(2 * P * I);
+  L.hs = take(4 * P * (I / 16));
+  L.tdown = take(8 * P * r);
+  L.acc = take(8 * T * d);
+  L.total = off;
+  return L;
+}
+// the token-tile kernels' shapes (every prefill unit runs on them)
+static bool pf_shape_ok(const edge0_moe_shape* s) {
+  if (!grouped_shape_ok(s)) return false;
+  const int d = s->d_model, g = s->group_size, I = s->d_inter, r = s->lora_rank;
+  const int gw = d / (4 * g), nw = I / 32;
+  return (g == 32 || g == 64) && d <= 2048 && d % (8 * g) == 0 &&
+         (gw == 2 || gw == 4 || gw == 8 || gw == 16) && I % 32 == 0 &&
+         (nw == 4 || nw == 8 || nw == 12 || nw == 16 || nw == 24 || nw == 32) && r <= kTileRank &&
+         r % 2 == 0;
+}
+}  // namespace e0
+
+extern "C" size_t edge0_prefill_workspace_bytes(const edge0_moe_shape* shape, int32_t max_tokens) {
+  if (!shape || !pf_shape_ok(shape) || max_tokens < 1 || max_tokens > kPfMaxTokens) return 0;
+  return pf_ws_layout(shape, max_tokens).total;
+}
+
+extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                 const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
+                                 const float* w, const void* x, void* y, void* workspace,
+                                 int32_t max_tokens, hipStream_t stream) {
+  if (!shape || !pf_shape_ok(shape) || !pool || !pool->base || !slot_table || !workspace ||
+      max_tokens < 1 || max_tokens > kPfMaxTokens || n_tokens < 0 || n_tokens > max_tokens)
+    return EDGE0_EINVAL;
+  if (n_tokens == 0) return EDGE0_OK;
+  if (!ids || !w || !x || !y || x == y) return EDGE0_EINVAL;
+  edge0_bundle_layout lay;
+  if (bundle_layout(shape, &lay) != EDGE0_OK || pool->slot_bytes < lay.bytes) return EDGE0_EINVAL;
+  const PfWs L = pf_ws_layout(shape, max_tokens);
+  char* ws = static_cast<char*>(workspace);
+  GrpArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool->base);
+  a.slot_bytes = pool->slot_bytes;
+  a.n_slots = pool->n_slots;
+  a.table = slot_table;
+  a.ids = ids;
+  a.w = w;
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.T = n_tokens;
+  a.d = shape->d_model;
+  a.E = shape->n_experts;
+  a.I = shape->d_inter;
+  a.K = shape->top_k;
+  a.g = shape->group_size;
+  a.r = shape->lora_rank;
+  a.scale = a.r > 0 ? shape->lora_alpha / (float)a.r : 0.f;
+  a.lay = lay;
+  a.P = n_tokens * a.K;
+  a.Amax = a.E < a.P ? a.E : a.P;
+  a.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  a.info = reinterpret_cast<int32_t*>(ws + L.info);
+  a.act_e = reinterpret_cast<int32_t*>(ws + L.act_e);
+  a.act_off = reinterpret_cast<int32_t*>(ws + L.act_off);
+  a.act_cnt = reinterpret_cast<int32_t*>(ws + L.act_cnt);
+  a.act_slot = reinterpret_cast<int32_t*>(ws + L.act_slot);
+  a.pair_tok = reinterpret_cast<int32_t*>(ws + L.pair_tok);
+  a.pair_src = reinterpret_cast<int32_t*>(ws + L.pair_src);
+  a.pair_w = reinterpret_cast<float*>(ws + L.pair_w);
+  a.t_in = reinterpret_cast<float*>(ws + L.t_in);
+  a.hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
+  a.hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
+  a.hs = reinterpret_cast<float*>(ws + L.hs);
+  a.tdown = reinterpret_cast<unsigned long long*>(ws + L.tdown);
+  a.acc = reinterpret_cast<unsigned long long*>(ws + L.acc);
+  a.tiles = reinterpret_cast<const int2*>(ws + L.tiles);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
+  int32_t* fill = reinterpret_cast<int32_t*>(ws + L.fill);
+  int32_t* keep = reinterpret_cast<int32_t*>(ws + L.keep);
+  float* keep_w = reinterpret_cast<float*>(ws + L.keep_w);
+  int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
+  const int pg = (a.P + 255) / 256;
+  k_pf_count<<<pg, 256, 0, stream>>>(a, cnt, keep, keep_w);
+  E0_CHECK_LAUNCH();
+  k_pf_scan<<<1, 1024, 0, stream>>>(a, cnt, fill, tiles);
+  E0_CHECK_LAUNCH();
+  k_pf_scatter<<<pg, 256, 0, stream>>>(a, keep, keep_w, fill);
+  E0_CHECK_LAUNCH();
+  const int units = pf_tiles_max(a.P, a.E);
+  if (a.r > 0) {
+    k_pf_lora_in<<<units, 256, 0, stream>>>(a);
+    E0_CHECK_LAUNCH();
+  }
+  int rc = launch_grp_tiles_gu(a, 1, kTileTok, units, stream);
+  if (rc == EDGE0_OK) rc = launch_grp_tiles_down(a, 1, kTileTok, units, stream);
   if (rc != EDGE0_OK) return rc;
   const int n_out = a.T * a.d;
   k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);

@@ -138,6 +138,9 @@ _SIG = {
     "edge0_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
     "edge0_workspace_error": (C.c_int, [_P, _P]),
     "edge0_route_commit": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P]),
+    "edge0_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape), C.c_int32]),
+    "edge0_moe_prefill": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, C.c_int32, _P,
+                                    _P, _P, _P, _P, C.c_int32, _P]),
     "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P]),
     "edge0_prerouter": (C.c_int, [C.POINTER(MoeShape), C.POINTER(Head), _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P]),
@@ -303,6 +306,21 @@ def new_grouped_workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
     if n == 0:
         raise Edge0Error(EDGE0_EINVAL, "edge0_grouped_workspace_bytes")
     return torch.zeros(int(n), dtype=torch.uint8, device=device)
+
+
+def new_prefill_workspace(shape: MoeShape, max_tokens: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace for edge0_moe_prefill calls of up to max_tokens."""
+    n = lib.edge0_prefill_workspace_bytes(C.byref(shape), max_tokens)
+    if n == 0:
+        raise Edge0Error(EDGE0_EINVAL, "edge0_prefill_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def edge0_moe_prefill(shape: MoeShape, pool: SlotPool, slot_table, n_tokens: int, ids, w, x, y,
+                      workspace, max_tokens: int, stream=None):
+    _check(lib.edge0_moe_prefill(C.byref(shape), C.byref(pool), _ptr(slot_table), n_tokens,
+                                 _ptr(ids), _ptr(w), _ptr(x), _ptr(y), _ptr(workspace), max_tokens,
+                                 _stream(stream)), "edge0_moe_prefill")
 
 
 def edge0_moe_grouped(shape: MoeShape, pool: SlotPool, slot_table, n_tokens: int, ids, w, x, y,
