@@ -19,12 +19,13 @@ step.  The same JSON line carries the other measurement rows under "rows":
          rotated order, medians
   d4     the grouped multi-token layer (K = 8) at 1, 4, 8, 16, 32 tokens per
          call on the rotated instances
+  prefill the whole-layer prefill call at 512, 2048 and 4096 tokens (K = 8)
 
 Every row has a roofline object and the oracle timed on this host's cores
 (1 thread and all threads) on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--no-cpu] [--rows all|none]
-  python bench.py --workload streamed|grouped|layer|tiny   (one row alone)
+  python bench.py --workload streamed|grouped|layer|tiny|prefill   (one row alone)
 """
 from __future__ import annotations
 
@@ -551,6 +552,93 @@ def row_grouped(args, log, inst):
     return out
 
 
+# ----------------------------------------------------------- f3: prefill
+def row_prefill(args, log, inst):
+    """Whole-layer prefill: one Qwen3-MoE-shaped layer (K = 8, Zipf(1.1)
+    routing) at 512, 2048 and 4096 tokens per call, rotated over the
+    instances; every expert of the layer is hit."""
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    S = inst.S.with_k(8)
+    sh = E.make_shape(S)
+    En, K, d, I, r = S.n_experts, S.top_k, S.d_model, S.d_inter, S.lora_rank
+    n_inst = inst.n_inst
+    bb = bundle_alg_bytes(S) + lora_alg_bytes(S)
+    Tmax = 4096
+    pws = E.new_prefill_workspace(sh, Tmax)
+    stream = torch.cuda.current_stream()
+    results = {}
+    for T in (512, 2048, 4096):
+        n_rot = 8  # routing/input sets, instance c % n_inst
+        routes = [G.grouped_routing(En, K, T, seed=args.seed * 1000 + 31 * T + i, layer=i)
+                  for i in range(n_rot)]
+        ids = [to_device(rt[0]) for rt in routes]
+        wts = [torch.from_numpy(rt[1]).cuda() for rt in routes]
+        xs = [to_device(G.hidden(S, 900 + T + i, n=T)) for i in range(n_rot)]
+        y = torch.empty((T, d), dtype=torch.int16, device="cuda")
+        union = float(np.mean([np.count_nonzero(np.bincount(rt[0].ravel(), minlength=En))
+                               for rt in routes]))
+
+        def run(n_calls):
+            for c in range(n_calls):
+                i, q = c % n_inst, c % n_rot
+                E.edge0_moe_prefill(sh, inst.pool.pool, inst.tables[i], T, ids[q], wts[q], xs[q],
+                                    y, pws, Tmax)
+        run(4)
+        torch.cuda.synchronize()
+        times = []
+        n_calls = 16 if T <= 512 else 8
+        for _ in range(5):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            run(n_calls)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            times.append(ev0.elapsed_time(ev1) * 1e3 / n_calls)
+        us = float(np.median(times))
+        nbytes = union * bb
+        flops = 2.0 * T * K * (3 * d * I + 2 * r * d + 2 * I * r + r * I + d * r)
+        results[T] = {"us_per_call": round(us, 1), "tok_s": round(T / (us * 1e-6), 1),
+                      "experts": round(union, 2), "expert_bytes": int(nbytes),
+                      "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                      "frac_of_bf16_mfma_peak": round(flops / (us * 1e-6) / 2.5e15, 4)}
+        log(f"[prefill] T={T}: {results[T]}")
+    assert E.edge0_workspace_error(pws) == 0
+    best = results[4096]
+    out = {"metric": "whole-layer prefill tok/s (one Qwen3-MoE-shaped layer, K=8)",
+           "value": best["tok_s"], "unit": "tok/s", "higher_is_better": True,
+           "config": {"workload": "one Qwen3-MoE-shaped layer, 512 / 2048 / 4096 tokens per call, "
+                                  f"K=8, Zipf(1.1) routing, {n_inst} rotated layer instances",
+                      "timing": "median of 5 runs"},
+           "roofline": {"kernel": "edge0_moe_prefill at 4096 tokens (bf16 MFMA token tiles)",
+                        "bound": "mfma", "achieved": best["tflops"], "peak": 2500.0,
+                        "unit": "TFLOP/s", "frac": round(best["tflops"] / 2500.0, 4),
+                        "traffic": None, "avg_launch_us": best["us_per_call"]},
+           "per_tokens": {str(k): v for k, v in results.items()}}
+    if not args.no_cpu:
+        import oracle as O
+        gen = G.StackGen(S, args.seed)
+        T = 4
+        idp, wp = G.grouped_routing(En, K, T, seed=5, layer=0)
+        xp = G.hidden(S, 906, n=T)
+        ex = {int(e): gen.expert(0, int(e)) for e in np.unique(idp)}
+        lo = {int(e): gen.lora(0, int(e)) for e in np.unique(idp)}
+
+        def unit():
+            t0 = time.perf_counter()
+            O.grouped_layer(ex, idp, wp.astype(np.float64), xp, S.group, lo,
+                            S.lora_alpha / S.lora_rank)
+            return time.perf_counter() - t0
+        s1, sn, thr, reps = oracle_timed(unit, 3.0)
+        out["cpu_baseline"] = cpu_record(T / s1, T / sn, "tok/s", thr,
+                                         f"{reps} calls of {T} tokens (K=8) per thread setting; "
+                                         "the oracle defines prefill token by token")
+    return out
+
+
 # ------------------------------------------------------------ D3: staged
 def h2d_bandwidth(host_mem, nbytes, n=128):
     """Pinned host -> device copy rate (GB/s) for n copies of nbytes each on
@@ -857,7 +945,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--rows", choices=["all", "none"], default="all",
                     help="all: the headline line also carries rows d0, d1_k4, d1_k8, d3, d4")
-    ap.add_argument("--workload", choices=["resident", "streamed", "grouped", "layer", "tiny"],
+    ap.add_argument("--workload", choices=["resident", "streamed", "grouped", "layer", "tiny",
+                                           "prefill"],
                     default="resident",
                     help="resident: the headline (40-layer stack, every bundle in HBM); the "
                          "others run one row alone: streamed (d3), grouped (d4), layer (d1), "
@@ -898,10 +987,10 @@ def main():
     if args.workload == "streamed":
         print(json.dumps(single_row_line(row_staged(args, log), args)), flush=True)
         return
-    if args.workload in ("grouped", "layer"):
+    if args.workload in ("grouped", "layer", "prefill"):
         inst = Instances(G.QWEN3_MOE, args.seed, log)
-        if args.workload == "grouped":
-            row = row_grouped(args, log, inst)
+        if args.workload in ("grouped", "prefill"):
+            row = (row_grouped if args.workload == "grouped" else row_prefill)(args, log, inst)
             print(json.dumps(single_row_line(row, args)), flush=True)
         else:
             for K in (4, 8):
@@ -922,6 +1011,7 @@ def main():
         rows["d1_k4"] = row_layer(args, log, inst, 4)
         rows["d1_k8"] = row_layer(args, log, inst, 8)
         rows["d4"] = row_grouped(args, log, inst)
+        rows["prefill"] = row_prefill(args, log, inst)
         del inst
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
