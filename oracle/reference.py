@@ -41,6 +41,7 @@ __all__ = [
     "softmax_topk", "softmax_at", "prerouter_feature", "prerouter_logits", "prerouter_commit",
     "rmsnorm", "stack_layer", "stack_step", "canonical_requests", "lru_replay",
     "grouped_layer", "topk_gap", "sigmoid_group_topk", "sigmoid_group_gaps", "NoSlotError",
+    "lora_delta", "requantize_affine", "merge_requant", "layer_retention",
 ]
 
 
@@ -477,3 +478,56 @@ def grouped_layer(experts, ids, w, x_bits, group: int, lora=None, scale: float =
     """y_j = sum_k w[j,k] FFN_{ids[j,k]}(x_j) for every token j."""
     return np.stack([moe_layer(experts, ids[j], w[j], x_bits[j], group, lora, scale)
                      for j in range(ids.shape[0])])
+
+
+# --------------------------------------------------------------------------
+# merging the LoRA into the int4 weights   [Edge0] §3.3 "Recovery LoRA:
+# Unmerged by Design" and its footnote 2 (weight-level retention)
+# --------------------------------------------------------------------------
+def lora_delta(A_bits, B_bits, scale: float) -> np.ndarray:
+    """delta = scale * B A  ([out][in], fp64), the LoRA's change of the weight."""
+    return scale * (bf16_to_f64(B_bits) @ bf16_to_f64(A_bits))
+
+
+def requantize_affine(W: np.ndarray, group: int):
+    """int4 affine quantisation of W [out][in] per group of `group` inputs
+    (reading: the plain min/max quantiser of the format, [Edge0] §2
+    "Quantization"): s = (max - min) / 15 and b = min, each rounded to bf16;
+    q = round((w - b) / s) to nearest (ties to even), clipped to 0..15; a
+    group whose s rounds to 0 keeps q = 0.  Returns (q, s bits, b bits)."""
+    W = np.asarray(W, dtype=np.float64)
+    out_dim, in_dim = W.shape
+    Wg = W.reshape(out_dim, in_dim // group, group)
+    lo, hi = Wg.min(axis=2), Wg.max(axis=2)
+    s_bits = f64_to_bf16_bits((hi - lo) / 15.0)
+    b_bits = f64_to_bf16_bits(lo)
+    s = bf16_to_f64(s_bits)[:, :, None]
+    b = bf16_to_f64(b_bits)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint((Wg - b) / np.where(s > 0, s, 1.0)), 0.0)
+    q = np.clip(q, 0, 15).astype(np.int64).reshape(out_dim, in_dim)
+    return q, s_bits, b_bits
+
+
+def merge_requant(words, s_bits, b_bits, A_bits, B_bits, scale: float, group: int):
+    """The merge the pages reject: W' = dequant(W) + delta, requantised to
+    int4.  Returns the requantised (q, s, b), the change that survived,
+    actual = dequant(W'') - dequant(W), and the weight-level retention
+    sum(actual * delta) / sum(delta^2) ([Edge0] §3.3, footnote 2)."""
+    W = dequant(words, s_bits, b_bits, group)
+    delta = lora_delta(A_bits, B_bits, scale)
+    q, s2, b2 = requantize_affine(W + delta, group)
+    g = group
+    Wr = (bf16_to_f64(s2).repeat(g, axis=1) * q + bf16_to_f64(b2).repeat(g, axis=1))
+    actual = Wr - W
+    den = float(np.sum(delta * delta))
+    return (q, s2, b2), actual, (float(np.sum(actual * delta)) / den if den > 0 else float("nan"))
+
+
+def layer_retention(y_unmerged, y_merged, y_base) -> float:
+    """Output-level retention 1 - |U - M| / |U - B| ([Edge0] §3.3, footnote
+    2, taken on a layer's output here rather than on the logits): U with
+    the unmerged LoRA, M on the merged and requantised weights, B on the
+    base weights alone."""
+    U, M, B = (np.asarray(v, dtype=np.float64) for v in (y_unmerged, y_merged, y_base))
+    return 1.0 - float(np.linalg.norm(U - M) / np.linalg.norm(U - B))
