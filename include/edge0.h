@@ -330,6 +330,25 @@ int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                       int32_t max_tokens, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Merge-and-requantise, the measurement behind keeping the LoRA unmerged
+ * ([Edge0] §3.3 "Recovery LoRA: Unmerged by Design" and its footnote 2).
+ * For each projection of one expert: W' = s q + b + (alpha/r) B A, then per
+ * group of g inputs s' = bf16((max - min) / 15), b' = bf16(min) (nearest,
+ * ties to even), q' = round((w' - b') / s') to nearest-even, clipped to
+ * 0..15 (0 where s' is 0); delta summed over the rank in fp32, in rank order.
+ *   src_bundle : device, one expert bundle of `shape` (with its LoRA)
+ *   dst_bundle : device, written in the LoRA-free layout of the same shape
+ *                (edge0_bundle_layout_of with lora_rank 0): the merged expert
+ *   stats_out  : device double [6]: sum(actual * delta), sum(delta^2) for
+ *                gate, up, down, actual = s' q' + b' - (s q + b); the weight
+ *                retention of a projection is the first over the second
+ *   workspace  : edge0_merge_workspace_bytes(shape) bytes (partial sums)
+ * The sums are reduced in a fixed order (the same bits every call). */
+size_t edge0_merge_workspace_bytes(const edge0_moe_shape* shape);
+int edge0_merge_requant(const edge0_moe_shape* shape, const void* src_bundle, void* dst_bundle,
+                        double* stats_out, void* workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
  * Decode stack: n_layers pre-norm residual MoE blocks (no attention),
  *   x_L = bf16(RMSNorm(h_L)),  RMSNorm(h) = h / sqrt(mean(h^2) + eps)
  *   routing_L = committed prediction (consumer layers, step > 0) or the

@@ -139,6 +139,8 @@ _SIG = {
     "edge0_workspace_error": (C.c_int, [_P, _P]),
     "edge0_route_commit": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P]),
     "edge0_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape), C.c_int32]),
+    "edge0_merge_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
+    "edge0_merge_requant": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P]),
     "edge0_moe_prefill": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, C.c_int32, _P,
                                     _P, _P, _P, _P, C.c_int32, _P]),
     "edge0_router": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -306,6 +308,19 @@ def new_grouped_workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
     if n == 0:
         raise Edge0Error(EDGE0_EINVAL, "edge0_grouped_workspace_bytes")
     return torch.zeros(int(n), dtype=torch.uint8, device=device)
+
+
+def edge0_merge_requant(shape: MoeShape, src_bundle, dst_bundle, stats_out, workspace=None,
+                        stream=None):
+    """Merges one expert's LoRA into its int4 weights (edge0_merge_requant);
+    stats_out: device float64 [6]."""
+    if workspace is None:
+        workspace = torch.empty(lib.edge0_merge_workspace_bytes(C.byref(shape)), dtype=torch.uint8,
+                                device="cuda")
+    _check(lib.edge0_merge_requant(C.byref(shape), _ptr(src_bundle), _ptr(dst_bundle),
+                                   _ptr(stats_out), _ptr(workspace), _stream(stream)),
+           "edge0_merge_requant")
+    return workspace
 
 
 def new_prefill_workspace(shape: MoeShape, max_tokens: int, device="cuda") -> torch.Tensor:
