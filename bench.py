@@ -20,12 +20,14 @@ step.  The same JSON line carries the other measurement rows under "rows":
   d4     the grouped multi-token layer (K = 8) at 1, 4, 8, 16, 32 tokens per
          call on the rotated instances
   prefill the whole-layer prefill call at 512, 2048 and 4096 tokens (K = 8)
+  merge  merge-and-requantise of one layer's experts: retention of the LoRA
+         delta in the weights and in the layer's outputs
 
 Every row has a roofline object and the oracle timed on this host's cores
 (1 thread and all threads) on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--no-cpu] [--rows all|none]
-  python bench.py --workload streamed|grouped|layer|tiny|prefill   (one row alone)
+  python bench.py --workload streamed|grouped|layer|tiny|prefill|merge   (one row alone)
 """
 from __future__ import annotations
 
@@ -639,6 +641,95 @@ def row_prefill(args, log, inst):
     return out
 
 
+# ------------------------------------------------------- f4: merge/requant
+def row_merge(args, log, inst):
+    """Merge-and-requantise every expert of one Qwen3-MoE-shaped layer: the
+    weight-level retention per projection over the layer, the output-level
+    retention 1 - |U - M| / |U - B| of layer calls on 64 tokens (U with the
+    unmerged LoRA, M on the merged experts, B on the base alone), and the
+    merge kernel's time."""
+    import torch
+    from synth import gen as G
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    S = inst.S
+    sh = E.make_shape(S)
+    sh0 = E.make_shape(S)
+    sh0.lora_rank = 0
+    En, d, I, g, r = S.n_experts, S.d_model, S.d_inter, S.group, S.lora_rank
+    bb0 = int(E.edge0_bundle_layout_of(sh0).bytes)
+    merged = torch.zeros(En * bb0, dtype=torch.uint8, device="cuda")
+    stats = torch.zeros((En, 6), dtype=torch.float64, device="cuda")
+    mws = torch.empty(E.lib.edge0_merge_workspace_bytes(E.C.byref(sh)), dtype=torch.uint8,
+                      device="cuda")
+    for e in range(4):  # warm
+        E.edge0_merge_requant(sh, inst.pool.slot_ptr(e), merged[e * bb0:(e + 1) * bb0], stats[e], mws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for e in range(En):  # layer instance 0
+        E.edge0_merge_requant(sh, inst.pool.slot_ptr(e), merged[e * bb0:(e + 1) * bb0], stats[e], mws)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / En
+    st = stats.cpu().numpy().sum(axis=0)
+    ret = {p: round(float(st[2 * i] / st[2 * i + 1]), 4) for i, p in enumerate(("gate", "up", "down"))}
+    # output level: 64 tokens through the layer three ways
+    ws = E.new_workspace(sh)
+    pool0 = E.SlotPool(merged.data_ptr(), bb0, En)
+    table = torch.arange(En, dtype=torch.int32, device="cuda")
+    U, M, B = [], [], []
+    rng = np.random.default_rng(args.seed + 41)
+    for i in range(64):
+        x = to_device(G.hidden(S, 5000 + i))
+        ids = torch.from_numpy(rng.choice(En, S.top_k, replace=False).astype(np.int32)).cuda()
+        wv = rng.uniform(0.1, 1.0, S.top_k)
+        w = torch.from_numpy((wv / wv.sum()).astype(np.float32)).cuda()
+        outs = []
+        for shp, pool in ((sh, inst.pool.pool), (sh0, pool0), (sh0, inst.pool.pool)):
+            y = torch.zeros(d, dtype=torch.int16, device="cuda")
+            E.edge0_moe_layer(shp, pool, table, ids, w, x, y, ws)
+            outs.append(y)
+        torch.cuda.synchronize()
+        for lst, y in zip((U, M, B), outs):
+            lst.append(y.cpu().numpy().view(np.uint16))
+    f = lambda a: (np.asarray(a, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    Uf, Mf, Bf = f(np.stack(U)), f(np.stack(M)), f(np.stack(B))
+    out_ret = 1.0 - float(np.linalg.norm(Uf - Mf) / np.linalg.norm(Uf - Bf))
+    # ALU work: per element of the three projections, the r-term delta twice
+    # (once for the group's range, once for the codes) and the requantisation
+    n_el = 3 * d * I
+    flops = n_el * (2 * 2 * r + 8)
+    log(f"[merge] {us:.1f} us per expert; weight retention {ret}; output retention {out_ret:.4f}")
+    out = {"metric": "merge-and-requantise: weight-level retention of the LoRA delta per projection",
+           "value": ret, "unit": "fraction of sum(delta^2)", "higher_is_better": True,
+           "config": {"workload": "every expert of one Qwen3-MoE-shaped layer (128), LoRA r=16 "
+                                  "alpha=32 merged into int4 group 64 and requantised",
+                      "output_retention_tokens": 64},
+           "output_retention": round(out_ret, 4),
+           "us_per_expert": round(us, 2),
+           "roofline": {"kernel": "k_merge_requant (one expert)", "bound": "alu",
+                        "achieved": round(flops / (us * 1e-6) / 1e12, 3), "peak": 157.3,
+                        "unit": "TFLOP/s", "frac": round(flops / (us * 1e-6) / 1e12 / 157.3, 4),
+                        "traffic": None, "avg_launch_us": round(us, 2),
+                        "note": "fp32 vector ALU count: 2 x (2r + 8) per weight element"}}
+    if not args.no_cpu:
+        import oracle as O
+        gen = G.StackGen(S, args.seed)
+        ex, lo = gen.expert(0, 0), gen.lora(0, 0)
+
+        def unit():
+            t0 = time.perf_counter()
+            for p in ("gate", "up", "down"):
+                O.merge_requant(ex[p + "_q"], ex[p + "_s"], ex[p + "_b"], lo["a_" + p],
+                                lo["b_" + p], S.lora_alpha / r, g)
+            return time.perf_counter() - t0
+        s1, sn, thr, reps = oracle_timed(unit, 3.0)
+        out["cpu_baseline"] = cpu_record(1e6 * s1, 1e6 * sn, "us/expert", thr,
+                                         f"{reps} experts merged by the oracle per thread setting")
+    return out
+
+
 # ------------------------------------------------------------ D3: staged
 def h2d_bandwidth(host_mem, nbytes, n=128):
     """Pinned host -> device copy rate (GB/s) for n copies of nbytes each on
@@ -946,7 +1037,7 @@ def main():
     ap.add_argument("--rows", choices=["all", "none"], default="all",
                     help="all: the headline line also carries rows d0, d1_k4, d1_k8, d3, d4")
     ap.add_argument("--workload", choices=["resident", "streamed", "grouped", "layer", "tiny",
-                                           "prefill"],
+                                           "prefill", "merge"],
                     default="resident",
                     help="resident: the headline (40-layer stack, every bundle in HBM); the "
                          "others run one row alone: streamed (d3), grouped (d4), layer (d1), "
@@ -987,10 +1078,11 @@ def main():
     if args.workload == "streamed":
         print(json.dumps(single_row_line(row_staged(args, log), args)), flush=True)
         return
-    if args.workload in ("grouped", "layer", "prefill"):
+    if args.workload in ("grouped", "layer", "prefill", "merge"):
         inst = Instances(G.QWEN3_MOE, args.seed, log)
-        if args.workload in ("grouped", "prefill"):
-            row = (row_grouped if args.workload == "grouped" else row_prefill)(args, log, inst)
+        if args.workload in ("grouped", "prefill", "merge"):
+            row = {"grouped": row_grouped, "prefill": row_prefill,
+                   "merge": row_merge}[args.workload](args, log, inst)
             print(json.dumps(single_row_line(row, args)), flush=True)
         else:
             for K in (4, 8):
@@ -1012,6 +1104,7 @@ def main():
         rows["d1_k8"] = row_layer(args, log, inst, 8)
         rows["d4"] = row_grouped(args, log, inst)
         rows["prefill"] = row_prefill(args, log, inst)
+        rows["merge"] = row_merge(args, log, inst)
         del inst
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

@@ -151,3 +151,58 @@ def test_merged_bundle_runs_in_the_layer(torch_cuda):
         torch.cuda.synchronize()
         y_o = O.moe_layer(merged, ids, w.astype(np.float64), x, S.group)
         assert rel_l2(O.bf16_to_f64(y.cpu().numpy().view(np.uint16)), y_o) <= REL_L2_MAX
+
+
+def test_output_retention_matches_oracle(torch_cuda):
+    """The output-level retention 1 - |U - M| / |U - B| of 32 tiny-layer
+    calls from the GPU's bf16 outputs (U with the LoRA, M on the merged
+    bundles, B on the base) against the oracle's fp64 value on the same
+    tokens; the bf16 rounding of the outputs allows 0.05."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    S = G.TINY
+    lay = DeviceLayer(S, seed=8, layer=1)
+    sh0 = E.make_shape(S)
+    sh0.lora_rank = 0
+    bb0 = int(E.edge0_bundle_layout_of(sh0).bytes)
+    pool_mem = torch.zeros(S.n_experts * bb0, dtype=torch.uint8, device="cuda")
+    stats = torch.zeros(6, dtype=torch.float64, device="cuda")
+    scale = S.lora_alpha / S.lora_rank
+    merged = {}
+    for e in range(S.n_experts):
+        E.edge0_merge_requant(lay.sh, lay.pool.slot_ptr(e), pool_mem[e * bb0:(e + 1) * bb0], stats)
+        m = {}
+        ex, lo = lay.experts[e], lay.loras[e]
+        for proj, n_in in (("gate", S.d_model), ("up", S.d_model), ("down", S.d_inter)):
+            (q, s2, b2), _, _ = O.merge_requant(ex[proj + "_q"], ex[proj + "_s"], ex[proj + "_b"],
+                                                lo["a_" + proj], lo["b_" + proj], scale, S.group)
+            qq = q.astype(np.uint32).reshape(q.shape[0], n_in // 8, 8) << (4 * np.arange(8, dtype=np.uint32))
+            m[proj + "_q"] = np.bitwise_or.reduce(qq, axis=2).astype(np.uint32)
+            m[proj + "_s"], m[proj + "_b"] = s2, b2
+        merged[e] = m
+    pool0 = E.SlotPool(pool_mem.data_ptr(), bb0, S.n_experts)
+    ws = E.new_workspace(lay.sh)
+    rng = np.random.default_rng(12)
+    gU, gM, gB, oU, oM, oB = ([] for _ in range(6))
+    for i in range(32):
+        xb = G.hidden(S, 400 + i)
+        ids = rng.choice(S.n_experts, S.top_k, replace=False).astype(np.int32)
+        w = np.full(S.top_k, 1.0 / S.top_k, np.float32)
+        outs = []
+        for shp, pool in ((lay.sh, lay.pool.pool), (sh0, pool0), (sh0, lay.pool.pool)):
+            y = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+            E.edge0_moe_layer(shp, pool, lay.table, torch.from_numpy(ids).cuda(),
+                              torch.from_numpy(w).cuda(), to_device(xb), y, ws)
+            outs.append(y)
+        torch.cuda.synchronize()
+        for lst, y in zip((gU, gM, gB), outs):
+            lst.append(O.bf16_to_f64(y.cpu().numpy().view(np.uint16)))
+        w64 = w.astype(np.float64)
+        oU.append(O.moe_layer(lay.experts, ids, w64, xb, S.group, lay.loras, scale))
+        oM.append(O.moe_layer(merged, ids, w64, xb, S.group))
+        oB.append(O.moe_layer(lay.experts, ids, w64, xb, S.group))
+    r_gpu = O.layer_retention(np.stack(gU), np.stack(gM), np.stack(gB))
+    r_or = O.layer_retention(np.stack(oU), np.stack(oM), np.stack(oB))
+    print(f"[merge] output retention: GPU {r_gpu:.4f}, oracle {r_or:.4f}")
+    assert abs(r_gpu - r_or) <= 0.05, (r_gpu, r_or)
