@@ -558,6 +558,50 @@ int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step, const int
  * set is in its slots (no event wait when it was staged on compute_stream
  * itself).  The slot table is written on the compute stream only. */
 int edge0_stager_wait(edge0_stager* sg, int32_t layer, int32_t step, hipStream_t compute_stream);
+/* -------------------------------------------------------------------------
+ * Expert files: the SSD tier under the pinned host pool ([Edge0] §3.1
+ * "Problem" and Figure 1: the weights live on the SSD, the page cache and the
+ * staged slots above them; the checkpoint is stacked per layer, so a layer's
+ * experts are direct reads).  One file per layer: a 4096-byte header (magic
+ * "E0LAYER1", version 1, the layer, the expert count, bundle and record
+ * bytes, the shape struct), then expert e's bundle in the device layout at
+ * offset 4096 + e * record_bytes, zero-padded to record_bytes (a multiple of
+ * 4096, so reads with O_DIRECT are aligned).
+ * ---------------------------------------------------------------------- */
+int64_t edge0_layer_file_record_bytes(const edge0_moe_shape* shape);
+/* Writes layer `layer`'s file from E bundles (host-readable pointers, the
+ * layout's bytes each).  EDGE0_EINVAL on an I/O error. */
+int edge0_layer_file_write(const char* path, const edge0_moe_shape* shape, int32_t layer,
+                           const void* const* bundles);
+
+/* The open files of n_layers layers (paths[L] is layer L's file; each header
+ * must name that layer and this shape), n_buffers pinned staging buffers of
+ * one record each (16..4096; at least the misses of one request) and
+ * n_threads I/O threads (1..64).  flags: EDGE0_FILE_DIRECT opens the files
+ * with O_DIRECT (reads bypass the page cache), else reads go through it.
+ * The handle must outlive every stager created on it. */
+#define EDGE0_FILE_DIRECT 1
+typedef struct edge0_filetier edge0_filetier;
+typedef struct {
+  int64_t reads;    /* records read */
+  int64_t bytes;    /* bytes read */
+  int64_t read_ns;  /* host time in read batches */
+} edge0_file_stats;
+int edge0_filetier_create(edge0_filetier** out, const edge0_moe_shape* shape, int32_t n_layers,
+                          const char* const* paths, int32_t n_buffers, int32_t n_threads,
+                          int32_t flags);
+int edge0_filetier_stats(const edge0_filetier* ft, edge0_file_stats* out);
+void edge0_filetier_destroy(edge0_filetier* ft);
+/* A stager whose misses come from the layer files: a request's misses are
+ * read in parallel (blocking the calling thread) into staging buffers, then
+ * copied into their slots on the request's stream as edge0_stage_experts
+ * copies host bundles (fill kernel or DMA); a staging buffer is reused once
+ * the copy that last read it has completed.  Everything else is as
+ * edge0_stager_create. */
+int edge0_stager_create_files(edge0_stager** out, const edge0_moe_shape* shape,
+                              const edge0_slot_pool* pool, int32_t n_layers,
+                              edge0_filetier* files, int32_t* slot_table);
+
 /* Applies the pending slot-table updates on compute_stream (the table then
  * maps every resident key once the stream reaches this point). */
 int edge0_stager_flush(edge0_stager* sg, hipStream_t compute_stream);

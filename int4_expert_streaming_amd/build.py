@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libedge0.so")
-SOURCES = ["api.hip", "route.hip", "moe.hip", "stack.hip", "flow.hip", "xstep.hip", "grouped.hip", "stager.hip", "merge.hip"]
+SOURCES = ["api.hip", "route.hip", "moe.hip", "stack.hip", "flow.hip", "xstep.hip", "grouped.hip", "stager.hip", "merge.hip", "filetier.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     # no packed-fp32 instructions in generated code

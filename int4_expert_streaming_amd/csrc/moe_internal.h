@@ -136,6 +136,12 @@ struct HeadBatch {
 };
 int launch_heads(const HeadBatch& hb, hipStream_t stream);
 
+// the file tier, for the stager
+int filetier_read(edge0_filetier* ft, const int32_t* keys, int n, const void** dev_out,
+                  int* buf_out);
+int filetier_mark(edge0_filetier* ft, const int* bufs, int n, hipStream_t stream);
+bool filetier_matches(const edge0_filetier* ft, const edge0_moe_shape& s, int n_layers);
+
 // what the stack runtime needs to know of a stager
 edge0_slot_pool stager_pool(const edge0_stager* sg);
 const int32_t* stager_table(const edge0_stager* sg);

@@ -232,6 +232,7 @@ struct edge0_stager {
   edge0_slot_pool pool;
   int64_t bundle_bytes = 0;
   std::vector<const void*> host;  // [L * E] device addresses of the pinned host bundles
+  edge0_filetier* files = nullptr;  // or: misses are read from the layer files
   int32_t* table = nullptr;
   EventRing ready;  // recorded after each request's copies, on its stream
   EventRing rel;    // recorded at each release, on the compute stream
@@ -362,6 +363,41 @@ extern "C" int edge0_stager_create(edge0_stager** out, const edge0_moe_shape* sh
   return EDGE0_OK;
 }
 
+extern "C" int edge0_stager_create_files(edge0_stager** out, const edge0_moe_shape* shape,
+                                         const edge0_slot_pool* pool, int32_t n_layers,
+                                         edge0_filetier* files, int32_t* slot_table) {
+  if (!out || !shape || !shape_ok(shape) || !pool || !pool->base || pool->n_slots < 1 || !files ||
+      !slot_table || n_layers < 1 || !filetier_matches(files, *shape, n_layers))
+    return EDGE0_EINVAL;
+  edge0_bundle_layout lay;
+  if (bundle_layout(shape, &lay) != EDGE0_OK) return EDGE0_EINVAL;
+  if (pool->slot_bytes < lay.bytes || pool->slot_bytes % 256 != 0) return EDGE0_EINVAL;
+  edge0_stager* sg = new (std::nothrow) edge0_stager();
+  if (!sg) return EDGE0_ENOMEM;
+  int rc = sg->lru.init(pool->n_slots, n_layers, shape->n_experts);
+  if (rc != EDGE0_OK) {
+    delete sg;
+    return rc;
+  }
+  sg->shape = *shape;
+  sg->pool = *pool;
+  sg->bundle_bytes = lay.bytes;
+  sg->files = files;
+  sg->table = slot_table;
+  sg->fill_q.assign(pool->n_slots, 0);
+  sg->rel_q.assign(pool->n_slots, 0);
+  const bool ok = sg->ready.init(kRing) && sg->rel.init(kRing) &&
+                  hipMemset(slot_table, 0xFF, (size_t)n_layers * shape->n_experts * 4) ==
+                      hipSuccess &&
+                  hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    edge0_stager_destroy(sg);
+    return EDGE0_EHIP;
+  }
+  *out = sg;
+  return EDGE0_OK;
+}
+
 extern "C" int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step,
                                    const int32_t* ids, int32_t n, int32_t* slots_out,
                                    hipStream_t stream) {
@@ -389,12 +425,24 @@ extern "C" int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step
   for (int j = 0; j < n_waits; ++j)
     if (hipStreamWaitEvent(stream, waits[j], 0) != hipSuccess) return EDGE0_EHIP;
   uint8_t* base = static_cast<uint8_t*>(sg->pool.base);
+  // file tier: the misses' records read into staging buffers first
+  const void* staged_src[16];
+  int staged_buf[16];
+  int n_miss = 0;
+  if (sg->files) {
+    int32_t miss_keys[16];
+    for (int i = 0; i < n; ++i)
+      if (!hit[i]) miss_keys[n_miss++] = keys[i];
+    if (n_miss > 0 && (rc = filetier_read(sg->files, miss_keys, n_miss, staged_src, staged_buf)) !=
+                          EDGE0_OK)
+      return rc;
+  }
   CopyList cl{};
   int n_copy = 0;
   for (int i = 0; i < n; ++i) {
     if (hit[i]) continue;
     const int s = slots[i];
-    cl.src[n_copy] = static_cast<const uint4*>(sg->host[keys[i]]);
+    cl.src[n_copy] = static_cast<const uint4*>(sg->files ? staged_src[n_copy] : sg->host[keys[i]]);
     cl.dst[n_copy++] = reinterpret_cast<uint4*>(base + (size_t)s * sg->pool.slot_bytes);
     sg->lru.stats.bytes_staged += sg->bundle_bytes;
     if (evicted[i] >= 0) sg->patches.emplace_back(evicted[i], -1);
@@ -408,6 +456,8 @@ extern "C" int edge0_stage_experts(edge0_stager* sg, int32_t layer, int32_t step
     if (hipMemcpyAsync(cl.dst[i], cl.src[i], (size_t)sg->bundle_bytes, hipMemcpyHostToDevice,
                        stream) != hipSuccess)
       return EDGE0_EHIP;
+  if (sg->files && n_miss > 0 && (rc = filetier_mark(sg->files, staged_buf, n_miss, stream)) != EDGE0_OK)
+    return rc;
   const uint64_t q = sg->ready.record(stream);
   if (q == 0) return EDGE0_EHIP;
   for (int i = 0; i < n; ++i)

@@ -174,6 +174,15 @@ _SIG = {
     "edge0_lru_destroy": (None, [_P]),
     "edge0_stager_create": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.POINTER(SlotPool),
                                       C.c_int32, C.POINTER(_P), _P]),
+    "edge0_stager_create_files": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape),
+                                            C.POINTER(SlotPool), C.c_int32, _P, _P]),
+    "edge0_layer_file_record_bytes": (C.c_int64, [C.POINTER(MoeShape)]),
+    "edge0_layer_file_write": (C.c_int, [C.c_char_p, C.POINTER(MoeShape), C.c_int32,
+                                         C.POINTER(_P)]),
+    "edge0_filetier_create": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.c_int32,
+                                        C.POINTER(C.c_char_p), C.c_int32, C.c_int32, C.c_int32]),
+    "edge0_filetier_stats": (C.c_int, [_P, _P]),
+    "edge0_filetier_destroy": (None, [_P]),
     "edge0_stage_experts": (C.c_int, [_P, C.c_int32, C.c_int32, _I32P, C.c_int32, _I32P, _P]),
     "edge0_stager_wait": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
     "edge0_stager_release": (C.c_int, [_P, C.c_int32, C.c_int32, _P]),
@@ -457,15 +466,61 @@ class Lru(_Handle):
 
 
 
-class Stager(_Handle):
-    """Owner of an edge0_stager handle: the LRU pool plus host-to-device staging."""
+EDGE0_FILE_DIRECT = 1
 
-    def __init__(self, shape: MoeShape, pool: SlotPool, n_layers: int, host_ptrs, slot_table):
-        self._keep = (host_ptrs, slot_table)
-        arr = (C.c_void_p * len(host_ptrs))(*host_ptrs)
+
+class FileStats(C.Structure):
+    _fields_ = [("reads", C.c_int64), ("bytes", C.c_int64), ("read_ns", C.c_int64)]
+
+
+def layer_file_write(path: str, shape: MoeShape, layer: int, bundle_ptrs):
+    """Writes one layer's expert file from E host-readable bundle pointers."""
+    arr = (C.c_void_p * len(bundle_ptrs))(*bundle_ptrs)
+    _check(lib.edge0_layer_file_write(path.encode(), C.byref(shape), layer, arr),
+           "edge0_layer_file_write")
+
+
+class FileTier(_Handle):
+    """Owner of an edge0_filetier handle: the open layer files, pinned staging
+    buffers and I/O threads."""
+
+    def __init__(self, shape: MoeShape, paths, n_buffers: int = 64, n_threads: int = 8,
+                 direct: bool = True):
+        self.shape = shape
+        arr = (C.c_char_p * len(paths))(*[p.encode() for p in paths])
         self._handle = C.c_void_p()
-        _check(lib.edge0_stager_create(C.byref(self._handle), C.byref(shape), C.byref(pool),
-                                       n_layers, arr, _ptr(slot_table)), "edge0_stager_create")
+        _check(lib.edge0_filetier_create(C.byref(self._handle), C.byref(shape), len(paths), arr,
+                                         n_buffers, n_threads, EDGE0_FILE_DIRECT if direct else 0),
+               "edge0_filetier_create")
+        self._register()
+
+    def stats(self) -> dict:
+        s = FileStats()
+        _check(lib.edge0_filetier_stats(self._handle, C.byref(s)), "edge0_filetier_stats")
+        return {k: int(getattr(s, k)) for k, _ in FileStats._fields_}
+
+    def close(self):
+        if self._handle:
+            lib.edge0_filetier_destroy(self._handle)
+            self._handle = C.c_void_p()
+
+
+class Stager(_Handle):
+    """Owner of an edge0_stager handle: the LRU pool plus host-to-device
+    staging, from pinned host bundles (host_ptrs) or from a FileTier."""
+
+    def __init__(self, shape: MoeShape, pool: SlotPool, n_layers: int, host_ptrs, slot_table,
+                 files: "FileTier | None" = None):
+        self._keep = (host_ptrs, slot_table, files)
+        self._handle = C.c_void_p()
+        if files is not None:
+            _check(lib.edge0_stager_create_files(C.byref(self._handle), C.byref(shape),
+                                                 C.byref(pool), n_layers, files._handle,
+                                                 _ptr(slot_table)), "edge0_stager_create_files")
+        else:
+            arr = (C.c_void_p * len(host_ptrs))(*host_ptrs)
+            _check(lib.edge0_stager_create(C.byref(self._handle), C.byref(shape), C.byref(pool),
+                                           n_layers, arr, _ptr(slot_table)), "edge0_stager_create")
         self._register()
 
     def stage(self, layer: int, step: int, ids, stream=None) -> np.ndarray:

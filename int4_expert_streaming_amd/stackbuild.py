@@ -99,6 +99,23 @@ class HostBundles:
         return self.mem[k * self.bundle_bytes:(k + 1) * self.bundle_bytes]
 
 
+def write_layer_files(host: "HostBundles", directory: str, n_experts: int, log=None):
+    """Writes every layer of the host tier to its expert file under
+    `directory` (layer_NNN.e0l); returns the paths in layer order."""
+    import os
+    os.makedirs(directory, exist_ok=True)
+    n_layers = len(host.ptrs) // n_experts
+    paths = []
+    t0 = time.time()
+    for L in range(n_layers):
+        path = os.path.join(directory, f"layer_{L:03d}.e0l")
+        E.layer_file_write(path, host.sh, L, host.ptrs[L * n_experts:(L + 1) * n_experts])
+        paths.append(path)
+    if log:
+        log(f"[files] {n_layers} layer files written to {directory} ({time.time() - t0:.1f}s)")
+    return paths
+
+
 def device_routers_heads(gen, n_layers, owners, threads=16):
     """Device copies of every layer's router and of the owner layers' heads
     (None elsewhere)."""
@@ -114,7 +131,7 @@ class StreamedStack:
     pinned host bundles by the library's stager, routed by a given trace."""
 
     def __init__(self, shape, gen, n_layers, owners, consumers, n_slots, eps=1e-6, threads=16,
-                 log=print, host=None, routers=None, heads=None):
+                 log=print, host=None, routers=None, heads=None, files=None):
         self.S = shape
         self.sh = E.make_shape(shape)
         En = shape.n_experts
@@ -122,7 +139,10 @@ class StreamedStack:
         self.spec = E.StackSpec(n_layers, owners[0], owners[1], consumers[0], consumers[1], eps)
         self.owners = range(owners[0], owners[1] + 1)
         self.consumers = range(consumers[0], consumers[1] + 1)
-        self.host = host if host is not None else HostBundles(shape, gen, n_layers, threads, log)
+        # bundles come from the pinned host tier, or from a FileTier's layer files
+        self.files = files
+        self.host = host if (host is not None or files is not None) else \
+            HostBundles(shape, gen, n_layers, threads, log)
         self.pool = SlotPoolBuffer(self.sh, n_slots)
         self.table = torch.full((n_layers, En), -1, dtype=torch.int32, device="cuda")
         if routers is None or heads is None:  # device copies, or built here
@@ -131,7 +151,8 @@ class StreamedStack:
         torch.cuda.synchronize()
         self.stack = E.Stack(self.sh, self.spec, self.pool.pool, self.table, self.routers,
                              self.heads)
-        self.stager = E.Stager(self.sh, self.pool.pool, n_layers, self.host.ptrs, self.table)
+        self.stager = E.Stager(self.sh, self.pool.pool, n_layers,
+                               None if files is not None else self.host.ptrs, self.table, files)
         self.copy_stream = torch.cuda.Stream()
 
     def step(self, h0, h_out, step, ids_dev, ids_host, next_ids_host, ahead=True):

@@ -42,14 +42,29 @@ def _resident(events, ids_of, n_slots, n_layers, n_experts):
     return table, tot
 
 
+def _streamed_stack(S, gen, n_layers, owners, consumers, n_slots, source, tmp_dir):
+    """The staged stack with its misses from pinned host bundles (source
+    "host") or from layer files written from them, read with O_DIRECT
+    ("file_direct") or through the page cache ("file_cached")."""
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import HostBundles, StreamedStack, write_layer_files
+    if source == "host":
+        return StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
+    host = HostBundles(S, gen, n_layers, log=None)
+    paths = write_layer_files(host, str(tmp_dir), S.n_experts)
+    ft = E.FileTier(E.make_shape(S), paths, n_buffers=32, n_threads=4,
+                    direct=source == "file_direct")
+    return StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None, host=host,
+                         files=ft)
+
+
 def _run(S, seed, n_layers, owners, consumers, n_slots, steps, ahead, layers_of, keep_p=0.1,
-         copy_mode=0, free_bias=False):
+         copy_mode=0, free_bias=False, source="host", tmp_dir=None):
     import torch
-    from int4_expert_streaming_amd.stackbuild import StreamedStack
     from int4_expert_streaming_amd.weights import to_device
     gen = G.StackGen(S, seed, free_bias=free_bias)
     En, K = S.n_experts, S.top_k
-    ss = StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
+    ss = _streamed_stack(S, gen, n_layers, owners, consumers, n_slots, source, tmp_dir)
     ss.stager.set_copy_mode(copy_mode)
     trace = G.zipf_trace(En, K, n_layers, steps + 1, seed + 100, keep_p=keep_p)
     trace_dev = torch.from_numpy(trace).cuda()
@@ -161,7 +176,7 @@ def test_stager_rejects_pageable_host_memory(torch_cuda):
     sg.close()
 
 
-def _run_loop(S, seed, n_layers, owners, consumers, n_slots, steps):
+def _run_loop(S, seed, n_layers, owners, consumers, n_slots, steps, source="host", tmp_dir=None):
     """The closed loop (EDGE0_STAGE_LOOP): no trace; router layers commit
     their own top-K, prediction-routed layers execute what their owner's
     head committed one step earlier, and those predictions are what the
@@ -172,12 +187,11 @@ def _run_loop(S, seed, n_layers, owners, consumers, n_slots, steps):
     predicted sets; every layer teacher-forced."""
     import torch
     from int4_expert_streaming_amd import edge0 as E
-    from int4_expert_streaming_amd.stackbuild import StreamedStack
     from int4_expert_streaming_amd.weights import to_device
     from tests.layer_setup import check_routing
     gen = G.StackGen(S, seed)
     En, K = S.n_experts, S.top_k
-    ss = StreamedStack(S, gen, n_layers, owners, consumers, n_slots, log=None)
+    ss = _streamed_stack(S, gen, n_layers, owners, consumers, n_slots, source, tmp_dir)
     own = range(owners[0], owners[1] + 1)
     con = range(consumers[0], consumers[1] + 1)
     h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
@@ -248,3 +262,29 @@ def test_qwen3moe_streamed_stack_closed_loop(torch_cuda):
     from the device (router layers' own top-K, the heads' predictions)."""
     ss = _run_loop(G.QWEN3_MOE, 2, 12, (2, 9), (3, 10), 64, 4)
     print(f"[streamed] qwen3moe loop: {ss.stager.stats()}")
+
+
+@pytest.mark.parametrize("source,ahead,copy_mode", [("file_direct", True, 0),
+                                                    ("file_direct", False, 1),
+                                                    ("file_cached", True, 1)])
+def test_small_streamed_stack_from_files(torch_cuda, tmp_path, source, ahead, copy_mode):
+    """The tiny staged stack with every miss read from the layer files (with
+    O_DIRECT or through the page cache) into pinned staging buffers, then
+    copied by the fill kernel or DMA: the same checks as from host memory."""
+    ss, worst = _run(G.TINY, 5, 10, (2, 7), (3, 8), 40, 6, ahead, lambda t: range(10),
+                     copy_mode=copy_mode, source=source, tmp_dir=tmp_path)
+    st = ss.files.stats()
+    assert st["reads"] == ss.stager.stats()["misses"] and st["bytes"] > 0
+    print(f"[streamed] tiny from files ({source}) ahead={ahead}: worst rel-L2 {worst:.3e}, {st}")
+
+
+@pytest.mark.timeout(900)
+def test_qwen3moe_streamed_from_files_and_loop(torch_cuda, tmp_path):
+    """12 Qwen3-MoE-shaped layers over a 64-slot pool from O_DIRECT layer
+    files: the trace arm for 4 steps, then the closed loop for 3."""
+    ss, worst = _run(G.QWEN3_MOE, 1, 12, (2, 9), (3, 10), 64, 4, True, lambda t: range(12),
+                     keep_p=0.06, source="file_direct", tmp_dir=tmp_path / "a")
+    assert ss.stager.stats()["evictions"] > 0
+    ss = _run_loop(G.QWEN3_MOE, 2, 12, (2, 9), (3, 10), 64, 3, source="file_direct",
+                   tmp_dir=tmp_path / "b")
+    print(f"[streamed] qwen3moe from files: worst rel-L2 {worst:.3e}, {ss.files.stats()}")
