@@ -22,12 +22,14 @@ step.  The same JSON line carries the other measurement rows under "rows":
   prefill the whole-layer prefill call at 512, 2048 and 4096 tokens (K = 8)
   merge  merge-and-requantise of one layer's experts: retention of the LoRA
          delta in the weights and in the layer's outputs
+  files  the d3 stack with the pool filled from per-layer expert files on
+         disk (O_DIRECT, and the page cache), the raw read rate as roofline
 
 Every row has a roofline object and the oracle timed on this host's cores
 (1 thread and all threads) on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--no-cpu] [--rows all|none]
-  python bench.py --workload streamed|grouped|layer|tiny|prefill|merge   (one row alone)
+  python bench.py --workload streamed|files|grouped|layer|tiny|prefill|merge   (one row alone)
 """
 from __future__ import annotations
 
@@ -907,6 +909,10 @@ def row_staged(args, log, rounds=5, warmup=16, steps=64):
                         "peak": round(bw, 2), "unit": "GB/s", "frac": round(achieved / bw, 4),
                         "traffic": None},
            "arms": arms}
+    if args.rows_files:
+        out_files = row_files(args, log, S, gen, host, routers, heads, trace, trace_dev, h0, h_out)
+    else:
+        out_files = None
     if not args.no_cpu:
         import oracle as O
         own, con = range(OWNERS[0], OWNERS[1] + 1), range(CONSUMERS[0], CONSUMERS[1] + 1)
@@ -918,7 +924,131 @@ def row_staged(args, log, rounds=5, warmup=16, steps=64):
                                          f"the oracle LRU replay of {total} steps of the trace "
                                          "(single-threaded Python)")
     del host
-    return out
+    return out, out_files
+
+
+def direct_read_gbps(paths, record_bytes, n_threads=16, seconds=3.0):
+    """Raw O_DIRECT read rate of the layer files (GB/s): n_threads threads
+    reading whole records chosen uniformly at random over every file (the
+    widest access pattern; the arms re-read Zipf-hot records), the disk
+    tier's roofline."""
+    import mmap
+    import threading
+    fds = [os.open(p, os.O_RDONLY | os.O_DIRECT) for p in paths]
+    n_rec = (os.fstat(fds[0]).st_size - 4096) // record_bytes
+    done = [0] * n_threads
+    stop = time.time() + seconds
+
+    def work(i):
+        buf = mmap.mmap(-1, record_bytes)
+        rng = np.random.default_rng(i)
+        while time.time() < stop:
+            fd = fds[int(rng.integers(len(fds)))]
+            os.preadv(fd, [buf], 4096 + int(rng.integers(n_rec)) * record_bytes)
+            done[i] += record_bytes
+    t0 = time.time()
+    th = [threading.Thread(target=work, args=(i,)) for i in range(n_threads)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    for fd in fds:
+        os.close(fd)
+    return sum(done) / (time.time() - t0) / 1e9
+
+
+FILE_ARMS = ("ahead_file", "demand_file", "loop_file", "ahead_pagecache")
+
+
+def row_files(args, log, S, gen, host, routers, heads, trace, trace_dev, h0, h_out, rounds=2,
+              warmup=8, steps=24):
+    """The staged stack with the 3 GiB pool filled from per-layer expert files
+    on the box's disk (the SSD tier under the pinned host pool): the
+    prediction arm, the on-demand arm and the closed loop reading with
+    O_DIRECT, and the prediction arm through the page cache (warm), rotated
+    over `rounds` rounds; the raw O_DIRECT read rate is the roofline."""
+    import shutil
+    import tempfile
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import StreamedStack, write_layer_files
+    d = tempfile.mkdtemp(prefix="e0_layers_", dir=os.environ.get("EDGE0_FILE_DIR", "/tmp"))
+    try:
+        paths = write_layer_files(host, d, S.n_experts, log=log)
+        sh = E.make_shape(S)
+        rec = int(E.lib.edge0_layer_file_record_bytes(E.C.byref(sh)))
+        ssd = direct_read_gbps(paths, rec)
+        n_slots = (3 << 30) // host.bundle_bytes
+        log(f"[files] O_DIRECT read rate {ssd:.2f} GB/s ({rec}-byte records, random, 16 threads)")
+        per_arm = {a: [] for a in FILE_ARMS}
+        total = warmup + steps
+        for rnd in range(rounds):
+            k = rnd % len(FILE_ARMS)
+            for arm in FILE_ARMS[k:] + FILE_ARMS[:k]:
+                ft = E.FileTier(sh, paths, n_buffers=64, n_threads=8,
+                                direct=not arm.endswith("pagecache"))
+                ss = StreamedStack(S, gen, N_LAYERS, OWNERS, CONSUMERS, n_slots, log=None,
+                                   host=host, routers=routers, heads=heads, files=ft)
+                mode = E.EDGE0_STAGE_LOOP if arm.startswith("loop") else arm.startswith("ahead")
+
+                def step(t):
+                    if arm.startswith("loop"):
+                        E.stack_step_staged(ss.stack, ss.stager, h0[t], h_out, t, None, None, None,
+                                            mode, ss.copy_stream)
+                    else:
+                        ss.step(h0[t], h_out, t, trace_dev[t], trace[t], trace[t + 1], mode)
+                for t in range(warmup):
+                    step(t)
+                torch.cuda.synchronize()
+                st0, f0 = ss.stager.stats(), ft.stats()
+                t0 = time.perf_counter()
+                for t in range(warmup, total):
+                    step(t)
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) * 1e3 / steps
+                st1, f1 = ss.stager.stats(), ft.stats()
+                dd = {k_: st1[k_] - st0[k_] for k_ in st1}
+                fb, fns = f1["bytes"] - f0["bytes"], f1["read_ns"] - f0["read_ns"]
+                per_arm[arm].append({"ms_per_step": ms,
+                                     "hit_rate": dd["hits"] / max(1, dd["touches"]),
+                                     "misses_per_step": dd["misses"] / steps,
+                                     "file_bytes_per_step": fb / steps,
+                                     "read_gbps": fb / max(1, fns)})
+                del ss
+                ft.close()
+                torch.cuda.synchronize()
+            log(f"[files] round {rnd}: " + ", ".join(f"{a} {per_arm[a][-1]['ms_per_step']:.1f} ms"
+                                                      for a in FILE_ARMS))
+        arms = {}
+        for a, recs in per_arm.items():
+            med = {k_: float(np.median([r[k_] for r in recs])) for k_ in recs[0]}
+            arms[a] = {"ms_per_step": round(med["ms_per_step"], 3),
+                       "tok_s": round(1000.0 / med["ms_per_step"], 2),
+                       "rounds_ms": [round(r["ms_per_step"], 3) for r in recs],
+                       "hit_rate": round(med["hit_rate"], 4),
+                       "misses_per_step": round(med["misses_per_step"], 2),
+                       "file_bytes_per_step": int(med["file_bytes_per_step"]),
+                       "read_gbps_in_batches": round(med["read_gbps"], 2),
+                       "ssd_ceiling_tok_s": round(ssd * 1e9 / max(1.0, med["file_bytes_per_step"]), 2)}
+        a = arms["ahead_file"]
+        achieved = a["file_bytes_per_step"] / (a["ms_per_step"] * 1e-3) / 1e9
+        return {"metric": "staged decode tok/s from expert files (batch 1, 40-layer MoE stack, "
+                          "3 GiB HBM pool, O_DIRECT)",
+                "value": a["tok_s"], "unit": "tok/s", "higher_is_better": True,
+                "config": {"workload": "40-layer Qwen3-MoE-shaped decode stack, experts read from "
+                                       "per-layer files on the box's disk into a 3 GiB HBM pool",
+                           "trace": "as the staged row (Zipf(1.1), overlap 0.25)",
+                           "timing": f"{rounds} rounds, arm order rotated, {warmup} warmup + "
+                                     f"{steps} timed steps per arm and round, host wall clock, "
+                                     "medians",
+                           "file_dir_fs": "ext4 virtio disk of the box (df of the directory)"},
+                "direct_read_gbps": round(ssd, 2),
+                "roofline": {"kernel": "disk reads (prediction arm's file bytes per step)",
+                             "bound": "ssd", "achieved": round(achieved, 2), "peak": round(ssd, 2),
+                             "unit": "GB/s", "frac": round(achieved / ssd, 4), "traffic": None},
+                "arms": arms}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
 
 
 # ------------------------------------------------------------ D2: stack
@@ -1037,7 +1167,7 @@ def main():
     ap.add_argument("--rows", choices=["all", "none"], default="all",
                     help="all: the headline line also carries rows d0, d1_k4, d1_k8, d3, d4")
     ap.add_argument("--workload", choices=["resident", "streamed", "grouped", "layer", "tiny",
-                                           "prefill", "merge"],
+                                           "prefill", "merge", "files"],
                     default="resident",
                     help="resident: the headline (40-layer stack, every bundle in HBM); the "
                          "others run one row alone: streamed (d3), grouped (d4), layer (d1), "
@@ -1053,7 +1183,11 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (hardware counter "
                          "calibration: known bytes moved) and exit")
+    ap.add_argument("--no-files", action="store_true",
+                    help="skip the expert-file row (writes 15 GB of layer files to EDGE0_FILE_DIR, "
+                         "default /tmp)")
     args = ap.parse_args()
+    args.rows_files = (not args.no_files) or args.workload == "files"
     if args.copy_calibration:
         import torch
         n = args.copy_calibration << 20
@@ -1075,8 +1209,10 @@ def main():
     import torch
     torch.cuda.set_device(0)
     from synth import gen as G
-    if args.workload == "streamed":
-        print(json.dumps(single_row_line(row_staged(args, log), args)), flush=True)
+    if args.workload in ("streamed", "files"):
+        d3, files_row = row_staged(args, log)
+        print(json.dumps(single_row_line(d3 if args.workload == "streamed" else files_row, args)),
+              flush=True)
         return
     if args.workload in ("grouped", "layer", "prefill", "merge"):
         inst = Instances(G.QWEN3_MOE, args.seed, log)
@@ -1108,7 +1244,9 @@ def main():
         del inst
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        rows["d3"] = row_staged(args, log)
+        rows["d3"], files_row = row_staged(args, log)
+        if files_row is not None:
+            rows["files"] = files_row
         out["rows"] = rows
         log(f"[bench] rows measured in {time.time() - t0:.0f}s")
     print(json.dumps(out), flush=True)
