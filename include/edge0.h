@@ -303,6 +303,27 @@ int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                       hipStream_t stream);
 
 /* -------------------------------------------------------------------------
+ * The same layer with the recovery LoRA given apart from the bundles
+ * ([Edge0] §3.3: the adapters ship as files beside the base weights, so a
+ * new adapter generation swaps files, not bundles).  Six bf16 factors per
+ * expert, row-major as in the bundle (a_gate [r][d], b_gate [I][r], a_up
+ * [r][d], b_up [I][r], a_down [r][I], b_down [d][r]); each pointer is expert
+ * 0's factor and expert e's is expert_stride * e elements further on.
+ * expert_stride = 0: one adapter shared by every expert.  The slot pool may
+ * then hold bundles in the LoRA-free layout (edge0_bundle_layout_of with
+ * lora_rank 0; the int4 arrays are at the same offsets either way).
+ * Results are those of edge0_moe_layer with the same adapters in the
+ * bundles, bit for bit.  lora may be NULL when lora_rank == 0. */
+typedef struct {
+  const void *a_gate, *b_gate, *a_up, *b_up, *a_down, *b_down;  /* device, bf16 */
+  int64_t expert_stride;                                        /* elements */
+} edge0_lora;
+int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                         const edge0_lora* lora, const int32_t* slot_table, const int32_t* ids,
+                         const float* w, const void* x, void* y, void* workspace,
+                         hipStream_t stream);
+
+/* -------------------------------------------------------------------------
  * Whole-layer prefill ([Edge0] §3.1 "Executor paths", whole-layer; §3.2
  * "Two consumption profiles": prefill takes every expert of a layer, and
  * there is nothing to predict).  The result is edge0_moe_grouped's, token by

@@ -48,7 +48,7 @@ struct GuW {
 // issued in order (not their values) passes the index of another wave
 template <int NJ, int RR = kWideRowsPerWave>
 __device__ __forceinline__ void gu_load(const MoeArgs& a, const uint8_t* b, int i0,
-                                        GuW<NJ, RR>& w, int wave = tid_here() >> 6) {
+                                        GuW<NJ, RR>& w, int wave = tid_here() >> 6, int k = 0) {
   constexpr int R = RR;
   const int lane = tid_here() & 63;
   const int d = a.d, g = a.g, ng = d / g, r = a.r;
@@ -78,8 +78,8 @@ __device__ __forceinline__ void gu_load(const MoeArgs& a, const uint8_t* b, int 
   // without a branch (lanes >= r, or r = 0, read an in-bundle word that is
   // never used), so no control flow separates these loads from their uses.
   const int rc = r > 0 ? r : 1;
-  const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.b_gate : 0));
-  const uint16_t* Bup = reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.b_up : 0));
+  const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(r > 0 ? E0_LORA(a, b, k, 1, a.lay.b_gate) : b);
+  const uint16_t* Bup = reinterpret_cast<const uint16_t*>(r > 0 ? E0_LORA(a, b, k, 3, a.lay.b_up) : b);
   const int rl = lane % rc;
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {

@@ -96,10 +96,11 @@ __global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
   const uint16_t* wrow = nullptr;
   if (active && router) wrow = li.w_router + (size_t)row * d;
   if (active && lora && !(li.flags & IN_TOPK)) {
-    const int s = resolve_slot(a, a.ids[row / (2 * r)]);
+    const int kk = row / (2 * r), up = (row / r) & 1;
+    const int s = resolve_slot(a, a.ids[kk]);
     if (s >= 0)
-      wrow = reinterpret_cast<const uint16_t*>(a.pool + (size_t)s * a.slot_bytes +
-                                               (((row / r) & 1) ? a.lay.a_up : a.lay.a_gate)) +
+      wrow = reinterpret_cast<const uint16_t*>(E0_LORA(a, a.pool + (size_t)s * a.slot_bytes, kk,
+                                                       up ? 2 : 0, up ? a.lay.a_up : a.lay.a_gate)) +
              (size_t)(row % r) * d;
   }
   const bool pref = wrow != nullptr && d <= 64 * kPrefChunks * 8;
@@ -190,7 +191,7 @@ template <int NJ>
 __device__ __forceinline__ void gate_up_wide(const MoeArgs& a, const uint8_t* b, int k, int i0,
                                              float* h_s, float* hrep_s) {
   GuW<NJ> w;
-  gu_load<NJ>(a, b, i0, w);
+  gu_load<NJ>(a, b, i0, w, tid_here() >> 6, k);
   const int lane = threadIdx.x & 63, r = a.r;
   float tg = 0.f, tu = 0.f;
   if (r > 0 && lane < r) {
@@ -231,7 +232,8 @@ __device__ __forceinline__ void gate_up_narrow(const MoeArgs& a, const uint8_t* 
     bb[st] = bp[row * ng + grp];
   }
   if (r > 0) {
-    const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate));
+    const uint16_t* B =
+        reinterpret_cast<const uint16_t*>(E0_LORA(a, b, k, p ? 3 : 1, p ? a.lay.b_up : a.lay.b_gate));
     const float* t = a.t_in + (size_t)(k * 2 + p) * r;
 #pragma unroll
     for (int m = 0; m < LPR; ++m) {
@@ -294,7 +296,8 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
   uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
   if ((int)threadIdx.x < r) {
     const uint4* src = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)threadIdx.x * a.I + i0);
+        reinterpret_cast<const uint16_t*>(E0_LORA(a, b, k, 4, a.lay.a_down)) + (size_t)threadIdx.x * a.I +
+        i0);
     ad0 = src[0];
     ad1 = src[1];
   }
@@ -768,7 +771,8 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
     bv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_b)[(size_t)grp * d + o];
     // B_down row o of the tile's expert (r bf16; an in-bundle word when r = 0)
     const uint4* Bdp = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(b + (r > 0 ? a.lay.b_down : 0)) + (size_t)o * r);
+        reinterpret_cast<const uint16_t*>(r > 0 ? E0_LORA(a, b, kk, 5, a.lay.b_down) : b) +
+        (size_t)o * r);
 #pragma unroll
     for (int j = 0; j < kBd; ++j) bdq[m][j] = (8 * j < r) ? Bdp[j] : make_uint4(0, 0, 0, 0);
   }
@@ -841,8 +845,8 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
           int slot = a.slots[kk];
           slot = (slot >= 0 && slot < a.n_slots) ? slot : 0;
           bw4 = reinterpret_cast<const uint4*>(
-              reinterpret_cast<const uint16_t*>(a.pool + (size_t)slot * a.slot_bytes +
-                                                a.lay.b_down) +
+              reinterpret_cast<const uint16_t*>(
+                  E0_LORA(a, a.pool + (size_t)slot * a.slot_bytes, kk, 5, a.lay.b_down)) +
               (size_t)o * r)[j];
         }
         const uint32_t bw[4] = {bw4.x, bw4.y, bw4.z, bw4.w};
@@ -909,10 +913,13 @@ __global__ void k_transpose_sb(const uint16_t* __restrict__ src, uint16_t* __res
 // ------------------------------------------------------------ host side
 int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const int32_t* table,
                   const int32_t* ids, const float* w, const void* x, void* y, void* workspace,
-                  MoeArgs* a) {
-  edge0_bundle_layout lay;
-  if (bundle_layout(sh, &lay) != EDGE0_OK) return EDGE0_EINVAL;
-  if (!pool || !pool->base || pool->n_slots <= 0 || pool->slot_bytes < lay.bytes ||
+                  MoeArgs* a, bool lora_in_bundle) {
+  edge0_bundle_layout lay, lay_pool;
+  edge0_moe_shape s0 = *sh;
+  if (!lora_in_bundle) s0.lora_rank = 0;  // the bundles hold the int4 arrays only
+  if (bundle_layout(sh, &lay) != EDGE0_OK || bundle_layout(&s0, &lay_pool) != EDGE0_OK)
+    return EDGE0_EINVAL;
+  if (!pool || !pool->base || pool->n_slots <= 0 || pool->slot_bytes < lay_pool.bytes ||
       pool->slot_bytes % 256 != 0 || !table || !ids || !w || !workspace)
     return EDGE0_EINVAL;
   const WsLayout L = ws_layout(sh);
@@ -948,6 +955,9 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   a->route_rows = 0;
   a->par = 0;
   a->lg_consumed = nullptr;
+  a->lora_sep = false;
+  a->lo_stride = 0;
+  for (auto& p : a->lo_base) p = nullptr;
   a->err_out = nullptr;
   a->spin = kFusedDefaultSpin;
   a->hf = reinterpret_cast<float*>(ws + L.hf);
@@ -1107,6 +1117,33 @@ extern "C" int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_po
   if (rc != EDGE0_OK) return rc;
   LayerIn li{};
   li.flags = IN_LORA;  // with r = 0 it only resolves the slots
+  if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+  if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
+  return launch_combine(a, stream);
+}
+
+extern "C" int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                    const edge0_lora* lora, const int32_t* slot_table,
+                                    const int32_t* ids, const float* w, const void* x, void* y,
+                                    void* workspace, hipStream_t stream) {
+  if (!shape || !shape_ok(shape) || !x || !y || x == y) return EDGE0_EINVAL;
+  const int r = shape->lora_rank;
+  if (r > 0 && (!lora || !lora->a_gate || !lora->b_gate || !lora->a_up || !lora->b_up ||
+                !lora->a_down || !lora->b_down || lora->expert_stride < 0))
+    return EDGE0_EINVAL;
+  // the bundles need not hold adapters: the pool is checked against the
+  // LoRA-free layout (the int4 arrays sit at the same offsets in both)
+  MoeArgs a;
+  int rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, workspace, &a, false);
+  if (rc != EDGE0_OK) return rc;
+  if (r > 0) {
+    a.lora_sep = true;
+    const void* f[6] = {lora->a_gate, lora->b_gate, lora->a_up, lora->b_up, lora->a_down, lora->b_down};
+    for (int i = 0; i < 6; ++i) a.lo_base[i] = static_cast<const uint8_t*>(f[i]);
+    a.lo_stride = lora->expert_stride * 2;  // bf16 elements
+  }
+  LayerIn li{};
+  li.flags = IN_LORA;
   if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
   if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
   return launch_combine(a, stream);

@@ -6,6 +6,14 @@
 
 namespace e0 {
 
+// Address of LoRA factor i of routed expert k, whose bundle is at b and has
+// the factor at bundle offset off: the bundle's copy, or the separate
+// adapter of expert ids[k] (clamped into range: an invalid id's expert has
+// weight 0 and is reported by the slot resolution).
+#define E0_LORA(a, b, k, i, off)                                                             \
+  ((a).lora_sep ? (a).lo_base[i] + (size_t)max(0, min((a).ids[k], (a).E - 1)) * (a).lo_stride \
+                : (b) + (off))
+
 struct MoeArgs {
   const uint8_t* pool;
   int64_t slot_bytes;
@@ -47,6 +55,13 @@ struct MoeArgs {
   // written, the other parity's entries are emptied for the next router layer
   float* lg_hand;
   int route_rows, par;
+  // adapters given apart from the bundles (edge0_moe_layer_lora): factor i
+  // (a_gate, b_gate, a_up, b_up, a_down, b_down) of expert e at
+  // lo_base[i] + e * lo_stride bytes; when lora_sep is false each expert's
+  // factors are in its bundle at the layout's offsets
+  bool lora_sep;
+  const uint8_t* lo_base[6];
+  int64_t lo_stride;
   // the E entries of lg_hand the launch before this layer's down kernel
   // read (a router layer's logits), or NULL: the down kernel empties them,
   // so every router layer finds both parities empty whatever the parities
@@ -62,7 +77,7 @@ constexpr int64_t kFusedDefaultSpin = 1 << 21;
 
 int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const int32_t* table,
                   const int32_t* ids, const float* w, const void* x, void* y, void* workspace,
-                  MoeArgs* a);
+                  MoeArgs* a, bool lora_in_bundle = true);
 // First launch of a layer (k_layer_in), by flags:
 //   IN_COMBINE: y_prev = bf16(acc_prev), h = bf16(h_prev + y_prev)
 //   IN_NORM:    x = bf16(RMSNorm(h)) (h = h_prev without IN_COMBINE)

@@ -138,6 +138,8 @@ _SIG = {
     "edge0_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
     "edge0_workspace_error": (C.c_int, [_P, _P]),
     "edge0_route_commit": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P]),
+    "edge0_moe_layer_lora": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P, _P, _P,
+                                       _P, _P, _P, _P]),
     "edge0_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape), C.c_int32]),
     "edge0_merge_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
     "edge0_merge_requant": (C.c_int, [C.POINTER(MoeShape), _P, _P, _P, _P, _P]),
@@ -282,6 +284,21 @@ def edge0_prerouter(shape: MoeShape, head: Head, x, ids_now, ids_prev, logits_ou
                                _ptr(ids_now),
                                _ptr(ids_prev), _ptr(logits_out), _ptr(ids_out), _ptr(w_out),
                                _ptr(workspace), _stream(stream)), "edge0_prerouter")
+
+
+class Lora(C.Structure):
+    """The six bf16 factors of expert 0 and the element stride to the next
+    expert's (0: one adapter shared by every expert)."""
+    _fields_ = [(k, C.c_void_p) for k in ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")] + \
+        [("expert_stride", C.c_int64)]
+
+
+def edge0_moe_layer_lora(shape: MoeShape, pool: SlotPool, lora: "Lora | None", slot_table, ids, w,
+                         x, y, workspace, stream=None):
+    _check(lib.edge0_moe_layer_lora(C.byref(shape), C.byref(pool),
+                                    None if lora is None else C.byref(lora), _ptr(slot_table),
+                                    _ptr(ids), _ptr(w), _ptr(x), _ptr(y), _ptr(workspace),
+                                    _stream(stream)), "edge0_moe_layer_lora")
 
 
 def edge0_moe_layer(shape: MoeShape, pool: SlotPool, slot_table, ids, w, x, y, workspace,
