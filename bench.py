@@ -50,9 +50,9 @@ METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak
 # the same counters read for a device copy of known size (256 MiB copy:
 # FETCH_SIZE 131084.7 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only
 # for the kernel sources it was taken on (hash below); otherwise None.
-TRAFFIC_RECORD = {"src_sha": "e051c80a550a4218", "fetch_kib": 4046.3, "write_kib": 66.9,
+TRAFFIC_RECORD = {"src_sha": "83408eb9736f2f52", "fetch_kib": 4049.6, "write_kib": 66.9,
                   "fetch_scale": 2.0, "write_scale": 1.0}
-KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "moe.hip")
+KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "heads_dev.h", "moe.hip")
 HBM_PEAK_GBPS = 8000.0
 N_LAYERS, OWNERS, CONSUMERS = 40, (6, 37), (7, 38)
 
@@ -1079,6 +1079,8 @@ def row_stack(args, log):
             log(f"[bench] {mode_name} mode unavailable ({e}); using per-layer graphs")
             mode_name = "graphs"
     persistent = mode_name in ("persistent", "xcd")
+    sched = {"folded": E.EDGE0_HEADS_FOLDED, "after": E.EDGE0_HEADS_AFTER_LAYERS}
+    ds.stack.set_head_schedule(sched[args.head_schedule])
     total = args.warmup + args.steps
     h0 = to_device(np.stack([G.stack_hidden(S, args.seed, t) for t in range(total)]))
     h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
@@ -1130,6 +1132,23 @@ def row_stack(args, log):
             k_bytes = fused_bytes(S)
             k_traffic = gate_up_traffic()
     ds.stack.set_timing(0)
+    other_sched = None
+    if mode_name == "graphs" and not args.no_head_ab:
+        # the other head schedule on the same stack, same step count
+        other = "after" if args.head_schedule == "folded" else "folded"
+        ds.stack.set_head_schedule(sched[other])
+        t0 = total + 8
+        for t in range(t0, t0 + args.warmup):
+            ds.step(h0[t % total], h_out, t)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for t in range(t0 + args.warmup, t0 + args.warmup + args.steps):
+            ds.step(h0[t % total], h_out, t)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        other_sched = {"schedule": other, "ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 5)}
+        ds.stack.set_head_schedule(sched[args.head_schedule])
+        log(f"[bench] heads {other}: {other_sched['ms_per_step'] * 1000:.1f} us/step")
     k_mean = float(np.mean(k_ms))
     k_gbps = k_bytes / (k_mean * 1e-3) / 1e9
     log(f"[bench] {ms_step * 1000:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), "
@@ -1143,6 +1162,7 @@ def row_stack(args, log):
         "data": "synthetic",
         "config": {"workload": "40-layer Qwen3-MoE-shaped decode stack, all experts resident",
                    "stack_mode": mode_name,
+                   "head_schedule": args.head_schedule if mode_name == "graphs" else "after",
                    "d_model": S.d_model, "n_experts": S.n_experts, "d_inter": S.d_inter,
                    "top_k": S.top_k, "group": S.group, "lora_rank": S.lora_rank,
                    "head_hidden": S.head_hidden, "layers": N_LAYERS, "heads": "6-37",
@@ -1151,6 +1171,8 @@ def row_stack(args, log):
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "roofline": rl,
     }
+    if other_sched is not None:
+        out["other_head_schedule"] = other_sched
     del ds
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -1188,6 +1210,11 @@ def main():
                          "default, the fastest here), the layers as one persistent launch per "
                          "step, the XCD-split persistent launch, or one XCD-split launch per "
                          "layer")
+    ap.add_argument("--head-schedule", choices=["folded", "after"], default="folded",
+                    help="graphs mode: the heads' rows beside the down launches (default) or "
+                         "batched after the last layer; the other is timed too for comparison")
+    ap.add_argument("--no-head-ab", action="store_true",
+                    help="do not time the other head schedule (profiling runs)")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="grouped row: also time other MFMA thresholds")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -427,8 +427,9 @@ int edge0_stack_get_buffers(const edge0_stack* st, edge0_stack_buffers* out);
 void edge0_stack_destroy(edge0_stack* st);
 
 /* How edge0_stack_step runs the layers (the results are the same, within
- * the tolerance of fp32 summation order; heads and the gathered routing run
- * as ordinary launches after the layers in both modes):
+ * the tolerance of fp32 summation order; the gathered routing runs as an
+ * ordinary launch after the layers in every mode, and so do the heads except
+ * under the folded head schedule below):
  *   EDGE0_STACK_GRAPHS (default): the step's per-layer launches, replayed as
  *     HIP graphs (two or three dependent launches per layer).
  *   EDGE0_STACK_PERSISTENT: one cooperative launch of K * d_inter / 16
@@ -477,6 +478,23 @@ void edge0_stack_destroy(edge0_stack* st);
 enum { EDGE0_STACK_GRAPHS = 0, EDGE0_STACK_PERSISTENT = 1, EDGE0_STACK_XCD = 2,
        EDGE0_STACK_XLAYER = 3 };
 int edge0_stack_set_mode(edge0_stack* st, int32_t mode);
+/* When the owner layers' heads run in a step of the EDGE0_STACK_GRAPHS mode
+ * ([Edge0] §3.2 "Head": the heads' evaluation stays off the layers'
+ * dependent chain; "Motivation": a head's prediction is consumed at the next
+ * token, so nothing in the step waits for it):
+ *   EDGE0_HEADS_FOLDED (default): head L's fc1 rows run as workgroups
+ *     appended to layer L's down-projection launch, and its fc2 rows and
+ *     routing commit as workgroups appended to layer L+1's, so no head
+ *     launch follows the last layer;
+ *   EDGE0_HEADS_AFTER_LAYERS: all heads as one batch (two launches) after
+ *     the last layer.
+ * The predictions are the same bit for bit either way (the same rows and
+ * commit code over the same inputs).  The other modes and the staged step
+ * run the heads after the layers whatever the setting.  Changing it waits
+ * for the device and rebuilds the step graphs.  EDGE0_EINVAL for another
+ * value. */
+enum { EDGE0_HEADS_AFTER_LAYERS = 0, EDGE0_HEADS_FOLDED = 1 };
+int edge0_stack_set_head_schedule(edge0_stack* st, int32_t schedule);
 /* Polls per bounded wait before a workgroup gives up (0: the default, about
  * a second): the persistent mode's phase waits, and in the graphs mode the
  * gate/up workgroups' wait for their expert's LoRA A x, which workgroups of

@@ -41,6 +41,7 @@
 #include <mutex>
 
 #include "gemv_dev.h"
+#include "heads_dev.h"
 #include "moe_internal.h"
 
 namespace e0 {
@@ -731,8 +732,9 @@ constexpr int kMaxSliceChunks = 64;  // expert-chunks per unit staged in LDS
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// One down unit: workgroup `bid` of the (d / 64) * S units.
 template <int TPW>
-__global__ __launch_bounds__(256) void k_down(MoeArgs a) {
+__device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) {
   __shared__ float red[4][64];
   __shared__ uint32_t hp_s[kMaxSliceChunks][32];  // hi pairs then lo pairs of each chunk
   __shared__ float hsum_s[kMaxSliceChunks];
@@ -741,8 +743,8 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   const int wave = uni(threadIdx.x >> 6);
   const int K = a.K, S = a.S, I = a.I, r = a.r, d = a.d;
   const int NC = I / 32;
-  const int rb = blockIdx.x / S;
-  const int sl = blockIdx.x % S;
+  const int rb = bid / S;
+  const int sl = bid % S;
   const int cps = (NC + S - 1) / S;
   const int c0 = sl * cps;
   const int ncs = min(NC, c0 + cps) - c0;
@@ -813,7 +815,7 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
       tdc_s[te][rr] = tp[rr] + tp[r + rr];
     }
   }
-  if (blockIdx.x == 0) {
+  if (bid == 0) {
     if (threadIdx.x < (unsigned)K) {
       const int slot = a.slots[threadIdx.x];
       if (slot < 0 || slot >= a.n_slots) set_error(a.err, EDGE0_ERANGE);
@@ -866,6 +868,26 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
   __syncthreads();
   if (wave == 0)
     atomicAdd(a.acc + o, to_fix(red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]));
+}
+
+template <int TPW>
+__global__ __launch_bounds__(256) void k_down(MoeArgs a) {
+  down_unit<TPW>(a, blockIdx.x);
+}
+
+// The same launch with one prerouter head's fc1 rows beside it (the stack's
+// folded head schedule): row y = 0 of the grid runs the head's workgroups
+// (dispatched first, so their loads go out before the units'), row y = 1 the
+// down units.  The role comes from the workgroup id alone, so no argument
+// load stands between a unit's start and its weight loads.
+template <int TPW>
+__global__ __launch_bounds__(256) void k_down_fc1(MoeArgs a, HeadPart h) {
+  if (blockIdx.y == 0) {
+    if ((int)blockIdx.x < h.n_wg) head_fc1_row(h, blockIdx.x * kHeadFc1Rows + (threadIdx.x >> 6));
+    return;
+  }
+  if ((int)blockIdx.x >= (a.d / 64) * a.S) return;
+  down_unit<TPW>(a, blockIdx.x);
 }
 
 // y = bf16 of the layer's fixed-point accumulator; optional residual
@@ -1005,7 +1027,8 @@ int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
   return EDGE0_OK;
 }
 
-int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
+int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing,
+                        const HeadPart* fc1) {
   const int cpr = a.d / 32;
   const int grid2 = a.K * (a.I / 16);
   if (timing && timing->which == 1 && cpr == 64) {
@@ -1030,23 +1053,34 @@ int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming
   E0_CHECK_LAUNCH();
   E0_MARK(1, false);
   }
-  return launch_down(a, stream, timing);
+  return launch_down(a, stream, timing, fc1);
 }
 
-int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing) {
+template <int TPW>
+static void launch_down_t(const MoeArgs& a, int units, const HeadPart* fc1, hipStream_t stream) {
+  if (fc1 == nullptr) {
+    k_down<TPW><<<units, 256, 0, stream>>>(a);
+  } else {
+    k_down_fc1<TPW><<<dim3(std::max(units, fc1->n_wg), 2), 256, 0, stream>>>(a, *fc1);
+  }
+}
+
+int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing,
+                const HeadPart* fc1) {
+  if (fc1 != nullptr && fc1->n_wg < 1) return EDGE0_EINVAL;
   E0_MARK(2, true);
   {
     const int NC = a.I / 32, cps = (NC + a.S - 1) / a.S;
     const int tpw = (a.K * cps + 3) / 4;
-    const int grid = (a.d / 64) * a.S;
-    if (tpw <= 1) k_down<1><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 2) k_down<2><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 3) k_down<3><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 4) k_down<4><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 6) k_down<6><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 8) k_down<8><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 12) k_down<12><<<grid, 256, 0, stream>>>(a);
-    else if (tpw <= 16) k_down<16><<<grid, 256, 0, stream>>>(a);
+    const int units = (a.d / 64) * a.S;
+    if (tpw <= 1) launch_down_t<1>(a, units, fc1, stream);
+    else if (tpw <= 2) launch_down_t<2>(a, units, fc1, stream);
+    else if (tpw <= 3) launch_down_t<3>(a, units, fc1, stream);
+    else if (tpw <= 4) launch_down_t<4>(a, units, fc1, stream);
+    else if (tpw <= 6) launch_down_t<6>(a, units, fc1, stream);
+    else if (tpw <= 8) launch_down_t<8>(a, units, fc1, stream);
+    else if (tpw <= 12) launch_down_t<12>(a, units, fc1, stream);
+    else if (tpw <= 16) launch_down_t<16>(a, units, fc1, stream);
     else return EDGE0_EINVAL;
   }
   E0_CHECK_LAUNCH();

@@ -111,9 +111,13 @@ struct LaunchTiming {
 };
 int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
                     const LaunchTiming* timing = nullptr);
-int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+// `fc1` (optional): a head's fc1 rows, run by workgroups of the down launch
+struct HeadPart;
+int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr,
+                        const HeadPart* fc1 = nullptr);
 // the down GEMV alone (after k_layer_fused)
-int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr);
+int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr,
+                const HeadPart* fc1 = nullptr);
 // Layer input + gate/up in one launch for a layer whose routing (a.ids) is
 // known before it starts; li carries the prologue (combine, residual, RMSNorm)
 // arguments.  Wide rows (d_model 2048 or 4096), lora_rank <= 16.
@@ -149,7 +153,55 @@ struct HeadBatch {
   uint32_t* err;
   RouteRule rule;                    // the commit (kind 0 in the stack)
 };
-int launch_heads(const HeadBatch& hb, hipStream_t stream);
+// fc1 = false: the fc2 rows and commits only (the fc1 rows ran already)
+int launch_heads(const HeadBatch& hb, hipStream_t stream, bool fc1 = true);
+
+// One head's fc1 (and residual) rows run as workgroups beside another
+// launch: the stack's folded head schedule runs head L's fc1 rows in layer
+// L's down-projection launch instead of after the step's last layer.  The
+// rows are the batched head kernel's own code, so the results are the same
+// bit for bit.
+struct HeadPart {
+  int n_wg;             // workgroups of kHeadFc1Rows rows
+  int d, E, K, H, has_res;
+  const uint16_t *w1x, *w1oh, *b1, *w2, *b2, *wl;
+  const uint16_t* x;
+  const int32_t *ids_now, *ids_prev;  // ids_prev NULL: no previous token
+  float *a, *res, *logits;
+  uint32_t* counter;    // completion counter of the fc2 workgroups (reset by the last)
+  int32_t* ids_out;
+  float* w_out;
+  uint32_t* err;
+  RouteRule rule;
+};
+constexpr int kHeadFc1Rows = 4;    // fc1 rows per 256-thread workgroup (a row per wave)
+// head i of a batch as a part (the workgroup count left to the caller)
+__host__ __device__ inline HeadPart head_part(const HeadBatch& hb, int i) {
+  HeadPart h{};
+  h.d = hb.d;
+  h.E = hb.E;
+  h.K = hb.K;
+  h.H = hb.H;
+  h.has_res = hb.has_res;
+  h.w1x = hb.w1x[i];
+  h.w1oh = hb.w1oh[i];
+  h.b1 = hb.b1[i];
+  h.w2 = hb.w2[i];
+  h.b2 = hb.b2[i];
+  h.wl = hb.wl[i];
+  h.x = hb.x + (size_t)i * hb.x_stride;
+  h.ids_now = hb.ids_now != nullptr ? hb.ids_now + (size_t)i * hb.ids_stride : nullptr;
+  h.ids_prev = hb.ids_prev != nullptr ? hb.ids_prev + (size_t)i * hb.ids_stride : nullptr;
+  h.a = hb.a + (size_t)i * hb.H;
+  h.res = hb.res + (size_t)i * hb.E;
+  h.logits = hb.logits + (size_t)i * hb.E;
+  h.counter = hb.counters + i;
+  h.ids_out = hb.ids_out + (size_t)i * hb.out_stride;
+  h.w_out = hb.w_out + (size_t)i * hb.out_stride;
+  h.err = hb.err;
+  h.rule = hb.rule;
+  return h;
+}
 
 // the file tier, for the stager
 int filetier_read(edge0_filetier* ft, const int32_t* keys, int n, const void** dev_out,

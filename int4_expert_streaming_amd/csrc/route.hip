@@ -11,6 +11,7 @@
 // loads per lane, fp32 accumulation, a wave butterfly for the row sum.  The
 // top-K runs in the last workgroup to finish (completion counter in the
 // workspace), so a router or head call is one or two launches.
+#include "heads_dev.h"
 #include "moe_internal.h"
 
 namespace e0 {
@@ -55,132 +56,30 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ wr,
 // workgroup of a head, per-head completion counter).  A batch of one is the
 // single-head call; the stack runs the heads of all owner layers of a step
 // as one batch after the step's layers ("one flush per step").
-__device__ __forceinline__ float gelu_erf_f(float z) {
-  return 0.5f * z * (1.f + erff(z * 0.70710678118654752440f));
-}
-
-// fc1 rows [0, H) of head i: a[i][h] = gelu(w1x[h] . x_i + sum of the one-hot
-// columns + b1[h]); residual rows [H, H+E): res[i][e] = wl[e] . x_i
+// fc1 rows [0, H) of head i and its residual rows [H, H+E): one wave per row
 __global__ __launch_bounds__(256) void k_heads_fc1(HeadBatch hb) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int H = hb.H, E = hb.E, K = hb.K, d = hb.d;
-  const int per = (H + (hb.has_res ? E : 0) + 3) / 4;
+  const int per = (hb.H + (hb.has_res ? hb.E : 0) + 3) / 4;
   const int i = blockIdx.x / per;
-  const int row = (blockIdx.x % per) * 4 + wave;
-  const uint16_t* x = hb.x + (size_t)i * hb.x_stride;
-  const bool fc1 = row < H;
-  const bool resrow = !fc1 && hb.has_res && row < H + E;
-  if (!fc1 && !resrow) return;
-  const uint16_t* wrow = fc1 ? hb.w1x[i] + (size_t)row * d : hb.wl[i] + (size_t)(row - H) * d;
-  RowPref pf;
-  const bool pref = d <= 64 * kPrefChunks * 8;
-  if (pref) row_prefetch(wrow, d, pf);
-  if (fc1) {
-    // one-hot columns: lane j < K this token's ids, K <= j < 2K the previous
-    // token's (block offset E); loaded with the row.  The blocks are binary
-    // multi-hots, so an id listed twice in one block sets its entry once:
-    // only its first listing in that block adds the column.
-    const bool prev = lane >= K;
-    int id = -1;
-    if (lane < 2 * K) {
-      const int32_t* src = prev ? hb.ids_prev : hb.ids_now;
-      if (src != nullptr) id = src[(size_t)i * hb.ids_stride + (prev ? lane - K : lane)];
-    }
-    bool first = true;
-    for (int j = 0; j < 2 * K; ++j) {
-      const int other = __shfl(id, j, kWave);
-      if (j < lane && (j >= K) == prev && other == id) first = false;
-    }
-    float g = 0.f;
-    if (lane < 2 * K && first) {
-      const int32_t* src = prev ? hb.ids_prev : hb.ids_now;
-      if (src != nullptr) {
-        if (id >= 0 && id < E) {
-          g = h2f(hb.w1oh[i][(size_t)(prev ? E + id : id) * H + row]);
-        } else {
-          set_error(hb.err, EDGE0_ERANGE);
-        }
-      }
-    }
-    const float b1 = hb.b1[i] != nullptr ? h2f(hb.b1[i][row]) : 0.f;
-    float s = pref ? row_dot_pref<true>(pf, x, d) : row_dot<true, false>(wrow, x, d);
-    float gs = 0.f;
-    for (int j = 0; j < 2 * K; ++j) gs += __shfl(g, j, kWave);  // fixed order
-    s += gs + b1;
-    if (lane == 0) hb.a[(size_t)i * H + row] = gelu_erf_f(s);
-  } else {
-    const float s = pref ? row_dot_pref<true>(pf, x, d) : row_dot<true, false>(wrow, x, d);
-    if (lane == 0) hb.res[(size_t)i * E + row - H] = s;
-  }
+  head_fc1_row(head_part(hb, i), (blockIdx.x % per) * 4 + (threadIdx.x >> 6));
 }
 
-// logits[i][e] = w2[e] . a_i + b2[e] + res[i][e], then head i's commit.
-// A workgroup covers 8 * kFc2Waves rows of one head (each wave 8 rows at a
-// time, one 16-byte chunk of each fp16 row per lane, the 8 row sums reduced
-// together), so a head spreads over E / 16 compute units; the logits go to
-// memory and the head's last workgroup to finish (completion counter, reset
-// by it) commits the top-K.
+// fc2 rows and each head's commit: a workgroup covers 8 * kFc2Waves rows of
+// one head, so a head spreads over E / 16 compute units; the logits go to
+// memory and the head's last workgroup to finish commits the top-K.
 constexpr int kFc2Waves = 2;
 __global__ __launch_bounds__(64 * kFc2Waves) void k_heads_fc2(HeadBatch hb) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = hb.H, E = hb.E, K = hb.K;
-  const int parts = (E + 8 * kFc2Waves - 1) / (8 * kFc2Waves);
+  const int parts = (hb.E + 8 * kFc2Waves - 1) / (8 * kFc2Waves);
   const int i = blockIdx.x / parts;
-  const int rb = (blockIdx.x % parts) * 8 * kFc2Waves + 8 * wave;
-  const float* av = hb.a + (size_t)i * H;
-  const uint16_t* w2 = hb.w2[i];
-  const int nch = H / 8;  // 16-byte chunks per row
-  if (rb < E) {
-    float v[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) v[m] = 0.f;
-    for (int c = lane; c < nch; c += 64) {
-      const float4 a0 = reinterpret_cast<const float4*>(av + 8 * c)[0];
-      const float4 a1 = reinterpret_cast<const float4*>(av + 8 * c)[1];
-      uint4 q[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        q[m] = rb + m < E ? reinterpret_cast<const uint4*>(w2 + (size_t)(rb + m) * H)[c]
-                          : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        float s = v[m];
-        s = fmaf(h2f(q[m].x & 0xFFFFu), a0.x, s);
-        s = fmaf(h2f(q[m].x >> 16), a0.y, s);
-        s = fmaf(h2f(q[m].y & 0xFFFFu), a0.z, s);
-        s = fmaf(h2f(q[m].y >> 16), a0.w, s);
-        s = fmaf(h2f(q[m].z & 0xFFFFu), a1.x, s);
-        s = fmaf(h2f(q[m].z >> 16), a1.y, s);
-        s = fmaf(h2f(q[m].w & 0xFFFFu), a1.z, s);
-        s = fmaf(h2f(q[m].w >> 16), a1.w, s);
-        v[m] = s;
-      }
-    }
-    // row rb + m ends up in lane 8 m
-    const float sum = wave_sums8(v);
-    if ((lane & 7) == 0) {
-      const int e = rb + (lane >> 3);
-      if (e < E) {
-        float s = sum;
-        if (hb.b2[i] != nullptr) s += h2f(hb.b2[i][e]);
-        if (hb.has_res) s += hb.res[(size_t)i * E + e];
-        st_dev(hb.logits + (size_t)i * E + e, s);
-      }
-    }
-  }
-  if (last_arrival(hb.counters + i, parts)) {
-    if (wave == 0)
-      wave_commit<true>(hb.logits + (size_t)i * E, E, K, hb.rule,
-                        hb.ids_out + (size_t)i * hb.out_stride, hb.w_out + (size_t)i * hb.out_stride);
-    if (tid == 0) __hip_atomic_store(hb.counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  head_fc2_part(head_part(hb, i), blockIdx.x % parts, parts);
 }
 
-int launch_heads(const HeadBatch& hb, hipStream_t stream) {
+int launch_heads(const HeadBatch& hb, hipStream_t stream, bool fc1) {
   if (hb.n < 1 || hb.n > kMaxHeads) return EDGE0_EINVAL;
-  const int per1 = (hb.H + (hb.has_res ? hb.E : 0) + 3) / 4;
-  k_heads_fc1<<<hb.n * per1, 256, 0, stream>>>(hb);
-  E0_CHECK_LAUNCH();
+  if (fc1) {
+    const int per1 = (hb.H + (hb.has_res ? hb.E : 0) + 3) / 4;
+    k_heads_fc1<<<hb.n * per1, 256, 0, stream>>>(hb);
+    E0_CHECK_LAUNCH();
+  }
   k_heads_fc2<<<hb.n * ((hb.E + 8 * kFc2Waves - 1) / (8 * kFc2Waves)), 64 * kFc2Waves, 0,
                 stream>>>(hb);
   E0_CHECK_LAUNCH();

@@ -70,6 +70,7 @@ struct edge0_stack {
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
   hipEvent_t ev_heads;       // staged steps: the heads of the step have run
   int32_t* loop_host;        // staged closed loop: pinned [2][L][K] ids read back
+  int head_schedule;         // EDGE0_HEADS_FOLDED (default) or EDGE0_HEADS_AFTER_LAYERS
   // persistent mode (EDGE0_STACK_PERSISTENT)
   int mode;
   uint32_t* flow_cnt;                // [kFlowMaxPhases][kFlowCounters][64] arrival counters
@@ -96,7 +97,40 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
   return L >= s.owner_first && L <= s.owner_last;
 }
 
-static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream);
+// fc1 false: the heads' fc1 rows ran beside the layers; only fc2 and the commits here
+static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1 = true);
+
+// The routing layer L executes at step s (its ids and weights).
+static int32_t* layer_ids(const edge0_stack* st, int L, int s) {
+  const bool by_pred = is_consumer(st->spec, L) && s > 0;
+  return (by_pred ? st->pred_ids[s % 3] : st->exec_ids[s & 1]) + (size_t)L * st->shape.top_k;
+}
+static float* layer_w(const edge0_stack* st, int L, int s) {
+  const bool by_pred = is_consumer(st->spec, L) && s > 0;
+  return (by_pred ? st->pred_w[s % 3] : st->exec_w[s & 1]) + (size_t)L * st->shape.top_k;
+}
+
+// The folded head schedule: head L's fc1 rows run beside layer L's down
+// projection (x_L and the routing layer L executed are complete by then);
+// the fc2 rows and commits of all heads run batched after the last layer.
+// The inputs are those of the batched heads: x_L, the routing of layer L at
+// this step and at the previous one.  False: no head rows beside layer L.
+static bool folded_fc1(const edge0_stack* st, int L, int step, HeadPart* out) {
+  const edge0_stack_spec& sp = st->spec;
+  if (st->head_schedule != EDGE0_HEADS_FOLDED || !is_owner(sp, L)) return false;
+  const int d = st->shape.d_model;
+  HeadBatch hb = st->heads_batch;
+  hb.x = st->x + (size_t)sp.owner_first * d;
+  hb.ids_now = hb.ids_prev = nullptr;
+  hb.ids_out = nullptr;  // the fc1 rows commit nothing
+  hb.w_out = nullptr;
+  HeadPart& h = *out;
+  h = head_part(hb, L - sp.owner_first);
+  h.n_wg = (h.H + (h.has_res ? h.E : 0) + kHeadFc1Rows - 1) / kHeadFc1Rows;
+  h.ids_now = layer_ids(st, L, step);
+  h.ids_prev = step > 0 ? layer_ids(st, L, step - 1) : nullptr;
+  return true;
+}
 
 // The XCD-split layers mode: per layer one launch of k_xlayer (the layer's
 // input, routing, gate/up, SwiGLU, down and combine), then the last layer's
@@ -222,9 +256,10 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     uint16_t* hL = st->h + (size_t)L * d;
     uint16_t* xL = st->x + (size_t)L * d;
     const bool by_pred = is_consumer(st->spec, L) && step > 0;
-    int32_t* ids = by_pred ? st->pred_ids[step % 3] + (size_t)L * K
-                           : st->exec_ids[step & 1] + (size_t)L * K;
-    float* w = by_pred ? st->pred_w[step % 3] + (size_t)L * K : st->exec_w[step & 1] + (size_t)L * K;
+    int32_t* ids = layer_ids(st, L, step);
+    float* w = layer_w(st, L, step);
+    HeadPart hpart;
+    const HeadPart* hp = folded_fc1(st, L, step, &hpart) ? &hpart : nullptr;
     int rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
                            st->y + (size_t)L * d, st->ws, &a);
     if (rc != EDGE0_OK) return rc;
@@ -252,7 +287,7 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       li.flags |= IN_LORA;
       if ((rc = launch_layer_fused(a, li, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
               EDGE0_OK ||
-          (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+          (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp)) != EDGE0_OK)
         return rc;
       continue;
     }
@@ -273,7 +308,7 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
         a.lg_consumed = a.lg_hand + (size_t)a.par * E;  // emptied again by the down kernel
         if ((rc = launch_layer_fused(a, lr, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
                 EDGE0_OK ||
-            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp)) != EDGE0_OK)
           return rc;
         continue;
       }
@@ -285,7 +320,8 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       l2.w_out = w;
       if ((rc = launch_layer_in(a, l2, stream)) != EDGE0_OK) return rc;
     }
-    if ((rc = launch_expert_gemvs(a, stream, st->timed_kernel > 0 ? &lt : nullptr)) != EDGE0_OK)
+    if ((rc = launch_expert_gemvs(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp)) !=
+        EDGE0_OK)
       return rc;
   }
   // the last layer's combine and residual
@@ -293,12 +329,12 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
   a.h_out = st->h + (size_t)Lc * d;
   const int rc = launch_combine(a, stream);
   if (rc != EDGE0_OK) return rc;
-  return enqueue_tail(st, step, stream);
+  return enqueue_tail(st, step, stream, st->head_schedule != EDGE0_HEADS_FOLDED);
 }
 
 // after the layers: the routing every layer executed, gathered, and every
 // owner layer's head, batched
-static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream) {
+static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1) {
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers;
   int rc = EDGE0_OK;
@@ -318,7 +354,7 @@ static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream) {
     hb.ids_prev = step > 0 ? st->run_ids[(step - 1) & 1] + (size_t)L0 * K : nullptr;
     hb.ids_out = st->pred_ids[(step + 1) % 3] + (size_t)(L0 + 1) * K;
     hb.w_out = st->pred_w[(step + 1) % 3] + (size_t)(L0 + 1) * K;
-    rc = launch_heads(hb, stream);
+    rc = launch_heads(hb, stream, fc1);
     if (rc != EDGE0_OK) return rc;
   }
   return EDGE0_OK;
@@ -502,6 +538,7 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   st->heads.assign(heads, heads + Lc);
   st->last_step = -1;
   st->spin = kFlowDefaultSpin;
+  st->head_schedule = EDGE0_HEADS_FOLDED;
   const size_t d = shape->d_model, K = shape->top_k;
   st->ws_bytes = edge0_workspace_bytes(shape);
   bool ok = hipMalloc((void**)&st->x, Lc * d * 2) == hipSuccess &&
@@ -934,6 +971,21 @@ extern "C" int edge0_stack_set_trace(edge0_stack* st, int32_t layer, uint64_t* t
   st->x_trace = reinterpret_cast<unsigned long long*>(trace);
   st->x_trace_layer = layer;
   // the per-layer mode's step graphs hold the trace pointer in their arguments
+  for (auto& g : st->graphs)
+    if (g) {
+      (void)hipGraphExecDestroy(g);
+      g = nullptr;
+    }
+  return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_set_head_schedule(edge0_stack* st, int32_t schedule) {
+  if (!st || (schedule != EDGE0_HEADS_FOLDED && schedule != EDGE0_HEADS_AFTER_LAYERS))
+    return EDGE0_EINVAL;
+  if (schedule == st->head_schedule) return EDGE0_OK;
+  // the step graphs hold the schedule: wait for any replay, then rebuild them
+  if (hipDeviceSynchronize() != hipSuccess) return EDGE0_EHIP;
+  st->head_schedule = schedule;
   for (auto& g : st->graphs)
     if (g) {
       (void)hipGraphExecDestroy(g);

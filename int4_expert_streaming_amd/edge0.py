@@ -160,6 +160,7 @@ _SIG = {
     "edge0_stack_destroy": (None, [_P]),
     "edge0_stack_set_timing": (C.c_int, [_P, C.c_int32]),
     "edge0_stack_set_mode": (C.c_int, [_P, C.c_int32]),
+    "edge0_stack_set_head_schedule": (C.c_int, [_P, C.c_int32]),
     "edge0_stack_set_spin_limit": (C.c_int, [_P, C.c_int64]),
     "edge0_stack_error": (C.c_int, [_P]),
     "edge0_stack_kernel_ms": (C.c_int, [_P, C.POINTER(C.c_float), C.c_int32,
@@ -321,6 +322,8 @@ EDGE0_STACK_GRAPHS = 0
 EDGE0_STACK_PERSISTENT = 1
 EDGE0_STACK_XCD = 2
 EDGE0_STACK_XLAYER = 3
+EDGE0_HEADS_AFTER_LAYERS = 0
+EDGE0_HEADS_FOLDED = 1
 
 
 def grouped_mfma_min(n: int) -> int:
@@ -395,6 +398,12 @@ class Stack(_Handle):
         """EDGE0_STACK_GRAPHS (per-layer launches as graphs) or
         EDGE0_STACK_PERSISTENT (one cooperative launch for the layers)."""
         _check(lib.edge0_stack_set_mode(self._handle, mode), "edge0_stack_set_mode")
+
+    def set_head_schedule(self, schedule: int):
+        """EDGE0_HEADS_FOLDED (heads beside the down launches) or
+        EDGE0_HEADS_AFTER_LAYERS (one batch after the last layer)."""
+        _check(lib.edge0_stack_set_head_schedule(self._handle, schedule),
+               "edge0_stack_set_head_schedule")
 
     def set_spin_limit(self, polls: int):
         _check(lib.edge0_stack_set_spin_limit(self._handle, polls), "edge0_stack_set_spin_limit")

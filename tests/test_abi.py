@@ -77,6 +77,7 @@ def test_null_arguments_rejected_before_launch(E):
     assert E.lib.edge0_moe_layer(C.byref(s), C.byref(pool), 1, 1, 1, 1, 2, 1,
                                  None) == E.EDGE0_EINVAL
     assert E.strerror(E.EDGE0_ERANGE).startswith("expert id")
+    assert E.lib.edge0_stack_set_head_schedule(None, E.EDGE0_HEADS_FOLDED) == E.EDGE0_EINVAL
 
 
 def test_workspace_sizes(E):

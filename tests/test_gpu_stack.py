@@ -163,6 +163,40 @@ def test_qwen3moe_stack_every_layer(torch_cuda):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("which", ["tiny", "qwen3moe"])
+def test_head_schedules_agree_bit_for_bit(torch_cuda, which):
+    """The folded head schedule (head L's rows beside the down launches of
+    layers L and L+1, the default that the checks above run) and the batched
+    heads after the last layer give the same bits in every buffer of every
+    step, the predictions included; a restart at step 0 reproduces them."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    from int4_expert_streaming_amd.weights import to_device
+    if which == "tiny":
+        S, seed = G.TINY, 5
+        ds = DeviceStack(S, G.StackGen(S, seed), 10, (2, 7), (3, 8))
+    else:
+        S, seed = G.QWEN3_MOE, 21
+        ds = _qwen3_stack(S, seed)
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    runs = []
+    for sched in (E.EDGE0_HEADS_FOLDED, E.EDGE0_HEADS_AFTER_LAYERS, E.EDGE0_HEADS_FOLDED):
+        print(f"[stack] {which}: head schedule {sched}", flush=True)
+        ds.stack.set_head_schedule(sched)
+        snaps = []
+        for t in range(4):
+            ds.step(to_device(G.stack_hidden(S, seed, t)), h_out, t)
+            snaps.append(_snapshot(ds))
+        runs.append(snaps)
+    for t in range(4):
+        for k in runs[0][t]:
+            assert np.array_equal(runs[0][t][k], runs[1][t][k]), (which, t, k)
+            assert np.array_equal(runs[0][t][k], runs[2][t][k]), (which, t, k)
+    assert ds.stack.error() == E.EDGE0_OK
+
+
+@pytest.mark.timeout(900)
 def test_qwen3moe_stack_free_bias_both_modes(torch_cuda):
     """The same stack with group biases drawn independently of the scales
     (b ~ U[-0.16, 0.04]), so a kernel that ignored b or derived it from s
