@@ -380,6 +380,15 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   __shared__ int32_t ids_w[16];
   __shared__ float w_w[16];
   __shared__ float lg_s[ROUTE ? kFusedMaxExperts : 1];
+  // The arguments the start depends on, in one batch of scalar loads: left
+  // to itself the compiler loads them group by group behind the branches
+  // that need them, a dependent round trip each before the first memory
+  // load of the workgroup goes out.
+  asm volatile("" ::"s"(a.d), "s"(a.r), "s"(a.I), "s"(a.K), "s"(a.E), "s"(a.n_prod),
+               "s"(a.prod_rows), "s"(a.n_slots), "s"(li.flags), "s"(a.route_rows));
+  asm volatile("" ::"s"(a.table), "s"(a.pool), "s"(a.slot_bytes), "s"(a.ids), "s"(a.acc_prev),
+               "s"(li.h_prev), "s"(a.lay.gate_q), "s"(a.lay.up_q), "s"(a.lay.gate_s),
+               "s"(a.lay.gate_b), "s"(a.lay.up_s), "s"(a.lay.up_b));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // compute waves 0-7; wave 8 waits for the hand-off.  Wave 8 issues wave
   // 0's loads too (tl, wl): no branch then separates any wave's loads from
