@@ -69,9 +69,17 @@ struct GrpArgs {
   float* hs;                   // [P][I/16]
   unsigned long long* tdown;   // [P][r] A_down h, fixed point
   unsigned long long* acc;     // [T][d] y, fixed point
-  // prefill: the tile list (active expert, tile within it), info[2] entries;
-  // NULL in the grouped call, whose grid enumerates every (tile, expert)
+  // prefill: the list of (active expert, 16-pair tile) for the LoRA A x,
+  // info[2] entries
   const int2* tiles;
+  // prefill's GEMM tiles: the list of (active expert, 64-pair tile),
+  // info[3] entries; each token's activation sum per input group [T][d/g];
+  // each pair's weighted output row, by unsorted pair [P][d] (fp32); the
+  // kept expert of each unsorted pair, or -1 (dropped repeat, invalid id)
+  const int2* tiles64;
+  const float* xsum;
+  float* ypair;
+  const int32_t* keep;
 };
 
 // ------------------------------------------------------------- bucketing
@@ -724,17 +732,7 @@ __global__ __launch_bounds__(256, 3) void k_grp_gu_tile(GrpArgs a, int tm, int m
   __shared__ GuTileLds sm;
   const int nblk = a.I / 16;
   const int blk = blockIdx.x % nblk;
-  int tt, act;
-  if (a.tiles != nullptr) {  // prefill: entry blockIdx / nblk of the tile list
-    const int li = blockIdx.x / nblk;
-    if (li >= a.info[2]) return;
-    const int2 te = a.tiles[li];
-    act = te.x;
-    tt = te.y;
-  } else {
-    tt = blockIdx.x / (a.Amax * nblk);
-    act = (blockIdx.x / nblk) % a.Amax;
-  }
+  const int tt = blockIdx.x / (a.Amax * nblk), act = (blockIdx.x / nblk) % a.Amax;
   // everything the start depends on, in one round trip
   const int n_act = a.info[0], cnt = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
   asm volatile("" ::"s"(n_act), "s"(cnt), "s"(slot), "s"(q0));
@@ -905,17 +903,7 @@ __global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int
   __shared__ float td_s[kTileTok][kTileRank];  // zero past the rank
   const int nrb = a.d / (64 * kDownNT);
   const int rb = blockIdx.x % nrb;
-  int tt, act;
-  if (a.tiles != nullptr) {  // prefill: entry blockIdx / nrb of the tile list
-    const int li = blockIdx.x / nrb;
-    if (li >= a.info[2]) return;
-    const int2 te = a.tiles[li];
-    act = te.x;
-    tt = te.y;
-  } else {
-    tt = blockIdx.x / (a.Amax * nrb);
-    act = (blockIdx.x / nrb) % a.Amax;
-  }
+  const int tt = blockIdx.x / (a.Amax * nrb), act = (blockIdx.x / nrb) % a.Amax;
   const int n_act = a.info[0], cnt = a.act_cnt[act], slot = a.act_slot[act], q0 = a.act_off[act];
   asm volatile("" ::"s"(n_act), "s"(cnt), "s"(slot), "s"(q0));
   const int t_first = tt * tm;
@@ -956,12 +944,12 @@ __global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
 // whole-layer; §3.2 "Two consumption profiles": prefill hits every expert of
 // a layer).  Token by token the same result as the grouped call, for up to
 // kPfMaxTokens tokens: the bucketing runs over many workgroups and lists
-// the (expert, 16-token tile) units that exist, so the tile kernels' grids
-// cover those units rather than every (tile, expert) combination, and each
-// tile's LoRA A x runs on MFMA.  Pairs are placed in an expert's run in
-// arrival order; a pair's results do not depend on its place (every MFMA
-// output element is its own row's dot product, and the outputs are added in
-// fixed point), so calls are bit-reproducible.
+// the (expert, tile) units that exist (16-pair tiles for the LoRA A x on
+// MFMA, 64-pair tiles for the gate/up and down GEMMs), so the grids cover
+// those units rather than every (tile, expert) combination.  Pairs are
+// placed in an expert's run in arrival order; a pair's results do not depend
+// on its place (every MFMA output element is its own row's dot product, and
+// a token's K rows are added in k order), so calls are bit-reproducible.
 constexpr int kPfMaxTokens = 4096;
 
 // pass 1: per pair, an id repeated within its token is dropped (its first
@@ -989,35 +977,41 @@ __global__ __launch_bounds__(256) void k_pf_count(GrpArgs a, int32_t* cnt, int32
 }
 
 // pass 2 (one workgroup, one expert per thread): exclusive scans of the
-// counts, the active flags and the tiles per expert; the active list, each
-// expert's first free position, the tile list; the counts cleared
+// counts, the active flags and the tiles per expert (16-pair tiles for the
+// LoRA A x, 64-pair tiles for the gate/up and down GEMMs); the active list,
+// each expert's first free position, both tile lists; the counts cleared
+constexpr int kPfTile = 64;  // pairs per prefill GEMM tile (4 waves x 16)
 __global__ __launch_bounds__(1024) void k_pf_scan(GrpArgs a, int32_t* cnt, int32_t* fill,
-                                                  int2* tiles) {
-  __shared__ int wtot[3][16];
+                                                  int2* tiles, int2* tiles64) {
+  __shared__ int wtot[4][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   const int c = tid < E ? cnt[tid] : 0;
   const int f = c > 0 ? 1 : 0;
-  const int nt = (c + kTileTok - 1) / kTileTok;
-  const int ic = wave_incl_scan(c), iff = wave_incl_scan(f), it = wave_incl_scan(nt);
+  const int nt = (c + kTileTok - 1) / kTileTok, n64 = (c + kPfTile - 1) / kPfTile;
+  const int ic = wave_incl_scan(c), iff = wave_incl_scan(f), it = wave_incl_scan(nt),
+            i64 = wave_incl_scan(n64);
   if (lane == 63) {
     wtot[0][wave] = ic;
     wtot[1][wave] = iff;
     wtot[2][wave] = it;
+    wtot[3][wave] = i64;
   }
   __syncthreads();
-  int bc = 0, bf = 0, bt = 0, tc = 0, tf = 0, tt = 0;
+  int bc = 0, bf = 0, bt = 0, b64 = 0, tc = 0, tf = 0, tt = 0, t64 = 0;
   for (int v = 0; v < 16; ++v) {
     if (v < wave) {
       bc += wtot[0][v];
       bf += wtot[1][v];
       bt += wtot[2][v];
+      b64 += wtot[3][v];
     }
     tc += wtot[0][v];
     tf += wtot[1][v];
     tt += wtot[2][v];
+    t64 += wtot[3][v];
   }
-  const int xc = bc + ic - c, xf = bf + iff - f, xt = bt + it - nt;
+  const int xc = bc + ic - c, xf = bf + iff - f, xt = bt + it - nt, x64 = b64 + i64 - n64;
   if (tid < E) {
     fill[tid] = xc;
     cnt[tid] = 0;
@@ -1030,12 +1024,14 @@ __global__ __launch_bounds__(1024) void k_pf_scan(GrpArgs a, int32_t* cnt, int32
       a.act_slot[xf] = ok ? slot : -1;
       if (!ok) set_error(a.err, EDGE0_ERANGE);
       for (int i = 0; i < nt; ++i) tiles[xt + i] = make_int2(xf, i);
+      for (int i = 0; i < n64; ++i) tiles64[x64 + i] = make_int2(xf, i);
     }
   }
   if (tid == 0) {
     a.info[0] = tf;
     a.info[1] = tc;
     a.info[2] = tt;
+    a.info[3] = t64;
   }
 }
 
@@ -1104,6 +1100,550 @@ __global__ __launch_bounds__(256) void k_pf_lora_in(GrpArgs a) {
       a.t_in[((size_t)src * 2 + q / r) * r + q % r] = t;
     }
   }
+}
+
+// ------------------------------------------------ prefill GEMM tiles
+// A workgroup of the gate/up and down GEMMs covers a 64-pair tile of one
+// expert (wave w: pairs 16 w .. 16 w + 15, the MFMA A rows) and a block of
+// weight rows, and walks the inputs one quantisation group at a time: the
+// group's activations (or h) and int4 words are staged in LDS, shared by the
+// four waves, double-buffered (the next group's loads go out while the
+// current one is multiplied); per group the products start from zero and
+// are folded in fp32 as s * acc + (b - 128 s) * (the group's activation
+// sum), as in the token tiles.  No atomics: the gate/up kernel stores h
+// (bf16 hi/lo pairs, pair order) and its per-32-row sums, the down kernel
+// computes A_down h itself (two more MFMAs per step against the A_down
+// rows) and stores each pair's weighted output row, and the combine sums a
+// token's K rows in k order.  Every output element is its own row's dot
+// product whatever its tile mates, so calls are bit-reproducible.
+
+// workgroup -> logical unit, XCD-aware: consecutive workgroups go to
+// different XCDs, so unit u = (id % 8) * (n / 8) + id / 8 keeps a range of
+// consecutive units (a tile's row blocks, an expert's tiles) on one XCD and
+// its L2 (n a multiple of 8)
+__device__ __forceinline__ int pf_unit() {
+  const int id = blockIdx.x, n = gridDim.x;
+  return (id % 8) * (n / 8) + id / 8;
+}
+
+// each token's activation sum per input group, fp32 in input order
+__global__ __launch_bounds__(256) void k_pf_xsum(GrpArgs a, float* xsum) {
+  const int ng = a.d / a.g;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.T * ng) return;
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)(i / ng) * a.d + (i % ng) * a.g);
+  float s = 0.f;
+  for (int c = 0; c < a.g / 8; ++c) {
+    const uint4 v = src[c];
+    s += bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) +
+         bf_lo(v.w) + bf_hi(v.w);
+  }
+  xsum[i] = s;
+}
+
+// 8 bf16 of an fp32 row as the hi and lo halves of an MFMA operand (k
+// inputs in natural order; zeros where `ok` is false)
+struct F8 {
+  float4 a, b;
+};
+__device__ __forceinline__ void split_hilo8(F8 f, bool ok, bf16x8_t& hi, bf16x8_t& lo) {
+  const float v[8] = {f.a.x, f.a.y, f.a.z, f.a.w, f.b.x, f.b.y, f.b.z, f.b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = ok ? v[2 * e] : 0.f, a1 = ok ? v[2 * e + 1] : 0.f;
+    const uint32_t h0 = f2bf(a0), h1 = f2bf(a1);
+    h[e] = h0 | (h1 << 16);
+    l[e] = f2bf(a0 - bf2f(h0)) | (f2bf(a1 - bf2f(h1)) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// Gate/up: unit (64-pair tile, 64 rows of gate and of up); wave w owns rows
+// 16 w .. 16 w + 15 of both over the tile's four 16-pair blocks, so each
+// int4 word is expanded once, straight from memory into registers, and
+// SwiGLU pairs gate and up in registers.  The activations go through LDS
+// (pair order, swizzled), two groups a step, double-buffered; the next
+// step's weights, scales and activations are loaded while the current one
+// is multiplied.  Within a group, lane quad j takes KS of its chunks, so
+// an MFMA never mixes groups.  Epilogue: the LoRA B t terms on MFMA (t as
+// bf16 hi + lo), h as bf16 hi/lo pairs through LDS to full-width stores,
+// and each wave's 16-row sums of h (hi + lo) for the down fold.
+constexpr int kPfRows = 64;  // gate and up rows per k_pf_gu workgroup
+template <int KS>
+__global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
+  constexpr int G = 32 * KS, CPG = G / 8, NGI = 2;  // inputs, chunks per group; groups a step
+  constexpr int CPB = 2 * CPG, STEP = 2 * G;         // 16-byte chunks, inputs a step
+  constexpr int XU = kPfTile * CPB / 256;            // activation chunks staged per thread
+  __shared__ __align__(16) uint4 xs[2][kPfTile * CPB];   // chunk c of pair m at CPB m + (c ^ m % CPB)
+  __shared__ __align__(16) float xsum_s[2][NGI][kPfTile];
+  __shared__ __align__(16) uint4 tlo[2][2][kPfTile][2];  // t of each pair: [gate, up][hi, lo]
+  const int nblk = a.I / kPfRows;
+  const int u = pf_unit();
+  const int li = u / nblk, blk = u % nblk;
+  if (li >= a.info[3]) return;
+  const int2 te = a.tiles64[li];
+  const int cnt = a.act_cnt[te.x], slot = a.act_slot[te.x], q0 = a.act_off[te.x];
+  if (slot < 0) return;  // reported by the scan; the down kernel writes zeros
+  const int t0 = te.y * kPfTile, mt = min(kPfTile, cnt - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int d = a.d, r = a.r, ng = d / G, nsteps = d / STEP;
+  const int row = blk * kPfRows + 16 * wave + n;  // this lane's weight row
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+  // staging duties: activation chunks (pairs past the tile repeat its last)
+  const uint16_t* xrow[XU];
+  int xdst[XU];
+#pragma unroll
+  for (int q = 0; q < XU; ++q) {
+    const int c = tid + 256 * q, m = c / CPB, cc = c % CPB;
+    xrow[q] = a.x + (size_t)a.pair_tok[q0 + t0 + min(m, mt - 1)] * d + 8 * cc;
+    xdst[q] = m * CPB + (cc ^ (m % CPB));
+  }
+  const int xstok = tid < kPfTile ? a.pair_tok[q0 + t0 + min(tid, mt - 1)] : 0;
+  // this lane's weight words: step s, k-step ks uses chunk (ks / KS) CPG + j KS + ks % KS
+  const uint32_t* wgp = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
+  const uint32_t* wup = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
+  const uint16_t* sgp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_s) + (size_t)row * ng;
+  const uint16_t* bgp = reinterpret_cast<const uint16_t*>(b + a.lay.gate_b) + (size_t)row * ng;
+  const uint16_t* sup = reinterpret_cast<const uint16_t*>(b + a.lay.up_s) + (size_t)row * ng;
+  const uint16_t* bup = reinterpret_cast<const uint16_t*>(b + a.lay.up_b) + (size_t)row * ng;
+  uint4 rx[XU];
+  float rxs[NGI];
+  // sc: gate s, gate b, up s, up b of the step's two groups, as loaded (bf16
+  // pairs, unpacked only where the fold uses them: work on a loaded value
+  // right after its load would wait for it there)
+  uint32_t wg[2 * KS], wu[2 * KS], sc[4];
+  auto load_x = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < XU; ++q) rx[q] = *reinterpret_cast<const uint4*>(xrow[q] + STEP * s);
+    if (tid < kPfTile)
+#pragma unroll
+      for (int gg = 0; gg < NGI; ++gg) rxs[gg] = a.xsum[(size_t)xstok * ng + s * NGI + gg];
+  };
+  auto load_w = [&](int s) {
+#pragma unroll
+    for (int ks = 0; ks < 2 * KS; ++ks) {
+      const int c = s * CPB + (ks / KS) * CPG + j * KS + ks % KS;
+      wg[ks] = wgp[c];
+      wu[ks] = wup[c];
+    }
+    sc[0] = *reinterpret_cast<const uint32_t*>(sgp + s * NGI);
+    sc[1] = *reinterpret_cast<const uint32_t*>(bgp + s * NGI);
+    sc[2] = *reinterpret_cast<const uint32_t*>(sup + s * NGI);
+    sc[3] = *reinterpret_cast<const uint32_t*>(bup + s * NGI);
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < XU; ++q) {
+      uint32_t o[4];
+      pair_perm8(rx[q].x, rx[q].y, rx[q].z, rx[q].w, o);
+      xs[buf][xdst[q]] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (tid < kPfTile)
+#pragma unroll
+      for (int gg = 0; gg < NGI; ++gg) xsum_s[buf][gg][tid] = rxs[gg];
+  };
+  // t of the tile's pairs (the LoRA A x launch), split hi/lo, rank-padded
+  if (r > 0 && tid < 2 * kPfTile) {
+    const int m = tid % kPfTile, p = tid / kPfTile;
+    const float* tp = a.t_in + ((size_t)a.pair_src[q0 + t0 + min(m, mt - 1)] * 2 + p) * r;
+    auto tk = [&](int k) { return k < r ? tp[k] : 0.f; };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const F8 f{make_float4(tk(8 * h), tk(8 * h + 1), tk(8 * h + 2), tk(8 * h + 3)),
+                 make_float4(tk(8 * h + 4), tk(8 * h + 5), tk(8 * h + 6), tk(8 * h + 7))};
+      bf16x8_t hi, lo;
+      split_hilo8(f, true, hi, lo);
+      tlo[p][0][m][h] = __builtin_bit_cast(uint4, hi);
+      tlo[p][1][m][h] = __builtin_bit_cast(uint4, lo);
+    }
+  }
+  load_x(0);
+  load_w(0);
+  store_x(0);
+  __syncthreads();
+  const Q4Consts kq = q4_consts();
+  f32x4_t acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    uint32_t cwg[2 * KS], cwu[2 * KS], csc[4];
+#pragma unroll
+    for (int ks = 0; ks < 2 * KS; ++ks) {
+      cwg[ks] = wg[ks];
+      cwu[ks] = wu[ks];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) csc[q] = sc[q];
+    if (s + 1 < nsteps) {
+      load_x(s + 1);
+      load_w(s + 1);
+    }
+    f32x4_t tmp[8];
+#pragma unroll
+    for (int ks = 0; ks < 2 * KS; ++ks) {
+      const int gg = ks / KS;
+      if (ks % KS == 0)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tmp[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int c = gg * CPG + j * KS + ks % KS;
+      const bf16x8_t bg = q4_operand_k(cwg[ks], kq), bu = q4_operand_k(cwu[ks], kq);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int m = 16 * tb + n;
+        const bf16x8_t xo = __builtin_bit_cast(bf16x8_t, xs[buf][m * CPB + (c ^ (m % CPB))]);
+        tmp[tb] = mfma16(xo, bg, tmp[tb]);
+        tmp[4 + tb] = mfma16(xo, bu, tmp[4 + tb]);
+      }
+      if (ks % KS == KS - 1) {
+        auto sv = [&](int q) { return gg == 0 ? bf_lo(csc[q]) : bf_hi(csc[q]); };
+        const float sg = sv(0), cg = sv(1) - 128.f * sg;
+        const float su = sv(2), cu = sv(3) - 128.f * su;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const float4 xv = *reinterpret_cast<const float4*>(&xsum_s[buf][gg][16 * tb + 4 * j]);
+          const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc[tb][v] += sg * tmp[tb][v] + cg * xa[v];
+            acc[4 + tb][v] += su * tmp[4 + tb][v] + cu * xa[v];
+          }
+        }
+      }
+    }
+    if (s + 1 < nsteps) store_x(buf ^ 1);
+    __syncthreads();
+  }
+  // LoRA B t: A = t of the pairs (ranks 8 j' .. as k, j' < 2), B = B rows
+  if (r > 0) {
+    bf16x8_t bl[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate)) +
+                          (size_t)row * r;
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 8 * j + 2 * e;
+        const uint32_t lo16 = (j < 2 && k < r) ? B[k] : 0u;
+        const uint32_t hi16 = (j < 2 && k + 1 < r) ? B[k + 1] : 0u;
+        w4[e] = lo16 | (hi16 << 16);
+      }
+      bl[p] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        f32x4_t lt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int m = 16 * tb + n;
+        uint4 t0v = tlo[p][0][m][j & 1], t1v = tlo[p][1][m][j & 1];
+        if (j >= 2) t0v = t1v = make_uint4(0, 0, 0, 0);  // ranks 16..31 of the k-step
+        const bf16x8_t th = __builtin_bit_cast(bf16x8_t, t0v);
+        const bf16x8_t tlw = __builtin_bit_cast(bf16x8_t, t1v);
+        lt = mfma16(th, bl[p], lt);
+        lt = mfma16(tlw, bl[p], lt);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[4 * p + tb][v] += a.scale * lt[v];
+      }
+  }
+  // SwiGLU; h hi/lo staged in LDS (the activation buffers are free now)
+  uint16_t* hst = reinterpret_cast<uint16_t*>(&xs[0][0]);  // [hi, lo][pair][64 rows]
+  const int hr = 16 * wave + n, pos = grp_pair_pos(hr);
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    float hv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * tb + 4 * j + v;
+      const float h = grp_silu(acc[tb][v]) * acc[4 + tb][v];
+      const uint32_t hi = f2bf(h), lo = f2bf(h - bf2f(hi));
+      hst[m * kPfRows + pos] = (uint16_t)hi;
+      hst[(kPfTile + m) * kPfRows + pos] = (uint16_t)lo;
+      hv[v] = row16_sum(bf2f(hi) + bf2f(lo));
+    }
+    if (n == 0)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * tb + 4 * j + v;
+        if (m < mt) a.hs[(size_t)(row / 16) * a.P + q0 + t0 + m] = hv[v];
+      }
+  }
+  __syncthreads();
+  // h to memory: 8 chunks of 8 per pair and half
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = tid + 256 * q, half = c >> 9, m = (c >> 3) & 63, cc = c & 7;
+    if (m < mt)
+      *reinterpret_cast<uint4*>((half ? a.hp_lo : a.hp_hi) + (size_t)(q0 + t0 + m) * a.I +
+                                blk * kPfRows + 8 * cc) =
+          *reinterpret_cast<const uint4*>(&hst[(half * kPfTile + m) * kPfRows + 8 * cc]);
+  }
+}
+
+// Down: unit (64-pair tile, 128 output rows); wave w owns two 16-row blocks
+// from 32 w over the four 16-pair blocks (h hi and lo, two
+// MFMAs per block and step), its int4 words straight into registers, h
+// through LDS (swizzled), 64 inputs a step, double-buffered; a group's
+// products are folded per group.  Wave w also forms A_down
+// h for pair block w (the same two MFMAs against the A_down rows in pair
+// order; no fold).  Epilogue: the LoRA-down term on MFMA (A_down h as bf16
+// hi + lo against the B_down rows), then each pair's row times its routing
+// weight, stored by unsorted pair.  A tile whose expert has no valid slot
+// stores zeros.
+// output rows per k_pf_down workgroup: 4 waves x 2 16-row blocks (four
+// blocks per wave need more registers than a wave has, and the compiler
+// then parks the staged h in scratch memory, behind a wait for its loads)
+__host__ __device__ constexpr int pf_out(int) { return 128; }
+template <int KS>
+__global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
+  constexpr int G = 32 * KS, NGD = 2 / KS;  // inputs per group; groups a step (64 inputs)
+  constexpr int CPB = 8;                     // 16-byte chunks a step
+  constexpr int HU = 2 * kPfTile * CPB / 256;
+  constexpr int kPfOut = pf_out(KS), RB = kPfOut / 64;  // rows per unit, 16-row blocks per wave
+  __shared__ __align__(16) uint4 hh[2][2][kPfTile * CPB];  // [buf][hi, lo], chunk c of pair m at 8 m + (c ^ m % 8)
+  __shared__ __align__(16) float hsum_s[2][NGD][kPfTile];
+  __shared__ __align__(16) uint4 ad[2][kTileRank * CPB];   // A_down rows (rank-padded), pair order
+  __shared__ __align__(16) float td_s[kPfTile][kTileRank + 4];
+  __shared__ int src_s[kPfTile];
+  __shared__ float pw_s[kPfTile];
+  const int nrb = a.d / kPfOut;
+  const int u = pf_unit();
+  const int li = u / nrb, rb = u % nrb;
+  if (li >= a.info[3]) return;
+  const int2 te = a.tiles64[li];
+  const int cnt = a.act_cnt[te.x], slot = a.act_slot[te.x], q0 = a.act_off[te.x];
+  const int t0 = te.y * kPfTile, mt = min(kPfTile, cnt - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int d = a.d, r = a.r, I = a.I, NC = I / 32, nsteps = I / 64, o0 = rb * kPfOut;
+  const int o = 16 * RB * wave + n;  // this lane's output rows in the unit: o + 16 rr
+  if (tid < kPfTile) {
+    const int q = q0 + t0 + min(tid, mt - 1);
+    src_s[tid] = a.pair_src[q];
+    pw_s[tid] = a.pair_w[q];
+  }
+  __syncthreads();
+  if (slot < 0) {
+    for (int e = tid; e < mt * kPfOut; e += 256)
+      a.ypair[(size_t)src_s[e / kPfOut] * d + o0 + e % kPfOut] = 0.f;
+    return;
+  }
+  const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+  const uint16_t* hrow[HU];
+  int hdst[HU], hhalf[HU];
+#pragma unroll
+  for (int q = 0; q < HU; ++q) {
+    const int c = tid + 256 * q, half = c / (kPfTile * CPB), rem = c % (kPfTile * CPB);
+    const int m = rem / CPB, cc = rem % CPB;
+    hhalf[q] = half;
+    hrow[q] = (half ? a.hp_lo : a.hp_hi) + (size_t)(q0 + t0 + min(m, mt - 1)) * I + 8 * cc;
+    hdst[q] = m * CPB + (cc ^ (m % 8));
+  }
+  const int hsm = q0 + t0 + min(tid, mt - 1);  // group sums: thread < 64 (block-major sums)
+  const int arr = tid / CPB, acc8 = tid % CPB; // A_down chunks: thread < 16 CPB
+  const uint16_t* adsrc = reinterpret_cast<const uint16_t*>(
+      b + (r > 0 ? a.lay.a_down : a.lay.down_q)) + (size_t)min(arr, max(r - 1, 0)) * I + 8 * acc8;
+  // this lane's weight words: word j of row o0 + o + 16 rr in each 32-input
+  // tile (64-row tile block (o0 + o) / 64, row (o0 + o) % 64 + 16 rr); its
+  // rows' scales
+  const uint32_t* dq = reinterpret_cast<const uint32_t*>(b + a.lay.down_q) +
+                       (((size_t)((o0 + o) / 64) * NC) * 64 + (o0 + o) % 64) * 4 + j;
+  const uint16_t* dsp = reinterpret_cast<const uint16_t*>(b + a.lay.down_s) + o0 + o;
+  const uint16_t* dbp = reinterpret_cast<const uint16_t*>(b + a.lay.down_b) + o0 + o;
+  // one step's loads, held in registers until the step before has been
+  // multiplied (no arithmetic on them before then: it would wait for them)
+  // (four separately named registers: as an array the compiler kept them
+  // in scratch memory)
+  static_assert(HU == 4, "four staged h chunks per thread");
+  uint4 sh0, sh1, sh2, sh3, sad = make_uint4(0, 0, 0, 0);
+  float shs[NGD][G / 16];
+  uint32_t sw[RB][2], ssc[RB][2][NGD];
+#pragma unroll
+  for (int gg = 0; gg < NGD; ++gg)
+#pragma unroll
+    for (int h2 = 0; h2 < G / 16; ++h2) shs[gg][h2] = 0.f;
+  const uint16_t *hr0 = hrow[0], *hr1 = hrow[1], *hr2 = hrow[2], *hr3 = hrow[3];
+  uint4* hd0 = &hh[0][hhalf[0]][hdst[0]];
+  uint4* hd1 = &hh[0][hhalf[1]][hdst[1]];
+  uint4* hd2 = &hh[0][hhalf[2]][hdst[2]];
+  uint4* hd3 = &hh[0][hhalf[3]][hdst[3]];
+  constexpr int kBufStride = 2 * kPfTile * CPB;  // uint4 per h buffer
+#define E0_PF_DOWN_LOAD(S)                                                                  \
+  {                                                                                         \
+    const int s_ = (S);                                                                     \
+    sh0 = *reinterpret_cast<const uint4*>(hr0 + 64 * s_);                                   \
+    sh1 = *reinterpret_cast<const uint4*>(hr1 + 64 * s_);                                   \
+    sh2 = *reinterpret_cast<const uint4*>(hr2 + 64 * s_);                                   \
+    sh3 = *reinterpret_cast<const uint4*>(hr3 + 64 * s_);                                   \
+    if (tid < kPfTile)                                                                      \
+      _Pragma("unroll") for (int gg = 0; gg < NGD; ++gg)                                   \
+          _Pragma("unroll") for (int h2 = 0; h2 < G / 16; ++h2) shs[gg][h2] =              \
+              a.hs[(size_t)((s_ * 64 + gg * G) / 16 + h2) * a.P + hsm];                     \
+    if (r > 0 && tid < kTileRank * CPB) sad = *reinterpret_cast<const uint4*>(adsrc + 64 * s_); \
+    _Pragma("unroll") for (int rr = 0; rr < RB; ++rr) {                                    \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) sw[rr][ks] =                        \
+          dq[(size_t)(2 * s_ + ks) * 64 * 4 + 16 * 4 * rr];                                 \
+      _Pragma("unroll") for (int gg = 0; gg < NGD; ++gg) {                                 \
+        const int gi = (s_ * 64) / G + gg;                                                  \
+        ssc[rr][0][gg] = dsp[(size_t)gi * d + 16 * rr];                                     \
+        ssc[rr][1][gg] = dbp[(size_t)gi * d + 16 * rr];                                     \
+      }                                                                                     \
+    }                                                                                       \
+  }
+#define E0_PF_DOWN_STORE(BUF)                                                               \
+  {                                                                                         \
+    const int b_ = (BUF);                                                                   \
+    hd0[b_ * kBufStride] = sh0;                                                             \
+    hd1[b_ * kBufStride] = sh1;                                                             \
+    hd2[b_ * kBufStride] = sh2;                                                             \
+    hd3[b_ * kBufStride] = sh3;                                                             \
+    if (tid < kPfTile)                                                                      \
+      _Pragma("unroll") for (int gg = 0; gg < NGD; ++gg) {                                 \
+        float sum = 0.f;                                                                    \
+        _Pragma("unroll") for (int h2 = 0; h2 < G / 16; ++h2) sum += shs[gg][h2];           \
+        hsum_s[b_][gg][tid] = sum;                                                          \
+      }                                                                                     \
+    if (r > 0 && tid < kTileRank * CPB) {                                                   \
+      uint32_t w4[4];                                                                       \
+      pair_perm8(sad.x, sad.y, sad.z, sad.w, w4);                                           \
+      ad[b_][tid] = arr < r ? make_uint4(w4[0], w4[1], w4[2], w4[3]) : make_uint4(0, 0, 0, 0); \
+    }                                                                                       \
+  }
+  E0_PF_DOWN_LOAD(0);
+  E0_PF_DOWN_STORE(0);
+  __syncthreads();
+  const Q4Consts kq = q4_consts();
+  f32x4_t acc[4 * RB], tda = f32x4_t{0.f, 0.f, 0.f, 0.f};  // acc[4 rr + pb]
+#pragma unroll
+  for (int q = 0; q < 4 * RB; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    uint32_t cwv[RB][2], csc[RB][2][NGD];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) cwv[rr][ks] = sw[rr][ks];
+#pragma unroll
+      for (int gg = 0; gg < NGD; ++gg) {
+        csc[rr][0][gg] = ssc[rr][0][gg];
+        csc[rr][1][gg] = ssc[rr][1][gg];
+      }
+    }
+    if (s + 1 < nsteps) E0_PF_DOWN_LOAD(s + 1);
+#pragma unroll
+    for (int gg = 0; gg < NGD; ++gg) {
+      // the group's k-steps (32 inputs each), two row blocks at a time
+#pragma unroll
+      for (int half = 0; half < RB / 2; ++half) {
+        f32x4_t tmp[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tmp[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kg = 0; kg < KS; ++kg) {
+          const int ks = gg * KS + kg, c = 4 * ks + j;
+          const bf16x8_t w0 = q4_operand_k(cwv[2 * half][ks], kq);
+          const bf16x8_t w1 = q4_operand_k(cwv[2 * half + 1][ks], kq);
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) {
+            const int m = 16 * pb + n, sw = m * CPB + (c ^ (m % 8));
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, hh[buf][0][sw]);
+            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, hh[buf][1][sw]);
+            tmp[pb] = mfma16(ah, w0, tmp[pb]);
+            tmp[pb] = mfma16(al, w0, tmp[pb]);
+            tmp[4 + pb] = mfma16(ah, w1, tmp[4 + pb]);
+            tmp[4 + pb] = mfma16(al, w1, tmp[4 + pb]);
+            if (half == 0 && pb == wave && r > 0) {
+              const bf16x8_t ao = __builtin_bit_cast(bf16x8_t, ad[buf][n * CPB + c]);
+              tda = mfma16(ah, ao, tda);
+              tda = mfma16(al, ao, tda);
+            }
+          }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int rr = 2 * half + h2;
+          const float sd = bf2f(csc[rr][0][gg]), cd = bf2f(csc[rr][1][gg]) - 128.f * sd;
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) {
+            const float4 hv = *reinterpret_cast<const float4*>(&hsum_s[buf][gg][16 * pb + 4 * j]);
+            const float ha[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[4 * rr + pb][v] += sd * tmp[4 * h2 + pb][v] + cd * ha[v];
+          }
+        }
+      }
+    }
+    if (s + 1 < nsteps) E0_PF_DOWN_STORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef E0_PF_DOWN_LOAD
+#undef E0_PF_DOWN_STORE
+  // LoRA-down: A = A_down h of the pairs (hi + lo), B = B_down rows
+  if (r > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) td_s[16 * wave + 4 * j + v][n] = tda[v];
+    __syncthreads();
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      bf16x8_t th, tl;
+      const float* tdr = &td_s[16 * pb + n][8 * (j & 1)];
+      split_hilo8(F8{*reinterpret_cast<const float4*>(tdr), *reinterpret_cast<const float4*>(tdr + 4)},
+                  j < 2, th, tl);
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const uint16_t* B =
+            reinterpret_cast<const uint16_t*>(b + a.lay.b_down) + (size_t)(o0 + o + 16 * rr) * r;
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 8 * j + 2 * e;
+          const uint32_t lo16 = (j < 2 && k < r) ? B[k] : 0u;
+          const uint32_t hi16 = (j < 2 && k + 1 < r) ? B[k + 1] : 0u;
+          w4[e] = lo16 | (hi16 << 16);
+        }
+        const bf16x8_t bd = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        f32x4_t lt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lt = mfma16(th, bd, lt);
+        lt = mfma16(tl, bd, lt);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[4 * rr + pb][v] += a.scale * lt[v];
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * pb + 4 * j + v;
+        if (m < mt)
+          a.ypair[(size_t)src_s[m] * d + o0 + o + 16 * rr] = pw_s[m] * acc[4 * rr + pb][v];
+      }
+}
+
+// y of each token: its kept pairs' rows added in k order, rounded once
+__global__ __launch_bounds__(256) void k_pf_combine(GrpArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // 4 outputs each
+  const int d4 = a.d / 4;
+  if (i >= a.T * d4) return;
+  const int t = i / d4, o = 4 * (i % d4);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < a.K; ++k) {
+    const int p = t * a.K + k;
+    if (a.keep[p] < 0) continue;
+    const float4 v = *reinterpret_cast<const float4*>(a.ypair + (size_t)p * a.d + o);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  *reinterpret_cast<uint2*>(a.y + (size_t)t * a.d + o) =
+      make_uint2(f2bf(s.x) | (f2bf(s.y) << 16), f2bf(s.z) | (f2bf(s.w) << 16));
 }
 
 // ------------------------------------------------------------- host side
@@ -1322,11 +1862,12 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
 // ------------------------------------------------------------ prefill host
 namespace e0 {
 struct PfWs {
-  size_t err, info, cnt, fill, keep, keep_w, tiles, act_e, act_off, act_cnt, act_slot, pair_tok,
-      pair_src, pair_w, t_in, hp_hi, hp_lo, hs, tdown, acc, total;
+  size_t err, info, cnt, fill, keep, keep_w, tiles, tiles64, act_e, act_off, act_cnt, act_slot,
+      pair_tok, pair_src, pair_w, t_in, hp_hi, hp_lo, hs, xsum, ypair, total;
 };
-// an upper bound of the tile list: sum over experts of ceil(count / 16)
+// upper bounds of the tile lists: sum over experts of ceil(count / tile)
 static int pf_tiles_max(int P, int E) { return (P + kTileTok - 1) / kTileTok + (E < P ? E : P); }
+static int pf_tiles64_max(int P, int E) { return (P + kPfTile - 1) / kPfTile + (E < P ? E : P); }
 static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
   PfWs L{};
   const size_t T = max_tokens, d = s->d_model, E = s->n_experts, I = s->d_inter;
@@ -1344,6 +1885,7 @@ static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
   L.keep = take(4 * P);
   L.keep_w = take(4 * P);
   L.tiles = take(8 * (size_t)pf_tiles_max((int)P, (int)E));
+  L.tiles64 = take(8 * (size_t)pf_tiles64_max((int)P, (int)E));
   L.act_e = take(4 * E);
   L.act_off = take(4 * E);
   L.act_cnt = take(4 * E);
@@ -1355,20 +1897,19 @@ static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
   L.hp_hi = take(2 * P * I);
   L.hp_lo = take(2 * P * I);
   L.hs = take(4 * P * (I / 16));
-  L.tdown = take(8 * P * r);
-  L.acc = take(8 * T * d);
+  L.xsum = take(4 * T * (d / s->group_size));
+  L.ypair = take(4 * P * d);
   L.total = off;
   return L;
 }
-// the token-tile kernels' shapes (every prefill unit runs on them)
+// the prefill kernels' shapes: the LoRA A x tiles (d / 4 a multiple of 32),
+// the gate/up units (32 rows) and the down units (64 output rows) over
+// whole groups of 32 or 64 inputs
 static bool pf_shape_ok(const edge0_moe_shape* s) {
   if (!grouped_shape_ok(s)) return false;
   const int d = s->d_model, g = s->group_size, I = s->d_inter, r = s->lora_rank;
-  const int gw = d / (4 * g), nw = I / 32;
-  return (g == 32 || g == 64) && d <= 2048 && d % (8 * g) == 0 &&
-         (gw == 2 || gw == 4 || gw == 8 || gw == 16) && I % 32 == 0 &&
-         (nw == 4 || nw == 8 || nw == 12 || nw == 16 || nw == 24 || nw == 32) && r <= kTileRank &&
-         r % 2 == 0;
+  return (g == 32 || g == 64) && d <= 2048 && d % 128 == 0 && d % pf_out(g / 32) == 0 &&
+         I % kPfRows == 0 && I % 64 == 0 && r <= kTileRank;
 }
 }  // namespace e0
 
@@ -1423,31 +1964,47 @@ extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_
   a.hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
   a.hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
   a.hs = reinterpret_cast<float*>(ws + L.hs);
-  a.tdown = reinterpret_cast<unsigned long long*>(ws + L.tdown);
-  a.acc = reinterpret_cast<unsigned long long*>(ws + L.acc);
   a.tiles = reinterpret_cast<const int2*>(ws + L.tiles);
+  a.tiles64 = reinterpret_cast<const int2*>(ws + L.tiles64);
+  a.xsum = reinterpret_cast<const float*>(ws + L.xsum);
+  a.ypair = reinterpret_cast<float*>(ws + L.ypair);
+  a.keep = reinterpret_cast<const int32_t*>(ws + L.keep);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
   int32_t* fill = reinterpret_cast<int32_t*>(ws + L.fill);
   int32_t* keep = reinterpret_cast<int32_t*>(ws + L.keep);
   float* keep_w = reinterpret_cast<float*>(ws + L.keep_w);
   int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
+  int2* tiles64 = reinterpret_cast<int2*>(ws + L.tiles64);
   const int pg = (a.P + 255) / 256;
   k_pf_count<<<pg, 256, 0, stream>>>(a, cnt, keep, keep_w);
   E0_CHECK_LAUNCH();
-  k_pf_scan<<<1, 1024, 0, stream>>>(a, cnt, fill, tiles);
+  k_pf_scan<<<1, 1024, 0, stream>>>(a, cnt, fill, tiles, tiles64);
   E0_CHECK_LAUNCH();
   k_pf_scatter<<<pg, 256, 0, stream>>>(a, keep, keep_w, fill);
   E0_CHECK_LAUNCH();
-  const int units = pf_tiles_max(a.P, a.E);
+  const int nxs = a.T * (a.d / a.g);
+  k_pf_xsum<<<(nxs + 255) / 256, 256, 0, stream>>>(a, reinterpret_cast<float*>(ws + L.xsum));
+  E0_CHECK_LAUNCH();
   if (a.r > 0) {
-    k_pf_lora_in<<<units, 256, 0, stream>>>(a);
+    k_pf_lora_in<<<pf_tiles_max(a.P, a.E), 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
   }
-  int rc = launch_grp_tiles_gu(a, 1, kTileTok, units, stream);
-  if (rc == EDGE0_OK) rc = launch_grp_tiles_down(a, 1, kTileTok, units, stream);
-  if (rc != EDGE0_OK) return rc;
-  const int n_out = a.T * a.d;
-  k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);
+  // the GEMM units: every (64-pair tile, row block), the grid a multiple of
+  // 8 for the XCD-aware order (units past the tile list return)
+  const int tiles_max = pf_tiles64_max(a.P, a.E);
+  const int g_gu = (tiles_max * (a.I / kPfRows) + 7) / 8 * 8;
+  const int g_dn = (tiles_max * (a.d / pf_out(a.g / 32)) + 7) / 8 * 8;
+  if (a.g == 64) {
+    k_pf_gu<2><<<g_gu, 256, 0, stream>>>(a);
+    E0_CHECK_LAUNCH();
+    k_pf_down<2><<<g_dn, 256, 0, stream>>>(a);
+  } else {
+    k_pf_gu<1><<<g_gu, 256, 0, stream>>>(a);
+    E0_CHECK_LAUNCH();
+    k_pf_down<1><<<g_dn, 256, 0, stream>>>(a);
+  }
+  E0_CHECK_LAUNCH();
+  k_pf_combine<<<(a.T * (a.d / 4) + 255) / 256, 256, 0, stream>>>(a);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
 }
