@@ -69,10 +69,7 @@ struct GrpArgs {
   float* hs;                   // [P][I/16]
   unsigned long long* tdown;   // [P][r] A_down h, fixed point
   unsigned long long* acc;     // [T][d] y, fixed point
-  // prefill: the list of (active expert, 16-pair tile) for the LoRA A x,
-  // info[2] entries
-  const int2* tiles;
-  // prefill's GEMM tiles: the list of (active expert, 64-pair tile),
+  // prefill: the list of (active expert, 64-pair tile),
   // info[3] entries; each token's activation sum per input group [T][d/g];
   // each pair's weighted output row, by unsorted pair [P][d] (fp32); the
   // kept expert of each unsorted pair, or -1 (dropped repeat, invalid id)
@@ -953,65 +950,73 @@ __global__ __launch_bounds__(256) void k_grp_out(GrpArgs a) {
 constexpr int kPfMaxTokens = 4096;
 
 // pass 1: per pair, an id repeated within its token is dropped (its first
-// listing keeps the weights summed in k order); kept pairs counted per expert
-__global__ __launch_bounds__(256) void k_pf_count(GrpArgs a, int32_t* cnt, int32_t* keep,
-                                                  float* keep_w) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= a.P) return;
-  const int K = a.K, k0 = p - p % K;
-  int e = a.ids[p];
-  float w = a.w[p];
-  if (e < 0 || e >= a.E) {
-    set_error(a.err, EDGE0_ERANGE);
-    e = -1;
-  } else {
-    bool dup = false;
-    for (int q = k0; q < p; ++q) dup |= a.ids[q] == e;
-    for (int q = p + 1; q < k0 + K; ++q)
-      if (a.ids[q] == e) w += a.w[q];
-    if (dup) e = -1;
+// listing keeps the weights summed in k order); kept pairs counted per
+// expert, in LDS per workgroup of kPfPairsPerWg pairs first (the global
+// counters then take at most E additions per workgroup: a few thousand
+// pairs adding one by one into E counters serialise on them)
+constexpr int kPfPairsPerWg = 4096;
+__global__ __launch_bounds__(1024) void k_pf_count(GrpArgs a, int32_t* cnt, int32_t* keep,
+                                                   float* keep_w) {
+  __shared__ int hist[1024];  // E <= 1024
+  for (int e = threadIdx.x; e < a.E; e += 1024) hist[e] = 0;
+  __syncthreads();
+  const int K = a.K;
+  for (int p = blockIdx.x * kPfPairsPerWg + threadIdx.x;
+       p < min(a.P, (blockIdx.x + 1) * kPfPairsPerWg); p += 1024) {
+    const int k0 = p - p % K;
+    int e = a.ids[p];
+    float w = a.w[p];
+    if (e < 0 || e >= a.E) {
+      set_error(a.err, EDGE0_ERANGE);
+      e = -1;
+    } else {
+      bool dup = false;
+      for (int q = k0; q < p; ++q) dup |= a.ids[q] == e;
+      for (int q = p + 1; q < k0 + K; ++q)
+        if (a.ids[q] == e) w += a.w[q];
+      if (dup) e = -1;
+    }
+    keep[p] = e;
+    keep_w[p] = w;
+    if (e >= 0) atomicAdd(&hist[e], 1);
   }
-  keep[p] = e;
-  keep_w[p] = w;
-  if (e >= 0) atomicAdd(cnt + e, 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += 1024)
+    if (hist[e] != 0) atomicAdd(cnt + e, hist[e]);
 }
 
 // pass 2 (one workgroup, one expert per thread): exclusive scans of the
-// counts, the active flags and the tiles per expert (16-pair tiles for the
-// LoRA A x, 64-pair tiles for the gate/up and down GEMMs); the active list,
-// each expert's first free position, both tile lists; the counts cleared
+// counts, the active flags and the 64-pair tiles per expert; the active
+// list, each expert's first free position, the tile list; the counts
+// cleared
 constexpr int kPfTile = 64;  // pairs per prefill GEMM tile (4 waves x 16)
 __global__ __launch_bounds__(1024) void k_pf_scan(GrpArgs a, int32_t* cnt, int32_t* fill,
-                                                  int2* tiles, int2* tiles64) {
-  __shared__ int wtot[4][16];
+                                                  int2* tiles64) {
+  __shared__ int wtot[3][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   const int c = tid < E ? cnt[tid] : 0;
   const int f = c > 0 ? 1 : 0;
-  const int nt = (c + kTileTok - 1) / kTileTok, n64 = (c + kPfTile - 1) / kPfTile;
-  const int ic = wave_incl_scan(c), iff = wave_incl_scan(f), it = wave_incl_scan(nt),
-            i64 = wave_incl_scan(n64);
+  const int n64 = (c + kPfTile - 1) / kPfTile;
+  const int ic = wave_incl_scan(c), iff = wave_incl_scan(f), i64 = wave_incl_scan(n64);
   if (lane == 63) {
     wtot[0][wave] = ic;
     wtot[1][wave] = iff;
-    wtot[2][wave] = it;
-    wtot[3][wave] = i64;
+    wtot[2][wave] = i64;
   }
   __syncthreads();
-  int bc = 0, bf = 0, bt = 0, b64 = 0, tc = 0, tf = 0, tt = 0, t64 = 0;
+  int bc = 0, bf = 0, b64 = 0, tc = 0, tf = 0, t64 = 0;
   for (int v = 0; v < 16; ++v) {
     if (v < wave) {
       bc += wtot[0][v];
       bf += wtot[1][v];
-      bt += wtot[2][v];
-      b64 += wtot[3][v];
+      b64 += wtot[2][v];
     }
     tc += wtot[0][v];
     tf += wtot[1][v];
-    tt += wtot[2][v];
-    t64 += wtot[3][v];
+    t64 += wtot[2][v];
   }
-  const int xc = bc + ic - c, xf = bf + iff - f, xt = bt + it - nt, x64 = b64 + i64 - n64;
+  const int xc = bc + ic - c, xf = bf + iff - f, x64 = b64 + i64 - n64;
   if (tid < E) {
     fill[tid] = xc;
     cnt[tid] = 0;
@@ -1023,51 +1028,71 @@ __global__ __launch_bounds__(1024) void k_pf_scan(GrpArgs a, int32_t* cnt, int32
       a.act_cnt[xf] = c;
       a.act_slot[xf] = ok ? slot : -1;
       if (!ok) set_error(a.err, EDGE0_ERANGE);
-      for (int i = 0; i < nt; ++i) tiles[xt + i] = make_int2(xf, i);
       for (int i = 0; i < n64; ++i) tiles64[x64 + i] = make_int2(xf, i);
     }
   }
   if (tid == 0) {
     a.info[0] = tf;
     a.info[1] = tc;
-    a.info[2] = tt;
     a.info[3] = t64;
   }
 }
 
-// pass 3: each kept pair to the next free position of its expert's run
-__global__ __launch_bounds__(256) void k_pf_scatter(GrpArgs a, const int32_t* keep,
-                                                    const float* keep_w, int32_t* fill) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= a.P) return;
-  const int e = keep[p];
-  if (e < 0) return;
-  const int dst = atomicAdd(fill + e, 1);
-  a.pair_tok[dst] = p / a.K;
-  a.pair_src[dst] = p;
-  a.pair_w[dst] = keep_w[p];
+// pass 3: each kept pair to a free position of its expert's run: the
+// workgroup ranks its pairs per expert in LDS and reserves one block per
+// expert (the order within a run is arrival order; results do not depend
+// on it)
+__global__ __launch_bounds__(1024) void k_pf_scatter(GrpArgs a, const int32_t* keep,
+                                                     const float* keep_w, int32_t* fill) {
+  __shared__ int lcnt[1024], lbase[1024];  // E <= 1024
+  constexpr int PPT = kPfPairsPerWg / 1024;
+  for (int e = threadIdx.x; e < a.E; e += 1024) lcnt[e] = 0;
+  __syncthreads();
+  int ev[PPT], rank[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = blockIdx.x * kPfPairsPerWg + threadIdx.x + 1024 * i;
+    ev[i] = p < a.P ? keep[p] : -1;
+    rank[i] = ev[i] >= 0 ? atomicAdd(&lcnt[ev[i]], 1) : 0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += 1024)
+    if (lcnt[e] != 0) lbase[e] = atomicAdd(fill + e, lcnt[e]);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    if (ev[i] < 0) continue;
+    const int p = blockIdx.x * kPfPairsPerWg + threadIdx.x + 1024 * i;
+    const int dst = lbase[ev[i]] + rank[i];
+    a.pair_tok[dst] = p / a.K;
+    a.pair_src[dst] = p;
+    a.pair_w[dst] = keep_w[p];
+  }
 }
 
-// LoRA A x of a tile's pairs, one workgroup per tile-list entry: the tile's
-// tokens (A operand, rows = tokens) against the expert's 2r LoRA A rows (B
-// operand; row q < r is A_gate's row q, then A_up's), bf16 MFMA 16x16x32
-// in one or two 16-row n-tiles; the 4 waves take quarters of d and their
-// partials are summed in LDS in wave order.  Both operands carry the same
-// 8 inputs per lane, in their natural order.
+// LoRA A x of a 64-pair tile, one workgroup per entry of the tile list: the
+// tile's tokens (A operand, rows = tokens, four 16-row blocks) against the
+// expert's 2r LoRA A rows (B operand; row q < r is A_gate's row q, then
+// A_up's), bf16 MFMA 16x16x32 in one or two 16-row n-tiles, each step's B
+// fragments loaded once for the four blocks; the 4 waves take quarters of
+// d and their partials are summed in LDS in wave order.  Both operands
+// carry the same 8 inputs per lane, in their natural order.
 __global__ __launch_bounds__(256) void k_pf_lora_in(GrpArgs a) {
-  __shared__ float part[4][kTileTok][2 * kTileRank];
+  __shared__ float part[4][kPfTile][2 * kTileRank];
   const int li = blockIdx.x;
-  if (li >= a.info[2]) return;
-  const int2 te = a.tiles[li];
+  if (li >= a.info[3]) return;
+  const int2 te = a.tiles64[li];
   const int cnt = a.act_cnt[te.x], slot = a.act_slot[te.x], q0 = a.act_off[te.x];
-  if (slot < 0) return;  // reported by the scan; the tile kernels skip it too
-  const int t0 = te.y * kTileTok, mt = min(kTileTok, cnt - t0);
+  if (slot < 0) return;  // reported by the scan; the GEMM kernels skip it too
+  const int t0 = te.y * kPfTile, mt = min(kPfTile, cnt - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int r = a.r, d = a.d;
   const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
-  const int tok = a.pair_tok[q0 + t0 + min(n, mt - 1)];  // past the tile: its last token again
-  const uint16_t* xr = a.x + (size_t)tok * d;
+  const uint16_t* xr[4];  // this lane's token in each 16-row block (past the tile: its last)
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+    xr[tb] = a.x + (size_t)a.pair_tok[q0 + t0 + min(16 * tb + n, mt - 1)] * d;
   const int q1 = n, q2 = 16 + n;  // this lane's B rows in the two n-tiles
   const uint16_t* w1 = reinterpret_cast<const uint16_t*>(b + (q1 < r ? a.lay.a_gate : a.lay.a_up)) +
                        (size_t)(q1 % r) * d;
@@ -1075,24 +1100,30 @@ __global__ __launch_bounds__(256) void k_pf_lora_in(GrpArgs a) {
                            b + (q2 < 2 * r ? (q2 < r ? a.lay.a_gate : a.lay.a_up) : a.lay.a_gate)) +
                        (size_t)(q2 < 2 * r ? q2 % r : 0) * d;
   const bool two = 2 * r > 16;
-  f32x4_t c1 = {0.f, 0.f, 0.f, 0.f}, c2 = c1;
+  f32x4_t c1[4], c2[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) c1[tb] = c2[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int kq = d / 4;
   for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 32) {
-    const bf16x8_t xo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr + k0 + 8 * j));
     const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w1 + k0 + 8 * j));
-    c1 = mfma16(xo, b1, c1);
-    if (two) {
-      const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w2 + k0 + 8 * j));
-      c2 = mfma16(xo, b2, c2);
+    const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w2 + k0 + 8 * j));
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const bf16x8_t xo =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xr[tb] + k0 + 8 * j));
+      c1[tb] = mfma16(xo, b1, c1[tb]);
+      if (two) c2[tb] = mfma16(xo, b2, c2[tb]);
     }
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    part[wave][4 * j + v][q1] = c1[v];
-    part[wave][4 * j + v][q2] = two ? c2[v] : 0.f;
-  }
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      part[wave][16 * tb + 4 * j + v][q1] = c1[tb][v];
+      part[wave][16 * tb + 4 * j + v][q2] = two ? c2[tb][v] : 0.f;
+    }
   __syncthreads();
-  for (int e = tid; e < kTileTok * 2 * r; e += 256) {
+  for (int e = tid; e < kPfTile * 2 * r; e += 256) {
     const int m = e / (2 * r), q = e % (2 * r);
     if (m < mt) {
       const float t = part[0][m][q] + part[1][m][q] + part[2][m][q] + part[3][m][q];
@@ -1862,11 +1893,10 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
 // ------------------------------------------------------------ prefill host
 namespace e0 {
 struct PfWs {
-  size_t err, info, cnt, fill, keep, keep_w, tiles, tiles64, act_e, act_off, act_cnt, act_slot,
+  size_t err, info, cnt, fill, keep, keep_w, tiles64, act_e, act_off, act_cnt, act_slot,
       pair_tok, pair_src, pair_w, t_in, hp_hi, hp_lo, hs, xsum, ypair, total;
 };
-// upper bounds of the tile lists: sum over experts of ceil(count / tile)
-static int pf_tiles_max(int P, int E) { return (P + kTileTok - 1) / kTileTok + (E < P ? E : P); }
+// an upper bound of the tile list: sum over experts of ceil(count / 64)
 static int pf_tiles64_max(int P, int E) { return (P + kPfTile - 1) / kPfTile + (E < P ? E : P); }
 static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
   PfWs L{};
@@ -1884,7 +1914,6 @@ static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
   L.fill = take(4 * E);
   L.keep = take(4 * P);
   L.keep_w = take(4 * P);
-  L.tiles = take(8 * (size_t)pf_tiles_max((int)P, (int)E));
   L.tiles64 = take(8 * (size_t)pf_tiles64_max((int)P, (int)E));
   L.act_e = take(4 * E);
   L.act_off = take(4 * E);
@@ -1964,7 +1993,6 @@ extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_
   a.hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
   a.hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
   a.hs = reinterpret_cast<float*>(ws + L.hs);
-  a.tiles = reinterpret_cast<const int2*>(ws + L.tiles);
   a.tiles64 = reinterpret_cast<const int2*>(ws + L.tiles64);
   a.xsum = reinterpret_cast<const float*>(ws + L.xsum);
   a.ypair = reinterpret_cast<float*>(ws + L.ypair);
@@ -1973,20 +2001,19 @@ extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_
   int32_t* fill = reinterpret_cast<int32_t*>(ws + L.fill);
   int32_t* keep = reinterpret_cast<int32_t*>(ws + L.keep);
   float* keep_w = reinterpret_cast<float*>(ws + L.keep_w);
-  int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
   int2* tiles64 = reinterpret_cast<int2*>(ws + L.tiles64);
-  const int pg = (a.P + 255) / 256;
-  k_pf_count<<<pg, 256, 0, stream>>>(a, cnt, keep, keep_w);
+  const int pg = (a.P + kPfPairsPerWg - 1) / kPfPairsPerWg;
+  k_pf_count<<<pg, 1024, 0, stream>>>(a, cnt, keep, keep_w);
   E0_CHECK_LAUNCH();
-  k_pf_scan<<<1, 1024, 0, stream>>>(a, cnt, fill, tiles, tiles64);
+  k_pf_scan<<<1, 1024, 0, stream>>>(a, cnt, fill, tiles64);
   E0_CHECK_LAUNCH();
-  k_pf_scatter<<<pg, 256, 0, stream>>>(a, keep, keep_w, fill);
+  k_pf_scatter<<<pg, 1024, 0, stream>>>(a, keep, keep_w, fill);
   E0_CHECK_LAUNCH();
   const int nxs = a.T * (a.d / a.g);
   k_pf_xsum<<<(nxs + 255) / 256, 256, 0, stream>>>(a, reinterpret_cast<float*>(ws + L.xsum));
   E0_CHECK_LAUNCH();
   if (a.r > 0) {
-    k_pf_lora_in<<<pf_tiles_max(a.P, a.E), 256, 0, stream>>>(a);
+    k_pf_lora_in<<<pf_tiles64_max(a.P, a.E), 256, 0, stream>>>(a);
     E0_CHECK_LAUNCH();
   }
   // the GEMM units: every (64-pair tile, row block), the grid a multiple of
