@@ -617,7 +617,7 @@ def row_prefill(args, log, inst):
            "config": {"workload": "one Qwen3-MoE-shaped layer, 512 / 2048 / 4096 tokens per call, "
                                   f"K=8, Zipf(1.1) routing, {n_inst} rotated layer instances",
                       "timing": "median of 5 runs"},
-           "roofline": {"kernel": "edge0_moe_prefill at 4096 tokens (bf16 MFMA token tiles)",
+           "roofline": {"kernel": "edge0_moe_prefill at 4096 tokens (LDS-staged int4 GEMMs on bf16 MFMA over 64-pair tiles)",
                         "bound": "mfma", "achieved": best["tflops"], "peak": 2500.0,
                         "unit": "TFLOP/s", "frac": round(best["tflops"] / 2500.0, 4),
                         "traffic": None, "avg_launch_us": best["us_per_call"]},
