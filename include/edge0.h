@@ -329,26 +329,44 @@ int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_slot_pool* po
  * there is nothing to predict).  The result is edge0_moe_grouped's, token by
  * token (an id repeated within a token's routing is kept once, its weights
  * summed in k order), for up to 4096 tokens per call: the (token, k) pairs
- * are bucketed by expert over many workgroups, each expert's tokens run in
- * tiles of up to 16 on bf16 MFMA (int4 weights as exact 128 + q), each
- * tile's LoRA A x on MFMA too, and every token's weighted rows are added in
- * fixed point (calls are bit-reproducible).
+ * are bucketed by expert over many workgroups into tiles of up to 64 pairs
+ * of one expert, which run through LDS-staged GEMMs on bf16 MFMA (int4
+ * weights as exact 128 + q, each group's affine folded in fp32, the LoRA
+ * terms on MFMA with t as bf16 hi + lo); each pair's weighted row is stored
+ * and every token's K rows are added in k order (calls are
+ * bit-reproducible).
  *   slot_table, ids, w, x, y : as edge0_moe_grouped ([n_tokens][K] routing,
  *                [n_tokens][d] bf16 in and out; y must not alias x)
  *   max_tokens : the token bound the workspace was sized for
  *                (1 <= max_tokens <= 4096, n_tokens <= max_tokens)
  *   workspace  : edge0_prefill_workspace_bytes(shape, max_tokens) bytes,
  *                zero-filled once before first use (calls leave it ready)
- * Shapes: those of the grouped call's MFMA tiles (d_model <= 2048 and a
- * multiple of 8 g, g of 32 or 64, d_inter / 32 in {4, 8, 12, 16, 24, 32},
- * even lora_rank <= 16); EDGE0_EINVAL otherwise.  An id or slot out of range
- * is recorded in the workspace error word (edge0_workspace_error) and its
- * pair contributes nothing. */
+ * Shapes: those of edge0_moe_grouped with g of 32 or 64, d_model <= 2048 and
+ * a multiple of 128 and of 4 g, d_inter a multiple of 64, lora_rank <= 16;
+ * EDGE0_EINVAL otherwise.  An id or slot out of range is recorded in the
+ * workspace error word (edge0_workspace_error) and its pair contributes
+ * nothing. */
 size_t edge0_prefill_workspace_bytes(const edge0_moe_shape* shape, int32_t max_tokens);
 int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
                       const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
                       const float* w, const void* x, void* y, void* workspace,
                       int32_t max_tokens, hipStream_t stream);
+
+/* The grouped and the prefill call with the recovery LoRA given apart from
+ * the bundles ([Edge0] §3.3), as edge0_moe_layer_lora: the six bf16 factors
+ * of expert 0 and the expert stride in elements (0: one adapter shared by
+ * every expert); the pool may hold LoRA-free bundles.  Results are those of
+ * edge0_moe_grouped / edge0_moe_prefill with the same adapters in the
+ * bundles, bit for bit.  lora may be NULL only when lora_rank == 0;
+ * EDGE0_EINVAL for a NULL factor or a negative stride. */
+int edge0_moe_grouped_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                           const edge0_lora* lora, const int32_t* slot_table, int32_t n_tokens,
+                           const int32_t* ids, const float* w, const void* x, void* y,
+                           void* workspace, int32_t flags, hipStream_t stream);
+int edge0_moe_prefill_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                           const edge0_lora* lora, const int32_t* slot_table, int32_t n_tokens,
+                           const int32_t* ids, const float* w, const void* x, void* y,
+                           void* workspace, int32_t max_tokens, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
  * Merge-and-requantise, the measurement behind keeping the LoRA unmerged

@@ -77,7 +77,20 @@ struct GrpArgs {
   const float* xsum;
   float* ypair;
   const int32_t* keep;
+  // adapters given apart from the bundles (the _lora calls): factor i
+  // (a_gate, b_gate, a_up, b_up, a_down, b_down) of expert e at lo_base[i] +
+  // e * lo_stride bytes; when lora_sep is false each expert's factors are in
+  // its bundle at the layout's offsets
+  bool lora_sep;
+  const uint8_t* lo_base[6];
+  int64_t lo_stride;
 };
+
+// LoRA factor i of expert e (its bundle b, offset off in the bundle)
+__device__ __forceinline__ const uint8_t* grp_lora(const GrpArgs& a, const uint8_t* b, int e, int i,
+                                                   int64_t off) {
+  return a.lora_sep ? a.lo_base[i] + (size_t)max(0, min(e, a.E - 1)) * a.lo_stride : b + off;
+}
 
 // ------------------------------------------------------------- bucketing
 // inclusive prefix sum over a wave
@@ -194,7 +207,8 @@ __device__ __forceinline__ void grp_lora_in(const GrpArgs& a, int wg) {
   if (s >= 0 && s < a.n_slots) {  // otherwise the bucketing reports the pair
     const uint8_t* b = a.pool + (size_t)s * (size_t)a.slot_bytes;
     const uint16_t* wrow =
-        reinterpret_cast<const uint16_t*>(b + (j ? a.lay.a_up : a.lay.a_gate)) + (size_t)rr * a.d;
+        reinterpret_cast<const uint16_t*>(grp_lora(a, b, e, j ? 2 : 0, j ? a.lay.a_up : a.lay.a_gate)) +
+        (size_t)rr * a.d;
     t = row_dot<false, false>(wrow, a.x + (size_t)(p / a.K) * a.d, a.d);
   }
   if ((threadIdx.x & 63) == 0) a.t_in[row] = t;
@@ -304,10 +318,11 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
     }
   }
   const bool has_l = r > 0 && lane < r;
+  const int e = a.lora_sep ? a.act_e[act] : 0;  // the expert, for adapters given apart
   float Bg[4] = {0.f, 0.f, 0.f, 0.f}, Bu[4] = {0.f, 0.f, 0.f, 0.f};
   if (has_l) {
-    const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(b + a.lay.b_gate);
-    const uint16_t* Bup = reinterpret_cast<const uint16_t*>(b + a.lay.b_up);
+    const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(grp_lora(a, b, e, 1, a.lay.b_gate));
+    const uint16_t* Bup = reinterpret_cast<const uint16_t*>(grp_lora(a, b, e, 3, a.lay.b_up));
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       Bg[ii] = bf2f(Bgp[(size_t)(row0 + ii) * r + lane]);
@@ -317,7 +332,8 @@ __global__ __launch_bounds__(256) void k_grp_gate_up(GrpArgs a, int min_cnt, int
   uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
   if ((int)threadIdx.x < r) {
     const uint4* src = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)threadIdx.x * a.I + i0);
+        reinterpret_cast<const uint16_t*>(grp_lora(a, b, e, 4, a.lay.a_down)) +
+        (size_t)threadIdx.x * a.I + i0);
     ad0 = src[0];
     ad1 = src[1];
   }
@@ -431,8 +447,9 @@ __global__ __launch_bounds__(256) void k_grp_down(GrpArgs a, int min_cnt, int ma
   // LoRA-down row o (wave 0): r <= 64 bf16 as packed pairs
   uint32_t bd[32];
   if (wave == 0) {
+    const int e = a.lora_sep ? a.act_e[act] : 0;  // the expert, for adapters given apart
     const uint32_t* src =
-        reinterpret_cast<const uint32_t*>(b + a.lay.b_down) + (size_t)o * (r / 2);
+        reinterpret_cast<const uint32_t*>(grp_lora(a, b, e, 5, a.lay.b_down)) + (size_t)o * (r / 2);
 #pragma unroll
     for (int m = 0; m < 32; ++m) bd[m] = 2 * m < r ? src[m] : 0u;
   }
@@ -607,8 +624,8 @@ struct GuTileLds {
 };
 
 template <int GW, int WPG>
-__device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int q0, int t0, int mt,
-                                        int blk, const uint32_t (&wg)[GW * WPG],
+__device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int e, int q0, int t0,
+                                        int mt, int blk, const uint32_t (&wg)[GW * WPG],
                                         const uint32_t (&wu)[GW * WPG], Q4Consts kq,
                                         GuTileLds& sm) {
   constexpr int NW = GW * WPG;
@@ -644,14 +661,16 @@ __device__ __forceinline__ void gu_tile(const GrpArgs& a, const uint8_t* b, int 
   }
   const int rr = tid & 15;
   const uint4* adp = reinterpret_cast<const uint4*>(
-      lora ? b + a.lay.a_down + ((size_t)min(rr, r - 1) * I + i0) * 2 : b + a.lay.gate_q);
+      lora ? grp_lora(a, b, e, 4, a.lay.a_down) + ((size_t)min(rr, r - 1) * I + i0) * 2
+           : b + a.lay.gate_q);
   const uint4 ad0 = adp[0], ad1 = adp[1];
   if (lora) {
     // rank entries past r are zero, so the epilogue's dot runs over
     // kTileRank entries with every read issued at once
     for (int t = tid; t < 2 * 16 * kTileRank; t += 256) {
       const int p = t / (16 * kTileRank), rw = (t / kTileRank) % 16, k = t % kTileRank;
-      const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate));
+      const uint16_t* B = reinterpret_cast<const uint16_t*>(
+          grp_lora(a, b, e, p ? 3 : 1, p ? a.lay.b_up : a.lay.b_gate));
       sm.bl[p][rw][k] = k < r ? bf2f(B[(size_t)(i0 + rw) * r + k]) : 0.f;
     }
     for (int t = tid; t < kTileTok * 2 * kTileRank; t += 256) {
@@ -753,7 +772,8 @@ __global__ __launch_bounds__(256, 3) void k_grp_gu_tile(GrpArgs a, int tm, int m
     }
   }
   const Q4Consts kq = q4_consts();
-  gu_tile<GW, WPG>(a, b, q0, t_first, min(tm, cnt - t_first), blk, wg, wu, kq, sm);
+  const int e = a.lora_sep ? a.act_e[act] : 0;  // the expert, for adapters given apart
+  gu_tile<GW, WPG>(a, b, e, q0, t_first, min(tm, cnt - t_first), blk, wg, wu, kq, sm);
 }
 
 // Down: workgroup (tile, active expert, kDownNT blocks of 64 output rows);
@@ -765,8 +785,8 @@ __global__ __launch_bounds__(256, 3) void k_grp_gu_tile(GrpArgs a, int tm, int m
 // weighted row added to its fixed-point output.  Dynamic LDS: hi and lo h
 // of tm pairs, rows of I bf16.  One tile per workgroup, as for gate/up.
 template <int NW, int WPG>
-__device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, int q0, int t0,
-                                          int mt, int tm, int rb,
+__device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, int e, int q0,
+                                          int t0, int mt, int tm, int rb,
                                           const uint32_t (&wd)[kDownNT][NW], Q4Consts kq,
                                           uint16_t* hsm, float (&gsum)[kTileTok][NW / WPG],
                                           float (&td_s)[kTileTok][kTileRank]) {
@@ -804,7 +824,7 @@ __device__ __forceinline__ void down_tile(const GrpArgs& a, const uint8_t* b, in
         dbr[t][G] = db[(size_t)G * d + o];
       }
       const uint32_t* src = reinterpret_cast<const uint32_t*>(
-          lora ? b + a.lay.b_down + (size_t)o * r * 2 : b + a.lay.down_q);
+          lora ? grp_lora(a, b, e, 5, a.lay.b_down) + (size_t)o * r * 2 : b + a.lay.down_q);
 #pragma unroll
       for (int k = 0; k < kTileRank / 2; ++k) bdw[t][k] = src[lora ? min(k, r / 2 - 1) : 0];
     }
@@ -923,7 +943,9 @@ __global__ __launch_bounds__(256, 2) void k_grp_down_tile(GrpArgs a, int tm, int
       }
   }
   const Q4Consts kq = q4_consts();
-  down_tile<NW, WPG>(a, b, q0, t_first, min(tm, cnt - t_first), tm, rb, wd, kq, hsm, gsum, td_s);
+  const int e = a.lora_sep ? a.act_e[act] : 0;  // the expert, for adapters given apart
+  down_tile<NW, WPG>(a, b, e, q0, t_first, min(tm, cnt - t_first), tm, rb, wd, kq, hsm, gsum,
+                     td_s);
 }
 
 // ------------------------------------------------------------ output
@@ -1094,10 +1116,13 @@ __global__ __launch_bounds__(256) void k_pf_lora_in(GrpArgs a) {
   for (int tb = 0; tb < 4; ++tb)
     xr[tb] = a.x + (size_t)a.pair_tok[q0 + t0 + min(16 * tb + n, mt - 1)] * d;
   const int q1 = n, q2 = 16 + n;  // this lane's B rows in the two n-tiles
-  const uint16_t* w1 = reinterpret_cast<const uint16_t*>(b + (q1 < r ? a.lay.a_gate : a.lay.a_up)) +
+  const int e = a.lora_sep ? a.act_e[te.x] : 0;  // the expert, for adapters given apart
+  const bool up1 = q1 >= r, up2 = q2 < 2 * r && q2 >= r;
+  const uint16_t* w1 = reinterpret_cast<const uint16_t*>(
+                           grp_lora(a, b, e, up1 ? 2 : 0, up1 ? a.lay.a_up : a.lay.a_gate)) +
                        (size_t)(q1 % r) * d;
   const uint16_t* w2 = reinterpret_cast<const uint16_t*>(
-                           b + (q2 < 2 * r ? (q2 < r ? a.lay.a_gate : a.lay.a_up) : a.lay.a_gate)) +
+                           grp_lora(a, b, e, up2 ? 2 : 0, up2 ? a.lay.a_up : a.lay.a_gate)) +
                        (size_t)(q2 < 2 * r ? q2 % r : 0) * d;
   const bool two = 2 * r > 16;
   f32x4_t c1[4], c2[4];
@@ -1223,6 +1248,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
   const int d = a.d, r = a.r, ng = d / G, nsteps = d / STEP;
   const int row = blk * kPfRows + 16 * wave + n;  // this lane's weight row
   const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+  const int e_lo = a.lora_sep ? a.act_e[te.x] : 0;  // the expert, for adapters given apart
   // staging duties: activation chunks (pairs past the tile repeat its last)
   const uint16_t* xrow[XU];
   int xdst[XU];
@@ -1353,7 +1379,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
     bf16x8_t bl[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const uint16_t* B = reinterpret_cast<const uint16_t*>(b + (p ? a.lay.b_up : a.lay.b_gate)) +
+      const uint16_t* B = reinterpret_cast<const uint16_t*>(
+                              grp_lora(a, b, e_lo, p ? 3 : 1, p ? a.lay.b_up : a.lay.b_gate)) +
                           (size_t)row * r;
       uint32_t w4[4];
 #pragma unroll
@@ -1476,8 +1503,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
   }
   const int hsm = q0 + t0 + min(tid, mt - 1);  // group sums: thread < 64 (block-major sums)
   const int arr = tid / CPB, acc8 = tid % CPB; // A_down chunks: thread < 16 CPB
+  const int e_lo = a.lora_sep ? a.act_e[te.x] : 0;  // the expert, for adapters given apart
   const uint16_t* adsrc = reinterpret_cast<const uint16_t*>(
-      b + (r > 0 ? a.lay.a_down : a.lay.down_q)) + (size_t)min(arr, max(r - 1, 0)) * I + 8 * acc8;
+      r > 0 ? grp_lora(a, b, e_lo, 4, a.lay.a_down) : b + a.lay.down_q) +
+      (size_t)min(arr, max(r - 1, 0)) * I + 8 * acc8;
   // this lane's weight words: word j of row o0 + o + 16 rr in each 32-input
   // tile (64-row tile block (o0 + o) / 64, row (o0 + o) % 64 + 16 rr); its
   // rows' scales
@@ -1627,7 +1656,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
         const uint16_t* B =
-            reinterpret_cast<const uint16_t*>(b + a.lay.b_down) + (size_t)(o0 + o + 16 * rr) * r;
+            reinterpret_cast<const uint16_t*>(grp_lora(a, b, e_lo, 5, a.lay.b_down)) +
+            (size_t)(o0 + o + 16 * rr) * r;
         uint32_t w4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1710,6 +1740,33 @@ static GrpWs grp_ws_layout(const edge0_moe_shape* s) {
   L.acc = take(8 * T * d);
   L.total = off;
   return L;
+}
+
+// The adapters of a call: in the bundles (lora NULL), or given apart, when
+// the pool may hold LoRA-free bundles (the int4 arrays sit at the same
+// offsets in both layouts).  Checks the pool's slot size against the layout
+// it must hold.
+static int grp_lora_args(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                         const edge0_lora* lora, GrpArgs& a) {
+  edge0_bundle_layout lay, lay_pool;
+  edge0_moe_shape s0 = *shape;
+  const int r = shape->lora_rank;
+  const bool sep = lora != nullptr && r > 0;
+  if (sep) s0.lora_rank = 0;
+  if (bundle_layout(shape, &lay) != EDGE0_OK || bundle_layout(&s0, &lay_pool) != EDGE0_OK ||
+      pool->slot_bytes < lay_pool.bytes)
+    return EDGE0_EINVAL;
+  if (sep && (!lora->a_gate || !lora->b_gate || !lora->a_up || !lora->b_up || !lora->a_down ||
+              !lora->b_down || lora->expert_stride < 0))
+    return EDGE0_EINVAL;
+  a.lay = lay;
+  a.lora_sep = sep;
+  if (sep) {
+    const void* f[6] = {lora->a_gate, lora->b_gate, lora->a_up, lora->b_up, lora->a_down, lora->b_down};
+    for (int i = 0; i < 6; ++i) a.lo_base[i] = static_cast<const uint8_t*>(f[i]);
+    a.lo_stride = lora->expert_stride * 2;  // bf16 elements
+  }
+  return EDGE0_OK;
 }
 
 static bool grouped_shape_ok(const edge0_moe_shape* s) {
@@ -1816,20 +1873,19 @@ extern "C" size_t edge0_grouped_workspace_bytes(const edge0_moe_shape* shape) {
   return grp_ws_layout(shape).total;
 }
 
-extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
-                                 const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
-                                 const float* w, const void* x, void* y, void* workspace,
-                                 int32_t flags, hipStream_t stream) {
+static int grouped_call(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                        const edge0_lora* lora, const int32_t* slot_table, int32_t n_tokens,
+                        const int32_t* ids, const float* w, const void* x, void* y,
+                        void* workspace, int32_t flags, hipStream_t stream) {
   if (!shape || !grouped_shape_ok(shape) || !pool || !pool->base || !slot_table || !workspace ||
       n_tokens < 0 || n_tokens > kGrpMaxTokens || (flags & ~(EDGE0_GROUPED_NO_MFMA | 0xFF00)) != 0)
     return EDGE0_EINVAL;
+  GrpArgs a{};
+  if (grp_lora_args(shape, pool, lora, a) != EDGE0_OK) return EDGE0_EINVAL;
   if (n_tokens == 0) return EDGE0_OK;
   if (!ids || !w || !x || !y) return EDGE0_EINVAL;
-  edge0_bundle_layout lay;
-  if (bundle_layout(shape, &lay) != EDGE0_OK || pool->slot_bytes < lay.bytes) return EDGE0_EINVAL;
   const GrpWs L = grp_ws_layout(shape);
   char* ws = static_cast<char*>(workspace);
-  GrpArgs a{};
   a.pool = static_cast<const uint8_t*>(pool->base);
   a.slot_bytes = pool->slot_bytes;
   a.n_slots = pool->n_slots;
@@ -1846,7 +1902,6 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
   a.g = shape->group_size;
   a.r = shape->lora_rank;
   a.scale = a.r > 0 ? shape->lora_alpha / (float)a.r : 0.f;
-  a.lay = lay;
   a.P = n_tokens * a.K;
   a.Amax = a.E < a.P ? a.E : a.P;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
@@ -1888,6 +1943,24 @@ extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_
   k_grp_out<<<(n_out + 255) / 256, 256, 0, stream>>>(a);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
+}
+
+extern "C" int edge0_moe_grouped(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                 const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
+                                 const float* w, const void* x, void* y, void* workspace,
+                                 int32_t flags, hipStream_t stream) {
+  return grouped_call(shape, pool, nullptr, slot_table, n_tokens, ids, w, x, y, workspace, flags,
+                      stream);
+}
+
+extern "C" int edge0_moe_grouped_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                      const edge0_lora* lora, const int32_t* slot_table,
+                                      int32_t n_tokens, const int32_t* ids, const float* w,
+                                      const void* x, void* y, void* workspace, int32_t flags,
+                                      hipStream_t stream) {
+  if (shape && shape->lora_rank > 0 && !lora) return EDGE0_EINVAL;
+  return grouped_call(shape, pool, lora, slot_table, n_tokens, ids, w, x, y, workspace, flags,
+                      stream);
 }
 
 // ------------------------------------------------------------ prefill host
@@ -1947,20 +2020,19 @@ extern "C" size_t edge0_prefill_workspace_bytes(const edge0_moe_shape* shape, in
   return pf_ws_layout(shape, max_tokens).total;
 }
 
-extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
-                                 const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
-                                 const float* w, const void* x, void* y, void* workspace,
-                                 int32_t max_tokens, hipStream_t stream) {
+static int prefill_call(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                        const edge0_lora* lora, const int32_t* slot_table, int32_t n_tokens,
+                        const int32_t* ids, const float* w, const void* x, void* y,
+                        void* workspace, int32_t max_tokens, hipStream_t stream) {
   if (!shape || !pf_shape_ok(shape) || !pool || !pool->base || !slot_table || !workspace ||
       max_tokens < 1 || max_tokens > kPfMaxTokens || n_tokens < 0 || n_tokens > max_tokens)
     return EDGE0_EINVAL;
+  GrpArgs a{};
+  if (grp_lora_args(shape, pool, lora, a) != EDGE0_OK) return EDGE0_EINVAL;
   if (n_tokens == 0) return EDGE0_OK;
   if (!ids || !w || !x || !y || x == y) return EDGE0_EINVAL;
-  edge0_bundle_layout lay;
-  if (bundle_layout(shape, &lay) != EDGE0_OK || pool->slot_bytes < lay.bytes) return EDGE0_EINVAL;
   const PfWs L = pf_ws_layout(shape, max_tokens);
   char* ws = static_cast<char*>(workspace);
-  GrpArgs a{};
   a.pool = static_cast<const uint8_t*>(pool->base);
   a.slot_bytes = pool->slot_bytes;
   a.n_slots = pool->n_slots;
@@ -1977,7 +2049,6 @@ extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_
   a.g = shape->group_size;
   a.r = shape->lora_rank;
   a.scale = a.r > 0 ? shape->lora_alpha / (float)a.r : 0.f;
-  a.lay = lay;
   a.P = n_tokens * a.K;
   a.Amax = a.E < a.P ? a.E : a.P;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
@@ -2034,4 +2105,22 @@ extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_
   k_pf_combine<<<(a.T * (a.d / 4) + 255) / 256, 256, 0, stream>>>(a);
   E0_CHECK_LAUNCH();
   return EDGE0_OK;
+}
+
+extern "C" int edge0_moe_prefill(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                 const int32_t* slot_table, int32_t n_tokens, const int32_t* ids,
+                                 const float* w, const void* x, void* y, void* workspace,
+                                 int32_t max_tokens, hipStream_t stream) {
+  return prefill_call(shape, pool, nullptr, slot_table, n_tokens, ids, w, x, y, workspace,
+                      max_tokens, stream);
+}
+
+extern "C" int edge0_moe_prefill_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
+                                      const edge0_lora* lora, const int32_t* slot_table,
+                                      int32_t n_tokens, const int32_t* ids, const float* w,
+                                      const void* x, void* y, void* workspace, int32_t max_tokens,
+                                      hipStream_t stream) {
+  if (shape && shape->lora_rank > 0 && !lora) return EDGE0_EINVAL;
+  return prefill_call(shape, pool, lora, slot_table, n_tokens, ids, w, x, y, workspace,
+                      max_tokens, stream);
 }

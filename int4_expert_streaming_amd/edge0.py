@@ -169,6 +169,10 @@ _SIG = {
     "edge0_grouped_workspace_bytes": (C.c_size_t, [C.POINTER(MoeShape)]),
     "edge0_moe_grouped": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, C.c_int32, _P,
                                     _P, _P, _P, _P, C.c_int32, _P]),
+    "edge0_moe_grouped_lora": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P,
+                                         C.c_int32, _P, _P, _P, _P, _P, C.c_int32, _P]),
+    "edge0_moe_prefill_lora": (C.c_int, [C.POINTER(MoeShape), C.POINTER(SlotPool), _P, _P,
+                                         C.c_int32, _P, _P, _P, _P, _P, C.c_int32, _P]),
     "edge0_lru_create": (C.c_int, [C.POINTER(_P), C.c_int32, C.c_int32, C.c_int32]),
     "edge0_lru_request": (C.c_int, [_P, C.c_int32, C.c_int32, _I32P, C.c_int32, _I32P, _I32P,
                                     _I32P]),
@@ -372,6 +376,24 @@ def edge0_moe_grouped(shape: MoeShape, pool: SlotPool, slot_table, n_tokens: int
     _check(lib.edge0_moe_grouped(C.byref(shape), C.byref(pool), _ptr(slot_table), n_tokens,
                                  _ptr(ids), _ptr(w), _ptr(x), _ptr(y), _ptr(workspace), flags,
                                  _stream(stream)), "edge0_moe_grouped")
+
+
+def edge0_moe_grouped_lora(shape: MoeShape, pool: SlotPool, lora: "Lora | None", slot_table,
+                           n_tokens: int, ids, w, x, y, workspace, flags: int = 0, stream=None):
+    _check(lib.edge0_moe_grouped_lora(C.byref(shape), C.byref(pool),
+                                      None if lora is None else C.byref(lora), _ptr(slot_table),
+                                      n_tokens, _ptr(ids), _ptr(w), _ptr(x), _ptr(y),
+                                      _ptr(workspace), flags, _stream(stream)),
+           "edge0_moe_grouped_lora")
+
+
+def edge0_moe_prefill_lora(shape: MoeShape, pool: SlotPool, lora: "Lora | None", slot_table,
+                           n_tokens: int, ids, w, x, y, workspace, max_tokens: int, stream=None):
+    _check(lib.edge0_moe_prefill_lora(C.byref(shape), C.byref(pool),
+                                      None if lora is None else C.byref(lora), _ptr(slot_table),
+                                      n_tokens, _ptr(ids), _ptr(w), _ptr(x), _ptr(y),
+                                      _ptr(workspace), max_tokens, _stream(stream)),
+           "edge0_moe_prefill_lora")
 
 
 class Stack(_Handle):

@@ -1,7 +1,9 @@
-"""The layer with its LoRA given apart from the bundles (edge0_moe_layer_lora,
+"""The layer, grouped and prefill calls with their LoRA given apart from the
+bundles (edge0_moe_layer_lora, edge0_moe_grouped_lora, edge0_moe_prefill_lora;
 [Edge0] §3.3: adapters ship beside the base weights): per-expert adapters in
-blocks of their own over a pool of LoRA-free bundles, bit-identical to
-edge0_moe_layer with the same adapters inside the bundles; one adapter
+blocks of their own over a pool of LoRA-free bundles, bit-identical to the
+bundled calls with the same adapters inside the bundles (the grouped call on
+its GEMV and its MFMA-tile paths, prefill at several sizes); one adapter
 shared by every expert (stride 0) against the oracle; arguments refused."""
 import numpy as np
 import pytest
@@ -123,3 +125,121 @@ def test_lora_argument_refusals(torch_cuda):
     torch.cuda.synchronize()
     y_o = O.moe_layer(lay.experts, np.arange(S.top_k), np.full(S.top_k, 0.25), G.hidden(S, 1), S.group)
     check_layer_output(y.cpu().numpy().view(np.uint16), y_o)
+
+
+def _pool0(E, S, lay):
+    """A pool of LoRA-free bundles holding the layer's int4 experts."""
+    from int4_expert_streaming_amd.weights import SlotPoolBuffer
+    sh0 = E.make_shape(S)
+    sh0.lora_rank = 0
+    pool0 = SlotPoolBuffer(sh0, S.n_experts)
+    for e in range(S.n_experts):
+        pool0.load(e, lay.experts[e])
+    return pool0
+
+
+@pytest.mark.parametrize("name,S,T,flags", [
+    ("tiny", G.TINY, 5, 0), ("tiny", G.TINY, 20, 1),
+    ("qwen3moe_k8", G.QWEN3_MOE.with_k(8), 1, 0), ("qwen3moe_k8", G.QWEN3_MOE.with_k(8), 2, 0),
+    ("qwen3moe_k8", G.QWEN3_MOE.with_k(8), 32, 0), ("qwen3moe_k8", G.QWEN3_MOE.with_k(8), 32, 1)])
+def test_grouped_separate_adapters_equal_bundled(torch_cuda, name, S, T, flags):
+    """flags 1: every expert on the GEMVs; 0: the MFMA tiles from 3 tokens."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    lay = DeviceLayer(S, seed=12, layer=2)
+    pool0 = _pool0(E, S, lay)
+    lo, keep = _adapters(lay.loras, list(range(S.n_experts)))
+    ws = E.new_grouped_workspace(lay.sh)
+    ids, w = G.grouped_routing(S.n_experts, S.top_k, T, seed=70 + T)
+    x = to_device(G.hidden(S, 90 + T, n=T))
+    ids_d = to_device(ids.astype(np.int32))
+    w_d = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    y_b = torch.zeros((T, S.d_model), dtype=torch.int16, device="cuda")
+    y_s = torch.zeros_like(y_b)
+    E.edge0_moe_grouped(lay.sh, lay.pool.pool, lay.table, T, ids_d, w_d, x, y_b, ws, flags)
+    E.edge0_moe_grouped_lora(lay.sh, pool0.pool, lo, lay.table, T, ids_d, w_d, x, y_s, ws, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(y_b, y_s), (name, T, flags)
+    assert E.edge0_workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("name,S,T", [("tiny", G.TINY, 17), ("tiny", G.TINY, 300),
+                                      ("qwen3moe_k8", G.QWEN3_MOE.with_k(8), 100),
+                                      ("qwen3moe_k8", G.QWEN3_MOE.with_k(8), 1024)])
+def test_prefill_separate_adapters_equal_bundled(torch_cuda, name, S, T):
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    lay = DeviceLayer(S, seed=13, layer=3)
+    pool0 = _pool0(E, S, lay)
+    lo, keep = _adapters(lay.loras, list(range(S.n_experts)))
+    ws = E.new_prefill_workspace(lay.sh, T)
+    ids, w = G.grouped_routing(S.n_experts, S.top_k, T, seed=110 + T)
+    x = to_device(G.hidden(S, 130 + T, n=T))
+    ids_d = to_device(ids.astype(np.int32))
+    w_d = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    y_b = torch.zeros((T, S.d_model), dtype=torch.int16, device="cuda")
+    y_s = torch.zeros_like(y_b)
+    E.edge0_moe_prefill(lay.sh, lay.pool.pool, lay.table, T, ids_d, w_d, x, y_b, ws, T)
+    E.edge0_moe_prefill_lora(lay.sh, pool0.pool, lo, lay.table, T, ids_d, w_d, x, y_s, ws, T)
+    torch.cuda.synchronize()
+    assert torch.equal(y_b, y_s), (name, T)
+    assert E.edge0_workspace_error(ws) == 0
+
+
+def test_prefill_shared_adapter_against_oracle(torch_cuda):
+    """expert_stride 0 on the prefill call: every expert uses one adapter."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.weights import to_device
+    S = G.QWEN3_MOE.with_k(8)
+    lay = DeviceLayer(S, seed=14, layer=0)
+    pool0 = _pool0(E, S, lay)
+    shared = G.lora_tensors(S, 14, 0, 999)
+    lo, keep = _adapters({0: shared}, [0])
+    lo.expert_stride = 0
+    T = 64
+    ws = E.new_prefill_workspace(lay.sh, T)
+    ids, w = G.grouped_routing(S.n_experts, S.top_k, T, seed=150)
+    xb = G.hidden(S, 151, n=T)
+    y = torch.zeros((T, S.d_model), dtype=torch.int16, device="cuda")
+    E.edge0_moe_prefill_lora(lay.sh, pool0.pool, lo, lay.table, T, to_device(ids.astype(np.int32)),
+                             torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda(),
+                             to_device(xb), y, ws, T)
+    torch.cuda.synchronize()
+    yb = y.cpu().numpy().view(np.uint16)
+    for j in range(0, T, 7):
+        y_o = O.moe_layer(lay.experts, ids[j], w[j].astype(np.float64), xb[j], S.group,
+                          {e: shared for e in range(S.n_experts)}, lay.scale)
+        check_layer_output(yb[j], y_o)
+
+
+def test_grouped_prefill_lora_refusals(torch_cuda):
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    S = G.TINY
+    lay = DeviceLayer(S, seed=15, layer=0)
+    wsg = E.new_grouped_workspace(lay.sh)
+    wsp = E.new_prefill_workspace(lay.sh, 4)
+    with pytest.raises(E.Edge0Error):  # rank 8 without adapters
+        E.edge0_moe_grouped_lora(lay.sh, lay.pool.pool, None, lay.table, 0, None, None, None,
+                                 None, wsg)
+    with pytest.raises(E.Edge0Error):
+        E.edge0_moe_prefill_lora(lay.sh, lay.pool.pool, None, lay.table, 0, None, None, None,
+                                 None, wsp, 4)
+    lo, keep = _adapters(lay.loras, list(range(S.n_experts)))
+    lo.expert_stride = -1
+    with pytest.raises(E.Edge0Error):
+        E.edge0_moe_grouped_lora(lay.sh, lay.pool.pool, lo, lay.table, 0, None, None, None,
+                                 None, wsg)
+    with pytest.raises(E.Edge0Error):
+        E.edge0_moe_prefill_lora(lay.sh, lay.pool.pool, lo, lay.table, 0, None, None, None,
+                                 None, wsp, 4)
+    # a pool too small for the bundled call but right for LoRA-free bundles
+    pool0 = _pool0(E, S, lay)
+    with pytest.raises(E.Edge0Error):
+        E.edge0_moe_grouped(lay.sh, pool0.pool, lay.table, 0, None, None, None, None, wsg)
+    lo.expert_stride = 0
+    E.edge0_moe_grouped_lora(lay.sh, pool0.pool, lo, lay.table, 0, None, None, None, None, wsg)
+    torch.cuda.synchronize()
