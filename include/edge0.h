@@ -420,6 +420,22 @@ int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
                        const edge0_stack_spec* spec, const edge0_slot_pool* pool,
                        const int32_t* slot_tables, const void* const* routers,
                        const edge0_head* heads);
+/* The same stack with each layer's recovery LoRA given apart from the
+ * bundles ([Edge0] §3.3: a new adapter generation swaps files, not bundles):
+ * layer_loras is a host array [n_layers] of edge0_lora (layer L's six
+ * factor pointers of expert 0 and the expert stride, 0 = one adapter for
+ * every expert of the layer), copied into the handle; the pointed-to
+ * factors stay caller-owned.  The pool, and a stager's host bundles, may
+ * hold LoRA-free bundles (edge0_bundle_layout_of with lora_rank 0), which
+ * also makes every staged bundle smaller.  Results are those of
+ * edge0_stack_create with the same adapters in the bundles, bit for bit.
+ * Only the EDGE0_STACK_GRAPHS mode runs such a stack (edge0_stack_set_mode
+ * refuses the others with EDGE0_EINVAL).  layer_loras may be NULL only when
+ * lora_rank == 0; EDGE0_EINVAL for a NULL factor or a negative stride. */
+int edge0_stack_create_lora(edge0_stack** out, const edge0_moe_shape* shape,
+                            const edge0_stack_spec* spec, const edge0_slot_pool* pool,
+                            const int32_t* slot_tables, const void* const* routers,
+                            const edge0_head* heads, const edge0_lora* layer_loras);
 
 /* Runs decode step `step` (0, 1, 2, ... in order) on h0 (device bf16 [d]),
  * writing the final hidden state to h_out (device bf16 [d]).  Uses a HIP

@@ -48,7 +48,8 @@ struct GuW {
 // issued in order (not their values) passes the index of another wave
 template <int NJ, int RR = kWideRowsPerWave>
 __device__ __forceinline__ void gu_load(const MoeArgs& a, const uint8_t* b, int i0,
-                                        GuW<NJ, RR>& w, int wave = tid_here() >> 6, int k = 0) {
+                                        GuW<NJ, RR>& w, int wave = tid_here() >> 6, int k = 0,
+                                        int e = -1) {
   constexpr int R = RR;
   const int lane = tid_here() & 63;
   const int d = a.d, g = a.g, ng = d / g, r = a.r;
@@ -78,8 +79,11 @@ __device__ __forceinline__ void gu_load(const MoeArgs& a, const uint8_t* b, int 
   // without a branch (lanes >= r, or r = 0, read an in-bundle word that is
   // never used), so no control flow separates these loads from their uses.
   const int rc = r > 0 ? r : 1;
-  const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(r > 0 ? E0_LORA(a, b, k, 1, a.lay.b_gate) : b);
-  const uint16_t* Bup = reinterpret_cast<const uint16_t*>(r > 0 ? E0_LORA(a, b, k, 3, a.lay.b_up) : b);
+  // (adapters given apart: expert e's, or routed expert k's when e < 0)
+  const uint16_t* Bgp = reinterpret_cast<const uint16_t*>(
+      r > 0 ? E0_LORA_E(a, b, (e >= 0 ? e : (a).ids[k]), 1, a.lay.b_gate) : b);
+  const uint16_t* Bup = reinterpret_cast<const uint16_t*>(
+      r > 0 ? E0_LORA_E(a, b, (e >= 0 ? e : (a).ids[k]), 3, a.lay.b_up) : b);
   const int rl = lane % rc;
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {

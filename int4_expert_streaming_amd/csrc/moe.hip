@@ -173,8 +173,9 @@ __global__ __launch_bounds__(256) void k_layer_in(MoeArgs a, LayerIn li) {
   if (li.flags & IN_TOPK) {
     const int s = resolve_slot(a, ids[k]);
     wrow = s < 0 ? nullptr
-                 : reinterpret_cast<const uint16_t*>(a.pool + (size_t)s * a.slot_bytes +
-                                                     (p ? a.lay.a_up : a.lay.a_gate)) +
+                 : reinterpret_cast<const uint16_t*>(E0_LORA_E(a, a.pool + (size_t)s * a.slot_bytes,
+                                                               ids[k], p ? 2 : 0,
+                                                               p ? a.lay.a_up : a.lay.a_gate)) +
                        (size_t)rr * d;
   }
   float t = 0.f;
@@ -385,7 +386,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   // that need them, a dependent round trip each before the first memory
   // load of the workgroup goes out.
   asm volatile("" ::"s"(a.d), "s"(a.r), "s"(a.I), "s"(a.K), "s"(a.E), "s"(a.n_prod),
-               "s"(a.prod_rows), "s"(a.n_slots), "s"(li.flags), "s"(a.route_rows));
+               "s"(a.prod_rows), "s"(a.n_slots), "s"(li.flags), "s"(a.route_rows),
+               "s"((int)a.lora_sep));
   asm volatile("" ::"s"(a.table), "s"(a.pool), "s"(a.slot_bytes), "s"(a.ids), "s"(a.acc_prev),
                "s"(li.h_prev), "s"(a.lay.gate_q), "s"(a.lay.up_q), "s"(a.lay.gate_s),
                "s"(a.lay.gate_b), "s"(a.lay.up_s), "s"(a.lay.up_b));
@@ -443,12 +445,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   // results are discarded
   // (the table words are passed by value: an array captured by a lambda is
   // placed in LDS by the compiler)
-  int slot = -1;
+  int slot = -1, eid = 0;  // eid: the routed expert (for adapters given apart)
   bool ok = false;
   const uint8_t* b = a.pool;
   const int t0 = tbl[0], t1 = tbl[1], t2 = tbl[2], t3 = tbl[3];
   static_assert(kFusedMaxExperts == 256, "four table words per lane");
   auto resolve = [&](int expert) {
+    eid = expert;
     slot = table_slot(t0, t1, t2, t3, expert, a.E, a.n_slots);
     ok = slot >= 0;
     b = a.pool + (size_t)(ok ? slot : 0) * (size_t)a.slot_bytes;
@@ -608,7 +611,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       const int u = min(tl + 512 * m, nu - 1);  // past nu: repeats of the last piece
       const int tr = tr0 + u / (d / 8);
       const uint4* row = reinterpret_cast<const uint4*>(
-                             b + (tr < r ? a.lay.a_gate : a.lay.a_up)) +
+                             E0_LORA_E(a, b, eid, tr < r ? 0 : 2,
+                                       tr < r ? a.lay.a_gate : a.lay.a_up)) +
                          (size_t)(tr % r) * (d / 8);
       ap[m] = row[u % (d / 8)];
     }
@@ -650,9 +654,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       li.ids_out[tid] = ids_w[tid];
       li.w_out[tid] = w_w[tid];
     }
-    gu_load<NJ, RW>(a, b, i0, gw, wl);
+    gu_load<NJ, RW>(a, b, i0, gw, wl, 0, eid);
   } else {
-    gu_load<NJ, RW>(a, b, i0, gw, wl);
+    gu_load<NJ, RW>(a, b, i0, gw, wl, 0, eid);
     form_x(lb == 0);
   }
   if (blk == 0 && tid == 0) {
@@ -666,7 +670,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
   if (sub < NSUB && rrd < r) {
     const uint4* src = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(b + a.lay.a_down) + (size_t)rrd * a.I + i0 + 16 * sub);
+        reinterpret_cast<const uint16_t*>(E0_LORA_E(a, b, eid, 4, a.lay.a_down)) + (size_t)rrd * a.I +
+        i0 + 16 * sub);
     ad0 = src[0];
     ad1 = src[1];
   }

@@ -10,9 +10,10 @@ namespace e0 {
 // the factor at bundle offset off: the bundle's copy, or the separate
 // adapter of expert ids[k] (clamped into range: an invalid id's expert has
 // weight 0 and is reported by the slot resolution).
-#define E0_LORA(a, b, k, i, off)                                                             \
-  ((a).lora_sep ? (a).lo_base[i] + (size_t)max(0, min((a).ids[k], (a).E - 1)) * (a).lo_stride \
+#define E0_LORA_E(a, b, e, i, off)                                                        \
+  ((a).lora_sep ? (a).lo_base[i] + (size_t)max(0, min((e), (a).E - 1)) * (a).lo_stride \
                 : (b) + (off))
+#define E0_LORA(a, b, k, i, off) E0_LORA_E(a, b, (a).ids[k], i, off)
 
 struct MoeArgs {
   const uint8_t* pool;

@@ -71,6 +71,7 @@ struct edge0_stack {
   hipEvent_t ev_heads;       // staged steps: the heads of the step have run
   int32_t* loop_host;        // staged closed loop: pinned [2][L][K] ids read back
   int head_schedule;         // EDGE0_HEADS_FOLDED (default) or EDGE0_HEADS_AFTER_LAYERS
+  std::vector<edge0_lora> loras;  // adapters given apart, one table per layer (empty: in the bundles)
   // persistent mode (EDGE0_STACK_PERSISTENT)
   int mode;
   uint32_t* flow_cnt;                // [kFlowMaxPhases][kFlowCounters][64] arrival counters
@@ -99,6 +100,16 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
 
 // fc1 false: the heads' fc1 rows ran beside the layers; only fc2 and the commits here
 static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1 = true);
+
+// Layer L's adapters given apart (edge0_stack_create_lora), if any
+static void stack_lora(const edge0_stack* st, int L, MoeArgs& a) {
+  if (st->loras.empty() || st->shape.lora_rank == 0) return;
+  const edge0_lora& lo = st->loras[L];
+  const void* f[6] = {lo.a_gate, lo.b_gate, lo.a_up, lo.b_up, lo.a_down, lo.b_down};
+  a.lora_sep = true;
+  for (int i = 0; i < 6; ++i) a.lo_base[i] = static_cast<const uint8_t*>(f[i]);
+  a.lo_stride = lo.expert_stride * 2;  // bf16 elements
+}
 
 // The routing layer L executes at step s (its ids and weights).
 static int32_t* layer_ids(const edge0_stack* st, int L, int s) {
@@ -261,8 +272,9 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
     HeadPart hpart;
     const HeadPart* hp = folded_fc1(st, L, step, &hpart) ? &hpart : nullptr;
     int rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
-                           st->y + (size_t)L * d, st->ws, &a);
+                           st->y + (size_t)L * d, st->ws, &a, st->loras.empty());
     if (rc != EDGE0_OK) return rc;
+    stack_lora(st, L, a);
     a.spin = st->spin;
     // fixed-point y accumulators alternate between layers
     unsigned long long* acc0 = a.acc;
@@ -503,13 +515,20 @@ static int enqueue_xstep_step(edge0_stack* st, int step, hipStream_t stream) {
   return enqueue_tail(st, step, stream);
 }
 
-extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
-                                  const edge0_stack_spec* spec, const edge0_slot_pool* pool,
-                                  const int32_t* slot_tables, const void* const* routers,
-                                  const edge0_head* heads) {
+static int stack_create(edge0_stack** out, const edge0_moe_shape* shape,
+                        const edge0_stack_spec* spec, const edge0_slot_pool* pool,
+                        const int32_t* slot_tables, const void* const* routers,
+                        const edge0_head* heads, const edge0_lora* loras) {
   if (!out || !shape || !shape_ok(shape) || !spec || !pool || !pool->base || !slot_tables ||
       !routers || !heads)
     return EDGE0_EINVAL;
+  if (loras != nullptr && shape->lora_rank > 0)
+    for (int L = 0; L < spec->n_layers; ++L) {
+      const edge0_lora& lo = loras[L];
+      if (!lo.a_gate || !lo.b_gate || !lo.a_up || !lo.b_up || !lo.a_down || !lo.b_down ||
+          lo.expert_stride < 0)
+        return EDGE0_EINVAL;
+    }
   // the step's fused routing (router layers and heads) is softmax-top-K
   if (shape->routing != EDGE0_ROUTE_SOFTMAX_TOPK) return EDGE0_EINVAL;
   const int Lc = spec->n_layers;
@@ -536,6 +555,7 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   st->tables = slot_tables;
   st->routers.assign(routers, routers + Lc);
   st->heads.assign(heads, heads + Lc);
+  if (loras != nullptr && shape->lora_rank > 0) st->loras.assign(loras, loras + Lc);
   st->last_step = -1;
   st->spin = kFlowDefaultSpin;
   st->head_schedule = EDGE0_HEADS_FOLDED;
@@ -610,6 +630,21 @@ extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shap
   }
   *out = st;
   return EDGE0_OK;
+}
+
+extern "C" int edge0_stack_create(edge0_stack** out, const edge0_moe_shape* shape,
+                                  const edge0_stack_spec* spec, const edge0_slot_pool* pool,
+                                  const int32_t* slot_tables, const void* const* routers,
+                                  const edge0_head* heads) {
+  return stack_create(out, shape, spec, pool, slot_tables, routers, heads, nullptr);
+}
+
+extern "C" int edge0_stack_create_lora(edge0_stack** out, const edge0_moe_shape* shape,
+                                       const edge0_stack_spec* spec, const edge0_slot_pool* pool,
+                                       const int32_t* slot_tables, const void* const* routers,
+                                       const edge0_head* heads, const edge0_lora* layer_loras) {
+  if (shape && shape->lora_rank > 0 && !layer_loras) return EDGE0_EINVAL;
+  return stack_create(out, shape, spec, pool, slot_tables, routers, heads, layer_loras);
 }
 
 extern "C" int edge0_stack_step(edge0_stack* st, const void* h0, void* h_out, int32_t step,
@@ -701,8 +736,9 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
              : plan.ids_dev + (size_t)L * K;
     float* w = w_exec + (size_t)L * K;
     rc = fill_moe_args(&sh, &st->pool, st->tables + (size_t)L * E, ids, w, xL,
-                       st->y + (size_t)L * d, st->ws, &a);
+                       st->y + (size_t)L * d, st->ws, &a, st->loras.empty());
     if (rc != EDGE0_OK) return rc;
+    stack_lora(st, L, a);
     unsigned long long* acc0 = a.acc;
     a.acc = acc0 + (size_t)(L & 1) * d;
     a.acc_prev = acc0 + (size_t)((L + 1) & 1) * d;
@@ -900,6 +936,8 @@ extern "C" int edge0_stack_set_mode(edge0_stack* st, int32_t mode) {
   if (!st || (mode != EDGE0_STACK_GRAPHS && mode != EDGE0_STACK_PERSISTENT &&
               mode != EDGE0_STACK_XCD && mode != EDGE0_STACK_XLAYER))
     return EDGE0_EINVAL;
+  // the one-launch and XCD-split modes read the adapters from the bundles
+  if (mode != EDGE0_STACK_GRAPHS && !st->loras.empty()) return EDGE0_EINVAL;
   if (mode == EDGE0_STACK_XLAYER) {
     if (!xstep_shape_ok(st->shape, st->spec.n_layers)) return EDGE0_EINVAL;
     if (!st->xl_acc) {

@@ -155,6 +155,9 @@ _SIG = {
                                   _P, _P]),
     "edge0_stack_create": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.POINTER(StackSpec),
                                      C.POINTER(SlotPool), _P, C.POINTER(_P), C.POINTER(Head)]),
+    "edge0_stack_create_lora": (C.c_int, [C.POINTER(_P), C.POINTER(MoeShape), C.POINTER(StackSpec),
+                                          C.POINTER(SlotPool), _P, C.POINTER(_P), C.POINTER(Head),
+                                          _P]),
     "edge0_stack_step": (C.c_int, [_P, _P, _P, C.c_int32, _P]),
     "edge0_stack_get_buffers": (C.c_int, [_P, C.POINTER(StackBuffers)]),
     "edge0_stack_destroy": (None, [_P]),
@@ -400,16 +403,26 @@ class Stack(_Handle):
     """Owner of an edge0_stack handle (decode stack runtime)."""
 
     def __init__(self, shape: MoeShape, spec: StackSpec, pool: SlotPool, slot_tables, routers,
-                 heads):
+                 heads, loras=None):
+        """loras: None (adapters in the bundles) or one Lora per layer
+        (edge0_stack_create_lora)."""
         self.shape, self.spec = shape, spec
-        self._keep = (slot_tables, routers, heads)
+        self._keep = (slot_tables, routers, heads, loras)
         n = spec.n_layers
         router_ptrs = (C.c_void_p * n)(*[_ptr(r) for r in routers])
         head_arr = (Head * n)(*[make_head(h) if h is not None else Head() for h in heads])
         self._handle = C.c_void_p()
-        _check(lib.edge0_stack_create(C.byref(self._handle), C.byref(shape), C.byref(spec),
-                                      C.byref(pool), _ptr(slot_tables), router_ptrs, head_arr),
-               "edge0_stack_create")
+        if loras is None:
+            _check(lib.edge0_stack_create(C.byref(self._handle), C.byref(shape), C.byref(spec),
+                                          C.byref(pool), _ptr(slot_tables), router_ptrs, head_arr),
+                   "edge0_stack_create")
+        else:
+            lora_arr = (Lora * n)(*loras)
+            self._keep = self._keep + (lora_arr,)
+            _check(lib.edge0_stack_create_lora(C.byref(self._handle), C.byref(shape), C.byref(spec),
+                                               C.byref(pool), _ptr(slot_tables), router_ptrs,
+                                               head_arr, C.cast(lora_arr, C.c_void_p)),
+                   "edge0_stack_create_lora")
         self._register()
 
     def step(self, h0, h_out, step: int, stream=None):

@@ -20,7 +20,10 @@ class DeviceStack:
     bf16 bits [E][d], head(L) -> dict of fp16 head arrays."""
 
     def __init__(self, shape, gen, n_layers=40, owners=(6, 37), consumers=(7, 38), eps=1e-6,
-                 threads=16, log=print):
+                 threads=16, log=print, separate_lora=False):
+        """separate_lora: LoRA-free bundles in the pool and each layer's
+        adapters in a device block of their own, one per expert
+        (edge0_stack_create_lora)."""
         self.S = shape
         self.sh = E.make_shape(shape)
         En = shape.n_experts
@@ -28,11 +31,21 @@ class DeviceStack:
         self.spec = E.StackSpec(n_layers, owners[0], owners[1], consumers[0], consumers[1], eps)
         self.owners = range(owners[0], owners[1] + 1)
         self.consumers = range(consumers[0], consumers[1] + 1)
-        self.pool = SlotPoolBuffer(self.sh, n_layers * En)
+        sep = separate_lora and shape.lora_rank > 0
+        self.sh_pool = E.make_shape(shape)
+        if sep:
+            self.sh_pool.lora_rank = 0  # the bundles hold the int4 arrays only
+        self.pool = SlotPoolBuffer(self.sh_pool, n_layers * En)
+        self.lora_blocks, self.loras = [], None
         t0 = time.time()
         with ThreadPoolExecutor(threads) as ex:
             for L in range(n_layers):
                 parts = list(ex.map(lambda e: (gen.expert(L, e), gen.lora(L, e)), range(En)))
+                if sep:
+                    lo, block = lora_block([p[1] for p in parts])
+                    self.lora_blocks.append(block)
+                    self.loras = (self.loras or []) + [lo]
+                    parts = [(p[0], None) for p in parts]
                 self._pack_layer(L, parts)
                 if log and (L % 8 == 7 or L == n_layers - 1):
                     log(f"[stack] packed layer {L + 1}/{n_layers} ({time.time() - t0:.1f}s)")
@@ -44,17 +57,32 @@ class DeviceStack:
         self.tables = torch.arange(n_layers * En, dtype=torch.int32, device="cuda").view(n_layers, En)
         torch.cuda.synchronize()
         self.stack = E.Stack(self.sh, self.spec, self.pool.pool, self.tables, self.routers,
-                             self.heads)
+                             self.heads, loras=self.loras)
         if log:
             log(f"[stack] ready: {n_layers} layers, pool {self.pool.mem.numel() / 1e9:.2f} GB "
                 f"({time.time() - t0:.1f}s)")
 
     def _pack_layer(self, L, parts):
         En = self.S.n_experts
-        pack_layer(self.sh, parts, lambda e: self.pool.slot_ptr(L * En + e))
+        pack_layer(self.sh_pool, parts, lambda e: self.pool.slot_ptr(L * En + e))
 
     def step(self, h0, h_out, step):
         self.stack.step(h0, h_out, step)
+
+
+LORA_FACTORS = ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+
+
+def lora_block(loras):
+    """One layer's adapters (loras[e] = the six bf16 factor arrays of expert
+    e) as one device block, [E][a_gate|b_gate|a_up|b_up|a_down|b_down], and
+    the Lora struct pointing at expert 0's factors with a stride of one
+    expert's block."""
+    rows = [np.concatenate([np.asarray(lo[f]).ravel() for f in LORA_FACTORS]) for lo in loras]
+    block = to_device(np.ascontiguousarray(np.stack(rows)).view(np.uint16))
+    offs = np.cumsum([0] + [np.asarray(loras[0][f]).size for f in LORA_FACTORS])
+    base = block.data_ptr()
+    return E.Lora(*[base + 2 * int(offs[i]) for i in range(6)], rows[0].size), block
 
 
 def pack_layer(sh, parts, dst_of):

@@ -197,6 +197,43 @@ def test_head_schedules_agree_bit_for_bit(torch_cuda, which):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("which", ["tiny", "qwen3moe"])
+def test_stack_separate_adapters_bit_identical(torch_cuda, which):
+    """edge0_stack_create_lora over LoRA-free bundles, each layer's adapters
+    in a block of their own, gives the bundled stack's bits in every buffer
+    of every step; the one-launch modes refuse such a stack."""
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    from int4_expert_streaming_amd.stackbuild import DeviceStack
+    from int4_expert_streaming_amd.weights import to_device
+    if which == "tiny":
+        S, seed, n, own, con = G.TINY, 6, 10, (2, 7), (3, 8)
+    else:
+        S, seed, n, own, con = G.QWEN3_MOE, 22, 40, (6, 37), (7, 38)
+    h_out = torch.zeros(S.d_model, dtype=torch.int16, device="cuda")
+    runs = []
+    for sep in (False, True):
+        print(f"[stack] {which}: adapters apart {sep}", flush=True)
+        ds = DeviceStack(S, G.StackGen(S, seed), n, own, con, log=None, separate_lora=sep)
+        snaps = []
+        for t in range(4):
+            ds.step(to_device(G.stack_hidden(S, seed, t)), h_out, t)
+            snaps.append(_snapshot(ds))
+        assert ds.stack.error() == E.EDGE0_OK
+        if sep:
+            assert ds.pool.slot_bytes < E.edge0_bundle_layout_of(ds.sh).bytes  # LoRA-free
+            with pytest.raises(E.Edge0Error):
+                ds.stack.set_mode(E.EDGE0_STACK_PERSISTENT)
+        runs.append(snaps)
+        del ds
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    for t in range(4):
+        for k in runs[0][t]:
+            assert np.array_equal(runs[0][t][k], runs[1][t][k]), (which, t, k)
+
+
+@pytest.mark.timeout(900)
 def test_qwen3moe_stack_free_bias_both_modes(torch_cuda):
     """The same stack with group biases drawn independently of the scales
     (b ~ U[-0.16, 0.04]), so a kernel that ignored b or derived it from s
