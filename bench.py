@@ -94,15 +94,15 @@ def step_bytes(S, n_routers):
 def fused_bytes(S):
     """Algorithmic bytes of one k_layer_fused launch (prediction-routed
     layer: input + gate/up): the K experts' gate and up int4 rows with scales
-    and biases, their LoRA A_gate/A_up rows and B_gate/B_up, the A_down
-    columns, the previous layer's h and fixed-point y, and what it writes
-    (h, y, x, the cleared accumulator, h as fp32 and hi/lo pairs, the 16-row
-    sums and A_down h partials)."""
+    and biases, their LoRA A_gate/A_up rows, the previous layer's h and
+    fixed-point y, and what it writes (h, y, x, the cleared accumulator, the
+    gate/up rows before their LoRA terms as fp32, and t = A x).  The LoRA B
+    terms, the SwiGLU and A_down h are the down launch's."""
     d, I, K, g, r = S.d_model, S.d_inter, S.top_k, S.group, S.lora_rank
     w = K * 2 * (I * d // 2 + 2 * I * (d // g) * 2)
-    lora = K * (2 * r * d * 2 + 2 * I * r * 2 + r * I * 2)
+    lora = K * 2 * r * d * 2
     reads = d * 2 + d * 8
-    writes = 3 * d * 2 + d * 8 + K * I * (4 + 2 + 2) + K * (I // 16) * (1 + r) * 4
+    writes = 3 * d * 2 + d * 8 + K * 2 * I * 4 + K * 2 * r * 4
     return w + lora + reads + writes
 
 
@@ -1210,9 +1210,10 @@ def main():
                          "default, the fastest here), the layers as one persistent launch per "
                          "step, the XCD-split persistent launch, or one XCD-split launch per "
                          "layer")
-    ap.add_argument("--head-schedule", choices=["folded", "after"], default="folded",
-                    help="graphs mode: the heads' rows beside the down launches (default) or "
-                         "batched after the last layer; the other is timed too for comparison")
+    ap.add_argument("--head-schedule", choices=["folded", "after"], default="after",
+                    help="graphs mode: the heads batched after the last layer (default) or "
+                         "their fc1 rows beside the down launches; the other is timed too for "
+                         "comparison")
     ap.add_argument("--no-head-ab", action="store_true",
                     help="do not time the other head schedule (profiling runs)")
     ap.add_argument("--mfma-sweep", action="store_true",

@@ -516,12 +516,12 @@ int edge0_stack_set_mode(edge0_stack* st, int32_t mode);
  * ([Edge0] §3.2 "Head": the heads' evaluation stays off the layers'
  * dependent chain; "Motivation": a head's prediction is consumed at the next
  * token, so nothing in the step waits for it):
- *   EDGE0_HEADS_FOLDED (default): head L's fc1 rows run as workgroups
- *     appended to layer L's down-projection launch, and its fc2 rows and
- *     routing commit as workgroups appended to layer L+1's, so no head
- *     launch follows the last layer;
- *   EDGE0_HEADS_AFTER_LAYERS: all heads as one batch (two launches) after
- *     the last layer.
+ *   EDGE0_HEADS_AFTER_LAYERS (default): all heads as one batch (two
+ *     launches: fc1 rows, then fc2 rows and the routing commits) after the
+ *     last layer;
+ *   EDGE0_HEADS_FOLDED: head L's fc1 rows run as workgroups appended to
+ *     layer L's down-projection launch; the fc2 rows and commits stay one
+ *     batch after the last layer.
  * The predictions are the same bit for bit either way (the same rows and
  * commit code over the same inputs).  The other modes and the staged step
  * run the heads after the layers whatever the setting.  Changing it waits

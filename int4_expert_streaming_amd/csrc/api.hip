@@ -84,7 +84,7 @@ WsLayout ws_layout(const edge0_moe_shape* s) {
   L.t_in = take(4 * K * 2 * r);
   L.t_hand = take(4 * K * 2 * r);
   L.lg_hand = take(4 * 2 * E);
-  L.hf = take(4 * K * I);
+  L.gu_pre = take(8 * K * I);
   L.hp_hi = take(2 * K * I);
   L.hp_lo = take(2 * K * I);
   L.hs = take(4 * K * (I / 16));

@@ -565,7 +565,7 @@ struct WsLayout {
   size_t t_in;                                    // fp32 [K][2][r]
   size_t t_hand;                                  // fp32 [K][2r] LoRA A x handed between workgroups
   size_t lg_hand;                                 // fp32 [2][E] router logits handed between workgroups
-  size_t hf;                                      // fp32 [K][I]
+  size_t gu_pre;                                  // fp32 [K][2][I] gate/up rows before LoRA
   size_t hp_hi, hp_lo;                            // u16 [K][I]
   size_t hs;                                      // fp32 [K][I/16]
   size_t tdpart;                                  // fp32 [K][I/16][r]

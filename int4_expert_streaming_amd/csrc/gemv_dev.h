@@ -15,13 +15,12 @@ __device__ __forceinline__ int pair_pos(int i) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.f + expf(-z)); }
 
-// store one row of h: fp32, the bf16 hi/lo split (hi = bf16(h), lo = bf16(h - hi));
+// store one row of h as its bf16 hi/lo split (hi = bf16(h), lo = bf16(h - hi));
 // returns hi + lo, the value the down GEMV sees
 __device__ __forceinline__ float store_h(const MoeArgs& a, int k, int i, float h) {
   const uint32_t hi = f2bf(h);
   const uint32_t lo = f2bf(h - bf2f(hi));
   const size_t base = (size_t)k * a.I;
-  a.hf[base + i] = h;
   a.hp_hi[base + pair_pos(i)] = (uint16_t)hi;
   a.hp_lo[base + pair_pos(i)] = (uint16_t)lo;
   return bf2f(hi) + bf2f(lo);

@@ -332,9 +332,11 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 //    workgroup and stores t = A x for its rows into t_hand;
 //  - K * d_inter / 16 gate/up workgroups (16 rows of one routed expert):
 //    each loads its int4 rows, forms x redundantly from L2-resident data
-//    (previous layer's fixed-point y, h, RMSNorm) into LDS and computes the
-//    rows' dot products, while a ninth wave waits (bounded) for the
-//    expert's t in t_hand; then the LoRA term and the SwiGLU epilogue.
+//    (previous layer's fixed-point y, h, RMSNorm) into LDS, computes the
+//    rows' dot products and stores them, without the LoRA term, to gu_pre.
+// The LoRA B t terms and the SwiGLU are the down kernel's (down_unit with
+// DEFER): t crosses the kernel boundary, so no workgroup of this launch
+// waits for another's stores.
 // ROUTE (a router layer): the producers first compute a.route_rows router
 // logits each from x and publish them through lg_hand (parity a.par; the
 // down kernel that follows empties them again); every workgroup then commits the
@@ -352,7 +354,7 @@ constexpr int kFusedRowsPerWave = 2;  // 8 waves: 16 rows of gate and up per wor
 constexpr int kFusedMaxExperts = 256;  // slot-table row held in 4 registers per lane
 constexpr int kFusedMaxProdRows = 8;   // A rows per producer: 2, 4 or 8
 constexpr int kFusedMaxRouteRows = 4;  // router rows per producer
-constexpr int kFusedThreads = 576;     // 8 compute waves + the hand-off wave
+constexpr int kFusedThreads = 512;     // 8 waves
 
 // slot of a (wave-uniform) expert id from the layer's table row held as
 // entries l + 64 j in word j of lane l; -1 when the id or the slot is out of
@@ -373,11 +375,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   constexpr int MU = kFusedMaxProdRows * NJ / 2;        // producer: A pieces per thread (max)
   constexpr int MR = (kFusedMaxRouteRows * NJ + 1) / 2;  // producer: router pieces per thread
   __shared__ uint16_t xs[2048 * NJ];
-  __shared__ float t_s[2][kFusedMaxRank];
   __shared__ float red[8];
   __shared__ float redp[MU][8];
-  __shared__ float h_s[ROWS];
-  __shared__ float hrep_s[ROWS];
   __shared__ int32_t ids_w[16];
   __shared__ float w_w[16];
   __shared__ float lg_s[ROUTE ? kFusedMaxExperts : 1];
@@ -392,11 +391,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
                "s"(li.h_prev), "s"(a.lay.gate_q), "s"(a.lay.up_q), "s"(a.lay.gate_s),
                "s"(a.lay.gate_b), "s"(a.lay.up_s), "s"(a.lay.up_b));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // compute waves 0-7; wave 8 waits for the hand-off.  Wave 8 issues wave
-  // 0's loads too (tl, wl): no branch then separates any wave's loads from
-  // their first use, so each wait covers only the loads issued before them
-  const bool cw = wave < 8;
-  const int tl = cw ? tid : tid - 512, wl = cw ? wave : 0;
   const int d = a.d, r = a.r;
   const int nwg = a.I / ROWS;
   const int P = a.n_prod;
@@ -432,7 +426,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
   unsigned long long av[PER];
 #pragma unroll
   for (int c = 0; c < NJ; ++c) {
-    const int j0 = 4 * (tl + 512 * c);
+    const int j0 = 4 * (tid + 512 * c);
     hq[c] = *reinterpret_cast<const uint2*>(li.h_prev + j0);
     const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0);
     const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(a.acc_prev + j0 + 2);
@@ -470,41 +464,37 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
     for (int m = 0; m < PER; ++m) asm volatile("" : "+v"(av[m]));
     float hv[PER];
     float ss = 0.f;
-    if (cw) {
-      uint32_t hb[PER];
+    uint32_t hb[PER];
 #pragma unroll
-      for (int c = 0; c < NJ; ++c) {
-        hb[4 * c + 0] = hq[c].x & 0xFFFFu;
-        hb[4 * c + 1] = hq[c].x >> 16;
-        hb[4 * c + 2] = hq[c].y & 0xFFFFu;
-        hb[4 * c + 3] = hq[c].y >> 16;
-      }
-#pragma unroll
-      for (int m = 0; m < PER; ++m) {
-        const uint32_t yb = comb ? f2bf(from_fix(av[m])) : 0u;
-        hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
-        ss = fmaf(hv[m], hv[m], ss);
-        av[m] = yb;  // keep y_prev's bits for the stores below
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) red[wave] = ss;
+    for (int c = 0; c < NJ; ++c) {
+      hb[4 * c + 0] = hq[c].x & 0xFFFFu;
+      hb[4 * c + 1] = hq[c].x >> 16;
+      hb[4 * c + 2] = hq[c].y & 0xFFFFu;
+      hb[4 * c + 3] = hq[c].y >> 16;
     }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const uint32_t yb = comb ? f2bf(from_fix(av[m])) : 0u;
+      hv[m] = bf2f(f2bf(bf2f(hb[m]) + bf2f(yb)));
+      ss = fmaf(hv[m], hv[m], ss);
+      av[m] = yb;  // keep y_prev's bits for the stores below
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
     for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
     const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
     uint32_t xw[2 * NJ];
-    if (cw) {
 #pragma unroll
-      for (int c = 0; c < NJ; ++c) {
-        xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
-        xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = make_uint2(xw[2 * c], xw[2 * c + 1]);
-      }
+    for (int c = 0; c < NJ; ++c) {
+      xw[2 * c] = f2bf(hv[4 * c] * inv) | (f2bf(hv[4 * c + 1] * inv) << 16);
+      xw[2 * c + 1] = f2bf(hv[4 * c + 2] * inv) | (f2bf(hv[4 * c + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(xs + 4 * (tid + 512 * c)) = make_uint2(xw[2 * c], xw[2 * c + 1]);
     }
     __syncthreads();
-    if (lead && cw) {
+    if (lead) {
 #pragma unroll
       for (int c = 0; c < NJ; ++c) {
         const int j0 = 4 * (tid + 512 * c);
@@ -565,7 +555,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       uint4 rp[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const int u = min(tl + 512 * m, max(nu - 1, 0));
+        const int u = min(tid + 512 * m, max(nu - 1, 0));
         rp[m] = reinterpret_cast<const uint4*>(li.w_router + (size_t)min(e0, a.E - 1) * d)[u];
       }
       form_x(false);
@@ -573,7 +563,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         const int u = tid + 512 * m;
-        if (512 * m < nu && cw) {  // uniform over each wave
+        if (512 * m < nu) {  // uniform over each wave
           const uint4 xq4 = xv[u % (d / 8)];
           float p = u < nu ? dot2bf(rp[m].x, xq4.x, 0.f) : 0.f;
           if (u < nu) {
@@ -608,7 +598,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
     uint4 ap[MU];
 #pragma unroll
     for (int m = 0; m < MU; ++m) {
-      const int u = min(tl + 512 * m, nu - 1);  // past nu: repeats of the last piece
+      const int u = min(tid + 512 * m, nu - 1);  // past nu: repeats of the last piece
       const int tr = tr0 + u / (d / 8);
       const uint4* row = reinterpret_cast<const uint4*>(
                              E0_LORA_E(a, b, eid, tr < r ? 0 : 2,
@@ -621,7 +611,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
 #pragma unroll
     for (int m = 0; m < MU; ++m) {
       const int u = tid + 512 * m;
-      if (512 * m < nu && cw) {  // uniform over each wave
+      if (512 * m < nu) {  // uniform over each wave
         const uint4 xq4 = xv[u % (d / 8)];
         float p = dot2bf(ap[m].x, xq4.x, 0.f);
         p = dot2bf(ap[m].y, xq4.y, p);
@@ -637,14 +627,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       for (int m = 0; 512 * m < nu; ++m)
         for (int w8 = 0; w8 < 8; ++w8)
           if ((512 * m + 64 * w8) / (d / 8) == tid) t += redp[m][w8];
-      if (!ok || __float_as_uint(t) == kTHandEmpty) t = ok ? __uint_as_float(0x7FC00000u) : 0.f;
-      st_dev(a.t_hand + (size_t)k * 2 * r + tr0 + tid, t);
+      a.t_hand[(size_t)k * 2 * r + tr0 + tid] = ok ? t : 0.f;
     }
     return;
   }
 
-  // gate/up workgroup: every weight load of the compute waves (HBM) and x;
-  // a routed layer loads the rows once its top-K is committed
+  // gate/up workgroup: every weight load (HBM) and x; a routed layer loads
+  // the rows once its top-K is committed
   GuW<NJ, RW> gw;
   if constexpr (ROUTE) {
     form_x(lb == 0);
@@ -654,80 +643,25 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
       li.ids_out[tid] = ids_w[tid];
       li.w_out[tid] = w_w[tid];
     }
-    gu_load<NJ, RW>(a, b, i0, gw, wl, 0, eid);
+    gu_load<NJ, RW>(a, b, i0, gw, wave, 0, eid);
   } else {
-    gu_load<NJ, RW>(a, b, i0, gw, wl, 0, eid);
+    gu_load<NJ, RW>(a, b, i0, gw, wave, 0, eid);
     form_x(lb == 0);
   }
   if (blk == 0 && tid == 0) {
     a.slots[k] = ok ? slot : -1;
     if (!ok) set_error(a.err, EDGE0_ERANGE);
   }
-  // A_down columns of the workgroup's rows: thread (sub, rr) = 16-row block
-  // sub, rank row rr
-  constexpr int NSUB = ROWS / 16;
-  const int sub = tid / 64, rrd = tid % 64;
-  uint4 ad0 = make_uint4(0, 0, 0, 0), ad1 = ad0;
-  if (sub < NSUB && rrd < r) {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(E0_LORA_E(a, b, eid, 4, a.lay.a_down)) + (size_t)rrd * a.I +
-        i0 + 16 * sub);
-    ad0 = src[0];
-    ad1 = src[1];
-  }
-  if (!ok) {
-    for (int t = tid; t < ROWS; t += 512) store_h(a, k, i0 + t, 0.f);
-    if (sub < NSUB && rrd < r) a.tdpart[((size_t)k * nblk + blk + sub) * r + rrd] = 0.f;
-    if (tid < NSUB) a.hs[(size_t)k * nblk + blk + tid] = 0.f;
-    return;
-  }
-  // 4. gate/up rows on x from LDS (compute waves), meanwhile the expert's
-  // t = A x from its producers (hand-off wave: lane l < 2r polls entry l)
+  // 4. the rows' dot products on x from LDS; lane (64 / 2RW) ii of the wave
+  // holds gate row ii, lane 32 + (64 / 2RW) ii its up row.  An invalid slot
+  // stores zeros (its producers store t = 0, so its h is 0).
   float v[2 * RW];
-  if (cw) {
-    gu_base<NJ, RW>(gw, xs, v);
-    // the dot products are done here, not after the barrier below
-#pragma unroll
-    for (int i = 0; i < 2 * RW; ++i) asm volatile("" : "+v"(v[i]));
-  } else if (r > 0 && lane < 2 * r) {
-    const float* src = a.t_hand + (size_t)k * 2 * r + lane;
-    uint32_t bits;
-    int64_t n = 0;
-    for (;;) {
-      bits = __float_as_uint(ld_dev(src));
-      if (bits != kTHandEmpty) break;
-      if (++n >= a.spin) {
-        set_error(a.err, EDGE0_EHIP);
-        bits = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    t_s[lane / r][lane % r] = __uint_as_float(bits);
-  }
-  __syncthreads();
-  // 5. the LoRA term and the 16-row epilogue
-  if (cw) {
-    float tg = 0.f, tu = 0.f;
-    if (r > 0 && lane < r) {
-      tg = t_s[0][lane];
-      tu = t_s[1][lane];
-    }
-    gu_epilogue<NJ, RW, true>(a, gw, k, i0, v, tg, tu, h_s, hrep_s);
-  }
-  __syncthreads();
-  if (tid < NSUB) {
-    float sm = 0.f;
-    for (int t = 0; t < 16; ++t) sm += hrep_s[16 * tid + t];
-    a.hs[(size_t)k * nblk + blk + tid] = sm;
-  }
-  if (sub < NSUB && rrd < r) {
-    const uint32_t wd[8] = {ad0.x, ad0.y, ad0.z, ad0.w, ad1.x, ad1.y, ad1.z, ad1.w};
-    const float* hsb = h_s + 16 * sub;
-    float sm = 0.f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) sm += bf_lo(wd[m]) * hsb[2 * m] + bf_hi(wd[m]) * hsb[2 * m + 1];
-    a.tdpart[((size_t)k * nblk + blk + sub) * r + rrd] = sm;
+  gu_base<NJ, RW>(gw, xs, v);
+  const float s1 = wave_sums_2r<RW>(v);
+  constexpr int kSpan = 64 / (2 * RW);
+  if ((lane & 31) % kSpan == 0) {
+    const int ii = (lane & 31) / kSpan, half = lane >> 5;
+    a.gu_pre[((size_t)k * 2 + half) * a.I + i0 + RW * wave + ii] = ok ? s1 : 0.f;
   }
 }
 
@@ -743,16 +677,26 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
 // all of a wave's tile loads are in flight together.  An expert whose slot is
 // invalid reads slot 0 with weight 0 (never an out-of-range address).
 constexpr int kMaxSliceChunks = 64;  // expert-chunks per unit staged in LDS
+constexpr int kMaxDeferT = 16 * 2 * kFusedMaxRank;  // t of up to 16 routed experts
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // One down unit: workgroup `bid` of the (d / 64) * S units.
-template <int TPW>
+// DEFER (after the fused layer kernel): the unit first finishes its tiles'
+// rows of h from gu_pre: each wave takes its own tiles, lane j < 32 row j of
+// the chunk's gate and lane 32 + j its up row, adds the LoRA term
+// scale * B[row] . t (t = A x of the expert, from the producers' t_hand),
+// and lane j forms h = SiLU(gate) * up, its hi/lo split, the chunk sum and
+// (with the A_down columns of the chunk) the chunk's part of A_down h.
+// Otherwise those come staged from the gate/up kernel's workspace rows.
+template <int TPW, bool DEFER>
 __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) {
   __shared__ float red[4][64];
   __shared__ uint32_t hp_s[kMaxSliceChunks][32];  // hi pairs then lo pairs of each chunk
   __shared__ float hsum_s[kMaxSliceChunks];
   __shared__ float tdc_s[kMaxSliceChunks][64];    // per tile: the chunk's part of A_down h
+  __shared__ float hf_s[DEFER ? 4 * TPW : 1][32];   // DEFER: each tile's h rows (fp32)
+  __shared__ float tt_s[DEFER ? kMaxDeferT : 1];    // DEFER: t of the K experts
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int K = a.K, S = a.S, I = a.I, r = a.r, d = a.d;
@@ -770,6 +714,10 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
   float wt[TPW];
   constexpr int kBd = 2;  // B_down pieces (8 ranks each) held per tile; more are read in the loop
   uint4 bdq[TPW][kBd];
+  // DEFER: lane (half = lane / 32, j = lane % 32): B_gate / B_up row 32 c + j
+  // (kFusedMaxRank = 16 ranks: two pieces); lane (qq = lane / 16, rr = lane % 16):
+  // A_down[rr][32 c + 8 qq .. + 7]
+  uint4 bgu[DEFER ? TPW : 1][2], adq[DEFER ? TPW : 1];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int t = wave * TPW + m;
@@ -791,9 +739,81 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
         (size_t)o * r);
 #pragma unroll
     for (int j = 0; j < kBd; ++j) bdq[m][j] = (8 * j < r) ? Bdp[j] : make_uint4(0, 0, 0, 0);
+    if constexpr (DEFER) {
+      const int half = lane >> 5, row = 32 * c + (lane & 31);
+      const uint4* Bp = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(
+              r > 0 ? E0_LORA(a, b, kk, half ? 3 : 1, half ? a.lay.b_up : a.lay.b_gate) : b) +
+          (size_t)(r > 0 ? row : 0) * r);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bgu[m][j] = (8 * j < r) ? Bp[j] : make_uint4(0, 0, 0, 0);
+      const int rr = lane & 15, qq = lane >> 4;
+      adq[m] = rr < r ? reinterpret_cast<const uint4*>(
+                            reinterpret_cast<const uint16_t*>(E0_LORA(a, b, kk, 4, a.lay.a_down)) +
+                            (size_t)rr * I + 32 * c + 8 * qq)[0]
+                      : make_uint4(0, 0, 0, 0);
+    }
   }
-  // stage the unit's activation pairs and chunk sums (all K experts) in LDS
-  {
+  if constexpr (DEFER) {
+    // the previous launch's outputs: each tile's gate/up rows and t
+    float gu[TPW];
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wave * TPW + m;
+      const int tc = t < nt ? t : 0;
+      const int kk = tc / ncs, c = c0 + tc % ncs;
+      gu[m] = a.gu_pre[((size_t)kk * 2 + (lane >> 5)) * I + 32 * c + (lane & 31)];
+    }
+    for (int i = threadIdx.x; i < K * 2 * r; i += 256) tt_s[i] = a.t_hand[i];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wave * TPW + m;
+      const int tc = t < nt ? t : 0;
+      const int kk = tc / ncs;
+      // the row's LoRA term: B[row] . t over the r ranks
+      const float* tv = tt_s + (size_t)kk * 2 * r + (lane >> 5) * r;
+      const uint32_t bw[8] = {bgu[m][0].x, bgu[m][0].y, bgu[m][0].z, bgu[m][0].w,
+                              bgu[m][1].x, bgu[m][1].y, bgu[m][1].z, bgu[m][1].w};
+      float dl = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 8; ++q2)
+        if (2 * q2 < r) {
+          dl += bf_lo(bw[q2]) * tv[2 * q2];
+          dl += bf_hi(bw[q2]) * tv[2 * q2 + 1];
+        }
+      const float pre = gu[m] + a.scale * dl;
+      const float up = __shfl_xor(pre, 32, kWave);
+      const float h = silu_f(pre) * up;  // lanes j < 32
+      const uint32_t hi = f2bf(h);
+      const uint32_t lo = f2bf(h - bf2f(hi));
+      float hr = lane < 32 ? bf2f(hi) + bf2f(lo) : 0.f;
+      if (lane < 32) {
+        const int pos = pair_pos(lane);
+        uint16_t* hp16 = reinterpret_cast<uint16_t*>(hp_s[wave * TPW + m]);
+        hp16[pos] = (uint16_t)hi;
+        hp16[32 + pos] = (uint16_t)lo;
+        hf_s[wave * TPW + m][lane] = h;
+      }
+      hr = wave_sum(hr);
+      if (lane == 0) hsum_s[wave * TPW + m] = hr;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      // the chunk's part of A_down h: lane (qq, rr) over rows 8 qq .. 8 qq + 7
+      const int rr = lane & 15, qq = lane >> 4;
+      const float* hq = hf_s[wave * TPW + m] + 8 * qq;
+      const uint32_t aw[4] = {adq[m].x, adq[m].y, adq[m].z, adq[m].w};
+      float sm = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) sm += bf_lo(aw[q2]) * hq[2 * q2] + bf_hi(aw[q2]) * hq[2 * q2 + 1];
+      sm += __shfl_xor(sm, 16, kWave);
+      sm += __shfl_xor(sm, 32, kWave);
+      if (qq == 0) tdc_s[wave * TPW + m][rr] = sm;
+    }
+  } else {
+    // stage the unit's activation pairs and chunk sums (all K experts) in LDS
     constexpr int kStage = kMaxSliceChunks * 32 / 256;  // words per thread
     uint32_t st[kStage];
 #pragma unroll
@@ -834,10 +854,8 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
       const int slot = a.slots[threadIdx.x];
       if (slot < 0 || slot >= a.n_slots) set_error(a.err, EDGE0_ERANGE);
     }
-    // the layer kernel before this one has consumed the LoRA hand-off
-    // entries: empty them for the next
-    for (int i = threadIdx.x; i < K * 2 * r; i += 256) a.t_hand[i] = __uint_as_float(kTHandEmpty);
-    // and the router logits it read, if it was a router layer
+    // the router logits the layer kernel before this one read, if it was a
+    // router layer: empty them for the next
     if (a.lg_consumed != nullptr)
       for (int i = threadIdx.x; i < a.E; i += 256) a.lg_consumed[i] = __uint_as_float(kTHandEmpty);
   }
@@ -884,9 +902,9 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
     atomicAdd(a.acc + o, to_fix(red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]));
 }
 
-template <int TPW>
+template <int TPW, bool DEFER>
 __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
-  down_unit<TPW>(a, blockIdx.x);
+  down_unit<TPW, DEFER>(a, blockIdx.x);
 }
 
 // The same launch with one prerouter head's fc1 rows beside it (the stack's
@@ -894,14 +912,14 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
 // (dispatched first, so their loads go out before the units'), row y = 1 the
 // down units.  The role comes from the workgroup id alone, so no argument
 // load stands between a unit's start and its weight loads.
-template <int TPW>
+template <int TPW, bool DEFER>
 __global__ __launch_bounds__(256) void k_down_fc1(MoeArgs a, HeadPart h) {
   if (blockIdx.y == 0) {
     if ((int)blockIdx.x < h.n_wg) head_fc1_row(h, blockIdx.x * kHeadFc1Rows + (threadIdx.x >> 6));
     return;
   }
   if ((int)blockIdx.x >= (a.d / 64) * a.S) return;
-  down_unit<TPW>(a, blockIdx.x);
+  down_unit<TPW, DEFER>(a, blockIdx.x);
 }
 
 // y = bf16 of the layer's fixed-point accumulator; optional residual
@@ -996,7 +1014,7 @@ int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const 
   for (auto& p : a->lo_base) p = nullptr;
   a->err_out = nullptr;
   a->spin = kFusedDefaultSpin;
-  a->hf = reinterpret_cast<float*>(ws + L.hf);
+  a->gu_pre = reinterpret_cast<float*>(ws + L.gu_pre);
   a->hp_hi = reinterpret_cast<uint16_t*>(ws + L.hp_hi);
   a->hp_lo = reinterpret_cast<uint16_t*>(ws + L.hp_lo);
   a->hs = reinterpret_cast<float*>(ws + L.hs);
@@ -1070,32 +1088,43 @@ int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming
   return launch_down(a, stream, timing, fc1);
 }
 
-template <int TPW>
+template <int TPW, bool DEFER>
 static void launch_down_t(const MoeArgs& a, int units, const HeadPart* fc1, hipStream_t stream) {
   if (fc1 == nullptr) {
-    k_down<TPW><<<units, 256, 0, stream>>>(a);
+    k_down<TPW, DEFER><<<units, 256, 0, stream>>>(a);
   } else {
-    k_down_fc1<TPW><<<dim3(std::max(units, fc1->n_wg), 2), 256, 0, stream>>>(a, *fc1);
+    k_down_fc1<TPW, DEFER><<<dim3(std::max(units, fc1->n_wg), 2), 256, 0, stream>>>(a, *fc1);
   }
 }
 
+template <bool DEFER>
+static int launch_down_tpw(const MoeArgs& a, int tpw, int units, const HeadPart* fc1,
+                           hipStream_t stream) {
+  if (tpw <= 1) launch_down_t<1, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 2) launch_down_t<2, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 3) launch_down_t<3, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 4) launch_down_t<4, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 6) launch_down_t<6, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 8) launch_down_t<8, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 12) launch_down_t<12, DEFER>(a, units, fc1, stream);
+  else if (tpw <= 16) launch_down_t<16, DEFER>(a, units, fc1, stream);
+  else return EDGE0_EINVAL;
+  return EDGE0_OK;
+}
+
 int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing,
-                const HeadPart* fc1) {
+                const HeadPart* fc1, bool defer) {
   if (fc1 != nullptr && fc1->n_wg < 1) return EDGE0_EINVAL;
+  // DEFER finishes the fused layer kernel's rows: at most 16 ranks and 16 experts
+  if (defer && (a.r > kFusedMaxRank || a.r % 8 != 0 || a.K > 16)) return EDGE0_EINVAL;
   E0_MARK(2, true);
   {
     const int NC = a.I / 32, cps = (NC + a.S - 1) / a.S;
     const int tpw = (a.K * cps + 3) / 4;
     const int units = (a.d / 64) * a.S;
-    if (tpw <= 1) launch_down_t<1>(a, units, fc1, stream);
-    else if (tpw <= 2) launch_down_t<2>(a, units, fc1, stream);
-    else if (tpw <= 3) launch_down_t<3>(a, units, fc1, stream);
-    else if (tpw <= 4) launch_down_t<4>(a, units, fc1, stream);
-    else if (tpw <= 6) launch_down_t<6>(a, units, fc1, stream);
-    else if (tpw <= 8) launch_down_t<8>(a, units, fc1, stream);
-    else if (tpw <= 12) launch_down_t<12>(a, units, fc1, stream);
-    else if (tpw <= 16) launch_down_t<16>(a, units, fc1, stream);
-    else return EDGE0_EINVAL;
+    const int rc = defer ? launch_down_tpw<true>(a, tpw, units, fc1, stream)
+                         : launch_down_tpw<false>(a, tpw, units, fc1, stream);
+    if (rc != EDGE0_OK) return rc;
   }
   E0_CHECK_LAUNCH();
   E0_MARK(2, false);

@@ -35,7 +35,9 @@ struct MoeArgs {
   uint32_t* err;
   uint32_t* cnt_down;
   float* t_in;
-  float* hf;
+  // [K][2][I]: gate then up rows of each routed expert without their LoRA
+  // term, from the fused layer kernel (its down kernel finishes them)
+  float* gu_pre;
   uint16_t* hp_hi;
   uint16_t* hp_lo;
   float* hs;
@@ -45,9 +47,8 @@ struct MoeArgs {
   const unsigned long long* acc_prev;  // [d] the previous layer's (combined by k_layer_in)
   int S;  // down slices
   // LoRA A x of the fused layer kernel, computed once per routed expert by
-  // n_prod producer workgroups (prod_rows A rows each) and handed to the
-  // gate/up workgroups through t_hand: an entry holds kTHandEmpty until its
-  // value is stored; the down kernel empties it again.  Waits give up after
+  // n_prod producer workgroups (prod_rows A rows each) into t_hand [K][2r];
+  // the down launch after it reads them.  Waits (router logits) give up after
   // `spin` polls (error EDGE0_EHIP).
   float* t_hand;
   int n_prod, prod_rows;
@@ -116,9 +117,10 @@ int launch_layer_in(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
 struct HeadPart;
 int launch_expert_gemvs(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr,
                         const HeadPart* fc1 = nullptr);
-// the down GEMV alone (after k_layer_fused)
+// the down GEMV alone; `defer` after k_layer_fused, whose gate/up rows (gu_pre,
+// without their LoRA terms) the down units finish into h themselves
 int launch_down(const MoeArgs& a, hipStream_t stream, const LaunchTiming* timing = nullptr,
-                const HeadPart* fc1 = nullptr);
+                const HeadPart* fc1 = nullptr, bool defer = false);
 // Layer input + gate/up in one launch for a layer whose routing (a.ids) is
 // known before it starts; li carries the prologue (combine, residual, RMSNorm)
 // arguments.  Wide rows (d_model 2048 or 4096), lora_rank <= 16.

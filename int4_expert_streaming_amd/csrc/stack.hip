@@ -70,7 +70,7 @@ struct edge0_stack {
   hipGraphExec_t graphs[8];  // [0] step 0, [1] step 1, [2 + s%6] later steps
   hipEvent_t ev_heads;       // staged steps: the heads of the step have run
   int32_t* loop_host;        // staged closed loop: pinned [2][L][K] ids read back
-  int head_schedule;         // EDGE0_HEADS_FOLDED (default) or EDGE0_HEADS_AFTER_LAYERS
+  int head_schedule;         // EDGE0_HEADS_AFTER_LAYERS (default) or EDGE0_HEADS_FOLDED
   std::vector<edge0_lora> loras;  // adapters given apart, one table per layer (empty: in the bundles)
   // persistent mode (EDGE0_STACK_PERSISTENT)
   int mode;
@@ -299,7 +299,7 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
       li.flags |= IN_LORA;
       if ((rc = launch_layer_fused(a, li, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
               EDGE0_OK ||
-          (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp)) != EDGE0_OK)
+          (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp, true)) != EDGE0_OK)
         return rc;
       continue;
     }
@@ -320,7 +320,7 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
         a.lg_consumed = a.lg_hand + (size_t)a.par * E;  // emptied again by the down kernel
         if ((rc = launch_layer_fused(a, lr, stream, st->timed_kernel > 0 ? &lt : nullptr)) !=
                 EDGE0_OK ||
-            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp)) != EDGE0_OK)
+            (rc = launch_down(a, stream, st->timed_kernel > 0 ? &lt : nullptr, hp, true)) != EDGE0_OK)
           return rc;
         continue;
       }
@@ -558,7 +558,7 @@ static int stack_create(edge0_stack** out, const edge0_moe_shape* shape,
   if (loras != nullptr && shape->lora_rank > 0) st->loras.assign(loras, loras + Lc);
   st->last_step = -1;
   st->spin = kFlowDefaultSpin;
-  st->head_schedule = EDGE0_HEADS_FOLDED;
+  st->head_schedule = EDGE0_HEADS_AFTER_LAYERS;
   const size_t d = shape->d_model, K = shape->top_k;
   st->ws_bytes = edge0_workspace_bytes(shape);
   bool ok = hipMalloc((void**)&st->x, Lc * d * 2) == hipSuccess &&
@@ -610,8 +610,6 @@ static int stack_create(edge0_stack** out, const edge0_moe_shape* shape,
     ok = hipMalloc((void**)&st->pred_ids[i], Lc * K * 4) == hipSuccess &&
          hipMalloc((void**)&st->pred_w[i], Lc * K * 4) == hipSuccess;
   ok = ok && hipMemset(st->ws, 0, st->ws_bytes) == hipSuccess &&
-       hipMemset(static_cast<uint8_t*>(st->ws) + ws_layout(shape).t_hand, 0xFF,
-                 (size_t)4 * K * 2 * shape->lora_rank) == hipSuccess &&
        hipMemset(static_cast<uint8_t*>(st->ws) + ws_layout(shape).lg_hand, 0xFF,
                  (size_t)4 * 2 * shape->n_experts) == hipSuccess &&
        hipMemset(st->x, 0, Lc * d * 2) == hipSuccess &&
