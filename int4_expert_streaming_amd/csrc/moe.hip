@@ -682,21 +682,12 @@ constexpr int kMaxDeferT = 16 * 2 * kFusedMaxRank;  // t of up to 16 routed expe
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // One down unit: workgroup `bid` of the (d / 64) * S units.
-// DEFER (after the fused layer kernel): the unit first finishes its tiles'
-// rows of h from gu_pre: each wave takes its own tiles, lane j < 32 row j of
-// the chunk's gate and lane 32 + j its up row, adds the LoRA term
-// scale * B[row] . t (t = A x of the expert, from the producers' t_hand),
-// and lane j forms h = SiLU(gate) * up, its hi/lo split, the chunk sum and
-// (with the A_down columns of the chunk) the chunk's part of A_down h.
-// Otherwise those come staged from the gate/up kernel's workspace rows.
-template <int TPW, bool DEFER>
+template <int TPW>
 __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) {
   __shared__ float red[4][64];
   __shared__ uint32_t hp_s[kMaxSliceChunks][32];  // hi pairs then lo pairs of each chunk
   __shared__ float hsum_s[kMaxSliceChunks];
   __shared__ float tdc_s[kMaxSliceChunks][64];    // per tile: the chunk's part of A_down h
-  __shared__ float hf_s[DEFER ? 4 * TPW : 1][32];   // DEFER: each tile's h rows (fp32)
-  __shared__ float tt_s[DEFER ? kMaxDeferT : 1];    // DEFER: t of the K experts
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int K = a.K, S = a.S, I = a.I, r = a.r, d = a.d;
@@ -714,10 +705,6 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
   float wt[TPW];
   constexpr int kBd = 2;  // B_down pieces (8 ranks each) held per tile; more are read in the loop
   uint4 bdq[TPW][kBd];
-  // DEFER: lane (half = lane / 32, j = lane % 32): B_gate / B_up row 32 c + j
-  // (kFusedMaxRank = 16 ranks: two pieces); lane (qq = lane / 16, rr = lane % 16):
-  // A_down[rr][32 c + 8 qq .. + 7]
-  uint4 bgu[DEFER ? TPW : 1][2], adq[DEFER ? TPW : 1];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int t = wave * TPW + m;
@@ -739,81 +726,9 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
         (size_t)o * r);
 #pragma unroll
     for (int j = 0; j < kBd; ++j) bdq[m][j] = (8 * j < r) ? Bdp[j] : make_uint4(0, 0, 0, 0);
-    if constexpr (DEFER) {
-      const int half = lane >> 5, row = 32 * c + (lane & 31);
-      const uint4* Bp = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint16_t*>(
-              r > 0 ? E0_LORA(a, b, kk, half ? 3 : 1, half ? a.lay.b_up : a.lay.b_gate) : b) +
-          (size_t)(r > 0 ? row : 0) * r);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bgu[m][j] = (8 * j < r) ? Bp[j] : make_uint4(0, 0, 0, 0);
-      const int rr = lane & 15, qq = lane >> 4;
-      adq[m] = rr < r ? reinterpret_cast<const uint4*>(
-                            reinterpret_cast<const uint16_t*>(E0_LORA(a, b, kk, 4, a.lay.a_down)) +
-                            (size_t)rr * I + 32 * c + 8 * qq)[0]
-                      : make_uint4(0, 0, 0, 0);
-    }
   }
-  if constexpr (DEFER) {
-    // the previous launch's outputs: each tile's gate/up rows and t
-    float gu[TPW];
-#pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      const int t = wave * TPW + m;
-      const int tc = t < nt ? t : 0;
-      const int kk = tc / ncs, c = c0 + tc % ncs;
-      gu[m] = a.gu_pre[((size_t)kk * 2 + (lane >> 5)) * I + 32 * c + (lane & 31)];
-    }
-    for (int i = threadIdx.x; i < K * 2 * r; i += 256) tt_s[i] = a.t_hand[i];
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      const int t = wave * TPW + m;
-      const int tc = t < nt ? t : 0;
-      const int kk = tc / ncs;
-      // the row's LoRA term: B[row] . t over the r ranks
-      const float* tv = tt_s + (size_t)kk * 2 * r + (lane >> 5) * r;
-      const uint32_t bw[8] = {bgu[m][0].x, bgu[m][0].y, bgu[m][0].z, bgu[m][0].w,
-                              bgu[m][1].x, bgu[m][1].y, bgu[m][1].z, bgu[m][1].w};
-      float dl = 0.f;
-#pragma unroll
-      for (int q2 = 0; q2 < 8; ++q2)
-        if (2 * q2 < r) {
-          dl += bf_lo(bw[q2]) * tv[2 * q2];
-          dl += bf_hi(bw[q2]) * tv[2 * q2 + 1];
-        }
-      const float pre = gu[m] + a.scale * dl;
-      const float up = __shfl_xor(pre, 32, kWave);
-      const float h = silu_f(pre) * up;  // lanes j < 32
-      const uint32_t hi = f2bf(h);
-      const uint32_t lo = f2bf(h - bf2f(hi));
-      float hr = lane < 32 ? bf2f(hi) + bf2f(lo) : 0.f;
-      if (lane < 32) {
-        const int pos = pair_pos(lane);
-        uint16_t* hp16 = reinterpret_cast<uint16_t*>(hp_s[wave * TPW + m]);
-        hp16[pos] = (uint16_t)hi;
-        hp16[32 + pos] = (uint16_t)lo;
-        hf_s[wave * TPW + m][lane] = h;
-      }
-      hr = wave_sum(hr);
-      if (lane == 0) hsum_s[wave * TPW + m] = hr;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      // the chunk's part of A_down h: lane (qq, rr) over rows 8 qq .. 8 qq + 7
-      const int rr = lane & 15, qq = lane >> 4;
-      const float* hq = hf_s[wave * TPW + m] + 8 * qq;
-      const uint32_t aw[4] = {adq[m].x, adq[m].y, adq[m].z, adq[m].w};
-      float sm = 0.f;
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) sm += bf_lo(aw[q2]) * hq[2 * q2] + bf_hi(aw[q2]) * hq[2 * q2 + 1];
-      sm += __shfl_xor(sm, 16, kWave);
-      sm += __shfl_xor(sm, 32, kWave);
-      if (qq == 0) tdc_s[wave * TPW + m][rr] = sm;
-    }
-  } else {
-    // stage the unit's activation pairs and chunk sums (all K experts) in LDS
+  // stage the unit's activation pairs and chunk sums (all K experts) in LDS
+  {
     constexpr int kStage = kMaxSliceChunks * 32 / 256;  // words per thread
     uint32_t st[kStage];
 #pragma unroll
@@ -902,9 +817,190 @@ __device__ __forceinline__ void down_unit(const MoeArgs& a, const unsigned bid) 
     atomicAdd(a.acc + o, to_fix(red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]));
 }
 
+// One down unit after the fused layer kernel, whose gate/up rows (gu_pre)
+// still lack their LoRA terms.  Same unit and tiles as down_unit; before its
+// tiles the unit finishes its chunks' rows of h: each wave takes its own
+// tiles, lane j < 32 row j of the chunk's gate and lane 32 + j its up row,
+// adds scale * B[row] . t (t = A x of the expert, from t_hand), and lane j
+// forms h = SiLU(gate) * up, its hi/lo split and the chunk sum; then lane
+// (qq, rr) forms A_down[rr][8 qq ..] . h, the chunk's part of A_down h.
+// Order of the loads: the arguments in one batch, then what needs no slot
+// (gu_pre, t), then the slot-dependent rows; the LoRA rows are read at
+// clamped in-row addresses and zeroed past the rank instead of behind
+// branches (r = 0, 8 or 16).
+template <int TPW>
+__device__ __forceinline__ void down_unit_defer(const MoeArgs& a, const unsigned bid) {
+  __shared__ float red[4][64];
+  __shared__ uint32_t hp_s[4 * TPW][32];  // hi pairs then lo pairs of each chunk
+  __shared__ float hf_s[4 * TPW][32];     // each chunk's h rows (fp32)
+  __shared__ float hsum_s[4 * TPW];
+  __shared__ float tdc_s[4 * TPW][kFusedMaxRank];  // per tile: the chunk's part of A_down h
+  __shared__ float tt_s[kMaxDeferT];                // t of the K experts, zero past K * 2r
+  asm volatile("" ::"s"(a.K), "s"(a.S), "s"(a.I), "s"(a.r), "s"(a.d), "s"(a.g), "s"(a.n_slots),
+               "s"(a.E), "s"((int)a.lora_sep));
+  asm volatile("" ::"s"(a.slots), "s"(a.w), "s"(a.pool), "s"(a.slot_bytes), "s"(a.gu_pre),
+               "s"(a.t_hand), "s"(a.ids));
+  asm volatile("" ::"s"(a.lay.down_q), "s"(a.lay.down_s), "s"(a.lay.down_b), "s"(a.lay.b_down),
+               "s"(a.lay.b_gate), "s"(a.lay.b_up), "s"(a.lay.a_down));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int K = a.K, S = a.S, I = a.I, r = a.r, d = a.d;
+  const int NC = I / 32;
+  const int rb = bid / S;
+  const int sl = bid % S;
+  const int cps = (NC + S - 1) / S;
+  const int c0 = sl * cps;
+  const int ncs = min(NC, c0 + cps) - c0;
+  const int nt = K * ncs;
+  const int o = rb * 64 + lane;
+  const int half = lane >> 5, j32 = lane & 31;  // gate (0) or up (1) row j32 of a chunk
+  const int rr = lane & 15, qq = lane >> 4;     // A_down rank rr, rows 8 qq .. 8 qq + 7
+  const int p1 = r > 8 ? 1 : 0;                 // second 8-rank piece of a LoRA row, if any
+  const int rrc = min(rr, max(r - 1, 0));
+  // 1. what the previous launch wrote and needs no slot: the tiles' gate/up
+  // rows and t (two entries per thread cover kMaxDeferT)
+  int kk_m[TPW], c_m[TPW];
+  float gu[TPW];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int t = wave * TPW + m;
+    const int tc = t < nt ? t : 0;
+    kk_m[m] = tc / ncs;
+    c_m[m] = c0 + tc % ncs;
+    gu[m] = a.gu_pre[((size_t)kk_m[m] * 2 + half) * I + 32 * c_m[m] + j32];
+  }
+  const int nT = K * 2 * r;
+  const float tv0 = a.t_hand[min(tid, max(nT - 1, 0))];
+  const float tv1 = a.t_hand[min(tid + 256, max(nT - 1, 0))];
+  // 2. each tile's slot, then its rows
+  uint4 q[TPW], bg[TPW][2], ad[TPW], bd[TPW][2];
+  uint32_t sv[TPW], bv[TPW];
+  float wt[TPW];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int t = wave * TPW + m;
+    const int kk = kk_m[m], c = c_m[m];
+    int slot = a.slots[kk];
+    const int eid = a.ids[kk];  // the expert, for adapters given apart
+    const float wk = a.w[kk];
+    const bool ok = slot >= 0 && slot < a.n_slots;
+    wt[m] = (t < nt && ok) ? wk : 0.f;
+    slot = ok ? slot : 0;
+    const uint8_t* b = a.pool + (size_t)slot * (size_t)a.slot_bytes;
+    const uint8_t* bgp =
+        r > 0 ? E0_LORA_E(a, b, eid, half ? 3 : 1, half ? a.lay.b_up : a.lay.b_gate) : b;
+    const uint8_t* adp = r > 0 ? E0_LORA_E(a, b, eid, 4, a.lay.a_down) : b;
+    const uint8_t* bdp = r > 0 ? E0_LORA_E(a, b, eid, 5, a.lay.b_down) : b;
+    const uint4* Bg = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(bgp) + (size_t)(32 * c + j32) * r);
+    bg[m][0] = Bg[0];
+    bg[m][1] = Bg[p1];
+    ad[m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(adp) +
+                                            (r > 0 ? (size_t)rrc * I + 32 * c + 8 * qq : 0));
+    const uint4* Bd =
+        reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(bdp) + (size_t)o * r);
+    bd[m][0] = Bd[0];
+    bd[m][1] = Bd[p1];
+    q[m] = reinterpret_cast<const uint4*>(b + a.lay.down_q)[((size_t)rb * NC + c) * 64 + lane];
+    const int grp = (32 * c) / a.g;
+    sv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_s)[(size_t)grp * d + o];
+    bv[m] = reinterpret_cast<const uint16_t*>(b + a.lay.down_b)[(size_t)grp * d + o];
+  }
+  // the pieces past the rank count as zeros (masked where they are used, so
+  // no branch waits for the loads here)
+  const uint32_t mk0 = r > 0 ? ~0u : 0u, mk1 = r > 8 ? ~0u : 0u, mka = rr < r ? ~0u : 0u;
+  tt_s[tid] = tid < nT ? tv0 : 0.f;
+  tt_s[tid + 256] = tid + 256 < nT ? tv1 : 0.f;
+  __syncthreads();
+  // 3. the tiles' rows of h
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int tl = wave * TPW + m;
+    const float* tv = tt_s + (size_t)kk_m[m] * 2 * r + half * r;
+    const uint32_t bw[8] = {bg[m][0].x & mk0, bg[m][0].y & mk0, bg[m][0].z & mk0,
+                            bg[m][0].w & mk0, bg[m][1].x & mk1, bg[m][1].y & mk1,
+                            bg[m][1].z & mk1, bg[m][1].w & mk1};
+    float dl = 0.f;
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2) {
+      dl += bf_lo(bw[q2]) * tv[2 * q2];
+      dl += bf_hi(bw[q2]) * tv[2 * q2 + 1];
+    }
+    const float pre = gu[m] + a.scale * dl;
+    const float up = __shfl_xor(pre, 32, kWave);
+    const float h = silu_f(pre) * up;  // lanes j < 32
+    const uint32_t hi = f2bf(h);
+    const uint32_t lo = f2bf(h - bf2f(hi));
+    float hr = half == 0 ? bf2f(hi) + bf2f(lo) : 0.f;
+    if (half == 0) {
+      const int pos = pair_pos(j32);
+      uint16_t* hp16 = reinterpret_cast<uint16_t*>(hp_s[tl]);
+      hp16[pos] = (uint16_t)hi;
+      hp16[32 + pos] = (uint16_t)lo;
+      hf_s[tl][j32] = h;
+    }
+    hr = wave_sum(hr);
+    if (lane == 0) hsum_s[tl] = hr;
+  }
+  __syncthreads();
+  // 4. each tile's chunk part of A_down h (zero for ranks past r)
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int tl = wave * TPW + m;
+    const float* hq = hf_s[tl] + 8 * qq;
+    const uint32_t aw[4] = {ad[m].x & mka, ad[m].y & mka, ad[m].z & mka, ad[m].w & mka};
+    float sm = 0.f;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) sm += bf_lo(aw[q2]) * hq[2 * q2] + bf_hi(aw[q2]) * hq[2 * q2 + 1];
+    sm += __shfl_xor(sm, 16, kWave);
+    sm += __shfl_xor(sm, 32, kWave);
+    if (qq == 0) tdc_s[tl][rr] = sm;
+  }
+  if (bid == 0) {
+    if (tid < K) {
+      const int slot = a.slots[tid];
+      if (slot < 0 || slot >= a.n_slots) set_error(a.err, EDGE0_ERANGE);
+    }
+    // the router logits the layer kernel before this one read, if it was a
+    // router layer: empty them for the next
+    if (a.lg_consumed != nullptr)
+      for (int i = tid; i < a.E; i += 256) a.lg_consumed[i] = __uint_as_float(kTHandEmpty);
+  }
+  __syncthreads();
+  // 5. the tiles: each adds w_k (s acc + (b - 128 s) sum h + scale B_down[o] . (A_down h)_c)
+  float part = 0.f;
+  const Q4Consts kq = q4_consts();
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int tl = wave * TPW + m;
+    if (tl < nt) {
+      const float s = bf2f(sv[m]), bb = bf2f(bv[m]);
+      const uint32_t* hp = hp_s[tl];
+      const float acc = chunk_dot128(q[m], hp, kq) + chunk_dot128(q[m], hp + 16, kq);
+      const uint32_t bw[8] = {bd[m][0].x & mk0, bd[m][0].y & mk0, bd[m][0].z & mk0,
+                              bd[m][0].w & mk0, bd[m][1].x & mk1, bd[m][1].y & mk1,
+                              bd[m][1].z & mk1, bd[m][1].w & mk1};
+      float dl = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 8; ++q2) {
+        dl += bf_lo(bw[q2]) * tdc_s[tl][2 * q2];
+        dl += bf_hi(bw[q2]) * tdc_s[tl][2 * q2 + 1];
+      }
+      part += wt[m] * (s * acc + (bb - 128.f * s) * hsum_s[tl] + a.scale * dl);
+    }
+  }
+  red[wave][lane] = part;
+  __syncthreads();
+  if (wave == 0)
+    atomicAdd(a.acc + o, to_fix(red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]));
+}
+
 template <int TPW, bool DEFER>
 __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
-  down_unit<TPW, DEFER>(a, blockIdx.x);
+  if constexpr (DEFER)
+    down_unit_defer<TPW>(a, blockIdx.x);
+  else
+    down_unit<TPW>(a, blockIdx.x);
 }
 
 // The same launch with one prerouter head's fc1 rows beside it (the stack's
@@ -919,7 +1015,10 @@ __global__ __launch_bounds__(256) void k_down_fc1(MoeArgs a, HeadPart h) {
     return;
   }
   if ((int)blockIdx.x >= (a.d / 64) * a.S) return;
-  down_unit<TPW, DEFER>(a, blockIdx.x);
+  if constexpr (DEFER)
+    down_unit_defer<TPW>(a, blockIdx.x);
+  else
+    down_unit<TPW>(a, blockIdx.x);
 }
 
 // y = bf16 of the layer's fixed-point accumulator; optional residual
