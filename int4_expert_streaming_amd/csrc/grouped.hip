@@ -1216,6 +1216,44 @@ __device__ __forceinline__ void split_hilo8(F8 f, bool ok, bf16x8_t& hi, bf16x8_
   lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
+// 8 floats as three bf16 MFMA operands, hi + mid + lo (24 significant bits:
+// the fp32 value to within its own rounding)
+__device__ __forceinline__ void split3_8(F8 f, bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
+  const float v[8] = {f.a.x, f.a.y, f.a.z, f.a.w, f.b.x, f.b.y, f.b.z, f.b.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t hh[2], mm[2], ll[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float x = v[2 * e + q];
+      hh[q] = f2bf(x);
+      const float r1 = x - bf2f(hh[q]);
+      mm[q] = f2bf(r1);
+      ll[q] = f2bf(r1 - bf2f(mm[q]));
+    }
+    h[e] = hh[0] | (hh[1] << 16);
+    m[e] = mm[0] | (mm[1] << 16);
+    l[e] = ll[0] | (ll[1] << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  mid = __builtin_bit_cast(bf16x8_t, make_uint4(m[0], m[1], m[2], m[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// c . x on MFMA to fp32 quality from three-way splits: the cross products
+// down to 2^-16 of the leading one (hi hi, hi mid, mid hi, hi lo, lo hi, mid mid)
+__device__ __forceinline__ f32x4_t mfma16_x3(const bf16x8_t (&a)[3], const bf16x8_t (&b)[3],
+                                             f32x4_t c) {
+  c = mfma16(a[0], b[0], c);
+  c = mfma16(a[0], b[1], c);
+  c = mfma16(a[1], b[0], c);
+  c = mfma16(a[0], b[2], c);
+  c = mfma16(a[2], b[0], c);
+  c = mfma16(a[1], b[1], c);
+  return c;
+}
+
 // Gate/up: unit (64-pair tile, 64 rows of gate and of up); wave w owns rows
 // 16 w .. 16 w + 15 of both over the tile's four 16-pair blocks, so each
 // int4 word is expanded once, straight from memory into registers, and
@@ -1223,9 +1261,15 @@ __device__ __forceinline__ void split_hilo8(F8 f, bool ok, bf16x8_t& hi, bf16x8_
 // (pair order, swizzled), two groups a step, double-buffered; the next
 // step's weights, scales and activations are loaded while the current one
 // is multiplied.  Within a group, lane quad j takes KS of its chunks, so
-// an MFMA never mixes groups.  Epilogue: the LoRA B t terms on MFMA (t as
-// bf16 hi + lo), h as bf16 hi/lo pairs through LDS to full-width stores,
-// and each wave's 16-row sums of h (hi + lo) for the down fold.
+// an MFMA never mixes groups, and a group's products enter the
+// accumulators as s * acc.  The group affine's other half,
+// sum over groups of (b - 128 s) * (the pair's activation sum of the
+// group), is a small product of its own: after the loop it runs on MFMA with
+// both factors split three ways into bf16 (it nearly cancels the 128 s part
+// of the first half, so it needs fp32's precision), added into the same
+// accumulators.  Epilogue: the LoRA B t terms on MFMA (t as bf16 hi +
+// lo), h as bf16 hi/lo pairs through LDS to full-width stores, and each
+// wave's 16-row sums of h (hi + lo) for the down fold.
 constexpr int kPfRows = 64;  // gate and up rows per k_pf_gu workgroup
 template <int KS>
 __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
@@ -1233,7 +1277,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
   constexpr int CPB = 2 * CPG, STEP = 2 * G;         // 16-byte chunks, inputs a step
   constexpr int XU = kPfTile * CPB / 256;            // activation chunks staged per thread
   __shared__ __align__(16) uint4 xs[2][kPfTile * CPB];   // chunk c of pair m at CPB m + (c ^ m % CPB)
-  __shared__ __align__(16) float xsum_s[2][NGI][kPfTile];
   __shared__ __align__(16) uint4 tlo[2][2][kPfTile][2];  // t of each pair: [gate, up][hi, lo]
   const int nblk = a.I / kPfRows;
   const int u = pf_unit();
@@ -1258,7 +1301,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
     xrow[q] = a.x + (size_t)a.pair_tok[q0 + t0 + min(m, mt - 1)] * d + 8 * cc;
     xdst[q] = m * CPB + (cc ^ (m % CPB));
   }
-  const int xstok = tid < kPfTile ? a.pair_tok[q0 + t0 + min(tid, mt - 1)] : 0;
   // this lane's weight words: step s, k-step ks uses chunk (ks / KS) CPG + j KS + ks % KS
   const uint32_t* wgp = reinterpret_cast<const uint32_t*>(b + a.lay.gate_q) + (size_t)row * (d / 8);
   const uint32_t* wup = reinterpret_cast<const uint32_t*>(b + a.lay.up_q) + (size_t)row * (d / 8);
@@ -1267,17 +1309,13 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
   const uint16_t* sup = reinterpret_cast<const uint16_t*>(b + a.lay.up_s) + (size_t)row * ng;
   const uint16_t* bup = reinterpret_cast<const uint16_t*>(b + a.lay.up_b) + (size_t)row * ng;
   uint4 rx[XU];
-  float rxs[NGI];
-  // sc: gate s, gate b, up s, up b of the step's two groups, as loaded (bf16
-  // pairs, unpacked only where the fold uses them: work on a loaded value
-  // right after its load would wait for it there)
-  uint32_t wg[2 * KS], wu[2 * KS], sc[4];
+  // sc: gate s, up s of the step's two groups, as loaded (bf16 pairs,
+  // unpacked only where the fold uses them: work on a loaded value right
+  // after its load would wait for it there)
+  uint32_t wg[2 * KS], wu[2 * KS], sc[2];
   auto load_x = [&](int s) {
 #pragma unroll
     for (int q = 0; q < XU; ++q) rx[q] = *reinterpret_cast<const uint4*>(xrow[q] + STEP * s);
-    if (tid < kPfTile)
-#pragma unroll
-      for (int gg = 0; gg < NGI; ++gg) rxs[gg] = a.xsum[(size_t)xstok * ng + s * NGI + gg];
   };
   auto load_w = [&](int s) {
 #pragma unroll
@@ -1287,9 +1325,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
       wu[ks] = wup[c];
     }
     sc[0] = *reinterpret_cast<const uint32_t*>(sgp + s * NGI);
-    sc[1] = *reinterpret_cast<const uint32_t*>(bgp + s * NGI);
-    sc[2] = *reinterpret_cast<const uint32_t*>(sup + s * NGI);
-    sc[3] = *reinterpret_cast<const uint32_t*>(bup + s * NGI);
+    sc[1] = *reinterpret_cast<const uint32_t*>(sup + s * NGI);
   };
   auto store_x = [&](int buf) {
 #pragma unroll
@@ -1298,9 +1334,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
       pair_perm8(rx[q].x, rx[q].y, rx[q].z, rx[q].w, o);
       xs[buf][xdst[q]] = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    if (tid < kPfTile)
-#pragma unroll
-      for (int gg = 0; gg < NGI; ++gg) xsum_s[buf][gg][tid] = rxs[gg];
   };
   // t of the tile's pairs (the LoRA A x launch), split hi/lo, rank-padded
   if (r > 0 && tid < 2 * kPfTile) {
@@ -1327,14 +1360,14 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
   for (int q = 0; q < 8; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    uint32_t cwg[2 * KS], cwu[2 * KS], csc[4];
+    uint32_t cwg[2 * KS], cwu[2 * KS], csc[2];
 #pragma unroll
     for (int ks = 0; ks < 2 * KS; ++ks) {
       cwg[ks] = wg[ks];
       cwu[ks] = wu[ks];
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) csc[q] = sc[q];
+    for (int q = 0; q < 2; ++q) csc[q] = sc[q];
     if (s + 1 < nsteps) {
       load_x(s + 1);
       load_w(s + 1);
@@ -1356,23 +1389,74 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
         tmp[4 + tb] = mfma16(xo, bu, tmp[4 + tb]);
       }
       if (ks % KS == KS - 1) {
-        auto sv = [&](int q) { return gg == 0 ? bf_lo(csc[q]) : bf_hi(csc[q]); };
-        const float sg = sv(0), cg = sv(1) - 128.f * sg;
-        const float su = sv(2), cu = sv(3) - 128.f * su;
+        const float sg = gg == 0 ? bf_lo(csc[0]) : bf_hi(csc[0]);
+        const float su = gg == 0 ? bf_lo(csc[1]) : bf_hi(csc[1]);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const float4 xv = *reinterpret_cast<const float4*>(&xsum_s[buf][gg][16 * tb + 4 * j]);
-          const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            acc[tb][v] += sg * tmp[tb][v] + cg * xa[v];
-            acc[4 + tb][v] += su * tmp[4 + tb][v] + cu * xa[v];
+            acc[tb][v] = fmaf(sg, tmp[tb][v], acc[tb][v]);
+            acc[4 + tb][v] = fmaf(su, tmp[4 + tb][v], acc[4 + tb][v]);
           }
-        }
       }
     }
     if (s + 1 < nsteps) store_x(buf ^ 1);
     __syncthreads();
+  }
+  // the groups' (b - 128 s) terms: A = the pairs' activation sums (pair n of
+  // block tb, groups k0 + 8 j ..), B = b - 128 s of row n over the same
+  // groups; 32 groups an MFMA (groups past ng count as zeros, read at
+  // clamped indices)
+  const bool gvec = ng % 32 == 0;
+  for (int k0 = 0; k0 < ng; k0 += 32) {
+    const int g0 = k0 + 8 * j;
+    float cg8[8], cu8[8];
+    if (gvec) {
+      const uint4 s8g = *reinterpret_cast<const uint4*>(sgp + g0);
+      const uint4 b8g = *reinterpret_cast<const uint4*>(bgp + g0);
+      const uint4 s8u = *reinterpret_cast<const uint4*>(sup + g0);
+      const uint4 b8u = *reinterpret_cast<const uint4*>(bup + g0);
+      const uint32_t sg4[4] = {s8g.x, s8g.y, s8g.z, s8g.w}, bg4[4] = {b8g.x, b8g.y, b8g.z, b8g.w};
+      const uint32_t su4[4] = {s8u.x, s8u.y, s8u.z, s8u.w}, bu4[4] = {b8u.x, b8u.y, b8u.z, b8u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cg8[2 * e] = bf_lo(bg4[e]) - 128.f * bf_lo(sg4[e]);
+        cg8[2 * e + 1] = bf_hi(bg4[e]) - 128.f * bf_hi(sg4[e]);
+        cu8[2 * e] = bf_lo(bu4[e]) - 128.f * bf_lo(su4[e]);
+        cu8[2 * e + 1] = bf_hi(bu4[e]) - 128.f * bf_hi(su4[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int gi = min(g0 + e, ng - 1);
+        const bool in = g0 + e < ng;
+        cg8[e] = in ? bf2f(bgp[gi]) - 128.f * bf2f(sgp[gi]) : 0.f;
+        cu8[e] = in ? bf2f(bup[gi]) - 128.f * bf2f(sup[gi]) : 0.f;
+      }
+    }
+    bf16x8_t cgs[3], cus[3];
+    split3_8(F8{make_float4(cg8[0], cg8[1], cg8[2], cg8[3]),
+                make_float4(cg8[4], cg8[5], cg8[6], cg8[7])}, cgs[0], cgs[1], cgs[2]);
+    split3_8(F8{make_float4(cu8[0], cu8[1], cu8[2], cu8[3]),
+                make_float4(cu8[4], cu8[5], cu8[6], cu8[7])}, cus[0], cus[1], cus[2]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int m = 16 * tb + n;
+      const float* xp = a.xsum + (size_t)a.pair_tok[q0 + t0 + min(m, mt - 1)] * ng;
+      F8 xf;
+      if (gvec) {
+        xf = F8{*reinterpret_cast<const float4*>(xp + g0), *reinterpret_cast<const float4*>(xp + g0 + 4)};
+      } else {
+        float x8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x8[e] = g0 + e < ng ? xp[min(g0 + e, ng - 1)] : 0.f;
+        xf = F8{make_float4(x8[0], x8[1], x8[2], x8[3]), make_float4(x8[4], x8[5], x8[6], x8[7])};
+      }
+      bf16x8_t xs3[3];
+      split3_8(xf, xs3[0], xs3[1], xs3[2]);
+      acc[tb] = mfma16_x3(xs3, cgs, acc[tb]);
+      acc[4 + tb] = mfma16_x3(xs3, cus, acc[4 + tb]);
+    }
   }
   // LoRA B t: A = t of the pairs (ranks 8 j' .. as k, j' < 2), B = B rows
   if (r > 0) {
