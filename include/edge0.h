@@ -331,8 +331,10 @@ int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_slot_pool* po
  * summed in k order), for up to 4096 tokens per call: the (token, k) pairs
  * are bucketed by expert over many workgroups into tiles of up to 64 pairs
  * of one expert, which run through LDS-staged GEMMs on bf16 MFMA (int4
- * weights as exact 128 + q, each group's affine folded in fp32, the LoRA
- * terms on MFMA with t as bf16 hi + lo); each pair's weighted row is stored
+ * weights as exact 128 + q; each group's scale applied in fp32 per group,
+ * the groups' (b - 128 s) terms against the per-group activation sums on
+ * MFMA to fp32 precision; the LoRA terms on MFMA with t as bf16 hi + lo);
+ * each pair's weighted row is stored
  * and every token's K rows are added in k order (calls are
  * bit-reproducible).
  *   slot_table, ids, w, x, y : as edge0_moe_grouped ([n_tokens][K] routing,
@@ -342,8 +344,8 @@ int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_slot_pool* po
  *   workspace  : edge0_prefill_workspace_bytes(shape, max_tokens) bytes,
  *                zero-filled once before first use (calls leave it ready)
  * Shapes: those of edge0_moe_grouped with g of 32 or 64, d_model <= 2048 and
- * a multiple of 128 and of 4 g, d_inter a multiple of 64, lora_rank <= 16;
- * EDGE0_EINVAL otherwise.  An id or slot out of range is recorded in the
+ * a multiple of 128 and of 4 g, d_inter a multiple of 64 with at most 32
+ * groups (d_inter / g <= 32), lora_rank <= 16; EDGE0_EINVAL otherwise.  An id or slot out of range is recorded in the
  * workspace error word (edge0_workspace_error) and its pair contributes
  * nothing. */
 size_t edge0_prefill_workspace_bytes(const edge0_moe_shape* shape, int32_t max_tokens);

@@ -1530,7 +1530,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
 // from 32 w over the four 16-pair blocks (h hi and lo, two
 // MFMAs per block and step), its int4 words straight into registers, h
 // through LDS (swizzled), 64 inputs a step, double-buffered; a group's
-// products are folded per group.  Wave w also forms A_down
+// products enter the accumulators as s * acc, and the groups' (b - 128 s)
+// terms run after the loop on MFMA against each pair's h sums per group,
+// kept in LDS as the steps stage them.  Wave w also forms A_down
 // h for pair block w (the same two MFMAs against the A_down rows in pair
 // order; no fold).  Epilogue: the LoRA-down term on MFMA (A_down h as bf16
 // hi + lo against the B_down rows), then each pair's row times its routing
@@ -1540,6 +1542,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gu(GrpArgs a) {
 // blocks per wave need more registers than a wave has, and the compiler
 // then parks the staged h in scratch memory, behind a wait for its loads)
 __host__ __device__ constexpr int pf_out(int) { return 128; }
+constexpr int kPfGroupsPad = 33;  // input groups of the down projection (I / g <= 32), padded
 template <int KS>
 __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
   constexpr int G = 32 * KS, NGD = 2 / KS;  // inputs per group; groups a step (64 inputs)
@@ -1547,7 +1550,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
   constexpr int HU = 2 * kPfTile * CPB / 256;
   constexpr int kPfOut = pf_out(KS), RB = kPfOut / 64;  // rows per unit, 16-row blocks per wave
   __shared__ __align__(16) uint4 hh[2][2][kPfTile * CPB];  // [buf][hi, lo], chunk c of pair m at 8 m + (c ^ m % 8)
-  __shared__ __align__(16) float hsum_s[2][NGD][kPfTile];
+  __shared__ __align__(16) float hsa[kPfTile][kPfGroupsPad];  // each pair's h sum per input group
   __shared__ __align__(16) uint4 ad[2][kTileRank * CPB];   // A_down rows (rank-padded), pair order
   __shared__ __align__(16) float td_s[kPfTile][kTileRank + 4];
   __shared__ int src_s[kPfTile];
@@ -1605,7 +1608,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
   static_assert(HU == 4, "four staged h chunks per thread");
   uint4 sh0, sh1, sh2, sh3, sad = make_uint4(0, 0, 0, 0);
   float shs[NGD][G / 16];
-  uint32_t sw[RB][2], ssc[RB][2][NGD];
+  uint32_t sw[RB][2], ssc[RB][NGD];  // weight words; the groups' scales s
 #pragma unroll
   for (int gg = 0; gg < NGD; ++gg)
 #pragma unroll
@@ -1631,14 +1634,11 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
     _Pragma("unroll") for (int rr = 0; rr < RB; ++rr) {                                    \
       _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) sw[rr][ks] =                        \
           dq[(size_t)(2 * s_ + ks) * 64 * 4 + 16 * 4 * rr];                                 \
-      _Pragma("unroll") for (int gg = 0; gg < NGD; ++gg) {                                 \
-        const int gi = (s_ * 64) / G + gg;                                                  \
-        ssc[rr][0][gg] = dsp[(size_t)gi * d + 16 * rr];                                     \
-        ssc[rr][1][gg] = dbp[(size_t)gi * d + 16 * rr];                                     \
-      }                                                                                     \
+      _Pragma("unroll") for (int gg = 0; gg < NGD; ++gg)                                   \
+          ssc[rr][gg] = dsp[(size_t)((s_ * 64) / G + gg) * d + 16 * rr];                    \
     }                                                                                       \
   }
-#define E0_PF_DOWN_STORE(BUF)                                                               \
+#define E0_PF_DOWN_STORE(BUF, S)                                                            \
   {                                                                                         \
     const int b_ = (BUF);                                                                   \
     hd0[b_ * kBufStride] = sh0;                                                             \
@@ -1649,7 +1649,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
       _Pragma("unroll") for (int gg = 0; gg < NGD; ++gg) {                                 \
         float sum = 0.f;                                                                    \
         _Pragma("unroll") for (int h2 = 0; h2 < G / 16; ++h2) sum += shs[gg][h2];           \
-        hsum_s[b_][gg][tid] = sum;                                                          \
+        hsa[tid][(S) * NGD + gg] = sum;                                                     \
       }                                                                                     \
     if (r > 0 && tid < kTileRank * CPB) {                                                   \
       uint32_t w4[4];                                                                       \
@@ -1658,7 +1658,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
     }                                                                                       \
   }
   E0_PF_DOWN_LOAD(0);
-  E0_PF_DOWN_STORE(0);
+  E0_PF_DOWN_STORE(0, 0);
   __syncthreads();
   const Q4Consts kq = q4_consts();
   f32x4_t acc[4 * RB], tda = f32x4_t{0.f, 0.f, 0.f, 0.f};  // acc[4 rr + pb]
@@ -1666,16 +1666,13 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
   for (int q = 0; q < 4 * RB; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    uint32_t cwv[RB][2], csc[RB][2][NGD];
+    uint32_t cwv[RB][2], csc[RB][NGD];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) cwv[rr][ks] = sw[rr][ks];
 #pragma unroll
-      for (int gg = 0; gg < NGD; ++gg) {
-        csc[rr][0][gg] = ssc[rr][0][gg];
-        csc[rr][1][gg] = ssc[rr][1][gg];
-      }
+      for (int gg = 0; gg < NGD; ++gg) csc[rr][gg] = ssc[rr][gg];
     }
     if (s + 1 < nsteps) E0_PF_DOWN_LOAD(s + 1);
 #pragma unroll
@@ -1710,22 +1707,50 @@ __global__ __launch_bounds__(256, 2) void k_pf_down(GrpArgs a) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int rr = 2 * half + h2;
-          const float sd = bf2f(csc[rr][0][gg]), cd = bf2f(csc[rr][1][gg]) - 128.f * sd;
+          const float sd = bf2f(csc[rr][gg]);
 #pragma unroll
-          for (int pb = 0; pb < 4; ++pb) {
-            const float4 hv = *reinterpret_cast<const float4*>(&hsum_s[buf][gg][16 * pb + 4 * j]);
-            const float ha[4] = {hv.x, hv.y, hv.z, hv.w};
+          for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[4 * rr + pb][v] += sd * tmp[4 * h2 + pb][v] + cd * ha[v];
-          }
+            for (int v = 0; v < 4; ++v)
+              acc[4 * rr + pb][v] = fmaf(sd, tmp[4 * h2 + pb][v], acc[4 * rr + pb][v]);
         }
       }
     }
-    if (s + 1 < nsteps) E0_PF_DOWN_STORE(buf ^ 1);
+    if (s + 1 < nsteps) E0_PF_DOWN_STORE(buf ^ 1, s + 1);
     __syncthreads();
   }
 #undef E0_PF_DOWN_LOAD
 #undef E0_PF_DOWN_STORE
+  // the groups' (b - 128 s) terms, as in the gate/up kernel: A = the pairs'
+  // h sums per group (from LDS), B = b - 128 s of the wave's rows, both
+  // split three ways (groups past I / g count as zeros)
+  {
+    const int ngi = I / G;
+    bf16x8_t hs3[4][3];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      float h8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h8[e] = 8 * j + e < ngi ? hsa[16 * pb + n][8 * j + e] : 0.f;
+      split3_8(F8{make_float4(h8[0], h8[1], h8[2], h8[3]), make_float4(h8[4], h8[5], h8[6], h8[7])},
+               hs3[pb][0], hs3[pb][1], hs3[pb][2]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      float c8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int gi = min(8 * j + e, ngi - 1);
+        const float sd = bf2f(dsp[(size_t)gi * d + 16 * rr]), bd = bf2f(dbp[(size_t)gi * d + 16 * rr]);
+        c8[e] = 8 * j + e < ngi ? bd - 128.f * sd : 0.f;
+      }
+      bf16x8_t cs3[3];
+      split3_8(F8{make_float4(c8[0], c8[1], c8[2], c8[3]), make_float4(c8[4], c8[5], c8[6], c8[7])},
+               cs3[0], cs3[1], cs3[2]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) acc[4 * rr + pb] = mfma16_x3(hs3[pb], cs3, acc[4 * rr + pb]);
+    }
+  }
   // LoRA-down: A = A_down h of the pairs (hi + lo), B = B_down rows
   if (r > 0) {
 #pragma unroll
@@ -2089,13 +2114,13 @@ static PfWs pf_ws_layout(const edge0_moe_shape* s, int max_tokens) {
   return L;
 }
 // the prefill kernels' shapes: the LoRA A x tiles (d / 4 a multiple of 32),
-// the gate/up units (32 rows) and the down units (64 output rows) over
-// whole groups of 32 or 64 inputs
+// the gate/up units (64 rows) and the down units (128 output rows) over
+// whole groups of 32 or 64 inputs, the down kernel's groups held in LDS
 static bool pf_shape_ok(const edge0_moe_shape* s) {
   if (!grouped_shape_ok(s)) return false;
   const int d = s->d_model, g = s->group_size, I = s->d_inter, r = s->lora_rank;
   return (g == 32 || g == 64) && d <= 2048 && d % 128 == 0 && d % pf_out(g / 32) == 0 &&
-         I % kPfRows == 0 && I % 64 == 0 && r <= kTileRank;
+         I % kPfRows == 0 && I % 64 == 0 && I / g < kPfGroupsPad && r <= kTileRank;
 }
 }  // namespace e0
 
