@@ -61,8 +61,11 @@ def check_layer(S, gen, L, t, snap, prev_snap, owners, consumers, report):
     # MoE output on the GPU's x and routing
     ids, w = snap["ids"][L], snap["w"][L].astype(np.float64)
     ex = {int(e): lay.expert(int(e)) for e in ids}
-    lo = {int(e): lay.lora(int(e)) for e in ids}
-    y_o = O.moe_layer(ex, ids, w, x_g, S.group, lo, S.lora_alpha / S.lora_rank)
+    if S.lora_rank > 0:
+        lo, scale = {int(e): lay.lora(int(e)) for e in ids}, S.lora_alpha / S.lora_rank
+    else:
+        lo, scale = None, 0.0
+    y_o = O.moe_layer(ex, ids, w, x_g, S.group, lo, scale)
     rel = rel_l2(O.bf16_to_f64(snap["y"][L]), y_o)
     assert rel <= REL_L2_MAX, (L, t, rel)
     # residual: h' = bf16(h + y)
@@ -296,6 +299,8 @@ def test_router_layers_same_parity_in_a_row(torch_cuda, n_layers):
 WIDE_SHAPES = {
     "d4096_k8_r8": G.MoEShape(4096, 16, 256, 8, 64, 8, 16.0, 64),
     "d2048_k8_r16": G.MoEShape(2048, 32, 384, 8, 64, 16, 32.0, 64),
+    # no adapters: the down launch finishes the gate/up rows with no LoRA term
+    "d2048_k4_r0": G.MoEShape(2048, 32, 384, 4, 64, 0, 0.0, 64),
 }
 
 
