@@ -485,7 +485,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
     float tot = 0.f;
 #pragma unroll
     for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
-    const float inv = 1.f / sqrtf(tot / (float)d + li.eps);
+    // without IN_NORM x is h itself (the single-layer call's given input)
+    const float inv = (li.flags & IN_NORM) ? 1.f / sqrtf(tot / (float)d + li.eps) : 1.f;
     uint32_t xw[2 * NJ];
 #pragma unroll
     for (int c = 0; c < NJ; ++c) {
@@ -495,17 +496,19 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_fused(MoeArgs a, LayerI
     }
     __syncthreads();
     if (lead) {
+      if (li.x_out != nullptr) {  // the stack's copies of x, y_prev and h
 #pragma unroll
-      for (int c = 0; c < NJ; ++c) {
-        const int j0 = 4 * (tid + 512 * c);
-        *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
-        if (comb)
-          *reinterpret_cast<uint2*>(li.y_prev_out + j0) =
-              make_uint2((uint32_t)av[4 * c] | ((uint32_t)av[4 * c + 1] << 16),
-                         (uint32_t)av[4 * c + 2] | ((uint32_t)av[4 * c + 3] << 16));
-        *reinterpret_cast<uint2*>(li.h_out + j0) =
-            make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
-                       f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
+        for (int c = 0; c < NJ; ++c) {
+          const int j0 = 4 * (tid + 512 * c);
+          *reinterpret_cast<uint2*>(li.x_out + j0) = make_uint2(xw[2 * c], xw[2 * c + 1]);
+          if (comb)
+            *reinterpret_cast<uint2*>(li.y_prev_out + j0) =
+                make_uint2((uint32_t)av[4 * c] | ((uint32_t)av[4 * c + 1] << 16),
+                           (uint32_t)av[4 * c + 2] | ((uint32_t)av[4 * c + 3] << 16));
+          *reinterpret_cast<uint2*>(li.h_out + j0) =
+              make_uint2(f2bf(hv[4 * c]) | (f2bf(hv[4 * c + 1]) << 16),
+                         f2bf(hv[4 * c + 2]) | (f2bf(hv[4 * c + 3]) << 16));
+        }
       }
       for (int j = tid; j < d; j += 512) a.acc[j] = 0ull;
     }
@@ -1064,6 +1067,28 @@ __global__ void k_transpose_sb(const uint16_t* __restrict__ src, uint16_t* __res
 }
 
 // ------------------------------------------------------------ host side
+// The single-layer call's launches.  Wide rows (layer_fused_ok): the fused
+// layer kernel with x as given (no residual, no RMSNorm) and the down launch
+// that finishes its gate/up rows; otherwise the LoRA A x launch, the gate/up
+// and down GEMVs.  Then the combine (y, and the error word for err_out).
+static int launch_layer_call(const MoeArgs& a, hipStream_t stream) {
+  int rc;
+  if (layer_fused_ok(a)) {
+    LayerIn li{};
+    li.flags = IN_LORA;
+    li.h_prev = a.x;
+    if ((rc = launch_layer_fused(a, li, stream)) != EDGE0_OK ||
+        (rc = launch_down(a, stream, nullptr, nullptr, true)) != EDGE0_OK)
+      return rc;
+  } else {
+    LayerIn li{};
+    li.flags = IN_LORA;  // with r = 0 it only resolves the slots
+    if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
+    if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
+  }
+  return launch_combine(a, stream);
+}
+
 int fill_moe_args(const edge0_moe_shape* sh, const edge0_slot_pool* pool, const int32_t* table,
                   const int32_t* ids, const float* w, const void* x, void* y, void* workspace,
                   MoeArgs* a, bool lora_in_bundle) {
@@ -1289,13 +1314,9 @@ extern "C" int edge0_moe_layer(const edge0_moe_shape* shape, const edge0_slot_po
                                const void* x, void* y, void* workspace, hipStream_t stream) {
   if (!shape || !shape_ok(shape) || !x || !y || x == y) return EDGE0_EINVAL;
   MoeArgs a;
-  int rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, workspace, &a);
+  const int rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, workspace, &a);
   if (rc != EDGE0_OK) return rc;
-  LayerIn li{};
-  li.flags = IN_LORA;  // with r = 0 it only resolves the slots
-  if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
-  if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
-  return launch_combine(a, stream);
+  return launch_layer_call(a, stream);
 }
 
 extern "C" int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_slot_pool* pool,
@@ -1318,11 +1339,7 @@ extern "C" int edge0_moe_layer_lora(const edge0_moe_shape* shape, const edge0_sl
     for (int i = 0; i < 6; ++i) a.lo_base[i] = static_cast<const uint8_t*>(f[i]);
     a.lo_stride = lora->expert_stride * 2;  // bf16 elements
   }
-  LayerIn li{};
-  li.flags = IN_LORA;
-  if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
-  if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
-  return launch_combine(a, stream);
+  return launch_layer_call(a, stream);
 }
 
 // ------------------------------------------------- no-allocation variant
@@ -1385,11 +1402,7 @@ extern "C" int edge0_moe_layer_noalloc(const edge0_moe_shape* shape, const edge0
   MoeArgs a;
   if ((rc = fill_moe_args(shape, pool, slot_table, ids, w, x, y, ws, &a)) != EDGE0_OK) return rc;
   a.err_out = error_out;
-  LayerIn li{};
-  li.flags = IN_LORA;
-  if ((rc = launch_layer_in(a, li, stream)) != EDGE0_OK) return rc;
-  if ((rc = launch_expert_gemvs(a, stream)) != EDGE0_OK) return rc;
-  return launch_combine(a, stream);
+  return launch_layer_call(a, stream);
 }
 
 extern "C" int edge0_pack_bundle(const edge0_moe_shape* shape, const edge0_expert_arrays* src,
