@@ -1026,18 +1026,7 @@ __global__ __launch_bounds__(256) void k_down_fc1(MoeArgs a, HeadPart h) {
 
 // y = bf16 of the layer's fixed-point accumulator; optional residual
 // h_out = bf16(h_res + y).  (In the stack the next layer's k_layer_in does it.)
-__global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
-  const int o = blockIdx.x * 256 + threadIdx.x;
-  if (o == 0 && a.err_out != nullptr) {
-    // every kernel that may record an error ran before this one
-    *a.err_out = *a.err != 0u ? EDGE0_ERANGE : EDGE0_OK;
-    *a.err = 0u;
-  }
-  if (o >= a.d) return;
-  const uint32_t yb = f2bf(from_fix(a.acc[o]));
-  a.y[o] = (uint16_t)yb;
-  if (a.h_out != nullptr) a.h_out[o] = (uint16_t)f2bf(bf2f(a.h_res[o]) + bf2f(yb));
-}
+__global__ __launch_bounds__(256) void k_combine(MoeArgs a) { combine_unit(a, blockIdx.x); }
 
 // ------------------------------------------------------------ bundle pack
 // down_q: logical u32 [d][I/8] -> tiled [d/64][I/32][64][4]

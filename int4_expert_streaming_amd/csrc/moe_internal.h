@@ -129,6 +129,21 @@ int launch_layer_fused(const MoeArgs& a, const LayerIn& li, hipStream_t stream,
                        const LaunchTiming* timing = nullptr);
 int launch_combine(const MoeArgs& a, hipStream_t stream);
 
+// y = bf16 of the layer's fixed-point accumulator, outputs 256 u .. 256 u +
+// 255; optional residual h_out = bf16(h_res + y); the error word moves to
+// err_out if one is given (every kernel that may record an error ran before)
+__device__ __forceinline__ void combine_unit(const MoeArgs& a, unsigned u) {
+  const int o = (int)u * 256 + (int)threadIdx.x;
+  if (o == 0 && a.err_out != nullptr) {
+    *a.err_out = *a.err != 0u ? EDGE0_ERANGE : EDGE0_OK;
+    *a.err = 0u;
+  }
+  if (o >= a.d) return;
+  const uint32_t yb = f2bf(from_fix(a.acc[o]));
+  a.y[o] = (uint16_t)yb;
+  if (a.h_out != nullptr) a.h_out[o] = (uint16_t)f2bf(bf2f(a.h_res[o]) + bf2f(yb));
+}
+
 // A batch of prerouter heads (one per owner layer): head i reads x at
 // x + i*x_stride and its routing at ids_now/ids_prev + i*ids_stride (ids_prev
 // may be NULL), and writes its committed ids/w at ids_out/w_out +

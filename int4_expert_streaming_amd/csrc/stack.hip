@@ -24,18 +24,31 @@
 namespace e0 {
 
 // routing each layer executed at step s, gathered into one [L][K] array
-__global__ void k_gather_routing(const int32_t* __restrict__ exec_ids,
-                                 const float* __restrict__ exec_w,
-                                 const int32_t* __restrict__ pred_ids,
-                                 const float* __restrict__ pred_w, int n_layers, int K,
-                                 int consumer_first, int consumer_last, int step,
-                                 int32_t* __restrict__ ids, float* __restrict__ w) {
-  for (int t = threadIdx.x; t < n_layers * K; t += blockDim.x) {
-    const int L = t / K;
-    const bool by_pred = L >= consumer_first && L <= consumer_last && step > 0;
-    ids[t] = by_pred ? pred_ids[t] : exec_ids[t];
-    w[t] = by_pred ? pred_w[t] : exec_w[t];
+struct GatherArgs {
+  const int32_t* exec_ids;
+  const float* exec_w;
+  const int32_t* pred_ids;
+  const float* pred_w;
+  int n_layers, K, consumer_first, consumer_last, step;
+  int32_t* ids;
+  float* w;
+};
+__device__ __forceinline__ void gather_routing(const GatherArgs& g) {
+  for (int t = threadIdx.x; t < g.n_layers * g.K; t += blockDim.x) {
+    const int L = t / g.K;
+    const bool by_pred = L >= g.consumer_first && L <= g.consumer_last && g.step > 0;
+    g.ids[t] = by_pred ? g.pred_ids[t] : g.exec_ids[t];
+    g.w[t] = by_pred ? g.pred_w[t] : g.exec_w[t];
   }
+}
+__global__ void k_gather_routing(GatherArgs g) { gather_routing(g); }
+// the last layer's combine (workgroups 1 ..) and the gather (workgroup 0) in
+// one launch: neither reads what the other writes
+__global__ __launch_bounds__(256) void k_combine_gather(MoeArgs a, GatherArgs g) {
+  if (blockIdx.x == 0)
+    gather_routing(g);
+  else
+    combine_unit(a, blockIdx.x - 1);
 }
 
 }  // namespace e0
@@ -99,7 +112,9 @@ static bool is_owner(const edge0_stack_spec& s, int L) {
 }
 
 // fc1 false: the heads' fc1 rows ran beside the layers; only fc2 and the commits here
-static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1 = true);
+// comb (optional): the last layer's combine, launched with the routing gather
+static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1 = true,
+                        const MoeArgs* comb = nullptr);
 
 // Layer L's adapters given apart (edge0_stack_create_lora), if any
 static void stack_lora(const edge0_stack* st, int L, MoeArgs& a) {
@@ -339,21 +354,23 @@ static int enqueue_step(edge0_stack* st, int step, hipStream_t stream) {
   // the last layer's combine and residual
   a.h_res = st->h + (size_t)(Lc - 1) * d;
   a.h_out = st->h + (size_t)Lc * d;
-  const int rc = launch_combine(a, stream);
-  if (rc != EDGE0_OK) return rc;
-  return enqueue_tail(st, step, stream, st->head_schedule != EDGE0_HEADS_FOLDED);
+  return enqueue_tail(st, step, stream, st->head_schedule != EDGE0_HEADS_FOLDED, &a);
 }
 
 // after the layers: the routing every layer executed, gathered, and every
 // owner layer's head, batched
-static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1) {
+static int enqueue_tail(edge0_stack* st, int step, hipStream_t stream, bool fc1,
+                        const MoeArgs* comb) {
   const edge0_moe_shape& sh = st->shape;
   const int d = sh.d_model, K = sh.top_k, Lc = st->spec.n_layers;
   int rc = EDGE0_OK;
-  k_gather_routing<<<1, 256, 0, stream>>>(st->exec_ids[step & 1], st->exec_w[step & 1],
-                                          st->pred_ids[step % 3], st->pred_w[step % 3], Lc, K,
-                                          st->spec.consumer_first, st->spec.consumer_last, step,
-                                          st->run_ids[step & 1], st->run_w[step & 1]);
+  const GatherArgs g{st->exec_ids[step & 1], st->exec_w[step & 1], st->pred_ids[step % 3],
+                     st->pred_w[step % 3],   Lc,  K,  st->spec.consumer_first,
+                     st->spec.consumer_last, step, st->run_ids[step & 1], st->run_w[step & 1]};
+  if (comb != nullptr)
+    k_combine_gather<<<1 + (comb->d + 255) / 256, 256, 0, stream>>>(*comb, g);
+  else
+    k_gather_routing<<<1, 256, 0, stream>>>(g);
   E0_CHECK_LAUNCH();
   // every owner layer's head, batched: layer L's head reads x_L and the
   // routing layer L executed now and at the previous step, and commits the
@@ -793,14 +810,15 @@ static int enqueue_staged_step(edge0_stack* st, edge0_stager* sg, const edge0_st
   if (loop) {
     // prediction-routed layers executed the heads' routing, the others their
     // router's
-    k_gather_routing<<<1, 256, 0, stream>>>(st->exec_ids[step & 1], w_exec, st->pred_ids[step % 3],
-                                            w_exec, Lc, K, st->spec.consumer_first,
-                                            st->spec.consumer_last, step, st->run_ids[step & 1],
-                                            st->run_w[step & 1]);
+    k_gather_routing<<<1, 256, 0, stream>>>(GatherArgs{
+        st->exec_ids[step & 1], w_exec, st->pred_ids[step % 3], w_exec, Lc, K,
+        st->spec.consumer_first, st->spec.consumer_last, step, st->run_ids[step & 1],
+        st->run_w[step & 1]});
   } else {
     // every layer executed the given ids
-    k_gather_routing<<<1, 256, 0, stream>>>(plan.ids_dev, w_exec, plan.ids_dev, w_exec, Lc, K, 1,
-                                            0, step, st->run_ids[step & 1], st->run_w[step & 1]);
+    k_gather_routing<<<1, 256, 0, stream>>>(GatherArgs{plan.ids_dev, w_exec, plan.ids_dev, w_exec,
+                                                       Lc, K, 1, 0, step, st->run_ids[step & 1],
+                                                       st->run_w[step & 1]});
   }
   E0_CHECK_LAUNCH();
   if (!ahead || st->spec.owner_first > st->spec.owner_last) return EDGE0_OK;
