@@ -50,7 +50,7 @@ METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak
 # the same counters read for a device copy of known size (256 MiB copy:
 # FETCH_SIZE 131084.7 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only
 # for the kernel sources it was taken on (hash below); otherwise None.
-TRAFFIC_RECORD = {"src_sha": "bdf0015865db7564", "fetch_kib": 3884.3, "write_kib": 54.1,
+TRAFFIC_RECORD = {"src_sha": "4f13358c59b78ab3", "fetch_kib": 3884.8, "write_kib": 54.1,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "heads_dev.h", "moe.hip")
 HBM_PEAK_GBPS = 8000.0
@@ -445,7 +445,7 @@ def row_layer(args, log, inst, K):
            "moe_bytes": b_moe, "head_bytes": b_head,
            "head_gbps": round(b_head / (us_head * 1e-6) / 1e9, 1),
            "head_plus_moe_gbps": round((b_moe + b_head) / (us_both * 1e-6) / 1e9, 1),
-           "roofline": roofline("edge0_moe_layer (slot/LoRA-in, int4 gate/up, int4 down, combine launches)",
+           "roofline": roofline("edge0_moe_layer (fused layer input + LoRA A x + int4 gate/up, int4 down with the LoRA epilogue, combine)",
                                 b_moe, us_moe)}
     if not args.no_cpu:
         import oracle as O
