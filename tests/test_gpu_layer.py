@@ -157,24 +157,31 @@ def test_moe_layer_deterministic_and_lora_zero(torch_cuda, name):
     assert not torch_cuda.equal(yz, outs[0])
 
 
-def test_bad_ids_are_reported_not_dereferenced(torch_cuda):
+@pytest.mark.parametrize("name", ["tiny", "qwen3moe_k8"])
+def test_bad_ids_are_reported_not_dereferenced(torch_cuda, name):
     """An id outside [0, E) or a slot of -1 is skipped on the device and
-    reported through the workspace error word."""
-    S = G.TINY
-    L = layer("tiny")
+    reported through the workspace error word (the narrow-row launches on the
+    tiny shape, the fused layer kernel and its down launch on the wide one)."""
+    S = SHAPES[name]
+    K = S.top_k
+    L = layer(name)
     x, xd = _x(S, 1)
-    w = torch_cuda.full((S.top_k,), 0.25, dtype=torch_cuda.float32, device="cuda")
+    w = torch_cuda.full((K,), 1.0 / K, dtype=torch_cuda.float32, device="cuda")
     y = torch_cuda.zeros(S.d_model, dtype=torch_cuda.int16, device="cuda")
-    bad = torch_cuda.tensor([0, 1, S.n_experts + 3, 2], dtype=torch_cuda.int32, device="cuda")
-    L.E.edge0_moe_layer(L.sh, L.pool.pool, L.table, bad, w, xd, y, L.ws)
+    good = [5] + [e for e in range(1, K + 1) if e != 5][:K - 1]
+    bad = list(good)
+    bad[2] = S.n_experts + 3
+    L.E.edge0_moe_layer(L.sh, L.pool.pool, L.table,
+                        torch_cuda.tensor(bad, dtype=torch_cuda.int32, device="cuda"), w, xd, y,
+                        L.ws)
     assert L.E.edge0_workspace_error(L.ws) == L.E.EDGE0_ERANGE
     table = L.table.clone()
     table[5] = -1
-    ids = torch_cuda.tensor([5, 1, 2, 3], dtype=torch_cuda.int32, device="cuda")
+    ids = torch_cuda.tensor(good, dtype=torch_cuda.int32, device="cuda")
     L.E.edge0_moe_layer(L.sh, L.pool.pool, table, ids, w, xd, y, L.ws)
     assert L.E.edge0_workspace_error(L.ws) == L.E.EDGE0_ERANGE
-    # the remaining experts still combine: compare with the oracle over ids 1..3
-    yo = L.oracle_y([1, 2, 3], [0.25, 0.25, 0.25], x)
+    # the remaining experts still combine: compare with the oracle over the others
+    yo = L.oracle_y(good[1:], [1.0 / K] * (K - 1), x)
     assert rel_l2(O.bf16_to_f64(_bits(y)), yo) <= REL_L2_MAX
     # and the next call on the same workspace is clean
     L.E.edge0_moe_layer(L.sh, L.pool.pool, L.table, ids, w, xd, y, L.ws)

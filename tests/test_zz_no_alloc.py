@@ -66,6 +66,17 @@ def test_noalloc_matches_workspace_call(torch_cuda):
     y_ref, y, ref_err, err = _both(torch, small, ids, w, G.hidden(S, 7))
     assert ref_err == E.EDGE0_OK and err == E.EDGE0_OK
     assert np.array_equal(y, y_ref)
+    # the same on the wide shape (fused layer kernel and its down launch)
+    S = big.S
+    ids = np.array([0, 1, 2, 3, S.n_experts + 7, 5, 6, 9], np.int32)
+    w = np.full(S.top_k, 1.0 / S.top_k, np.float32)
+    y_ref, y, ref_err, err = _both(torch, big, ids, w, G.hidden(S, 8))
+    assert ref_err == E.EDGE0_ERANGE and err == E.EDGE0_ERANGE
+    assert np.array_equal(y, y_ref)
+    ids[4] = 4
+    y_ref, y, ref_err, err = _both(torch, big, ids, w, G.hidden(S, 9))
+    assert ref_err == E.EDGE0_OK and err == E.EDGE0_OK
+    assert np.array_equal(y, y_ref)
 
 
 def test_noalloc_refuses_oversized_shape(torch_cuda):
