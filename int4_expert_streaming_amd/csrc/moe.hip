@@ -332,11 +332,12 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 //    workgroup and stores t = A x for its rows into t_hand;
 //  - K * d_inter / 16 gate/up workgroups (16 rows of one routed expert):
 //    each loads its int4 rows, forms x redundantly from L2-resident data
-//    (previous layer's fixed-point y, h, RMSNorm) into LDS, computes the
-//    rows' dot products and stores them, without the LoRA term, to gu_pre.
-// The LoRA B t terms and the SwiGLU are the down kernel's (down_unit with
-// DEFER): t crosses the kernel boundary, so no workgroup of this launch
-// waits for another's stores.
+//    (previous layer's fixed-point y, h, RMSNorm; without IN_NORM x is
+//    li.h_prev as given, the single-layer call) into LDS, computes the rows'
+//    dot products and stores them, without the LoRA term, to gu_pre.
+// The LoRA B t terms and the SwiGLU are the down launch's (down_unit_defer):
+// t crosses the kernel boundary, so no workgroup of this launch waits for
+// another's stores.
 // ROUTE (a router layer): the producers first compute a.route_rows router
 // logits each from x and publish them through lg_hand (parity a.par; the
 // down kernel that follows empties them again); every workgroup then commits the
@@ -344,9 +345,9 @@ __global__ __launch_bounds__(gate_up_threads(CPR)) void k_gate_up(MoeArgs a) {
 // loads its expert's rows, and gate/up workgroup 0 stores the committed
 // ids/w.  Otherwise the routing (a.ids, a.w) is given and the rows are
 // loaded before x is formed.
-// Gate/up workgroup 0 stores h, y_prev, x and clears this layer's
-// accumulator; the first workgroup of each expert publishes its slot for the
-// down kernel.  One launch replaces the router / layer-input launch and the
+// Gate/up workgroup 0 clears this layer's accumulator and, in the stack
+// (li.x_out given), stores h, y_prev and x; the first workgroup of each
+// expert publishes its slot for the down kernel.  One launch replaces the router / layer-input launch and the
 // gate/up GEMV, and A x is computed once per expert instead of once per
 // workgroup.
 constexpr int kFusedMaxRank = 16;
