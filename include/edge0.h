@@ -376,15 +376,19 @@ int edge0_moe_prefill_lora(const edge0_moe_shape* shape, const edge0_slot_pool* 
  * For each projection of one expert: W' = s q + b + (alpha/r) B A, then per
  * group of g inputs s' = bf16((max - min) / 15), b' = bf16(min) (nearest,
  * ties to even), q' = round((w' - b') / s') to nearest-even, clipped to
- * 0..15 (0 where s' is 0); delta summed over the rank in fp32, in rank order.
+ * 0..15 (0 where s' is 0).
  *   src_bundle : device, one expert bundle of `shape` (with its LoRA)
  *   dst_bundle : device, written in the LoRA-free layout of the same shape
  *                (edge0_bundle_layout_of with lora_rank 0): the merged expert
  *   stats_out  : device double [6]: sum(actual * delta), sum(delta^2) for
  *                gate, up, down, actual = s' q' + b' - (s q + b); the weight
  *                retention of a projection is the first over the second
- *   workspace  : edge0_merge_workspace_bytes(shape) bytes (partial sums)
- * The sums are reduced in a fixed order (the same bits every call). */
+ *   workspace  : edge0_merge_workspace_bytes(shape) bytes (partial sums);
+ *                calls that share a workspace must not overlap
+ * The sums are reduced in a fixed order (the same bits every call).  On the
+ * GPU, delta is an fp32 sum of the exact bf16 products (on the matrix cores
+ * for groups of up to 128 inputs), and q' is decided from (w' - b') times the
+ * fp32 reciprocal of s'. */
 size_t edge0_merge_workspace_bytes(const edge0_moe_shape* shape);
 int edge0_merge_requant(const edge0_moe_shape* shape, const void* src_bundle, void* dst_bundle,
                         double* stats_out, void* workspace, hipStream_t stream);

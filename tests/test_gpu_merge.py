@@ -84,6 +84,7 @@ def test_merge_requant_parity(torch_cuda, name, S, experts):
     scale = S.lora_alpha / S.lora_rank
     for e in experts:
         print(f"[merge] {name} expert {e}", flush=True)
+        stats.fill_(float("nan"))  # every call must write all six figures
         ws = E.edge0_merge_requant(lay.sh, lay.pool.slot_ptr(e), dst, stats, ws)
         torch.cuda.synchronize()
         buf = dst.cpu().numpy()
@@ -110,6 +111,70 @@ def test_merge_requant_parity(torch_cuda, name, S, experts):
             print(f"[merge] {name} e{e} {proj}: retention {ret_gpu:.4f} (oracle {ret:.4f}), "
                   f"{n_waived_g} groups and {n_near} codes at near-ties")
 
+
+
+# Group widths and ranks beyond the two model shapes: groups of 128 and 96
+# inputs (two inputs per lane in the wave kernel, the second one partly
+# masked for 96), groups of 256 (the one-thread-per-group kernel), rank 0
+# (no delta: the stats stay 0 and the merge is the base requantised), and
+# rank 64 and 32 (the widest slices of A).
+WIDTH_CASES = [
+    ("g128_r32", G.MoEShape(512, 2, 256, 1, 128, 32, 64.0, 64), True),
+    ("g96_r64", G.MoEShape(6144, 2, 192, 1, 96, 64, 128.0, 64), True),
+    ("g256_r16", G.MoEShape(512, 2, 256, 1, 256, 16, 32.0, 64), True),
+    ("g64_r0", G.MoEShape(256, 2, 128, 1, 64, 8, 16.0, 64), False),
+    ("g32_r64", G.MoEShape(256, 2, 128, 1, 32, 64, 128.0, 64), True),
+]
+
+
+@pytest.mark.parametrize("name,S,lora", WIDTH_CASES, ids=[c[0] for c in WIDTH_CASES])
+def test_merge_requant_group_widths(torch_cuda, name, S, lora):
+    import torch
+    from int4_expert_streaming_amd import edge0 as E
+    lay = DeviceLayer(S, seed=9, layer=1, lora=lora)
+    sh0 = E.make_shape(S)
+    sh0.lora_rank = 0
+    lay0 = E.edge0_bundle_layout_of(sh0)
+    d, I, g = S.d_model, S.d_inter, S.group
+    r = S.lora_rank if lora else 0
+    scale = S.lora_alpha / S.lora_rank if lora else 0.0
+    stats = torch.zeros(6, dtype=torch.float64, device="cuda")
+    ws = None
+    for e in range(S.n_experts):
+        print(f"[merge] {name} expert {e}", flush=True)
+        dst = torch.full((int(lay0.bytes),), 0xA5, dtype=torch.uint8, device="cuda")
+        stats.fill_(float("nan"))  # every call must write all six figures
+        ws = E.edge0_merge_requant(lay.sh, lay.pool.slot_ptr(e), dst, stats, ws)
+        torch.cuda.synchronize()
+        buf = dst.cpu().numpy()
+        st = stats.cpu().numpy()
+        ex = lay.experts[e]
+
+        def arr(off, n, dt):
+            return np.frombuffer(buf[off:off + n * np.dtype(dt).itemsize].tobytes(), dtype=dt)
+        for p, (proj, n_out, n_in) in enumerate((("gate", I, d), ("up", I, d), ("down", d, I))):
+            qo = getattr(lay0, proj + "_q")
+            if proj == "down":
+                q_gpu = _down_codes(arr(qo, d * I // 8, np.uint32), d, I)
+                s_gpu = arr(lay0.down_s, (I // g) * d, np.uint16).reshape(I // g, d).T
+                b_gpu = arr(lay0.down_b, (I // g) * d, np.uint16).reshape(I // g, d).T
+            else:
+                q_gpu = _unpack_rows(arr(qo, n_out * n_in // 8, np.uint32).reshape(n_out, n_in // 8), n_in)
+                s_gpu = arr(getattr(lay0, proj + "_s"), n_out * (n_in // g), np.uint16).reshape(n_out, -1)
+                b_gpu = arr(getattr(lay0, proj + "_b"), n_out * (n_in // g), np.uint16).reshape(n_out, -1)
+            if lora:
+                A, B = lay.loras[e]["a_" + proj], lay.loras[e]["b_" + proj]
+            else:
+                A, B = np.zeros((0, n_in), np.uint16), np.zeros((n_out, 0), np.uint16)
+            ret, n_waived_g, n_near = _check_projection(
+                q_gpu, s_gpu, b_gpu, ex[proj + "_q"], ex[proj + "_s"], ex[proj + "_b"],
+                A, B, scale, g)
+            if r == 0:
+                assert st[2 * p] == 0.0 and st[2 * p + 1] == 0.0, (proj, st)
+            else:
+                ret_gpu = st[2 * p] / st[2 * p + 1]
+                assert abs(ret_gpu - ret) <= 1e-3 * max(1.0, abs(ret)) + 1e-4, (proj, ret_gpu, ret)
+            print(f"[merge] {name} e{e} {proj}: {n_waived_g} groups and {n_near} codes at near-ties")
 
 def test_merged_bundle_runs_in_the_layer(torch_cuda):
     """Merged bundles (LoRA-free layout) in a pool of their own through
