@@ -112,18 +112,20 @@ def test_merge_requant_parity(torch_cuda, name, S, experts):
                   f"{n_waived_g} groups and {n_near} codes at near-ties")
 
 
-
-# Group widths and ranks beyond the two model shapes: groups of 128 and 96
-# inputs (two inputs per lane in the wave kernel, the second one partly
-# masked for 96), groups of 256 (the one-thread-per-group kernel), rank 0
+# Group widths and ranks beyond the two model shapes: groups of 128, 96 and
+# 32 inputs (8, 6 and 2 blocks of 16 inputs per unit of the matrix-core
+# kernel), groups of 256 (the one-thread-per-group kernel), rank 0
 # (no delta: the stats stay 0 and the merge is the base requantised), and
-# rank 64 and 32 (the widest slices of A).
+# ranks 8, 32 and 64 (one, one and two rank chunks of the matrix-core
+# product; 64 at 128 inputs is the kernel's largest register set).
 WIDTH_CASES = [
     ("g128_r32", G.MoEShape(512, 2, 256, 1, 128, 32, 64.0, 64), True),
     ("g96_r64", G.MoEShape(6144, 2, 192, 1, 96, 64, 128.0, 64), True),
     ("g256_r16", G.MoEShape(512, 2, 256, 1, 256, 16, 32.0, 64), True),
     ("g64_r0", G.MoEShape(256, 2, 128, 1, 64, 8, 16.0, 64), False),
     ("g32_r64", G.MoEShape(256, 2, 128, 1, 32, 64, 128.0, 64), True),
+    ("g128_r64", G.MoEShape(512, 2, 256, 1, 128, 64, 128.0, 64), True),
+    ("g64_r8", G.MoEShape(512, 2, 256, 1, 64, 8, 16.0, 64), True),
 ]
 
 
