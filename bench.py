@@ -1132,7 +1132,7 @@ def row_stack(args, log):
             k_bytes = xlayer_bytes(S)
             k_traffic = None
         else:
-            k_name = "k_layer_fused (layer input + int4 gate/up GEMV + LoRA + SwiGLU)"
+            k_name = "k_layer_fused (layer input + LoRA A x + int4 gate/up GEMV; the LoRA B terms and SwiGLU follow in the down launch)"
             k_bytes = fused_bytes(S)
             k_traffic = gate_up_traffic()
     ds.stack.set_timing(0)
