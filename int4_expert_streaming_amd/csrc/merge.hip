@@ -12,8 +12,11 @@
 // Per group: s' = bf16((max W' - min W') / 15), b' = bf16(min W') (nearest,
 // ties to even), q' = round((W' - b') / s') to nearest-even clipped to 0..15
 // (q' = 0 when s' is 0), written into the merged bundle (the LoRA-free
-// layout of the same shape).  sum(actual delta) and sum(delta^2) are kept
-// in fp64, actual = s' q' + b' - W.
+// layout of the same shape).  The quotient is taken as (W' - b') times the
+// hardware fp32 reciprocal of s' (a few ulp from the exact quotient, so a
+// code can differ only where the quotient is that close to k + 1/2).
+// sum(actual delta) and sum(delta^2), actual = s' q' + b' - W, are added in
+// fp64 (k_merge_mfma first adds each lane's 4 g/16 terms of a unit in fp32).
 //
 // k_merge_mfma (groups of 32, 64, 96 or 128 inputs): one wave per group and
 // 16 rows of one projection; the 16 x g block of delta is one small matrix
