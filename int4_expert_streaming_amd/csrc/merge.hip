@@ -181,6 +181,7 @@ constexpr int kMergeRows = 16;  // rows of one projection per wave
 constexpr int kMergeWaves = 4;  // waves per workgroup
 
 typedef __attribute__((ext_vector_type(8))) __bf16 mg_bf16x8;
+typedef __attribute__((ext_vector_type(4))) short mg_bf16x4;  // bf16 bits
 typedef __attribute__((ext_vector_type(4))) float mg_f32x4;
 
 // Order-preserving integer keys of finite floats (the magnitude bits of a
@@ -242,10 +243,29 @@ __device__ __forceinline__ void merge_block(const MergeArgs& a, const MergeProj&
     return (size_t)o * (d / 8) + (size_t)G * (g / 8) + w;
   };
   auto sb_at = [&](int o) -> size_t { return DOWN ? (size_t)G * d + o : (size_t)o * gpr + G; };
-  // every load first: the operands, the code words, the scales and biases
+  // every load first: the operands, the code words, the scales and biases.
+  // Ranks 8 and 16 take one v_mfma_f32_16x16x16_bf16 per block (lane (n, j)
+  // supplies ranks 4j .. 4j + 3), wider ranks chunks of 32.
+  constexpr bool K16 = RK > 0 && RK <= 16;
   mg_bf16x8 opb[KC > 0 ? KC : 1], opa[KC > 0 ? KC : 1][NB];
+  mg_bf16x4 opb4, opa4[NB];
+  if constexpr (K16) {
+    const int k0 = 4 * j;
+    const bool kv = k0 < RK;
+    const int kc = kv ? k0 : 0;
+    const uint2 braw = *reinterpret_cast<const uint2*>(m.B + (size_t)(row0 + n) * RK + kc);
+    opb4 = __builtin_bit_cast(mg_bf16x4, kv ? braw : make_uint2(0, 0));
+    const uint16_t* ab = m.A + (size_t)kc * n_in + (size_t)G * g + n;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
+    for (int mb = 0; mb < NB; ++mb) {
+      const uint32_t w0 = (uint32_t)ab[16 * mb] | ((uint32_t)ab[(size_t)n_in + 16 * mb] << 16);
+      const uint32_t w1 = (uint32_t)ab[(size_t)2 * n_in + 16 * mb] |
+                          ((uint32_t)ab[(size_t)3 * n_in + 16 * mb] << 16);
+      opa4[mb] = __builtin_bit_cast(mg_bf16x4, kv ? make_uint2(w0, w1) : make_uint2(0, 0));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < (K16 ? 0 : KC); ++c) {
     const int k0 = 32 * c + 8 * j;  // this lane's first rank of the chunk
     const bool kv = k0 < RK;
     const int kc = kv ? k0 : 0;
@@ -280,9 +300,13 @@ __device__ __forceinline__ void merge_block(const MergeArgs& a, const MergeProj&
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) {
     acc[mb] = mg_f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (K16) {
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(opb4, opa4[mb], acc[mb], 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opb[c], opa[c][mb], acc[mb], 0, 0, 0);
+      for (int c = 0; c < KC; ++c)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opb[c], opa[c][mb], acc[mb], 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
