@@ -214,10 +214,12 @@ __device__ __forceinline__ void row16_minmax(float& lo, float& hi) {
 
 // One wave: 16 rows (row0 + 0..15) of one projection and one group of
 // g = 16 NB inputs.  The delta of the 16 x g block is B[rows][0..r) times
-// A[0..r)[group] on v_mfma_f32_16x16x32_bf16 (rank chunks of 32, zero past
-// r): lane l = (n = l % 16, j = l / 16) supplies row n's ranks 8j .. 8j + 7
-// of the chunk and column n's (of a 16-input block) same ranks, and holds
-// the products for rows 4j + v (v < 4) at input n of each block m.  The
+// A[0..r)[group] on the matrix cores, per 16-input block one
+// v_mfma_f32_16x16x16_bf16 for r <= 16 or v_mfma_f32_16x16x32_bf16 per
+// chunk of 32 ranks (zero past r): lane l = (n = l % 16, j = l / 16)
+// supplies row n's ranks 4j .. 4j + 3 (8j .. 8j + 7 of a chunk) and column
+// n's same ranks, and holds the products for rows 4j + v (v < 4) at input n
+// of each block m.  The
 // lane's 4 NB elements are then requantised; each group's range is the
 // lane's and then its 16-lane row's.  The codes are written as bytes into
 // the wave's LDS tile [16][g] and read back 8 at a time as code words.
