@@ -370,7 +370,13 @@ void k_merge_mfma(MergeArgs a) {
   __shared__ __align__(16) uint8_t tile[kMergeWaves][kMergeRows * g];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kMergeWaves + wave;
+  // XCD-aware order: consecutive workgroups go to different XCDs (round-robin
+  // over 8), so logical block L = (id % 8) (n / 8) + id / 8 gives each XCD a
+  // contiguous range of units, whole 16-row blocks whose B rows then come
+  // from memory once
+  const int nb = gridDim.x;
+  const int bid = nb % 8 == 0 ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int unit = bid * kMergeWaves + wave;
   float sad = 0.f, sdd = 0.f;  // this lane's 4 NB terms
   if (unit < a.n_units) {
     // unit -> (projection, block of 16 rows, group); the group runs fastest
@@ -401,11 +407,11 @@ void k_merge_mfma(MergeArgs a) {
     const int q = threadIdx.x;
     double x = 0.0;
     for (int w2 = 0; w2 < kMergeWaves; ++w2) {
-      const int uw = blockIdx.x * kMergeWaves + w2;
+      const int uw = bid * kMergeWaves + w2;
       const int pw = uw < a.u_gu ? 0 : (uw < 2 * a.u_gu ? 1 : 2);
       if (uw < a.n_units && pw == (q >> 1)) x += red[w2][q & 1];
     }
-    a.partial[(size_t)blockIdx.x * 6 + q] = x;
+    a.partial[(size_t)bid * 6 + q] = x;
   }
 }
 
