@@ -53,6 +53,10 @@ METRIC = "decode tok/s (batch 1, 40-layer MoE stack) + achieved HBM GB/s vs peak
 TRAFFIC_RECORD = {"src_sha": "af617369d9b2ef8e", "fetch_kib": 3884.8, "write_kib": 54.1,
                   "fetch_scale": 2.0, "write_scale": 1.0}
 KERNEL_SOURCES = ("common.h", "moe_internal.h", "gemv_dev.h", "heads_dev.h", "moe.hip")
+# the same two counters for k_merge_mfma<16, 4> (one Qwen3-MoE-shaped expert),
+# valid for the merge source they were taken on
+MERGE_TRAFFIC_RECORD = {"src_sha": "e4afe3fcf46594bb", "fetch_kib": 1677.8, "write_kib": 2646.0,
+                        "fetch_scale": 2.0, "write_scale": 1.0}
 HBM_PEAK_GBPS = 8000.0
 N_LAYERS, OWNERS, CONSUMERS = 40, (6, 37), (7, 38)
 
@@ -122,6 +126,18 @@ def xlayer_bytes(S):
     layer's h and fixed-point y read; x, y, h and the fixed-point y written."""
     d = S.d_model
     return moe_alg_bytes(S) + d * 2 + d * 8 + 3 * d * 2 + d * 8
+
+
+def merge_traffic():
+    """Counter-derived HBM bytes per k_merge_mfma launch, or None if merge.hip
+    changed since the counters were taken."""
+    import hashlib
+    with open(os.path.join(ROOT, "int4_expert_streaming_amd", "csrc", "merge.hip"), "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    r = MERGE_TRAFFIC_RECORD
+    if h != r["src_sha"]:
+        return None
+    return int((r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"]) * 1024)
 
 
 def gate_up_traffic():
@@ -713,7 +729,8 @@ def row_merge(args, log, inst):
            "roofline": {"kernel": "k_merge_mfma + k_merge_sum (one expert)", "bound": "alu",
                         "achieved": round(flops / (us * 1e-6) / 1e12, 3), "peak": 157.3,
                         "unit": "TFLOP/s", "frac": round(flops / (us * 1e-6) / 1e12 / 157.3, 4),
-                        "traffic": None, "avg_launch_us": round(us, 2),
+                        "traffic": merge_traffic(), "traffic_kernel": "k_merge_mfma only",
+                        "avg_launch_us": round(us, 2),
                         "hbm_bytes_per_expert": hbm_bytes,
                         "hbm_gbps": round(hbm_bytes / (us * 1e-6) / 1e9, 1),
                         "note": "fp32 count: 2r + 8 per weight element (the delta's 2r run on "
